@@ -1,0 +1,394 @@
+"""Pins of the CPU oracle to facts fixed by the pages and by mathematics.
+
+Each test checks the oracle against something other than itself: hand-built
+vectors from the pages, closed forms, brute-force searches, exact rational
+arithmetic, invariants and independent library routines.  A plausible mistake
+in the oracle (a dropped term, a wrong sign or index, a transposed operand, a
+wrong Qmax, a symmetric instead of asymmetric range, a swapped nibble order)
+fails at least one of them.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synth_inputs as SI
+from oracle import lbq_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32 = np.float32
+
+
+def _f32_ulp(x):
+    x = np.abs(np.asarray(x, dtype=F32))
+    return (np.nextafter(x, F32(np.inf)) - x).astype(np.float64)
+
+
+# ---------------------------------------------------------------- packing
+
+def _packing_rows():
+    rows = []
+    with open(os.path.join(GOLDEN, "packing_vectors.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            b, codes, packed = [p.strip() for p in line.split("|")]
+            rows.append((int(b), [int(c) for c in codes.split()],
+                         [int(h, 16) for h in packed.split()]))
+    return rows
+
+
+@pytest.mark.parametrize("bits,codes,expect", _packing_rows())
+def test_packing_golden_vectors(bits, codes, expect):
+    got = O.pack_codes(np.array([codes], dtype=np.uint8), bits)[0]
+    assert list(got) == expect
+    back = O.unpack_codes(np.array([expect], dtype=np.uint8), bits)[0]
+    assert list(back) == codes
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_unpack_pack_identity(bits):
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 1 << bits, size=(5, 64)).astype(np.uint8)
+    assert np.array_equal(O.unpack_codes(O.pack_codes(codes, bits), bits), codes)
+    raw = rng.integers(0, 256, size=(3, 16)).astype(np.uint8)
+    assert np.array_equal(O.pack_codes(O.unpack_codes(raw, bits), bits), raw)
+
+
+# ---------------------------------------------------------------- bf16
+
+def test_bf16_matches_torch_cpu_conversion():
+    import torch
+    rng = np.random.default_rng(11)
+    x = np.concatenate([
+        rng.standard_normal(1_000_000).astype(F32) * F32(3.0),
+        (rng.standard_normal(20000) * 1e-38).astype(F32),       # subnormals
+        (rng.standard_normal(20000) * 1e30).astype(F32),
+        np.array([0.0, -0.0, 1.0, -1.0, 3.4e38, -3.4e38, 1e-45], dtype=F32),
+    ])
+    # exact ties: low 16 bits == 0x8000, both parities of the kept bit
+    ties = (rng.integers(0x0080, 0x7F00, size=4000, dtype=np.uint32) << np.uint32(16)) | np.uint32(0x8000)
+    x = np.concatenate([x, ties.view(F32), (-ties.view(F32)).astype(F32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.bf16_bits(x), ref)
+    assert np.array_equal(O.bf16_to_f64(ref), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).double().numpy())
+
+
+# ---------------------------------------------------------------- MinMax
+
+CASES = [(4, 128), (2, 64), (4, 64), (2, 128)]
+
+
+@pytest.mark.parametrize("bits,group", CASES)
+def test_minmax_codes_are_nearest_level_bruteforce(bits, group):
+    """With the stored (s, z), every code is the level (q - z)*s nearest to w
+    among q in [0, Qmax], found by exhaustive fp64 search (ties excused)."""
+    qmax = (1 << bits) - 1
+    W = SI.gaussian_weights(101, 48, 4 * group, outlier_seed=102)
+    codes, s, z = O.minmax_quantize(W, bits, group)
+    N, K = W.shape
+    w = W.astype(np.float64).reshape(N, K // group, group)
+    levels = (np.arange(qmax + 1)[None, None, :] - z.astype(np.float64)[:, :, None]) * s.astype(np.float64)[:, :, None]
+    dist = np.abs(w[..., None] - levels[:, :, None, :])
+    best = dist.argmin(axis=-1)
+    got = codes.reshape(best.shape).astype(np.int64)
+    srt = np.sort(dist, axis=-1)
+    near_tie = (srt[..., 1] - srt[..., 0]) <= 4 * _f32_ulp(w) + 1e-300
+    bad = (best != got) & ~near_tie
+    assert not bad.any()
+
+
+@pytest.mark.parametrize("bits,group", CASES)
+def test_minmax_scale_and_zero_closed_form(bits, group):
+    """s*Qmax spans the group's range including 0 (to one fp32 rounding), the
+    group minimum gets code 0 when it is negative and the maximum gets Qmax."""
+    qmax = (1 << bits) - 1
+    W = SI.gaussian_weights(103, 32, 4 * group, outlier_seed=104)
+    codes, s, z = O.minmax_quantize(W, bits, group)
+    N, K = W.shape
+    Wg = W.astype(np.float64).reshape(N, K // group, group)
+    cg = codes.reshape(N, K // group, group)
+    span = np.maximum(0, Wg.max(-1)) - np.minimum(0, Wg.min(-1))
+    assert np.all(np.abs(s.astype(np.float64) * qmax - span) <= span * 2.0 ** -22)
+    # zero point: (0 - z) * s reproduces the group minimum to within s/2
+    assert np.all(np.abs(-z.astype(np.float64) * s - np.minimum(0, Wg.min(-1))) <= 0.5 * s * (1 + 2.0 ** -20))
+    imin = Wg.argmin(-1)[..., None]
+    imax = Wg.argmax(-1)[..., None]
+    assert np.all(np.take_along_axis(cg, imin, -1) == 0)
+    assert np.all(np.take_along_axis(cg, imax, -1) == qmax)
+
+
+@pytest.mark.parametrize("bits,group", CASES)
+def test_minmax_error_bound(bits, group):
+    """|w - (q - z) s| <= s (1/2 + 2^-18), in fp64 against the stored fp32 s."""
+    W = np.concatenate([SI.gaussian_weights(105, 64, 512, outlier_seed=106),
+                        SI.student_t_weights(107, 64, 512)])
+    codes, s, z = O.minmax_quantize(W, bits, group)
+    err = np.abs(W.astype(np.float64) - O.minmax_exact(codes, s, z, group))
+    bound = np.repeat(s.astype(np.float64), group, axis=1) * (0.5 + 2.0 ** -18)
+    assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("bits,group", CASES)
+def test_minmax_requantize_with_fixed_params_is_identity(bits, group):
+    """quantize(dequantize(q)) == q with the stored (s, z) held fixed, both for
+    the fp32 product and for the bf16-rounded dequantized weight."""
+    W = SI.gaussian_weights(108, 40, 512, outlier_seed=109)
+    codes, s, z = O.minmax_quantize(W, bits, group)
+    N, K = W.shape
+    qmax = (1 << bits) - 1
+    srep = np.repeat(s, group, axis=1)
+    zrep = np.repeat(z.astype(np.int32), group, axis=1)
+    w32 = ((codes.astype(np.int32) - zrep).astype(F32) * srep).astype(F32)
+    wbf = O.bf16_to_f64(O.minmax_dequant_bf16(codes, s, z, group)).astype(F32)
+    for wh in (w32, wbf):
+        q2 = np.clip(np.rint(wh / srep).astype(np.int32) + zrep, 0, qmax)
+        assert np.array_equal(q2, codes.astype(np.int32))
+
+
+def test_minmax_all_zero_weight():
+    W = np.zeros((4, 256), dtype=F32)
+    for bits, group in CASES:
+        codes, s, z = O.minmax_quantize(W, bits, group)
+        assert np.all(codes == 0) and np.all(z == 0) and np.all(s == 1)
+        assert np.all(O.minmax_exact(codes, s, z, group) == 0)
+        assert np.all(O.minmax_dequant_bf16(codes, s, z, group) == 0)
+
+
+@pytest.mark.parametrize("bits,group", CASES)
+def test_minmax_single_nonzero_per_group(bits, group):
+    """One nonzero v per group: range [min(0,v), max(0,v)], so v > 0 gives
+    z = 0, code(v) = Qmax, others 0; v < 0 gives z = Qmax, code(v) = 0, others Qmax."""
+    qmax = (1 << bits) - 1
+    rng = np.random.default_rng(110)
+    N, K = 6, 4 * group
+    W = np.zeros((N, K), dtype=F32)
+    pos = rng.integers(0, group, size=(N, K // group))
+    vals = (rng.uniform(0.01, 3.0, size=(N, K // group)) * np.where(rng.random((N, K // group)) < 0.5, -1, 1)).astype(F32)
+    for i in range(N):
+        for j in range(K // group):
+            W[i, j * group + pos[i, j]] = vals[i, j]
+    codes, s, z = O.minmax_quantize(W, bits, group)
+    cg = codes.reshape(N, K // group, group)
+    for i in range(N):
+        for j in range(K // group):
+            v = float(vals[i, j])
+            assert s[i, j] == F32(abs(v)) / F32(qmax)
+            if v > 0:
+                assert z[i, j] == 0 and cg[i, j, pos[i, j]] == qmax
+                assert np.count_nonzero(cg[i, j]) == 1
+            else:
+                assert z[i, j] == qmax and cg[i, j, pos[i, j]] == 0
+                assert np.count_nonzero(cg[i, j] == qmax) == group - 1
+
+
+@pytest.mark.parametrize("bits,group", CASES)
+def test_minmax_power_of_two_grid_is_lossless(bits, group):
+    W = SI.grid_weights(111, 8, 4 * group, group, bits, exp=4)
+    codes, s, z = O.minmax_quantize(W, bits, group)
+    assert np.all(s == F32(2.0 ** -4))
+    assert np.array_equal(O.minmax_exact(codes, s, z, group), W.astype(np.float64))
+    assert np.array_equal(O.bf16_to_f64(O.minmax_dequant_bf16(codes, s, z, group)), W.astype(np.float64))
+
+
+def test_minmax_single_signed_group_range_includes_zero():
+    """An all-positive group keeps lo = 0 (the reading that the range covers 0)."""
+    W = np.full((1, 128), 0.5, dtype=F32)
+    W[0, :64] = 0.2
+    codes, s, z = O.minmax_quantize(W, 4, 128)
+    assert z[0, 0] == 0 and s[0, 0] == F32(0.5) / F32(15)
+    assert codes[0, 64] == 15 and codes[0, 0] == 6  # 0.2 / (0.5/15) = 6
+
+
+# ---------------------------------------------------------------- NF4
+
+def test_nf4_codebook_invariants():
+    c = O.nf4_codebook()
+    assert c.dtype == F32 and c.shape == (16,)
+    assert np.all(np.diff(c.astype(np.float64)) > 0)
+    assert c[0] == F32(-1.0) and c[7] == F32(0.0) and c[15] == F32(1.0)
+    assert np.count_nonzero(c < 0) == 7 and np.count_nonzero(c > 0) == 8
+
+
+def test_nf4_codebook_against_scipy_normal_quantiles():
+    """Recompute the levels with scipy's ndtri (an independent routine) and
+    check the forward CDF puts them at the evenly spaced probabilities."""
+    from scipy.special import ndtr, ndtri
+    delta = 1.0 - 0.5 * (1.0 / 30.0 + 1.0 / 32.0)
+    top = ndtri(delta)
+    pos = ndtri(np.linspace(delta, 0.5, 9)[:-1])
+    neg = -ndtri(np.linspace(delta, 0.5, 8)[:-1])
+    ref = np.sort(np.concatenate([pos, neg, [0.0]])) / top
+    c = O.nf4_codebook()
+    assert np.array_equal(ref.astype(F32), c)
+    probs = ndtr(c[8:].astype(np.float64) * top)
+    assert np.allclose(probs[::-1], np.linspace(delta, 0.5, 9)[:-1], atol=1e-6)
+
+
+def test_nf4_codebook_golden_file():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "nf4_codebook.txt")) if not l.startswith("#")]
+    stored = np.array([int(r[0], 16) for r in rows], dtype=np.uint32).view(F32)
+    assert np.array_equal(stored, O.nf4_codebook())
+
+
+def test_nf4_encode_is_nearest_level_bruteforce():
+    W = SI.gaussian_weights(120, 64, 512, outlier_seed=121)
+    codes, a = O.nf4_quantize(W, 64)
+    c = O.nf4_codebook().astype(np.float64)
+    blocks = W.reshape(-1, 64)
+    x = (blocks / a[:, None]).astype(np.float64)  # the same fp32 x the rule sees
+    d = np.abs(x[..., None] - c)
+    best = d.argmin(-1)  # ties -> lower index (argmin returns the first)
+    srt = np.sort(d, -1)
+    near = (srt[..., 1] - srt[..., 0]) <= 2 * _f32_ulp(x) + 1e-12
+    got = codes.reshape(-1, 64)
+    assert not ((best != got) & ~near).any()
+    # the block's absmax element encodes to an extreme level
+    i = np.abs(blocks).argmax(1)
+    ext = got[np.arange(len(i)), i]
+    assert np.all((ext == 0) | (ext == 15))
+
+
+def test_nf4_special_blocks():
+    W = np.zeros((2, 128), dtype=F32)
+    W[1, 64:] = np.tile(np.array([-0.5, 0.0, 0.5, 0.0], dtype=F32), 16)
+    codes, a = O.nf4_quantize(W, 64)
+    assert np.all(codes[0] == 7) and np.all(codes[1, :64] == 7)
+    assert a[0] == 0 and a[2] == 0 and a[3] == F32(0.5)
+    assert list(codes[1, 64:68]) == [0, 7, 15, 7]
+    assert np.array_equal(O.nf4_exact(codes, a, 64), W.astype(np.float64))
+
+
+def test_nf4_requantize_with_fixed_absmax_is_identity():
+    W = SI.gaussian_weights(122, 32, 512)
+    codes, a = O.nf4_quantize(W, 64)
+    c = O.nf4_codebook()
+    wh = (c[codes.reshape(-1, 64)] * a[:, None]).astype(F32)
+    safe = np.where(a == 0, F32(1), a)
+    x = wh / safe[:, None]
+    again = np.searchsorted(O.nf4_midpoints(c), x, side="left")
+    assert np.array_equal(again, codes.reshape(-1, 64))
+
+
+# ---------------------------------------------------------------- double quant
+
+def test_double_quant_values():
+    rng = np.random.default_rng(130)
+    a = np.abs(rng.standard_normal(1000)).astype(F32) * F32(0.05)
+    q2, c2 = O.double_quant(a, 256)
+    assert c2.shape == (4,) and q2.dtype == np.int8
+    for b in range(4):
+        seg = a[b * 256:(b + 1) * 256]
+        assert c2[b] == seg.max() / F32(127)
+        assert q2[b * 256 + int(seg.argmax())] == 127
+        # brute force: each q2 is the nearest of 0..127 to a / c2 (ties excused)
+        lv = np.arange(128) * np.float64(c2[b])
+        d = np.abs(seg.astype(np.float64)[:, None] - lv)
+        best = d.argmin(1)
+        srt = np.sort(d, 1)
+        near = (srt[:, 1] - srt[:, 0]) <= 4 * _f32_ulp(seg) + 1e-300
+        assert not ((best != q2[b * 256:(b + 1) * 256]) & ~near).any()
+    ah = O.double_dequant_absmax(q2, c2, 256)
+    assert np.all(np.abs(ah.astype(np.float64) - a) <= 0.5 * np.repeat(c2, 256)[:1000] * (1 + 2.0 ** -20))
+    zq, zc = O.double_quant(np.zeros(300, dtype=F32), 256)
+    assert np.all(zq == 0) and np.all(zc == 0)
+
+
+def test_double_quant_saving_closed_form():
+    vals = dict(l.split() for l in open(os.path.join(GOLDEN, "dq_saving.txt")) if not l.startswith("#"))
+    expect = float(vals["bits_per_param"])
+    assert expect == 0.5 - (8 / 64 + 32 / (64 * 256))
+    for shapes in (SI.LLAMA3_8B, SI.LLAMA3_70B, SI.QWEN15_110B):
+        for n, k in shapes.values():
+            assert O.dq_saving_bits_per_param(n, k) == expect
+    # the byte counts the oracle actually produces agree with the formula
+    W = SI.gaussian_weights(131, 64, 1024)
+    codes, a = O.nf4_quantize(W, 64)
+    q2, c2 = O.double_quant(a, 256)
+    saved = a.nbytes - (q2.nbytes + c2.nbytes)
+    assert 8.0 * saved / W.size == expect
+    gb = float(vals["params_65b"]) * expect / 8
+    assert abs(gb - float(vals["saving_bytes_65b_approx"])) < 0.05e9
+
+
+# ---------------------------------------------------------------- matmuls
+
+def _frac_bf16(bits):
+    return [[Fraction(float(v)) for v in row] for row in O.bf16_to_f64(bits)]
+
+
+def _frac_mat(a):
+    return [[Fraction(float(v)) for v in row] for row in a]
+
+
+def test_linear_fwd_matches_exact_rational_triple_loop():
+    W = SI.gaussian_weights(140, 5, 128)
+    q = O.quantize(W, "minmax", 4, 64)
+    X = SI.bf16_normal(141, (3, 128))
+    Y = O.linear_fwd(X, q["w_exact"])
+    Xf, Wf = _frac_bf16(X), _frac_mat(q["w_exact"])
+    for m in range(3):
+        for n in range(5):
+            exact = sum(Xf[m][k] * Wf[n][k] for k in range(128))
+            assert abs(float(exact) - Y[m, n]) <= 1e-12 * max(1.0, abs(float(exact)))
+
+
+def test_grid_matmul_is_exact_and_adjoint():
+    """Grid weights and small-integer activations: every fp64 sum is exact, so
+    forward and input-gradient must equal exact integer arithmetic, and
+    <dY, X W^T> == <dY W, X> pins the transposes."""
+    W = SI.grid_weights(142, 16, 256, 128, 4)
+    q = O.quantize(W, "minmax", 4, 128)
+    X = SI.bf16_small_ints(143, (4, 256))
+    dY = SI.bf16_small_ints(144, (4, 16))
+    Wi = (W.astype(np.float64) * 16).astype(np.int64)
+    Xi = O.bf16_to_f64(X).astype(np.int64)
+    dYi = O.bf16_to_f64(dY).astype(np.int64)
+    Y = O.linear_fwd(X, q["w_exact"])
+    dX = O.linear_bwd_dx(dY, q["w_exact"])
+    Yi = np.array([[sum(int(Xi[m, k]) * int(Wi[n, k]) for k in range(256)) for n in range(16)] for m in range(4)])
+    dXi = np.array([[sum(int(dYi[m, n]) * int(Wi[n, k]) for n in range(16)) for k in range(256)] for m in range(4)])
+    assert np.array_equal(Y * 16, Yi.astype(np.float64))
+    assert np.array_equal(dX * 16, dXi.astype(np.float64))
+    assert (dYi * Yi).sum() == (dXi * Xi).sum()
+
+
+def test_lora_zero_weight_is_pure_adapter_branch():
+    rng_shapes = (3, 64, 8, 4)  # M, K, N, r
+    M, K, N, r = rng_shapes
+    W = np.zeros((N, K), dtype=F32)
+    q = O.quantize(W, "nf4", double_quant_on=True)
+    assert np.all(q["w_exact"] == 0)
+    X = SI.bf16_normal(150, (M, K))
+    A = SI.bf16_normal(151, (r, K), std=0.01)
+    B = SI.bf16_normal(152, (N, r), std=0.01)
+    for sigma in (1.0, 2.0):
+        Y = O.lora_fwd(X, q["w_exact"], A, B, sigma)
+        Xf, Af, Bf = _frac_bf16(X), _frac_bf16(A), _frac_bf16(B)
+        for m in range(M):
+            for n in range(N):
+                t = [sum(Xf[m][k] * Af[j][k] for k in range(K)) for j in range(r)]
+                exact = Fraction(sigma) * sum(t[j] * Bf[n][j] for j in range(r))
+                assert abs(float(exact) - Y[m, n]) <= 1e-12 * max(1e-6, abs(float(exact)))
+
+
+def test_channel_mix_equals_unsplit_layer():
+    """Splitting the output channels into two sub-tensors of one format and
+    scattering them back reproduces the unsplit layer exactly."""
+    W = SI.gaussian_weights(160, 32, 256)
+    X = SI.bf16_normal(161, (3, 256))
+    rows4 = SI.channel_mask(162, 32)
+    rows2 = np.setdiff1d(np.arange(32), rows4).astype(np.int32)
+    full = O.quantize(W, "minmax", 4, 128)
+    p4 = O.quantize(W[rows4], "minmax", 4, 128)
+    p2 = O.quantize(W[rows2], "minmax", 4, 128)
+    Y = O.channel_mix_fwd(X, [(rows4, p4["w_exact"]), (rows2, p2["w_exact"])])
+    assert np.array_equal(Y, O.linear_fwd(X, full["w_exact"]))
+
+
+def test_rel_errors_definition():
+    ref = np.array([[3.0, 4.0]])
+    fro, mx = O.rel_errors(ref + np.array([[0.0, 0.5]]), ref)
+    assert fro == pytest.approx(0.1) and mx == pytest.approx(0.125)

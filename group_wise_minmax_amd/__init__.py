@@ -1,0 +1,258 @@
+"""group_wise_minmax_amd -- low-bit group-wise weight quantization and the fused
+dequantize-then-matmul of a frozen low-bit linear layer on AMD MI355X (gfx950).
+
+This package is a thin binding over the C ABI of ``liblbq.so``
+(``include/lbq.h``): every function below only marshals torch tensors into
+pointers and sizes, allocates outputs with torch, and calls the library on the
+current HIP stream.  All arithmetic runs in the library's HIP kernels; there is
+no fallback.  The functions carry the C names:
+
+    lbq_layout, lbq_quantize, lbq_dequant, lbq_linear_fwd, lbq_linear_bwd_dx,
+    lbq_lora_fwd, lbq_nf4_codebook
+
+Formats (cited by page title and section):
+  * MinMax INT4 g128 / INT2 g64 -- GreenBit.AI, "只需单卡RTX 3090，低比特量化训练
+    就能实现LLaMA-3 8B全参微调", section 模型量化;
+  * NF4 with optional double quantization of the absmax -- "QLoRA技术在量化微调中的应用",
+    section QLoRA技术原理; bitsandbytes FSDP-QLoRA guide, step 2 parameter table.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+from ._lib import (LBQ_MINMAX, LBQ_NF4, Desc, LbqError, QTensor, Sizes, check, lib,  # noqa: F401
+                   STATUS_CODE, EXPORTED, LIB_PATH)
+
+__all__ = [
+    "QuantizedWeight", "make_desc", "lbq_layout", "lbq_quantize", "lbq_dequant",
+    "lbq_linear_fwd", "lbq_linear_bwd_dx", "lbq_lora_fwd", "lbq_nf4_codebook",
+    "lbq_linear_workspace_bytes", "lbq_lora_workspace_bytes", "LbqError", "version",
+]
+
+_FMT = {"minmax": LBQ_MINMAX, "nf4": LBQ_NF4}
+
+
+def version() -> str:
+    return lib.lbq_version().decode()
+
+
+def make_desc(fmt: str, n: int, k: int, bits: int = 4, group: Optional[int] = None,
+              double_quant: bool = True) -> Desc:
+    """Descriptor for W[n][k]. MinMax: bits 4/2, group 128/64 (default 128 for
+    4-bit, 64 for 2-bit). NF4: absmax block 64, optional double quant (256)."""
+    if fmt not in _FMT:
+        raise ValueError(f"format must be one of {sorted(_FMT)}")
+    d = Desc()
+    d.format = _FMT[fmt]
+    if fmt == "minmax":
+        d.bits = bits
+        d.group = group if group is not None else (128 if bits == 4 else 64)
+        d.double_quant = 0
+        d.dq_block = 0
+    else:
+        d.bits = 4
+        d.group = 64 if group is None else group
+        d.double_quant = 1 if double_quant else 0
+        d.dq_block = 256 if double_quant else 0
+    d.reserved = 0
+    d.n = n
+    d.k = k
+    return d
+
+
+def lbq_layout(desc: Desc) -> dict:
+    s = Sizes()
+    check(lib.lbq_layout(ctypes.byref(desc), ctypes.byref(s)), "lbq_layout")
+    return {f: getattr(s, f) for f, _ in Sizes._fields_}
+
+
+def lbq_nf4_codebook() -> list:
+    buf = (ctypes.c_float * 16)()
+    lib.lbq_nf4_codebook(buf)
+    return list(buf)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+@dataclass
+class QuantizedWeight:
+    """Device buffers of one quantized weight plus its descriptor."""
+    desc: Desc
+    packed: torch.Tensor
+    scales: Optional[torch.Tensor] = None
+    zeros: Optional[torch.Tensor] = None
+    absmax: Optional[torch.Tensor] = None
+    absmax_q: Optional[torch.Tensor] = None
+    absmax_scale: Optional[torch.Tensor] = None
+    out_rows: Optional[torch.Tensor] = field(default=None)
+
+    @property
+    def n(self) -> int:
+        return self.desc.n
+
+    @property
+    def k(self) -> int:
+        return self.desc.k
+
+    @property
+    def device(self) -> torch.device:
+        return self.packed.device
+
+    def qtensor(self) -> QTensor:
+        q = QTensor()
+        q.packed = _ptr(self.packed)
+        q.scales = _ptr(self.scales)
+        q.zeros = _ptr(self.zeros)
+        q.absmax = _ptr(self.absmax)
+        q.absmax_q = _ptr(self.absmax_q)
+        q.absmax_scale = _ptr(self.absmax_scale)
+        q.out_rows = _ptr(self.out_rows)
+        return q
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in
+                   (self.packed, self.scales, self.zeros, self.absmax, self.absmax_q,
+                    self.absmax_scale) if t is not None)
+
+    @staticmethod
+    def empty(desc: Desc, device) -> "QuantizedWeight":
+        sz = lbq_layout(desc)
+        dev = torch.device(device)
+        n, k = desc.n, desc.k
+        qw = QuantizedWeight(desc, torch.empty((n, sz["packed"] // n), dtype=torch.uint8, device=dev))
+        if sz["scales"]:
+            qw.scales = torch.empty((n, sz["scales"] // 4 // n), dtype=torch.float32, device=dev)
+            qw.zeros = torch.empty((n, sz["zeros"] // n), dtype=torch.uint8, device=dev)
+        if sz["absmax"]:
+            qw.absmax = torch.empty(sz["absmax"] // 4, dtype=torch.float32, device=dev)
+        if sz["absmax_q"]:
+            qw.absmax_q = torch.empty(sz["absmax_q"], dtype=torch.int8, device=dev)
+            qw.absmax_scale = torch.empty(sz["absmax_scale"] // 4, dtype=torch.float32, device=dev)
+        return qw
+
+
+def lbq_quantize(W: torch.Tensor, fmt: str = "minmax", bits: int = 4, group: Optional[int] = None,
+                 double_quant: bool = True, out: Optional[QuantizedWeight] = None) -> QuantizedWeight:
+    """Quantize a device fp32 weight W[n][k] (see ``lbq_quantize`` in lbq.h)."""
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [n, k]")
+    _need(W, "W", torch.float32)
+    desc = make_desc(fmt, W.shape[0], W.shape[1], bits, group, double_quant)
+    qw = out if out is not None else QuantizedWeight.empty(desc, W.device)
+    q = qw.qtensor()
+    check(lib.lbq_quantize(ctypes.byref(desc), W.data_ptr(), ctypes.byref(q), _stream(W.device)),
+          "lbq_quantize")
+    qw.desc = desc
+    return qw
+
+
+def lbq_dequant(qw: QuantizedWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 W_hat[n][k] (see ``lbq_dequant`` in lbq.h)."""
+    if out is None:
+        out = torch.empty((qw.n, qw.k), dtype=torch.bfloat16, device=qw.device)
+    _need(out, "out", torch.bfloat16, (qw.n, qw.k))
+    q = qw.qtensor()
+    check(lib.lbq_dequant(ctypes.byref(qw.desc), ctypes.byref(q), out.data_ptr(), _stream(qw.device)),
+          "lbq_dequant")
+    return out
+
+
+def lbq_linear_workspace_bytes(qw: QuantizedWeight, m: int) -> int:
+    return lib.lbq_linear_workspace_bytes(ctypes.byref(qw.desc), m)
+
+
+def lbq_lora_workspace_bytes(qw: QuantizedWeight, m: int, r: int) -> int:
+    return lib.lbq_lora_workspace_bytes(ctypes.byref(qw.desc), m, r)
+
+
+def _ws(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    return torch.empty(((nbytes + 15) // 16) * 16, dtype=torch.uint8, device=device)
+
+
+def lbq_linear_fwd(X: torch.Tensor, qw: QuantizedWeight, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X . deq(W)^T in bf16 (see ``lbq_linear_fwd`` in lbq.h).  With
+    ``qw.out_rows`` set, ``out`` must be given and only those columns are written."""
+    _need(X, "X", torch.bfloat16)
+    m = X.shape[0]
+    if X.dim() != 2 or X.shape[1] != qw.k:
+        raise ValueError(f"X must be [m, {qw.k}]")
+    if out is None:
+        if qw.out_rows is not None:
+            raise ValueError("out must be given when out_rows is set")
+        out = torch.empty((m, qw.n), dtype=torch.bfloat16, device=X.device)
+    if out.dtype != torch.bfloat16 or out.dim() != 2 or out.shape[0] != m or out.stride(1) != 1:
+        raise ValueError("out must be bf16 [m, >=n] with unit column stride")
+    nbytes = lbq_linear_workspace_bytes(qw, m)
+    if workspace is None:
+        workspace = _ws(nbytes, X.device)
+    q = qw.qtensor()
+    check(lib.lbq_linear_fwd(ctypes.byref(qw.desc), ctypes.byref(q), X.data_ptr(), m, out.data_ptr(),
+                             out.stride(0), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                             _stream(X.device)), "lbq_linear_fwd")
+    return out
+
+
+def lbq_linear_bwd_dx(dY: torch.Tensor, qw: QuantizedWeight,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dX = dY . deq(W) in bf16 (see ``lbq_linear_bwd_dx`` in lbq.h)."""
+    _need(dY, "dY", torch.bfloat16)
+    if dY.dim() != 2 or dY.shape[1] != qw.n:
+        raise ValueError(f"dY must be [m, {qw.n}]")
+    m = dY.shape[0]
+    if out is None:
+        out = torch.empty((m, qw.k), dtype=torch.bfloat16, device=dY.device)
+    _need(out, "out", torch.bfloat16, (m, qw.k))
+    q = qw.qtensor()
+    check(lib.lbq_linear_bwd_dx(ctypes.byref(qw.desc), ctypes.byref(q), dY.data_ptr(), m,
+                                out.data_ptr(), _stream(dY.device)), "lbq_linear_bwd_dx")
+    return out
+
+
+def lbq_lora_fwd(X: torch.Tensor, qw: QuantizedWeight, A: torch.Tensor, B: torch.Tensor,
+                 sigma: float, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X . deq(W)^T + sigma (X A^T) B^T (see ``lbq_lora_fwd`` in lbq.h)."""
+    _need(X, "X", torch.bfloat16)
+    _need(A, "A", torch.bfloat16)
+    _need(B, "B", torch.bfloat16)
+    m = X.shape[0]
+    r = A.shape[0]
+    if A.shape[1] != qw.k or B.shape != (qw.n, r):
+        raise ValueError("A must be [r, k] and B [n, r]")
+    if out is None:
+        if qw.out_rows is not None:
+            raise ValueError("out must be given when out_rows is set")
+        out = torch.empty((m, qw.n), dtype=torch.bfloat16, device=X.device)
+    nbytes = lbq_lora_workspace_bytes(qw, m, r)
+    if workspace is None:
+        workspace = _ws(nbytes, X.device)
+    q = qw.qtensor()
+    check(lib.lbq_lora_fwd(ctypes.byref(qw.desc), ctypes.byref(q), X.data_ptr(), m, A.data_ptr(),
+                           B.data_ptr(), r, float(sigma), out.data_ptr(), out.stride(0),
+                           _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                           _stream(X.device)), "lbq_lora_fwd")
+    return out

@@ -1,0 +1,290 @@
+// Quantize / pack and standalone dequantize kernels for gfx950.
+//
+// Bit-exactness: every fp32 step below is one IEEE binary32 operation rounded
+// to nearest-even.  Contraction into FMA is switched off for this file (here
+// and with -ffp-contract=off on its compile line), division is the correctly
+// rounded v_div_scale/fmas/fixup sequence, and rne() is v_rndne_f32.
+//
+// Sources:
+//   MinMax: GreenBit.AI, "只需单卡RTX 3090，低比特量化训练就能实现LLaMA-3 8B全参微调",
+//           section 模型量化 -- group-wise MinMax, INT4 g128 / INT2 g64, RTN.
+//   NF4 + double quantization: "QLoRA技术在量化微调中的应用", section
+//           QLoRA技术原理 -- NF4 for normal weights; the absmax constants are
+//           quantized a second time.
+//   Packing: bitsandbytes FSDP-QLoRA guide, section 量化数据的存储 -- two codes
+//           per byte, the even-indexed code in the high nibble.
+#pragma clang fp contract(off)
+
+#include "lbq_device.h"
+
+namespace lbq {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ void load8(const float* __restrict__ p, float w[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+  w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+}
+
+// ---------------------------------------------------------------------------
+// MinMax.  One lane owns a chunk of 8 consecutive weights; the G/8 lanes of a
+// group are adjacent in the wave and combine their min/max with xor shuffles.
+// Chunks never straddle groups or rows (k % G == 0, G % 8 == 0).
+// ---------------------------------------------------------------------------
+template <int BITS, int G>
+__global__ __launch_bounds__(kThreads) void k_quant_minmax(const float* __restrict__ W,
+                                                          uint8_t* __restrict__ packed,
+                                                          float* __restrict__ scales,
+                                                          uint8_t* __restrict__ zeros,
+                                                          int64_t nchunks) {
+  constexpr int QMAX = (1 << BITS) - 1;
+  constexpr int LPG = G / 8;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  // Whole waves iterate together so the shuffles below see converged waves.
+  const int64_t bound = (nchunks + 63) & ~int64_t(63);
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < bound; c += stride) {
+    const bool valid = c < nchunks;
+    float w[8];
+    if (valid) {
+      load8(W + 8 * c, w);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = 0.f;
+    }
+    float mn = w[0], mx = w[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+      mn = fminf(mn, w[i]);
+      mx = fmaxf(mx, w[i]);
+    }
+#pragma unroll
+    for (int o = 1; o < LPG; o <<= 1) {
+      mn = fminf(mn, __shfl_xor(mn, o));
+      mx = fmaxf(mx, __shfl_xor(mx, o));
+    }
+    const float lo = fminf(0.f, mn);
+    const float hi = fmaxf(0.f, mx);
+    float s = (hi - lo) / (float)QMAX;
+    if (s == 0.f) s = 1.f;
+    int z = (int)__builtin_rintf(-lo / s);
+    z = z < 0 ? 0 : (z > QMAX ? QMAX : z);
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int q = (int)__builtin_rintf(w[i] / s) + z;
+      q = q < 0 ? 0 : (q > QMAX ? QMAX : q);
+      if constexpr (BITS == 4) {
+        word |= (uint32_t)q << (8 * (i >> 1) + ((i & 1) ? 0 : 4));
+      } else {
+        word |= (uint32_t)q << (8 * (i >> 2) + 6 - 2 * (i & 3));
+      }
+    }
+    if (valid) {
+      if constexpr (BITS == 4) {
+        reinterpret_cast<uint32_t*>(packed)[c] = word;
+      } else {
+        reinterpret_cast<uint16_t*>(packed)[c] = (uint16_t)word;
+      }
+      if ((c % LPG) == 0) {
+        scales[c / LPG] = s;
+        zeros[c / LPG] = (uint8_t)z;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// NF4.  A workgroup owns a run of 256 consecutive 64-blocks (16384 weights),
+// which is exactly one double-quantization block: the 256 absmax values stay
+// in LDS and the second-level int8 codes are produced in the same launch.
+// Eight lanes share a 64-block (8 weights each).
+// ---------------------------------------------------------------------------
+template <bool DQ>
+__global__ __launch_bounds__(kThreads) void k_quant_nf4(const float* __restrict__ W,
+                                                       uint8_t* __restrict__ packed,
+                                                       float* __restrict__ absmax,
+                                                       int8_t* __restrict__ absmax_q,
+                                                       float* __restrict__ absmax_scale,
+                                                       int64_t nblocks, Nf4Table tab) {
+  __shared__ float mids[16];
+  __shared__ float am[256];
+  __shared__ float red[kThreads / 64];
+  const int t = threadIdx.x;
+  if (t < 15) mids[t] = (tab.c[t] + tab.c[t + 1]) * 0.5f;
+  __syncthreads();
+
+  const int64_t b0 = (int64_t)blockIdx.x * 256;
+  const int nb_here = (int)((nblocks - b0) < 256 ? (nblocks - b0) : 256);
+
+#pragma unroll 2
+  for (int it = 0; it < 8; ++it) {
+    const int lb = it * 32 + (t >> 3);
+    const bool valid = lb < nb_here;
+    const int64_t c = (b0 + lb) * 8 + (t & 7);
+    float w[8];
+    if (valid) {
+      load8(W + 8 * c, w);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = 0.f;
+    }
+    float a = fabsf(w[0]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) a = fmaxf(a, fabsf(w[i]));
+    a = fmaxf(a, __shfl_xor(a, 1));
+    a = fmaxf(a, __shfl_xor(a, 2));
+    a = fmaxf(a, __shfl_xor(a, 4));
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int code = 7;
+      if (a != 0.f) {
+        const float x = w[i] / a;
+        // number of midpoints strictly below x (binary search, 4 probes)
+        code = (x > mids[7]) ? 8 : 0;
+        code += (x > mids[code + 3]) ? 4 : 0;
+        code += (x > mids[code + 1]) ? 2 : 0;
+        code += (x > mids[code]) ? 1 : 0;
+      }
+      word |= (uint32_t)code << (8 * (i >> 1) + ((i & 1) ? 0 : 4));
+    }
+    if (valid) {
+      reinterpret_cast<uint32_t*>(packed)[c] = word;
+      if ((t & 7) == 0) {
+        if constexpr (DQ) {
+          am[lb] = a;
+        } else {
+          absmax[b0 + lb] = a;
+        }
+      }
+    }
+  }
+
+  if constexpr (DQ) {
+    __syncthreads();
+    const float v = t < nb_here ? am[t] : 0.f;  // absmax >= 0: 0 is neutral
+    float m = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    m = red[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, red[i]);
+    const float c2 = m / 127.f;
+    if (t < nb_here) {
+      int q2 = 0;
+      if (c2 != 0.f) {
+        q2 = (int)__builtin_rintf(v / c2);
+        q2 = q2 < 0 ? 0 : (q2 > 127 ? 127 : q2);
+      }
+      absmax_q[b0 + t] = (int8_t)q2;
+    }
+    if (t == 0) absmax_scale[blockIdx.x] = c2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize to bf16: one lane per chunk of 8 codes, one 16-byte store.
+// ---------------------------------------------------------------------------
+template <int KIND>
+__global__ __launch_bounds__(kThreads) void k_dequant(WView w, uint16_t* __restrict__ out,
+                                                     int64_t nchunks, Nf4Table tab) {
+  using T = WKindTraits<KIND>;
+  __shared__ float cb[16];
+  if constexpr (T::fmt == FMT_NF4) {
+    if (threadIdx.x < 16) cb[threadIdx.x] = tab.c[threadIdx.x];
+    __syncthreads();
+  }
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < nchunks; c += stride) {
+    uint32_t word;
+    if constexpr (T::bits == 4) {
+      word = reinterpret_cast<const uint32_t*>(w.packed)[c];
+    } else {
+      word = reinterpret_cast<const uint16_t*>(w.packed)[c];
+    }
+    float v[8];
+    if constexpr (T::fmt == FMT_MINMAX) {
+      const int64_t g = c / (T::group / 8);
+      const float s = w.scales[g];
+      const int z = w.zeros[g];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (float)(code_of<T::bits>(word, i) - z) * s;
+    } else {
+      const float a = nf4_block_scale<T::dq>(w, c >> 3);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = cb[code_of<4>(word, i)] * a;
+    }
+    uint4 o;
+    o.x = pack_bf16x2(v[0], v[1]);
+    o.y = pack_bf16x2(v[2], v[3]);
+    o.z = pack_bf16x2(v[4], v[5]);
+    o.w = pack_bf16x2(v[6], v[7]);
+    reinterpret_cast<uint4*>(out)[c] = o;
+  }
+}
+
+int grid_for(int64_t nchunks) {
+  int64_t g = (nchunks + kThreads - 1) / kThreads;
+  if (g > 16384) g = 16384;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+template <int KIND>
+struct DequantLauncher {
+  static hipError_t run(const WView& w, uint16_t* out, const Nf4Table& tab, hipStream_t s) {
+    const int64_t nchunks = w.n * w.k / 8;
+    hipLaunchKernelGGL((k_dequant<KIND>), dim3(grid_for(nchunks)), dim3(kThreads), 0, s, w, out,
+                       nchunks, tab);
+    return hipGetLastError();
+  }
+};
+
+}  // namespace
+
+hipError_t launch_quant_minmax(int bits, int group, const float* W, uint8_t* packed,
+                               float* scales, uint8_t* zeros, int64_t n, int64_t k,
+                               hipStream_t s) {
+  const int64_t nchunks = n * k / 8;
+  const dim3 grid(grid_for(nchunks)), block(kThreads);
+  if (bits == 4 && group == 128) {
+    hipLaunchKernelGGL((k_quant_minmax<4, 128>), grid, block, 0, s, W, packed, scales, zeros, nchunks);
+  } else if (bits == 4 && group == 64) {
+    hipLaunchKernelGGL((k_quant_minmax<4, 64>), grid, block, 0, s, W, packed, scales, zeros, nchunks);
+  } else if (bits == 2 && group == 64) {
+    hipLaunchKernelGGL((k_quant_minmax<2, 64>), grid, block, 0, s, W, packed, scales, zeros, nchunks);
+  } else if (bits == 2 && group == 128) {
+    hipLaunchKernelGGL((k_quant_minmax<2, 128>), grid, block, 0, s, W, packed, scales, zeros, nchunks);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_nf4(bool dq, const float* W, uint8_t* packed, float* absmax,
+                            int8_t* absmax_q, float* absmax_scale, int64_t n, int64_t k,
+                            const Nf4Table& tab, hipStream_t s) {
+  const int64_t nblocks = n * k / 64;
+  const dim3 grid((unsigned)((nblocks + 255) / 256)), block(kThreads);
+  if (dq) {
+    hipLaunchKernelGGL((k_quant_nf4<true>), grid, block, 0, s, W, packed, absmax, absmax_q,
+                       absmax_scale, nblocks, tab);
+  } else {
+    hipLaunchKernelGGL((k_quant_nf4<false>), grid, block, 0, s, W, packed, absmax, absmax_q,
+                       absmax_scale, nblocks, tab);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(WKind kind, const WView& w, uint16_t* out, const Nf4Table& tab,
+                          hipStream_t s) {
+  return dispatch_kind<DequantLauncher>(kind, w, out, tab, s);
+}
+
+}  // namespace lbq

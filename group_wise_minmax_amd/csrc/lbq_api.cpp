@@ -1,0 +1,315 @@
+// C-ABI entry points of liblbq (declared in include/lbq.h): host-side
+// validation, buffer layout, NF4 codebook and kernel dispatch.  Every argument
+// check runs before anything is enqueued; nothing here synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "lbq.h"
+#include "lbq_internal.h"
+
+namespace {
+
+thread_local std::string g_detail;
+
+lbq_status fail(lbq_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+lbq_status fail(lbq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return s;
+}
+
+lbq_status ok() {
+  g_detail.clear();
+  return LBQ_OK;
+}
+
+lbq_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(LBQ_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// ---- NF4 codebook ----------------------------------------------------------
+// Standard normal quantile by bisection on Phi(x) = erfc(-x/sqrt 2)/2 in fp64,
+// run until the bracket cannot shrink further.
+double normal_quantile(double p) {
+  double lo = -40.0, hi = 40.0;
+  for (int it = 0; it < 2000; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (mid == lo || mid == hi) break;
+    const double cdf = 0.5 * std::erfc(-mid / std::sqrt(2.0));
+    if (cdf < p) {
+      lo = mid;
+    } else {
+      hi = mid;
+    }
+  }
+  return 0.5 * (lo + hi);
+}
+
+// NF4 levels ("QLoRA技术在量化微调中的应用", section QLoRA技术原理: a 4-bit
+// NormalFloat type for normally distributed weights).  Eight positive levels
+// are the normal quantiles of 9 evenly spaced probabilities from delta down to
+// 1/2 without the last; seven negative levels likewise from 8 points; plus an
+// exact zero; all divided by the quantile at delta so the extremes are +-1.
+lbq::Nf4Table make_nf4_table() {
+  const double delta = 1.0 - 0.5 * (1.0 / 30.0 + 1.0 / 32.0);
+  std::vector<double> v;
+  for (int i = 0; i < 8; ++i) v.push_back(normal_quantile(delta + (0.5 - delta) * i / 8.0));
+  for (int i = 0; i < 7; ++i) v.push_back(-normal_quantile(delta + (0.5 - delta) * i / 7.0));
+  v.push_back(0.0);
+  std::sort(v.begin(), v.end());
+  const double top = normal_quantile(delta);
+  lbq::Nf4Table t;
+  for (int i = 0; i < 16; ++i) t.c[i] = (float)(v[i] / top);
+  return t;
+}
+
+const lbq::Nf4Table& nf4_table() {
+  static const lbq::Nf4Table t = make_nf4_table();
+  return t;
+}
+
+// ---- validation ------------------------------------------------------------
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+lbq_status check_desc(const lbq_desc* d) {
+  if (d == nullptr) return fail(LBQ_E_NULL, "desc is NULL");
+  if (d->reserved != 0) return fail(LBQ_E_FORMAT, "desc.reserved must be 0");
+  if (d->format == LBQ_MINMAX) {
+    if (d->bits != 4 && d->bits != 2) return fail(LBQ_E_FORMAT, "MINMAX bits must be 4 or 2 (got %d)", d->bits);
+    if (d->group != 128 && d->group != 64) return fail(LBQ_E_FORMAT, "MINMAX group must be 64 or 128 (got %d)", d->group);
+    if (d->double_quant != 0 || d->dq_block != 0) return fail(LBQ_E_FORMAT, "MINMAX takes no double quantization");
+  } else if (d->format == LBQ_NF4) {
+    if (d->bits != 4) return fail(LBQ_E_FORMAT, "NF4 bits must be 4 (got %d)", d->bits);
+    if (d->group != 64) return fail(LBQ_E_FORMAT, "NF4 absmax block must be 64 (got %d)", d->group);
+    if (d->double_quant != 0 && d->double_quant != 1) return fail(LBQ_E_FORMAT, "double_quant must be 0 or 1");
+    if (d->dq_block != (d->double_quant ? 256 : 0)) return fail(LBQ_E_FORMAT, "dq_block must be 256 with double_quant=1 and 0 otherwise");
+  } else {
+    return fail(LBQ_E_FORMAT, "unknown format %d (MINMAX=0, NF4=1)", d->format);
+  }
+  if (d->n < 1 || d->n > (int64_t(1) << 31) - 1) return fail(LBQ_E_SHAPE, "n must be in [1, 2^31) (got %lld)", (long long)d->n);
+  if (d->k < 64 || d->k > (int64_t(1) << 24)) return fail(LBQ_E_SHAPE, "k must be in [64, 2^24] (got %lld)", (long long)d->k);
+  if (d->k % 64 != 0 || d->k % d->group != 0) return fail(LBQ_E_SHAPE, "k (%lld) must be a multiple of 64 and of the group", (long long)d->k);
+  if (d->n * d->k > (int64_t(1) << 40)) return fail(LBQ_E_SHAPE, "n*k too large");
+  return LBQ_OK;
+}
+
+lbq::WKind kind_of(const lbq_desc* d) {
+  if (d->format == LBQ_NF4) return d->double_quant ? lbq::WK_NF4DQ : lbq::WK_NF4;
+  if (d->bits == 4) return d->group == 128 ? lbq::WK_I4G128 : lbq::WK_I4G64;
+  return d->group == 64 ? lbq::WK_I2G64 : lbq::WK_I2G128;
+}
+
+void sizes_of(const lbq_desc* d, lbq_sizes* s) {
+  std::memset(s, 0, sizeof *s);
+  s->packed = (size_t)(d->n * d->k * d->bits / 8);
+  if (d->format == LBQ_MINMAX) {
+    s->scales = (size_t)(d->n * (d->k / d->group)) * sizeof(float);
+    s->zeros = (size_t)(d->n * (d->k / d->group));
+  } else {
+    const int64_t nb = d->n * d->k / 64;
+    if (d->double_quant) {
+      s->absmax_q = (size_t)nb;
+      s->absmax_scale = (size_t)((nb + 255) / 256) * sizeof(float);
+    } else {
+      s->absmax = (size_t)nb * sizeof(float);
+    }
+  }
+}
+
+// Pointers of `q` that the format reads (or writes, for quantize).
+lbq_status check_qtensor(const lbq_desc* d, const lbq_qtensor* q) {
+  if (q == nullptr) return fail(LBQ_E_NULL, "qtensor is NULL");
+  if (q->packed == nullptr) return fail(LBQ_E_NULL, "qtensor.packed is NULL");
+  if (!aligned(q->packed, 16)) return fail(LBQ_E_ALIGN, "qtensor.packed must be 16-byte aligned");
+  if (d->format == LBQ_MINMAX) {
+    if (q->scales == nullptr || q->zeros == nullptr) return fail(LBQ_E_NULL, "MINMAX needs scales and zeros");
+    if (!aligned(q->scales, 4)) return fail(LBQ_E_ALIGN, "scales must be 4-byte aligned");
+  } else if (d->double_quant) {
+    if (q->absmax_q == nullptr || q->absmax_scale == nullptr) return fail(LBQ_E_NULL, "NF4 with double quant needs absmax_q and absmax_scale");
+    if (!aligned(q->absmax_scale, 4)) return fail(LBQ_E_ALIGN, "absmax_scale must be 4-byte aligned");
+  } else {
+    if (q->absmax == nullptr) return fail(LBQ_E_NULL, "NF4 needs absmax");
+    if (!aligned(q->absmax, 4)) return fail(LBQ_E_ALIGN, "absmax must be 4-byte aligned");
+  }
+  return LBQ_OK;
+}
+
+lbq::WView view_of(const lbq_desc* d, const lbq_qtensor* q) {
+  lbq::WView w;
+  w.packed = static_cast<const uint8_t*>(q->packed);
+  w.scales = q->scales;
+  w.zeros = q->zeros;
+  w.absmax = q->absmax;
+  w.absmax_q = q->absmax_q;
+  w.absmax_scale = q->absmax_scale;
+  w.n = d->n;
+  w.k = d->k;
+  return w;
+}
+
+lbq_status check_fwd_common(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X,
+                            int64_t m, uint16_t* Y, int64_t ldy) {
+  lbq_status st = check_desc(desc);
+  if (st != LBQ_OK) return st;
+  if ((st = check_qtensor(desc, q)) != LBQ_OK) return st;
+  if (m < 0 || m > (int64_t(1) << 31) - 1) return fail(LBQ_E_SHAPE, "m must be in [0, 2^31) (got %lld)", (long long)m);
+  if (m == 0) return LBQ_OK;
+  if (X == nullptr || Y == nullptr) return fail(LBQ_E_NULL, "X and Y must be non-NULL");
+  if (!aligned(X, 16)) return fail(LBQ_E_ALIGN, "X must be 16-byte aligned");
+  if (!aligned(Y, 2)) return fail(LBQ_E_ALIGN, "Y must be 2-byte aligned");
+  if (q->out_rows == nullptr && ldy < desc->n) return fail(LBQ_E_SHAPE, "ldy (%lld) < n (%lld)", (long long)ldy, (long long)desc->n);
+  if (ldy < 1) return fail(LBQ_E_SHAPE, "ldy must be >= 1");
+  return LBQ_OK;
+}
+
+int32_t round_rank(int32_t r) { return (r + 31) / 32 * 32; }
+
+}  // namespace
+
+extern "C" {
+
+lbq_status lbq_layout(const lbq_desc* desc, lbq_sizes* out) {
+  lbq_status st = check_desc(desc);
+  if (st != LBQ_OK) return st;
+  if (out == nullptr) return fail(LBQ_E_NULL, "out is NULL");
+  sizes_of(desc, out);
+  return ok();
+}
+
+lbq_status lbq_quantize(const lbq_desc* desc, const float* W, const lbq_qtensor* q, void* stream) {
+  lbq_status st = check_desc(desc);
+  if (st != LBQ_OK) return st;
+  if ((st = check_qtensor(desc, q)) != LBQ_OK) return st;
+  if (W == nullptr) return fail(LBQ_E_NULL, "W is NULL");
+  if (!aligned(W, 16)) return fail(LBQ_E_ALIGN, "W must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (desc->format == LBQ_MINMAX) {
+    e = lbq::launch_quant_minmax(desc->bits, desc->group, W, static_cast<uint8_t*>(q->packed),
+                                 q->scales, q->zeros, desc->n, desc->k, s);
+  } else {
+    e = lbq::launch_quant_nf4(desc->double_quant != 0, W, static_cast<uint8_t*>(q->packed),
+                              q->absmax, q->absmax_q, q->absmax_scale, desc->n, desc->k,
+                              nf4_table(), s);
+  }
+  return hip_status(e, "lbq_quantize");
+}
+
+lbq_status lbq_dequant(const lbq_desc* desc, const lbq_qtensor* q, uint16_t* W_bf16, void* stream) {
+  lbq_status st = check_desc(desc);
+  if (st != LBQ_OK) return st;
+  if ((st = check_qtensor(desc, q)) != LBQ_OK) return st;
+  if (W_bf16 == nullptr) return fail(LBQ_E_NULL, "W_bf16 is NULL");
+  if (!aligned(W_bf16, 16)) return fail(LBQ_E_ALIGN, "W_bf16 must be 16-byte aligned");
+  return hip_status(lbq::launch_dequant(kind_of(desc), view_of(desc, q), W_bf16, nf4_table(),
+                                        static_cast<hipStream_t>(stream)),
+                    "lbq_dequant");
+}
+
+size_t lbq_linear_workspace_bytes(const lbq_desc* desc, int64_t m) {
+  (void)desc;
+  (void)m;
+  return 0;
+}
+
+lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X,
+                          int64_t m, uint16_t* Y, int64_t ldy, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  lbq_status st = check_fwd_common(desc, q, X, m, Y, ldy);
+  if (st != LBQ_OK || m == 0) return st == LBQ_OK ? ok() : st;
+  const lbq::LoraEpi none{nullptr, nullptr, 0, 0};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const lbq::WView w = view_of(desc, q);
+  hipError_t e = (m <= lbq::kGemvMaxM)
+                     ? lbq::launch_gemv(kind_of(desc), w, X, m, Y, ldy, q->out_rows, none, nf4_table(), s)
+                     : lbq::launch_gemm_fwd(kind_of(desc), w, X, m, Y, ldy, q->out_rows, none, nf4_table(), s);
+  return hip_status(e, "lbq_linear_fwd");
+}
+
+lbq_status lbq_linear_bwd_dx(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* dY,
+                             int64_t m, uint16_t* dX, void* stream) {
+  lbq_status st = check_desc(desc);
+  if (st != LBQ_OK) return st;
+  if ((st = check_qtensor(desc, q)) != LBQ_OK) return st;
+  if (q->out_rows != nullptr) return fail(LBQ_E_UNSUPPORTED, "lbq_linear_bwd_dx does not take out_rows");
+  if (m < 0 || m > (int64_t(1) << 31) - 1) return fail(LBQ_E_SHAPE, "m must be in [0, 2^31)");
+  if (m == 0) return ok();
+  if (dY == nullptr || dX == nullptr) return fail(LBQ_E_NULL, "dY and dX must be non-NULL");
+  if (!aligned(dY, 16) || !aligned(dX, 16)) return fail(LBQ_E_ALIGN, "dY and dX must be 16-byte aligned");
+  if (desc->n % 8 != 0) return fail(LBQ_E_SHAPE, "lbq_linear_bwd_dx needs n %% 8 == 0 (got %lld)", (long long)desc->n);
+  return hip_status(lbq::launch_bwd_dx(kind_of(desc), view_of(desc, q), dY, m, dX, nf4_table(),
+                                       static_cast<hipStream_t>(stream)),
+                    "lbq_linear_bwd_dx");
+}
+
+size_t lbq_lora_workspace_bytes(const lbq_desc* desc, int64_t m, int32_t r) {
+  (void)desc;
+  if (m <= 0 || r < 1) return 0;
+  return (size_t)m * (size_t)round_rank(r) * sizeof(uint16_t);
+}
+
+lbq_status lbq_lora_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X, int64_t m,
+                        const uint16_t* A, const uint16_t* B, int32_t r, float sigma, uint16_t* Y,
+                        int64_t ldy, void* workspace, size_t ws_bytes, void* stream) {
+  lbq_status st = check_fwd_common(desc, q, X, m, Y, ldy);
+  if (st != LBQ_OK) return st;
+  if (r < 1 || r > 64) return fail(LBQ_E_SHAPE, "LoRA rank r must be in [1, 64] (got %d)", r);
+  if (m == 0) return ok();
+  if (A == nullptr || B == nullptr) return fail(LBQ_E_NULL, "LoRA A and B must be non-NULL");
+  if (!aligned(A, 16)) return fail(LBQ_E_ALIGN, "LoRA A must be 16-byte aligned");
+  if (!aligned(B, 2)) return fail(LBQ_E_ALIGN, "LoRA B must be 2-byte aligned");
+  if (!std::isfinite(sigma)) return fail(LBQ_E_SHAPE, "sigma must be finite");
+  const size_t need = lbq_lora_workspace_bytes(desc, m, r);
+  if (workspace == nullptr || ws_bytes < need) return fail(LBQ_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  if (!aligned(workspace, 16)) return fail(LBQ_E_ALIGN, "workspace must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t rp = round_rank(r);
+  uint16_t* T = static_cast<uint16_t*>(workspace);
+  hipError_t e = lbq::launch_lora_t(X, m, desc->k, A, r, rp, sigma, T, s);
+  if (e != hipSuccess) return hip_status(e, "lbq_lora_fwd (adapter product)");
+  const lbq::LoraEpi lora{T, B, r, rp};
+  const lbq::WView w = view_of(desc, q);
+  e = (m <= lbq::kGemvMaxM)
+          ? lbq::launch_gemv(kind_of(desc), w, X, m, Y, ldy, q->out_rows, lora, nf4_table(), s)
+          : lbq::launch_gemm_fwd(kind_of(desc), w, X, m, Y, ldy, q->out_rows, lora, nf4_table(), s);
+  return hip_status(e, "lbq_lora_fwd");
+}
+
+void lbq_nf4_codebook(float out[16]) {
+  const lbq::Nf4Table& t = nf4_table();
+  for (int i = 0; i < 16; ++i) out[i] = t.c[i];
+}
+
+const char* lbq_strerror(lbq_status s) {
+  switch (s) {
+    case LBQ_OK: return "ok";
+    case LBQ_E_NULL: return "required pointer is NULL";
+    case LBQ_E_SHAPE: return "shape out of range or inconsistent";
+    case LBQ_E_FORMAT: return "unknown or unsupported quantization format";
+    case LBQ_E_ALIGN: return "pointer or leading dimension misaligned";
+    case LBQ_E_WORKSPACE: return "workspace missing or too small";
+    case LBQ_E_UNSUPPORTED: return "request not supported by this build";
+    case LBQ_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* lbq_last_error_detail(void) { return g_detail.c_str(); }
+
+const char* lbq_version(void) { return "lbq 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Device-side helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lbq_internal.h"
+
+namespace lbq {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// fp32 -> bf16 bits, round to nearest, ties to even (NaN is out of contract).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Two fp32 -> one dword of two bf16 (lo in bits 15..0).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// acc + a.lo*b.lo + a.hi*b.hi with fp32 accumulation (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// v_perm_b32: bytes of {hi:lo} selected by `sel` (0..3 -> lo, 4..7 -> hi).
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+// (lo16(a), lo16(b)) and (hi16(a), hi16(b)) as bf16 pairs.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x07060302u); }
+
+// D(16x16, f32) += A(16x32) * B(32x16), bf16 operands.  Lane l holds
+// A[l%16][kslot(l/16, 0..7)], B[kslot(l/16, 0..7)][l%16] and
+// D[4*(l/16) + i][l%16], i = 0..3.
+__device__ __forceinline__ f32x4_t mfma16x16x32(const u32x4_t& a, const u32x4_t& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Integer code of element i (0..7) from the packed bytes of a chunk of 8
+// consecutive codes: 4-bit chunks are one dword (4 bytes), 2-bit chunks a
+// 16-bit word.  Even element -> high nibble (4-bit); first element -> bits
+// 7..6 (2-bit).
+template <int BITS>
+__device__ __forceinline__ int code_of(uint32_t word, int i) {
+  if constexpr (BITS == 4) {
+    return (word >> (8 * (i >> 1) + ((i & 1) ? 0 : 4))) & 0xF;
+  } else {
+    return (word >> (8 * (i >> 2) + 6 - 2 * (i & 3))) & 0x3;
+  }
+}
+
+template <int K> struct WKindTraits;
+template <> struct WKindTraits<WK_I4G128> { static constexpr int fmt = FMT_MINMAX, bits = 4, group = 128; static constexpr bool dq = false; };
+template <> struct WKindTraits<WK_I4G64>  { static constexpr int fmt = FMT_MINMAX, bits = 4, group = 64;  static constexpr bool dq = false; };
+template <> struct WKindTraits<WK_I2G64>  { static constexpr int fmt = FMT_MINMAX, bits = 2, group = 64;  static constexpr bool dq = false; };
+template <> struct WKindTraits<WK_I2G128> { static constexpr int fmt = FMT_MINMAX, bits = 2, group = 128; static constexpr bool dq = false; };
+template <> struct WKindTraits<WK_NF4>    { static constexpr int fmt = FMT_NF4,    bits = 4, group = 64;  static constexpr bool dq = false; };
+template <> struct WKindTraits<WK_NF4DQ>  { static constexpr int fmt = FMT_NF4,    bits = 4, group = 64;  static constexpr bool dq = true; };
+
+// Block absmax of NF4 block `blk` (fp32, or fl(q2 * c2) under double quant).
+template <bool DQ>
+__device__ __forceinline__ float nf4_block_scale(const WView& w, int64_t blk) {
+  if constexpr (DQ) {
+    return (float)w.absmax_q[blk] * w.absmax_scale[blk >> 8];
+  } else {
+    return w.absmax[blk];
+  }
+}
+
+// Dispatch a functor templated on the weight kind.
+template <template <int> class F, typename... Args>
+hipError_t dispatch_kind(WKind kind, Args&&... args) {
+  switch (kind) {
+    case WK_I4G128: return F<WK_I4G128>::run(args...);
+    case WK_I4G64: return F<WK_I4G64>::run(args...);
+    case WK_I2G64: return F<WK_I2G64>::run(args...);
+    case WK_I2G128: return F<WK_I2G128>::run(args...);
+    case WK_NF4: return F<WK_NF4>::run(args...);
+    case WK_NF4DQ: return F<WK_NF4DQ>::run(args...);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lbq

@@ -1,0 +1,70 @@
+// Internal interface between the C-ABI layer (lbq_api.cpp) and the gfx950
+// kernels.  Not installed; the public interface is include/lbq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lbq {
+
+enum Fmt : int { FMT_MINMAX = 0, FMT_NF4 = 1 };
+
+// One quantized weight as the kernels see it (device pointers + shape).
+struct WView {
+  const uint8_t* packed;
+  const float* scales;
+  const uint8_t* zeros;
+  const float* absmax;
+  const int8_t* absmax_q;
+  const float* absmax_scale;
+  int64_t n, k;
+};
+
+// The 16 NF4 levels, passed by value to every kernel that needs them.
+struct Nf4Table {
+  float c[16];
+};
+
+// LoRA epilogue operands: T = bf16(sigma * X A^T) [m][rp] (rp = r rounded up
+// to a multiple of 32, zero padded) and B [n][r] bf16.  t == nullptr: none.
+struct LoraEpi {
+  const uint16_t* t;
+  const uint16_t* b;
+  int32_t r;
+  int32_t rp;
+};
+
+// Supported weight encodings (format, bits, group, double quant).
+enum WKind : int {
+  WK_I4G128 = 0,  // MinMax 4-bit, group 128
+  WK_I4G64 = 1,   // MinMax 4-bit, group 64
+  WK_I2G64 = 2,   // MinMax 2-bit, group 64
+  WK_I2G128 = 3,  // MinMax 2-bit, group 128
+  WK_NF4 = 4,     // NF4, block 64, fp32 absmax
+  WK_NF4DQ = 5,   // NF4, block 64, int8 absmax + fp32 scale per 256 blocks
+};
+
+// ---- launchers (each returns hipGetLastError() after the launch) ----------
+hipError_t launch_quant_minmax(int bits, int group, const float* W, uint8_t* packed,
+                               float* scales, uint8_t* zeros, int64_t n, int64_t k,
+                               hipStream_t s);
+hipError_t launch_quant_nf4(bool dq, const float* W, uint8_t* packed, float* absmax,
+                            int8_t* absmax_q, float* absmax_scale, int64_t n, int64_t k,
+                            const Nf4Table& tab, hipStream_t s);
+hipError_t launch_dequant(WKind kind, const WView& w, uint16_t* out, const Nf4Table& tab,
+                          hipStream_t s);
+hipError_t launch_gemv(WKind kind, const WView& w, const uint16_t* X, int64_t m,
+                       uint16_t* Y, int64_t ldy, const int32_t* out_rows,
+                       const LoraEpi& lora, const Nf4Table& tab, hipStream_t s);
+hipError_t launch_gemm_fwd(WKind kind, const WView& w, const uint16_t* X, int64_t m,
+                           uint16_t* Y, int64_t ldy, const int32_t* out_rows,
+                           const LoraEpi& lora, const Nf4Table& tab, hipStream_t s);
+hipError_t launch_bwd_dx(WKind kind, const WView& w, const uint16_t* dY, int64_t m,
+                         uint16_t* dX, const Nf4Table& tab, hipStream_t s);
+hipError_t launch_lora_t(const uint16_t* X, int64_t m, int64_t k, const uint16_t* A,
+                         int32_t r, int32_t rp, float sigma, uint16_t* T, hipStream_t s);
+
+// Largest m served by the wavefront-reduction GEMV; larger m use MFMA tiles.
+constexpr int64_t kGemvMaxM = 4;
+
+}  // namespace lbq

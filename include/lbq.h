@@ -1,0 +1,207 @@
+/*
+ * lbq -- group-wise low-bit weight quantization and the fused
+ * dequantize-then-matmul of a frozen low-bit linear layer, for AMD MI355X
+ * (gfx950).  Plain C ABI: pointers and sizes only, no framework types.
+ *
+ * Sources (cited by page title and section):
+ *   [GB]  GreenBit.AI, "只需单卡RTX 3090，低比特量化训练就能实现LLaMA-3 8B全参微调",
+ *         section 模型量化: classic group-wise MinMax quantizer, INT4 with
+ *         group size 128 and INT2 with group size 64 as the base
+ *         representations (chosen per layer or per channel), round-to-nearest.
+ *   [BNB] bitsandbytes FSDP-QLoRA guide (walk-through of docs/source/fsdp_qlora.md),
+ *         section 量化数据的存储: two 4-bit codes per byte, even-indexed code in
+ *         the high nibble; packed bytes may be viewed as any dtype of equal
+ *         width without changing them; section 通过BitsAndBytesConfig配置: the
+ *         kernel unpacks and dequantizes weights to the compute dtype (bf16)
+ *         before the matmul; step 2's parameter table: quant type nf4 or fp4
+ *         (type-checked), double quantization of the absmax statistics;
+ *         step 4: LoRA adapters (lora_alpha, r).
+ *   [QL]  "QLoRA技术在量化微调中的应用", section QLoRA技术原理: NF4 for normally
+ *         distributed weights; double quantization of the quantization
+ *         constants; gradients are backpropagated through the frozen 4-bit
+ *         model into low-rank adapters.
+ *
+ * Conventions shared by every entry point
+ *   Ownership:  every buffer is device memory owned by the caller; the library
+ *               never allocates or frees device memory and keeps no device
+ *               state between calls.
+ *   Execution:  every call that touches the device only enqueues kernels on
+ *               `stream` (a hipStream_t passed as void*, NULL = the default
+ *               stream) and returns without synchronizing.
+ *   Errors:     argument, shape, format and alignment errors are detected on
+ *               the host before anything is enqueued and returned as a status;
+ *               a failed launch returns LBQ_E_HIP.  lbq_last_error_detail()
+ *               gives a human-readable message for the last failure on the
+ *               calling thread.  Inputs containing NaN or Inf are outside the
+ *               contract.
+ *   Layouts:    row-major.  W is n x k (out x in, like a linear layer's
+ *               weight); X is m x k; Y is m x ldy; dY is m x n; dX is m x k.
+ *               bf16 tensors are passed as uint16_t bit patterns.
+ *   Alignment:  `packed`, W, X, dY, dX, LoRA A and the LoRA workspace must
+ *               be 16-byte aligned; Y, LoRA B 2-byte aligned; scales, absmax
+ *               and absmax_scale 4-byte aligned.
+ */
+#ifndef LBQ_H
+#define LBQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LBQ_OK = 0,
+  LBQ_E_NULL = 1,        /* a required pointer is NULL                       */
+  LBQ_E_SHAPE = 2,       /* n, k, m, r, ldy out of range or inconsistent     */
+  LBQ_E_FORMAT = 3,      /* unknown format / bits / group / dq settings      */
+  LBQ_E_ALIGN = 4,       /* a pointer or leading dimension is misaligned     */
+  LBQ_E_WORKSPACE = 5,   /* workspace missing or smaller than required       */
+  LBQ_E_UNSUPPORTED = 6, /* valid request this build does not implement      */
+  LBQ_E_HIP = 7          /* the HIP runtime reported an error                */
+} lbq_status;
+
+typedef enum {
+  LBQ_MINMAX = 0, /* asymmetric group-wise MinMax RTN [GB]                   */
+  LBQ_NF4 = 1     /* 4-bit NormalFloat, blockwise absmax, optional DQ [QL]   */
+} lbq_format;
+
+/* Describes one quantized weight W[n][k].
+ *   MINMAX: bits in {4, 2}, group in {64, 128}, k % group == 0;
+ *           double_quant = 0, dq_block = 0.
+ *   NF4:    bits = 4, group = 64 (absmax block; blocks run row-major and never
+ *           straddle rows because k % 64 == 0); double_quant in {0, 1};
+ *           dq_block = 256 when double_quant = 1, else 0.
+ * n >= 1, k >= 64. */
+typedef struct {
+  int32_t format;
+  int32_t bits;
+  int32_t group;
+  int32_t double_quant;
+  int32_t dq_block;
+  int32_t reserved; /* must be 0 */
+  int64_t n;
+  int64_t k;
+} lbq_desc;
+
+/* Device buffers of one quantized weight.  Which fields are used:
+ *   packed        all formats  u8[n][k*bits/8]; 4-bit: byte i of a row holds
+ *                              code 2i in bits 7..4 and code 2i+1 in bits 3..0
+ *                              [BNB]; 2-bit: code 4i in bits 7..6, then 5..4,
+ *                              3..2, 1..0.  Only the bytes matter: the caller
+ *                              may hold them in any dtype of the same size.
+ *   scales        MINMAX       f32[n][k/group]
+ *   zeros         MINMAX       u8 [n][k/group]  (integer zero point 0..2^bits-1)
+ *   absmax        NF4, DQ=0    f32[n*k/64]
+ *   absmax_q      NF4, DQ=1    i8 [n*k/64]      (0..127)
+ *   absmax_scale  NF4, DQ=1    f32[ceil(n*k/64/256)]
+ *   out_rows      optional (forward only): int32[n]; row i of W writes output
+ *                 column out_rows[i] of Y (channel-mix scatter [GB]).  NULL
+ *                 means row i writes column i.  Entries must be distinct and
+ *                 in [0, ldy); this is the caller's responsibility.
+ * Unused fields are ignored. */
+typedef struct {
+  void* packed;
+  float* scales;
+  uint8_t* zeros;
+  float* absmax;
+  int8_t* absmax_q;
+  float* absmax_scale;
+  const int32_t* out_rows;
+} lbq_qtensor;
+
+/* Byte sizes of every buffer of a quantized weight (0 for unused ones). */
+typedef struct {
+  size_t packed;
+  size_t scales;
+  size_t zeros;
+  size_t absmax;
+  size_t absmax_q;
+  size_t absmax_scale;
+} lbq_sizes;
+
+/* Host only, no device access.  Validates `desc` and returns the sizes of the
+ * buffers lbq_quantize fills.  Errors: LBQ_E_NULL, LBQ_E_FORMAT, LBQ_E_SHAPE. */
+lbq_status lbq_layout(const lbq_desc* desc, lbq_sizes* out);
+
+/* Quantize fp32 W[n][k] (device) into the buffers of `q`.
+ *   MINMAX [GB] 模型量化: per row and group of `group` consecutive weights:
+ *     lo = min(0, min w), hi = max(0, max w); s = fl(fl(hi-lo)/(2^bits-1)),
+ *     s := 1 if it is 0; z = clamp(rne(fl(-lo/s)), 0, 2^bits-1);
+ *     q = clamp(rne(fl(w/s)) + z, 0, 2^bits-1); codes packed as above.
+ *   NF4 [QL] QLoRA技术原理: per block of 64: a = max|w|; codes 7 if a == 0, else
+ *     the number of fp32 codebook midpoints strictly below fl(w/a).  With
+ *     double_quant = 1 the block absmax values are re-quantized in runs of
+ *     256: c2 = fl(max/127), q2 = clamp(rne(fl(a/c2)), 0, 127) (0 if c2 == 0);
+ *     the 4-bit codes always use the un-quantized a.
+ * Every fp32 step is one IEEE operation rounded to nearest-even (true
+ * division, no contraction); results are bit-exact across runs.
+ * Pure: it never inspects the old contents of the outputs. */
+lbq_status lbq_quantize(const lbq_desc* desc, const float* W, const lbq_qtensor* q,
+                        void* stream);
+
+/* Dequantize to bf16 W_bf16[n][k] (device) [BNB] 通过BitsAndBytesConfig配置:
+ *   MINMAX: bf16(fl((q - z) * s));  NF4: bf16(fl(c[code] * A)) with A the block
+ *   absmax, or fl(q2 * c2) under double quantization.  bf16 rounding is
+ *   round-to-nearest-even; the result is bit-exact. */
+lbq_status lbq_dequant(const lbq_desc* desc, const lbq_qtensor* q, uint16_t* W_bf16,
+                       void* stream);
+
+/* Workspace bytes lbq_linear_fwd needs for m rows (0 when none). */
+size_t lbq_linear_workspace_bytes(const lbq_desc* desc, int64_t m);
+
+/* Forward of the frozen low-bit linear layer, Y = X . deq(W)^T:
+ *   Y[i][col(j)] = bf16( sum_k X[i][k] * w_hat[j][k] ),  col(j) = out_rows ?
+ *   out_rows[j] : j, with w_hat the dequantized weight and fp32 accumulation.
+ * X: bf16 [m][k] (device); Y: bf16 [m][ldy] (device), ldy >= n (or >
+ * max(out_rows)); only the n addressed columns of each row are written.
+ * m >= 0 (m == 0 is an empty batch: nothing is read or written).  `workspace` must hold lbq_linear_workspace_bytes(desc, m) bytes
+ * (may be NULL when that is 0).  Decode sizes (small m) run a wavefront-
+ * reduction GEMV streaming the packed weight; larger m run an LDS-tiled
+ * bf16-MFMA GEMM that dequantizes tiles in registers. */
+lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X,
+                          int64_t m, uint16_t* Y, int64_t ldy, void* workspace,
+                          size_t ws_bytes, void* stream);
+
+/* Input gradient through the frozen weight, dX = dY . deq(W) ([QL]
+ * QLoRA技术原理: gradients pass through the frozen 4-bit model):
+ *   dX[i][k] = bf16( sum_j dY[i][j] * w_hat[j][k] ), fp32 accumulation.
+ * dY: bf16 [m][n]; dX: bf16 [m][k] (device).  out_rows must be NULL
+ * (LBQ_E_UNSUPPORTED otherwise). */
+lbq_status lbq_linear_bwd_dx(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* dY,
+                             int64_t m, uint16_t* dX, void* stream);
+
+/* Workspace bytes lbq_lora_fwd needs for m rows and rank r. */
+size_t lbq_lora_workspace_bytes(const lbq_desc* desc, int64_t m, int32_t r);
+
+/* Forward with a LoRA branch ([BNB] step 4; [QL] QLoRA技术原理):
+ *   Y = X . deq(W)^T + sigma * (X . A^T) . B^T,  sigma = lora_alpha / r.
+ * A: bf16 [r][k], B: bf16 [n][r] (device), 1 <= r <= 64.  The adapter
+ * product T = sigma * X . A^T is formed in fp32 and rounded once to bf16
+ * before it meets B.  Other arguments as lbq_linear_fwd; `workspace` must
+ * hold lbq_lora_workspace_bytes(desc, m, r) bytes. */
+lbq_status lbq_lora_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X,
+                        int64_t m, const uint16_t* A, const uint16_t* B, int32_t r,
+                        float sigma, uint16_t* Y, int64_t ldy, void* workspace,
+                        size_t ws_bytes, void* stream);
+
+/* Host only.  The library's NF4 codebook (16 fp32 levels, ascending, with
+ * c[0] = -1, c[7] = 0, c[15] = 1), computed by the library from normal
+ * quantiles at evenly spaced probabilities [QL]. */
+void lbq_nf4_codebook(float out[16]);
+
+/* Host only.  Static text for a status code. */
+const char* lbq_strerror(lbq_status s);
+
+/* Host only.  Detail of the last failure on the calling thread ("" if none). */
+const char* lbq_last_error_detail(void);
+
+/* Host only.  Library version string. */
+const char* lbq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LBQ_H */

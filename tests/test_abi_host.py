@@ -1,0 +1,221 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports every
+symbol include/lbq.h declares, computes buffer sizes by the closed forms, and
+rejects every malformed request before touching the device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import lbq_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import group_wise_minmax_amd as L
+    return L
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "lbq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lbq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol(L):
+    lib = ctypes.CDLL(L.LIB_PATH)
+    decl = declared_symbols()
+    assert len(decl) >= 12
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert set(decl) == set(L.EXPORTED)
+    assert "gfx950" in L.version()
+
+
+def test_nf4_codebook_matches_oracle(L):
+    """The library builds its table itself (bisection on erfc); the oracle
+    uses a different quantile routine.  After fp32 rounding they must agree."""
+    lib_tab = np.array(L.lbq_nf4_codebook(), dtype=np.float32)
+    assert np.array_equal(lib_tab, O.nf4_codebook())
+
+
+@pytest.mark.parametrize("fmt,bits,group,dq,n,k", [
+    ("minmax", 4, 128, False, 4096, 4096), ("minmax", 2, 64, False, 1024, 8192),
+    ("minmax", 4, 64, False, 3, 192), ("minmax", 2, 128, False, 5, 384),
+    ("nf4", 4, 64, True, 14336, 4096), ("nf4", 4, 64, False, 7, 64), ("nf4", 4, 64, True, 3, 320),
+])
+def test_layout_closed_forms(L, fmt, bits, group, dq, n, k):
+    s = L.lbq_layout(L.make_desc(fmt, n, k, bits, group, dq))
+    assert s["packed"] == n * k * bits // 8
+    if fmt == "minmax":
+        assert s["scales"] == 4 * n * k // group and s["zeros"] == n * k // group
+        assert s["absmax"] == s["absmax_q"] == s["absmax_scale"] == 0
+    else:
+        nb = n * k // 64
+        if dq:
+            assert s["absmax_q"] == nb and s["absmax_scale"] == 4 * (-(-nb // 256)) and s["absmax"] == 0
+        else:
+            assert s["absmax"] == 4 * nb and s["absmax_q"] == 0
+        assert s["scales"] == s["zeros"] == 0
+
+
+def test_layout_double_quant_saving(L):
+    """Bits per parameter saved by double quantization, from the library's own
+    byte counts: 0.373046875 on every 8B / 70B / 110B shape."""
+    import synth_inputs as SI
+    for shapes in (SI.LLAMA3_8B, SI.LLAMA3_70B, SI.QWEN15_110B):
+        for n, k in shapes.values():
+            a = L.lbq_layout(L.make_desc("nf4", n, k, double_quant=False))
+            b = L.lbq_layout(L.make_desc("nf4", n, k, double_quant=True))
+            saved = a["absmax"] - (b["absmax_q"] + b["absmax_scale"])
+            assert 8.0 * saved / (n * k) == 0.373046875
+
+
+def _desc(L, **kw):
+    d = L.make_desc("minmax", 64, 256, 4, 128)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(format=7), "LBQ_E_FORMAT"), (dict(bits=3), "LBQ_E_FORMAT"), (dict(bits=8), "LBQ_E_FORMAT"),
+    (dict(group=32), "LBQ_E_FORMAT"), (dict(group=100), "LBQ_E_FORMAT"),
+    (dict(double_quant=1), "LBQ_E_FORMAT"), (dict(reserved=1), "LBQ_E_FORMAT"),
+    (dict(n=0), "LBQ_E_SHAPE"), (dict(k=0), "LBQ_E_SHAPE"), (dict(k=96), "LBQ_E_SHAPE"),
+    (dict(k=192), "LBQ_E_SHAPE"), (dict(n=-5), "LBQ_E_SHAPE"),
+])
+def test_layout_rejects_bad_desc(L, kw, code):
+    with pytest.raises(L.LbqError) as e:
+        L.lbq_layout(_desc(L, **kw))
+    assert e.value.name == code
+
+
+def test_nf4_type_check(L):
+    """Only the nf4 type exists among 4-bit float types (fp4 is not built):
+    a wrong quant type is a format error, as the type check in the
+    bitsandbytes guide's parameter table makes it."""
+    d = L.make_desc("nf4", 64, 256)
+    d.bits = 2
+    with pytest.raises(L.LbqError) as e:
+        L.lbq_layout(d)
+    assert e.value.name == "LBQ_E_FORMAT"
+    d = L.make_desc("nf4", 64, 256)
+    d.group = 128
+    with pytest.raises(L.LbqError):
+        L.lbq_layout(d)
+    d = L.make_desc("nf4", 64, 256, double_quant=True)
+    d.dq_block = 128
+    with pytest.raises(L.LbqError):
+        L.lbq_layout(d)
+
+
+# Error paths of the device entry points: every one must be caught on the host
+# before any launch, so fake (never dereferenced) addresses are enough here.
+FAKE = 0x7F0000000000  # 16-byte aligned, never touched
+
+
+def _q(L, **kw):
+    q = L.QTensor()
+    q.packed = FAKE
+    q.scales = FAKE + 0x1000
+    q.zeros = FAKE + 0x2000
+    q.absmax = FAKE + 0x3000
+    q.absmax_q = FAKE + 0x4000
+    q.absmax_scale = FAKE + 0x5000
+    for k, v in kw.items():
+        setattr(q, k, v)
+    return q
+
+
+def _status(L, rc):
+    return L._lib.STATUS[rc]
+
+
+def test_quantize_error_paths(L):
+    lib = L.lib
+    d = L.make_desc("minmax", 64, 256)
+    B = ctypes.byref
+    assert _status(L, lib.lbq_quantize(None, FAKE, B(_q(L)), None)) == "LBQ_E_NULL"
+    assert _status(L, lib.lbq_quantize(B(d), None, B(_q(L)), None)) == "LBQ_E_NULL"
+    assert _status(L, lib.lbq_quantize(B(d), FAKE, None, None)) == "LBQ_E_NULL"
+    assert _status(L, lib.lbq_quantize(B(d), FAKE, B(_q(L, packed=None)), None)) == "LBQ_E_NULL"
+    assert _status(L, lib.lbq_quantize(B(d), FAKE, B(_q(L, scales=None)), None)) == "LBQ_E_NULL"
+    assert _status(L, lib.lbq_quantize(B(d), FAKE, B(_q(L, zeros=None)), None)) == "LBQ_E_NULL"
+    assert _status(L, lib.lbq_quantize(B(d), FAKE + 4, B(_q(L)), None)) == "LBQ_E_ALIGN"
+    assert _status(L, lib.lbq_quantize(B(d), FAKE, B(_q(L, packed=FAKE + 8)), None)) == "LBQ_E_ALIGN"
+    assert _status(L, lib.lbq_quantize(B(d), FAKE, B(_q(L, scales=FAKE + 2)), None)) == "LBQ_E_ALIGN"
+    assert "16-byte" in lib.lbq_last_error_detail().decode() or "4-byte" in lib.lbq_last_error_detail().decode()
+    dn = L.make_desc("nf4", 64, 256, double_quant=True)
+    assert _status(L, lib.lbq_quantize(B(dn), FAKE, B(_q(L, absmax_q=None)), None)) == "LBQ_E_NULL"
+    assert _status(L, lib.lbq_quantize(B(dn), FAKE, B(_q(L, absmax_scale=None)), None)) == "LBQ_E_NULL"
+    dn0 = L.make_desc("nf4", 64, 256, double_quant=False)
+    assert _status(L, lib.lbq_quantize(B(dn0), FAKE, B(_q(L, absmax=None)), None)) == "LBQ_E_NULL"
+
+
+def test_dequant_error_paths(L):
+    lib = L.lib
+    d = L.make_desc("minmax", 64, 256, 2, 64)
+    B = ctypes.byref
+    assert _status(L, lib.lbq_dequant(B(d), B(_q(L)), None, None)) == "LBQ_E_NULL"
+    assert _status(L, lib.lbq_dequant(B(d), B(_q(L)), FAKE + 2, None)) == "LBQ_E_ALIGN"
+    bad = L.make_desc("minmax", 64, 256, 4, 128)
+    bad.bits = 1
+    assert _status(L, lib.lbq_dequant(B(bad), B(_q(L)), FAKE, None)) == "LBQ_E_FORMAT"
+
+
+def test_fwd_error_paths(L):
+    lib = L.lib
+    d = L.make_desc("minmax", 64, 256)
+    B = ctypes.byref
+    q = _q(L)
+    assert _status(L, lib.lbq_linear_fwd(B(d), B(q), FAKE, -1, FAKE, 64, None, 0, None)) == "LBQ_E_SHAPE"
+    assert _status(L, lib.lbq_linear_fwd(B(d), B(q), None, 4, FAKE, 64, None, 0, None)) == "LBQ_E_NULL"
+    assert _status(L, lib.lbq_linear_fwd(B(d), B(q), FAKE, 4, None, 64, None, 0, None)) == "LBQ_E_NULL"
+    assert _status(L, lib.lbq_linear_fwd(B(d), B(q), FAKE + 2, 4, FAKE, 64, None, 0, None)) == "LBQ_E_ALIGN"
+    assert _status(L, lib.lbq_linear_fwd(B(d), B(q), FAKE, 4, FAKE + 1, 64, None, 0, None)) == "LBQ_E_ALIGN"
+    assert _status(L, lib.lbq_linear_fwd(B(d), B(q), FAKE, 4, FAKE, 60, None, 0, None)) == "LBQ_E_SHAPE"
+    # m == 0 is an empty batch: a no-op that touches nothing
+    assert _status(L, lib.lbq_linear_fwd(B(d), B(q), None, 0, None, 64, None, 0, None)) == "LBQ_OK"
+
+
+def test_bwd_error_paths(L):
+    lib = L.lib
+    B = ctypes.byref
+    d = L.make_desc("minmax", 64, 256)
+    assert _status(L, lib.lbq_linear_bwd_dx(B(d), B(_q(L, out_rows=FAKE)), FAKE, 4, FAKE, None)) == "LBQ_E_UNSUPPORTED"
+    assert _status(L, lib.lbq_linear_bwd_dx(B(d), B(_q(L)), None, 4, FAKE, None)) == "LBQ_E_NULL"
+    assert _status(L, lib.lbq_linear_bwd_dx(B(d), B(_q(L)), FAKE + 8, 4, FAKE, None)) == "LBQ_E_ALIGN"
+    d2 = L.make_desc("minmax", 60, 256)
+    assert _status(L, lib.lbq_linear_bwd_dx(B(d2), B(_q(L)), FAKE, 4, FAKE, None)) == "LBQ_E_SHAPE"
+    assert _status(L, lib.lbq_linear_bwd_dx(B(d), B(_q(L)), None, 0, None, None)) == "LBQ_OK"
+
+
+def test_lora_error_paths(L):
+    lib = L.lib
+    B = ctypes.byref
+    d = L.make_desc("nf4", 64, 256, double_quant=True)
+    q = _q(L)
+    need = lib.lbq_lora_workspace_bytes(B(d), 8, 16)
+    assert need == 8 * 32 * 2
+    assert lib.lbq_lora_workspace_bytes(B(d), 8, 33) == 8 * 64 * 2
+    args = lambda r=16, ws=FAKE, wsb=need, A=FAKE, Bm=FAKE, sigma=1.0: lib.lbq_lora_fwd(
+        B(d), B(q), FAKE, 8, A, Bm, r, sigma, FAKE, 64, ws, wsb, None)
+    assert _status(L, args(r=0)) == "LBQ_E_SHAPE"
+    assert _status(L, args(r=65)) == "LBQ_E_SHAPE"
+    assert _status(L, args(ws=None)) == "LBQ_E_WORKSPACE"
+    assert _status(L, args(wsb=need - 1)) == "LBQ_E_WORKSPACE"
+    assert _status(L, args(A=None)) == "LBQ_E_NULL"
+    assert _status(L, args(A=FAKE + 2)) == "LBQ_E_ALIGN"
+    assert _status(L, args(Bm=FAKE + 1)) == "LBQ_E_ALIGN"
+    assert _status(L, args(sigma=float("inf"))) == "LBQ_E_SHAPE"
+    assert _status(L, args(ws=FAKE + 8)) == "LBQ_E_ALIGN"
+
+
+def test_strerror_covers_every_status(L):
+    for code in range(8):
+        assert L.lib.lbq_strerror(code).decode() not in ("", "unknown status")
+    assert L.lib.lbq_strerror(99).decode() == "unknown status"

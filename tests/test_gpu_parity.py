@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.
+
+* quantize (codes, packed bytes, scales, zeros, absmax, absmax_q,
+  absmax_scale) and dequantize (bf16) must be bit-exact;
+* forward / input-gradient / LoRA must meet the matmul tolerance (relative
+  Frobenius <= 5e-3, max-abs <= 2e-2 max|Y_ref| against fp64), and on inputs
+  whose every partial sum is exact in fp32 they must equal bf16(exact) bit for
+  bit, whichever kernel (GEMV or MFMA tile) runs.
+
+Sizes span several tiles plus ragged tails (n not a multiple of the tile,
+short K, m that is not a multiple of 16 or 128).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as SI
+from oracle import lbq_oracle as O
+from gpu_util import (DEV, assert_close, bf16_bits_host, check_quantized_equal,
+                            to_dev_bf16, to_dev_f32)
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = [
+    ("minmax", 4, 128, False), ("minmax", 2, 64, False), ("minmax", 4, 64, False),
+    ("minmax", 2, 128, False), ("nf4", 4, 64, False), ("nf4", 4, 64, True),
+]
+FMT_IDS = ["i4g128", "i2g64", "i4g64", "i2g128", "nf4", "nf4dq"]
+
+
+@pytest.fixture(scope="module")
+def L():
+    import group_wise_minmax_amd as L
+    assert torch.cuda.is_available()
+    return L
+
+
+def _quant_pair(L, W, fmt, bits, group, dq):
+    qw = L.lbq_quantize(to_dev_f32(W), fmt, bits, group, dq)
+    ref = O.quantize(W, fmt, bits, group, dq)
+    return qw, ref
+
+
+# ------------------------------------------------------------------ quantize
+
+
+@pytest.mark.parametrize("fmtspec", FORMATS, ids=FMT_IDS)
+@pytest.mark.parametrize("shape", [(256, 256), (3, 384), (1, 128), (37, 1280), (1000, 4096)])
+def test_quantize_and_dequant_bitexact(L, fmtspec, shape):
+    fmt, bits, group, dq = fmtspec
+    n, k = shape
+    W = SI.gaussian_weights(SI.seed_of(1, 0, 0) + n, n, k, outlier_seed=SI.seed_of(1, 0, 1) + n)
+    qw, ref = _quant_pair(L, W, fmt, bits, group, dq)
+    wb = L.lbq_dequant(qw)
+    torch.cuda.synchronize()
+    check_quantized_equal(qw, ref, fmt, dq)
+    assert np.array_equal(bf16_bits_host(wb), ref["w_bf16"])
+
+
+@pytest.mark.parametrize("fmtspec", FORMATS, ids=FMT_IDS)
+def test_quantize_heavy_tailed_and_special_groups(L, fmtspec):
+    fmt, bits, group, dq = fmtspec
+    W = SI.student_t_weights(5010, 64, 1024)
+    W[0, :] = 0.0                                   # all-zero rows / groups / blocks
+    W[1, 5] = 3.0                                    # single nonzero groups
+    W[2, :128] = -0.25                               # single-signed group
+    W[3, 64:128] = np.tile(np.array([-0.5, 0.0, 0.5, 0.0], dtype=np.float32), 16)
+    qw, ref = _quant_pair(L, W, fmt, bits, group, dq)
+    wb = L.lbq_dequant(qw)
+    torch.cuda.synchronize()
+    check_quantized_equal(qw, ref, fmt, dq)
+    assert np.array_equal(bf16_bits_host(wb), ref["w_bf16"])
+
+
+def test_quantize_config0_is_deterministic(L):
+    """Single linear layer of 256x256, INT4 g128: two runs give identical bytes."""
+    W = SI.gaussian_weights(SI.seed_of(0, 0, 0), 256, 256)
+    a = L.lbq_quantize(to_dev_f32(W), "minmax", 4, 128)
+    b = L.lbq_quantize(to_dev_f32(W), "minmax", 4, 128)
+    torch.cuda.synchronize()
+    assert torch.equal(a.packed, b.packed) and torch.equal(a.scales, b.scales)
+
+
+# ------------------------------------------------------------------ forward
+
+FWD_M = [1, 2, 3, 4, 5, 8, 16, 100, 130]
+
+
+@pytest.mark.parametrize("fmtspec", FORMATS, ids=FMT_IDS)
+@pytest.mark.parametrize("nk", [(300, 384), (256, 256), (1040, 1280)])
+@pytest.mark.parametrize("m", FWD_M)
+def test_forward_tolerance(L, fmtspec, nk, m):
+    fmt, bits, group, dq = fmtspec
+    n, k = nk
+    W = SI.gaussian_weights(7000 + n, n, k, outlier_seed=7001 + n)
+    X = SI.bf16_normal(7002 + m, (m, k))
+    qw, ref = _quant_pair(L, W, fmt, bits, group, dq)
+    Y = L.lbq_linear_fwd(to_dev_bf16(X), qw)
+    torch.cuda.synchronize()
+    assert_close(bf16_bits_host(Y), O.linear_fwd(X, ref["w_exact"]), what=f"{fmt}{bits}g{group} m={m}")
+
+
+@pytest.mark.parametrize("fmtspec", FORMATS, ids=FMT_IDS)
+@pytest.mark.parametrize("m", [1, 3, 4])
+def test_forward_gemv_many_rows(L, fmtspec, m):
+    """n >= 4096 takes the four-rows-per-wave GEMV; 4097 leaves a ragged wave."""
+    fmt, bits, group, dq = fmtspec
+    W = SI.gaussian_weights(7100, 4097, 512, outlier_seed=7101)
+    X = SI.bf16_normal(7102, (m, 512))
+    qw, ref = _quant_pair(L, W, fmt, bits, group, dq)
+    Y = L.lbq_linear_fwd(to_dev_bf16(X), qw)
+    torch.cuda.synchronize()
+    assert_close(bf16_bits_host(Y), O.linear_fwd(X, ref["w_exact"]))
+
+
+@pytest.mark.parametrize("bits,group", [(4, 128), (2, 64), (4, 64), (2, 128)])
+@pytest.mark.parametrize("m", [1, 2, 4, 7, 16, 130])
+def test_forward_exact_on_grid_minmax(L, bits, group, m):
+    """Lossless power-of-two-grid weights and integer activations: every
+    partial sum is exact in fp32, so Y must equal bf16(X W^T) bit for bit."""
+    n, k = 272, 512
+    W = SI.grid_weights(7200, n, k, group, bits)
+    X = SI.bf16_small_ints(7201 + m, (m, k))
+    qw, ref = _quant_pair(L, W, "minmax", bits, group, False)
+    assert np.array_equal(ref["w_exact"], W.astype(np.float64))
+    Y = L.lbq_linear_fwd(to_dev_bf16(X), qw)
+    torch.cuda.synchronize()
+    exact = O.bf16_to_f64(X) @ W.astype(np.float64).T
+    assert np.array_equal(bf16_bits_host(Y), O.bf16_bits(exact.astype(np.float32)))
+
+
+@pytest.mark.parametrize("m", [1, 3, 16, 130])
+def test_forward_exact_on_grid_nf4(L, m):
+    """NF4 blocks holding only {-a, 0, +a} (a a power of two) encode to the
+    levels -1, 0, +1 exactly, so again Y == bf16(exact)."""
+    n, k = 200, 640
+    rng = np.random.default_rng(7300)
+    signs = rng.integers(-1, 2, size=(n * k // 64, 64)).astype(np.float64)
+    signs[:, 0] = 1.0  # every block reaches +a, so its absmax is a
+    a = 2.0 ** rng.integers(-6, -2, size=(n * k // 64, 1))
+    W = (signs * a).astype(np.float32).reshape(n, k)
+    X = SI.bf16_small_ints(7301 + m, (m, k))
+    qw, ref = _quant_pair(L, W, "nf4", 4, 64, False)
+    assert np.array_equal(ref["w_exact"], W.astype(np.float64))
+    Y = L.lbq_linear_fwd(to_dev_bf16(X), qw)
+    torch.cuda.synchronize()
+    exact = O.bf16_to_f64(X) @ W.astype(np.float64).T
+    assert np.array_equal(bf16_bits_host(Y), O.bf16_bits(exact.astype(np.float32)))
+
+
+def test_forward_empty_batch_and_strided_output(L):
+    W = SI.gaussian_weights(7400, 128, 256)
+    qw = L.lbq_quantize(to_dev_f32(W), "minmax", 4, 128)
+    X = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    Y = L.lbq_linear_fwd(X, qw)
+    assert Y.shape == (0, 128)
+    # ldy > n: only the first n columns are written
+    Xb = SI.bf16_normal(7401, (5, 256))
+    out = torch.full((5, 136), 7.0, dtype=torch.bfloat16, device=DEV)
+    L.lbq_linear_fwd(to_dev_bf16(Xb), qw, out=out[:, :])
+    torch.cuda.synchronize()
+    ref = O.quantize(W, "minmax", 4, 128)
+    assert_close(bf16_bits_host(out[:, :128]), O.linear_fwd(Xb, ref["w_exact"]))
+    assert torch.all(out[:, 128:] == 7.0)
+
+
+def test_forward_repeatable_bits(L):
+    W = SI.gaussian_weights(7500, 1024, 1024)
+    X = to_dev_bf16(SI.bf16_normal(7501, (300, 1024)))
+    qw = L.lbq_quantize(to_dev_f32(W), "nf4", double_quant=True)
+    a = L.lbq_linear_fwd(X, qw).clone()
+    b = L.lbq_linear_fwd(X, qw)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ------------------------------------------------------------------ backward
+
+
+@pytest.mark.parametrize("fmtspec", FORMATS, ids=FMT_IDS)
+@pytest.mark.parametrize("nk", [(264, 384), (1024, 1280)])
+@pytest.mark.parametrize("m", [1, 5, 64, 130])
+def test_bwd_dx_tolerance(L, fmtspec, nk, m):
+    fmt, bits, group, dq = fmtspec
+    n, k = nk
+    W = SI.gaussian_weights(8000 + n, n, k, outlier_seed=8001 + n)
+    dY = SI.bf16_normal(8002 + m, (m, n))
+    qw, ref = _quant_pair(L, W, fmt, bits, group, dq)
+    dX = L.lbq_linear_bwd_dx(to_dev_bf16(dY), qw)
+    torch.cuda.synchronize()
+    assert_close(bf16_bits_host(dX), O.linear_bwd_dx(dY, ref["w_exact"]), what=f"bwd {fmt} m={m}")
+
+
+@pytest.mark.parametrize("bits,group", [(4, 128), (2, 64)])
+@pytest.mark.parametrize("m", [3, 130])
+def test_bwd_dx_exact_on_grid(L, bits, group, m):
+    n, k = 136, 640
+    W = SI.grid_weights(8100, n, k, group, bits)
+    dY = SI.bf16_small_ints(8101 + m, (m, n))
+    qw, _ = _quant_pair(L, W, "minmax", bits, group, False)
+    dX = L.lbq_linear_bwd_dx(to_dev_bf16(dY), qw)
+    torch.cuda.synchronize()
+    exact = O.bf16_to_f64(dY) @ W.astype(np.float64)
+    assert np.array_equal(bf16_bits_host(dX), O.bf16_bits(exact.astype(np.float32)))
+
+
+# ------------------------------------------------------------------ LoRA
+
+
+@pytest.mark.parametrize("fmtspec", [FORMATS[0], FORMATS[5]], ids=["i4g128", "nf4dq"])
+@pytest.mark.parametrize("m", [1, 4, 40, 130])
+@pytest.mark.parametrize("r", [16, 8, 40])
+def test_lora_tolerance(L, fmtspec, m, r):
+    fmt, bits, group, dq = fmtspec
+    n, k = 320, 512
+    W = SI.gaussian_weights(9000, n, k)
+    X = SI.bf16_normal(9001 + m, (m, k))
+    A = SI.bf16_normal(9002, (r, k), std=0.01)
+    B = SI.bf16_normal(9003, (n, r), std=0.01)
+    qw, ref = _quant_pair(L, W, fmt, bits, group, dq)
+    Y = L.lbq_lora_fwd(to_dev_bf16(X), qw, to_dev_bf16(A), to_dev_bf16(B), 16.0 / r)
+    torch.cuda.synchronize()
+    assert_close(bf16_bits_host(Y), O.lora_fwd(X, ref["w_exact"], A, B, 16.0 / r))
+
+
+@pytest.mark.parametrize("m", [2, 130])
+@pytest.mark.parametrize("sigma", [1.0, 2.0])
+def test_lora_branch_alone_on_zero_weight(L, m, sigma):
+    """W == 0 quantizes to exact zeros, leaving only sigma (X A^T) B^T: a wrong
+    sigma or a transposed adapter cannot hide behind the base matmul."""
+    n, k, r = 256, 384, 16
+    W = np.zeros((n, k), dtype=np.float32)
+    X = SI.bf16_normal(9100 + m, (m, k))
+    A = SI.bf16_normal(9101, (r, k), std=0.01)
+    B = SI.bf16_normal(9102, (n, r), std=0.01)
+    qw, ref = _quant_pair(L, W, "nf4", 4, 64, True)
+    Y = L.lbq_lora_fwd(to_dev_bf16(X), qw, to_dev_bf16(A), to_dev_bf16(B), sigma)
+    torch.cuda.synchronize()
+    assert_close(bf16_bits_host(Y), O.lora_fwd(X, ref["w_exact"], A, B, sigma))
+
+
+# ------------------------------------------------------------------ mixed precision
+
+
+@pytest.mark.parametrize("m", [1, 3, 16, 130])
+def test_channel_mix_scatter(L, m):
+    """25% of the output channels in INT4 g128, 75% in INT2 g64, each a
+    separate quantized tensor whose out_rows scatter into one Y."""
+    n, k = 512, 384
+    W = SI.gaussian_weights(9200, n, k, outlier_seed=9201)
+    rows4 = SI.channel_mask(9202, n)
+    rows2 = np.setdiff1d(np.arange(n), rows4).astype(np.int32)
+    X = SI.bf16_normal(9203 + m, (m, k))
+    q4, r4 = _quant_pair(L, W[rows4], "minmax", 4, 128, False)
+    q2, r2 = _quant_pair(L, W[rows2], "minmax", 2, 64, False)
+    q4.out_rows = torch.from_numpy(rows4).to(DEV)
+    q2.out_rows = torch.from_numpy(rows2).to(DEV)
+    Y = torch.zeros((m, n), dtype=torch.bfloat16, device=DEV)
+    Xd = to_dev_bf16(X)
+    L.lbq_linear_fwd(Xd, q4, out=Y)
+    L.lbq_linear_fwd(Xd, q2, out=Y)
+    torch.cuda.synchronize()
+    ref = O.channel_mix_fwd(X, [(rows4, r4["w_exact"]), (rows2, r2["w_exact"])])
+    assert_close(bf16_bits_host(Y), ref)

@@ -1,0 +1,337 @@
+#!/usr/bin/env python3
+"""Benchmark of the lbq hot path on one MI355X.
+
+One step is one pass of the whole hot path over a LLaMA-3-8B decoder layer
+(q, k, v, o, gate, up, down) plus the 70B-shaped mixed-precision dispatch:
+
+  quant_int4   quantize + pack the 7 fp32 weights, MinMax INT4 g128
+  quant_nf4dq  quantize + pack the 7 weights, NF4 block 64 + double quant
+  dequant      dequantize the 7 NF4-DQ weights to bf16
+  gemv_m1      Y = X W^T at m = 1, INT4 g128, over R distinct weight copies
+               (R * 118 MB > 2 x 256 MB Infinity Cache, so weights stream from HBM)
+  gemv_m16     the same at m = 16
+  gemm_m2048   INT4 g128 forward at m = 2048
+  fwd_m4096    NF4-DQ forward at m = 4096 (2 x 2048 tokens)       <- headline
+  lora_m4096   NF4-DQ forward + rank-16 LoRA on q and v at m = 4096
+  bwd_m4096    NF4-DQ input gradient dX = dY deq(W) at m = 4096
+  chmix_70b    70B-shaped layer, per-channel 25% INT4 g128 / 75% INT2 g64,
+               forward at m = 1 and m = 1024
+
+Each phase is captured once as a HIP graph (torch.cuda.CUDAGraph) and replayed,
+so the timed region holds device work only; HIP events on the launch stream
+bracket every phase of every step.  The JSON line's ``value`` is the dequant-
+GEMM TFLOP/s of fwd_m4096 (2*m*n*k summed over the 7 linears / phase time);
+``gemv_m1_hbm_GBps`` is the other half of the headline metric.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dequant-GEMM TFLOP/s at M=4096; GEMV HBM GB/s at M=1 (LLaMA-3-8B shapes)"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "group_wise_minmax_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, units_per_launch: float):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, or None
+    when no summary exists or the kernels changed since it was taken."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    ent = data.get("kernels", {}).get(kernel)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+def build_workload(L, SI, torch, dev, R):
+    """Allocate every input/output once; return the phase list."""
+    shapes = SI.LLAMA3_8B
+    names = list(shapes)
+    W = {nm: SI.dev_gaussian_weights(SI.seed_of(2, i, SI.SLOT_W), *shapes[nm], dev)
+         for i, nm in enumerate(names)}
+    q4 = {nm: L.QuantizedWeight.empty(L.make_desc("minmax", *shapes[nm], 4, 128), dev) for nm in names}
+    qn = {nm: L.QuantizedWeight.empty(L.make_desc("nf4", *shapes[nm], double_quant=True), dev) for nm in names}
+    for nm in names:
+        L.lbq_quantize(W[nm], "minmax", 4, 128, out=q4[nm])
+        L.lbq_quantize(W[nm], "nf4", double_quant=True, out=qn[nm])
+    # R independent copies of the INT4 layer for the decode phases
+    copies = [q4]
+    for _ in range(R - 1):
+        copies.append({nm: L.QuantizedWeight(q.desc, q.packed.clone(), q.scales.clone(), q.zeros.clone())
+                       for nm, q in q4.items()})
+    wbf = {nm: torch.empty(shapes[nm], dtype=torch.bfloat16, device=dev) for nm in names}
+    K_of = {nm: shapes[nm][1] for nm in names}
+    N_of = {nm: shapes[nm][0] for nm in names}
+    X1 = {nm: SI.dev_bf16_normal(SI.seed_of(2, i, SI.SLOT_X), (1, K_of[nm]), dev) for i, nm in enumerate(names)}
+    X16 = {nm: SI.dev_bf16_normal(SI.seed_of(2, i, SI.SLOT_X) + 100, (16, K_of[nm]), dev) for i, nm in enumerate(names)}
+    X2k = {nm: SI.dev_bf16_normal(SI.seed_of(2, i, SI.SLOT_X) + 200, (2048, K_of[nm]), dev) for i, nm in enumerate(names)}
+    X4k = {nm: SI.dev_bf16_normal(SI.seed_of(3, i, SI.SLOT_X), (4096, K_of[nm]), dev) for i, nm in enumerate(names)}
+    dY = {nm: SI.dev_bf16_normal(SI.seed_of(3, i, SI.SLOT_DY), (4096, N_of[nm]), dev) for i, nm in enumerate(names)}
+    Y1 = {nm: torch.empty((1, N_of[nm]), dtype=torch.bfloat16, device=dev) for nm in names}
+    Y16 = {nm: torch.empty((16, N_of[nm]), dtype=torch.bfloat16, device=dev) for nm in names}
+    Y2k = {nm: torch.empty((2048, N_of[nm]), dtype=torch.bfloat16, device=dev) for nm in names}
+    Y4k = {nm: torch.empty((4096, N_of[nm]), dtype=torch.bfloat16, device=dev) for nm in names}
+    dX = {nm: torch.empty((4096, K_of[nm]), dtype=torch.bfloat16, device=dev) for nm in names}
+    lora = {}
+    for nm in ("q", "v"):
+        i = names.index(nm)
+        A = SI.dev_bf16_normal(SI.seed_of(3, i, SI.SLOT_A), (16, K_of[nm]), dev, std=0.01)
+        B = SI.dev_bf16_normal(SI.seed_of(3, i, SI.SLOT_B), (N_of[nm], 16), dev, std=0.01)
+        ws = torch.empty(L.lbq_lora_workspace_bytes(qn[nm], 4096, 16), dtype=torch.uint8, device=dev)
+        lora[nm] = (A, B, ws, torch.empty((4096, N_of[nm]), dtype=torch.bfloat16, device=dev))
+
+    # 70B-shaped channel-mix layer (quantized once at setup)
+    s70 = SI.LLAMA3_70B
+    cm = []
+    for i, nm in enumerate(s70):
+        n, k = s70[nm]
+        w = SI.dev_gaussian_weights(SI.seed_of(4, i, SI.SLOT_W), n, k, dev)
+        rows4 = SI.dev_channel_mask(SI.seed_of(4, i, SI.SLOT_CHMASK), n, dev)
+        mask = torch.zeros(n, dtype=torch.bool, device=dev)
+        mask[rows4.long()] = True
+        rows2 = torch.nonzero(~mask).flatten().to(torch.int32)
+        a = L.lbq_quantize(w[rows4.long()].contiguous(), "minmax", 4, 128)
+        b = L.lbq_quantize(w[rows2.long()].contiguous(), "minmax", 2, 64)
+        a.out_rows, b.out_rows = rows4, rows2
+        del w
+        x1 = SI.dev_bf16_normal(SI.seed_of(4, i, SI.SLOT_X), (1, k), dev)
+        x1k = SI.dev_bf16_normal(SI.seed_of(4, i, SI.SLOT_X) + 100, (1024, k), dev)
+        cm.append((nm, a, b, x1, x1k, torch.empty((1, n), dtype=torch.bfloat16, device=dev),
+                   torch.empty((1024, n), dtype=torch.bfloat16, device=dev)))
+    torch.cuda.synchronize()
+
+    def p_quant_int4():
+        for nm in names:
+            L.lbq_quantize(W[nm], "minmax", 4, 128, out=q4[nm])
+
+    def p_quant_nf4dq():
+        for nm in names:
+            L.lbq_quantize(W[nm], "nf4", double_quant=True, out=qn[nm])
+
+    def p_dequant():
+        for nm in names:
+            L.lbq_dequant(qn[nm], out=wbf[nm])
+
+    def p_gemv(X, Y):
+        def f():
+            for c in copies:
+                for nm in names:
+                    L.lbq_linear_fwd(X[nm], c[nm], out=Y[nm])
+        return f
+
+    def p_gemm(qs, X, Y):
+        def f():
+            for nm in names:
+                L.lbq_linear_fwd(X[nm], qs[nm], out=Y[nm])
+        return f
+
+    def p_lora():
+        for nm, (A, B, ws, Y) in lora.items():
+            L.lbq_lora_fwd(X4k[nm], qn[nm], A, B, 1.0, out=Y, workspace=ws)
+
+    def p_bwd():
+        for nm in names:
+            L.lbq_linear_bwd_dx(dY[nm], qn[nm], out=dX[nm])
+
+    def p_chmix():
+        for nm, a, b, x1, x1k, y1, y1k in cm:
+            L.lbq_linear_fwd(x1, a, out=y1)
+            L.lbq_linear_fwd(x1, b, out=y1)
+            L.lbq_linear_fwd(x1k, a, out=y1k)
+            L.lbq_linear_fwd(x1k, b, out=y1k)
+
+    def bytes_fwd(q, m, n, k):
+        return q.nbytes() + 2 * m * k + 2 * m * n
+
+    flop = lambda m: sum(2 * m * n * k for n, k in shapes.values())
+    gemv_bytes = lambda m: sum(bytes_fwd(c[nm], m, N_of[nm], K_of[nm]) for c in copies for nm in names)
+    quant_bytes = lambda qs: sum(4 * N_of[nm] * K_of[nm] + qs[nm].nbytes() for nm in names)
+    phases = [
+        ("quant_int4", p_quant_int4, {"bound": "hbm", "bytes": quant_bytes(q4), "launches": 7}),
+        ("quant_nf4dq", p_quant_nf4dq, {"bound": "hbm", "bytes": quant_bytes(qn), "launches": 7}),
+        ("dequant", p_dequant, {"bound": "hbm", "bytes": sum(qn[nm].nbytes() + 2 * N_of[nm] * K_of[nm] for nm in names), "launches": 7}),
+        ("gemv_m1", p_gemv(X1, Y1), {"bound": "hbm", "bytes": gemv_bytes(1), "launches": 7 * R}),
+        ("gemv_m16", p_gemv(X16, Y16), {"bound": "hbm", "bytes": gemv_bytes(16), "launches": 7 * R}),
+        ("gemm_m2048", p_gemm(q4, X2k, Y2k), {"bound": "mfma", "flop": flop(2048), "launches": 7}),
+        ("fwd_m4096", p_gemm(qn, X4k, Y4k), {"bound": "mfma", "flop": flop(4096), "launches": 7}),
+        ("lora_m4096", p_lora, {"bound": "mfma", "flop": sum(2 * 4096 * N_of[nm] * K_of[nm] + 2 * 4096 * 16 * (K_of[nm] + N_of[nm]) for nm in lora), "launches": 4}),
+        ("bwd_m4096", p_bwd, {"bound": "mfma", "flop": flop(4096), "launches": 7}),
+        ("chmix_70b", p_chmix, {"bound": "hbm", "bytes": sum(bytes_fwd(a, 1, a.n, a.k) + bytes_fwd(b, 1, b.n, b.k) for _, a, b, *_ in cm), "launches": 28}),
+    ]
+    return phases
+
+
+def cpu_baseline():
+    """The oracle, as it stands, on a bounded sample of the headline workload:
+    NF4 + double quantization of the 8B gate projection (14336 x 4096) and the
+    fp64 forward of all 4096 rows.  Reported in TFLOP/s of
+    the forward's 2*m*n*k over the whole oracle time (quantize + dequant +
+    matmul)."""
+    import numpy as np
+    import synth_inputs as SI
+    from oracle import lbq_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    n, k, m = 14336, 4096, 4096
+    W = SI.gaussian_weights(SI.seed_of(3, 4, SI.SLOT_W), n, k, outlier_seed=SI.seed_of(3, 4, SI.SLOT_OUTLIER))
+    X = SI.bf16_normal(SI.seed_of(3, 4, SI.SLOT_X), (m, k))
+    t0 = time.perf_counter()
+    ref = O.quantize(W, "nf4", double_quant_on=True)
+    Y = O.linear_fwd(X, ref["w_exact"])
+    dt = time.perf_counter() - t0
+    assert Y.shape == (m, n)
+    return {"value": round(2.0 * m * n * k / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"NF4+DQ quantize of the 8B gate projection ({n}x{k}) + fp64 forward of {m} of 4096 rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--copies", type=int, default=6, help="distinct INT4 layer copies for the decode phases")
+    ap.add_argument("--phases", default="", help="comma-separated subset of phases (profiling)")
+    ap.add_argument("--eager", action="store_true", help="launch phases directly instead of replaying graphs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+    import group_wise_minmax_amd as L
+    import synth_inputs as SI
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_setup = time.perf_counter()
+    phases = build_workload(L, SI, torch, dev, args.copies)
+    if args.phases:
+        keep = set(args.phases.split(","))
+        phases = [p for p in phases if p[0] in keep]
+    print(f"# setup {time.perf_counter() - t_setup:.1f}s; phases: {[p[0] for p in phases]}", file=sys.stderr, flush=True)
+
+    runners = []
+    for name, fn, info in phases:
+        fn()  # eager warm call (first-launch costs stay out of the graph)
+        torch.cuda.synchronize()
+        if args.eager:
+            runners.append((name, fn, info))
+        else:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            runners.append((name, g.replay, info))
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for _, run, _ in runners:
+            run()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+           for name, _, _ in runners}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        for name, run, _ in runners:
+            evs[name][s][0].record()
+            run()
+            evs[name][s][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / K * 1e3
+
+    report = {}
+    for name, _, info in runners:
+        ms = sum(a.elapsed_time(b) for a, b in evs[name]) / K
+        ent = {"ms": round(ms, 4), "launches": info["launches"], "avg_launch_us": round(ms * 1e3 / info["launches"], 3)}
+        if info["bound"] == "hbm":
+            gbps = info["bytes"] / (ms * 1e-3) / 1e9
+            ent.update(GBps=round(gbps, 1), bytes=info["bytes"], hbm_frac=round(gbps / HBM_PEAK_GBPS, 4))
+        else:
+            tf = info["flop"] / (ms * 1e-3) / 1e12
+            ent.update(TFLOPs=round(tf, 1), flop=info["flop"], mfma_frac=round(tf / BF16_PEAK_TFLOPS, 4))
+        report[name] = ent
+        print(f"# {name:12s} {json.dumps(ent)}", file=sys.stderr, flush=True)
+
+    head = report.get("fwd_m4096")
+    value = head["TFLOPs"] if head else None
+    gemv = report.get("gemv_m1")
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "LLaMA-3-8B decoder layer (q,k,v,o 4096/1024 x 4096; gate,up 14336x4096; down 4096x14336): "
+                        "INT4 g128 + NF4-DQ quantize, dequant, GEMV m=1/16 (INT4 g128, 6 weight copies), "
+                        "GEMM m=2048 (INT4), fwd m=4096 (NF4-DQ, headline), LoRA r=16 on q,v, bwd dX m=4096; "
+                        "plus 70B-shaped channel-mix (25% INT4 g128 / 75% INT2 g64) at m=1 and 1024",
+            "gemm_m": 4096, "gemv_m": 1, "headline_format": "nf4+dq (fwd m=4096); int4 g128 (gemv m=1)",
+            "graph_replay": not args.eager,
+        },
+        "gemv_m1_hbm_GBps": gemv["GBps"] if gemv else None,
+        "phases": report,
+    }
+    if head:
+        per_launch = head["flop"] / head["launches"]
+        ach = per_launch / (head["avg_launch_us"] * 1e-6) / 1e12
+        out["roofline"] = {"kernel": "k_gemm_fwd<NF4DQ> (m=4096, 7 linears)", "bound": "mfma",
+                           "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                           "traffic": load_traffic("fwd_m4096", per_launch)}
+    if gemv:
+        per_launch = gemv["bytes"] / gemv["launches"]
+        ach = per_launch / (gemv["avg_launch_us"] * 1e-6) / 1e9
+        out["roofline_gemv_m1"] = {"kernel": "k_gemv<INT4 g128, m=1> (7 linears x copies)", "bound": "hbm",
+                                   "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                   "frac": round(ach / HBM_PEAK_GBPS, 4),
+                                   "traffic": load_traffic("gemv_m1", per_launch)}
+    if not args.no_cpu_baseline:
+        print("# cpu_baseline: timing the oracle on a bounded sample ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

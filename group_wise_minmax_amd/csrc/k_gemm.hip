@@ -61,7 +61,7 @@ __device__ __forceinline__ void dequant32(const WView& w, const float* cb, int64
   }
 }
 
-template <int KIND, int BM, int BN>
+template <int KIND, int BM, int BN, bool LORA>
 __global__ __launch_bounds__(256) void k_gemm_fwd(WView w, const uint16_t* __restrict__ X, int m,
                                                  uint16_t* __restrict__ Y, int64_t ldy,
                                                  const int32_t* __restrict__ out_rows,
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(WView w, const uint16_t* __res
   }
 
   // LoRA slab: acc += B_lora[n][:] . T[m][:], r zero-padded to rp (multiple of 32).
-  if (lora.t != nullptr) {
+  if constexpr (LORA) {
     for (int ks = 0; ks < lora.rp; ks += 32) {
       u32x4_t af[TN], bf[TM];
 #pragma unroll
@@ -232,8 +232,13 @@ struct GemmFwdLauncher {
                         hipStream_t s) {
     constexpr int BM = 128, BN = 128;
     const dim3 grid((unsigned)((w.n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
-    hipLaunchKernelGGL((k_gemm_fwd<KIND, BM, BN>), grid, dim3(256), 0, s, w, X, (int)m, Y, ldy,
-                       out_rows, lora, tab);
+    if (lora.t != nullptr) {
+      hipLaunchKernelGGL((k_gemm_fwd<KIND, BM, BN, true>), grid, dim3(256), 0, s, w, X, (int)m, Y,
+                         ldy, out_rows, lora, tab);
+    } else {
+      hipLaunchKernelGGL((k_gemm_fwd<KIND, BM, BN, false>), grid, dim3(256), 0, s, w, X, (int)m, Y,
+                         ldy, out_rows, lora, tab);
+    }
     return hipGetLastError();
   }
 };

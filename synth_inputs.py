@@ -127,3 +127,49 @@ def grid_weights(seed: int, n: int, k: int, group: int, bits: int,
     perm = rng.permuted(np.broadcast_to(np.arange(group), (n, ng, group)), axis=2)
     dev = np.take_along_axis(dev, perm, axis=2)
     return (dev.astype(np.float64) * 2.0 ** (-exp)).astype(np.float32).reshape(n, k)
+
+
+# ---------------------------------------------------------------------------
+# Device-side generators for full-size layers (bench).  Same recipes as above,
+# drawn with torch's seeded device RNG (Philox) so that 0.2-0.9 G-parameter
+# layers are produced in milliseconds.  Tests that compare with the oracle copy
+# the generated tensor back to the host; nothing here is method arithmetic.
+# ---------------------------------------------------------------------------
+
+
+def dev_gaussian_weights(seed: int, n: int, k: int, device, std: float = 0.02,
+                         outlier_p: float = 0.001, outlier_mult: float = 20.0):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    w = torch.randn((n, k), generator=g, device=device, dtype=torch.float32) * std
+    if outlier_p > 0:
+        mask = torch.rand((n, k), generator=g, device=device) < outlier_p
+        w = torch.where(mask, w * outlier_mult, w)
+    return w
+
+
+def dev_student_t_weights(seed: int, n: int, k: int, device, std: float = 0.015, nu: float = 5.0):
+    """Student-t(nu) as normal / sqrt(chi2_nu / nu), rescaled to ``std``."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    z = torch.randn((n, k), generator=g, device=device, dtype=torch.float32)
+    chi2 = torch.zeros((n, k), device=device, dtype=torch.float32)
+    for _ in range(int(nu)):
+        chi2 += torch.randn((n, k), generator=g, device=device, dtype=torch.float32) ** 2
+    t = z / torch.sqrt(chi2 / nu)
+    return t * (std / (nu / (nu - 2.0)) ** 0.5)
+
+
+def dev_bf16_normal(seed: int, shape, device, std: float = 1.0):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
+
+
+def dev_channel_mask(seed: int, n: int, device, frac4: float = 0.25):
+    import torch
+    idx = channel_mask(seed, n, frac4)
+    return torch.from_numpy(idx).to(device)

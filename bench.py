@@ -186,10 +186,10 @@ def build_workload(L, SI, torch, dev, R):
 
 def cpu_baseline():
     """The oracle, as it stands, on a bounded sample of the headline workload:
-    NF4 + double quantization of the 8B gate projection (14336 x 4096) and the
-    fp64 forward of all 4096 rows.  Reported in TFLOP/s of
-    the forward's 2*m*n*k over the whole oracle time (quantize + dequant +
-    matmul)."""
+    NF4 + double quantization of all 7 linears of the 8B layer, then the fp64
+    forward Y = X W^T and input gradient dX = dY W at m = 4096 for the 7
+    linears.  Reported in TFLOP/s of the matmuls' 2*m*n*k (forward and input
+    gradient) over the whole oracle time, quantization included."""
     import numpy as np
     import synth_inputs as SI
     from oracle import lbq_oracle as O
@@ -198,17 +198,24 @@ def cpu_baseline():
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
-    n, k, m = 14336, 4096, 4096
-    W = SI.gaussian_weights(SI.seed_of(3, 4, SI.SLOT_W), n, k, outlier_seed=SI.seed_of(3, 4, SI.SLOT_OUTLIER))
-    X = SI.bf16_normal(SI.seed_of(3, 4, SI.SLOT_X), (m, k))
-    t0 = time.perf_counter()
-    ref = O.quantize(W, "nf4", double_quant_on=True)
-    Y = O.linear_fwd(X, ref["w_exact"])
-    dt = time.perf_counter() - t0
-    assert Y.shape == (m, n)
-    return {"value": round(2.0 * m * n * k / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+    m = 4096
+    flop = 0.0
+    dt = 0.0
+    for i, (nm, (n, k)) in enumerate(SI.LLAMA3_8B.items()):
+        W = SI.gaussian_weights(SI.seed_of(3, i, SI.SLOT_W), n, k, outlier_seed=SI.seed_of(3, i, SI.SLOT_OUTLIER))
+        X = SI.bf16_normal(SI.seed_of(3, i, SI.SLOT_X), (m, k))
+        dY = SI.bf16_normal(SI.seed_of(3, i, SI.SLOT_DY), (m, n))
+        t0 = time.perf_counter()
+        ref = O.quantize(W, "nf4", double_quant_on=True)
+        Y = O.linear_fwd(X, ref["w_exact"])
+        dX = O.linear_bwd_dx(dY, ref["w_exact"])
+        dt += time.perf_counter() - t0
+        assert Y.shape == (m, n) and dX.shape == (m, k)
+        flop += 4.0 * m * n * k
+        del W, X, dY, ref, Y, dX
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"NF4+DQ quantize of the 8B gate projection ({n}x{k}) + fp64 forward of {m} of 4096 rows"}
+            "sample": "NF4+DQ quantize of the 7 LLaMA-3-8B linears + fp64 forward and input gradient at m=4096"}
 
 
 def main():

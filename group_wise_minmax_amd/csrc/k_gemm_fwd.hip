@@ -1,0 +1,344 @@
+// Prefill / training-size forward (m > 4): Y = X . deq(W)^T (+ LoRA) on bf16
+// MFMA (v_mfma_f32_16x16x32_bf16) with LDS-staged, double-buffered tiles.
+//
+// bitsandbytes FSDP-QLoRA guide, section 通过BitsAndBytesConfig配置: the packed
+// weight is unpacked and dequantized to the bf16 compute dtype inside the
+// kernel that does the matmul.  LoRA: same guide, step 4 (LoraConfig), and
+// "QLoRA技术在量化微调中的应用", section QLoRA技术原理 (low-rank adapters on a
+// frozen 4-bit base).
+//
+// Workgroup tile: BN rows of W (output columns) x BM rows of X, K-step 64.
+// Per K-step each thread fetches 32 packed codes of one W row (16 bytes for
+// 4-bit, 8 for 2-bit) and a few 16-byte chunks of X, dequantizes the codes in
+// registers (one fp32 FMA per weight, hardware bf16 packing) and writes both
+// into the idle half of a double-buffered LDS tile while the MFMAs consume the
+// other half; one barrier per K-step.  The packed weight is therefore read
+// from memory once per workgroup tile at a quarter (4-bit) or an eighth
+// (2-bit) of its bf16 size, and dequantized exactly once per tile.
+//
+// MFMA operand A is the weight (rows n), B is X (rows m); a lane's four
+// accumulators are four consecutive n of one m, so the epilogue writes 8
+// contiguous bytes of a Y row.  Workgroups are renumbered so that each of the
+// 8 XCDs (each with its own L2) receives a contiguous run of tiles, walked in
+// groups of 4 X-row tiles so that concurrently running tiles share operands.
+#include "lbq_device.h"
+
+namespace lbq {
+
+namespace {
+
+constexpr int BK = 64;       // K per LDS stage
+constexpr int LDK = BK + 8;  // padded LDS row (bf16 elements): conflict-free 16-byte reads
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+// 32 codes of one row -> 16 dwords of bf16 pairs (element 2i in the low half).
+// MinMax: (q - z) * s evaluated as fma(q, s, -z*s); NF4: c[code] * a.
+template <int KIND>
+__device__ __forceinline__ void dequant32(const u32x4_t& raw, float s, float zs,
+                                          const f32x2_t* __restrict__ pairlut, uint32_t out[16]) {
+  using T = WKindTraits<KIND>;
+  if constexpr (T::fmt == FMT_MINMAX && T::bits == 4) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t ev = (raw[d] >> 4) & 0x0F0F0F0Fu;  // elements 0,2,4,6 of the dword
+      const uint32_t od = raw[d] & 0x0F0F0F0Fu;         // elements 1,3,5,7
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float qe = (float)((ev >> (8 * i)) & 0xFFu);
+        const float qo = (float)((od >> (8 * i)) & 0xFFu);
+        out[4 * d + i] = cvt_pk_bf16(fmaf(qe, s, -zs), fmaf(qo, s, -zs));
+      }
+    }
+  } else if constexpr (T::fmt == FMT_MINMAX) {
+    // 2-bit: 32 codes in raw[0..1]; byte j of a dword holds elements 4j..4j+3, first in bits 7..6
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const uint32_t c0 = (raw[d] >> 6) & 0x03030303u, c1 = (raw[d] >> 4) & 0x03030303u;
+      const uint32_t c2 = (raw[d] >> 2) & 0x03030303u, c3 = raw[d] & 0x03030303u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float q0 = (float)((c0 >> (8 * j)) & 0xFFu), q1 = (float)((c1 >> (8 * j)) & 0xFFu);
+        const float q2 = (float)((c2 >> (8 * j)) & 0xFFu), q3 = (float)((c3 >> (8 * j)) & 0xFFu);
+        out[8 * d + 2 * j] = cvt_pk_bf16(fmaf(q0, s, -zs), fmaf(q1, s, -zs));
+        out[8 * d + 2 * j + 1] = cvt_pk_bf16(fmaf(q2, s, -zs), fmaf(q3, s, -zs));
+      }
+    }
+  } else {
+    // NF4: byte -> (c[hi nibble], c[lo nibble]) from an LDS table, times the block absmax s
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x2_t c = pairlut[(raw[d] >> (8 * i)) & 0xFFu];
+        out[4 * d + i] = cvt_pk_bf16(c[0] * s, c[1] * s);
+      }
+  }
+}
+
+// Tile index of workgroup `bid` among nx * ny tiles, XCD-aware and grouped.
+__device__ __forceinline__ void tile_of(int bid, int nx, int ny, int& tx, int& ty) {
+  const int total = nx * ny;
+  // hardware round-robins workgroups over 8 XCDs: give XCD j the contiguous
+  // logical range [j*per, (j+1)*per) (the remainder goes to the first XCDs)
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int per = total >> 3, rem = total & 7;
+  const int start = xcd * per + (xcd < rem ? xcd : rem);
+  int t = start + slot;
+  if (slot >= per + (xcd < rem ? 1 : 0)) t = bid;  // cannot happen for grid == total
+  constexpr int GM = 4;  // X-row tiles per group
+  const int group = t / (GM * nx);
+  const int first = group * GM;
+  const int gm = (ny - first) < GM ? (ny - first) : GM;
+  const int r = t - group * GM * nx;
+  ty = first + r % gm;
+  tx = r / gm;
+}
+
+template <int KIND, int BN, int BM, int WGN, int WGM, bool LORA>
+__global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint16_t* __restrict__ X,
+                                                          int m, uint16_t* __restrict__ Y,
+                                                          int64_t ldy,
+                                                          const int32_t* __restrict__ out_rows,
+                                                          LoraEpi lora, Nf4Table tab) {
+  using T = WKindTraits<KIND>;
+  constexpr int NT = WGN * WGM * 64;
+  static_assert(NT == 2 * BN, "each thread owns 32 codes of one W row per stage");
+  constexpr int WN = BN / WGN, WM = BM / WGM;
+  constexpr int TN = WN / 16, TM = WM / 16;
+  constexpr int XCH = BM * BK / 8 / NT;  // 16-byte X chunks per thread per stage
+  static_assert(XCH * NT * 8 == BM * BK, "X tile split");
+
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][BN * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][BM * LDK];
+  __shared__ f32x2_t pairlut[T::fmt == FMT_NF4 ? 256 : 1];
+  __shared__ float cbs[16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wn = wave % WGN, wm = wave / WGN;
+  const int li = lane & 15, lg = lane >> 4;
+  const int nx = (int)((w.n + BN - 1) / BN), ny = (m + BM - 1) / BM;
+  int tx, ty;
+  tile_of(blockIdx.x, nx, ny, tx, ty);
+  const int64_t n0 = (int64_t)tx * BN;
+  const int64_t m0 = (int64_t)ty * BM;
+  const int64_t K = w.k;
+  const int64_t KB = K * T::bits / 8;
+  const bool vec_store = out_rows == nullptr && (ldy & 3) == 0 &&
+                         (reinterpret_cast<uintptr_t>(Y) & 7) == 0;
+
+  if constexpr (T::fmt == FMT_NF4) {
+    // constant indices keep the kernel-argument table out of scratch memory
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (tid == i) cbs[i] = tab.c[i];
+    __syncthreads();
+    for (int b = tid; b < 256; b += NT) pairlut[b] = (f32x2_t){cbs[b >> 4], cbs[b & 15]};
+  }
+
+  // W ownership: row n0 + (tid >> 1), codes [32*(tid&1), +32) of each stage.
+  const int wrow = tid >> 1, whalf = tid & 1;
+  const int64_t wn_g = n0 + wrow;
+  const bool wrow_ok = wn_g < w.n;
+  const uint8_t* wsrc = w.packed + (wrow_ok ? wn_g : 0) * KB;
+  const int64_t gpr = K / T::group;  // groups (or absmax blocks) per row
+  const int64_t grow = (wrow_ok ? wn_g : 0) * gpr;
+
+  f32x4_t acc[TN][TM];
+#pragma unroll
+  for (int a = 0; a < TN; ++a)
+#pragma unroll
+    for (int b = 0; b < TM; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  u32x4_t xr[XCH];
+  u32x4_t wr;
+  float ws_s = 0.f, ws_zs = 0.f;  // scale and zero*scale of the owned group
+  auto load_stage = [&](int64_t kt) {
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int c = tid + NT * i;
+      const int row = c >> 3, col = (c & 7) * 8;
+      const int64_t mr = m0 + row;
+      xr[i] = (mr < m) ? *reinterpret_cast<const u32x4_t*>(X + mr * K + kt + col)
+                       : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    const int64_t kk = kt + 32 * whalf;
+    if (wrow_ok) {
+      if constexpr (T::bits == 4) {
+        wr = *reinterpret_cast<const u32x4_t*>(wsrc + kk / 2);
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(wsrc + kk / 4);
+        wr = u32x4_t{v.x, v.y, 0u, 0u};
+      }
+      const int64_t gi = grow + kk / T::group;
+      if constexpr (T::fmt == FMT_MINMAX) {
+        ws_s = w.scales[gi];
+        ws_zs = (float)w.zeros[gi] * ws_s;
+      } else {
+        ws_s = nf4_block_scale<T::dq>(w, gi);
+      }
+    } else {
+      wr = u32x4_t{0u, 0u, 0u, 0u};
+      ws_s = 0.f;
+      ws_zs = 0.f;
+    }
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int c = tid + NT * i;
+      const int row = c >> 3, col = (c & 7) * 8;
+      *reinterpret_cast<u32x4_t*>(&Xs[buf][row * LDK + col]) = xr[i];
+    }
+    uint32_t d[16];
+    dequant32<KIND>(wr, ws_s, ws_zs, pairlut, d);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x4_t*>(&Ws[buf][wrow * LDK + 32 * whalf + 8 * j]) =
+          u32x4_t{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]};
+  };
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < BK; ks += 32) {
+      u32x4_t af[TN], bf[TM];
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+        af[a] = *reinterpret_cast<const u32x4_t*>(&Ws[buf][(wn * WN + 16 * a + li) * LDK + ks + 8 * lg]);
+#pragma unroll
+      for (int b = 0; b < TM; ++b)
+        bf[b] = *reinterpret_cast<const u32x4_t*>(&Xs[buf][(wm * WM + 16 * b + li) * LDK + ks + 8 * lg]);
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b) acc[a][b] = mfma16x16x32(af[a], bf[b], acc[a][b]);
+    }
+  };
+
+  if constexpr (T::fmt == FMT_NF4) __syncthreads();  // pair table visible
+  load_stage(0);
+  store_stage(0);
+  if (BK < K) load_stage(BK);
+  __syncthreads();
+  int buf = 0;
+  for (int64_t kt = 0; kt < K; kt += BK) {
+    if (kt + BK < K) {
+      store_stage(buf ^ 1);
+      if (kt + 2 * BK < K) load_stage(kt + 2 * BK);
+    }
+    compute(buf);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  // LoRA slab: acc += B_lora[n][:] . T[m][:], r zero-padded to rp (multiple of 32).
+  if constexpr (LORA) {
+    for (int ks = 0; ks < lora.rp; ks += 32) {
+      u32x4_t af[TN], bf[TM];
+#pragma unroll
+      for (int a = 0; a < TN; ++a) {
+        const int64_t n = n0 + wn * WN + 16 * a + li;
+        uint32_t v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c0 = ks + 8 * lg + 2 * j;
+          uint32_t lo = 0, hi = 0;
+          if (n < w.n && c0 < lora.r) lo = lora.b[n * lora.r + c0];
+          if (n < w.n && c0 + 1 < lora.r) hi = lora.b[n * lora.r + c0 + 1];
+          v[j] = lo | (hi << 16);
+        }
+        af[a] = u32x4_t{v[0], v[1], v[2], v[3]};
+      }
+#pragma unroll
+      for (int b = 0; b < TM; ++b) {
+        const int64_t mr = m0 + wm * WM + 16 * b + li;
+        bf[b] = (mr < m) ? *reinterpret_cast<const u32x4_t*>(lora.t + mr * lora.rp + ks + 8 * lg)
+                         : u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b) acc[a][b] = mfma16x16x32(af[a], bf[b], acc[a][b]);
+    }
+  }
+
+  // Epilogue: lane holds D[n = base + 4*lg + i][m = base + li], i = 0..3.
+#pragma unroll
+  for (int a = 0; a < TN; ++a) {
+    const int64_t nb = n0 + wn * WN + 16 * a + 4 * lg;
+#pragma unroll
+    for (int b = 0; b < TM; ++b) {
+      const int64_t mr = m0 + wm * WM + 16 * b + li;
+      if (mr >= m) continue;
+      uint16_t* yrow = Y + mr * ldy;
+      if (vec_store && nb + 3 < w.n) {
+        uint2 v;
+        v.x = cvt_pk_bf16(acc[a][b][0], acc[a][b][1]);
+        v.y = cvt_pk_bf16(acc[a][b][2], acc[a][b][3]);
+        *reinterpret_cast<uint2*>(yrow + nb) = v;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t n = nb + i;
+          if (n < w.n) yrow[out_rows ? (int64_t)out_rows[n] : n] = (uint16_t)bf16_rne(acc[a][b][i]);
+        }
+      }
+    }
+  }
+}
+
+template <int KIND, int BN, int BM, int WGN, int WGM>
+hipError_t launch_cfg(const WView& w, const uint16_t* X, int64_t m, uint16_t* Y, int64_t ldy,
+                      const int32_t* out_rows, const LoraEpi& lora, const Nf4Table& tab,
+                      hipStream_t s) {
+  const int64_t tiles = ((w.n + BN - 1) / BN) * ((m + BM - 1) / BM);
+  const dim3 grid((unsigned)tiles), block(WGN * WGM * 64);
+  if (lora.t != nullptr) {
+    hipLaunchKernelGGL((k_gemm_fwd<KIND, BN, BM, WGN, WGM, true>), grid, block, 0, s, w, X, (int)m,
+                       Y, ldy, out_rows, lora, tab);
+  } else {
+    hipLaunchKernelGGL((k_gemm_fwd<KIND, BN, BM, WGN, WGM, false>), grid, block, 0, s, w, X, (int)m,
+                       Y, ldy, out_rows, lora, tab);
+  }
+  return hipGetLastError();
+}
+
+// Fraction of the chip's 256 CUs kept busy by `tiles` one-per-CU workgroups.
+double fill(int64_t tiles) {
+  const int64_t waves = (tiles + 255) / 256;
+  return (double)tiles / (double)(waves * 256);
+}
+
+template <int KIND>
+struct GemmFwdLauncher {
+  static hipError_t run(const WView& w, const uint16_t* X, int64_t m, uint16_t* Y, int64_t ldy,
+                        const int32_t* out_rows, const LoraEpi& lora, const Nf4Table& tab,
+                        hipStream_t s) {
+    // Pick the tile with the best (chip fill x per-tile efficiency).  The
+    // per-tile factors are the measured throughput of each shape relative to
+    // 256x256 (8 waves of 128x64) at full occupancy.
+    const int64_t t256x256 = ((w.n + 255) / 256) * ((m + 255) / 256);
+    const int64_t t256x128 = ((w.n + 255) / 256) * ((m + 127) / 128);
+    const int64_t t128x128 = ((w.n + 127) / 128) * ((m + 127) / 128);
+    const double e0 = fill(t256x256) * 1.00;
+    const double e1 = fill(t256x128) * 0.66;
+    const double e2 = fill(t128x128) * 0.45;
+    if (e0 >= e1 && e0 >= e2) return launch_cfg<KIND, 256, 256, 2, 4>(w, X, m, Y, ldy, out_rows, lora, tab, s);
+    if (e1 >= e2) return launch_cfg<KIND, 256, 128, 4, 2>(w, X, m, Y, ldy, out_rows, lora, tab, s);
+    return launch_cfg<KIND, 128, 128, 2, 2>(w, X, m, Y, ldy, out_rows, lora, tab, s);
+  }
+};
+
+}  // namespace
+
+hipError_t launch_gemm_fwd(WKind kind, const WView& w, const uint16_t* X, int64_t m,
+                           uint16_t* Y, int64_t ldy, const int32_t* out_rows,
+                           const LoraEpi& lora, const Nf4Table& tab, hipStream_t s) {
+  return dispatch_kind<GemmFwdLauncher>(kind, w, X, m, Y, ldy, out_rows, lora, tab, s);
+}
+
+}  // namespace lbq

@@ -1,0 +1,338 @@
+// Single-token decode (m == 1): y = deq(W) . x as a streaming GEMV, the
+// HBM-bound half of the frozen low-bit linear layer.
+//
+// The kernel that unpacks and dequantizes the weight to bf16 before the
+// matmul: bitsandbytes FSDP-QLoRA guide, section 通过BitsAndBytesConfig配置.
+// Weight formats: GreenBit.AI "只需单卡RTX 3090，低比特量化训练就能实现LLaMA-3
+// 8B全参微调", section 模型量化 (MinMax INT4 g128 / INT2 g64) and
+// "QLoRA技术在量化微调中的应用", section QLoRA技术原理 (NF4, double quantization).
+//
+// Structure.
+//  * Prologue: the workgroup stages x in LDS once, already arranged the way the
+//    dot products consume it (see below), with the sum of x over every 16-byte
+//    weight chunk (MinMax).  For NF4 it also builds a 256-entry byte -> pair of
+//    bf16 levels table, 32 copies so each lane of a 32-lane half reads its own
+//    bank.
+//  * Work: a wave owns a run of groups of R consecutive rows; each step loads
+//    CB 16-byte chunks of each of the R rows (lanes contiguous along K, 1 KiB
+//    of a row per chunk index), and the loads of step s+1 (weights, scales,
+//    zero points or block absmax) are issued before step s is computed, so
+//    memory and VALU work overlap within a wave.
+//  * MinMax: codes never become (q - z) * s per weight.  The low and high
+//    nibbles (or 2-bit crumbs) of a weight dword are split into byte vectors
+//    and v_perm_b32 lays two of them next to the byte 0x43, giving the bf16
+//    numbers 128 + q (exact for q < 128) as a pair; v_dot2_f32_bf16 multiplies
+//    the pair into x.  Per chunk (inside one group):
+//        sum x (q - z) s = s * (sum x (128 + q) - (128 + z) sum x).
+//    x is stored in LDS in the same pair order, so the weight side costs about
+//    1.4 VALU operations per code.
+//  * NF4: each packed byte (two codes) indexes the table and the pair is dotted
+//    with x; the block absmax scales the chunk sum.
+#include "lbq_device.h"
+
+namespace lbq {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kLutCopies = 32;
+constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1.0, 1.0)
+constexpr uint32_t k43 = 0x43434343u;    // bf16 exponent byte of 128
+
+// Bytes 0/1 (or 2/3) of `v`, each followed by 0x43: two bf16 numbers 128 + b.
+__device__ __forceinline__ uint32_t pair01(uint32_t v) { return perm_b32(k43, v, 0x04010400u); }
+__device__ __forceinline__ uint32_t pair23(uint32_t v) { return perm_b32(k43, v, 0x04030402u); }
+
+template <int KIND>
+struct Gemv1Traits {
+  using T = WKindTraits<KIND>;
+  static constexpr int CPC = 16 * 8 / T::bits;  // codes per 16-byte chunk
+  static constexpr int XD = CPC / 2;            // x dwords per chunk
+  static constexpr int XQ = XD / 4;             // 16-byte x quads per chunk
+  static constexpr int GRP = T::fmt == FMT_MINMAX ? T::group : 64;
+};
+
+// x chunk (natural order, XD dwords) -> the order the weight pairs use.
+template <int KIND>
+__device__ __forceinline__ void arrange_x(const uint32_t* xn, uint32_t* xo) {
+  using T = WKindTraits<KIND>;
+  if constexpr (T::fmt == FMT_NF4) {
+#pragma unroll
+    for (int j = 0; j < Gemv1Traits<KIND>::XD; ++j) xo[j] = xn[j];
+  } else if constexpr (T::bits == 4) {
+    // weight dword d (codes 8d..8d+7): pairs (1,3) (5,7) (0,2) (4,6)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t a = xn[4 * d], b = xn[4 * d + 1], c = xn[4 * d + 2], e = xn[4 * d + 3];
+      xo[4 * d + 0] = pair_hi(a, b);
+      xo[4 * d + 1] = pair_hi(c, e);
+      xo[4 * d + 2] = pair_lo(a, b);
+      xo[4 * d + 3] = pair_lo(c, e);
+    }
+  } else {
+    // weight dword d (codes 16d..16d+15), crumb t of byte j = code 4j + t:
+    // pairs (3,7) (11,15) (2,6) (10,14) (1,5) (9,13) (0,4) (8,12)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t* v = xn + 8 * d;  // v[i] = (x_{2i}, x_{2i+1})
+      xo[8 * d + 0] = pair_hi(v[1], v[3]);
+      xo[8 * d + 1] = pair_hi(v[5], v[7]);
+      xo[8 * d + 2] = pair_lo(v[1], v[3]);
+      xo[8 * d + 3] = pair_lo(v[5], v[7]);
+      xo[8 * d + 4] = pair_hi(v[0], v[2]);
+      xo[8 * d + 5] = pair_hi(v[4], v[6]);
+      xo[8 * d + 6] = pair_lo(v[0], v[2]);
+      xo[8 * d + 7] = pair_lo(v[4], v[6]);
+    }
+  }
+}
+
+// Dot product of one 16-byte weight chunk with its arranged x (two chains).
+template <int KIND>
+__device__ __forceinline__ float chunk_dot(const u32x4_t& wq, const uint32_t* xa,
+                                           const uint32_t* lut, int lane32) {
+  using T = WKindTraits<KIND>;
+  float p0 = 0.f, p1 = 0.f;
+  if constexpr (T::fmt == FMT_NF4) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t byte = (wq[d] >> (8 * j)) & 0xFFu;
+        const uint32_t e = lut[byte * kLutCopies + lane32];
+        if (j & 1) p1 = dot2_bf16(e, xa[4 * d + j], p1);
+        else p0 = dot2_bf16(e, xa[4 * d + j], p0);
+      }
+  } else if constexpr (T::bits == 4) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t lo = wq[d] & 0x0F0F0F0Fu;         // codes 1,3,5,7
+      const uint32_t hi = (wq[d] >> 4) & 0x0F0F0F0Fu;  // codes 0,2,4,6
+      p0 = dot2_bf16(pair01(lo), xa[4 * d + 0], p0);
+      p1 = dot2_bf16(pair23(lo), xa[4 * d + 1], p1);
+      p0 = dot2_bf16(pair01(hi), xa[4 * d + 2], p0);
+      p1 = dot2_bf16(pair23(hi), xa[4 * d + 3], p1);
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t c3 = wq[d] & 0x03030303u;
+      const uint32_t c2 = (wq[d] >> 2) & 0x03030303u;
+      const uint32_t c1 = (wq[d] >> 4) & 0x03030303u;
+      const uint32_t c0 = (wq[d] >> 6) & 0x03030303u;
+      p0 = dot2_bf16(pair01(c3), xa[8 * d + 0], p0);
+      p1 = dot2_bf16(pair23(c3), xa[8 * d + 1], p1);
+      p0 = dot2_bf16(pair01(c2), xa[8 * d + 2], p0);
+      p1 = dot2_bf16(pair23(c2), xa[8 * d + 3], p1);
+      p0 = dot2_bf16(pair01(c1), xa[8 * d + 4], p0);
+      p1 = dot2_bf16(pair23(c1), xa[8 * d + 5], p1);
+      p0 = dot2_bf16(pair01(c0), xa[8 * d + 6], p0);
+      p1 = dot2_bf16(pair23(c0), xa[8 * d + 7], p1);
+    }
+  }
+  return p0 + p1;
+}
+
+template <int KIND, int R, int CB>
+struct Step {
+  u32x4_t wq[CB][R];
+  float sc[CB][R];
+  int zq[CB][R];
+};
+
+template <int KIND, int R, int CB>
+__global__ __launch_bounds__(kThreads) void k_gemv1(WView w, const uint16_t* __restrict__ X,
+                                                   uint16_t* __restrict__ Y,
+                                                   const int32_t* __restrict__ out_rows,
+                                                   LoraEpi lora, Nf4Table tab, int gpw) {
+  using T = WKindTraits<KIND>;
+  using G = Gemv1Traits<KIND>;
+  constexpr int CPC = G::CPC, XD = G::XD, XQ = G::XQ, GRP = G::GRP;
+  extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int KB = (int)(w.k * T::bits / 8);  // bytes per packed row (< 2^24)
+  const int nchunk = KB / 16;               // 16-byte chunks per row
+  const int gpr = (int)(w.k / GRP);         // metadata entries per row
+
+  uint32_t* lut = smem;                                               // NF4 table
+  uint32_t* xq = smem + (T::fmt == FMT_NF4 ? 256 * kLutCopies : 0);  // [XQ][nchunk] quads
+  float* xsum = reinterpret_cast<float*>(xq + (size_t)XQ * 4 * nchunk);
+
+  // ---- work: groups of R rows, steps of CB chunk indices per lane ------------
+  const int ngroups = (int)((w.n + R - 1) / R);
+  const int cpl = (nchunk + 63) / 64;      // chunk indices per lane and row
+  const int nsteps = (cpl + CB - 1) / CB;  // steps per group
+  const int gw = blockIdx.x * (kThreads / 64) + wave;
+  const int g0 = gw * gpw;
+  const int g1 = min(g0 + gpw, ngroups);
+  const int total = g0 < g1 ? (g1 - g0) * nsteps : 0;
+  const int lane32 = lane & 31;
+
+  auto load = [&](int s, Step<KIND, R, CB>& st) {
+    const int g = g0 + s / nsteps, b = s % nsteps;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = min((int64_t)g * R + r, w.n - 1);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int c = min((b * CB + cb) * 64 + lane, nchunk - 1);  // clamped: always valid
+        st.wq[cb][r] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(w.packed + row * KB + (int64_t)c * 16));
+        const int64_t gi = row * gpr + (c * CPC) / GRP;
+        if constexpr (T::fmt == FMT_MINMAX) {
+          st.sc[cb][r] = w.scales[gi];
+          st.zq[cb][r] = w.zeros[gi];
+        } else {
+          st.sc[cb][r] = nf4_block_scale<T::dq>(w, gi);
+          st.zq[cb][r] = 0;
+        }
+      }
+    }
+  };
+
+  // The first step's weight loads go out before x is staged, so their latency
+  // overlaps the prologue.
+  Step<KIND, R, CB> A, B;
+  if (total > 0) load(0, A);
+
+  // ---- prologue: arranged x (and chunk sums) in LDS; NF4 table --------------
+  __shared__ float cbs[16];
+  if constexpr (T::fmt == FMT_NF4) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (tid == i) cbs[i] = tab.c[i];
+    lds_barrier();
+    for (int e = tid; e < 256 * kLutCopies; e += kThreads) {
+      const int b = e / kLutCopies;
+      lut[e] = (uint32_t)bf16_rne(cbs[b >> 4]) | ((uint32_t)bf16_rne(cbs[b & 15]) << 16);
+    }
+  }
+  for (int c = tid; c < nchunk; c += kThreads) {
+    uint32_t xn[XD], xo[XD];
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(X + (int64_t)c * CPC);
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+      const u32x4_t v = src[q];
+      xn[4 * q] = v[0]; xn[4 * q + 1] = v[1]; xn[4 * q + 2] = v[2]; xn[4 * q + 3] = v[3];
+    }
+    if constexpr (T::fmt == FMT_MINMAX) {
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < XD; j += 2) {
+        s0 = dot2_bf16(xn[j], kOnes, s0);
+        s1 = dot2_bf16(xn[j + 1], kOnes, s1);
+      }
+      xsum[c] = s0 + s1;
+    }
+    arrange_x<KIND>(xn, xo);
+#pragma unroll
+    for (int q = 0; q < XQ; ++q)
+      reinterpret_cast<u32x4_t*>(xq)[(size_t)q * nchunk + c] =
+          u32x4_t{xo[4 * q], xo[4 * q + 1], xo[4 * q + 2], xo[4 * q + 3]};
+  }
+  lds_barrier();
+
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+
+  auto compute = [&](int s, const Step<KIND, R, CB>& st) {
+    const int g = g0 + s / nsteps, b = s % nsteps;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c = (b * CB + cb) * 64 + lane;
+      const bool cok = c < nchunk;
+      const int cc = cok ? c : 0;
+      uint32_t xa[XD];
+#pragma unroll
+      for (int q = 0; q < XQ; ++q) {
+        const u32x4_t v = reinterpret_cast<const u32x4_t*>(xq)[(size_t)q * nchunk + cc];
+        xa[4 * q] = v[0]; xa[4 * q + 1] = v[1]; xa[4 * q + 2] = v[2]; xa[4 * q + 3] = v[3];
+      }
+      const float xs = (T::fmt == FMT_MINMAX) ? xsum[cc] : 0.f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float p = chunk_dot<KIND>(st.wq[cb][r], xa, lut, lane32);
+        const float sr = (cok && (int64_t)g * R + r < w.n) ? st.sc[cb][r] : 0.f;
+        if constexpr (T::fmt == FMT_MINMAX) {
+          acc[r] = fmaf(sr, fmaf(-(float)(128 + st.zq[cb][r]), xs, p), acc[r]);
+        } else {
+          acc[r] = fmaf(sr, p, acc[r]);
+        }
+      }
+    }
+    if (b == nsteps - 1) {  // group finished: LoRA term, wave reduction, store
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int64_t row = (int64_t)g * R + r;
+        if (lora.t != nullptr && lane < lora.r && row < w.n)
+          acc[r] = fmaf(bf16_lo(lora.t[lane]), bf16_lo(lora.b[row * lora.r + lane]), acc[r]);
+        const float v = wave_sum(acc[r]);
+        if (lane == 0 && row < w.n) Y[out_rows ? (int64_t)out_rows[row] : row] = (uint16_t)bf16_rne(v);
+        acc[r] = 0.f;
+      }
+    }
+  };
+
+  int s = 0;
+  if (total == 0) return;
+  for (;;) {
+    if (s + 1 < total) load(s + 1, B);
+    compute(s, A);
+    if (++s >= total) break;
+    if (s + 1 < total) load(s + 1, A);
+    compute(s, B);
+    if (++s >= total) break;
+  }
+}
+
+template <int KIND, int R, int CB>
+hipError_t launch_r(const WView& w, const uint16_t* X, uint16_t* Y, const int32_t* out_rows,
+                    const LoraEpi& lora, const Nf4Table& tab, hipStream_t s) {
+  using T = WKindTraits<KIND>;
+  using G = Gemv1Traits<KIND>;
+  const int64_t KB = w.k * T::bits / 8;
+  const int64_t nchunk = KB / 16;
+  const size_t lds = (T::fmt == FMT_NF4 ? 256 * kLutCopies * 4 : 0) + (size_t)nchunk * G::XD * 4 +
+                     (T::fmt == FMT_MINMAX ? (size_t)nchunk * 4 : 0);
+  const int64_t ngroups = (w.n + R - 1) / R;
+  const int64_t cpl = (nchunk + 63) / 64;
+  const int64_t nsteps = (cpl + CB - 1) / CB;
+  // About four steps per wave for overlap, but never fewer workgroups than CUs.
+  int64_t waves = (ngroups * nsteps + 3) / 4;
+  waves = waves < 1024 ? 1024 : waves;
+  waves = waves > ngroups ? ngroups : waves;
+  const int64_t gpw = (ngroups + waves - 1) / waves;
+  const int64_t nw = (ngroups + gpw - 1) / gpw;
+  const dim3 grid((unsigned)((nw + 3) / 4));
+  hipLaunchKernelGGL((k_gemv1<KIND, R, CB>), grid, dim3(kThreads), lds, s, w, X, Y, out_rows, lora,
+                     tab, (int)gpw);
+  return hipGetLastError();
+}
+
+template <int KIND>
+struct Gemv1Launcher {
+  static hipError_t run(const WView& w, const uint16_t* X, uint16_t* Y, const int32_t* out_rows,
+                        const LoraEpi& lora, const Nf4Table& tab, hipStream_t s) {
+    return launch_r<KIND, 2, (WKindTraits<KIND>::fmt == FMT_NF4 ? 2 : 1)>(w, X, Y, out_rows, lora, tab, s);
+  }
+};
+
+}  // namespace
+
+size_t gemv1_lds_bytes(WKind kind, int64_t k) {
+  const bool nf4 = kind == WK_NF4 || kind == WK_NF4DQ;
+  const int bits = (kind == WK_I2G64 || kind == WK_I2G128) ? 2 : 4;
+  const int64_t nchunk = k * bits / 8 / 16;
+  const int xd = 16 * 8 / bits / 2;
+  return (nf4 ? 256 * kLutCopies * 4 : 0) + (size_t)(nchunk * xd * 4) + (nf4 ? 0 : (size_t)nchunk * 4);
+}
+
+hipError_t launch_gemv1(WKind kind, const WView& w, const uint16_t* X, uint16_t* Y,
+                        const int32_t* out_rows, const LoraEpi& lora, const Nf4Table& tab,
+                        hipStream_t s) {
+  return dispatch_kind<Gemv1Launcher>(kind, w, X, Y, out_rows, lora, tab, s);
+}
+
+}  // namespace lbq

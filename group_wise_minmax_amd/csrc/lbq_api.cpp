@@ -176,6 +176,19 @@ lbq_status check_fwd_common(const lbq_desc* desc, const lbq_qtensor* q, const ui
 
 int32_t round_rank(int32_t r) { return (r + 31) / 32 * 32; }
 
+// Forward kernel choice: single-token decode streams the weight with x staged
+// in LDS; other decode sizes use the multi-row GEMV; larger m the MFMA tiles.
+hipError_t dispatch_fwd(const lbq_desc* desc, const lbq::WView& w, const uint16_t* X, int64_t m,
+                        uint16_t* Y, int64_t ldy, const int32_t* out_rows,
+                        const lbq::LoraEpi& lora, hipStream_t s) {
+  const lbq::WKind kind = kind_of(desc);
+  if (m == 1 && lbq::gemv1_lds_bytes(kind, desc->k) <= 65536)
+    return lbq::launch_gemv1(kind, w, X, Y, out_rows, lora, nf4_table(), s);
+  if (m <= lbq::kGemvMaxM)
+    return lbq::launch_gemv(kind, w, X, m, Y, ldy, out_rows, lora, nf4_table(), s);
+  return lbq::launch_gemm_fwd(kind, w, X, m, Y, ldy, out_rows, lora, nf4_table(), s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -234,10 +247,7 @@ lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint
   const lbq::LoraEpi none{nullptr, nullptr, 0, 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
   const lbq::WView w = view_of(desc, q);
-  hipError_t e = (m <= lbq::kGemvMaxM)
-                     ? lbq::launch_gemv(kind_of(desc), w, X, m, Y, ldy, q->out_rows, none, nf4_table(), s)
-                     : lbq::launch_gemm_fwd(kind_of(desc), w, X, m, Y, ldy, q->out_rows, none, nf4_table(), s);
-  return hip_status(e, "lbq_linear_fwd");
+  return hip_status(dispatch_fwd(desc, w, X, m, Y, ldy, q->out_rows, none, s), "lbq_linear_fwd");
 }
 
 lbq_status lbq_linear_bwd_dx(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* dY,
@@ -283,10 +293,7 @@ lbq_status lbq_lora_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16
   if (e != hipSuccess) return hip_status(e, "lbq_lora_fwd (adapter product)");
   const lbq::LoraEpi lora{T, B, r, rp};
   const lbq::WView w = view_of(desc, q);
-  e = (m <= lbq::kGemvMaxM)
-          ? lbq::launch_gemv(kind_of(desc), w, X, m, Y, ldy, q->out_rows, lora, nf4_table(), s)
-          : lbq::launch_gemm_fwd(kind_of(desc), w, X, m, Y, ldy, q->out_rows, lora, nf4_table(), s);
-  return hip_status(e, "lbq_lora_fwd");
+  return hip_status(dispatch_fwd(desc, w, X, m, Y, ldy, q->out_rows, lora, s), "lbq_lora_fwd");
 }
 
 void lbq_nf4_codebook(float out[16]) {

@@ -49,6 +49,30 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const u32x4_t& a, const u32x4_t&
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Sum over the 64 lanes of a wave, result in every lane: four DPP steps
+// (xor 1, xor 2 within quads, half-row and row mirrors) and two cross-row
+// exchanges.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141>(v);  // row_half_mirror
+  v += dpp_f32<0x140>(v);  // row_mirror
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Barrier that orders LDS accesses only: global loads issued before it stay
+// in flight (a full __syncthreads() would wait for them as well).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt untouched
+  __builtin_amdgcn_s_barrier();
+}
+
 // Integer code of element i (0..7) from the packed bytes of a chunk of 8
 // consecutive codes: 4-bit chunks are one dword (4 bytes), 2-bit chunks a
 // 16-bit word.  Even element -> high nibble (4-bit); first element -> bits

@@ -56,6 +56,12 @@ hipError_t launch_dequant(WKind kind, const WView& w, uint16_t* out, const Nf4Ta
 hipError_t launch_gemv(WKind kind, const WView& w, const uint16_t* X, int64_t m,
                        uint16_t* Y, int64_t ldy, const int32_t* out_rows,
                        const LoraEpi& lora, const Nf4Table& tab, hipStream_t s);
+// m == 1 decode GEMV with x staged in LDS; usable when gemv1_lds_bytes(kind, k)
+// fits in 64 KiB of dynamic LDS.
+size_t gemv1_lds_bytes(WKind kind, int64_t k);
+hipError_t launch_gemv1(WKind kind, const WView& w, const uint16_t* X, uint16_t* Y,
+                        const int32_t* out_rows, const LoraEpi& lora, const Nf4Table& tab,
+                        hipStream_t s);
 hipError_t launch_gemm_fwd(WKind kind, const WView& w, const uint16_t* X, int64_t m,
                            uint16_t* Y, int64_t ldy, const int32_t* out_rows,
                            const LoraEpi& lora, const Nf4Table& tab, hipStream_t s);

@@ -177,16 +177,25 @@ lbq_status check_fwd_common(const lbq_desc* desc, const lbq_qtensor* q, const ui
 int32_t round_rank(int32_t r) { return (r + 31) / 32 * 32; }
 
 // Forward kernel choice: single-token decode streams the weight with x staged
-// in LDS; other decode sizes use the multi-row GEMV; larger m the MFMA tiles.
+// in LDS (or the multi-row GEMV when x does not fit); 2 <= m <= 64 uses the
+// small-batch MFMA kernel (fp32 partials in `ws` when K is split); larger m
+// the LDS-tiled MFMA GEMM.
 hipError_t dispatch_fwd(const lbq_desc* desc, const lbq::WView& w, const uint16_t* X, int64_t m,
                         uint16_t* Y, int64_t ldy, const int32_t* out_rows,
-                        const lbq::LoraEpi& lora, hipStream_t s) {
+                        const lbq::LoraEpi& lora, void* ws, hipStream_t s) {
   const lbq::WKind kind = kind_of(desc);
   if (m == 1 && lbq::gemv1_lds_bytes(kind, desc->k) <= 65536)
     return lbq::launch_gemv1(kind, w, X, Y, out_rows, lora, nf4_table(), s);
-  if (m <= lbq::kGemvMaxM)
-    return lbq::launch_gemv(kind, w, X, m, Y, ldy, out_rows, lora, nf4_table(), s);
+  if (m == 1) return lbq::launch_gemv(kind, w, X, m, Y, ldy, out_rows, lora, nf4_table(), s);
+  if (m <= lbq::kSkinnyMaxM)
+    return lbq::launch_skinny(kind, w, X, m, Y, ldy, out_rows, static_cast<float*>(ws), lora,
+                              nf4_table(), s);
   return lbq::launch_gemm_fwd(kind, w, X, m, Y, ldy, out_rows, lora, nf4_table(), s);
+}
+
+size_t fwd_workspace(const lbq_desc* desc, int64_t m, bool lora) {
+  if (m >= 2 && m <= lbq::kSkinnyMaxM) return lbq::skinny_workspace_bytes(desc->n, desc->k, m, lora);
+  return 0;
 }
 
 }  // namespace
@@ -232,22 +241,24 @@ lbq_status lbq_dequant(const lbq_desc* desc, const lbq_qtensor* q, uint16_t* W_b
 }
 
 size_t lbq_linear_workspace_bytes(const lbq_desc* desc, int64_t m) {
-  (void)desc;
-  (void)m;
-  return 0;
+  if (check_desc(desc) != LBQ_OK || m < 1) return 0;
+  return fwd_workspace(desc, m, false);
 }
 
 lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X,
                           int64_t m, uint16_t* Y, int64_t ldy, void* workspace, size_t ws_bytes,
                           void* stream) {
-  (void)workspace;
-  (void)ws_bytes;
   lbq_status st = check_fwd_common(desc, q, X, m, Y, ldy);
   if (st != LBQ_OK || m == 0) return st == LBQ_OK ? ok() : st;
+  const size_t need = fwd_workspace(desc, m, false);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
+    return fail(LBQ_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  if (need > 0 && !aligned(workspace, 16)) return fail(LBQ_E_ALIGN, "workspace must be 16-byte aligned");
   const lbq::LoraEpi none{nullptr, nullptr, 0, 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
   const lbq::WView w = view_of(desc, q);
-  return hip_status(dispatch_fwd(desc, w, X, m, Y, ldy, q->out_rows, none, s), "lbq_linear_fwd");
+  return hip_status(dispatch_fwd(desc, w, X, m, Y, ldy, q->out_rows, none, workspace, s),
+                    "lbq_linear_fwd");
 }
 
 lbq_status lbq_linear_bwd_dx(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* dY,
@@ -266,10 +277,15 @@ lbq_status lbq_linear_bwd_dx(const lbq_desc* desc, const lbq_qtensor* q, const u
                     "lbq_linear_bwd_dx");
 }
 
+// LoRA workspace: bf16 T = sigma X A^T [m][rp], then (16-byte aligned) the
+// small-batch kernel's fp32 partials when that kernel runs.
+static size_t lora_t_bytes(int64_t m, int32_t r) {
+  return ((size_t)m * (size_t)round_rank(r) * sizeof(uint16_t) + 15) / 16 * 16;
+}
+
 size_t lbq_lora_workspace_bytes(const lbq_desc* desc, int64_t m, int32_t r) {
-  (void)desc;
-  if (m <= 0 || r < 1) return 0;
-  return (size_t)m * (size_t)round_rank(r) * sizeof(uint16_t);
+  if (check_desc(desc) != LBQ_OK || m <= 0 || r < 1) return 0;
+  return lora_t_bytes(m, r) + fwd_workspace(desc, m, true);
 }
 
 lbq_status lbq_lora_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X, int64_t m,
@@ -293,7 +309,8 @@ lbq_status lbq_lora_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16
   if (e != hipSuccess) return hip_status(e, "lbq_lora_fwd (adapter product)");
   const lbq::LoraEpi lora{T, B, r, rp};
   const lbq::WView w = view_of(desc, q);
-  return hip_status(dispatch_fwd(desc, w, X, m, Y, ldy, q->out_rows, lora, s), "lbq_lora_fwd");
+  void* part = static_cast<uint8_t*>(workspace) + lora_t_bytes(m, r);
+  return hip_status(dispatch_fwd(desc, w, X, m, Y, ldy, q->out_rows, lora, part, s), "lbq_lora_fwd");
 }
 
 void lbq_nf4_codebook(float out[16]) {

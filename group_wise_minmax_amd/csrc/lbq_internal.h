@@ -62,6 +62,14 @@ size_t gemv1_lds_bytes(WKind kind, int64_t k);
 hipError_t launch_gemv1(WKind kind, const WView& w, const uint16_t* X, uint16_t* Y,
                         const int32_t* out_rows, const LoraEpi& lora, const Nf4Table& tab,
                         hipStream_t s);
+// 2 <= m <= kSkinnyMaxM: MFMA with the weight streamed once; K split over
+// skinny_splits() workgroups whose fp32 partials (workspace) are summed by a
+// second kernel when more than one range is used or a LoRA term is added.
+int skinny_splits(int64_t n, int64_t k, int64_t m);
+size_t skinny_workspace_bytes(int64_t n, int64_t k, int64_t m, bool lora);
+hipError_t launch_skinny(WKind kind, const WView& w, const uint16_t* X, int64_t m, uint16_t* Y,
+                         int64_t ldy, const int32_t* out_rows, float* part, const LoraEpi& lora,
+                         const Nf4Table& tab, hipStream_t s);
 hipError_t launch_gemm_fwd(WKind kind, const WView& w, const uint16_t* X, int64_t m,
                            uint16_t* Y, int64_t ldy, const int32_t* out_rows,
                            const LoraEpi& lora, const Nf4Table& tab, hipStream_t s);
@@ -70,7 +78,9 @@ hipError_t launch_bwd_dx(WKind kind, const WView& w, const uint16_t* dY, int64_t
 hipError_t launch_lora_t(const uint16_t* X, int64_t m, int64_t k, const uint16_t* A,
                          int32_t r, int32_t rp, float sigma, uint16_t* T, hipStream_t s);
 
-// Largest m served by the wavefront-reduction GEMV; larger m use MFMA tiles.
+// Largest m served by the wavefront-reduction GEMV (used for m == 1 when x does
+// not fit the LDS-staged kernel) and by the small-batch MFMA kernel.
 constexpr int64_t kGemvMaxM = 4;
+constexpr int64_t kSkinnyMaxM = 64;
 
 }  // namespace lbq

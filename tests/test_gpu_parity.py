@@ -84,7 +84,7 @@ def test_quantize_config0_is_deterministic(L):
 
 # ------------------------------------------------------------------ forward
 
-FWD_M = [1, 2, 3, 4, 5, 8, 16, 100, 130]
+FWD_M = [1, 2, 3, 4, 5, 8, 16, 20, 33, 64, 65, 100, 130]
 
 
 @pytest.mark.parametrize("fmtspec", FORMATS, ids=FMT_IDS)

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint1
   // W ownership: row n0 + (tid >> 1), codes [32*(tid&1), +32) of each stage.
   const int wrow = tid >> 1, whalf = tid & 1;
   const int64_t wn_g = n0 + wrow;
-  const bool wrow_ok = wn_g < w.n;
+  const bool wrow_ok = wn_g < w.n;  // rows past n read row 0 and are zeroed
   const uint8_t* wsrc = w.packed + (wrow_ok ? wn_g : 0) * KB;
   const int64_t gpr = K / T::group;  // groups (or absmax blocks) per row
   const int64_t grow = (wrow_ok ? wn_g : 0) * gpr;
@@ -155,37 +155,37 @@ __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint1
 #pragma unroll
     for (int b = 0; b < TM; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Prefetch registers.  Loads are unconditional from clamped addresses (no
+  // branches, so they are all in flight at once); the metadata stays raw here
+  // and is combined in store_stage, one K-step later, so no wave waits on it.
   u32x4_t xr[XCH];
   u32x4_t wr;
-  float ws_s = 0.f, ws_zs = 0.f;  // scale and zero*scale of the owned group
+  float md_s = 0.f;  // scale (MinMax), absmax or second-level scale (NF4)
+  int md_i = 0;      // zero point (MinMax) or int8 absmax code (NF4 + DQ)
   auto load_stage = [&](int64_t kt) {
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int c = tid + NT * i;
       const int row = c >> 3, col = (c & 7) * 8;
-      const int64_t mr = m0 + row;
-      xr[i] = (mr < m) ? *reinterpret_cast<const u32x4_t*>(X + mr * K + kt + col)
-                       : u32x4_t{0u, 0u, 0u, 0u};
+      const int64_t mr = min(m0 + row, (int64_t)m - 1);
+      xr[i] = *reinterpret_cast<const u32x4_t*>(X + mr * K + kt + col);
     }
     const int64_t kk = kt + 32 * whalf;
-    if (wrow_ok) {
-      if constexpr (T::bits == 4) {
-        wr = *reinterpret_cast<const u32x4_t*>(wsrc + kk / 2);
-      } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(wsrc + kk / 4);
-        wr = u32x4_t{v.x, v.y, 0u, 0u};
-      }
-      const int64_t gi = grow + kk / T::group;
-      if constexpr (T::fmt == FMT_MINMAX) {
-        ws_s = w.scales[gi];
-        ws_zs = (float)w.zeros[gi] * ws_s;
-      } else {
-        ws_s = nf4_block_scale<T::dq>(w, gi);
-      }
+    if constexpr (T::bits == 4) {
+      wr = *reinterpret_cast<const u32x4_t*>(wsrc + kk / 2);
     } else {
-      wr = u32x4_t{0u, 0u, 0u, 0u};
-      ws_s = 0.f;
-      ws_zs = 0.f;
+      const uint2 v = *reinterpret_cast<const uint2*>(wsrc + kk / 4);
+      wr = u32x4_t{v.x, v.y, 0u, 0u};
+    }
+    const int64_t gi = grow + kk / T::group;
+    if constexpr (T::fmt == FMT_MINMAX) {
+      md_s = w.scales[gi];
+      md_i = w.zeros[gi];
+    } else if constexpr (T::dq) {
+      md_i = w.absmax_q[gi];
+      md_s = w.absmax_scale[gi >> 8];
+    } else {
+      md_s = w.absmax[gi];
     }
   };
   auto store_stage = [&](int buf) {
@@ -196,6 +196,16 @@ __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint1
       *reinterpret_cast<u32x4_t*>(&Xs[buf][row * LDK + col]) = xr[i];
     }
     uint32_t d[16];
+    float ws_s, ws_zs = 0.f;
+    if constexpr (T::fmt == FMT_MINMAX) {
+      ws_s = md_s;
+      ws_zs = (float)md_i * md_s;
+    } else if constexpr (T::dq) {
+      ws_s = (float)md_i * md_s;
+    } else {
+      ws_s = md_s;
+    }
+    if (!wrow_ok) ws_s = ws_zs = 0.f;  // rows past n contribute zeros
     dequant32<KIND>(wr, ws_s, ws_zs, pairlut, d);
 #pragma unroll
     for (int j = 0; j < 4; ++j)

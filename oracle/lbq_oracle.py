@@ -31,7 +31,7 @@ Sources (cited by page title and section):
         0.37 bit per parameter; gradients flow through the frozen 4-bit model
         into low-rank adapters.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * MinMax is asymmetric with an integer zero point; the group range always
     includes 0 (lo = min(0, min w), hi = max(0, max w)); a scale that comes
     out as 0 (an all-zero group) is replaced by 1.

@@ -19,7 +19,7 @@ def main():
         f.write("# Written by tests/golden/make_golden.py from oracle.nf4_codebook():\n")
         f.write("# normal quantiles at evenly spaced probabilities, exact zero, scaled to [-1, 1]\n")
         f.write("# (\"QLoRA技术在量化微调中的应用\", section QLoRA技术原理: NF4 suits normally\n")
-        f.write("# distributed weights; the exact construction is a reading, see DESIGN.md).\n")
+        f.write("# distributed weights; the exact construction is a reading of that remark).\n")
         for v in c:
             f.write("%08x %.9g\n" % (int(v.view("uint32")), float(v)))
 

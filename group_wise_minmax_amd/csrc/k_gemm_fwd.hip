@@ -27,14 +27,12 @@ namespace lbq {
 
 namespace {
 
-constexpr int BK = 64;       // K per LDS stage
-constexpr int LDK = BK + 8;  // padded LDS row (bf16 elements): conflict-free 16-byte reads
+constexpr int BK = 64;  // K per LDS stage: one tile row is 128 bytes
 
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
-}
+// Byte offset of logical 16-byte chunk c (0..7) of row r in a tile whose
+// chunks are stored at position c ^ (r & 7): conflict-free for the MFMA
+// operand reads (16 rows x 4 chunk columns) and for whole-row writes.
+__device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * 128u + 16u * (c ^ (r & 7u)); }
 
 // 32 codes of one row -> 16 dwords of bf16 pairs (element 2i in the low half).
 // MinMax: (q - z) * s evaluated as fma(q, s, -z*s); NF4: c[code] * a.
@@ -80,25 +78,6 @@ __device__ __forceinline__ void dequant32(const u32x4_t& raw, float s, float zs,
   }
 }
 
-// Tile index of workgroup `bid` among nx * ny tiles, XCD-aware and grouped.
-__device__ __forceinline__ void tile_of(int bid, int nx, int ny, int& tx, int& ty) {
-  const int total = nx * ny;
-  // hardware round-robins workgroups over 8 XCDs: give XCD j the contiguous
-  // logical range [j*per, (j+1)*per) (the remainder goes to the first XCDs)
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int per = total >> 3, rem = total & 7;
-  const int start = xcd * per + (xcd < rem ? xcd : rem);
-  int t = start + slot;
-  if (slot >= per + (xcd < rem ? 1 : 0)) t = bid;  // cannot happen for grid == total
-  constexpr int GM = 4;  // X-row tiles per group
-  const int group = t / (GM * nx);
-  const int first = group * GM;
-  const int gm = (ny - first) < GM ? (ny - first) : GM;
-  const int r = t - group * GM * nx;
-  ty = first + r % gm;
-  tx = r / gm;
-}
-
 template <int KIND, int BN, int BM, int WGN, int WGM, bool LORA>
 __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint16_t* __restrict__ X,
                                                           int m, uint16_t* __restrict__ Y,
@@ -113,8 +92,8 @@ __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint1
   constexpr int XCH = BM * BK / 8 / NT;  // 16-byte X chunks per thread per stage
   static_assert(XCH * NT * 8 == BM * BK, "X tile split");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][BN * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][BN * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][BM * BK];
   __shared__ f32x2_t pairlut[T::fmt == FMT_NF4 ? 256 : 1];
   __shared__ float cbs[16];
 
@@ -192,8 +171,7 @@ __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint1
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int c = tid + NT * i;
-      const int row = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<u32x4_t*>(&Xs[buf][row * LDK + col]) = xr[i];
+      *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(&Xs[buf][0]) + swz(c >> 3, c & 7)) = xr[i];
     }
     uint32_t d[16];
     float ws_s, ws_zs = 0.f;
@@ -209,19 +187,25 @@ __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint1
     dequant32<KIND>(wr, ws_s, ws_zs, pairlut, d);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x4_t*>(&Ws[buf][wrow * LDK + 32 * whalf + 8 * j]) =
+      *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(&Ws[buf][0]) + swz(wrow, 4 * whalf + j)) =
           u32x4_t{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]};
   };
+  // Operand rows of this lane: W rows wn*WN + 16*a + li, X rows wm*WM + 16*b + li
+  // (row & 7 == li & 7), chunk 4*(ks/32) + lg of each.
+  const uint32_t a_base = swz(wn * WN + li, lg), a_base1 = swz(wn * WN + li, 4 + lg);
+  const uint32_t b_base = swz(wm * WM + li, lg), b_base1 = swz(wm * WM + li, 4 + lg);
   auto compute = [&](int buf) {
+    const char* wsb = reinterpret_cast<const char*>(&Ws[buf][0]);
+    const char* xsb = reinterpret_cast<const char*>(&Xs[buf][0]);
 #pragma unroll
     for (int ks = 0; ks < BK; ks += 32) {
       u32x4_t af[TN], bf[TM];
 #pragma unroll
       for (int a = 0; a < TN; ++a)
-        af[a] = *reinterpret_cast<const u32x4_t*>(&Ws[buf][(wn * WN + 16 * a + li) * LDK + ks + 8 * lg]);
+        af[a] = *reinterpret_cast<const u32x4_t*>(wsb + (ks ? a_base1 : a_base) + a * 16 * 128);
 #pragma unroll
       for (int b = 0; b < TM; ++b)
-        bf[b] = *reinterpret_cast<const u32x4_t*>(&Xs[buf][(wm * WM + 16 * b + li) * LDK + ks + 8 * lg]);
+        bf[b] = *reinterpret_cast<const u32x4_t*>(xsb + (ks ? b_base1 : b_base) + b * 16 * 128);
 #pragma unroll
       for (int a = 0; a < TN; ++a)
 #pragma unroll

@@ -166,6 +166,12 @@ lbq_status check_fwd_common(const lbq_desc* desc, const lbq_qtensor* q, const ui
   if ((st = check_qtensor(desc, q)) != LBQ_OK) return st;
   if (m < 0 || m > (int64_t(1) << 31) - 1) return fail(LBQ_E_SHAPE, "m must be in [0, 2^31) (got %lld)", (long long)m);
   if (m == 0) return LBQ_OK;
+  // The GEMM addresses X and the weight with 32-bit byte offsets (plus one
+  // tile of slack past the last row).
+  if ((uint64_t)(m + 256) * (uint64_t)desc->k * 2 >= (uint64_t(1) << 32) ||
+      (uint64_t)(desc->n + 256) * (uint64_t)desc->k >= (uint64_t(1) << 32))
+    return fail(LBQ_E_SHAPE, "(m + 256) * k * 2 and (n + 256) * k must be below 2^32 (m %lld, n %lld, k %lld)",
+                (long long)m, (long long)desc->n, (long long)desc->k);
   if (X == nullptr || Y == nullptr) return fail(LBQ_E_NULL, "X and Y must be non-NULL");
   if (!aligned(X, 16)) return fail(LBQ_E_ALIGN, "X must be 16-byte aligned");
   if (!aligned(Y, 2)) return fail(LBQ_E_ALIGN, "Y must be 2-byte aligned");
@@ -179,7 +185,7 @@ int32_t round_rank(int32_t r) { return (r + 31) / 32 * 32; }
 // Forward kernel choice: single-token decode streams the weight with x staged
 // in LDS (or the multi-row GEMV when x does not fit); 2 <= m <= 64 uses the
 // small-batch MFMA kernel (fp32 partials in `ws` when K is split); larger m
-// the LDS-tiled MFMA GEMM.
+// the MFMA GEMM with the dequantized weight tile in LDS.
 hipError_t dispatch_fwd(const lbq_desc* desc, const lbq::WView& w, const uint16_t* X, int64_t m,
                         uint16_t* Y, int64_t ldy, const int32_t* out_rows,
                         const lbq::LoraEpi& lora, void* ws, hipStream_t s) {

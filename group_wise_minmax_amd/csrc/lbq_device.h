@@ -19,7 +19,15 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Two fp32 -> one dword of two bf16 (lo in bits 15..0).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> one dword of two bf16 with the hardware RNE conversion
+// (v_cvt_pk_bf16_f32); lo in bits 15..0.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+// Two fp32 -> one dword of two bf16 (lo in bits 15..0), software RNE.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return bf16_rne(lo) | (bf16_rne(hi) << 16);
 }
@@ -84,6 +92,25 @@ __device__ __forceinline__ int code_of(uint32_t word, int i) {
   } else {
     return (word >> (8 * (i >> 2) + 6 - 2 * (i & 3))) & 0x3;
   }
+}
+
+// Tile index of workgroup `bid` among nx * ny tiles, XCD-aware and grouped.
+__device__ __forceinline__ void tile_of(int bid, int nx, int ny, int& tx, int& ty) {
+  const int total = nx * ny;
+  // hardware round-robins workgroups over 8 XCDs: give XCD j the contiguous
+  // logical range [j*per, (j+1)*per) (the remainder goes to the first XCDs)
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int per = total >> 3, rem = total & 7;
+  const int start = xcd * per + (xcd < rem ? xcd : rem);
+  int t = start + slot;
+  if (slot >= per + (xcd < rem ? 1 : 0)) t = bid;  // cannot happen for grid == total
+  constexpr int GM = 4;  // X-row tiles per group
+  const int group = t / (GM * nx);
+  const int first = group * GM;
+  const int gm = (ny - first) < GM ? (ny - first) : GM;
+  const int r = t - group * GM * nx;
+  ty = first + r % gm;
+  tx = r / gm;
 }
 
 template <int K> struct WKindTraits;

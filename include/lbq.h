@@ -156,10 +156,13 @@ size_t lbq_linear_workspace_bytes(const lbq_desc* desc, int64_t m);
  *   out_rows[j] : j, with w_hat the dequantized weight and fp32 accumulation.
  * X: bf16 [m][k] (device); Y: bf16 [m][ldy] (device), ldy >= n (or >
  * max(out_rows)); only the n addressed columns of each row are written.
- * m >= 0 (m == 0 is an empty batch: nothing is read or written).  `workspace` must hold lbq_linear_workspace_bytes(desc, m) bytes
- * (may be NULL when that is 0).  Decode sizes (small m) run a wavefront-
- * reduction GEMV streaming the packed weight; larger m run an LDS-tiled
- * bf16-MFMA GEMM that dequantizes tiles in registers. */
+ * m >= 0 (m == 0 is an empty batch: nothing is read or written);
+ * (m + 256) * k * 2 and (n + 256) * k must be below 2^32 (LBQ_E_SHAPE
+ * otherwise: the GEMM uses 32-bit byte offsets).  `workspace` must hold
+ * lbq_linear_workspace_bytes(desc, m) bytes (may be NULL when that is 0).
+ * m == 1 runs a GEMV that streams the packed weight once; 2 <= m <= 64 a
+ * bf16-MFMA kernel that streams it once with K split over workgroups; larger
+ * m a bf16-MFMA GEMM whose weight tiles are dequantized once into LDS. */
 lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X,
                           int64_t m, uint16_t* Y, int64_t ldy, void* workspace,
                           size_t ws_bytes, void* stream);

@@ -9,43 +9,90 @@ namespace {
 // ---------------------------------------------------------------------------
 // Input gradient dX = dY . deq(W) ("QLoRA技术在量化微调中的应用", section
 // QLoRA技术原理: backpropagation through the frozen quantized weights).
-// The reduction runs over n, while the packed weight is contiguous along k:
-// each thread dequantizes 8 codes of 4 consecutive rows and writes them to LDS
-// transposed (k-major, 4 n per 8-byte store), so MFMA operand A (rows k) reads
-// 8 consecutive n with one 16-byte LDS load.  B is dY (rows m).
+//
+// Workgroup tile: BKO columns of dX (k) x BM rows (m), reduction over n in
+// stages of 64, WGK x WGM waves.  MFMA operand A is the dequantized weight
+// transposed (rows k, 8 consecutive n per lane), B is dY (rows m), so each
+// lane's accumulators are four consecutive k of one m and the epilogue writes
+// 8 contiguous bytes of a dX row.
+//
+// The packed weight is contiguous along k, the reduction runs along n: per
+// stage a thread loads 8 codes (one k-chunk) of 4 consecutive rows n,
+// dequantizes them and writes, for each of its 8 k, the 4 values of the rows
+// as one 8-byte LDS store into the k-major tile.  The n-quad is the lane's low
+// 4 bits, which (with the row swizzle) keeps these column writes
+// bank-conflict free.  dY chunks are staged like X in the forward GEMM.  Both
+// tiles are double-buffered with one barrier per stage, and every global load
+// goes through a buffer resource (reads past the end return zeros), so rows
+// past n, m or k need no guards.
 // ---------------------------------------------------------------------------
-constexpr int BNR = 64;        // reduction (n) per stage
-constexpr int LDN = BNR + 8;   // padded LDS row
+constexpr int BNR = 64;  // reduction (n) per stage = one 128-byte LDS row
 
-template <int KIND, int BM, int BKO>
-__global__ __launch_bounds__(256) void k_bwd_dx(WView w, const uint16_t* __restrict__ dY, int m,
-                                               uint16_t* __restrict__ dX, Nf4Table tab) {
+template <int KIND, int BKO, int BM, int WGK, int WGM>
+__global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_t* __restrict__ dY,
+                                                        int m, uint16_t* __restrict__ dX,
+                                                        Nf4Table tab) {
   using T = WKindTraits<KIND>;
-  static_assert(BKO == 128, "16 chunks of 8 codes per row");
-  constexpr int WK = BKO / 2, WM = BM / 2;
+  constexpr int NT = WGK * WGM * 64;
+  constexpr int WK = BKO / WGK, WM = BM / WGM;
   constexpr int TK = WK / 16, TM = WM / 16;
-  constexpr int DCH = BM * BNR / 8 / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t Wt[BKO * LDN];
-  __shared__ __attribute__((aligned(16))) uint16_t Ds[BM * LDN];
-  __shared__ float cb[16];
+  constexpr int KCH = BKO / 8;                 // 8-code k-chunks per tile row
+  static_assert(KCH * 16 == NT, "a thread owns one k-chunk of 4 rows n per stage");
+  constexpr int DCH = BM * BNR / 8 / NT;       // 16-byte dY chunks per thread per stage
+  static_assert(DCH * NT * 8 == BM * BNR, "dY tile split");
+
+  __shared__ __attribute__((aligned(16))) uint16_t Wt[2][BKO * BNR];
+  __shared__ __attribute__((aligned(16))) uint16_t Ds[2][BM * BNR];
+  __shared__ f32x2_t pairlut[T::fmt == FMT_NF4 ? 256 : 1];
+  __shared__ float cbs[16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wk = wave & 1, wm = wave >> 1;
+  const int wk = wave % WGK, wm = wave / WGK;
   const int li = lane & 15, lg = lane >> 4;
-  const int64_t k0 = (int64_t)blockIdx.x * BKO;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
+  const int nx = (int)((w.k + BKO - 1) / BKO), ny = (m + BM - 1) / BM;
+  int tx, ty;
+  tile_of(blockIdx.x, nx, ny, tx, ty);
+  const int64_t k0 = (int64_t)tx * BKO;
+  const int64_t m0 = (int64_t)ty * BM;
   const int64_t K = w.k, N = w.n;
   const int64_t KB = K * T::bits / 8;
+  const int64_t gpr = K / T::group;
 
   if constexpr (T::fmt == FMT_NF4) {
-    if (tid < 16) cb[tid] = tab.c[tid];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (tid == i) cbs[i] = tab.c[i];
+    __syncthreads();
+    for (int b = tid; b < 256; b += NT) pairlut[b] = (f32x2_t){cbs[b >> 4], cbs[b & 15]};
   }
 
-  // W ownership: rows 4*(tid>>4) .. +3 of the stage, codes [8*(tid&15), +8) of the k tile.
-  const int quad = tid >> 4, chunk = tid & 15;
-  const int64_t kc = k0 + 8 * chunk;
-  const bool kc_ok = kc < K;
+  const int64_t nblk = N * gpr;
+  const __amdgpu_buffer_rsrc_t r_w = make_rsrc(w.packed, N * KB);
+  const __amdgpu_buffer_rsrc_t r_d = make_rsrc(dY, (int64_t)m * N * 2);
+  __amdgpu_buffer_rsrc_t r_s, r_z;
+  if constexpr (T::fmt == FMT_MINMAX) {
+    r_s = make_rsrc(w.scales, nblk * 4);
+    r_z = make_rsrc(w.zeros, nblk);
+  } else if constexpr (T::dq) {
+    r_s = make_rsrc(w.absmax_scale, ((nblk + 255) >> 8) * 4);
+    r_z = make_rsrc(w.absmax_q, nblk);
+  } else {
+    r_s = make_rsrc(w.absmax, nblk * 4);
+    r_z = r_s;
+  }
+
+  // Weight ownership: rows 4*q .. 4*q+3 of each stage, codes [8*c, +8) of the
+  // k tile, with q = lane & 15 and c = (NT/64 waves) x 4 chunks.
+  const int q = lane & 15, c = 4 * wave + lg;
+  const int64_t kc = k0 + 8 * c;
+  const uint32_t w_voff = (uint32_t)(4 * q * KB + kc * T::bits / 8);
+  const uint32_t g_voff = (uint32_t)(4 * q * gpr + kc / T::group);
+  // dY chunks of this thread: chunk ci = tid + NT*i -> row ci >> 3, chunk ci & 7.
+  const uint32_t d_voff = (uint32_t)(((m0 + (tid >> 3)) * N + 8 * (tid & 7)) * 2);
+  char* const wt_base = reinterpret_cast<char*>(&Wt[0][0]);
+  char* const ds_base = reinterpret_cast<char*>(&Ds[0][0]);
+  constexpr uint32_t WT_BUF = BKO * BNR * 2, DS_BUF = BM * BNR * 2;
 
   f32x4_t acc[TK][TM];
 #pragma unroll
@@ -55,88 +102,109 @@ __global__ __launch_bounds__(256) void k_bwd_dx(WView w, const uint16_t* __restr
 
   u32x4_t dr[DCH];
   uint32_t wr[4];
+  float md_s[4];
+  int md_i[4];
   auto load_stage = [&](int64_t nt) {
 #pragma unroll
     for (int i = 0; i < DCH; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 3, col = (c & 7) * 8;
-      const int64_t mr = m0 + row;
-      dr[i] = (mr < m && nt + col < N)
-                  ? *reinterpret_cast<const u32x4_t*>(dY + mr * N + nt + col)
-                  : u32x4_t{0u, 0u, 0u, 0u};
+      // chunk tid + NT*i: NT/8 rows further down per i
+      const int so = (int)((NT / 8) * i * N * 2 + nt * 2);
+      dr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_d, d_voff, so, 0));
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t n = nt + 4 * quad + r;
-      if (n < N && kc_ok) {
-        if constexpr (T::bits == 4) {
-          wr[r] = *reinterpret_cast<const uint32_t*>(w.packed + n * KB + kc / 2);
-        } else {
-          wr[r] = *reinterpret_cast<const uint16_t*>(w.packed + n * KB + kc / 4);
-        }
+      const int so = (int)((nt + r) * KB);
+      if constexpr (T::bits == 4) {
+        wr[r] = __builtin_amdgcn_raw_buffer_load_b32(r_w, w_voff, so, 0);
       } else {
-        wr[r] = 0u;
+        wr[r] = __builtin_amdgcn_raw_buffer_load_b16(r_w, w_voff, so, 0);
+      }
+      const int go = (int)((nt + r) * gpr);
+      if constexpr (T::fmt == FMT_MINMAX) {
+        md_s[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, g_voff * 4, go * 4, 0));
+        md_i[r] = __builtin_amdgcn_raw_buffer_load_b8(r_z, g_voff, go, 0);
+      } else if constexpr (T::dq) {
+        md_i[r] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(r_z, g_voff, go, 0);
+        md_s[r] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(r_s, ((g_voff + (uint32_t)go) >> 8) * 4, 0, 0));
+      } else {
+        md_s[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, g_voff * 4, go * 4, 0));
       }
     }
   };
-  auto store_stage = [&](int64_t nt) {
+  auto store_stage = [&](int buf) {
+    char* ds = ds_base + buf * DS_BUF;
 #pragma unroll
     for (int i = 0; i < DCH; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<u32x4_t*>(&Ds[row * LDN + col]) = dr[i];
+      const int ci = tid + NT * i;
+      *reinterpret_cast<u32x4_t*>(ds + swz(ci >> 3, ci & 7)) = dr[i];
     }
+    // v[r][j]: row 4q + r, code j of the chunk
     float v[4][8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t n = nt + 4 * quad + r;
-      if (n < N && kc_ok) {
-        if constexpr (T::fmt == FMT_MINMAX) {
-          const int64_t gi = n * (K / T::group) + kc / T::group;
-          const float s = w.scales[gi];
-          const int z = w.zeros[gi];
+      if constexpr (T::fmt == FMT_MINMAX) {
+        const float s = md_s[r], zs = (float)md_i[r] * md_s[r];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) v[r][j] = (float)(code_of<T::bits>(wr[r], j) - z) * s;
-        } else {
-          const float a = nf4_block_scale<T::dq>(w, n * (K / 64) + kc / 64);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) v[r][j] = cb[code_of<4>(wr[r], j)] * a;
-        }
+        for (int j = 0; j < 8; ++j) v[r][j] = fmaf((float)code_of<T::bits>(wr[r], j), s, -zs);
       } else {
+        const float a = T::dq ? (float)md_i[r] * md_s[r] : md_s[r];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[r][j] = 0.f;
+        for (int j = 0; j < 4; ++j) {
+          const f32x2_t cc = pairlut[(wr[r] >> (8 * j)) & 0xFFu];
+          v[r][2 * j] = cc[0] * a;
+          v[r][2 * j + 1] = cc[1] * a;
+        }
       }
     }
+    char* wt = wt_base + buf * WT_BUF;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       uint2 p;
-      p.x = pack_bf16x2(v[0][j], v[1][j]);
-      p.y = pack_bf16x2(v[2][j], v[3][j]);
-      *reinterpret_cast<uint2*>(&Wt[(8 * chunk + j) * LDN + 4 * quad]) = p;
+      p.x = cvt_pk_bf16(v[0][j], v[1][j]);
+      p.y = cvt_pk_bf16(v[2][j], v[3][j]);
+      *reinterpret_cast<uint2*>(wt + swz(8 * c + j, q >> 1) + 8 * (q & 1)) = p;
     }
   };
-
-  __syncthreads();
-  load_stage(0);
-  for (int64_t nt = 0; nt < N; nt += BNR) {
-    __syncthreads();
-    store_stage(nt);
-    __syncthreads();
-    if (nt + BNR < N) load_stage(nt + BNR);
+  // Operand rows: Wt rows wk*WK + 16*a + li, Ds rows wm*WM + 16*b + li; chunk
+  // 4*(ks/32) + lg of each.
+  const uint32_t a_base = swz(wk * WK + li, lg), a_base1 = swz(wk * WK + li, 4 + lg);
+  const uint32_t b_base = swz(wm * WM + li, lg), b_base1 = swz(wm * WM + li, 4 + lg);
+  auto compute = [&](int buf) {
+    const char* wt = wt_base + buf * WT_BUF;
+    const char* ds = ds_base + buf * DS_BUF;
 #pragma unroll
     for (int ks = 0; ks < BNR; ks += 32) {
       u32x4_t af[TK], bf[TM];
 #pragma unroll
       for (int a = 0; a < TK; ++a)
-        af[a] = *reinterpret_cast<const u32x4_t*>(&Wt[(wk * WK + 16 * a + li) * LDN + ks + 8 * lg]);
+        af[a] = *reinterpret_cast<const u32x4_t*>(wt + (ks ? a_base1 : a_base) + a * 16 * 128);
 #pragma unroll
       for (int b = 0; b < TM; ++b)
-        bf[b] = *reinterpret_cast<const u32x4_t*>(&Ds[(wm * WM + 16 * b + li) * LDN + ks + 8 * lg]);
+        bf[b] = *reinterpret_cast<const u32x4_t*>(ds + (ks ? b_base1 : b_base) + b * 16 * 128);
 #pragma unroll
       for (int a = 0; a < TK; ++a)
 #pragma unroll
         for (int b = 0; b < TM; ++b) acc[a][b] = mfma16x16x32(af[a], bf[b], acc[a][b]);
     }
+  };
+
+  // n % 8 == 0, so a 64-wide stage past N only meets zero weights (buffer
+  // reads past the end) times finite dY values.
+  if constexpr (T::fmt == FMT_NF4) __syncthreads();  // pair table visible
+  load_stage(0);
+  store_stage(0);
+  if (BNR < N) load_stage(BNR);
+  __syncthreads();
+  int buf = 0;
+  for (int64_t nt = 0; nt < N; nt += BNR) {
+    if (nt + BNR < N) {
+      store_stage(buf ^ 1);
+      if (nt + 2 * BNR < N) load_stage(nt + 2 * BNR);
+    }
+    compute(buf);
+    __syncthreads();
+    buf ^= 1;
   }
 
 #pragma unroll
@@ -148,21 +216,36 @@ __global__ __launch_bounds__(256) void k_bwd_dx(WView w, const uint16_t* __restr
       const int64_t mr = m0 + wm * WM + 16 * b + li;
       if (mr >= m) continue;
       uint2 v;
-      v.x = pack_bf16x2(acc[a][b][0], acc[a][b][1]);
-      v.y = pack_bf16x2(acc[a][b][2], acc[a][b][3]);
+      v.x = cvt_pk_bf16(acc[a][b][0], acc[a][b][1]);
+      v.y = cvt_pk_bf16(acc[a][b][2], acc[a][b][3]);
       *reinterpret_cast<uint2*>(dX + mr * K + kb) = v;
     }
   }
+}
+
+template <int KIND, int BKO, int BM, int WGK, int WGM>
+hipError_t launch_bwd_cfg(const WView& w, const uint16_t* dY, int64_t m, uint16_t* dX,
+                          const Nf4Table& tab, hipStream_t s) {
+  const int64_t tiles = ((w.k + BKO - 1) / BKO) * ((m + BM - 1) / BM);
+  hipLaunchKernelGGL((k_bwd_dx<KIND, BKO, BM, WGK, WGM>), dim3((unsigned)tiles), dim3(WGK * WGM * 64),
+                     0, s, w, dY, (int)m, dX, tab);
+  return hipGetLastError();
+}
+
+double bwd_fill(int64_t tiles) {
+  const int64_t waves = (tiles + 255) / 256;
+  return (double)tiles / (double)(waves * 256);
 }
 
 template <int KIND>
 struct BwdLauncher {
   static hipError_t run(const WView& w, const uint16_t* dY, int64_t m, uint16_t* dX,
                         const Nf4Table& tab, hipStream_t s) {
-    constexpr int BM = 128, BKO = 128;
-    const dim3 grid((unsigned)((w.k + BKO - 1) / BKO), (unsigned)((m + BM - 1) / BM));
-    hipLaunchKernelGGL((k_bwd_dx<KIND, BM, BKO>), grid, dim3(256), 0, s, w, dY, (int)m, dX, tab);
-    return hipGetLastError();
+    // 256 x 256 tiles (8 waves of 128 x 64) unless they leave most of the chip idle.
+    const int64_t t256 = ((w.k + 255) / 256) * ((m + 255) / 256);
+    const int64_t t128 = ((w.k + 127) / 128) * ((m + 127) / 128);
+    if (bwd_fill(t256) >= 0.5 * bwd_fill(t128)) return launch_bwd_cfg<KIND, 256, 256, 2, 4>(w, dY, m, dX, tab, s);
+    return launch_bwd_cfg<KIND, 128, 128, 2, 2>(w, dY, m, dX, tab, s);
   }
 };
 

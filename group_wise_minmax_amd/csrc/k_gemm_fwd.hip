@@ -29,10 +29,6 @@ namespace {
 
 constexpr int BK = 64;  // K per LDS stage: one tile row is 128 bytes
 
-// Byte offset of logical 16-byte chunk c (0..7) of row r in a tile whose
-// chunks are stored at position c ^ (r & 7): conflict-free for the MFMA
-// operand reads (16 rows x 4 chunk columns) and for whole-row writes.
-__device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * 128u + 16u * (c ^ (r & 7u)); }
 
 // 32 codes of one row -> 16 dwords of bf16 pairs (element 2i in the low half).
 // MinMax: (q - z) * s evaluated as fma(q, s, -z*s); NF4: c[code] * a.

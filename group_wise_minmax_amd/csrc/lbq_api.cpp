@@ -278,6 +278,10 @@ lbq_status lbq_linear_bwd_dx(const lbq_desc* desc, const lbq_qtensor* q, const u
   if (dY == nullptr || dX == nullptr) return fail(LBQ_E_NULL, "dY and dX must be non-NULL");
   if (!aligned(dY, 16) || !aligned(dX, 16)) return fail(LBQ_E_ALIGN, "dY and dX must be 16-byte aligned");
   if (desc->n % 8 != 0) return fail(LBQ_E_SHAPE, "lbq_linear_bwd_dx needs n %% 8 == 0 (got %lld)", (long long)desc->n);
+  if ((uint64_t)(m + 256) * (uint64_t)desc->n * 2 >= (uint64_t(1) << 32) ||
+      (uint64_t)(desc->n + 256) * (uint64_t)desc->k >= (uint64_t(1) << 32))
+    return fail(LBQ_E_SHAPE, "(m + 256) * n * 2 and (n + 256) * k must be below 2^32 (m %lld, n %lld, k %lld)",
+                (long long)m, (long long)desc->n, (long long)desc->k);
   return hip_status(lbq::launch_bwd_dx(kind_of(desc), view_of(desc, q), dY, m, dX, nf4_table(),
                                        static_cast<hipStream_t>(stream)),
                     "lbq_linear_bwd_dx");

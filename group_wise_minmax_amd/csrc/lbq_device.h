@@ -94,6 +94,18 @@ __device__ __forceinline__ int code_of(uint32_t word, int i) {
   }
 }
 
+// LDS tiles of 64 bf16 (128 bytes) per row store the eight 16-byte chunks of
+// row r at position c ^ (r & 7).  Byte offset of logical chunk c of row r.
+// Measured on gfx950 this keeps MFMA operand reads (16 rows x 4 chunk columns,
+// ds_read_b128) and whole-row or 8-byte column writes free of bank conflicts.
+__device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * 128u + 16u * (c ^ (r & 7u)); }
+
+// Raw buffer resource over `bytes` bytes at p; loads at or past `bytes`
+// return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+
 // Tile index of workgroup `bid` among nx * ny tiles, XCD-aware and grouped.
 __device__ __forceinline__ void tile_of(int bid, int nx, int ny, int& tx, int& ty) {
   const int total = nx * ny;

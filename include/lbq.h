@@ -170,8 +170,9 @@ lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint
 /* Input gradient through the frozen weight, dX = dY . deq(W) ([QL]
  * QLoRA技术原理: gradients pass through the frozen 4-bit model):
  *   dX[i][k] = bf16( sum_j dY[i][j] * w_hat[j][k] ), fp32 accumulation.
- * dY: bf16 [m][n]; dX: bf16 [m][k] (device).  out_rows must be NULL
- * (LBQ_E_UNSUPPORTED otherwise). */
+ * dY: bf16 [m][n]; dX: bf16 [m][k] (device), both 16-byte aligned; n % 8
+ * == 0; (m + 256) * n * 2 and (n + 256) * k below 2^32 (LBQ_E_SHAPE
+ * otherwise).  out_rows must be NULL (LBQ_E_UNSUPPORTED otherwise). */
 lbq_status lbq_linear_bwd_dx(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* dY,
                              int64_t m, uint16_t* dX, void* stream);
 

@@ -14,8 +14,11 @@ One step is one pass of the whole hot path over a LLaMA-3-8B decoder layer
   fwd_m4096    NF4-DQ forward at m = 4096 (2 x 2048 tokens)       <- headline
   lora_m4096   NF4-DQ forward + rank-16 LoRA on q and v at m = 4096
   bwd_m4096    NF4-DQ input gradient dX = dY deq(W) at m = 4096
-  chmix_70b    70B-shaped layer, per-channel 25% INT4 g128 / 75% INT2 g64,
-               forward at m = 1 and m = 1024
+  chmix_70b_m1     70B-shaped layer, per-channel 25% INT4 g128 / 75% INT2 g64
+                   (two launches per linear, each scattering its rows of Y), m = 1
+  chmix_70b_m1024  the same at m = 1024
+  copy_1g      (only with --phases) a plain 1 GiB device-to-device copy, the
+               reference kernel for scaling hardware byte counters
 
 Each phase is captured once as a HIP graph (torch.cuda.CUDAGraph) and replayed,
 so the timed region holds device work only; HIP events on the launch stream
@@ -52,7 +55,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, units_per_launch: float):
+def load_traffic(kernel: str, units_per_launch=None):
     """HBM bytes per launch from committed rocprofv3 --pmc summaries, or None
     when no summary exists or the kernels changed since it was taken."""
     path = os.path.join(PROFILES, "traffic.json")
@@ -66,10 +69,60 @@ def load_traffic(kernel: str, units_per_launch: float):
     return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
-def build_workload(L, SI, torch, dev, R):
-    """Allocate every input/output once; return the phase list."""
+ALL_PHASES = ("quant_int4", "quant_nf4dq", "dequant", "gemv_m1", "gemv_m16", "gemm_m2048",
+              "fwd_m4096", "lora_m4096", "bwd_m4096", "chmix_70b_m1", "chmix_70b_m1024")
+EXTRA_PHASES = ("copy_1g",)  # opt-in: plain 1 GiB device copy (counter calibration)
+
+
+# Kernel-name patterns (rocprofv3 demangled names) of the kernels whose HBM
+# traffic the JSON line reports.
+TRAFFIC_KERNELS = {
+    "fwd_m4096_big": "k_gemm_fwd<5, 256, 256, 2, 4, false>",
+    "gemv_m1": "k_gemv1<0,",
+}
+
+
+def write_traffic(fetch_csv: str, write_csv: str) -> dict:
+    """profiles/traffic.json from two rocprofv3 --pmc runs (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch) of `--phases fwd_m4096,gemv_m1,copy_1g
+    --eager`.  Each counter is scaled by what it reads for the plain 1 GiB
+    device copy (2^30 bytes read and 2^30 written)."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return vals
+
+    fe, wr = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    copy_f = max(v for k, vs in fe.items() if "copy" in k.lower() for v in vs)
+    copy_w = max(v for k, vs in wr.items() if "copy" in k.lower() for v in vs)
+    cf, cw = float(1 << 30) / copy_f, float(1 << 30) / copy_w
+    out = {"kernel_source_hash": kernel_source_hash(),
+           "copy_1GiB": {"FETCH_SIZE_bytes": copy_f, "WRITE_SIZE_bytes": copy_w, "fetch_factor": cf, "write_factor": cw},
+           "kernels": {}}
+    for key, pat in TRAFFIC_KERNELS.items():
+        f = [v for k, vs in fe.items() if pat in k for v in vs]
+        w = [v for k, vs in wr.items() if pat in k for v in vs]
+        if f and w:
+            fb, wb = sum(f) / len(f) * cf, sum(w) / len(w) * cw
+            out["kernels"][key] = {"dispatches": len(f), "fetch_bytes_per_launch": round(fb),
+                                   "write_bytes_per_launch": round(wb), "hbm_bytes_per_launch": round(fb + wb)}
+    with open(os.path.join(PROFILES, "traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    return out
+
+
+def build_workload(L, SI, torch, dev, R, want):
+    """Allocate the inputs/outputs of the phases in `want` once; return the phase list."""
     shapes = SI.LLAMA3_8B
     names = list(shapes)
+    K_of = {nm: shapes[nm][1] for nm in names}
+    N_of = {nm: shapes[nm][0] for nm in names}
+    need = lambda *ph: any(p in want for p in ph)
     W = {nm: SI.dev_gaussian_weights(SI.seed_of(2, i, SI.SLOT_W), *shapes[nm], dev)
          for i, nm in enumerate(names)}
     q4 = {nm: L.QuantizedWeight.empty(L.make_desc("minmax", *shapes[nm], 4, 128), dev) for nm in names}
@@ -77,50 +130,62 @@ def build_workload(L, SI, torch, dev, R):
     for nm in names:
         L.lbq_quantize(W[nm], "minmax", 4, 128, out=q4[nm])
         L.lbq_quantize(W[nm], "nf4", double_quant=True, out=qn[nm])
+    if not need("quant_int4", "quant_nf4dq"):
+        W = None
     # R independent copies of the INT4 layer for the decode phases
     copies = [q4]
-    for _ in range(R - 1):
-        copies.append({nm: L.QuantizedWeight(q.desc, q.packed.clone(), q.scales.clone(), q.zeros.clone())
-                       for nm, q in q4.items()})
-    wbf = {nm: torch.empty(shapes[nm], dtype=torch.bfloat16, device=dev) for nm in names}
-    K_of = {nm: shapes[nm][1] for nm in names}
-    N_of = {nm: shapes[nm][0] for nm in names}
-    X1 = {nm: SI.dev_bf16_normal(SI.seed_of(2, i, SI.SLOT_X), (1, K_of[nm]), dev) for i, nm in enumerate(names)}
-    X16 = {nm: SI.dev_bf16_normal(SI.seed_of(2, i, SI.SLOT_X) + 100, (16, K_of[nm]), dev) for i, nm in enumerate(names)}
-    X2k = {nm: SI.dev_bf16_normal(SI.seed_of(2, i, SI.SLOT_X) + 200, (2048, K_of[nm]), dev) for i, nm in enumerate(names)}
-    X4k = {nm: SI.dev_bf16_normal(SI.seed_of(3, i, SI.SLOT_X), (4096, K_of[nm]), dev) for i, nm in enumerate(names)}
-    dY = {nm: SI.dev_bf16_normal(SI.seed_of(3, i, SI.SLOT_DY), (4096, N_of[nm]), dev) for i, nm in enumerate(names)}
-    Y1 = {nm: torch.empty((1, N_of[nm]), dtype=torch.bfloat16, device=dev) for nm in names}
-    Y16 = {nm: torch.empty((16, N_of[nm]), dtype=torch.bfloat16, device=dev) for nm in names}
-    Y2k = {nm: torch.empty((2048, N_of[nm]), dtype=torch.bfloat16, device=dev) for nm in names}
-    Y4k = {nm: torch.empty((4096, N_of[nm]), dtype=torch.bfloat16, device=dev) for nm in names}
-    dX = {nm: torch.empty((4096, K_of[nm]), dtype=torch.bfloat16, device=dev) for nm in names}
+    if need("gemv_m1", "gemv_m16"):
+        for _ in range(R - 1):
+            copies.append({nm: L.QuantizedWeight(q.desc, q.packed.clone(), q.scales.clone(), q.zeros.clone())
+                           for nm, q in q4.items()})
+    wbf = {nm: torch.empty(shapes[nm], dtype=torch.bfloat16, device=dev) for nm in names} if need("dequant") else {}
+
+    def xs(cfg, slot, off, m, dim_of, on):
+        if not on:
+            return {}
+        return {nm: SI.dev_bf16_normal(SI.seed_of(cfg, i, slot) + off, (m, dim_of[nm]), dev) for i, nm in enumerate(names)}
+
+    def ys(m, dim_of, on):
+        return {nm: torch.empty((m, dim_of[nm]), dtype=torch.bfloat16, device=dev) for nm in names} if on else {}
+
+    X1, Y1 = xs(2, SI.SLOT_X, 0, 1, K_of, need("gemv_m1")), ys(1, N_of, need("gemv_m1"))
+    X16, Y16 = xs(2, SI.SLOT_X, 100, 16, K_of, need("gemv_m16")), ys(16, N_of, need("gemv_m16"))
+    X2k, Y2k = xs(2, SI.SLOT_X, 200, 2048, K_of, need("gemm_m2048")), ys(2048, N_of, need("gemm_m2048"))
+    X4k = xs(3, SI.SLOT_X, 0, 4096, K_of, need("fwd_m4096", "lora_m4096"))
+    Y4k = ys(4096, N_of, need("fwd_m4096"))
+    dY, dX = xs(3, SI.SLOT_DY, 0, 4096, N_of, need("bwd_m4096")), ys(4096, K_of, need("bwd_m4096"))
     lora = {}
-    for nm in ("q", "v"):
-        i = names.index(nm)
-        A = SI.dev_bf16_normal(SI.seed_of(3, i, SI.SLOT_A), (16, K_of[nm]), dev, std=0.01)
-        B = SI.dev_bf16_normal(SI.seed_of(3, i, SI.SLOT_B), (N_of[nm], 16), dev, std=0.01)
-        ws = torch.empty(L.lbq_lora_workspace_bytes(qn[nm], 4096, 16), dtype=torch.uint8, device=dev)
-        lora[nm] = (A, B, ws, torch.empty((4096, N_of[nm]), dtype=torch.bfloat16, device=dev))
+    if need("lora_m4096"):
+        for nm in ("q", "v"):
+            i = names.index(nm)
+            A = SI.dev_bf16_normal(SI.seed_of(3, i, SI.SLOT_A), (16, K_of[nm]), dev, std=0.01)
+            B = SI.dev_bf16_normal(SI.seed_of(3, i, SI.SLOT_B), (N_of[nm], 16), dev, std=0.01)
+            ws = torch.empty(L.lbq_lora_workspace_bytes(qn[nm], 4096, 16), dtype=torch.uint8, device=dev)
+            lora[nm] = (A, B, ws, torch.empty((4096, N_of[nm]), dtype=torch.bfloat16, device=dev))
 
     # 70B-shaped channel-mix layer (quantized once at setup)
     s70 = SI.LLAMA3_70B
     cm = []
-    for i, nm in enumerate(s70):
-        n, k = s70[nm]
-        w = SI.dev_gaussian_weights(SI.seed_of(4, i, SI.SLOT_W), n, k, dev)
-        rows4 = SI.dev_channel_mask(SI.seed_of(4, i, SI.SLOT_CHMASK), n, dev)
-        mask = torch.zeros(n, dtype=torch.bool, device=dev)
-        mask[rows4.long()] = True
-        rows2 = torch.nonzero(~mask).flatten().to(torch.int32)
-        a = L.lbq_quantize(w[rows4.long()].contiguous(), "minmax", 4, 128)
-        b = L.lbq_quantize(w[rows2.long()].contiguous(), "minmax", 2, 64)
-        a.out_rows, b.out_rows = rows4, rows2
-        del w
-        x1 = SI.dev_bf16_normal(SI.seed_of(4, i, SI.SLOT_X), (1, k), dev)
-        x1k = SI.dev_bf16_normal(SI.seed_of(4, i, SI.SLOT_X) + 100, (1024, k), dev)
-        cm.append((nm, a, b, x1, x1k, torch.empty((1, n), dtype=torch.bfloat16, device=dev),
-                   torch.empty((1024, n), dtype=torch.bfloat16, device=dev)))
+    if need("chmix_70b_m1", "chmix_70b_m1024"):
+        for i, nm in enumerate(s70):
+            n, k = s70[nm]
+            w = SI.dev_gaussian_weights(SI.seed_of(4, i, SI.SLOT_W), n, k, dev)
+            rows4 = SI.dev_channel_mask(SI.seed_of(4, i, SI.SLOT_CHMASK), n, dev)
+            mask = torch.zeros(n, dtype=torch.bool, device=dev)
+            mask[rows4.long()] = True
+            rows2 = torch.nonzero(~mask).flatten().to(torch.int32)
+            a = L.lbq_quantize(w[rows4.long()].contiguous(), "minmax", 4, 128)
+            b = L.lbq_quantize(w[rows2.long()].contiguous(), "minmax", 2, 64)
+            a.out_rows, b.out_rows = rows4, rows2
+            del w
+            x1 = SI.dev_bf16_normal(SI.seed_of(4, i, SI.SLOT_X), (1, k), dev)
+            x1k = SI.dev_bf16_normal(SI.seed_of(4, i, SI.SLOT_X) + 100, (1024, k), dev)
+            cm.append((nm, a, b, x1, x1k, torch.empty((1, n), dtype=torch.bfloat16, device=dev),
+                       torch.empty((1024, n), dtype=torch.bfloat16, device=dev)))
+    cp_src = cp_dst = None
+    if need("copy_1g"):
+        cp_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        cp_dst = torch.empty_like(cp_src)
     torch.cuda.synchronize()
 
     def p_quant_int4():
@@ -148,6 +213,9 @@ def build_workload(L, SI, torch, dev, R):
                 L.lbq_linear_fwd(X[nm], qs[nm], out=Y[nm])
         return f
 
+    def gemm_units(qs, X, Y):
+        return [(nm, (lambda nm=nm: L.lbq_linear_fwd(X[nm], qs[nm], out=Y[nm]))) for nm in names]
+
     def p_lora():
         for nm, (A, B, ws, Y) in lora.items():
             L.lbq_lora_fwd(X4k[nm], qn[nm], A, B, 1.0, out=Y, workspace=ws)
@@ -156,12 +224,18 @@ def build_workload(L, SI, torch, dev, R):
         for nm in names:
             L.lbq_linear_bwd_dx(dY[nm], qn[nm], out=dX[nm])
 
-    def p_chmix():
+    def p_chmix_m1():
         for nm, a, b, x1, x1k, y1, y1k in cm:
             L.lbq_linear_fwd(x1, a, out=y1)
             L.lbq_linear_fwd(x1, b, out=y1)
+
+    def p_chmix_m1024():
+        for nm, a, b, x1, x1k, y1, y1k in cm:
             L.lbq_linear_fwd(x1k, a, out=y1k)
             L.lbq_linear_fwd(x1k, b, out=y1k)
+
+    def p_copy():
+        cp_dst.copy_(cp_src)
 
     def bytes_fwd(q, m, n, k):
         return q.nbytes() + 2 * m * k + 2 * m * n
@@ -170,18 +244,22 @@ def build_workload(L, SI, torch, dev, R):
     gemv_bytes = lambda m: sum(bytes_fwd(c[nm], m, N_of[nm], K_of[nm]) for c in copies for nm in names)
     quant_bytes = lambda qs: sum(4 * N_of[nm] * K_of[nm] + qs[nm].nbytes() for nm in names)
     phases = [
-        ("quant_int4", p_quant_int4, {"bound": "hbm", "bytes": quant_bytes(q4), "launches": 7}),
-        ("quant_nf4dq", p_quant_nf4dq, {"bound": "hbm", "bytes": quant_bytes(qn), "launches": 7}),
-        ("dequant", p_dequant, {"bound": "hbm", "bytes": sum(qn[nm].nbytes() + 2 * N_of[nm] * K_of[nm] for nm in names), "launches": 7}),
-        ("gemv_m1", p_gemv(X1, Y1), {"bound": "hbm", "bytes": gemv_bytes(1), "launches": 7 * R}),
-        ("gemv_m16", p_gemv(X16, Y16), {"bound": "hbm", "bytes": gemv_bytes(16), "launches": 7 * R}),
-        ("gemm_m2048", p_gemm(q4, X2k, Y2k), {"bound": "mfma", "flop": flop(2048), "launches": 7}),
-        ("fwd_m4096", p_gemm(qn, X4k, Y4k), {"bound": "mfma", "flop": flop(4096), "launches": 7}),
-        ("lora_m4096", p_lora, {"bound": "mfma", "flop": sum(2 * 4096 * N_of[nm] * K_of[nm] + 2 * 4096 * 16 * (K_of[nm] + N_of[nm]) for nm in lora), "launches": 4}),
-        ("bwd_m4096", p_bwd, {"bound": "mfma", "flop": flop(4096), "launches": 7}),
-        ("chmix_70b", p_chmix, {"bound": "hbm", "bytes": sum(bytes_fwd(a, 1, a.n, a.k) + bytes_fwd(b, 1, b.n, b.k) for _, a, b, *_ in cm), "launches": 28}),
+        ("quant_int4", p_quant_int4, lambda: {"bound": "hbm", "bytes": quant_bytes(q4), "launches": 7}),
+        ("quant_nf4dq", p_quant_nf4dq, lambda: {"bound": "hbm", "bytes": quant_bytes(qn), "launches": 7}),
+        ("dequant", p_dequant, lambda: {"bound": "hbm", "bytes": sum(qn[nm].nbytes() + 2 * N_of[nm] * K_of[nm] for nm in names), "launches": 7}),
+        ("gemv_m1", p_gemv(X1, Y1), lambda: {"bound": "hbm", "bytes": gemv_bytes(1), "launches": 7 * R}),
+        ("gemv_m16", p_gemv(X16, Y16), lambda: {"bound": "hbm", "bytes": gemv_bytes(16), "launches": 7 * R}),
+        ("gemm_m2048", p_gemm(q4, X2k, Y2k), lambda: {"bound": "mfma", "flop": flop(2048), "launches": 7}),
+        ("fwd_m4096", p_gemm(qn, X4k, Y4k), lambda: {"bound": "mfma", "flop": flop(4096), "launches": 7,
+                                                      "units": gemm_units(qn, X4k, Y4k),
+                                                      "unit_flop": {nm: 2 * 4096 * n * k for nm, (n, k) in shapes.items()}}),
+        ("lora_m4096", p_lora, lambda: {"bound": "mfma", "flop": sum(2 * 4096 * N_of[nm] * K_of[nm] + 2 * 4096 * 16 * (K_of[nm] + N_of[nm]) for nm in lora), "launches": 4}),
+        ("bwd_m4096", p_bwd, lambda: {"bound": "mfma", "flop": flop(4096), "launches": 7}),
+        ("chmix_70b_m1", p_chmix_m1, lambda: {"bound": "hbm", "bytes": sum(bytes_fwd(a, 1, a.n, a.k) + bytes_fwd(b, 1, b.n, b.k) for _, a, b, *_ in cm), "launches": 14}),
+        ("chmix_70b_m1024", p_chmix_m1024, lambda: {"bound": "mfma", "flop": sum(2 * 1024 * (a.n + b.n) * a.k for _, a, b, *_ in cm), "launches": 14}),
+        ("copy_1g", p_copy, lambda: {"bound": "hbm", "bytes": 2 << 30, "launches": 1}),
     ]
-    return phases
+    return [(nm, fn, info()) for nm, fn, info in phases if nm in want]
 
 
 def cpu_baseline():
@@ -227,7 +305,12 @@ def main():
     ap.add_argument("--phases", default="", help="comma-separated subset of phases (profiling)")
     ap.add_argument("--eager", action="store_true", help="launch phases directly instead of replaying graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        print(json.dumps(write_traffic(*args.traffic_from)), flush=True)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -242,47 +325,61 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t_setup = time.perf_counter()
-    phases = build_workload(L, SI, torch, dev, args.copies)
-    if args.phases:
-        keep = set(args.phases.split(","))
-        phases = [p for p in phases if p[0] in keep]
+    want = set(args.phases.split(",")) if args.phases else set(ALL_PHASES)
+    unknown = want - set(ALL_PHASES) - set(EXTRA_PHASES)
+    if unknown:
+        print(json.dumps({"error": f"unknown phases {sorted(unknown)}"}), flush=True)
+        sys.exit(2)
+    phases = build_workload(L, SI, torch, dev, args.copies, want)
     print(f"# setup {time.perf_counter() - t_setup:.1f}s; phases: {[p[0] for p in phases]}", file=sys.stderr, flush=True)
 
-    runners = []
-    for name, fn, info in phases:
+    # A phase runs as one graph, or (phases with "units", the headline) as one
+    # graph per linear so that each kernel launch is bracketed by its own events.
+    def capture(fn):
         fn()  # eager warm call (first-launch costs stay out of the graph)
         torch.cuda.synchronize()
         if args.eager:
-            runners.append((name, fn, info))
-        else:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                fn()
-            runners.append((name, g.replay, info))
+            return fn
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g.replay
+
+    runners = []
+    for name, fn, info in phases:
+        units = info.get("units") or [(name, fn)]
+        runners.append((name, [(u, capture(f)) for u, f in units], info))
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
-        for _, run, _ in runners:
-            run()
+        for _, units, _ in runners:
+            for _, run in units:
+                run()
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-           for name, _, _ in runners}
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    evs = {name: [[ev() for _ in range(len(units) + 1)] for _ in range(K)] for name, units, _ in runners}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
-        for name, run, _ in runners:
-            evs[name][s][0].record()
-            run()
-            evs[name][s][1].record()
+        for name, units, _ in runners:
+            e = evs[name][s]
+            e[0].record()
+            for j, (_, run) in enumerate(units):
+                run()
+                e[j + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / K * 1e3
 
     report = {}
-    for name, _, info in runners:
-        ms = sum(a.elapsed_time(b) for a, b in evs[name]) / K
+    unit_us = {}
+    for name, units, info in runners:
+        ms = sum(e[0].elapsed_time(e[-1]) for e in evs[name]) / K
+        if len(units) > 1:
+            unit_us[name] = {u: sum(e[j].elapsed_time(e[j + 1]) for e in evs[name]) / K * 1e3
+                             for j, (u, _) in enumerate(units)}
         ent = {"ms": round(ms, 4), "launches": info["launches"], "avg_launch_us": round(ms * 1e3 / info["launches"], 3)}
         if info["bound"] == "hbm":
             gbps = info["bytes"] / (ms * 1e-3) / 1e9
@@ -321,16 +418,23 @@ def main():
         "phases": report,
     }
     if head:
-        per_launch = head["flop"] / head["launches"]
-        ach = per_launch / (head["avg_launch_us"] * 1e-6) / 1e12
-        out["roofline"] = {"kernel": "k_gemm_fwd<NF4DQ> (m=4096, 7 linears)", "bound": "mfma",
-                           "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+        # Dominant kernel: the 256 x 256-tile NF4+DQ GEMM that serves q, o, gate,
+        # up and down at m = 4096 (k and v, N = 1024, take 128 x 128 tiles).
+        big = ("q", "o", "gate", "up", "down")
+        uf = next(info for name, _, info in runners if name == "fwd_m4096")["unit_flop"]
+        us = unit_us["fwd_m4096"]
+        t_big = sum(us[u] for u in big)
+        ach = sum(uf[u] for u in big) / (t_big * 1e-6) / 1e12
+        out["roofline"] = {"kernel": "k_gemm_fwd<NF4+DQ, 256x256 tile> (q, o, gate, up, down at m=4096)",
+                           "bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                           "traffic": load_traffic("fwd_m4096", per_launch)}
+                           "traffic": load_traffic("fwd_m4096_big", None),
+                           "avg_launch_us": round(t_big / len(big), 2),
+                           "per_linear_us": {u: round(v, 2) for u, v in us.items()}}
     if gemv:
         per_launch = gemv["bytes"] / gemv["launches"]
         ach = per_launch / (gemv["avg_launch_us"] * 1e-6) / 1e9
-        out["roofline_gemv_m1"] = {"kernel": "k_gemv<INT4 g128, m=1> (7 linears x copies)", "bound": "hbm",
+        out["roofline_gemv_m1"] = {"kernel": "k_gemv1<INT4 g128> (m=1, 7 linears x copies)", "bound": "hbm",
                                    "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                    "frac": round(ach / HBM_PEAK_GBPS, 4),
                                    "traffic": load_traffic("gemv_m1", per_launch)}

@@ -140,7 +140,7 @@ struct Step {
   int zq[CB][R];
 };
 
-template <int KIND, int R, int CB>
+template <int KIND, int R, int CB, int D>
 __global__ __launch_bounds__(kThreads) void k_gemv1(WView w, const uint16_t* __restrict__ X,
                                                    uint16_t* __restrict__ Y,
                                                    const int32_t* __restrict__ out_rows,
@@ -191,10 +191,13 @@ __global__ __launch_bounds__(kThreads) void k_gemv1(WView w, const uint16_t* __r
     }
   };
 
-  // The first step's weight loads go out before x is staged, so their latency
-  // overlaps the prologue.
-  Step<KIND, R, CB> A, B;
-  if (total > 0) load(0, A);
+  // The loads of the first D steps go out before x is staged, so their
+  // latency overlaps the prologue; afterwards each computed step's slot is
+  // refilled with the step D ahead (a ring of D steps in registers).
+  Step<KIND, R, CB> st[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+    if (i < total) load(i, st[i]);
 
   // ---- prologue: arranged x (and chunk sums) in LDS; NF4 table --------------
   __shared__ float cbs[16];
@@ -275,21 +278,23 @@ __global__ __launch_bounds__(kThreads) void k_gemv1(WView w, const uint16_t* __r
     }
   };
 
-  int s = 0;
-  if (total == 0) return;
-  for (;;) {
-    if (s + 1 < total) load(s + 1, B);
-    compute(s, A);
-    if (++s >= total) break;
-    if (s + 1 < total) load(s + 1, A);
-    compute(s, B);
-    if (++s >= total) break;
+  for (int s = 0; s < total; s += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      if (s + i >= total) break;
+      compute(s + i, st[i]);
+      if (s + i + D < total) load(s + i + D, st[i]);
+    }
   }
 }
 
-template <int KIND, int R, int CB>
+// spw: target steps per wave (each wave keeps up to D steps of loads in
+// flight); the grid never has fewer than min_waves waves when there is that
+// much work.
+template <int KIND, int R, int CB, int D>
 hipError_t launch_r(const WView& w, const uint16_t* X, uint16_t* Y, const int32_t* out_rows,
-                    const LoraEpi& lora, const Nf4Table& tab, hipStream_t s) {
+                    const LoraEpi& lora, const Nf4Table& tab, hipStream_t s, int spw = 4,
+                    int min_waves = 1024) {
   using T = WKindTraits<KIND>;
   using G = Gemv1Traits<KIND>;
   const int64_t KB = w.k * T::bits / 8;
@@ -299,14 +304,13 @@ hipError_t launch_r(const WView& w, const uint16_t* X, uint16_t* Y, const int32_
   const int64_t ngroups = (w.n + R - 1) / R;
   const int64_t cpl = (nchunk + 63) / 64;
   const int64_t nsteps = (cpl + CB - 1) / CB;
-  // About four steps per wave for overlap, but never fewer workgroups than CUs.
-  int64_t waves = (ngroups * nsteps + 3) / 4;
-  waves = waves < 1024 ? 1024 : waves;
+  int64_t waves = (ngroups * nsteps + spw - 1) / spw;
+  waves = waves < min_waves ? min_waves : waves;
   waves = waves > ngroups ? ngroups : waves;
   const int64_t gpw = (ngroups + waves - 1) / waves;
   const int64_t nw = (ngroups + gpw - 1) / gpw;
   const dim3 grid((unsigned)((nw + 3) / 4));
-  hipLaunchKernelGGL((k_gemv1<KIND, R, CB>), grid, dim3(kThreads), lds, s, w, X, Y, out_rows, lora,
+  hipLaunchKernelGGL((k_gemv1<KIND, R, CB, D>), grid, dim3(kThreads), lds, s, w, X, Y, out_rows, lora,
                      tab, (int)gpw);
   return hipGetLastError();
 }
@@ -315,7 +319,13 @@ template <int KIND>
 struct Gemv1Launcher {
   static hipError_t run(const WView& w, const uint16_t* X, uint16_t* Y, const int32_t* out_rows,
                         const LoraEpi& lora, const Nf4Table& tab, hipStream_t s) {
-    return launch_r<KIND, 2, (WKindTraits<KIND>::fmt == FMT_NF4 ? 2 : 1)>(w, X, Y, out_rows, lora, tab, s);
+    // Measured on the LLaMA-3-8B shapes: MinMax keeps 4 steps of 2 rows x 16 B
+    // per lane in flight with about 2 steps per wave; NF4 (2 chunks per step)
+    // 2 steps with about 4 per wave.
+    if constexpr (WKindTraits<KIND>::fmt == FMT_NF4)
+      return launch_r<KIND, 2, 2, 2>(w, X, Y, out_rows, lora, tab, s, 4);
+    else
+      return launch_r<KIND, 2, 1, 4>(w, X, Y, out_rows, lora, tab, s, 2);
   }
 };
 

@@ -77,7 +77,7 @@ EXTRA_PHASES = ("copy_1g",)  # opt-in: plain 1 GiB device copy (counter calibrat
 # Kernel-name patterns (rocprofv3 demangled names) of the kernels whose HBM
 # traffic the JSON line reports.
 TRAFFIC_KERNELS = {
-    "fwd_m4096_big": "k_gemm_fwd<5, 256, 256, 2, 4, false>",
+    "fwd_m4096_big": "k_gemm_fwd<5, 256, 256, 4, 2, false>",
     "gemv_m1": "k_gemv1<0,",
 }
 

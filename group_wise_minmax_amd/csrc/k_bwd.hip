@@ -268,18 +268,32 @@ __global__ __launch_bounds__(256) void k_lora_t(const uint16_t* __restrict__ X, 
   for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int64_t mr = m0 + li;
   const int64_t steps = K / 32;
-  for (int64_t s = wave; s < steps; s += 4) {
-    const int64_t k = 32 * s + 8 * lg;
-    const u32x4_t a = (mr < m) ? *reinterpret_cast<const u32x4_t*>(X + mr * K + k)
-                               : u32x4_t{0u, 0u, 0u, 0u};
+  // Buffer resources: X rows past m and A rows past r read as zeros.
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (int64_t)m * K * 2);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (int64_t)r * K * 2);
+  const uint32_t xo = (uint32_t)((mr * K + 8 * lg) * 2);
+  // Wave w takes K-steps w, w+4, ...; U steps' loads are issued before their MFMAs.
+  constexpr int U = 4;
+  for (int64_t s0 = wave; s0 < steps; s0 += 4 * U) {
+    u32x4_t xa[U], ab[U][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (t < nt) {
-        const int j = 16 * t + li;
-        const u32x4_t b = (j < r) ? *reinterpret_cast<const u32x4_t*>(A + (int64_t)j * K + k)
-                                  : u32x4_t{0u, 0u, 0u, 0u};
-        acc[t] = mfma16x16x32(a, b, acc[t]);
-      }
+    for (int u = 0; u < U; ++u) {
+      const int64_t s = min(s0 + 4 * u, steps - 1);  // clamped; extra steps are masked below
+      const int ko = (int)(32 * s * 2);
+      xa[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, xo, ko, 0));
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (t < nt)
+          ab[u][t] = __builtin_bit_cast(
+              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                           ra, (uint32_t)(((16 * t + li) * K + 8 * lg) * 2), ko, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + 4 * u >= steps) break;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (t < nt) acc[t] = mfma16x16x32(xa[u], ab[u][t], acc[t]);
     }
   }
 #pragma unroll

@@ -20,7 +20,7 @@
 // accumulators are four consecutive n of one m, so the epilogue writes 8
 // contiguous bytes of a Y row.  Workgroups are renumbered so that each of the
 // 8 XCDs (each with its own L2) receives a contiguous run of tiles, walked in
-// groups of 4 X-row tiles so that concurrently running tiles share operands.
+// groups of 2 X-row tiles so that concurrently running tiles share operands.
 #include "lbq_device.h"
 
 namespace lbq {
@@ -82,7 +82,9 @@ __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint1
                                                           LoraEpi lora, Nf4Table tab) {
   using T = WKindTraits<KIND>;
   constexpr int NT = WGN * WGM * 64;
-  static_assert(NT == 2 * BN, "each thread owns 32 codes of one W row per stage");
+  constexpr int CPT = BN * BK / NT;  // codes of one W row a thread dequantizes per stage
+  constexpr int NQ = CPT / 32;       // 32-code pieces per thread
+  static_assert(CPT == 32 || CPT == 64, "a thread owns 32 or 64 codes of one W row per stage");
   constexpr int WN = BN / WGN, WM = BM / WGM;
   constexpr int TN = WN / 16, TM = WM / 16;
   constexpr int XCH = BM * BK / 8 / NT;  // 16-byte X chunks per thread per stage
@@ -116,8 +118,8 @@ __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint1
     for (int b = tid; b < 256; b += NT) pairlut[b] = (f32x2_t){cbs[b >> 4], cbs[b & 15]};
   }
 
-  // W ownership: row n0 + (tid >> 1), codes [32*(tid&1), +32) of each stage.
-  const int wrow = tid >> 1, whalf = tid & 1;
+  // W ownership: row n0 + wrow, codes [CPT*wpart, +CPT) of each stage.
+  const int wrow = tid / (BK / CPT), wpart = tid % (BK / CPT);
   const int64_t wn_g = n0 + wrow;
   const bool wrow_ok = wn_g < w.n;  // rows past n read row 0 and are zeroed
   const uint8_t* wsrc = w.packed + (wrow_ok ? wn_g : 0) * KB;
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint1
   // branches, so they are all in flight at once); the metadata stays raw here
   // and is combined in store_stage, one K-step later, so no wave waits on it.
   u32x4_t xr[XCH];
-  u32x4_t wr;
+  u32x4_t wr[NQ];
   float md_s = 0.f;  // scale (MinMax), absmax or second-level scale (NF4)
   int md_i = 0;      // zero point (MinMax) or int8 absmax code (NF4 + DQ)
   auto load_stage = [&](int64_t kt) {
@@ -145,12 +147,15 @@ __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint1
       const int64_t mr = min(m0 + row, (int64_t)m - 1);
       xr[i] = *reinterpret_cast<const u32x4_t*>(X + mr * K + kt + col);
     }
-    const int64_t kk = kt + 32 * whalf;
-    if constexpr (T::bits == 4) {
-      wr = *reinterpret_cast<const u32x4_t*>(wsrc + kk / 2);
-    } else {
-      const uint2 v = *reinterpret_cast<const uint2*>(wsrc + kk / 4);
-      wr = u32x4_t{v.x, v.y, 0u, 0u};
+    const int64_t kk = kt + CPT * wpart;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      if constexpr (T::bits == 4) {
+        wr[q] = *reinterpret_cast<const u32x4_t*>(wsrc + (kk + 32 * q) / 2);
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(wsrc + (kk + 32 * q) / 4);
+        wr[q] = u32x4_t{v.x, v.y, 0u, 0u};
+      }
     }
     const int64_t gi = grow + kk / T::group;
     if constexpr (T::fmt == FMT_MINMAX) {
@@ -169,7 +174,6 @@ __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint1
       const int c = tid + NT * i;
       *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(&Xs[buf][0]) + swz(c >> 3, c & 7)) = xr[i];
     }
-    uint32_t d[16];
     float ws_s, ws_zs = 0.f;
     if constexpr (T::fmt == FMT_MINMAX) {
       ws_s = md_s;
@@ -180,11 +184,16 @@ __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint1
       ws_s = md_s;
     }
     if (!wrow_ok) ws_s = ws_zs = 0.f;  // rows past n contribute zeros
-    dequant32<KIND>(wr, ws_s, ws_zs, pairlut, d);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(&Ws[buf][0]) + swz(wrow, 4 * whalf + j)) =
-          u32x4_t{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]};
+    for (int q = 0; q < NQ; ++q) {
+      uint32_t d[16];
+      dequant32<KIND>(wr[q], ws_s, ws_zs, pairlut, d);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(&Ws[buf][0]) +
+                                    swz(wrow, (CPT / 8) * wpart + 4 * q + j)) =
+            u32x4_t{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]};
+    }
   };
   // Operand rows of this lane: W rows wn*WN + 16*a + li, X rows wm*WM + 16*b + li
   // (row & 7 == li & 7), chunk 4*(ks/32) + lg of each.
@@ -310,14 +319,14 @@ struct GemmFwdLauncher {
                         hipStream_t s) {
     // Pick the tile with the best (chip fill x per-tile efficiency).  The
     // per-tile factors are the measured throughput of each shape relative to
-    // 256x256 (8 waves of 128x64) at full occupancy.
+    // 256x256 (8 waves of 64x128) at full occupancy.
     const int64_t t256x256 = ((w.n + 255) / 256) * ((m + 255) / 256);
     const int64_t t256x128 = ((w.n + 255) / 256) * ((m + 127) / 128);
     const int64_t t128x128 = ((w.n + 127) / 128) * ((m + 127) / 128);
     const double e0 = fill(t256x256) * 1.00;
-    const double e1 = fill(t256x128) * 0.66;
-    const double e2 = fill(t128x128) * 0.45;
-    if (e0 >= e1 && e0 >= e2) return launch_cfg<KIND, 256, 256, 2, 4>(w, X, m, Y, ldy, out_rows, lora, tab, s);
+    const double e1 = fill(t256x128) * 0.78;
+    const double e2 = fill(t128x128) * 0.74;
+    if (e0 >= e1 && e0 >= e2) return launch_cfg<KIND, 256, 256, 4, 2>(w, X, m, Y, ldy, out_rows, lora, tab, s);
     if (e1 >= e2) return launch_cfg<KIND, 256, 128, 4, 2>(w, X, m, Y, ldy, out_rows, lora, tab, s);
     return launch_cfg<KIND, 128, 128, 2, 2>(w, X, m, Y, ldy, out_rows, lora, tab, s);
   }

@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv1(WView w, const uint16_t* __r
   constexpr int CPC = G::CPC, XD = G::XD, XQ = G::XQ, GRP = G::GRP;
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int KB = (int)(w.k * T::bits / 8);  // bytes per packed row (< 2^24)
   const int nchunk = KB / 16;               // 16-byte chunks per row
   const int gpr = (int)(w.k / GRP);         // metadata entries per row
@@ -169,22 +169,43 @@ __global__ __launch_bounds__(kThreads) void k_gemv1(WView w, const uint16_t* __r
   const int total = g0 < g1 ? (g1 - g0) * nsteps : 0;
   const int lane32 = lane & 31;
 
+  // Buffer loads: the row base is a wave-uniform scalar offset, the lane's
+  // chunk a 32-bit vector offset (the boundary keeps (n + 256) * k < 2^32).
+  const int64_t nmeta = w.n * gpr;
+  const __amdgpu_buffer_rsrc_t r_w = make_rsrc(w.packed, w.n * KB);
+  __amdgpu_buffer_rsrc_t r_s, r_z;
+  if constexpr (T::fmt == FMT_MINMAX) {
+    r_s = make_rsrc(w.scales, nmeta * 4);
+    r_z = make_rsrc(w.zeros, nmeta);
+  } else if constexpr (T::dq) {
+    r_s = make_rsrc(w.absmax_scale, ((nmeta + 255) >> 8) * 4);
+    r_z = make_rsrc(w.absmax_q, nmeta);
+  } else {
+    r_s = make_rsrc(w.absmax, nmeta * 4);
+    r_z = r_s;
+  }
   auto load = [&](int s, Step<KIND, R, CB>& st) {
     const int g = g0 + s / nsteps, b = s % nsteps;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int64_t row = min((int64_t)g * R + r, w.n - 1);
+      const int row = (int)min((int64_t)g * R + r, w.n - 1);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const int c = min((b * CB + cb) * 64 + lane, nchunk - 1);  // clamped: always valid
-        st.wq[cb][r] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4_t*>(w.packed + row * KB + (int64_t)c * 16));
-        const int64_t gi = row * gpr + (c * CPC) / GRP;
+        st.wq[cb][r] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_w, (uint32_t)c * 16u, row * KB, 2 /*nt*/));
+        const int gc = (c * CPC) / GRP;  // metadata entry of the chunk within the row
         if constexpr (T::fmt == FMT_MINMAX) {
-          st.sc[cb][r] = w.scales[gi];
-          st.zq[cb][r] = w.zeros[gi];
+          st.sc[cb][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)gc * 4u, row * gpr * 4, 0));
+          st.zq[cb][r] = __builtin_amdgcn_raw_buffer_load_b8(r_z, (uint32_t)gc, row * gpr, 0);
+        } else if constexpr (T::dq) {
+          const int q2 = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(r_z, (uint32_t)gc, row * gpr, 0);
+          const float c2 = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)((row * gpr + gc) >> 8) * 4u, 0, 0));
+          st.sc[cb][r] = (float)q2 * c2;
+          st.zq[cb][r] = 0;
         } else {
-          st.sc[cb][r] = nf4_block_scale<T::dq>(w, gi);
+          st.sc[cb][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)gc * 4u, row * gpr * 4, 0));
           st.zq[cb][r] = 0;
         }
       }

@@ -294,6 +294,26 @@ def lora_fwd(X_bits, W_exact, A_bits, B_bits, sigma: float) -> np.ndarray:
     return X @ W_exact.T + float(sigma) * (T @ bf16_to_f64(B_bits).T)
 
 
+def lora_bwd(X_bits, dY_bits, W_exact, A_bits, B_bits, sigma: float):
+    """Gradients of Y = X . W^T + sigma * (X . A^T) . B^T for a frozen W, in
+    fp64 ("QLoRA技术在量化微调中的应用", section QLoRA技术原理: the gradient
+    passes through the frozen quantized weight into the low-rank adapters):
+
+        dX = dY . W + sigma * (dY . B) . A      [m, K]
+        dA = sigma * (dY . B)^T . X             [r, K]
+        dB = sigma * dY^T . (X . A^T)           [N, r]
+    """
+    X = bf16_to_f64(X_bits)
+    dY = bf16_to_f64(dY_bits)
+    A = bf16_to_f64(A_bits)
+    B = bf16_to_f64(B_bits)
+    G = float(sigma) * (dY @ B)
+    dX = dY @ W_exact + G @ A
+    dA = G.T @ X
+    dB = float(sigma) * (dY.T @ (X @ A.T))
+    return dX, dA, dB
+
+
 def channel_mix_fwd(X_bits, parts) -> np.ndarray:
     """Channel-mix forward: ``parts`` is a list of (out_rows int[n_i], W_exact
     [n_i, K]); output channel out_rows[j] of Y takes row j of W_i."""

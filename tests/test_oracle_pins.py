@@ -392,3 +392,66 @@ def test_rel_errors_definition():
     ref = np.array([[3.0, 4.0]])
     fro, mx = O.rel_errors(ref + np.array([[0.0, 0.5]]), ref)
     assert fro == pytest.approx(0.1) and mx == pytest.approx(0.125)
+
+
+# ---------------------------------------------------------------------------
+# LoRA backward ("QLoRA技术在量化微调中的应用", section QLoRA技术原理): pinned to
+# the forward by adjoint identities, and to brute force on a tiny case.
+# ---------------------------------------------------------------------------
+
+
+def _lora_case(seed, m=5, n=12, k=16, r=3):
+    rng = np.random.default_rng(seed)
+    X = SI.bf16_normal(seed + 1, (m, k))
+    dY = SI.bf16_normal(seed + 2, (m, n))
+    A = SI.bf16_normal(seed + 3, (r, k), std=0.5)
+    B = SI.bf16_normal(seed + 4, (n, r), std=0.5)
+    W = rng.standard_normal((n, k))
+    return X, dY, W, A, B
+
+
+def test_lora_bwd_adjoint_of_forward():
+    """<dY, dY_dir> with the directional change of the forward equals the
+    gradients paired with the direction.  The forward is bilinear in (A, B),
+    so the central difference over +/- a direction is exact."""
+    for sigma in (1.0, 2.0):
+        X, dY, W, A, B = _lora_case(11)
+        dX, dA, dB = O.lora_bwd(X, dY, W, A, B, sigma)
+        rng = np.random.default_rng(5)
+        dAd = rng.standard_normal(A.shape)
+        dBd = rng.standard_normal(B.shape)
+        Xf, dYf, Af, Bf = (O.bf16_to_f64(t) for t in (X, dY, A, B))
+
+        def fwd(Xv, Av, Bv):
+            return Xv @ W.T + sigma * (Xv @ Av.T) @ Bv.T
+
+        diff = (fwd(Xf, Af + dAd, Bf + dBd) - fwd(Xf, Af - dAd, Bf - dBd)) / 2.0
+        lhs = float(np.sum(dYf * diff))
+        rhs = float(np.sum(dA * dAd) + np.sum(dB * dBd))
+        assert abs(lhs - rhs) <= 1e-9 * max(1.0, abs(lhs))
+        # dX: the forward is linear in X
+        dXd = rng.standard_normal(Xf.shape)
+        lhs = float(np.sum(dYf * (fwd(Xf + dXd, Af, Bf) - fwd(Xf, Af, Bf))))
+        assert abs(lhs - float(np.sum(dX * dXd))) <= 1e-9 * max(1.0, abs(lhs))
+
+
+def test_lora_bwd_brute_force_tiny():
+    X, dY, W, A, B = _lora_case(23, m=3, n=4, k=5, r=2)
+    sigma = 2.0
+    dX, dA, dB = O.lora_bwd(X, dY, W, A, B, sigma)
+    Xf, dYf, Af, Bf = (O.bf16_to_f64(t) for t in (X, dY, A, B))
+    m, k = Xf.shape
+    n, r = Bf.shape
+    for a in range(m):
+        for c in range(k):
+            v = sum(dYf[a, i] * W[i, c] for i in range(n))
+            v += sum(sigma * dYf[a, i] * Bf[i, j] * Af[j, c] for i in range(n) for j in range(r))
+            assert abs(dX[a, c] - v) <= 1e-12 * max(1.0, abs(v))
+    for j in range(r):
+        for c in range(k):
+            v = sum(sigma * dYf[a, i] * Bf[i, j] * Xf[a, c] for a in range(m) for i in range(n))
+            assert abs(dA[j, c] - v) <= 1e-12 * max(1.0, abs(v))
+    for i in range(n):
+        for j in range(r):
+            v = sum(sigma * dYf[a, i] * Xf[a, c] * Af[j, c] for a in range(m) for c in range(k))
+            assert abs(dB[i, j] - v) <= 1e-12 * max(1.0, abs(v))

@@ -14,6 +14,8 @@ One step is one pass of the whole hot path over a LLaMA-3-8B decoder layer
   fwd_m4096    NF4-DQ forward at m = 4096 (2 x 2048 tokens)       <- headline
   lora_m4096   NF4-DQ forward + rank-16 LoRA on q and v at m = 4096
   bwd_m4096    NF4-DQ input gradient dX = dY deq(W) at m = 4096
+  lora_bwd_m4096  NF4-DQ LoRA backward (dX with the adapter term, dA, dB),
+               rank 16 on q and v, at m = 4096
   chmix_70b_m1     70B-shaped layer, per-channel 25% INT4 g128 / 75% INT2 g64
                    (two launches per linear, each scattering its rows of Y), m = 1
   chmix_70b_m1024  the same at m = 1024
@@ -70,7 +72,7 @@ def load_traffic(kernel: str, units_per_launch=None):
 
 
 ALL_PHASES = ("quant_int4", "quant_nf4dq", "dequant", "gemv_m1", "gemv_m16", "gemm_m2048",
-              "fwd_m4096", "lora_m4096", "bwd_m4096", "chmix_70b_m1", "chmix_70b_m1024")
+              "fwd_m4096", "lora_m4096", "bwd_m4096", "lora_bwd_m4096", "chmix_70b_m1", "chmix_70b_m1024")
 EXTRA_PHASES = ("copy_1g",)  # opt-in: plain 1 GiB device copy (counter calibration)
 
 
@@ -151,17 +153,24 @@ def build_workload(L, SI, torch, dev, R, want):
     X1, Y1 = xs(2, SI.SLOT_X, 0, 1, K_of, need("gemv_m1")), ys(1, N_of, need("gemv_m1"))
     X16, Y16 = xs(2, SI.SLOT_X, 100, 16, K_of, need("gemv_m16")), ys(16, N_of, need("gemv_m16"))
     X2k, Y2k = xs(2, SI.SLOT_X, 200, 2048, K_of, need("gemm_m2048")), ys(2048, N_of, need("gemm_m2048"))
-    X4k = xs(3, SI.SLOT_X, 0, 4096, K_of, need("fwd_m4096", "lora_m4096"))
+    X4k = xs(3, SI.SLOT_X, 0, 4096, K_of, need("fwd_m4096", "lora_m4096", "lora_bwd_m4096"))
     Y4k = ys(4096, N_of, need("fwd_m4096"))
-    dY, dX = xs(3, SI.SLOT_DY, 0, 4096, N_of, need("bwd_m4096")), ys(4096, K_of, need("bwd_m4096"))
+    dY = xs(3, SI.SLOT_DY, 0, 4096, N_of, need("bwd_m4096", "lora_bwd_m4096"))
+    dX = ys(4096, K_of, need("bwd_m4096", "lora_bwd_m4096"))
     lora = {}
-    if need("lora_m4096"):
+    if need("lora_m4096", "lora_bwd_m4096"):
         for nm in ("q", "v"):
             i = names.index(nm)
             A = SI.dev_bf16_normal(SI.seed_of(3, i, SI.SLOT_A), (16, K_of[nm]), dev, std=0.01)
             B = SI.dev_bf16_normal(SI.seed_of(3, i, SI.SLOT_B), (N_of[nm], 16), dev, std=0.01)
             ws = torch.empty(L.lbq_lora_workspace_bytes(qn[nm], 4096, 16), dtype=torch.uint8, device=dev)
             lora[nm] = (A, B, ws, torch.empty((4096, N_of[nm]), dtype=torch.bfloat16, device=dev))
+    lora_bwd = {}
+    if need("lora_bwd_m4096"):
+        for nm, (A, B, _, _) in lora.items():
+            ws = torch.empty(L.lbq_lora_bwd_workspace_bytes(qn[nm], 4096, 16), dtype=torch.uint8, device=dev)
+            lora_bwd[nm] = (A, B, ws, torch.empty((16, K_of[nm]), dtype=torch.float32, device=dev),
+                            torch.empty((N_of[nm], 16), dtype=torch.float32, device=dev))
 
     # 70B-shaped channel-mix layer (quantized once at setup)
     s70 = SI.LLAMA3_70B
@@ -224,6 +233,10 @@ def build_workload(L, SI, torch, dev, R, want):
         for nm in names:
             L.lbq_linear_bwd_dx(dY[nm], qn[nm], out=dX[nm])
 
+    def p_lora_bwd():
+        for nm, (A, B, ws, dA, dB) in lora_bwd.items():
+            L.lbq_lora_bwd(X4k[nm], dY[nm], qn[nm], A, B, 1.0, dX=dX[nm], dA=dA, dB=dB, workspace=ws)
+
     def p_chmix_m1():
         for nm, a, b, x1, x1k, y1, y1k in cm:
             L.lbq_linear_fwd(x1, a, out=y1)
@@ -255,6 +268,8 @@ def build_workload(L, SI, torch, dev, R, want):
                                                       "unit_flop": {nm: 2 * 4096 * n * k for nm, (n, k) in shapes.items()}}),
         ("lora_m4096", p_lora, lambda: {"bound": "mfma", "flop": sum(2 * 4096 * N_of[nm] * K_of[nm] + 2 * 4096 * 16 * (K_of[nm] + N_of[nm]) for nm in lora), "launches": 4}),
         ("bwd_m4096", p_bwd, lambda: {"bound": "mfma", "flop": flop(4096), "launches": 7}),
+        # dX = dY W + G A, G = dY B, T = X A^T, dA = G^T X, dB = (T^T dY)^T
+        ("lora_bwd_m4096", p_lora_bwd, lambda: {"bound": "mfma", "flop": sum(2 * 4096 * N_of[nm] * K_of[nm] + 2 * 4096 * 16 * (2 * N_of[nm] + 3 * K_of[nm]) for nm in lora_bwd), "launches": 14}),
         ("chmix_70b_m1", p_chmix_m1, lambda: {"bound": "hbm", "bytes": sum(bytes_fwd(a, 1, a.n, a.k) + bytes_fwd(b, 1, b.n, b.k) for _, a, b, *_ in cm), "launches": 14}),
         ("chmix_70b_m1024", p_chmix_m1024, lambda: {"bound": "mfma", "flop": sum(2 * 1024 * (a.n + b.n) * a.k for _, a, b, *_ in cm), "launches": 14}),
         ("copy_1g", p_copy, lambda: {"bound": "hbm", "bytes": 2 << 30, "launches": 1}),

@@ -256,3 +256,43 @@ def lbq_lora_fwd(X: torch.Tensor, qw: QuantizedWeight, A: torch.Tensor, B: torch
                            _ptr(workspace), 0 if workspace is None else workspace.numel(),
                            _stream(X.device)), "lbq_lora_fwd")
     return out
+
+
+def lbq_lora_bwd_workspace_bytes(qw: QuantizedWeight, m: int, r: int) -> int:
+    return lib.lbq_lora_bwd_workspace_bytes(ctypes.byref(qw.desc), m, r)
+
+
+def lbq_lora_bwd(X: torch.Tensor, dY: torch.Tensor, qw: QuantizedWeight, A: torch.Tensor,
+                 B: torch.Tensor, sigma: float, dX: Optional[torch.Tensor] = None,
+                 dA: Optional[torch.Tensor] = None, dB: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None):
+    """(dX bf16 [m, k], dA fp32 [r, k], dB fp32 [n, r]) of ``lbq_lora_fwd`` for a
+    frozen weight (see ``lbq_lora_bwd`` in lbq.h)."""
+    _need(X, "X", torch.bfloat16)
+    _need(dY, "dY", torch.bfloat16)
+    _need(A, "A", torch.bfloat16)
+    _need(B, "B", torch.bfloat16)
+    m, r = X.shape[0], A.shape[0]
+    if X.dim() != 2 or X.shape[1] != qw.k or dY.shape != (m, qw.n):
+        raise ValueError(f"X must be [m, {qw.k}] and dY [m, {qw.n}]")
+    if A.shape[1] != qw.k or B.shape != (qw.n, r):
+        raise ValueError("A must be [r, k] and B [n, r]")
+    dev = X.device
+    if dX is None:
+        dX = torch.empty((m, qw.k), dtype=torch.bfloat16, device=dev)
+    if dA is None:
+        dA = torch.empty((r, qw.k), dtype=torch.float32, device=dev)
+    if dB is None:
+        dB = torch.empty((qw.n, r), dtype=torch.float32, device=dev)
+    _need(dX, "dX", torch.bfloat16, (m, qw.k))
+    _need(dA, "dA", torch.float32, (r, qw.k))
+    _need(dB, "dB", torch.float32, (qw.n, r))
+    nbytes = lbq_lora_bwd_workspace_bytes(qw, m, r)
+    if workspace is None:
+        workspace = _ws(nbytes, dev)
+    q = qw.qtensor()
+    check(lib.lbq_lora_bwd(ctypes.byref(qw.desc), ctypes.byref(q), X.data_ptr(), dY.data_ptr(), m,
+                           A.data_ptr(), B.data_ptr(), r, float(sigma), dX.data_ptr(), dA.data_ptr(),
+                           dB.data_ptr(), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                           _stream(dev)), "lbq_lora_bwd")
+    return dX, dA, dB

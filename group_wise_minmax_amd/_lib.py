@@ -23,6 +23,7 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 EXPORTED = (
     "lbq_layout", "lbq_quantize", "lbq_dequant", "lbq_linear_workspace_bytes",
     "lbq_linear_fwd", "lbq_linear_bwd_dx", "lbq_lora_workspace_bytes", "lbq_lora_fwd",
+    "lbq_lora_bwd_workspace_bytes", "lbq_lora_bwd",
     "lbq_nf4_codebook", "lbq_strerror", "lbq_last_error_detail", "lbq_version",
 )
 
@@ -69,6 +70,8 @@ def _load() -> ctypes.CDLL:
         "lbq_linear_bwd_dx": (I32, [DP, QP, P, I64, P, P]),
         "lbq_lora_workspace_bytes": (SZ, [DP, I64, I32]),
         "lbq_lora_fwd": (I32, [DP, QP, P, I64, P, P, I32, ctypes.c_float, P, I64, P, SZ, P]),
+        "lbq_lora_bwd_workspace_bytes": (SZ, [DP, I64, I32]),
+        "lbq_lora_bwd": (I32, [DP, QP, P, P, I64, P, P, I32, ctypes.c_float, P, P, P, P, SZ, P]),
         "lbq_nf4_codebook": (None, [ctypes.POINTER(ctypes.c_float)]),
         "lbq_strerror": (ctypes.c_char_p, [I32]),
         "lbq_last_error_detail": (ctypes.c_char_p, []),

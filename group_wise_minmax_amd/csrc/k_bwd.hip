@@ -28,10 +28,10 @@ namespace {
 // ---------------------------------------------------------------------------
 constexpr int BNR = 64;  // reduction (n) per stage = one 128-byte LDS row
 
-template <int KIND, int BKO, int BM, int WGK, int WGM>
+template <int KIND, int BKO, int BM, int WGK, int WGM, bool LORA>
 __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_t* __restrict__ dY,
                                                         int m, uint16_t* __restrict__ dX,
-                                                        Nf4Table tab) {
+                                                        LoraDx lora, Nf4Table tab) {
   using T = WKindTraits<KIND>;
   constexpr int NT = WGK * WGM * 64;
   constexpr int WK = BKO / WGK, WM = BM / WGM;
@@ -207,6 +207,37 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_
     buf ^= 1;
   }
 
+  // LoRA slab: acc[k][m] += sum over j of A[j][k] * G[m][j], r zero-padded to rp.
+  if constexpr (LORA) {
+    for (int ks = 0; ks < lora.rp; ks += 32) {
+      u32x4_t la[TK], lb[TM];
+#pragma unroll
+      for (int a = 0; a < TK; ++a) {
+        const int64_t k = k0 + wk * WK + 16 * a + li;
+        uint32_t v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c0 = ks + 8 * lg + 2 * j;
+          uint32_t lo = 0, hi = 0;
+          if (k < K && c0 < lora.r) lo = lora.a[(int64_t)c0 * K + k];
+          if (k < K && c0 + 1 < lora.r) hi = lora.a[(int64_t)(c0 + 1) * K + k];
+          v[j] = lo | (hi << 16);
+        }
+        la[a] = u32x4_t{v[0], v[1], v[2], v[3]};
+      }
+#pragma unroll
+      for (int b = 0; b < TM; ++b) {
+        const int64_t mr = m0 + wm * WM + 16 * b + li;
+        lb[b] = (mr < m) ? *reinterpret_cast<const u32x4_t*>(lora.g + mr * lora.rp + ks + 8 * lg)
+                         : u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int a = 0; a < TK; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b) acc[a][b] = mfma16x16x32(la[a], lb[b], acc[a][b]);
+    }
+  }
+
 #pragma unroll
   for (int a = 0; a < TK; ++a) {
     const int64_t kb = k0 + wk * WK + 16 * a + 4 * lg;
@@ -225,10 +256,15 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_
 
 template <int KIND, int BKO, int BM, int WGK, int WGM>
 hipError_t launch_bwd_cfg(const WView& w, const uint16_t* dY, int64_t m, uint16_t* dX,
-                          const Nf4Table& tab, hipStream_t s) {
+                          const LoraDx& lora, const Nf4Table& tab, hipStream_t s) {
   const int64_t tiles = ((w.k + BKO - 1) / BKO) * ((m + BM - 1) / BM);
-  hipLaunchKernelGGL((k_bwd_dx<KIND, BKO, BM, WGK, WGM>), dim3((unsigned)tiles), dim3(WGK * WGM * 64),
-                     0, s, w, dY, (int)m, dX, tab);
+  if (lora.g != nullptr) {
+    hipLaunchKernelGGL((k_bwd_dx<KIND, BKO, BM, WGK, WGM, true>), dim3((unsigned)tiles),
+                       dim3(WGK * WGM * 64), 0, s, w, dY, (int)m, dX, lora, tab);
+  } else {
+    hipLaunchKernelGGL((k_bwd_dx<KIND, BKO, BM, WGK, WGM, false>), dim3((unsigned)tiles),
+                       dim3(WGK * WGM * 64), 0, s, w, dY, (int)m, dX, lora, tab);
+  }
   return hipGetLastError();
 }
 
@@ -240,12 +276,12 @@ double bwd_fill(int64_t tiles) {
 template <int KIND>
 struct BwdLauncher {
   static hipError_t run(const WView& w, const uint16_t* dY, int64_t m, uint16_t* dX,
-                        const Nf4Table& tab, hipStream_t s) {
+                        const LoraDx& lora, const Nf4Table& tab, hipStream_t s) {
     // 256 x 256 tiles (8 waves of 128 x 64) unless they leave most of the chip idle.
     const int64_t t256 = ((w.k + 255) / 256) * ((m + 255) / 256);
     const int64_t t128 = ((w.k + 127) / 128) * ((m + 127) / 128);
-    if (bwd_fill(t256) >= 0.5 * bwd_fill(t128)) return launch_bwd_cfg<KIND, 256, 256, 2, 4>(w, dY, m, dX, tab, s);
-    return launch_bwd_cfg<KIND, 128, 128, 2, 2>(w, dY, m, dX, tab, s);
+    if (bwd_fill(t256) >= 0.5 * bwd_fill(t128)) return launch_bwd_cfg<KIND, 256, 256, 2, 4>(w, dY, m, dX, lora, tab, s);
+    return launch_bwd_cfg<KIND, 128, 128, 2, 2>(w, dY, m, dX, lora, tab, s);
   }
 };
 
@@ -320,8 +356,8 @@ __global__ __launch_bounds__(256) void k_lora_t(const uint16_t* __restrict__ X, 
 }  // namespace
 
 hipError_t launch_bwd_dx(WKind kind, const WView& w, const uint16_t* dY, int64_t m,
-                         uint16_t* dX, const Nf4Table& tab, hipStream_t s) {
-  return dispatch_kind<BwdLauncher>(kind, w, dY, m, dX, tab, s);
+                         uint16_t* dX, const LoraDx& lora, const Nf4Table& tab, hipStream_t s) {
+  return dispatch_kind<BwdLauncher>(kind, w, dY, m, dX, lora, tab, s);
 }
 
 hipError_t launch_lora_t(const uint16_t* X, int64_t m, int64_t k, const uint16_t* A, int32_t r,

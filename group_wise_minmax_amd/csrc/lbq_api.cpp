@@ -204,6 +204,26 @@ size_t fwd_workspace(const lbq_desc* desc, int64_t m, bool lora) {
   return 0;
 }
 
+// Checks shared by the two input-gradient entries (m == 0 passes).
+lbq_status check_bwd_common(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* dY,
+                            int64_t m, uint16_t* dX, const char* who) {
+  lbq_status st = check_desc(desc);
+  if (st != LBQ_OK) return st;
+  if ((st = check_qtensor(desc, q)) != LBQ_OK) return st;
+  if (q->out_rows != nullptr) return fail(LBQ_E_UNSUPPORTED, "%s does not take out_rows", who);
+  if (m < 0 || m > (int64_t(1) << 31) - 1) return fail(LBQ_E_SHAPE, "m must be in [0, 2^31)");
+  if (m == 0) return LBQ_OK;
+  if (dY == nullptr || dX == nullptr) return fail(LBQ_E_NULL, "dY and dX must be non-NULL");
+  if (!aligned(dY, 16) || !aligned(dX, 16)) return fail(LBQ_E_ALIGN, "dY and dX must be 16-byte aligned");
+  if (desc->n % 8 != 0) return fail(LBQ_E_SHAPE, "%s needs n %% 8 == 0 (got %lld)", who, (long long)desc->n);
+  if ((uint64_t)(m + 256) * (uint64_t)desc->n * 2 >= (uint64_t(1) << 32) ||
+      (uint64_t)(m + 256) * (uint64_t)desc->k * 2 >= (uint64_t(1) << 32) ||
+      (uint64_t)(desc->n + 256) * (uint64_t)desc->k >= (uint64_t(1) << 32))
+    return fail(LBQ_E_SHAPE, "(m + 256) * n * 2, (m + 256) * k * 2 and (n + 256) * k must be below 2^32 "
+                "(m %lld, n %lld, k %lld)", (long long)m, (long long)desc->n, (long long)desc->k);
+  return LBQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -269,23 +289,71 @@ lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint
 
 lbq_status lbq_linear_bwd_dx(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* dY,
                              int64_t m, uint16_t* dX, void* stream) {
-  lbq_status st = check_desc(desc);
-  if (st != LBQ_OK) return st;
-  if ((st = check_qtensor(desc, q)) != LBQ_OK) return st;
-  if (q->out_rows != nullptr) return fail(LBQ_E_UNSUPPORTED, "lbq_linear_bwd_dx does not take out_rows");
-  if (m < 0 || m > (int64_t(1) << 31) - 1) return fail(LBQ_E_SHAPE, "m must be in [0, 2^31)");
-  if (m == 0) return ok();
-  if (dY == nullptr || dX == nullptr) return fail(LBQ_E_NULL, "dY and dX must be non-NULL");
-  if (!aligned(dY, 16) || !aligned(dX, 16)) return fail(LBQ_E_ALIGN, "dY and dX must be 16-byte aligned");
-  if (desc->n % 8 != 0) return fail(LBQ_E_SHAPE, "lbq_linear_bwd_dx needs n %% 8 == 0 (got %lld)", (long long)desc->n);
-  if ((uint64_t)(m + 256) * (uint64_t)desc->n * 2 >= (uint64_t(1) << 32) ||
-      (uint64_t)(desc->n + 256) * (uint64_t)desc->k >= (uint64_t(1) << 32))
-    return fail(LBQ_E_SHAPE, "(m + 256) * n * 2 and (n + 256) * k must be below 2^32 (m %lld, n %lld, k %lld)",
-                (long long)m, (long long)desc->n, (long long)desc->k);
-  return hip_status(lbq::launch_bwd_dx(kind_of(desc), view_of(desc, q), dY, m, dX, nf4_table(),
+  lbq_status st = check_bwd_common(desc, q, dY, m, dX, "lbq_linear_bwd_dx");
+  if (st != LBQ_OK || m == 0) return st == LBQ_OK ? ok() : st;
+  const lbq::LoraDx none{nullptr, nullptr, 0, 0};
+  return hip_status(lbq::launch_bwd_dx(kind_of(desc), view_of(desc, q), dY, m, dX, none, nf4_table(),
                                        static_cast<hipStream_t>(stream)),
                     "lbq_linear_bwd_dx");
 }
+
+// LoRA backward workspace (16-byte aligned pieces): Bt = B^T [rp][n] bf16,
+// G = bf16(sigma dY B) [m][rp], T = bf16(sigma X A^T) [m][rp], then the fp32
+// partial sums of the dA / dB reductions (reused by both).
+static size_t align16(size_t b) { return (b + 15) / 16 * 16; }
+
+size_t lbq_lora_bwd_workspace_bytes(const lbq_desc* desc, int64_t m, int32_t r) {
+  if (check_desc(desc) != LBQ_OK || m <= 0 || r < 1 || r > 64) return 0;
+  const size_t rp = (size_t)round_rank(r);
+  const size_t part = std::max(lbq::lora_outer_part_bytes(m, desc->k, r), lbq::lora_outer_part_bytes(m, desc->n, r));
+  return align16(rp * (size_t)desc->n * 2) + 2 * align16((size_t)m * rp * 2) + align16(part);
+}
+
+lbq_status lbq_lora_bwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X,
+                        const uint16_t* dY, int64_t m, const uint16_t* A, const uint16_t* B,
+                        int32_t r, float sigma, uint16_t* dX, float* dA, float* dB,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  lbq_status st = check_bwd_common(desc, q, dY, m, dX, "lbq_lora_bwd");
+  if (st != LBQ_OK) return st;
+  if (r < 1 || r > 64) return fail(LBQ_E_SHAPE, "LoRA rank r must be in [1, 64] (got %d)", r);
+  if (A == nullptr || B == nullptr || dA == nullptr || dB == nullptr)
+    return fail(LBQ_E_NULL, "A, B, dA and dB must be non-NULL");
+  if (!std::isfinite(sigma)) return fail(LBQ_E_SHAPE, "sigma must be finite");
+  if (!aligned(dA, 4) || !aligned(dB, 4)) return fail(LBQ_E_ALIGN, "dA and dB must be 4-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (m == 0) {  // an empty batch has zero adapter gradients
+    hipError_t e = lbq::launch_fill_zero_f32(dA, (int64_t)r * desc->k, s);
+    if (e == hipSuccess) e = lbq::launch_fill_zero_f32(dB, desc->n * (int64_t)r, s);
+    return hip_status(e, "lbq_lora_bwd (empty batch)");
+  }
+  if (X == nullptr) return fail(LBQ_E_NULL, "X must be non-NULL");
+  if (!aligned(X, 16) || !aligned(A, 16)) return fail(LBQ_E_ALIGN, "X and A must be 16-byte aligned");
+  if (!aligned(B, 2)) return fail(LBQ_E_ALIGN, "B must be 2-byte aligned");
+  if (desc->n % 64 != 0) return fail(LBQ_E_SHAPE, "lbq_lora_bwd needs n %% 64 == 0 (got %lld)", (long long)desc->n);
+  const size_t need = lbq_lora_bwd_workspace_bytes(desc, m, r);
+  if (workspace == nullptr || ws_bytes < need) return fail(LBQ_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  if (!aligned(workspace, 16)) return fail(LBQ_E_ALIGN, "workspace must be 16-byte aligned");
+  const int32_t rp = round_rank(r);
+  uint8_t* p = static_cast<uint8_t*>(workspace);
+  uint16_t* Bt = reinterpret_cast<uint16_t*>(p);
+  p += align16((size_t)rp * (size_t)desc->n * 2);
+  uint16_t* G = reinterpret_cast<uint16_t*>(p);
+  p += align16((size_t)m * rp * 2);
+  uint16_t* T = reinterpret_cast<uint16_t*>(p);
+  p += align16((size_t)m * rp * 2);
+  float* part = reinterpret_cast<float*>(p);
+  hipError_t e = lbq::launch_transpose_b(B, desc->n, r, rp, Bt, s);
+  if (e == hipSuccess) e = lbq::launch_lora_t(dY, m, desc->n, Bt, r, rp, sigma, G, s);
+  if (e == hipSuccess) e = lbq::launch_lora_t(X, m, desc->k, A, r, rp, sigma, T, s);
+  if (e != hipSuccess) return hip_status(e, "lbq_lora_bwd (adapter products)");
+  const lbq::LoraDx lora{G, A, r, rp};
+  e = lbq::launch_bwd_dx(kind_of(desc), view_of(desc, q), dY, m, dX, lora, nf4_table(), s);
+  if (e != hipSuccess) return hip_status(e, "lbq_lora_bwd (input gradient)");
+  e = lbq::launch_lora_outer(G, r, rp, X, m, desc->k, false, part, dA, s);
+  if (e == hipSuccess) e = lbq::launch_lora_outer(T, r, rp, dY, m, desc->n, true, part, dB, s);
+  return hip_status(e, "lbq_lora_bwd (adapter gradients)");
+}
+
 
 // LoRA workspace: bf16 T = sigma X A^T [m][rp], then (16-byte aligned) the
 // small-batch kernel's fp32 partials when that kernel runs.

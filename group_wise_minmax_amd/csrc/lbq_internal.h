@@ -34,6 +34,15 @@ struct LoraEpi {
   int32_t rp;
 };
 
+// LoRA term of the input gradient: dX += G . A with G = bf16(sigma * dY . B)
+// [m][rp] (zero past r) and A [r][k] bf16.  g == nullptr: none.
+struct LoraDx {
+  const uint16_t* g;
+  const uint16_t* a;
+  int32_t r;
+  int32_t rp;
+};
+
 // Supported weight encodings (format, bits, group, double quant).
 enum WKind : int {
   WK_I4G128 = 0,  // MinMax 4-bit, group 128
@@ -74,7 +83,16 @@ hipError_t launch_gemm_fwd(WKind kind, const WView& w, const uint16_t* X, int64_
                            uint16_t* Y, int64_t ldy, const int32_t* out_rows,
                            const LoraEpi& lora, const Nf4Table& tab, hipStream_t s);
 hipError_t launch_bwd_dx(WKind kind, const WView& w, const uint16_t* dY, int64_t m,
-                         uint16_t* dX, const Nf4Table& tab, hipStream_t s);
+                         uint16_t* dX, const LoraDx& lora, const Nf4Table& tab, hipStream_t s);
+// LoRA backward helpers: Bt = B^T zero-padded to rp rows; out = sum over rows t
+// of P[t][j] * Q[t][c] (fp32, [r][C], or [C][r] with transpose) using `part`
+// (lora_outer_part_bytes) for per-range partial sums.
+hipError_t launch_transpose_b(const uint16_t* B, int64_t n, int32_t r, int32_t rp, uint16_t* Bt,
+                              hipStream_t s);
+size_t lora_outer_part_bytes(int64_t m, int64_t C, int32_t r);
+hipError_t launch_lora_outer(const uint16_t* P, int32_t r, int32_t rp, const uint16_t* Q, int64_t m,
+                             int64_t C, bool transpose, float* part, float* out, hipStream_t s);
+hipError_t launch_fill_zero_f32(float* p, int64_t count, hipStream_t s);
 hipError_t launch_lora_t(const uint16_t* X, int64_t m, int64_t k, const uint16_t* A,
                          int32_t r, int32_t rp, float sigma, uint16_t* T, hipStream_t s);
 

@@ -176,6 +176,28 @@ lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint
 lbq_status lbq_linear_bwd_dx(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* dY,
                              int64_t m, uint16_t* dX, void* stream);
 
+/* Workspace bytes lbq_lora_bwd needs for m rows and rank r (0 for m <= 0). */
+size_t lbq_lora_bwd_workspace_bytes(const lbq_desc* desc, int64_t m, int32_t r);
+
+/* Backward of lbq_lora_fwd for a frozen quantized weight ([QL]
+ * QLoRA技术原理: the gradient flows through the frozen 4-bit weight into the
+ * low-rank adapters, which are the only trained parameters):
+ *   G  = sigma * dY . B                  [m][r], rounded once to bf16
+ *   dX = dY . deq(W) + G . A             bf16 [m][k]
+ *   dA = G^T . X                         fp32 [r][k]
+ *   dB = sigma * dY^T . (X . A^T)        fp32 [n][r]  (X . A^T rounded once to
+ *                                         bf16, as in the forward)
+ * X: bf16 [m][k], dY: bf16 [m][n], A: bf16 [r][k], B: bf16 [n][r] (device);
+ * X, A, dY, dX 16-byte aligned, dA, dB 4-byte aligned; 1 <= r <= 64;
+ * n % 64 == 0; the size limits of lbq_linear_bwd_dx and lbq_linear_fwd apply.
+ * m == 0 writes zeros to dA and dB and nothing else.  `workspace` must hold
+ * lbq_lora_bwd_workspace_bytes(desc, m, r) bytes (16-byte aligned).  dA and dB
+ * are summed in a fixed order (run-to-run identical). */
+lbq_status lbq_lora_bwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X,
+                        const uint16_t* dY, int64_t m, const uint16_t* A, const uint16_t* B,
+                        int32_t r, float sigma, uint16_t* dX, float* dA, float* dB,
+                        void* workspace, size_t ws_bytes, void* stream);
+
 /* Workspace bytes lbq_lora_fwd needs for m rows and rank r. */
 size_t lbq_lora_workspace_bytes(const lbq_desc* desc, int64_t m, int32_t r);
 

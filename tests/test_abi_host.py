@@ -216,6 +216,40 @@ def test_lora_error_paths(L):
     assert _status(L, args(ws=FAKE + 8)) == "LBQ_E_ALIGN"
 
 
+def test_lora_bwd_error_paths(L):
+    lib = L.lib
+    B = ctypes.byref
+    d = L.make_desc("nf4", 64, 256, double_quant=True)
+    q = _q(L)
+    need = lib.lbq_lora_bwd_workspace_bytes(B(d), 8, 16)
+    # B^T [32][n] + G and T [m][32] bf16, then fp32 partials of at least [16][max(n, k)]
+    assert need >= 32 * 64 * 2 + 2 * 8 * 32 * 2 + 16 * 256 * 4 and need % 16 == 0
+    assert lib.lbq_lora_bwd_workspace_bytes(B(d), 0, 16) == 0
+    assert lib.lbq_lora_bwd_workspace_bytes(B(d), 8, 65) == 0
+
+    def args(m=8, r=16, ws=FAKE, wsb=need, X=FAKE, A=FAKE, Bm=FAKE, dA=FAKE, dB=FAKE, sigma=1.0, desc=d):
+        return lib.lbq_lora_bwd(B(desc), B(q), X, FAKE, m, A, Bm, r, sigma, FAKE, dA, dB, ws, wsb, None)
+
+    assert _status(L, args(r=0)) == "LBQ_E_SHAPE"
+    assert _status(L, args(r=65)) == "LBQ_E_SHAPE"
+    assert _status(L, args(sigma=float("nan"))) == "LBQ_E_SHAPE"
+    assert _status(L, args(A=None)) == "LBQ_E_NULL"
+    assert _status(L, args(dB=None)) == "LBQ_E_NULL"
+    assert _status(L, args(X=None)) == "LBQ_E_NULL"
+    assert _status(L, args(X=FAKE + 8)) == "LBQ_E_ALIGN"
+    assert _status(L, args(A=FAKE + 2)) == "LBQ_E_ALIGN"
+    assert _status(L, args(Bm=FAKE + 1)) == "LBQ_E_ALIGN"
+    assert _status(L, args(dA=FAKE + 2)) == "LBQ_E_ALIGN"
+    assert _status(L, args(ws=None)) == "LBQ_E_WORKSPACE"
+    assert _status(L, args(wsb=need - 1)) == "LBQ_E_WORKSPACE"
+    assert _status(L, args(ws=FAKE + 8)) == "LBQ_E_ALIGN"
+    d96 = L.make_desc("nf4", 96, 256, double_quant=True)  # n % 64 != 0
+    need96 = lib.lbq_lora_bwd_workspace_bytes(B(d96), 8, 16)
+    assert _status(L, args(desc=d96, wsb=need96)) == "LBQ_E_SHAPE"
+    assert _status(L, lib.lbq_lora_bwd(B(d), B(_q(L, out_rows=FAKE)), FAKE, FAKE, 8, FAKE, FAKE, 16, 1.0,
+                                       FAKE, FAKE, FAKE, FAKE, need, None)) == "LBQ_E_UNSUPPORTED"
+
+
 def test_strerror_covers_every_status(L):
     for code in range(8):
         assert L.lib.lbq_strerror(code).decode() not in ("", "unknown status")

@@ -124,9 +124,20 @@ def test_8b_nf4dq_layer(li):
         ref_l = O.lora_fwd(Xh, w_ref, bf16_bits_host(A), bf16_bits_host(B), 1.0)
         assert_close(bf16_bits_host(Yl[ms_t]), ref_l, what=f"{nm} lora m={m}")
         del Yl
+    dY = SI.dev_bf16_normal(SI.seed_of(3, li, SI.SLOT_DY), (m, n), DEV)
+    if nm in ("q", "v"):
+        # LoRA backward: dX on the sampled rows, dA and dB in full (they sum over all m rows).
+        dXl, dA, dB = L.lbq_lora_bwd(X, dY, qw, A, B, 1.0)
+        Ah, Bh = bf16_bits_host(A), bf16_bits_host(B)
+        rX, _, _ = O.lora_bwd(Xh, bf16_rows(dY, ms), w_ref, Ah, Bh, 1.0)
+        assert_close(bf16_bits_host(dXl[ms_t]), rX, what=f"{nm} lora bwd dX m={m}")
+        del dXl
+        _, rA, rB = O.lora_bwd(bf16_bits_host(X), bf16_bits_host(dY), np.zeros((n, k)), Ah, Bh, 1.0)
+        for got, want, what in ((dA, rA, "dA"), (dB, rB, "dB")):
+            fro, mx = O.rel_errors(host(got).astype(np.float64), want)
+            assert fro <= 5e-3 and mx <= 2e-2, f"{nm} lora bwd {what}: rel_fro={fro:.3e} max_rel={mx:.3e}"
     del X
 
-    dY = SI.dev_bf16_normal(SI.seed_of(3, li, SI.SLOT_DY), (m, n), DEV)
     dX = L.lbq_linear_bwd_dx(dY, qw)
     assert_close(bf16_bits_host(dX[ms_t]), O.linear_bwd_dx(bf16_rows(dY, ms), w_ref),
                  what=f"{nm} nf4dq bwd m={m}")

@@ -17,7 +17,7 @@ import torch
 
 import synth_inputs as SI
 from oracle import lbq_oracle as O
-from gpu_util import (DEV, assert_close, bf16_bits_host, check_quantized_equal,
+from gpu_util import (DEV, assert_close, bf16_bits_host, check_quantized_equal, host,
                             to_dev_bf16, to_dev_f32)
 
 pytestmark = pytest.mark.gpu
@@ -238,6 +238,84 @@ def test_lora_branch_alone_on_zero_weight(L, m, sigma):
     Y = L.lbq_lora_fwd(to_dev_bf16(X), qw, to_dev_bf16(A), to_dev_bf16(B), sigma)
     torch.cuda.synchronize()
     assert_close(bf16_bits_host(Y), O.lora_fwd(X, ref["w_exact"], A, B, sigma))
+
+
+def assert_close_f32(got: torch.Tensor, ref: np.ndarray, what=""):
+    """fp32 adapter gradients against the fp64 oracle, to the matmul tolerance."""
+    fro, mx = O.rel_errors(host(got).astype(np.float64), ref)
+    assert fro <= 5e-3 and mx <= 2e-2, f"{what}: rel_fro={fro:.3e} max_rel={mx:.3e}"
+
+
+@pytest.mark.parametrize("fmtspec", [FORMATS[0], FORMATS[5]], ids=["i4g128", "nf4dq"])
+@pytest.mark.parametrize("m", [1, 5, 64, 130, 300])
+@pytest.mark.parametrize("r", [16, 8, 40, 64])
+def test_lora_bwd_tolerance(L, fmtspec, m, r):
+    fmt, bits, group, dq = fmtspec
+    n, k = 320, 512
+    W = SI.gaussian_weights(9300, n, k)
+    X = SI.bf16_normal(9301 + m, (m, k))
+    dY = SI.bf16_normal(9302 + m, (m, n))
+    A = SI.bf16_normal(9303, (r, k), std=0.01)
+    B = SI.bf16_normal(9304, (n, r), std=0.01)
+    sigma = 16.0 / r
+    qw, ref = _quant_pair(L, W, fmt, bits, group, dq)
+    dX, dA, dB = L.lbq_lora_bwd(to_dev_bf16(X), to_dev_bf16(dY), qw, to_dev_bf16(A), to_dev_bf16(B), sigma)
+    torch.cuda.synchronize()
+    rX, rA, rB = O.lora_bwd(X, dY, ref["w_exact"], A, B, sigma)
+    assert_close(bf16_bits_host(dX), rX, what=f"lora bwd dX {fmt} m={m} r={r}")
+    assert_close_f32(dA, rA, what=f"lora bwd dA m={m} r={r}")
+    assert_close_f32(dB, rB, what=f"lora bwd dB m={m} r={r}")
+
+
+@pytest.mark.parametrize("m", [3, 130])
+@pytest.mark.parametrize("sigma", [1.0, 2.0])
+def test_lora_bwd_on_zero_weight(L, m, sigma):
+    """W == 0 leaves dX = sigma (dY B) A alone: the adapter term of the input
+    gradient is checked without the base product to hide a wrong sigma or a
+    transposed factor."""
+    n, k, r = 256, 384, 16
+    W = np.zeros((n, k), dtype=np.float32)
+    X = SI.bf16_normal(9310 + m, (m, k))
+    dY = SI.bf16_normal(9311 + m, (m, n))
+    A = SI.bf16_normal(9312, (r, k), std=0.05)
+    B = SI.bf16_normal(9313, (n, r), std=0.05)
+    qw, ref = _quant_pair(L, W, "nf4", 4, 64, True)
+    dX, dA, dB = L.lbq_lora_bwd(to_dev_bf16(X), to_dev_bf16(dY), qw, to_dev_bf16(A), to_dev_bf16(B), sigma)
+    torch.cuda.synchronize()
+    rX, rA, rB = O.lora_bwd(X, dY, ref["w_exact"], A, B, sigma)
+    assert np.abs(ref["w_exact"]).max() == 0.0
+    assert_close(bf16_bits_host(dX), rX, what=f"zero-W lora dX sigma={sigma}")
+    assert_close_f32(dA, rA, what="zero-W dA")
+    assert_close_f32(dB, rB, what="zero-W dB")
+
+
+def test_lora_bwd_empty_batch_zeros_adapter_grads(L):
+    n, k, r = 128, 256, 16
+    qw, _ = _quant_pair(L, SI.gaussian_weights(9320, n, k), "minmax", 4, 128, False)
+    X = torch.empty((0, k), dtype=torch.bfloat16, device=DEV)
+    dY = torch.empty((0, n), dtype=torch.bfloat16, device=DEV)
+    A = to_dev_bf16(SI.bf16_normal(9321, (r, k)))
+    B = to_dev_bf16(SI.bf16_normal(9322, (n, r)))
+    dA = torch.full((r, k), 7.0, dtype=torch.float32, device=DEV)
+    dB = torch.full((n, r), 7.0, dtype=torch.float32, device=DEV)
+    _, dA, dB = L.lbq_lora_bwd(X, dY, qw, A, B, 1.0, dA=dA, dB=dB)
+    torch.cuda.synchronize()
+    assert not host(dA).any() and not host(dB).any()
+
+
+def test_lora_bwd_deterministic(L):
+    n, k, r, m = 512, 1024, 16, 700
+    qw, _ = _quant_pair(L, SI.gaussian_weights(9330, n, k), "nf4", 4, 64, True)
+    X = to_dev_bf16(SI.bf16_normal(9331, (m, k)))
+    dY = to_dev_bf16(SI.bf16_normal(9332, (m, n)))
+    A = to_dev_bf16(SI.bf16_normal(9333, (r, k), std=0.01))
+    B = to_dev_bf16(SI.bf16_normal(9334, (n, r), std=0.01))
+    first = [t.clone() for t in L.lbq_lora_bwd(X, dY, qw, A, B, 1.0)]
+    for _ in range(2):
+        again = L.lbq_lora_bwd(X, dY, qw, A, B, 1.0)
+        for a, b in zip(first, again):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
 
 
 # ------------------------------------------------------------------ mixed precision

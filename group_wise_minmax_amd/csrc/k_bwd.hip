@@ -285,74 +285,6 @@ struct BwdLauncher {
   }
 };
 
-// ---------------------------------------------------------------------------
-// LoRA prologue: T[m][j] = bf16(sigma * sum_k X[m][k] A[j][k]) for j < r, and 0
-// for r <= j < rp.  A workgroup owns 16 rows of X; its four waves split the
-// K-steps and reduce through LDS.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_lora_t(const uint16_t* __restrict__ X, int m, int64_t K,
-                                               const uint16_t* __restrict__ A, int r, int rp,
-                                               float sigma, uint16_t* __restrict__ Tout) {
-  __shared__ f32x4_t red[4][4][64];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int li = lane & 15, lg = lane >> 4;
-  const int64_t m0 = (int64_t)blockIdx.x * 16;
-  const int nt = rp / 16;
-  f32x4_t acc[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int64_t mr = m0 + li;
-  const int64_t steps = K / 32;
-  // Buffer resources: X rows past m and A rows past r read as zeros.
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (int64_t)m * K * 2);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (int64_t)r * K * 2);
-  const uint32_t xo = (uint32_t)((mr * K + 8 * lg) * 2);
-  // Wave w takes K-steps w, w+4, ...; U steps' loads are issued before their MFMAs.
-  constexpr int U = 4;
-  for (int64_t s0 = wave; s0 < steps; s0 += 4 * U) {
-    u32x4_t xa[U], ab[U][4];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t s = min(s0 + 4 * u, steps - 1);  // clamped; extra steps are masked below
-      const int ko = (int)(32 * s * 2);
-      xa[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, xo, ko, 0));
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (t < nt)
-          ab[u][t] = __builtin_bit_cast(
-              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                           ra, (uint32_t)(((16 * t + li) * K + 8 * lg) * 2), ko, 0));
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (s0 + 4 * u >= steps) break;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (t < nt) acc[t] = mfma16x16x32(xa[u], ab[u][t], acc[t]);
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < 4; ++t) red[wave][t][lane] = acc[t];
-  __syncthreads();
-  if (wave == 0) {
-    for (int t = 0; t < nt; ++t) {
-      f32x4_t v = red[0][t][lane];
-#pragma unroll
-      for (int q = 1; q < 4; ++q) {
-        const f32x4_t u = red[q][t][lane];
-        v[0] += u[0]; v[1] += u[1]; v[2] += u[2]; v[3] += u[3];
-      }
-      const int j = 16 * t + li;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t row = m0 + 4 * lg + i;
-        if (row < m) Tout[row * rp + j] = (uint16_t)((j < r) ? bf16_rne(sigma * v[i]) : 0u);
-      }
-    }
-  }
-}
-
 }  // namespace
 
 hipError_t launch_bwd_dx(WKind kind, const WView& w, const uint16_t* dY, int64_t m,
@@ -360,11 +292,5 @@ hipError_t launch_bwd_dx(WKind kind, const WView& w, const uint16_t* dY, int64_t
   return dispatch_kind<BwdLauncher>(kind, w, dY, m, dX, lora, tab, s);
 }
 
-hipError_t launch_lora_t(const uint16_t* X, int64_t m, int64_t k, const uint16_t* A, int32_t r,
-                         int32_t rp, float sigma, uint16_t* T, hipStream_t s) {
-  const dim3 grid((unsigned)((m + 15) / 16));
-  hipLaunchKernelGGL(k_lora_t, grid, dim3(256), 0, s, X, (int)m, k, A, (int)r, (int)rp, sigma, T);
-  return hipGetLastError();
-}
 
 }  // namespace lbq

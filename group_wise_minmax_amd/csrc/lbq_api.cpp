@@ -181,6 +181,7 @@ lbq_status check_fwd_common(const lbq_desc* desc, const lbq_qtensor* q, const ui
 }
 
 int32_t round_rank(int32_t r) { return (r + 31) / 32 * 32; }
+int64_t round_rows(int64_t m) { return (m + 31) / 32 * 32; }
 
 // Forward kernel choice: single-token decode streams the weight with x staged
 // in LDS (or the multi-row GEMV when x does not fit); 2 <= m <= 64 uses the
@@ -302,11 +303,15 @@ lbq_status lbq_linear_bwd_dx(const lbq_desc* desc, const lbq_qtensor* q, const u
 // partial sums of the dA / dB reductions (reused by both).
 static size_t align16(size_t b) { return (b + 15) / 16 * 16; }
 
+// LoRA backward workspace: Bt [rp][n], G [m][rp], Gt and Tt [rp][mp] (bf16),
+// then fp32 partial sums shared by the four reductions (they run in turn).
 size_t lbq_lora_bwd_workspace_bytes(const lbq_desc* desc, int64_t m, int32_t r) {
   if (check_desc(desc) != LBQ_OK || m <= 0 || r < 1 || r > 64) return 0;
   const size_t rp = (size_t)round_rank(r);
-  const size_t part = std::max(lbq::lora_outer_part_bytes(m, desc->k, r), lbq::lora_outer_part_bytes(m, desc->n, r));
-  return align16(rp * (size_t)desc->n * 2) + 2 * align16((size_t)m * rp * 2) + align16(part);
+  const size_t mp = (size_t)round_rows(m);
+  const size_t part = std::max(std::max(lbq::lora_xa_part_bytes(m, desc->n, r), lbq::lora_xa_part_bytes(m, desc->k, r)),
+                               std::max(lbq::lora_outer_part_bytes(m, desc->k, r), lbq::lora_outer_part_bytes(m, desc->n, r)));
+  return align16(rp * (size_t)desc->n * 2) + align16((size_t)m * rp * 2) + 2 * align16(rp * mp * 2) + align16(part);
 }
 
 lbq_status lbq_lora_bwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X,
@@ -334,36 +339,42 @@ lbq_status lbq_lora_bwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16
   if (workspace == nullptr || ws_bytes < need) return fail(LBQ_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
   if (!aligned(workspace, 16)) return fail(LBQ_E_ALIGN, "workspace must be 16-byte aligned");
   const int32_t rp = round_rank(r);
+  const int64_t mp = round_rows(m);
   uint8_t* p = static_cast<uint8_t*>(workspace);
   uint16_t* Bt = reinterpret_cast<uint16_t*>(p);
   p += align16((size_t)rp * (size_t)desc->n * 2);
   uint16_t* G = reinterpret_cast<uint16_t*>(p);
   p += align16((size_t)m * rp * 2);
-  uint16_t* T = reinterpret_cast<uint16_t*>(p);
-  p += align16((size_t)m * rp * 2);
+  uint16_t* Gt = reinterpret_cast<uint16_t*>(p);
+  p += align16((size_t)rp * mp * 2);
+  uint16_t* Tt = reinterpret_cast<uint16_t*>(p);
+  p += align16((size_t)rp * mp * 2);
   float* part = reinterpret_cast<float*>(p);
+  // G = bf16(sigma dY B) row-major for the input gradient and transposed for
+  // dA; T = bf16(sigma X A^T) transposed for dB.
   hipError_t e = lbq::launch_transpose_b(B, desc->n, r, rp, Bt, s);
-  if (e == hipSuccess) e = lbq::launch_lora_t(dY, m, desc->n, Bt, r, rp, sigma, G, s);
-  if (e == hipSuccess) e = lbq::launch_lora_t(X, m, desc->k, A, r, rp, sigma, T, s);
+  if (e == hipSuccess) e = lbq::launch_lora_xa(dY, m, desc->n, Bt, r, rp, sigma, part, G, Gt, mp, s);
+  if (e == hipSuccess) e = lbq::launch_lora_xa(X, m, desc->k, A, r, rp, sigma, part, nullptr, Tt, mp, s);
   if (e != hipSuccess) return hip_status(e, "lbq_lora_bwd (adapter products)");
   const lbq::LoraDx lora{G, A, r, rp};
   e = lbq::launch_bwd_dx(kind_of(desc), view_of(desc, q), dY, m, dX, lora, nf4_table(), s);
   if (e != hipSuccess) return hip_status(e, "lbq_lora_bwd (input gradient)");
-  e = lbq::launch_lora_outer(G, r, rp, X, m, desc->k, false, part, dA, s);
-  if (e == hipSuccess) e = lbq::launch_lora_outer(T, r, rp, dY, m, desc->n, true, part, dB, s);
+  e = lbq::launch_lora_outer(Gt, mp, r, X, m, desc->k, false, part, dA, s);
+  if (e == hipSuccess) e = lbq::launch_lora_outer(Tt, mp, r, dY, m, desc->n, true, part, dB, s);
   return hip_status(e, "lbq_lora_bwd (adapter gradients)");
 }
 
 
-// LoRA workspace: bf16 T = sigma X A^T [m][rp], then (16-byte aligned) the
-// small-batch kernel's fp32 partials when that kernel runs.
+// LoRA workspace: bf16 T = sigma X A^T [m][rp], then (16-byte aligned) fp32
+// partial sums, first of T's product and then of the small-batch kernel when
+// that kernel runs.
 static size_t lora_t_bytes(int64_t m, int32_t r) {
   return ((size_t)m * (size_t)round_rank(r) * sizeof(uint16_t) + 15) / 16 * 16;
 }
 
 size_t lbq_lora_workspace_bytes(const lbq_desc* desc, int64_t m, int32_t r) {
-  if (check_desc(desc) != LBQ_OK || m <= 0 || r < 1) return 0;
-  return lora_t_bytes(m, r) + fwd_workspace(desc, m, true);
+  if (check_desc(desc) != LBQ_OK || m <= 0 || r < 1 || r > 64) return 0;
+  return lora_t_bytes(m, r) + std::max(lbq::lora_xa_part_bytes(m, desc->k, r), fwd_workspace(desc, m, true));
 }
 
 lbq_status lbq_lora_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X, int64_t m,
@@ -383,11 +394,11 @@ lbq_status lbq_lora_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int32_t rp = round_rank(r);
   uint16_t* T = static_cast<uint16_t*>(workspace);
-  hipError_t e = lbq::launch_lora_t(X, m, desc->k, A, r, rp, sigma, T, s);
+  void* part = static_cast<uint8_t*>(workspace) + lora_t_bytes(m, r);
+  hipError_t e = lbq::launch_lora_xa(X, m, desc->k, A, r, rp, sigma, static_cast<float*>(part), T, nullptr, m, s);
   if (e != hipSuccess) return hip_status(e, "lbq_lora_fwd (adapter product)");
   const lbq::LoraEpi lora{T, B, r, rp};
   const lbq::WView w = view_of(desc, q);
-  void* part = static_cast<uint8_t*>(workspace) + lora_t_bytes(m, r);
   return hip_status(dispatch_fwd(desc, w, X, m, Y, ldy, q->out_rows, lora, part, s), "lbq_lora_fwd");
 }
 

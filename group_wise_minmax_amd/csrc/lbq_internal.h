@@ -84,17 +84,24 @@ hipError_t launch_gemm_fwd(WKind kind, const WView& w, const uint16_t* X, int64_
                            const LoraEpi& lora, const Nf4Table& tab, hipStream_t s);
 hipError_t launch_bwd_dx(WKind kind, const WView& w, const uint16_t* dY, int64_t m,
                          uint16_t* dX, const LoraDx& lora, const Nf4Table& tab, hipStream_t s);
-// LoRA backward helpers: Bt = B^T zero-padded to rp rows; out = sum over rows t
-// of P[t][j] * Q[t][c] (fp32, [r][C], or [C][r] with transpose) using `part`
-// (lora_outer_part_bytes) for per-range partial sums.
+// Adapter products and gradients (k_lora.hip).
+// Bt = B^T zero-padded to rp rows.
 hipError_t launch_transpose_b(const uint16_t* B, int64_t n, int32_t r, int32_t rp, uint16_t* Bt,
                               hipStream_t s);
+// T = bf16(sigma * X . A^T) (X [m][K], A [r][K]) into Trm [m][rp] and/or the
+// transposed Ttr [rp][mp] (mp >= m, a multiple of 32), zero past r and past m;
+// either output may be null.  `part` holds lora_xa_part_bytes(m, K, r) bytes.
+size_t lora_xa_part_bytes(int64_t m, int64_t K, int32_t r);
+hipError_t launch_lora_xa(const uint16_t* X, int64_t m, int64_t K, const uint16_t* A, int32_t r,
+                          int32_t rp, float sigma, float* part, uint16_t* Trm, uint16_t* Ttr,
+                          int64_t mp, hipStream_t s);
+// out = sum over rows t < m of Pt[j][t] * Q[t][c] (Pt [rp][mp], zero past m;
+// Q [m][C], C % 8 == 0), fp32 [r][C], or [C][r] with transpose.  `part`
+// holds lora_outer_part_bytes(m, C, r) bytes.
 size_t lora_outer_part_bytes(int64_t m, int64_t C, int32_t r);
-hipError_t launch_lora_outer(const uint16_t* P, int32_t r, int32_t rp, const uint16_t* Q, int64_t m,
+hipError_t launch_lora_outer(const uint16_t* Pt, int64_t mp, int32_t r, const uint16_t* Q, int64_t m,
                              int64_t C, bool transpose, float* part, float* out, hipStream_t s);
 hipError_t launch_fill_zero_f32(float* p, int64_t count, hipStream_t s);
-hipError_t launch_lora_t(const uint16_t* X, int64_t m, int64_t k, const uint16_t* A,
-                         int32_t r, int32_t rp, float sigma, uint16_t* T, hipStream_t s);
 
 // Largest m served by the wavefront-reduction GEMV (used for m == 1 when x does
 // not fit the LDS-staged kernel) and by the small-batch MFMA kernel.

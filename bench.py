@@ -8,8 +8,11 @@ One step is one pass of the whole hot path over a LLaMA-3-8B decoder layer
   quant_nf4dq  quantize + pack the 7 weights, NF4 block 64 + double quant
   dequant      dequantize the 7 NF4-DQ weights to bf16
   gemv_m1      Y = X W^T at m = 1, INT4 g128, over R distinct weight copies
-               (R * 118 MB > 2 x 256 MB Infinity Cache, so weights stream from HBM)
-  gemv_m16     the same at m = 16
+               (R * 118 MB > 2 x 256 MB Infinity Cache, so weights stream from HBM);
+               q/k/v and gate/up share X and run as one launch each
+               (lbq_linear_fwd_grouped), o and down alone: 4 launches per layer
+  gemv_m1_per_linear  the same with one launch per linear (7 per layer)
+  gemv_m16     m = 16, one launch per linear
   gemm_m2048   INT4 g128 forward at m = 2048
   fwd_m4096    NF4-DQ forward at m = 4096 (2 x 2048 tokens)       <- headline
   lora_m4096   NF4-DQ forward + rank-16 LoRA on q and v at m = 4096
@@ -17,7 +20,8 @@ One step is one pass of the whole hot path over a LLaMA-3-8B decoder layer
   lora_bwd_m4096  NF4-DQ LoRA backward (dX with the adapter term, dA, dB),
                rank 16 on q and v, at m = 4096
   chmix_70b_m1     70B-shaped layer, per-channel 25% INT4 g128 / 75% INT2 g64
-                   (two launches per linear, each scattering its rows of Y), m = 1
+                   (each format's rows scatter into Y), m = 1: the linears that
+                   share X in one call, one launch per format (8 per layer)
   chmix_70b_m1024  the same at m = 1024
   copy_1g      (only with --phases) a plain 1 GiB device-to-device copy, the
                reference kernel for scaling hardware byte counters
@@ -71,7 +75,7 @@ def load_traffic(kernel: str, units_per_launch=None):
     return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
-ALL_PHASES = ("quant_int4", "quant_nf4dq", "dequant", "gemv_m1", "gemv_m16", "gemm_m2048",
+ALL_PHASES = ("quant_int4", "quant_nf4dq", "dequant", "gemv_m1", "gemv_m1_per_linear", "gemv_m16", "gemm_m2048",
               "fwd_m4096", "lora_m4096", "bwd_m4096", "lora_bwd_m4096", "chmix_70b_m1", "chmix_70b_m1024")
 EXTRA_PHASES = ("copy_1g",)  # opt-in: plain 1 GiB device copy (counter calibration)
 
@@ -79,8 +83,8 @@ EXTRA_PHASES = ("copy_1g",)  # opt-in: plain 1 GiB device copy (counter calibrat
 # Kernel-name patterns (rocprofv3 demangled names) of the kernels whose HBM
 # traffic the JSON line reports.
 TRAFFIC_KERNELS = {
-    "fwd_m4096_big": "k_gemm_fwd<5, 256, 256, 4, 2, false>",
-    "gemv_m1": "k_gemv1<0,",
+    "fwd_m4096_big": ("k_gemm_fwd<5, 256, 256, 4, 2, false>",),
+    "gemv_m1": ("k_gemv1<0,", "k_gemv1_set<0,"),
 }
 
 
@@ -106,9 +110,9 @@ def write_traffic(fetch_csv: str, write_csv: str) -> dict:
     out = {"kernel_source_hash": kernel_source_hash(),
            "copy_1GiB": {"FETCH_SIZE_bytes": copy_f, "WRITE_SIZE_bytes": copy_w, "fetch_factor": cf, "write_factor": cw},
            "kernels": {}}
-    for key, pat in TRAFFIC_KERNELS.items():
-        f = [v for k, vs in fe.items() if pat in k for v in vs]
-        w = [v for k, vs in wr.items() if pat in k for v in vs]
+    for key, pats in TRAFFIC_KERNELS.items():
+        f = [v for k, vs in fe.items() if any(p in k for p in pats) for v in vs]
+        w = [v for k, vs in wr.items() if any(p in k for p in pats) for v in vs]
         if f and w:
             fb, wb = sum(f) / len(f) * cf, sum(w) / len(w) * cw
             out["kernels"][key] = {"dispatches": len(f), "fetch_bytes_per_launch": round(fb),
@@ -150,7 +154,7 @@ def build_workload(L, SI, torch, dev, R, want):
     def ys(m, dim_of, on):
         return {nm: torch.empty((m, dim_of[nm]), dtype=torch.bfloat16, device=dev) for nm in names} if on else {}
 
-    X1, Y1 = xs(2, SI.SLOT_X, 0, 1, K_of, need("gemv_m1")), ys(1, N_of, need("gemv_m1"))
+    X1, Y1 = xs(2, SI.SLOT_X, 0, 1, K_of, need("gemv_m1", "gemv_m1_per_linear")), ys(1, N_of, need("gemv_m1", "gemv_m1_per_linear"))
     X16, Y16 = xs(2, SI.SLOT_X, 100, 16, K_of, need("gemv_m16")), ys(16, N_of, need("gemv_m16"))
     X2k, Y2k = xs(2, SI.SLOT_X, 200, 2048, K_of, need("gemm_m2048")), ys(2048, N_of, need("gemm_m2048"))
     X4k = xs(3, SI.SLOT_X, 0, 4096, K_of, need("fwd_m4096", "lora_m4096", "lora_bwd_m4096"))
@@ -216,6 +220,19 @@ def build_workload(L, SI, torch, dev, R, want):
                     L.lbq_linear_fwd(X[nm], c[nm], out=Y[nm])
         return f
 
+    # Linears that read the same activation in a decoder layer: one launch each.
+    GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+
+    def p_gemv_grouped(X, Y):
+        def f():
+            for c in copies:
+                for g in GROUPS:
+                    if len(g) == 1:
+                        L.lbq_linear_fwd(X[g[0]], c[g[0]], out=Y[g[0]])
+                    else:
+                        L.lbq_linear_fwd_grouped(X[g[0]], [c[nm] for nm in g], outs=[Y[nm] for nm in g])
+        return f
+
     def p_gemm(qs, X, Y):
         def f():
             for nm in names:
@@ -238,9 +255,14 @@ def build_workload(L, SI, torch, dev, R, want):
             L.lbq_lora_bwd(X4k[nm], dY[nm], qn[nm], A, B, 1.0, dX=dX[nm], dA=dA, dB=dB, workspace=ws)
 
     def p_chmix_m1():
-        for nm, a, b, x1, x1k, y1, y1k in cm:
-            L.lbq_linear_fwd(x1, a, out=y1)
-            L.lbq_linear_fwd(x1, b, out=y1)
+        # per activation group, both row sets of every linear in one call
+        # (one launch per format: INT4 g128 and INT2 g64)
+        by = {e[0]: e for e in cm}
+        for g in GROUPS:
+            x1 = by[g[0]][3]
+            qs = [q for nm in g for q in by[nm][1:3]]
+            ys = [by[nm][5] for nm in g for _ in range(2)]
+            L.lbq_linear_fwd_grouped(x1, qs, outs=ys)
 
     def p_chmix_m1024():
         for nm, a, b, x1, x1k, y1, y1k in cm:
@@ -255,12 +277,16 @@ def build_workload(L, SI, torch, dev, R, want):
 
     flop = lambda m: sum(2 * m * n * k for n, k in shapes.values())
     gemv_bytes = lambda m: sum(bytes_fwd(c[nm], m, N_of[nm], K_of[nm]) for c in copies for nm in names)
+    # grouped: X is read once per launch
+    gemv_bytes_grouped = lambda: sum(c[nm].nbytes() + 2 * N_of[nm] for c in copies for nm in names) + \
+        len(copies) * sum(2 * K_of[g[0]] for g in GROUPS)
     quant_bytes = lambda qs: sum(4 * N_of[nm] * K_of[nm] + qs[nm].nbytes() for nm in names)
     phases = [
         ("quant_int4", p_quant_int4, lambda: {"bound": "hbm", "bytes": quant_bytes(q4), "launches": 7}),
         ("quant_nf4dq", p_quant_nf4dq, lambda: {"bound": "hbm", "bytes": quant_bytes(qn), "launches": 7}),
         ("dequant", p_dequant, lambda: {"bound": "hbm", "bytes": sum(qn[nm].nbytes() + 2 * N_of[nm] * K_of[nm] for nm in names), "launches": 7}),
-        ("gemv_m1", p_gemv(X1, Y1), lambda: {"bound": "hbm", "bytes": gemv_bytes(1), "launches": 7 * R}),
+        ("gemv_m1", p_gemv_grouped(X1, Y1), lambda: {"bound": "hbm", "bytes": gemv_bytes_grouped(), "launches": len(GROUPS) * R}),
+        ("gemv_m1_per_linear", p_gemv(X1, Y1), lambda: {"bound": "hbm", "bytes": gemv_bytes(1), "launches": 7 * R}),
         ("gemv_m16", p_gemv(X16, Y16), lambda: {"bound": "hbm", "bytes": gemv_bytes(16), "launches": 7 * R}),
         ("gemm_m2048", p_gemm(q4, X2k, Y2k), lambda: {"bound": "mfma", "flop": flop(2048), "launches": 7}),
         ("fwd_m4096", p_gemm(qn, X4k, Y4k), lambda: {"bound": "mfma", "flop": flop(4096), "launches": 7,
@@ -270,7 +296,7 @@ def build_workload(L, SI, torch, dev, R, want):
         ("bwd_m4096", p_bwd, lambda: {"bound": "mfma", "flop": flop(4096), "launches": 7}),
         # dX = dY W + G A, G = dY B, T = X A^T, dA = G^T X, dB = (T^T dY)^T
         ("lora_bwd_m4096", p_lora_bwd, lambda: {"bound": "mfma", "flop": sum(2 * 4096 * N_of[nm] * K_of[nm] + 2 * 4096 * 16 * (2 * N_of[nm] + 3 * K_of[nm]) for nm in lora_bwd), "launches": 14}),
-        ("chmix_70b_m1", p_chmix_m1, lambda: {"bound": "hbm", "bytes": sum(bytes_fwd(a, 1, a.n, a.k) + bytes_fwd(b, 1, b.n, b.k) for _, a, b, *_ in cm), "launches": 14}),
+        ("chmix_70b_m1", p_chmix_m1, lambda: {"bound": "hbm", "bytes": sum(a.nbytes() + b.nbytes() + 2 * (a.n + b.n) for _, a, b, *_ in cm) + sum(2 * next(a.k for nm, a, *_ in cm if nm == g[0]) for g in GROUPS), "launches": 2 * len(GROUPS)}),
         ("chmix_70b_m1024", p_chmix_m1024, lambda: {"bound": "mfma", "flop": sum(2 * 1024 * (a.n + b.n) * a.k for _, a, b, *_ in cm), "launches": 14}),
         ("copy_1g", p_copy, lambda: {"bound": "hbm", "bytes": 2 << 30, "launches": 1}),
     ]
@@ -449,7 +475,7 @@ def main():
     if gemv:
         per_launch = gemv["bytes"] / gemv["launches"]
         ach = per_launch / (gemv["avg_launch_us"] * 1e-6) / 1e9
-        out["roofline_gemv_m1"] = {"kernel": "k_gemv1<INT4 g128> (m=1, 7 linears x copies)", "bound": "hbm",
+        out["roofline_gemv_m1"] = {"kernel": "k_gemv1 / k_gemv1_set <INT4 g128> (m=1: q/k/v, o, gate/up, down launches x copies)", "bound": "hbm",
                                    "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                    "frac": round(ach / HBM_PEAK_GBPS, 4),
                                    "traffic": load_traffic("gemv_m1", per_launch)}

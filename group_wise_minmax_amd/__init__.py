@@ -24,7 +24,7 @@ from typing import Optional
 
 import torch
 
-from ._lib import (LBQ_MINMAX, LBQ_NF4, Desc, LbqError, QTensor, Sizes, check, lib,  # noqa: F401
+from ._lib import (LBQ_MAX_GROUP, LBQ_MINMAX, LBQ_NF4, Desc, LbqError, QTensor, Sizes, check, lib,  # noqa: F401
                    STATUS_CODE, EXPORTED, LIB_PATH)
 
 __all__ = [
@@ -214,6 +214,48 @@ def lbq_linear_fwd(X: torch.Tensor, qw: QuantizedWeight, out: Optional[torch.Ten
                              out.stride(0), _ptr(workspace), 0 if workspace is None else workspace.numel(),
                              _stream(X.device)), "lbq_linear_fwd")
     return out
+
+
+def lbq_linear_fwd_grouped_workspace_bytes(qws, m: int) -> int:
+    descs = (Desc * len(qws))(*[q.desc for q in qws])
+    return lib.lbq_linear_fwd_grouped_workspace_bytes(len(qws), descs, m)
+
+
+def lbq_linear_fwd_grouped(X: torch.Tensor, qws, outs=None, workspace: Optional[torch.Tensor] = None):
+    """Ys[i] = X . deq(W_i)^T for weights that share X and k (see
+    ``lbq_linear_fwd_grouped`` in lbq.h).  Returns the list of outputs; an
+    ``outs`` entry is required where that weight has ``out_rows`` (several
+    weights may scatter into one tensor)."""
+    _need(X, "X", torch.bfloat16)
+    qws = list(qws)
+    count = len(qws)
+    if not 1 <= count <= LBQ_MAX_GROUP:
+        raise ValueError(f"between 1 and {LBQ_MAX_GROUP} weights")
+    m = X.shape[0]
+    if X.dim() != 2 or any(q.k != X.shape[1] for q in qws):
+        raise ValueError("X must be [m, k] with every weight's k")
+    outs = list(outs) if outs is not None else [None] * count
+    if len(outs) != count:
+        raise ValueError("one output per weight")
+    for i, (q, o) in enumerate(zip(qws, outs)):
+        if o is None:
+            if q.out_rows is not None:
+                raise ValueError(f"outs[{i}] must be given when out_rows is set")
+            outs[i] = torch.empty((m, q.n), dtype=torch.bfloat16, device=X.device)
+        o = outs[i]
+        if o.dtype != torch.bfloat16 or o.dim() != 2 or o.shape[0] != m or o.stride(1) != 1:
+            raise ValueError(f"outs[{i}] must be bf16 [m, >=n] with unit column stride")
+    descs = (Desc * count)(*[q.desc for q in qws])
+    qts = (QTensor * count)(*[q.qtensor() for q in qws])
+    ys = (ctypes.c_void_p * count)(*[o.data_ptr() for o in outs])
+    ldys = (ctypes.c_int64 * count)(*[o.stride(0) for o in outs])
+    nbytes = lib.lbq_linear_fwd_grouped_workspace_bytes(count, descs, m)
+    if workspace is None:
+        workspace = _ws(nbytes, X.device)
+    check(lib.lbq_linear_fwd_grouped(count, descs, qts, X.data_ptr(), m, ys, ldys, _ptr(workspace),
+                                     0 if workspace is None else workspace.numel(), _stream(X.device)),
+          "lbq_linear_fwd_grouped")
+    return outs
 
 
 def lbq_linear_bwd_dx(dY: torch.Tensor, qw: QuantizedWeight,

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(HERE, "liblbq.so")
 
 LBQ_MINMAX = 0
 LBQ_NF4 = 1
+LBQ_MAX_GROUP = 8
 
 STATUS = {
     0: "LBQ_OK", 1: "LBQ_E_NULL", 2: "LBQ_E_SHAPE", 3: "LBQ_E_FORMAT", 4: "LBQ_E_ALIGN",
@@ -22,7 +23,8 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 EXPORTED = (
     "lbq_layout", "lbq_quantize", "lbq_dequant", "lbq_linear_workspace_bytes",
-    "lbq_linear_fwd", "lbq_linear_bwd_dx", "lbq_lora_workspace_bytes", "lbq_lora_fwd",
+    "lbq_linear_fwd", "lbq_linear_fwd_grouped_workspace_bytes", "lbq_linear_fwd_grouped",
+    "lbq_linear_bwd_dx", "lbq_lora_workspace_bytes", "lbq_lora_fwd",
     "lbq_lora_bwd_workspace_bytes", "lbq_lora_bwd",
     "lbq_nf4_codebook", "lbq_strerror", "lbq_last_error_detail", "lbq_version",
 )
@@ -67,6 +69,8 @@ def _load() -> ctypes.CDLL:
         "lbq_dequant": (I32, [DP, QP, P, P]),
         "lbq_linear_workspace_bytes": (SZ, [DP, I64]),
         "lbq_linear_fwd": (I32, [DP, QP, P, I64, P, I64, P, SZ, P]),
+        "lbq_linear_fwd_grouped_workspace_bytes": (SZ, [I32, DP, I64]),
+        "lbq_linear_fwd_grouped": (I32, [I32, DP, QP, P, I64, ctypes.POINTER(P), ctypes.POINTER(I64), P, SZ, P]),
         "lbq_linear_bwd_dx": (I32, [DP, QP, P, I64, P, P]),
         "lbq_lora_workspace_bytes": (SZ, [DP, I64, I32]),
         "lbq_lora_fwd": (I32, [DP, QP, P, I64, P, P, I32, ctypes.c_float, P, I64, P, SZ, P]),

@@ -29,7 +29,7 @@ COMMON = [
 ]
 # Quantize/dequantize must be bit-exact: one IEEE op per step, no contraction.
 PER_FILE = {"k_quant.hip": ["-ffp-contract=off"]}
-SOURCES = ["lbq_api.cpp", "k_quant.hip", "k_gemv.hip", "k_gemv1.hip", "k_skinny.hip", "k_gemm_fwd.hip", "k_bwd.hip", "k_lora.hip"]
+SOURCES = ["lbq_api.cpp", "k_quant.hip", "k_gemv1.hip", "k_skinny.hip", "k_gemm_fwd.hip", "k_bwd.hip", "k_lora.hip"]
 
 
 def hipcc() -> str:

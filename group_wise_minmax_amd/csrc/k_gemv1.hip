@@ -8,24 +8,30 @@
 // "QLoRA技术在量化微调中的应用", section QLoRA技术原理 (NF4, double quantization).
 //
 // Structure.
-//  * Prologue: the workgroup stages x in LDS once, already arranged the way the
-//    dot products consume it (see below), with the sum of x over every 16-byte
-//    weight chunk (MinMax).  For NF4 it also builds a 256-entry byte -> pair of
-//    bf16 levels table, 32 copies so each lane of a 32-lane half reads its own
-//    bank.
+//  * One launch serves up to kGemvMaxGroup weights that share x and K (q, k and v
+//    of a layer, gate and up, or the INT4 and INT2 row sets of a mixed-precision
+//    layer in separate launches per kind): the waves are dealt out per weight,
+//    so a wave works on one weight for its whole life.
+//  * x either comes from global memory with each step (the 8-16 KiB vector
+//    stays in L1/L2 and no barrier delays the first weight loads), or, for long
+//    rows, is staged in LDS once per workgroup.  Either way it is arranged the
+//    way the dot products consume it (see below), with the sum of x over every
+//    16-byte weight chunk (MinMax).  NF4 builds a 256-entry byte -> pair of
+//    bf16 levels table in LDS, 32 copies so each lane of a 32-lane half reads
+//    its own bank.
 //  * Work: a wave owns a run of groups of R consecutive rows; each step loads
 //    CB 16-byte chunks of each of the R rows (lanes contiguous along K, 1 KiB
-//    of a row per chunk index), and the loads of step s+1 (weights, scales,
-//    zero points or block absmax) are issued before step s is computed, so
-//    memory and VALU work overlap within a wave.
+//    of a row per chunk index), and the loads of up to D steps (weights,
+//    scales, zero points or block absmax) are in flight while earlier steps
+//    are computed.
 //  * MinMax: codes never become (q - z) * s per weight.  The low and high
 //    nibbles (or 2-bit crumbs) of a weight dword are split into byte vectors
 //    and v_perm_b32 lays two of them next to the byte 0x43, giving the bf16
 //    numbers 128 + q (exact for q < 128) as a pair; v_dot2_f32_bf16 multiplies
 //    the pair into x.  Per chunk (inside one group):
 //        sum x (q - z) s = s * (sum x (128 + q) - (128 + z) sum x).
-//    x is stored in LDS in the same pair order, so the weight side costs about
-//    1.4 VALU operations per code.
+//    x is arranged in the same pair order, so the weight side costs about 1.4
+//    VALU operations per code.
 //  * NF4: each packed byte (two codes) indexes the table and the pair is dotted
 //    with x; the block absmax scales the chunk sum.
 #include "lbq_device.h"
@@ -138,19 +144,58 @@ struct Step {
   u32x4_t wq[CB][R];
   float sc[CB][R];
   int zq[CB][R];
+  u32x4_t xv[CB][Gemv1Traits<KIND>::XQ];  // x of the chunk (global-x mode only)
 };
 
-template <int KIND, int R, int CB, int D>
-__global__ __launch_bounds__(kThreads) void k_gemv1(WView w, const uint16_t* __restrict__ X,
-                                                   uint16_t* __restrict__ Y,
-                                                   const int32_t* __restrict__ out_rows,
-                                                   LoraEpi lora, Nf4Table tab, int gpw) {
+// The weights of one launch.  Waves [wave_end[i-1], wave_end[i]) work on
+// weight i, which has ngroups[i] groups of R rows.  Arrays of fields (not of
+// structs) so that a wave finds its weight from one scalar load of wave_end.
+struct Gemv1Set {
+  WView w[kGemvMaxGroup];
+  uint16_t* y[kGemvMaxGroup];
+  const int32_t* out_rows[kGemvMaxGroup];
+  int wave_end[kGemvMaxGroup];
+  int ngroups[kGemvMaxGroup];
+  int count;
+};
+
+// x chunk `c` (natural order, from global or from the raw quads) -> arranged
+// dwords and, for MinMax, the chunk's sum of x.
+template <int KIND>
+__device__ __forceinline__ float x_chunk(const u32x4_t* xv, uint32_t* xa) {
+  using G = Gemv1Traits<KIND>;
+  uint32_t xn[G::XD];
+#pragma unroll
+  for (int q = 0; q < G::XQ; ++q) {
+    xn[4 * q] = xv[q][0]; xn[4 * q + 1] = xv[q][1]; xn[4 * q + 2] = xv[q][2]; xn[4 * q + 3] = xv[q][3];
+  }
+  float s0 = 0.f, s1 = 0.f;
+  if constexpr (WKindTraits<KIND>::fmt == FMT_MINMAX) {
+#pragma unroll
+    for (int j = 0; j < G::XD; j += 2) {
+      s0 = dot2_bf16(xn[j], kOnes, s0);
+      s1 = dot2_bf16(xn[j + 1], kOnes, s1);
+    }
+  }
+  arrange_x<KIND>(xn, xa);
+  return s0 + s1;
+}
+
+// The work of one wave (and its share of the workgroup prologue): weight `w`,
+// output `Y` / `out_rows`, row groups [g0, g1) of R rows; `total` == 0 for a
+// wave without work (it still joins the prologue's barriers).
+template <int KIND, int R, int CB, int D, bool XG>
+__device__ __forceinline__ void gemv1_body(const WView& w, uint16_t* __restrict__ Y,
+                                           const int32_t* __restrict__ out_rows, int g0, int g1,
+                                           bool active, const uint16_t* __restrict__ X,
+                                           const LoraEpi& lora, const Nf4Table& tab) {
   using T = WKindTraits<KIND>;
   using G = Gemv1Traits<KIND>;
   constexpr int CPC = G::CPC, XD = G::XD, XQ = G::XQ, GRP = G::GRP;
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int lane = tid & 63;
+
   const int KB = (int)(w.k * T::bits / 8);  // bytes per packed row (< 2^24)
   const int nchunk = KB / 16;               // 16-byte chunks per row
   const int gpr = (int)(w.k / GRP);         // metadata entries per row
@@ -160,19 +205,16 @@ __global__ __launch_bounds__(kThreads) void k_gemv1(WView w, const uint16_t* __r
   float* xsum = reinterpret_cast<float*>(xq + (size_t)XQ * 4 * nchunk);
 
   // ---- work: groups of R rows, steps of CB chunk indices per lane ------------
-  const int ngroups = (int)((w.n + R - 1) / R);
   const int cpl = (nchunk + 63) / 64;      // chunk indices per lane and row
   const int nsteps = (cpl + CB - 1) / CB;  // steps per group
-  const int gw = blockIdx.x * (kThreads / 64) + wave;
-  const int g0 = gw * gpw;
-  const int g1 = min(g0 + gpw, ngroups);
-  const int total = g0 < g1 ? (g1 - g0) * nsteps : 0;
+  const int total = (active && g0 < g1) ? (g1 - g0) * nsteps : 0;
   const int lane32 = lane & 31;
 
   // Buffer loads: the row base is a wave-uniform scalar offset, the lane's
   // chunk a 32-bit vector offset (the boundary keeps (n + 256) * k < 2^32).
   const int64_t nmeta = w.n * gpr;
   const __amdgpu_buffer_rsrc_t r_w = make_rsrc(w.packed, w.n * KB);
+  const __amdgpu_buffer_rsrc_t r_x = make_rsrc(X, w.k * 2);
   __amdgpu_buffer_rsrc_t r_s, r_z;
   if constexpr (T::fmt == FMT_MINMAX) {
     r_s = make_rsrc(w.scales, nmeta * 4);
@@ -187,14 +229,14 @@ __global__ __launch_bounds__(kThreads) void k_gemv1(WView w, const uint16_t* __r
   auto load = [&](int s, Step<KIND, R, CB>& st) {
     const int g = g0 + s / nsteps, b = s % nsteps;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int row = (int)min((int64_t)g * R + r, w.n - 1);
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c = min((b * CB + cb) * 64 + lane, nchunk - 1);  // clamped: always valid
+      const int gc = (c * CPC) / GRP;  // metadata entry of the chunk within the row
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int c = min((b * CB + cb) * 64 + lane, nchunk - 1);  // clamped: always valid
+      for (int r = 0; r < R; ++r) {
+        const int row = (int)min((int64_t)g * R + r, w.n - 1);
         st.wq[cb][r] = __builtin_bit_cast(
             u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_w, (uint32_t)c * 16u, row * KB, 2 /*nt*/));
-        const int gc = (c * CPC) / GRP;  // metadata entry of the chunk within the row
         if constexpr (T::fmt == FMT_MINMAX) {
           st.sc[cb][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)gc * 4u, row * gpr * 4, 0));
           st.zq[cb][r] = __builtin_amdgcn_raw_buffer_load_b8(r_z, (uint32_t)gc, row * gpr, 0);
@@ -209,18 +251,24 @@ __global__ __launch_bounds__(kThreads) void k_gemv1(WView w, const uint16_t* __r
           st.zq[cb][r] = 0;
         }
       }
+      if constexpr (XG) {
+#pragma unroll
+        for (int q = 0; q < XQ; ++q)
+          st.xv[cb][q] = __builtin_bit_cast(
+              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_x, (uint32_t)(c * CPC * 2 + 16 * q), 0, 0));
+      }
     }
   };
 
-  // The loads of the first D steps go out before x is staged, so their
-  // latency overlaps the prologue; afterwards each computed step's slot is
-  // refilled with the step D ahead (a ring of D steps in registers).
+  // The loads of the first D steps go out before the prologue, so their
+  // latency overlaps it; afterwards each computed step's slot is refilled with
+  // the step D ahead (a ring of D steps in registers).
   Step<KIND, R, CB> st[D];
 #pragma unroll
   for (int i = 0; i < D; ++i)
     if (i < total) load(i, st[i]);
 
-  // ---- prologue: arranged x (and chunk sums) in LDS; NF4 table --------------
+  // ---- prologue: NF4 table; arranged x (and chunk sums) in LDS ---------------
   __shared__ float cbs[16];
   if constexpr (T::fmt == FMT_NF4) {
 #pragma unroll
@@ -232,30 +280,22 @@ __global__ __launch_bounds__(kThreads) void k_gemv1(WView w, const uint16_t* __r
       lut[e] = (uint32_t)bf16_rne(cbs[b >> 4]) | ((uint32_t)bf16_rne(cbs[b & 15]) << 16);
     }
   }
-  for (int c = tid; c < nchunk; c += kThreads) {
-    uint32_t xn[XD], xo[XD];
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(X + (int64_t)c * CPC);
+  if constexpr (!XG) {
+    for (int c = tid; c < nchunk; c += kThreads) {
+      u32x4_t xv[XQ];
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(X + (int64_t)c * CPC);
 #pragma unroll
-    for (int q = 0; q < XQ; ++q) {
-      const u32x4_t v = src[q];
-      xn[4 * q] = v[0]; xn[4 * q + 1] = v[1]; xn[4 * q + 2] = v[2]; xn[4 * q + 3] = v[3];
+      for (int q = 0; q < XQ; ++q) xv[q] = src[q];
+      uint32_t xo[XD];
+      const float sx = x_chunk<KIND>(xv, xo);
+      if constexpr (T::fmt == FMT_MINMAX) xsum[c] = sx;
+#pragma unroll
+      for (int q = 0; q < XQ; ++q)
+        reinterpret_cast<u32x4_t*>(xq)[(size_t)q * nchunk + c] =
+            u32x4_t{xo[4 * q], xo[4 * q + 1], xo[4 * q + 2], xo[4 * q + 3]};
     }
-    if constexpr (T::fmt == FMT_MINMAX) {
-      float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-      for (int j = 0; j < XD; j += 2) {
-        s0 = dot2_bf16(xn[j], kOnes, s0);
-        s1 = dot2_bf16(xn[j + 1], kOnes, s1);
-      }
-      xsum[c] = s0 + s1;
-    }
-    arrange_x<KIND>(xn, xo);
-#pragma unroll
-    for (int q = 0; q < XQ; ++q)
-      reinterpret_cast<u32x4_t*>(xq)[(size_t)q * nchunk + c] =
-          u32x4_t{xo[4 * q], xo[4 * q + 1], xo[4 * q + 2], xo[4 * q + 3]};
   }
-  lds_barrier();
+  if constexpr (!XG || T::fmt == FMT_NF4) lds_barrier();
 
   float acc[R];
 #pragma unroll
@@ -267,14 +307,19 @@ __global__ __launch_bounds__(kThreads) void k_gemv1(WView w, const uint16_t* __r
     for (int cb = 0; cb < CB; ++cb) {
       const int c = (b * CB + cb) * 64 + lane;
       const bool cok = c < nchunk;
-      const int cc = cok ? c : 0;
       uint32_t xa[XD];
+      float xs;
+      if constexpr (XG) {
+        xs = x_chunk<KIND>(st.xv[cb], xa);
+      } else {
+        const int cc = cok ? c : 0;
 #pragma unroll
-      for (int q = 0; q < XQ; ++q) {
-        const u32x4_t v = reinterpret_cast<const u32x4_t*>(xq)[(size_t)q * nchunk + cc];
-        xa[4 * q] = v[0]; xa[4 * q + 1] = v[1]; xa[4 * q + 2] = v[2]; xa[4 * q + 3] = v[3];
+        for (int q = 0; q < XQ; ++q) {
+          const u32x4_t v = reinterpret_cast<const u32x4_t*>(xq)[(size_t)q * nchunk + cc];
+          xa[4 * q] = v[0]; xa[4 * q + 1] = v[1]; xa[4 * q + 2] = v[2]; xa[4 * q + 3] = v[3];
+        }
+        xs = (T::fmt == FMT_MINMAX) ? xsum[cc] : 0.f;
       }
-      const float xs = (T::fmt == FMT_MINMAX) ? xsum[cc] : 0.f;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const float p = chunk_dot<KIND>(st.wq[cb][r], xa, lut, lane32);
@@ -309,61 +354,123 @@ __global__ __launch_bounds__(kThreads) void k_gemv1(WView w, const uint16_t* __r
   }
 }
 
-// spw: target steps per wave (each wave keeps up to D steps of loads in
-// flight); the grid never has fewer than min_waves waves when there is that
-// much work.
-template <int KIND, int R, int CB, int D>
-hipError_t launch_r(const WView& w, const uint16_t* X, uint16_t* Y, const int32_t* out_rows,
-                    const LoraEpi& lora, const Nf4Table& tab, hipStream_t s, int spw = 4,
-                    int min_waves = 1024) {
+// One weight (with an optional LoRA term): waves take gpw row groups each.
+template <int KIND, int R, int CB, int D, bool XG>
+__global__ __launch_bounds__(kThreads) void k_gemv1(WView w, const uint16_t* __restrict__ X,
+                                                   uint16_t* __restrict__ Y,
+                                                   const int32_t* __restrict__ out_rows,
+                                                   LoraEpi lora, Nf4Table tab, int gpw) {
+  const int gw = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ngroups = (int)((w.n + R - 1) / R);
+  const int g0 = gw * gpw;
+  gemv1_body<KIND, R, CB, D, XG>(w, Y, out_rows, g0, min(g0 + gpw, ngroups), true, X, lora, tab);
+}
+
+// Several weights sharing x: each wave finds its weight from the wave ranges.
+template <int KIND, int R, int CB, int D, bool XG>
+__global__ __launch_bounds__(kThreads) void k_gemv1_set(Gemv1Set set, const uint16_t* __restrict__ X,
+                                                       Nf4Table tab, int gpw) {
+  const int gw = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int pi = 0, wbeg = 0, wlast = set.wave_end[0];
+#pragma unroll
+  for (int i = 1; i < kGemvMaxGroup; ++i)
+    if (i < set.count) {
+      if (gw >= set.wave_end[i - 1]) { pi = i; wbeg = set.wave_end[i - 1]; }
+      wlast = set.wave_end[i];
+    }
+  const int g0 = (gw - wbeg) * gpw;
+  const LoraEpi none{nullptr, nullptr, 0, 0};
+  gemv1_body<KIND, R, CB, D, XG>(set.w[pi], set.y[pi], set.out_rows[pi], g0, min(g0 + gpw, set.ngroups[pi]),
+                                 gw < wlast, X, none, tab);
+}
+
+// Dynamic LDS per workgroup: the NF4 table, plus the arranged x and chunk sums
+// when x is staged.
+template <int KIND>
+size_t lds_bytes(int64_t k, bool xg) {
   using T = WKindTraits<KIND>;
   using G = Gemv1Traits<KIND>;
-  const int64_t KB = w.k * T::bits / 8;
-  const int64_t nchunk = KB / 16;
-  const size_t lds = (T::fmt == FMT_NF4 ? 256 * kLutCopies * 4 : 0) + (size_t)nchunk * G::XD * 4 +
-                     (T::fmt == FMT_MINMAX ? (size_t)nchunk * 4 : 0);
-  const int64_t ngroups = (w.n + R - 1) / R;
-  const int64_t cpl = (nchunk + 63) / 64;
-  const int64_t nsteps = (cpl + CB - 1) / CB;
-  int64_t waves = (ngroups * nsteps + spw - 1) / spw;
+  const int64_t nchunk = k * T::bits / 8 / 16;
+  size_t b = T::fmt == FMT_NF4 ? 256 * kLutCopies * 4 : 0;
+  if (!xg) b += (size_t)nchunk * G::XD * 4 + (T::fmt == FMT_MINMAX ? (size_t)nchunk * 4 : 0);
+  return b;
+}
+
+// spw: target steps per wave (each wave keeps up to D steps of loads in
+// flight); the grid never has fewer than min_waves waves when there is that
+// much work.  The row groups of all weights share one wave budget; each
+// weight gets whole waves.
+template <int KIND, int R, int CB, int D, bool XG>
+hipError_t launch_set(const WView* ws, uint16_t* const* ys, const int32_t* const* orows, int count,
+                      const uint16_t* X, const LoraEpi& lora, const Nf4Table& tab, hipStream_t s,
+                      int spw, int min_waves = 1024) {
+  using T = WKindTraits<KIND>;
+  const int64_t nchunk = ws[0].k * T::bits / 8 / 16;
+  const int64_t nsteps = ((nchunk + 63) / 64 + CB - 1) / CB;
+  int64_t groups = 0;
+  for (int i = 0; i < count; ++i) groups += (ws[i].n + R - 1) / R;
+  int64_t waves = (groups * nsteps + spw - 1) / spw;
   waves = waves < min_waves ? min_waves : waves;
-  waves = waves > ngroups ? ngroups : waves;
-  const int64_t gpw = (ngroups + waves - 1) / waves;
-  const int64_t nw = (ngroups + gpw - 1) / gpw;
-  const dim3 grid((unsigned)((nw + 3) / 4));
-  hipLaunchKernelGGL((k_gemv1<KIND, R, CB, D>), grid, dim3(kThreads), lds, s, w, X, Y, out_rows, lora,
-                     tab, (int)gpw);
+  waves = waves > groups ? groups : waves;
+  const int64_t gpw = (groups + waves - 1) / waves;
+  Gemv1Set set{};
+  set.count = count;
+  int64_t wend = 0;
+  for (int i = 0; i < count; ++i) {
+    const int64_t ng = (ws[i].n + R - 1) / R;
+    wend += (ng + gpw - 1) / gpw;
+    set.w[i] = ws[i];
+    set.y[i] = ys[i];
+    set.out_rows[i] = orows[i];
+    set.wave_end[i] = (int)wend;
+    set.ngroups[i] = (int)ng;
+  }
+  const dim3 grid((unsigned)((wend + 3) / 4));
+  const size_t lds = lds_bytes<KIND>(ws[0].k, XG);
+  if (count == 1)
+    hipLaunchKernelGGL((k_gemv1<KIND, R, CB, D, XG>), grid, dim3(kThreads), lds, s, ws[0], X, ys[0], orows[0],
+                       lora, tab, (int)gpw);
+  else
+    hipLaunchKernelGGL((k_gemv1_set<KIND, R, CB, D, XG>), grid, dim3(kThreads), lds, s, set, X, tab, (int)gpw);
   return hipGetLastError();
 }
 
 template <int KIND>
 struct Gemv1Launcher {
-  static hipError_t run(const WView& w, const uint16_t* X, uint16_t* Y, const int32_t* out_rows,
-                        const LoraEpi& lora, const Nf4Table& tab, hipStream_t s) {
-    // Measured on the LLaMA-3-8B shapes: MinMax keeps 4 steps of 2 rows x 16 B
-    // per lane in flight with about 2 steps per wave; NF4 (2 chunks per step)
-    // 2 steps with about 4 per wave.
-    if constexpr (WKindTraits<KIND>::fmt == FMT_NF4)
-      return launch_r<KIND, 2, 2, 2>(w, X, Y, out_rows, lora, tab, s, 4);
-    else
-      return launch_r<KIND, 2, 1, 4>(w, X, Y, out_rows, lora, tab, s, 2);
+  static hipError_t run(const WView* ws, uint16_t* const* ys, const int32_t* const* orows, int count,
+                        const uint16_t* X, const LoraEpi& lora, const Nf4Table& tab, hipStream_t s) {
+    using T = WKindTraits<KIND>;
+    const int64_t k = ws[0].k;
+    // Measured on the LLaMA-3-8B shapes.  4-bit MinMax with rows up to 8192
+    // reads x from global memory: under 2048 rows in all, one row per wave
+    // with 2 steps in flight (more waves); otherwise 2 rows with one step in
+    // flight.  Longer rows stage x in LDS and keep 4 steps of 2 rows in
+    // flight.  NF4 (2 chunks per step) stages x with 2 steps in flight, about
+    // 4 per wave.  Rows whose staged x would not fit 64 KiB read x from
+    // global memory.
+    const bool fits = lds_bytes<KIND>(k, false) <= 65536;
+    int64_t rows = 0;
+    for (int i = 0; i < count; ++i) rows += ws[i].n;
+    if constexpr (T::fmt == FMT_NF4) {
+      if (fits) return launch_set<KIND, 2, 2, 2, false>(ws, ys, orows, count, X, lora, tab, s, 4);
+      return launch_set<KIND, 2, 2, 1, true>(ws, ys, orows, count, X, lora, tab, s, 4);
+    } else {
+      if ((T::bits == 4 && k <= 8192) || !fits) {
+        if (rows < 2048) return launch_set<KIND, 1, 1, 2, true>(ws, ys, orows, count, X, lora, tab, s, 2);
+        return launch_set<KIND, 2, 1, 1, true>(ws, ys, orows, count, X, lora, tab, s, 2);
+      }
+      return launch_set<KIND, 2, 1, 4, false>(ws, ys, orows, count, X, lora, tab, s, 2);
+    }
   }
 };
 
 }  // namespace
 
-size_t gemv1_lds_bytes(WKind kind, int64_t k) {
-  const bool nf4 = kind == WK_NF4 || kind == WK_NF4DQ;
-  const int bits = (kind == WK_I2G64 || kind == WK_I2G128) ? 2 : 4;
-  const int64_t nchunk = k * bits / 8 / 16;
-  const int xd = 16 * 8 / bits / 2;
-  return (nf4 ? 256 * kLutCopies * 4 : 0) + (size_t)(nchunk * xd * 4) + (nf4 ? 0 : (size_t)nchunk * 4);
-}
-
-hipError_t launch_gemv1(WKind kind, const WView& w, const uint16_t* X, uint16_t* Y,
-                        const int32_t* out_rows, const LoraEpi& lora, const Nf4Table& tab,
+hipError_t launch_gemv1(WKind kind, const WView* ws, uint16_t* const* ys, const int32_t* const* out_rows,
+                        int count, const uint16_t* X, const LoraEpi& lora, const Nf4Table& tab,
                         hipStream_t s) {
-  return dispatch_kind<Gemv1Launcher>(kind, w, X, Y, out_rows, lora, tab, s);
+  if (count < 1 || count > kGemvMaxGroup) return hipErrorInvalidValue;
+  return dispatch_kind<Gemv1Launcher>(kind, ws, ys, out_rows, count, X, lora, tab, s);
 }
 
 }  // namespace lbq

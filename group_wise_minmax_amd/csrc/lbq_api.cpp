@@ -183,17 +183,14 @@ lbq_status check_fwd_common(const lbq_desc* desc, const lbq_qtensor* q, const ui
 int32_t round_rank(int32_t r) { return (r + 31) / 32 * 32; }
 int64_t round_rows(int64_t m) { return (m + 31) / 32 * 32; }
 
-// Forward kernel choice: single-token decode streams the weight with x staged
-// in LDS (or the multi-row GEMV when x does not fit); 2 <= m <= 64 uses the
-// small-batch MFMA kernel (fp32 partials in `ws` when K is split); larger m
-// the MFMA GEMM with the dequantized weight tile in LDS.
+// Forward kernel choice: single-token decode streams the weight (GEMV);
+// 2 <= m <= 64 uses the small-batch MFMA kernel (fp32 partials in `ws` when K
+// is split); larger m the MFMA GEMM with the dequantized weight tile in LDS.
 hipError_t dispatch_fwd(const lbq_desc* desc, const lbq::WView& w, const uint16_t* X, int64_t m,
                         uint16_t* Y, int64_t ldy, const int32_t* out_rows,
                         const lbq::LoraEpi& lora, void* ws, hipStream_t s) {
   const lbq::WKind kind = kind_of(desc);
-  if (m == 1 && lbq::gemv1_lds_bytes(kind, desc->k) <= 65536)
-    return lbq::launch_gemv1(kind, w, X, Y, out_rows, lora, nf4_table(), s);
-  if (m == 1) return lbq::launch_gemv(kind, w, X, m, Y, ldy, out_rows, lora, nf4_table(), s);
+  if (m == 1) return lbq::launch_gemv1(kind, &w, &Y, &out_rows, 1, X, lora, nf4_table(), s);
   if (m <= lbq::kSkinnyMaxM)
     return lbq::launch_skinny(kind, w, X, m, Y, ldy, out_rows, static_cast<float*>(ws), lora,
                               nf4_table(), s);
@@ -286,6 +283,66 @@ lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint
   const lbq::WView w = view_of(desc, q);
   return hip_status(dispatch_fwd(desc, w, X, m, Y, ldy, q->out_rows, none, workspace, s),
                     "lbq_linear_fwd");
+}
+
+size_t lbq_linear_fwd_grouped_workspace_bytes(int32_t count, const lbq_desc* descs, int64_t m) {
+  if (count < 1 || count > LBQ_MAX_GROUP || descs == nullptr) return 0;
+  size_t need = 0;
+  for (int32_t i = 0; i < count; ++i)
+    if (check_desc(&descs[i]) == LBQ_OK) need = std::max(need, fwd_workspace(&descs[i], m, false));
+  return need;
+}
+
+lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lbq_qtensor* qs,
+                                  const uint16_t* X, int64_t m, uint16_t* const* Ys, const int64_t* ldys,
+                                  void* workspace, size_t ws_bytes, void* stream) {
+  if (count < 1 || count > LBQ_MAX_GROUP)
+    return fail(LBQ_E_SHAPE, "count must be in [1, %d] (got %d)", LBQ_MAX_GROUP, count);
+  if (descs == nullptr || qs == nullptr || Ys == nullptr || ldys == nullptr)
+    return fail(LBQ_E_NULL, "descs, qs, Ys and ldys must be non-NULL");
+  for (int32_t i = 0; i < count; ++i) {
+    const lbq_status st = check_fwd_common(&descs[i], &qs[i], X, m, Ys[i], ldys[i]);
+    if (st != LBQ_OK) return st;
+    if (descs[i].k != descs[0].k)
+      return fail(LBQ_E_SHAPE, "weight %d has k = %lld, weight 0 has %lld", i, (long long)descs[i].k,
+                  (long long)descs[0].k);
+  }
+  if (m == 0) return ok();
+  const size_t need = lbq_linear_fwd_grouped_workspace_bytes(count, descs, m);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
+    return fail(LBQ_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  if (need > 0 && !aligned(workspace, 16)) return fail(LBQ_E_ALIGN, "workspace must be 16-byte aligned");
+  const lbq::LoraEpi none{nullptr, nullptr, 0, 0};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (m == 1) {
+    // One launch per distinct weight kind, in order of first appearance.
+    bool done[LBQ_MAX_GROUP] = {};
+    for (int32_t i = 0; i < count && e == hipSuccess; ++i) {
+      if (done[i]) continue;
+      const lbq::WKind kind = kind_of(&descs[i]);
+      lbq::WView ws[LBQ_MAX_GROUP];
+      uint16_t* ys[LBQ_MAX_GROUP];
+      const int32_t* rows[LBQ_MAX_GROUP];
+      int c = 0;
+      for (int32_t j = i; j < count; ++j) {
+        if (done[j] || kind_of(&descs[j]) != kind) continue;
+        done[j] = true;
+        ws[c] = view_of(&descs[j], &qs[j]);
+        ys[c] = Ys[j];
+        rows[c] = qs[j].out_rows;
+        ++c;
+      }
+      e = lbq::launch_gemv1(kind, ws, ys, rows, c, X, none, nf4_table(), s);
+    }
+  } else {
+    // Larger batches launch each weight in turn (the workspace is reused:
+    // launches on one stream run in order).
+    for (int32_t i = 0; i < count && e == hipSuccess; ++i)
+      e = dispatch_fwd(&descs[i], view_of(&descs[i], &qs[i]), X, m, Ys[i], ldys[i], qs[i].out_rows, none,
+                       workspace, s);
+  }
+  return hip_status(e, "lbq_linear_fwd_grouped");
 }
 
 lbq_status lbq_linear_bwd_dx(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* dY,

@@ -62,14 +62,11 @@ hipError_t launch_quant_nf4(bool dq, const float* W, uint8_t* packed, float* abs
                             const Nf4Table& tab, hipStream_t s);
 hipError_t launch_dequant(WKind kind, const WView& w, uint16_t* out, const Nf4Table& tab,
                           hipStream_t s);
-hipError_t launch_gemv(WKind kind, const WView& w, const uint16_t* X, int64_t m,
-                       uint16_t* Y, int64_t ldy, const int32_t* out_rows,
-                       const LoraEpi& lora, const Nf4Table& tab, hipStream_t s);
-// m == 1 decode GEMV with x staged in LDS; usable when gemv1_lds_bytes(kind, k)
-// fits in 64 KiB of dynamic LDS.
-size_t gemv1_lds_bytes(WKind kind, int64_t k);
-hipError_t launch_gemv1(WKind kind, const WView& w, const uint16_t* X, uint16_t* Y,
-                        const int32_t* out_rows, const LoraEpi& lora, const Nf4Table& tab,
+// m == 1 decode GEMV over up to kGemvMaxGroup weights of one kind that share x
+// and k (ws[i], ys[i], out_rows[i] per weight; the LoRA term only with count 1).
+constexpr int kGemvMaxGroup = 8;
+hipError_t launch_gemv1(WKind kind, const WView* ws, uint16_t* const* ys, const int32_t* const* out_rows,
+                        int count, const uint16_t* X, const LoraEpi& lora, const Nf4Table& tab,
                         hipStream_t s);
 // 2 <= m <= kSkinnyMaxM: MFMA with the weight streamed once; K split over
 // skinny_splits() workgroups whose fp32 partials (workspace) are summed by a
@@ -103,9 +100,7 @@ hipError_t launch_lora_outer(const uint16_t* Pt, int64_t mp, int32_t r, const ui
                              int64_t C, bool transpose, float* part, float* out, hipStream_t s);
 hipError_t launch_fill_zero_f32(float* p, int64_t count, hipStream_t s);
 
-// Largest m served by the wavefront-reduction GEMV (used for m == 1 when x does
-// not fit the LDS-staged kernel) and by the small-batch MFMA kernel.
-constexpr int64_t kGemvMaxM = 4;
+// Largest m served by the small-batch MFMA kernel.
 constexpr int64_t kSkinnyMaxM = 64;
 
 }  // namespace lbq

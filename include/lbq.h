@@ -167,6 +167,28 @@ lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint
                           int64_t m, uint16_t* Y, int64_t ldy, void* workspace,
                           size_t ws_bytes, void* stream);
 
+/* Largest count accepted by lbq_linear_fwd_grouped. */
+#define LBQ_MAX_GROUP 8
+
+/* Workspace bytes lbq_linear_fwd_grouped needs for m rows (0 when none). */
+size_t lbq_linear_fwd_grouped_workspace_bytes(int32_t count, const lbq_desc* descs, int64_t m);
+
+/* Forward of several frozen linears that read the same input X (the q, k and
+ * v projections of an attention block, gate and up of an MLP, or the INT4 and
+ * INT2 row sets of a channel-mixed layer, [GB] 模型量化):
+ *   Ys[i] = X . deq(W_i)^T   for 0 <= i < count, each as in lbq_linear_fwd.
+ * descs, qs, Ys, ldys: host arrays of `count` entries (1 <= count <=
+ * LBQ_MAX_GROUP); every weight has the same k.  Several weights may scatter
+ * (out_rows) into disjoint columns of one Y.  Every weight is checked as in
+ * lbq_linear_fwd before anything is enqueued.  At m == 1 the weights of one
+ * kind stream through a single GEMV launch (one launch per distinct kind); at
+ * larger m each weight is launched in turn, reusing the workspace
+ * (lbq_linear_fwd_grouped_workspace_bytes). */
+lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lbq_qtensor* qs,
+                                  const uint16_t* X, int64_t m, uint16_t* const* Ys,
+                                  const int64_t* ldys, void* workspace, size_t ws_bytes,
+                                  void* stream);
+
 /* Input gradient through the frozen weight, dX = dY . deq(W) ([QL]
  * QLoRA技术原理: gradients pass through the frozen 4-bit model):
  *   dX[i][k] = bf16( sum_j dY[i][j] * w_hat[j][k] ), fp32 accumulation.

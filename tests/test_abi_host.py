@@ -219,6 +219,41 @@ def test_lora_error_paths(L):
     assert _status(L, args(ws=FAKE + 8)) == "LBQ_E_ALIGN"
 
 
+def test_grouped_fwd_error_paths(L):
+    lib = L.lib
+    import re
+    hdr = open(L._lib.HERE + "/../include/lbq.h").read()
+    assert int(re.search(r"#define LBQ_MAX_GROUP (\d+)", hdr).group(1)) == L.LBQ_MAX_GROUP
+    d = [L.make_desc("minmax", 64, 256), L.make_desc("minmax", 32, 256, 2, 64), L.make_desc("nf4", 128, 256, double_quant=True)]
+
+    def call(descs=d, qs=None, X=FAKE, m=1, ys=None, ldys=None, ws=None, wsb=0, count=None):
+        c = len(descs) if count is None else count
+        D = (L.Desc * len(descs))(*descs)
+        Q = (L.QTensor * len(descs))(*(qs or [_q(L) for _ in descs]))
+        Y = (ctypes.c_void_p * len(descs))(*(ys or [FAKE] * len(descs)))
+        LD = (ctypes.c_int64 * len(descs))(*(ldys or [x.n for x in descs]))
+        return _status(L, lib.lbq_linear_fwd_grouped(c, D, Q, X, m, Y, LD, ws, wsb, None))
+
+    assert call(count=0) == "LBQ_E_SHAPE"
+    assert call(descs=d * 3) == "LBQ_E_SHAPE"  # 9 > LBQ_MAX_GROUP
+    assert _status(L, lib.lbq_linear_fwd_grouped(1, None, None, FAKE, 1, None, None, None, 0, None)) == "LBQ_E_NULL"
+    assert call(descs=[d[0], L.make_desc("minmax", 64, 512)]) == "LBQ_E_SHAPE"  # k differs
+    assert call(X=FAKE + 8) == "LBQ_E_ALIGN"
+    assert call(ys=[FAKE, FAKE + 1, FAKE]) == "LBQ_E_ALIGN"  # weight 1's Y
+    assert call(ldys=[64, 31, 128]) == "LBQ_E_SHAPE"  # weight 1's ldy < n
+    assert call(m=0) == "LBQ_OK"  # empty batch: nothing enqueued
+    # a K split at m = 16 needs fp32 partials: the largest of the weights' workspaces
+    dk = [L.make_desc("minmax", 64, 8192), L.make_desc("nf4", 1024, 8192, double_quant=True)]
+    D = (L.Desc * 2)(*dk)
+    need = lib.lbq_linear_fwd_grouped_workspace_bytes(2, D, 16)
+    assert need == max(lib.lbq_linear_workspace_bytes(ctypes.byref(x), 16) for x in dk) > 0
+    assert lib.lbq_linear_fwd_grouped_workspace_bytes(2, D, 1) == 0
+    assert lib.lbq_linear_fwd_grouped_workspace_bytes(0, D, 16) == 0
+    assert call(descs=dk, m=16, ws=None, wsb=0) == "LBQ_E_WORKSPACE"
+    assert call(descs=dk, m=16, ws=FAKE, wsb=need - 1) == "LBQ_E_WORKSPACE"
+    assert call(descs=dk, m=16, ws=FAKE + 8, wsb=need) == "LBQ_E_ALIGN"
+
+
 def test_lora_bwd_error_paths(L):
     lib = L.lib
     B = ctypes.byref

@@ -104,7 +104,7 @@ def test_forward_tolerance(L, fmtspec, nk, m):
 @pytest.mark.parametrize("fmtspec", FORMATS, ids=FMT_IDS)
 @pytest.mark.parametrize("m", [1, 3, 4])
 def test_forward_gemv_many_rows(L, fmtspec, m):
-    """n >= 4096 takes the four-rows-per-wave GEMV; 4097 leaves a ragged wave."""
+    """n = 4097 rows: many waves per launch and a ragged last row group."""
     fmt, bits, group, dq = fmtspec
     W = SI.gaussian_weights(7100, 4097, 512, outlier_seed=7101)
     X = SI.bf16_normal(7102, (m, 512))
@@ -338,6 +338,70 @@ def test_channel_mix_scatter(L, m):
     Xd = to_dev_bf16(X)
     L.lbq_linear_fwd(Xd, q4, out=Y)
     L.lbq_linear_fwd(Xd, q2, out=Y)
+    Yg = torch.zeros((m, n), dtype=torch.bfloat16, device=DEV)
+    L.lbq_linear_fwd_grouped(Xd, [q4, q2], outs=[Yg, Yg])  # both row sets in one call
     torch.cuda.synchronize()
     ref = O.channel_mix_fwd(X, [(rows4, r4["w_exact"]), (rows2, r2["w_exact"])])
     assert_close(bf16_bits_host(Y), ref)
+    assert np.array_equal(bf16_bits_host(Yg), bf16_bits_host(Y))
+
+
+@pytest.mark.parametrize("fmtspec", FORMATS, ids=FMT_IDS)
+def test_forward_gemv_long_rows(L, fmtspec):
+    """k = 36864: the arranged x no longer fits the GEMV's LDS budget, so x is
+    read from global memory with every step."""
+    fmt, bits, group, dq = fmtspec
+    n, k = 72, 36864
+    W = SI.gaussian_weights(9300, n, k, outlier_seed=9301)
+    X = SI.bf16_normal(9302, (1, k))
+    qw, ref = _quant_pair(L, W, fmt, bits, group, dq)
+    Y = L.lbq_linear_fwd(to_dev_bf16(X), qw)
+    torch.cuda.synchronize()
+    assert_close(bf16_bits_host(Y), O.linear_fwd(X, ref["w_exact"]), what=f"{fmt}{bits}g{group} long rows")
+
+
+# ------------------------------------------------------------------ grouped forward (shared X)
+
+GROUP_SETS = {
+    "three_i4g128": [FORMATS[0]] * 3,
+    "mixed_kinds": [FORMATS[0], FORMATS[1], FORMATS[5], FORMATS[0]],
+}
+
+
+@pytest.mark.parametrize("name", list(GROUP_SETS))
+@pytest.mark.parametrize("k", [1280, 12288])
+@pytest.mark.parametrize("m", [1, 16, 130])
+def test_grouped_fwd_matches_single(L, name, k, m):
+    """Weights sharing X in one call: each output equals the single-weight
+    forward bit for bit (same kernels, same per-row order) and the oracle
+    within the matmul tolerance.  Ragged n; at m = 1 same-kind weights share
+    one launch and the mixed set needs three."""
+    specs = GROUP_SETS[name]
+    ns = [300, 64, 520, 130][:len(specs)]
+    X = SI.bf16_normal(9400 + m, (m, k))
+    qws, refs = [], []
+    for i, ((fmt, bits, group, dq), n) in enumerate(zip(specs, ns)):
+        qw, ref = _quant_pair(L, SI.gaussian_weights(9410 + i, n, k, outlier_seed=9420 + i), fmt, bits, group, dq)
+        qws.append(qw)
+        refs.append(ref)
+    Xd = to_dev_bf16(X)
+    Ys = L.lbq_linear_fwd_grouped(Xd, qws)
+    singles = [L.lbq_linear_fwd(Xd, q) for q in qws]
+    torch.cuda.synchronize()
+    for i, (Y, Y1, ref) in enumerate(zip(Ys, singles, refs)):
+        assert np.array_equal(bf16_bits_host(Y), bf16_bits_host(Y1)), f"{name} weight {i}: grouped != single"
+        assert_close(bf16_bits_host(Y), O.linear_fwd(X, ref["w_exact"]), what=f"{name} weight {i} m={m}")
+
+
+def test_grouped_fwd_exact_on_grid(L):
+    """Three grid weights in one m = 1 launch: exact integer arithmetic, so
+    every output is bf16(X W_i^T) bit for bit."""
+    k = 2048
+    X = SI.bf16_small_ints(9450, (1, k))
+    Ws = [SI.grid_weights(9451 + i, n, k, 128, 4) for i, n in enumerate((136, 8, 72))]
+    qws = [_quant_pair(L, W, "minmax", 4, 128, False)[0] for W in Ws]
+    Ys = L.lbq_linear_fwd_grouped(to_dev_bf16(X), qws)
+    torch.cuda.synchronize()
+    for W, Y in zip(Ws, Ys):
+        exact = O.bf16_to_f64(X) @ W.astype(np.float64).T
+        assert np.array_equal(bf16_bits_host(Y), O.bf16_bits(exact.astype(np.float32)))

@@ -14,7 +14,10 @@ One step is one pass of the whole hot path over a LLaMA-3-8B decoder layer
   gemv_m1_per_linear  the same with one launch per linear (7 per layer)
   gemv_m16     m = 16, one launch per linear
   gemm_m2048   INT4 g128 forward at m = 2048
-  fwd_m4096    NF4-DQ forward at m = 4096 (2 x 2048 tokens)       <- headline
+  fwd_m4096    NF4-DQ forward at m = 4096 (2 x 2048 tokens)       <- headline;
+               q/k/v and gate/up share X and run as one GEMM launch each
+               (their column tiles side by side), o and down alone
+  fwd_m4096_per_linear  the same with one launch per linear
   lora_m4096   NF4-DQ forward + rank-16 LoRA on q and v at m = 4096
   bwd_m4096    NF4-DQ input gradient dX = dY deq(W) at m = 4096
   lora_bwd_m4096  NF4-DQ LoRA backward (dX with the adapter term, dA, dB),
@@ -30,7 +33,8 @@ Each phase is captured once as a HIP graph (torch.cuda.CUDAGraph) and replayed,
 so the timed region holds device work only; HIP events on the launch stream
 bracket every phase of every step.  The JSON line's ``value`` is the dequant-
 GEMM TFLOP/s of fwd_m4096 (2*m*n*k summed over the 7 linears / phase time);
-``gemv_m1_hbm_GBps`` is the other half of the headline metric.
+``gemv_m1_hbm_GBps`` is the other half of the headline metric.  Both count
+the same 7 linears as the per-linear phases; only the launches differ.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -76,14 +80,15 @@ def load_traffic(kernel: str, units_per_launch=None):
 
 
 ALL_PHASES = ("quant_int4", "quant_nf4dq", "dequant", "gemv_m1", "gemv_m1_per_linear", "gemv_m16", "gemm_m2048",
-              "fwd_m4096", "lora_m4096", "bwd_m4096", "lora_bwd_m4096", "chmix_70b_m1", "chmix_70b_m1024")
+              "fwd_m4096", "fwd_m4096_per_linear", "lora_m4096", "bwd_m4096", "lora_bwd_m4096", "chmix_70b_m1",
+              "chmix_70b_m1024")
 EXTRA_PHASES = ("copy_1g",)  # opt-in: plain 1 GiB device copy (counter calibration)
 
 
 # Kernel-name patterns (rocprofv3 demangled names) of the kernels whose HBM
 # traffic the JSON line reports.
 TRAFFIC_KERNELS = {
-    "fwd_m4096_big": ("k_gemm_fwd<5, 256, 256, 4, 2, false>",),
+    "fwd_m4096_big": ("k_gemm_fwd<5, 256, 256, 4, 2, false>", "k_gemm_fwd_set<5, 256, 256, 4, 2>"),
     "gemv_m1": ("k_gemv1<0,", "k_gemv1_set<0,"),
 }
 
@@ -157,8 +162,8 @@ def build_workload(L, SI, torch, dev, R, want):
     X1, Y1 = xs(2, SI.SLOT_X, 0, 1, K_of, need("gemv_m1", "gemv_m1_per_linear")), ys(1, N_of, need("gemv_m1", "gemv_m1_per_linear"))
     X16, Y16 = xs(2, SI.SLOT_X, 100, 16, K_of, need("gemv_m16")), ys(16, N_of, need("gemv_m16"))
     X2k, Y2k = xs(2, SI.SLOT_X, 200, 2048, K_of, need("gemm_m2048")), ys(2048, N_of, need("gemm_m2048"))
-    X4k = xs(3, SI.SLOT_X, 0, 4096, K_of, need("fwd_m4096", "lora_m4096", "lora_bwd_m4096"))
-    Y4k = ys(4096, N_of, need("fwd_m4096"))
+    X4k = xs(3, SI.SLOT_X, 0, 4096, K_of, need("fwd_m4096", "fwd_m4096_per_linear", "lora_m4096", "lora_bwd_m4096"))
+    Y4k = ys(4096, N_of, need("fwd_m4096", "fwd_m4096_per_linear"))
     dY = xs(3, SI.SLOT_DY, 0, 4096, N_of, need("bwd_m4096", "lora_bwd_m4096"))
     dX = ys(4096, K_of, need("bwd_m4096", "lora_bwd_m4096"))
     lora = {}
@@ -239,6 +244,13 @@ def build_workload(L, SI, torch, dev, R, want):
                 L.lbq_linear_fwd(X[nm], qs[nm], out=Y[nm])
         return f
 
+    def gemm_group_units(qs, X, Y):
+        def unit(g):
+            if len(g) == 1:
+                return lambda: L.lbq_linear_fwd(X[g[0]], qs[g[0]], out=Y[g[0]])
+            return lambda: L.lbq_linear_fwd_grouped(X[g[0]], [qs[nm] for nm in g], outs=[Y[nm] for nm in g])
+        return [("+".join(g), unit(g)) for g in GROUPS]
+
     def gemm_units(qs, X, Y):
         return [(nm, (lambda nm=nm: L.lbq_linear_fwd(X[nm], qs[nm], out=Y[nm]))) for nm in names]
 
@@ -289,9 +301,12 @@ def build_workload(L, SI, torch, dev, R, want):
         ("gemv_m1_per_linear", p_gemv(X1, Y1), lambda: {"bound": "hbm", "bytes": gemv_bytes(1), "launches": 7 * R}),
         ("gemv_m16", p_gemv(X16, Y16), lambda: {"bound": "hbm", "bytes": gemv_bytes(16), "launches": 7 * R}),
         ("gemm_m2048", p_gemm(q4, X2k, Y2k), lambda: {"bound": "mfma", "flop": flop(2048), "launches": 7}),
-        ("fwd_m4096", p_gemm(qn, X4k, Y4k), lambda: {"bound": "mfma", "flop": flop(4096), "launches": 7,
-                                                      "units": gemm_units(qn, X4k, Y4k),
-                                                      "unit_flop": {nm: 2 * 4096 * n * k for nm, (n, k) in shapes.items()}}),
+        ("fwd_m4096", None, lambda: {"bound": "mfma", "flop": flop(4096), "launches": len(GROUPS),
+                                     "units": gemm_group_units(qn, X4k, Y4k),
+                                     "unit_flop": {"+".join(g): sum(2 * 4096 * N_of[nm] * K_of[nm] for nm in g) for g in GROUPS}}),
+        ("fwd_m4096_per_linear", None, lambda: {"bound": "mfma", "flop": flop(4096), "launches": 7,
+                                                "units": gemm_units(qn, X4k, Y4k),
+                                                "unit_flop": {nm: 2 * 4096 * n * k for nm, (n, k) in shapes.items()}}),
         ("lora_m4096", p_lora, lambda: {"bound": "mfma", "flop": sum(2 * 4096 * N_of[nm] * K_of[nm] + 2 * 4096 * 16 * (K_of[nm] + N_of[nm]) for nm in lora), "launches": 4}),
         ("bwd_m4096", p_bwd, lambda: {"bound": "mfma", "flop": flop(4096), "launches": 7}),
         # dX = dY W + G A, G = dY B, T = X A^T, dA = G^T X, dB = (T^T dY)^T
@@ -459,19 +474,19 @@ def main():
         "phases": report,
     }
     if head:
-        # Dominant kernel: the 256 x 256-tile NF4+DQ GEMM that serves q, o, gate,
-        # up and down at m = 4096 (k and v, N = 1024, take 128 x 128 tiles).
-        big = ("q", "o", "gate", "up", "down")
+        # Dominant kernel: the 256 x 256-tile NF4+DQ GEMM launches at m = 4096
+        # (o, gate+up side by side, down; the q+k+v launch takes 256 x 128 tiles).
+        big = ("o", "gate+up", "down")
         uf = next(info for name, _, info in runners if name == "fwd_m4096")["unit_flop"]
         us = unit_us["fwd_m4096"]
         t_big = sum(us[u] for u in big)
         ach = sum(uf[u] for u in big) / (t_big * 1e-6) / 1e12
-        out["roofline"] = {"kernel": "k_gemm_fwd<NF4+DQ, 256x256 tile> (q, o, gate, up, down at m=4096)",
+        out["roofline"] = {"kernel": "k_gemm_fwd / k_gemm_fwd_set <NF4+DQ, 256x256 tiles> (o, gate+up, down at m=4096)",
                            "bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(ach / BF16_PEAK_TFLOPS, 4),
                            "traffic": load_traffic("fwd_m4096_big", None),
                            "avg_launch_us": round(t_big / len(big), 2),
-                           "per_linear_us": {u: round(v, 2) for u, v in us.items()}}
+                           "per_launch_us": {u: round(v, 2) for u, v in us.items()}}
     if gemv:
         per_launch = gemv["bytes"] / gemv["launches"]
         ach = per_launch / (gemv["avg_launch_us"] * 1e-6) / 1e9

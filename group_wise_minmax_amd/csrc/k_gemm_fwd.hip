@@ -74,12 +74,12 @@ __device__ __forceinline__ void dequant32(const u32x4_t& raw, float s, float zs,
   }
 }
 
+// One BN x BM output tile (tx, ty) of Y = X . deq(W)^T (+ the LoRA slab).
 template <int KIND, int BN, int BM, int WGN, int WGM, bool LORA>
-__global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint16_t* __restrict__ X,
-                                                          int m, uint16_t* __restrict__ Y,
-                                                          int64_t ldy,
-                                                          const int32_t* __restrict__ out_rows,
-                                                          LoraEpi lora, Nf4Table tab) {
+__device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __restrict__ X, int m,
+                                              uint16_t* __restrict__ Y, int64_t ldy,
+                                              const int32_t* __restrict__ out_rows,
+                                              const LoraEpi& lora, const Nf4Table& tab, int tx, int ty) {
   using T = WKindTraits<KIND>;
   constexpr int NT = WGN * WGM * 64;
   constexpr int CPT = BN * BK / NT;  // codes of one W row a thread dequantizes per stage
@@ -99,9 +99,6 @@ __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint1
   const int lane = tid & 63, wave = tid >> 6;
   const int wn = wave % WGN, wm = wave / WGN;
   const int li = lane & 15, lg = lane >> 4;
-  const int nx = (int)((w.n + BN - 1) / BN), ny = (m + BM - 1) / BM;
-  int tx, ty;
-  tile_of(blockIdx.x, nx, ny, tx, ty);
   const int64_t n0 = (int64_t)tx * BN;
   const int64_t m0 = (int64_t)ty * BM;
   const int64_t K = w.k;
@@ -290,6 +287,68 @@ __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint1
   }
 }
 
+template <int KIND, int BN, int BM, int WGN, int WGM, bool LORA>
+__global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint16_t* __restrict__ X,
+                                                          int m, uint16_t* __restrict__ Y,
+                                                          int64_t ldy,
+                                                          const int32_t* __restrict__ out_rows,
+                                                          LoraEpi lora, Nf4Table tab) {
+  const int nx = (int)((w.n + BN - 1) / BN), ny = (m + BM - 1) / BM;
+  int tx, ty;
+  tile_of(blockIdx.x, nx, ny, tx, ty);
+  gemm_fwd_tile<KIND, BN, BM, WGN, WGM, LORA>(w, X, m, Y, ldy, out_rows, lora, tab, tx, ty);
+}
+
+// Several weights that share X: their column tiles are laid side by side
+// (weight i owns tile columns [tile_end[i-1], tile_end[i])), so one launch
+// covers them all and its last round of tiles is shared.
+struct GemmSet {
+  WView w[kGemvMaxGroup];
+  uint16_t* y[kGemvMaxGroup];
+  int64_t ldy[kGemvMaxGroup];
+  const int32_t* out_rows[kGemvMaxGroup];
+  int tile_end[kGemvMaxGroup];
+  int count;
+};
+
+template <int KIND, int BN, int BM, int WGN, int WGM>
+__global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd_set(GemmSet set, const uint16_t* __restrict__ X,
+                                                              int m, Nf4Table tab) {
+  int nx = set.tile_end[0];
+#pragma unroll
+  for (int i = 1; i < kGemvMaxGroup; ++i)
+    if (i < set.count) nx = set.tile_end[i];
+  int tx, ty;
+  tile_of(blockIdx.x, nx, (m + BM - 1) / BM, tx, ty);
+  int pi = 0, tbeg = 0;
+#pragma unroll
+  for (int i = 1; i < kGemvMaxGroup; ++i)
+    if (i < set.count && tx >= set.tile_end[i - 1]) { pi = i; tbeg = set.tile_end[i - 1]; }
+  const LoraEpi none{nullptr, nullptr, 0, 0};
+  gemm_fwd_tile<KIND, BN, BM, WGN, WGM, false>(set.w[pi], X, m, set.y[pi], set.ldy[pi], set.out_rows[pi],
+                                               none, tab, tx - tbeg, ty);
+}
+
+template <int KIND, int BN, int BM, int WGN, int WGM>
+hipError_t launch_set_cfg(const WView* ws, uint16_t* const* ys, const int64_t* ldys,
+                          const int32_t* const* orows, int count, const uint16_t* X, int64_t m,
+                          const Nf4Table& tab, hipStream_t s) {
+  GemmSet set{};
+  set.count = count;
+  int64_t nx = 0;
+  for (int i = 0; i < count; ++i) {
+    nx += (ws[i].n + BN - 1) / BN;
+    set.w[i] = ws[i];
+    set.y[i] = ys[i];
+    set.ldy[i] = ldys[i];
+    set.out_rows[i] = orows[i];
+    set.tile_end[i] = (int)nx;
+  }
+  const dim3 grid((unsigned)(nx * ((m + BM - 1) / BM))), block(WGN * WGM * 64);
+  hipLaunchKernelGGL((k_gemm_fwd_set<KIND, BN, BM, WGN, WGM>), grid, block, 0, s, set, X, (int)m, tab);
+  return hipGetLastError();
+}
+
 template <int KIND, int BN, int BM, int WGN, int WGM>
 hipError_t launch_cfg(const WView& w, const uint16_t* X, int64_t m, uint16_t* Y, int64_t ldy,
                       const int32_t* out_rows, const LoraEpi& lora, const Nf4Table& tab,
@@ -312,27 +371,55 @@ double fill(int64_t tiles) {
   return (double)tiles / (double)(waves * 256);
 }
 
+// Tile shape with the best (chip fill x per-tile efficiency) for weights of
+// n[0..count) rows: 0 = 256x256, 1 = 256x128, 2 = 128x128.  The per-tile
+// factors are the measured throughput of each shape relative to 256x256 (8
+// waves of 64x128) at full occupancy.
+int pick_tile(const WView* ws, int count, int64_t m) {
+  int64_t t0 = 0, t1 = 0, t2 = 0;
+  for (int i = 0; i < count; ++i) {
+    t0 += ((ws[i].n + 255) / 256) * ((m + 255) / 256);
+    t1 += ((ws[i].n + 255) / 256) * ((m + 127) / 128);
+    t2 += ((ws[i].n + 127) / 128) * ((m + 127) / 128);
+  }
+  const double e0 = fill(t0) * 1.00, e1 = fill(t1) * 0.78, e2 = fill(t2) * 0.74;
+  if (e0 >= e1 && e0 >= e2) return 0;
+  return e1 >= e2 ? 1 : 2;
+}
+
 template <int KIND>
 struct GemmFwdLauncher {
   static hipError_t run(const WView& w, const uint16_t* X, int64_t m, uint16_t* Y, int64_t ldy,
                         const int32_t* out_rows, const LoraEpi& lora, const Nf4Table& tab,
                         hipStream_t s) {
-    // Pick the tile with the best (chip fill x per-tile efficiency).  The
-    // per-tile factors are the measured throughput of each shape relative to
-    // 256x256 (8 waves of 64x128) at full occupancy.
-    const int64_t t256x256 = ((w.n + 255) / 256) * ((m + 255) / 256);
-    const int64_t t256x128 = ((w.n + 255) / 256) * ((m + 127) / 128);
-    const int64_t t128x128 = ((w.n + 127) / 128) * ((m + 127) / 128);
-    const double e0 = fill(t256x256) * 1.00;
-    const double e1 = fill(t256x128) * 0.78;
-    const double e2 = fill(t128x128) * 0.74;
-    if (e0 >= e1 && e0 >= e2) return launch_cfg<KIND, 256, 256, 4, 2>(w, X, m, Y, ldy, out_rows, lora, tab, s);
-    if (e1 >= e2) return launch_cfg<KIND, 256, 128, 4, 2>(w, X, m, Y, ldy, out_rows, lora, tab, s);
-    return launch_cfg<KIND, 128, 128, 2, 2>(w, X, m, Y, ldy, out_rows, lora, tab, s);
+    switch (pick_tile(&w, 1, m)) {
+      case 0: return launch_cfg<KIND, 256, 256, 4, 2>(w, X, m, Y, ldy, out_rows, lora, tab, s);
+      case 1: return launch_cfg<KIND, 256, 128, 4, 2>(w, X, m, Y, ldy, out_rows, lora, tab, s);
+      default: return launch_cfg<KIND, 128, 128, 2, 2>(w, X, m, Y, ldy, out_rows, lora, tab, s);
+    }
+  }
+};
+
+template <int KIND>
+struct GemmFwdSetLauncher {
+  static hipError_t run(const WView* ws, uint16_t* const* ys, const int64_t* ldys, const int32_t* const* orows,
+                        int count, const uint16_t* X, int64_t m, const Nf4Table& tab, hipStream_t s) {
+    switch (pick_tile(ws, count, m)) {
+      case 0: return launch_set_cfg<KIND, 256, 256, 4, 2>(ws, ys, ldys, orows, count, X, m, tab, s);
+      case 1: return launch_set_cfg<KIND, 256, 128, 4, 2>(ws, ys, ldys, orows, count, X, m, tab, s);
+      default: return launch_set_cfg<KIND, 128, 128, 2, 2>(ws, ys, ldys, orows, count, X, m, tab, s);
+    }
   }
 };
 
 }  // namespace
+
+hipError_t launch_gemm_fwd_set(WKind kind, const WView* ws, uint16_t* const* ys, const int64_t* ldys,
+                               const int32_t* const* out_rows, int count, const uint16_t* X, int64_t m,
+                               const Nf4Table& tab, hipStream_t s) {
+  if (count < 1 || count > kGemvMaxGroup) return hipErrorInvalidValue;
+  return dispatch_kind<GemmFwdSetLauncher>(kind, ws, ys, ldys, out_rows, count, X, m, tab, s);
+}
 
 hipError_t launch_gemm_fwd(WKind kind, const WView& w, const uint16_t* X, int64_t m,
                            uint16_t* Y, int64_t ldy, const int32_t* out_rows,

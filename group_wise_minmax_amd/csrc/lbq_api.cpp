@@ -315,7 +315,7 @@ lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lb
   const lbq::LoraEpi none{nullptr, nullptr, 0, 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  if (m == 1) {
+  if (m == 1 || m > lbq::kSkinnyMaxM) {
     // One launch per distinct weight kind, in order of first appearance.
     bool done[LBQ_MAX_GROUP] = {};
     for (int32_t i = 0; i < count && e == hipSuccess; ++i) {
@@ -323,6 +323,7 @@ lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lb
       const lbq::WKind kind = kind_of(&descs[i]);
       lbq::WView ws[LBQ_MAX_GROUP];
       uint16_t* ys[LBQ_MAX_GROUP];
+      int64_t lds[LBQ_MAX_GROUP];
       const int32_t* rows[LBQ_MAX_GROUP];
       int c = 0;
       for (int32_t j = i; j < count; ++j) {
@@ -330,14 +331,16 @@ lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lb
         done[j] = true;
         ws[c] = view_of(&descs[j], &qs[j]);
         ys[c] = Ys[j];
+        lds[c] = ldys[j];
         rows[c] = qs[j].out_rows;
         ++c;
       }
-      e = lbq::launch_gemv1(kind, ws, ys, rows, c, X, none, nf4_table(), s);
+      if (m == 1) e = lbq::launch_gemv1(kind, ws, ys, rows, c, X, none, nf4_table(), s);
+      else e = lbq::launch_gemm_fwd_set(kind, ws, ys, lds, rows, c, X, m, nf4_table(), s);
     }
   } else {
-    // Larger batches launch each weight in turn (the workspace is reused:
-    // launches on one stream run in order).
+    // The small-batch kernel launches each weight in turn (the workspace is
+    // reused: launches on one stream run in order).
     for (int32_t i = 0; i < count && e == hipSuccess; ++i)
       e = dispatch_fwd(&descs[i], view_of(&descs[i], &qs[i]), X, m, Ys[i], ldys[i], qs[i].out_rows, none,
                        workspace, s);

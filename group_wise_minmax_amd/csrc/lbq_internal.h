@@ -79,6 +79,11 @@ hipError_t launch_skinny(WKind kind, const WView& w, const uint16_t* X, int64_t 
 hipError_t launch_gemm_fwd(WKind kind, const WView& w, const uint16_t* X, int64_t m,
                            uint16_t* Y, int64_t ldy, const int32_t* out_rows,
                            const LoraEpi& lora, const Nf4Table& tab, hipStream_t s);
+// m > kSkinnyMaxM over up to kGemvMaxGroup weights of one kind that share X
+// (their column tiles side by side in one launch).
+hipError_t launch_gemm_fwd_set(WKind kind, const WView* ws, uint16_t* const* ys, const int64_t* ldys,
+                               const int32_t* const* out_rows, int count, const uint16_t* X, int64_t m,
+                               const Nf4Table& tab, hipStream_t s);
 hipError_t launch_bwd_dx(WKind kind, const WView& w, const uint16_t* dY, int64_t m,
                          uint16_t* dX, const LoraDx& lora, const Nf4Table& tab, hipStream_t s);
 // Adapter products and gradients (k_lora.hip).

@@ -180,10 +180,11 @@ size_t lbq_linear_fwd_grouped_workspace_bytes(int32_t count, const lbq_desc* des
  * descs, qs, Ys, ldys: host arrays of `count` entries (1 <= count <=
  * LBQ_MAX_GROUP); every weight has the same k.  Several weights may scatter
  * (out_rows) into disjoint columns of one Y.  Every weight is checked as in
- * lbq_linear_fwd before anything is enqueued.  At m == 1 the weights of one
- * kind stream through a single GEMV launch (one launch per distinct kind); at
- * larger m each weight is launched in turn, reusing the workspace
- * (lbq_linear_fwd_grouped_workspace_bytes). */
+ * lbq_linear_fwd before anything is enqueued.  At m == 1 and m > 64 the
+ * weights of one kind run in a single launch (one launch per distinct kind:
+ * a GEMV streaming all of them, or a GEMM whose column tiles cover all of
+ * them); for 2 <= m <= 64 each weight is launched in turn, reusing the
+ * workspace (lbq_linear_fwd_grouped_workspace_bytes). */
 lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lbq_qtensor* qs,
                                   const uint16_t* X, int64_t m, uint16_t* const* Ys,
                                   const int64_t* ldys, void* workspace, size_t ws_bytes,

@@ -144,6 +144,36 @@ def test_8b_nf4dq_layer(li):
 
 
 # ---------------------------------------------------------------------------
+# LLaMA-3-8B layer, linears that share X in one launch (q/k/v, gate/up), as the
+# benchmark runs them: bit-identical to one launch per linear (whose outputs
+# the tests above check against the oracle)
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("fmt,m", [("int4", 1), ("nf4dq", 1), ("nf4dq", 4096), ("int4", 2048)])
+def test_8b_grouped_matches_single(fmt, m):
+    for group in (("q", "k", "v"), ("gate", "up")):
+        qws = []
+        for nm in group:
+            li = NAMES.index(nm)
+            n, k = SI.LLAMA3_8B[nm]
+            W = SI.dev_gaussian_weights(SI.seed_of(2, li, SI.SLOT_W), n, k, DEV)
+            if fmt == "int4":
+                qws.append(L.lbq_quantize(W, "minmax", 4, 128))
+            else:
+                qws.append(L.lbq_quantize(W, "nf4", double_quant=True))
+            del W
+        k = qws[0].k
+        X = SI.dev_bf16_normal(SI.seed_of(3, NAMES.index(group[0]), SI.SLOT_X), (m, k), DEV)
+        Ys = L.lbq_linear_fwd_grouped(X, qws)
+        for nm, q, Y in zip(group, qws, Ys):
+            Y1 = L.lbq_linear_fwd(X, q)
+            assert torch.equal(Y.view(torch.int16), Y1.view(torch.int16)), f"{fmt} {nm} m={m}: grouped != single"
+        del Ys, qws, X
+        torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
 # 70B-shaped layer, channel-mix 25% INT4 g128 / 75% INT2 g64, m = 1 and 1024
 # ---------------------------------------------------------------------------
 

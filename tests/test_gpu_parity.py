@@ -370,12 +370,13 @@ GROUP_SETS = {
 
 @pytest.mark.parametrize("name", list(GROUP_SETS))
 @pytest.mark.parametrize("k", [1280, 12288])
-@pytest.mark.parametrize("m", [1, 16, 130])
+@pytest.mark.parametrize("m", [1, 16, 130, 300])
 def test_grouped_fwd_matches_single(L, name, k, m):
     """Weights sharing X in one call: each output equals the single-weight
     forward bit for bit (same kernels, same per-row order) and the oracle
     within the matmul tolerance.  Ragged n; at m = 1 same-kind weights share
-    one launch and the mixed set needs three."""
+    one launch and the mixed set needs three; at m > 64 the GEMM lays the
+    weights' column tiles side by side."""
     specs = GROUP_SETS[name]
     ns = [300, 64, 520, 130][:len(specs)]
     X = SI.bf16_normal(9400 + m, (m, k))

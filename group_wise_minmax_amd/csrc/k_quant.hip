@@ -189,8 +189,36 @@ __global__ __launch_bounds__(kThreads) void k_quant_nf4(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Dequantize to bf16: one lane per chunk of 8 codes, one 16-byte store.
+// Dequantize to bf16: a lane handles chunks of 8 codes (one packed load, one
+// 16-byte store), four chunks a grid stride apart per iteration so that four
+// loads are in flight; every load and store instruction of a wave covers a
+// contiguous run of memory.
 // ---------------------------------------------------------------------------
+template <int KIND>
+__device__ __forceinline__ u32x4_t dequant8(const WView& w, int64_t c, const float* cb) {
+  using T = WKindTraits<KIND>;
+  uint32_t word;
+  if constexpr (T::bits == 4) {
+    word = reinterpret_cast<const uint32_t*>(w.packed)[c];
+  } else {
+    word = reinterpret_cast<const uint16_t*>(w.packed)[c];
+  }
+  float v[8];
+  if constexpr (T::fmt == FMT_MINMAX) {
+    const int64_t g = c / (T::group / 8);
+    const float s = w.scales[g];
+    const int z = w.zeros[g];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)(code_of<T::bits>(word, i) - z) * s;
+  } else {
+    const float a = nf4_block_scale<T::dq>(w, c >> 3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = cb[code_of<4>(word, i)] * a;
+  }
+  return u32x4_t{cvt_pk_bf16(v[0], v[1]), cvt_pk_bf16(v[2], v[3]), cvt_pk_bf16(v[4], v[5]),
+                 cvt_pk_bf16(v[6], v[7])};
+}
+
 template <int KIND>
 __global__ __launch_bounds__(kThreads) void k_dequant(WView w, uint16_t* __restrict__ out,
                                                      int64_t nchunks, Nf4Table tab) {
@@ -200,33 +228,17 @@ __global__ __launch_bounds__(kThreads) void k_dequant(WView w, uint16_t* __restr
     if (threadIdx.x < 16) cb[threadIdx.x] = tab.c[threadIdx.x];
     __syncthreads();
   }
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(out);
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < nchunks; c += stride) {
-    uint32_t word;
-    if constexpr (T::bits == 4) {
-      word = reinterpret_cast<const uint32_t*>(w.packed)[c];
-    } else {
-      word = reinterpret_cast<const uint16_t*>(w.packed)[c];
-    }
-    float v[8];
-    if constexpr (T::fmt == FMT_MINMAX) {
-      const int64_t g = c / (T::group / 8);
-      const float s = w.scales[g];
-      const int z = w.zeros[g];
+  int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; c + 3 * stride < nchunks; c += 4 * stride) {
+    u32x4_t o[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = (float)(code_of<T::bits>(word, i) - z) * s;
-    } else {
-      const float a = nf4_block_scale<T::dq>(w, c >> 3);
+    for (int p = 0; p < 4; ++p) o[p] = dequant8<KIND>(w, c + p * stride, cb);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = cb[code_of<4>(word, i)] * a;
-    }
-    uint4 o;
-    o.x = pack_bf16x2(v[0], v[1]);
-    o.y = pack_bf16x2(v[2], v[3]);
-    o.z = pack_bf16x2(v[4], v[5]);
-    o.w = pack_bf16x2(v[6], v[7]);
-    reinterpret_cast<uint4*>(out)[c] = o;
+    for (int p = 0; p < 4; ++p) __builtin_nontemporal_store(o[p], dst + c + p * stride);
   }
+  for (; c < nchunks; c += stride) dst[c] = dequant8<KIND>(w, c, cb);
 }
 
 int grid_for(int64_t nchunks) {
@@ -240,7 +252,7 @@ template <int KIND>
 struct DequantLauncher {
   static hipError_t run(const WView& w, uint16_t* out, const Nf4Table& tab, hipStream_t s) {
     const int64_t nchunks = w.n * w.k / 8;
-    hipLaunchKernelGGL((k_dequant<KIND>), dim3(grid_for(nchunks)), dim3(kThreads), 0, s, w, out,
+    hipLaunchKernelGGL((k_dequant<KIND>), dim3(grid_for((nchunks + 3) / 4)), dim3(kThreads), 0, s, w, out,
                        nchunks, tab);
     return hipGetLastError();
   }

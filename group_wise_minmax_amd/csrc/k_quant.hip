@@ -23,11 +23,13 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// 8 consecutive fp32 weights, read once: non-temporal loads (they stream past
+// the caches, as the packed output does on the way out).
 __device__ __forceinline__ void load8(const float* __restrict__ p, float w[8]) {
-  const float4 a = reinterpret_cast<const float4*>(p)[0];
-  const float4 b = reinterpret_cast<const float4*>(p)[1];
-  w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-  w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  const f32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  const f32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p) + 1);
+  w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
+  w[4] = b[0]; w[5] = b[1]; w[6] = b[2]; w[7] = b[3];
 }
 
 // ---------------------------------------------------------------------------
@@ -85,9 +87,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_minmax(const float* __restri
     }
     if (valid) {
       if constexpr (BITS == 4) {
-        reinterpret_cast<uint32_t*>(packed)[c] = word;
+        __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(packed) + c);
       } else {
-        reinterpret_cast<uint16_t*>(packed)[c] = (uint16_t)word;
+        __builtin_nontemporal_store((uint16_t)word, reinterpret_cast<uint16_t*>(packed) + c);
       }
       if ((c % LPG) == 0) {
         scales[c / LPG] = s;
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_nf4(const float* __restrict_
       word |= (uint32_t)code << (8 * (i >> 1) + ((i & 1) ? 0 : 4));
     }
     if (valid) {
-      reinterpret_cast<uint32_t*>(packed)[c] = word;
+      __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(packed) + c);
       if ((t & 7) == 0) {
         if constexpr (DQ) {
           am[lb] = a;

@@ -12,11 +12,12 @@
 //    of a layer, gate and up, or the INT4 and INT2 row sets of a mixed-precision
 //    layer in separate launches per kind): the waves are dealt out per weight,
 //    so a wave works on one weight for its whole life.
-//  * x either comes from global memory with each step (the 8-16 KiB vector
-//    stays in L1/L2 and no barrier delays the first weight loads), or, for long
-//    rows, is staged in LDS once per workgroup.  Either way it is arranged the
-//    way the dot products consume it (see below), with the sum of x over every
-//    16-byte weight chunk (MinMax).  NF4 builds a 256-entry byte -> pair of
+//  * x either comes from global memory with each step (4-bit MinMax: the
+//    vector stays in L1/L2 and no barrier delays the first weight loads), or
+//    is staged in LDS once per workgroup (2-bit MinMax, whose 16-byte chunk
+//    needs 128 bytes of x, and NF4), unless the staged copy would not fit.
+//    Either way it is arranged the way the dot products consume it (see
+//    below), with the sum of x over every 16-byte weight chunk (MinMax).  NF4 builds a 256-entry byte -> pair of
 //    bf16 levels table in LDS, 32 copies so each lane of a 32-lane half reads
 //    its own bank.
 //  * Work: a wave owns a run of groups of R consecutive rows; each step loads
@@ -441,25 +442,28 @@ struct Gemv1Launcher {
                         const uint16_t* X, const LoraEpi& lora, const Nf4Table& tab, hipStream_t s) {
     using T = WKindTraits<KIND>;
     const int64_t k = ws[0].k;
-    // Measured on the LLaMA-3-8B shapes.  4-bit MinMax with rows up to 8192
-    // reads x from global memory: under 2048 rows in all, one row per wave
-    // with 2 steps in flight (more waves); otherwise 2 rows with one step in
-    // flight.  Longer rows stage x in LDS and keep 4 steps of 2 rows in
-    // flight.  NF4 (2 chunks per step) stages x with 2 steps in flight, about
-    // 4 per wave.  Rows whose staged x would not fit 64 KiB read x from
-    // global memory.
+    // Measured on the LLaMA-3-8B and 70B-shaped layers (all weights of one
+    // launch together).  4-bit MinMax reads x from global memory and takes 2
+    // chunks (32 B) of each row per step: 1 row per wave with 2 steps in
+    // flight under 2048 rows in all (more waves), 2 rows with 2 steps up to
+    // 8192 rows of length <= 8192, else 2 rows with 1 step.  2-bit MinMax
+    // (128 B of x per chunk) and NF4 stage x in LDS: 2 chunks per step with 2
+    // steps in flight, or, for 2-bit rows longer than 8192, 1 chunk with 4.
+    // Rows whose staged x would not fit 64 KiB read x from global memory.
     const bool fits = lds_bytes<KIND>(k, false) <= 65536;
     int64_t rows = 0;
     for (int i = 0; i < count; ++i) rows += ws[i].n;
-    if constexpr (T::fmt == FMT_NF4) {
+    if constexpr (T::fmt == FMT_MINMAX && T::bits == 4) {
+      if (rows < 2048) return launch_set<KIND, 1, 2, 2, true>(ws, ys, orows, count, X, lora, tab, s, 1);
+      if (rows <= 8192 && k <= 8192) return launch_set<KIND, 2, 2, 2, true>(ws, ys, orows, count, X, lora, tab, s, 1);
+      return launch_set<KIND, 2, 2, 1, true>(ws, ys, orows, count, X, lora, tab, s, 1);
+    } else if constexpr (T::fmt == FMT_MINMAX) {
+      if (!fits) return launch_set<KIND, 2, 1, 1, true>(ws, ys, orows, count, X, lora, tab, s, 2);
+      if (k <= 8192) return launch_set<KIND, 2, 2, 2, false>(ws, ys, orows, count, X, lora, tab, s, 1);
+      return launch_set<KIND, 2, 1, 4, false>(ws, ys, orows, count, X, lora, tab, s, 2);
+    } else {
       if (fits) return launch_set<KIND, 2, 2, 2, false>(ws, ys, orows, count, X, lora, tab, s, 4);
       return launch_set<KIND, 2, 2, 1, true>(ws, ys, orows, count, X, lora, tab, s, 4);
-    } else {
-      if ((T::bits == 4 && k <= 8192) || !fits) {
-        if (rows < 2048) return launch_set<KIND, 1, 1, 2, true>(ws, ys, orows, count, X, lora, tab, s, 2);
-        return launch_set<KIND, 2, 1, 1, true>(ws, ys, orows, count, X, lora, tab, s, 2);
-      }
-      return launch_set<KIND, 2, 1, 4, false>(ws, ys, orows, count, X, lora, tab, s, 2);
     }
   }
 };

@@ -2,17 +2,21 @@
 """Benchmark of the lbq hot path on one MI355X.
 
 One step is one pass of the whole hot path over a LLaMA-3-8B decoder layer
-(q, k, v, o, gate, up, down) plus the 70B-shaped mixed-precision dispatch:
+(q, k, v, o, gate, up, down) plus the 70B-shaped mixed-precision dispatch, in
+this order:
 
-  quant_int4   quantize + pack the 7 fp32 weights, MinMax INT4 g128
-  quant_nf4dq  quantize + pack the 7 weights, NF4 block 64 + double quant
-  dequant      dequantize the 7 NF4-DQ weights to bf16
   gemv_m1      Y = X W^T at m = 1, INT4 g128, over R distinct weight copies
                (R * 118 MB > 2 x 256 MB Infinity Cache, so weights stream from HBM);
                q/k/v and gate/up share X and run as one launch each
                (lbq_linear_fwd_grouped), o and down alone: 4 launches per layer
   gemv_m1_per_linear  the same with one launch per linear (7 per layer)
   gemv_m16     m = 16, one launch per linear
+  chmix_70b_m1     70B-shaped layer, per-channel 25% INT4 g128 / 75% INT2 g64
+                   (each format's rows scatter into Y), m = 1: the linears that
+                   share X in one call, one launch per format (8 per layer)
+  quant_int4   quantize + pack the 7 fp32 weights, MinMax INT4 g128
+  quant_nf4dq  quantize + pack the 7 weights, NF4 block 64 + double quant
+  dequant      dequantize the 7 NF4-DQ weights to bf16
   gemm_m2048   INT4 g128 forward at m = 2048
   fwd_m4096    NF4-DQ forward at m = 4096 (2 x 2048 tokens)       <- headline;
                q/k/v and gate/up share X and run as one GEMM launch each
@@ -22,10 +26,7 @@ One step is one pass of the whole hot path over a LLaMA-3-8B decoder layer
   bwd_m4096    NF4-DQ input gradient dX = dY deq(W) at m = 4096
   lora_bwd_m4096  NF4-DQ LoRA backward (dX with the adapter term, dA, dB),
                rank 16 on q and v, at m = 4096
-  chmix_70b_m1     70B-shaped layer, per-channel 25% INT4 g128 / 75% INT2 g64
-                   (each format's rows scatter into Y), m = 1: the linears that
-                   share X in one call, one launch per format (8 per layer)
-  chmix_70b_m1024  the same at m = 1024
+  chmix_70b_m1024  the 70B-shaped channel-mix layer at m = 1024
   copy_1g      (only with --phases) a plain 1 GiB device-to-device copy, the
                reference kernel for scaling hardware byte counters
 
@@ -294,12 +295,13 @@ def build_workload(L, SI, torch, dev, R, want):
         len(copies) * sum(2 * K_of[g[0]] for g in GROUPS)
     quant_bytes = lambda qs: sum(4 * N_of[nm] * K_of[nm] + qs[nm].nbytes() for nm in names)
     phases = [
-        ("quant_int4", p_quant_int4, lambda: {"bound": "hbm", "bytes": quant_bytes(q4), "launches": 7}),
-        ("quant_nf4dq", p_quant_nf4dq, lambda: {"bound": "hbm", "bytes": quant_bytes(qn), "launches": 7}),
-        ("dequant", p_dequant, lambda: {"bound": "hbm", "bytes": sum(qn[nm].nbytes() + 2 * N_of[nm] * K_of[nm] for nm in names), "launches": 7}),
         ("gemv_m1", p_gemv_grouped(X1, Y1), lambda: {"bound": "hbm", "bytes": gemv_bytes_grouped(), "launches": len(GROUPS) * R}),
         ("gemv_m1_per_linear", p_gemv(X1, Y1), lambda: {"bound": "hbm", "bytes": gemv_bytes(1), "launches": 7 * R}),
         ("gemv_m16", p_gemv(X16, Y16), lambda: {"bound": "hbm", "bytes": gemv_bytes(16), "launches": 7 * R}),
+        ("chmix_70b_m1", p_chmix_m1, lambda: {"bound": "hbm", "bytes": sum(a.nbytes() + b.nbytes() + 2 * (a.n + b.n) for _, a, b, *_ in cm) + sum(2 * next(a.k for nm, a, *_ in cm if nm == g[0]) for g in GROUPS), "launches": 2 * len(GROUPS)}),
+        ("quant_int4", p_quant_int4, lambda: {"bound": "hbm", "bytes": quant_bytes(q4), "launches": 7}),
+        ("quant_nf4dq", p_quant_nf4dq, lambda: {"bound": "hbm", "bytes": quant_bytes(qn), "launches": 7}),
+        ("dequant", p_dequant, lambda: {"bound": "hbm", "bytes": sum(qn[nm].nbytes() + 2 * N_of[nm] * K_of[nm] for nm in names), "launches": 7}),
         ("gemm_m2048", p_gemm(q4, X2k, Y2k), lambda: {"bound": "mfma", "flop": flop(2048), "launches": 7}),
         ("fwd_m4096", None, lambda: {"bound": "mfma", "flop": flop(4096), "launches": len(GROUPS),
                                      "units": gemm_group_units(qn, X4k, Y4k),
@@ -311,10 +313,13 @@ def build_workload(L, SI, torch, dev, R, want):
         ("bwd_m4096", p_bwd, lambda: {"bound": "mfma", "flop": flop(4096), "launches": 7}),
         # dX = dY W + G A, G = dY B, T = X A^T, dA = G^T X, dB = (T^T dY)^T
         ("lora_bwd_m4096", p_lora_bwd, lambda: {"bound": "mfma", "flop": sum(2 * 4096 * N_of[nm] * K_of[nm] + 2 * 4096 * 16 * (2 * N_of[nm] + 3 * K_of[nm]) for nm in lora_bwd), "launches": 14}),
-        ("chmix_70b_m1", p_chmix_m1, lambda: {"bound": "hbm", "bytes": sum(a.nbytes() + b.nbytes() + 2 * (a.n + b.n) for _, a, b, *_ in cm) + sum(2 * next(a.k for nm, a, *_ in cm if nm == g[0]) for g in GROUPS), "launches": 2 * len(GROUPS)}),
         ("chmix_70b_m1024", p_chmix_m1024, lambda: {"bound": "mfma", "flop": sum(2 * 1024 * (a.n + b.n) * a.k for _, a, b, *_ in cm), "launches": 14}),
         ("copy_1g", p_copy, lambda: {"bound": "hbm", "bytes": 2 << 30, "launches": 1}),
     ]
+    # Decode phases (HBM-bound reads) run first in each step, after the
+    # compute-bound GEMMs of the previous step, so that they do not inherit the
+    # write-back of the hundreds of MB the quantize/dequant phases leave dirty
+    # in the caches.
     return [(nm, fn, info()) for nm, fn, info in phases if nm in want]
 
 

@@ -135,6 +135,31 @@ class QuantizedWeight:
                    (self.packed, self.scales, self.zeros, self.absmax, self.absmax_q,
                     self.absmax_scale) if t is not None)
 
+    def to_bytes(self) -> bytes:
+        """The weight and its quantization state as one blob (see
+        ``lbq_serialize`` in lbq.h); ``out_rows`` is not part of it."""
+        nbytes = lib.lbq_serialized_bytes(ctypes.byref(self.desc))
+        buf = ctypes.create_string_buffer(nbytes)
+        q = self.qtensor()
+        check(lib.lbq_serialize(ctypes.byref(self.desc), ctypes.byref(q), buf, nbytes, _stream(self.device)),
+              "lbq_serialize")
+        return buf.raw
+
+    @staticmethod
+    def from_bytes(blob: bytes, device) -> "QuantizedWeight":
+        """Rebuild a weight from ``to_bytes`` output into new device buffers."""
+        desc = Desc()
+        check(lib.lbq_blob_desc(blob, len(blob), ctypes.byref(desc)), "lbq_blob_desc")
+        qw = QuantizedWeight.empty(desc, device)
+        q = qw.qtensor()
+        check(lib.lbq_deserialize(blob, len(blob), ctypes.byref(q), _stream(qw.device)), "lbq_deserialize")
+        return qw
+
+    def storage_view(self, dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+        """The packed bytes reinterpreted as ``dtype`` (same bits, no copy):
+        the float storage a sharding framework can hold them in."""
+        return self.packed.view(dtype)
+
     @staticmethod
     def empty(desc: Desc, device) -> "QuantizedWeight":
         sz = lbq_layout(desc)

@@ -26,6 +26,7 @@ EXPORTED = (
     "lbq_linear_fwd", "lbq_linear_fwd_grouped_workspace_bytes", "lbq_linear_fwd_grouped",
     "lbq_linear_bwd_dx", "lbq_lora_workspace_bytes", "lbq_lora_fwd",
     "lbq_lora_bwd_workspace_bytes", "lbq_lora_bwd",
+    "lbq_serialized_bytes", "lbq_serialize", "lbq_blob_desc", "lbq_deserialize",
     "lbq_nf4_codebook", "lbq_strerror", "lbq_last_error_detail", "lbq_version",
 )
 
@@ -76,6 +77,10 @@ def _load() -> ctypes.CDLL:
         "lbq_lora_fwd": (I32, [DP, QP, P, I64, P, P, I32, ctypes.c_float, P, I64, P, SZ, P]),
         "lbq_lora_bwd_workspace_bytes": (SZ, [DP, I64, I32]),
         "lbq_lora_bwd": (I32, [DP, QP, P, P, I64, P, P, I32, ctypes.c_float, P, P, P, P, SZ, P]),
+        "lbq_serialized_bytes": (SZ, [DP]),
+        "lbq_serialize": (I32, [DP, QP, P, SZ, P]),
+        "lbq_blob_desc": (I32, [P, SZ, DP]),
+        "lbq_deserialize": (I32, [P, SZ, QP, P]),
         "lbq_nf4_codebook": (None, [ctypes.POINTER(ctypes.c_float)]),
         "lbq_strerror": (ctypes.c_char_p, [I32]),
         "lbq_last_error_detail": (ctypes.c_char_p, []),

@@ -111,6 +111,13 @@ lbq::WKind kind_of(const lbq_desc* d) {
   return d->group == 64 ? lbq::WK_I2G64 : lbq::WK_I2G128;
 }
 
+// Serialized blob: "LBQ1", uint32 version, the descriptor, six uint64 byte
+// counts, then the buffers at 16-byte boundaries.
+constexpr char kBlobMagic[4] = {'L', 'B', 'Q', '1'};
+constexpr uint32_t kBlobVersion = 1;
+constexpr size_t kBlobHeader = 96;
+static_assert(sizeof(lbq_desc) == 40, "blob layout assumes a 40-byte descriptor");
+
 void sizes_of(const lbq_desc* d, lbq_sizes* s) {
   std::memset(s, 0, sizeof *s);
   s->packed = (size_t)(d->n * d->k * d->bits / 8);
@@ -460,6 +467,95 @@ lbq_status lbq_lora_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16
   const lbq::LoraEpi lora{T, B, r, rp};
   const lbq::WView w = view_of(desc, q);
   return hip_status(dispatch_fwd(desc, w, X, m, Y, ldy, q->out_rows, lora, part, s), "lbq_lora_fwd");
+}
+
+// ---- serialization --------------------------------------------------------
+
+size_t lbq_serialized_bytes(const lbq_desc* desc) {
+  if (check_desc(desc) != LBQ_OK) return 0;
+  lbq_sizes z;
+  sizes_of(desc, &z);
+  return kBlobHeader + align16(z.packed) + align16(z.scales) + align16(z.zeros) + align16(z.absmax) +
+         align16(z.absmax_q) + align16(z.absmax_scale);
+}
+
+lbq_status lbq_serialize(const lbq_desc* desc, const lbq_qtensor* q, void* blob, size_t blob_bytes,
+                         void* stream) {
+  lbq_status st = check_desc(desc);
+  if (st != LBQ_OK) return st;
+  if ((st = check_qtensor(desc, q)) != LBQ_OK) return st;
+  if (blob == nullptr) return fail(LBQ_E_NULL, "blob is NULL");
+  const size_t need = lbq_serialized_bytes(desc);
+  if (blob_bytes < need) return fail(LBQ_E_SHAPE, "blob needs %zu bytes (got %zu)", need, blob_bytes);
+  lbq_sizes z;
+  sizes_of(desc, &z);
+  uint8_t* b = static_cast<uint8_t*>(blob);
+  std::memset(b, 0, need);
+  std::memcpy(b, kBlobMagic, 4);
+  const uint32_t version = kBlobVersion;
+  std::memcpy(b + 4, &version, 4);
+  std::memcpy(b + 8, desc, sizeof(lbq_desc));
+  const uint64_t counts[6] = {z.packed, z.scales, z.zeros, z.absmax, z.absmax_q, z.absmax_scale};
+  std::memcpy(b + 48, counts, sizeof(counts));
+  const void* src[6] = {q->packed, q->scales, q->zeros, q->absmax, q->absmax_q, q->absmax_scale};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  size_t off = kBlobHeader;
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < 6 && e == hipSuccess; ++i) {
+    if (counts[i] > 0) e = hipMemcpyAsync(b + off, src[i], counts[i], hipMemcpyDeviceToHost, s);
+    off += align16(counts[i]);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return hip_status(e, "lbq_serialize");
+}
+
+lbq_status lbq_blob_desc(const void* blob, size_t blob_bytes, lbq_desc* desc) {
+  if (blob == nullptr || desc == nullptr) return fail(LBQ_E_NULL, "blob and desc must be non-NULL");
+  if (blob_bytes < kBlobHeader) return fail(LBQ_E_SHAPE, "blob shorter than its %zu-byte header", kBlobHeader);
+  const uint8_t* b = static_cast<const uint8_t*>(blob);
+  if (std::memcmp(b, kBlobMagic, 4) != 0) return fail(LBQ_E_FORMAT, "not an lbq blob (magic)");
+  uint32_t version;
+  std::memcpy(&version, b + 4, 4);
+  if (version != kBlobVersion) return fail(LBQ_E_FORMAT, "blob version %u (this library reads %u)", version, kBlobVersion);
+  lbq_desc d;
+  std::memcpy(&d, b + 8, sizeof(lbq_desc));
+  if (check_desc(&d) != LBQ_OK) {
+    const std::string why = g_detail;
+    return fail(LBQ_E_FORMAT, "blob descriptor invalid: %s", why.c_str());
+  }
+  lbq_sizes z;
+  sizes_of(&d, &z);
+  uint64_t counts[6];
+  std::memcpy(counts, b + 48, sizeof(counts));
+  const uint64_t want[6] = {z.packed, z.scales, z.zeros, z.absmax, z.absmax_q, z.absmax_scale};
+  for (int i = 0; i < 6; ++i)
+    if (counts[i] != want[i]) return fail(LBQ_E_FORMAT, "blob byte count %d is %llu, the descriptor needs %llu", i,
+                                          (unsigned long long)counts[i], (unsigned long long)want[i]);
+  const size_t need = lbq_serialized_bytes(&d);
+  if (blob_bytes < need) return fail(LBQ_E_SHAPE, "blob holds %zu of its %zu bytes", blob_bytes, need);
+  *desc = d;
+  return ok();
+}
+
+lbq_status lbq_deserialize(const void* blob, size_t blob_bytes, const lbq_qtensor* q, void* stream) {
+  lbq_desc d;
+  lbq_status st = lbq_blob_desc(blob, blob_bytes, &d);
+  if (st != LBQ_OK) return st;
+  if ((st = check_qtensor(&d, q)) != LBQ_OK) return st;
+  lbq_sizes z;
+  sizes_of(&d, &z);
+  const uint64_t counts[6] = {z.packed, z.scales, z.zeros, z.absmax, z.absmax_q, z.absmax_scale};
+  void* dst[6] = {q->packed, q->scales, q->zeros, q->absmax, q->absmax_q, q->absmax_scale};
+  const uint8_t* b = static_cast<const uint8_t*>(blob);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  size_t off = kBlobHeader;
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < 6 && e == hipSuccess; ++i) {
+    if (counts[i] > 0) e = hipMemcpyAsync(dst[i], b + off, counts[i], hipMemcpyHostToDevice, s);
+    off += align16(counts[i]);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return hip_status(e, "lbq_deserialize");
 }
 
 void lbq_nf4_codebook(float out[16]) {

@@ -235,6 +235,43 @@ lbq_status lbq_lora_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16
                         float sigma, uint16_t* Y, int64_t ldy, void* workspace,
                         size_t ws_bytes, void* stream);
 
+/* ---- Serialization ([BNB] 源码纵深: the state dict saves the 4-bit weight
+ * together with its quantization-state fields so that the layer can be rebuilt
+ * exactly; section 量化数据的存储: the packed bytes are plain bytes, whatever
+ * dtype holds them).  A blob is little-endian host memory:
+ *   bytes  0..3   the characters "LBQ1"
+ *          4..7   uint32 version, 1
+ *          8..47  the lbq_desc (reserved = 0)
+ *         48..95  six uint64 byte counts, as lbq_layout reports them, of
+ *                 packed, scales, zeros, absmax, absmax_q, absmax_scale
+ *         96..    those six buffers in that order, each starting at a
+ *                 multiple of 16 bytes (zero padding in between)
+ * out_rows belongs to a use of the weight, not to the weight, and is not
+ * stored. */
+
+/* Host only.  Bytes of the blob for `desc` (0 if `desc` is invalid). */
+size_t lbq_serialized_bytes(const lbq_desc* desc);
+
+/* Copies the weight's buffers (device) into `blob` (host, at least
+ * lbq_serialized_bytes(desc) bytes) on `stream` and waits for the copies:
+ * unlike the other device calls it returns only when `blob` is complete.
+ * Errors: those of lbq_layout, LBQ_E_NULL, LBQ_E_SHAPE (blob too small),
+ * LBQ_E_HIP. */
+lbq_status lbq_serialize(const lbq_desc* desc, const lbq_qtensor* q, void* blob, size_t blob_bytes,
+                         void* stream);
+
+/* Host only.  Validates a blob's header and byte counts and writes its
+ * descriptor to *desc, so that the caller can size the device buffers with
+ * lbq_layout.  LBQ_E_FORMAT for a wrong magic, version, descriptor or byte
+ * count, LBQ_E_SHAPE for a blob shorter than its contents. */
+lbq_status lbq_blob_desc(const void* blob, size_t blob_bytes, lbq_desc* desc);
+
+/* Copies a blob into the device buffers `q` (sized by lbq_layout of the
+ * blob's descriptor) on `stream` and waits for the copies.  The restored
+ * weight dequantizes and multiplies bit for bit like the serialized one.
+ * Errors: those of lbq_blob_desc, LBQ_E_NULL, LBQ_E_ALIGN, LBQ_E_HIP. */
+lbq_status lbq_deserialize(const void* blob, size_t blob_bytes, const lbq_qtensor* q, void* stream);
+
 /* Host only.  The library's NF4 codebook (16 fp32 levels, ascending, with
  * c[0] = -1, c[7] = 0, c[15] = 1), computed by the library from normal
  * quantiles at evenly spaced probabilities [QL]. */

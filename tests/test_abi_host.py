@@ -288,6 +288,42 @@ def test_lora_bwd_error_paths(L):
                                        FAKE, FAKE, FAKE, FAKE, need, None)) == "LBQ_E_UNSUPPORTED"
 
 
+def test_blob_header_and_error_paths(L):
+    """The blob layout as lbq.h documents it, built by hand here (no device
+    access: every path below fails or finishes before any copy)."""
+    import struct
+    lib = L.lib
+    B = ctypes.byref
+    for args in (("minmax", 3, 384, 4, 128), ("minmax", 5, 256, 2, 64), ("nf4", 7, 512)):
+        d = L.make_desc(*args) if args[0] == "minmax" else L.make_desc(*args, double_quant=True)
+        sz = L.lbq_layout(d)
+        keys = ("packed", "scales", "zeros", "absmax", "absmax_q", "absmax_scale")
+        total = 96 + sum((sz[k] + 15) // 16 * 16 for k in keys)
+        assert lib.lbq_serialized_bytes(B(d)) == total
+        hdr = b"LBQ1" + struct.pack("<I", 1) + bytes(d) + struct.pack("<6Q", *[sz[k] for k in keys])
+        assert len(hdr) == 96
+        blob = hdr + bytes(total - 96)
+        out = L.Desc()
+        assert _status(L, lib.lbq_blob_desc(blob, len(blob), B(out))) == "LBQ_OK"
+        assert bytes(out) == bytes(d)
+        assert _status(L, lib.lbq_blob_desc(b"LBQ2" + blob[4:], len(blob), B(out))) == "LBQ_E_FORMAT"
+        assert _status(L, lib.lbq_blob_desc(blob[:4] + struct.pack("<I", 2) + blob[8:], len(blob), B(out))) == "LBQ_E_FORMAT"
+        assert _status(L, lib.lbq_blob_desc(blob, len(blob) - 1, B(out))) == "LBQ_E_SHAPE"
+        assert _status(L, lib.lbq_blob_desc(blob, 95, B(out))) == "LBQ_E_SHAPE"
+        wrong = hdr[:48] + struct.pack("<Q", sz["packed"] + 16) + hdr[56:]
+        assert _status(L, lib.lbq_blob_desc(wrong + blob[96:], len(blob), B(out))) == "LBQ_E_FORMAT"
+        bad = L.make_desc("minmax", 3, 384)
+        bad.bits = 3
+        assert _status(L, lib.lbq_blob_desc(hdr[:8] + bytes(bad) + hdr[48:] + blob[96:], len(blob), B(out))) == "LBQ_E_FORMAT"
+        assert _status(L, lib.lbq_blob_desc(None, len(blob), B(out))) == "LBQ_E_NULL"
+        # checks that stop before any copy
+        assert _status(L, lib.lbq_serialize(B(d), B(_q(L)), blob, total - 1, None)) == "LBQ_E_SHAPE"
+        assert _status(L, lib.lbq_serialize(B(d), B(_q(L)), None, total, None)) == "LBQ_E_NULL"
+        assert _status(L, lib.lbq_deserialize(blob, len(blob), B(_q(L, packed=None)), None)) == "LBQ_E_NULL"
+        assert _status(L, lib.lbq_deserialize(b"XBQ1" + blob[4:], len(blob), B(_q(L)), None)) == "LBQ_E_FORMAT"
+    assert lib.lbq_serialized_bytes(B(L.make_desc("minmax", 0, 256))) == 0
+
+
 def test_strerror_covers_every_status(L):
     for code in range(8):
         assert L.lib.lbq_strerror(code).decode() not in ("", "unknown status")

@@ -406,3 +406,47 @@ def test_grouped_fwd_exact_on_grid(L):
     for W, Y in zip(Ws, Ys):
         exact = O.bf16_to_f64(X) @ W.astype(np.float64).T
         assert np.array_equal(bf16_bits_host(Y), O.bf16_bits(exact.astype(np.float32)))
+
+
+# ------------------------------------------------------------------ serialization
+
+
+@pytest.mark.parametrize("fmtspec", FORMATS, ids=FMT_IDS)
+def test_serialize_round_trip(L, fmtspec):
+    """Weight -> blob -> new device buffers: every stored byte, the dequantized
+    weight and a forward are identical, and the blob's sections are the
+    buffers' bytes at the offsets lbq.h documents."""
+    fmt, bits, group, dq = fmtspec
+    W = SI.gaussian_weights(9500, 37, 1280, outlier_seed=9501)
+    qw, ref = _quant_pair(L, W, fmt, bits, group, dq)
+    blob = qw.to_bytes()
+    back = L.QuantizedWeight.from_bytes(blob, DEV)
+    torch.cuda.synchronize()
+    check_quantized_equal(back, ref, fmt, dq)
+    assert bytes(back.desc) == bytes(qw.desc)
+    # section offsets: header 96 bytes, then each buffer on a 16-byte boundary
+    off = 96
+    for t in (qw.packed, qw.scales, qw.zeros, qw.absmax, qw.absmax_q, qw.absmax_scale):
+        if t is None:
+            continue
+        b = host(t).tobytes()
+        assert blob[off:off + len(b)] == b
+        off += (len(b) + 15) // 16 * 16
+    assert off == len(blob)
+    assert torch.equal(L.lbq_dequant(back).view(torch.int16), L.lbq_dequant(qw).view(torch.int16))
+    X = to_dev_bf16(SI.bf16_normal(9502, (3, 1280)))
+    assert torch.equal(L.lbq_linear_fwd(X, back).view(torch.int16), L.lbq_linear_fwd(X, qw).view(torch.int16))
+
+
+@pytest.mark.parametrize("fmtspec", [FORMATS[0], FORMATS[1], FORMATS[5]], ids=["i4g128", "i2g64", "nf4dq"])
+def test_packed_bytes_survive_a_bf16_storage(L, fmtspec):
+    """The packed bytes held as bf16 (the float storage a sharding framework
+    needs) and viewed back as bytes dequantize identically."""
+    fmt, bits, group, dq = fmtspec
+    W = SI.gaussian_weights(9510, 64, 1024)
+    qw, _ = _quant_pair(L, W, fmt, bits, group, dq)
+    as_bf16 = qw.storage_view(torch.bfloat16).clone()   # a separate float tensor
+    assert as_bf16.dtype == torch.bfloat16 and as_bf16.numel() * 2 == qw.packed.numel()
+    moved = L.QuantizedWeight(qw.desc, as_bf16.view(torch.uint8), qw.scales, qw.zeros, qw.absmax, qw.absmax_q,
+                              qw.absmax_scale)
+    assert torch.equal(L.lbq_dequant(moved).view(torch.int16), L.lbq_dequant(qw).view(torch.int16))

@@ -363,3 +363,51 @@ def lbq_lora_bwd(X: torch.Tensor, dY: torch.Tensor, qw: QuantizedWeight, A: torc
                            dB.data_ptr(), _ptr(workspace), 0 if workspace is None else workspace.numel(),
                            _stream(dev)), "lbq_lora_bwd")
     return dX, dA, dB
+
+
+class _LoraLinearFn(torch.autograd.Function):
+    """Y = X . deq(W)^T + sigma (X . A^T) . B^T with a frozen quantized W:
+    forward through ``lbq_lora_fwd``, backward through ``lbq_lora_bwd`` (the
+    gradient reaches X and the adapters, never W)."""
+
+    @staticmethod
+    def forward(ctx, X, A, B, qw, sigma):
+        lead = X.shape[:-1]
+        X2 = X.reshape(-1, qw.k).to(torch.bfloat16).contiguous()
+        A16 = A.detach().to(torch.bfloat16).contiguous()
+        B16 = B.detach().to(torch.bfloat16).contiguous()
+        Y = lbq_lora_fwd(X2, qw, A16, B16, sigma)
+        ctx.save_for_backward(X2, A16, B16)
+        ctx.qw, ctx.sigma, ctx.x_shape, ctx.x_dtype = qw, sigma, X.shape, X.dtype
+        ctx.a_dtype, ctx.b_dtype = A.dtype, B.dtype
+        return Y.reshape(*lead, qw.n)
+
+    @staticmethod
+    def backward(ctx, dY):
+        X2, A16, B16 = ctx.saved_tensors
+        dY2 = dY.reshape(-1, ctx.qw.n).to(torch.bfloat16).contiguous()
+        dX, dA, dB = lbq_lora_bwd(X2, dY2, ctx.qw, A16, B16, ctx.sigma)
+        return (dX.reshape(ctx.x_shape).to(ctx.x_dtype), dA.to(ctx.a_dtype), dB.to(ctx.b_dtype), None, None)
+
+
+class LbqLoraLinear(torch.nn.Module):
+    """A frozen low-bit linear layer with trainable LoRA adapters (r <= 64,
+    n % 64 == 0).  A [r, k] and B [n, r] are parameters (fp32 masters by
+    default; the kernels see them rounded to bf16); B starts at zero, so the
+    adapted layer starts equal to the frozen one."""
+
+    def __init__(self, qw: QuantizedWeight, r: int = 16, lora_alpha: float = 16.0,
+                 dtype: torch.dtype = torch.float32, generator: Optional[torch.Generator] = None):
+        super().__init__()
+        if not 1 <= r <= 64 or qw.n % 64 != 0:
+            raise ValueError("LbqLoraLinear needs 1 <= r <= 64 and n % 64 == 0")
+        self.qw = qw
+        self.sigma = lora_alpha / r
+        bound = 1.0 / qw.k ** 0.5
+        a = torch.empty((r, qw.k), dtype=dtype, device=qw.device)
+        a.uniform_(-bound, bound, generator=generator)
+        self.A = torch.nn.Parameter(a)
+        self.B = torch.nn.Parameter(torch.zeros((qw.n, r), dtype=dtype, device=qw.device))
+
+    def forward(self, X: torch.Tensor) -> torch.Tensor:
+        return _LoraLinearFn.apply(X, self.A, self.B, self.qw, self.sigma)

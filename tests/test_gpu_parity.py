@@ -318,6 +318,37 @@ def test_lora_bwd_deterministic(L):
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
 
 
+def test_lora_autograd_layer(L):
+    """LbqLoraLinear through torch.autograd: forward, dX, dA and dB against the
+    oracle (X of shape [2, 3, k]: leading dimensions flatten to m = 6); a
+    fresh layer (B = 0) reproduces the frozen forward."""
+    n, k, r, alpha = 256, 512, 16, 32.0
+    qw, ref = _quant_pair(L, SI.gaussian_weights(9600, n, k), "nf4", 4, 64, True)
+    X = SI.bf16_normal(9601, (2, 3, k))
+    dY = SI.bf16_normal(9602, (2, 3, n))
+    A = SI.bf16_normal(9603, (r, k), std=0.01)
+    B = SI.bf16_normal(9604, (n, r), std=0.01)
+    fresh = L.LbqLoraLinear(qw, r=r, lora_alpha=alpha)
+    Xd = to_dev_bf16(X)
+    assert torch.equal(fresh(Xd).reshape(6, n).view(torch.int16), L.lbq_linear_fwd(Xd.reshape(6, k), qw).view(torch.int16))
+    layer = L.LbqLoraLinear(qw, r=r, lora_alpha=alpha)
+    with torch.no_grad():
+        layer.A.copy_(to_dev_bf16(A).float())
+        layer.B.copy_(to_dev_bf16(B).float())
+    Xg = to_dev_bf16(X).requires_grad_(True)
+    Y = layer(Xg)
+    Y.backward(to_dev_bf16(dY))
+    torch.cuda.synchronize()
+    sigma = alpha / r
+    Xf, dYf = X.reshape(6, k), dY.reshape(6, n)
+    assert_close(bf16_bits_host(Y.detach().reshape(6, n)), O.lora_fwd(Xf, ref["w_exact"], A, B, sigma), what="autograd fwd")
+    rX, rA, rB = O.lora_bwd(Xf, dYf, ref["w_exact"], A, B, sigma)
+    assert Xg.grad.dtype == torch.bfloat16 and layer.A.grad.dtype == torch.float32
+    assert_close(bf16_bits_host(Xg.grad.reshape(6, k)), rX, what="autograd dX")
+    assert_close_f32(layer.A.grad, rA, what="autograd dA")
+    assert_close_f32(layer.B.grad, rB, what="autograd dB")
+
+
 # ------------------------------------------------------------------ mixed precision
 
 

@@ -30,9 +30,9 @@ this order:
   copy_1g      (only with --phases) a plain 1 GiB device-to-device copy, the
                reference kernel for scaling hardware byte counters
 
-Each phase is captured once as a HIP graph (torch.cuda.CUDAGraph) and replayed,
-so the timed region holds device work only; HIP events on the launch stream
-bracket every phase of every step.  The JSON line's ``value`` is the dequant-
+Each phase (or each launch of the headline phases) is captured once as a HIP
+graph (torch.cuda.CUDAGraph) and replayed K times back to back between two HIP
+events on the launch stream, so the timed region holds device work only.  The JSON line's ``value`` is the dequant-
 GEMM TFLOP/s of fwd_m4096 (2*m*n*k summed over the 7 linears / phase time);
 ``gemv_m1_hbm_GBps`` is the other half of the headline metric.  Both count
 the same 7 linears as the per-linear phases; only the launches differ.
@@ -395,7 +395,7 @@ def main():
     print(f"# setup {time.perf_counter() - t_setup:.1f}s; phases: {[p[0] for p in phases]}", file=sys.stderr, flush=True)
 
     # A phase runs as one graph, or (phases with "units", the headline) as one
-    # graph per linear so that each kernel launch is bracketed by its own events.
+    # graph per launch so that each launch is timed on its own.
     def capture(fn):
         fn()  # eager warm call (first-launch costs stay out of the graph)
         torch.cuda.synchronize()
@@ -418,18 +418,22 @@ def main():
                 run()
     torch.cuda.synchronize()
 
+    # The K steps run unit by unit: each unit's graph is replayed K times back
+    # to back between two events, so a unit's time is that of K consecutive
+    # launches (the next replay is queued while one runs) and no unit inherits
+    # another phase's cache write-back.  The work timed is exactly K steps.
     K = args.steps
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    evs = {name: [[ev() for _ in range(len(units) + 1)] for _ in range(K)] for name, units, _ in runners}
+    evs = {name: [(ev(), ev()) for _ in units] for name, units, _ in runners}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(K):
-        for name, units, _ in runners:
-            e = evs[name][s]
-            e[0].record()
-            for j, (_, run) in enumerate(units):
+    for name, units, _ in runners:
+        for j, (_, run) in enumerate(units):
+            a, b = evs[name][j]
+            a.record()
+            for _ in range(K):
                 run()
-                e[j + 1].record()
+            b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / K * 1e3
@@ -437,10 +441,10 @@ def main():
     report = {}
     unit_us = {}
     for name, units, info in runners:
-        ms = sum(e[0].elapsed_time(e[-1]) for e in evs[name]) / K
+        per_unit = [a.elapsed_time(b) / K for a, b in evs[name]]
+        ms = sum(per_unit)
         if len(units) > 1:
-            unit_us[name] = {u: sum(e[j].elapsed_time(e[j + 1]) for e in evs[name]) / K * 1e3
-                             for j, (u, _) in enumerate(units)}
+            unit_us[name] = {u: per_unit[j] * 1e3 for j, (u, _) in enumerate(units)}
         ent = {"ms": round(ms, 4), "launches": info["launches"], "avg_launch_us": round(ms * 1e3 / info["launches"], 3)}
         if info["bound"] == "hbm":
             gbps = info["bytes"] / (ms * 1e-3) / 1e9

@@ -10,6 +10,8 @@ this order:
                q/k/v and gate/up share X and run as one launch each
                (lbq_linear_fwd_grouped), o and down alone: 4 launches per layer
   gemv_m1_per_linear  the same with one launch per linear (7 per layer)
+  gemv_m4      m = 4, launched like gemv_m1 (the rows of X staged together;
+               down, k = 14336, takes the small-batch MFMA kernel)
   gemv_m16     m = 16, one launch per linear
   chmix_70b_m1     70B-shaped layer, per-channel 25% INT4 g128 / 75% INT2 g64
                    (each format's rows scatter into Y), m = 1: the linears that
@@ -80,7 +82,7 @@ def load_traffic(kernel: str, units_per_launch=None):
     return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
-ALL_PHASES = ("quant_int4", "quant_nf4dq", "dequant", "gemv_m1", "gemv_m1_per_linear", "gemv_m16", "gemm_m2048",
+ALL_PHASES = ("quant_int4", "quant_nf4dq", "dequant", "gemv_m1", "gemv_m1_per_linear", "gemv_m4", "gemv_m16", "gemm_m2048",
               "fwd_m4096", "fwd_m4096_per_linear", "lora_m4096", "bwd_m4096", "lora_bwd_m4096", "chmix_70b_m1",
               "chmix_70b_m1024")
 EXTRA_PHASES = ("copy_1g",)  # opt-in: plain 1 GiB device copy (counter calibration)
@@ -161,6 +163,7 @@ def build_workload(L, SI, torch, dev, R, want):
         return {nm: torch.empty((m, dim_of[nm]), dtype=torch.bfloat16, device=dev) for nm in names} if on else {}
 
     X1, Y1 = xs(2, SI.SLOT_X, 0, 1, K_of, need("gemv_m1", "gemv_m1_per_linear")), ys(1, N_of, need("gemv_m1", "gemv_m1_per_linear"))
+    X4, Y4 = xs(2, SI.SLOT_X, 50, 4, K_of, need("gemv_m4")), ys(4, N_of, need("gemv_m4"))
     X16, Y16 = xs(2, SI.SLOT_X, 100, 16, K_of, need("gemv_m16")), ys(16, N_of, need("gemv_m16"))
     X2k, Y2k = xs(2, SI.SLOT_X, 200, 2048, K_of, need("gemm_m2048")), ys(2048, N_of, need("gemm_m2048"))
     X4k = xs(3, SI.SLOT_X, 0, 4096, K_of, need("fwd_m4096", "fwd_m4096_per_linear", "lora_m4096", "lora_bwd_m4096"))
@@ -291,12 +294,13 @@ def build_workload(L, SI, torch, dev, R, want):
     flop = lambda m: sum(2 * m * n * k for n, k in shapes.values())
     gemv_bytes = lambda m: sum(bytes_fwd(c[nm], m, N_of[nm], K_of[nm]) for c in copies for nm in names)
     # grouped: X is read once per launch
-    gemv_bytes_grouped = lambda: sum(c[nm].nbytes() + 2 * N_of[nm] for c in copies for nm in names) + \
-        len(copies) * sum(2 * K_of[g[0]] for g in GROUPS)
+    gemv_bytes_grouped = lambda m: sum(c[nm].nbytes() + 2 * m * N_of[nm] for c in copies for nm in names) + \
+        len(copies) * sum(2 * m * K_of[g[0]] for g in GROUPS)
     quant_bytes = lambda qs: sum(4 * N_of[nm] * K_of[nm] + qs[nm].nbytes() for nm in names)
     phases = [
-        ("gemv_m1", p_gemv_grouped(X1, Y1), lambda: {"bound": "hbm", "bytes": gemv_bytes_grouped(), "launches": len(GROUPS) * R}),
+        ("gemv_m1", p_gemv_grouped(X1, Y1), lambda: {"bound": "hbm", "bytes": gemv_bytes_grouped(1), "launches": len(GROUPS) * R}),
         ("gemv_m1_per_linear", p_gemv(X1, Y1), lambda: {"bound": "hbm", "bytes": gemv_bytes(1), "launches": 7 * R}),
+        ("gemv_m4", p_gemv_grouped(X4, Y4), lambda: {"bound": "hbm", "bytes": gemv_bytes_grouped(4), "launches": len(GROUPS) * R}),
         ("gemv_m16", p_gemv(X16, Y16), lambda: {"bound": "hbm", "bytes": gemv_bytes(16), "launches": 7 * R}),
         ("chmix_70b_m1", p_chmix_m1, lambda: {"bound": "hbm", "bytes": sum(a.nbytes() + b.nbytes() + 2 * (a.n + b.n) for _, a, b, *_ in cm) + sum(2 * next(a.k for nm, a, *_ in cm if nm == g[0]) for g in GROUPS), "launches": 2 * len(GROUPS)}),
         ("quant_int4", p_quant_int4, lambda: {"bound": "hbm", "bytes": quant_bytes(q4), "launches": 7}),

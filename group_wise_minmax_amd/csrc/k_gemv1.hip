@@ -154,6 +154,7 @@ struct Step {
 struct Gemv1Set {
   WView w[kGemvMaxGroup];
   uint16_t* y[kGemvMaxGroup];
+  int64_t ldy[kGemvMaxGroup];  // row stride of y (several x rows only)
   const int32_t* out_rows[kGemvMaxGroup];
   int wave_end[kGemvMaxGroup];
   int ngroups[kGemvMaxGroup];
@@ -385,6 +386,255 @@ __global__ __launch_bounds__(kThreads) void k_gemv1_set(Gemv1Set set, const uint
                                  gw < wlast, X, none, tab);
 }
 
+// ---------------------------------------------------------------------------
+// Several x rows (2 <= m <= MV <= 4): the same streaming of the weight, with
+// the arranged x of every row staged in LDS.  A chunk's codes become bf16
+// pairs once and are dotted with each row's x; per row the sums run in the
+// same order as the one-row kernel's, so each output row is bit for bit what
+// the one-row kernel gives for that row of x.
+// ---------------------------------------------------------------------------
+
+// The pairs of one 16-byte weight chunk, in the order arrange_x lays out x.
+template <int KIND>
+__device__ __forceinline__ void chunk_pairs(const u32x4_t& wq, const uint32_t* lut, int lane32, uint32_t* wv) {
+  using T = WKindTraits<KIND>;
+  if constexpr (T::fmt == FMT_NF4) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wv[4 * d + j] = lut[((wq[d] >> (8 * j)) & 0xFFu) * kLutCopies + lane32];
+  } else if constexpr (T::bits == 4) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t lo = wq[d] & 0x0F0F0F0Fu, hi = (wq[d] >> 4) & 0x0F0F0F0Fu;
+      wv[4 * d + 0] = pair01(lo);
+      wv[4 * d + 1] = pair23(lo);
+      wv[4 * d + 2] = pair01(hi);
+      wv[4 * d + 3] = pair23(hi);
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t c3 = wq[d] & 0x03030303u, c2 = (wq[d] >> 2) & 0x03030303u;
+      const uint32_t c1 = (wq[d] >> 4) & 0x03030303u, c0 = (wq[d] >> 6) & 0x03030303u;
+      wv[8 * d + 0] = pair01(c3);
+      wv[8 * d + 1] = pair23(c3);
+      wv[8 * d + 2] = pair01(c2);
+      wv[8 * d + 3] = pair23(c2);
+      wv[8 * d + 4] = pair01(c1);
+      wv[8 * d + 5] = pair23(c1);
+      wv[8 * d + 6] = pair01(c0);
+      wv[8 * d + 7] = pair23(c0);
+    }
+  }
+}
+
+// Same two alternating chains as chunk_dot.
+template <int XD>
+__device__ __forceinline__ float dot_pairs(const uint32_t* wv, const uint32_t* xa) {
+  float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < XD; ++i) {
+    if (i & 1) p1 = dot2_bf16(wv[i], xa[i], p1);
+    else p0 = dot2_bf16(wv[i], xa[i], p0);
+  }
+  return p0 + p1;
+}
+
+template <int KIND, int R, int CB, int D, int MV>
+__device__ __forceinline__ void gemvm_body(const WView& w, uint16_t* __restrict__ Y, int64_t ldy,
+                                           const int32_t* __restrict__ out_rows, int g0, int g1, bool active,
+                                           const uint16_t* __restrict__ X, int m, const LoraEpi& lora,
+                                           const Nf4Table& tab) {
+  using T = WKindTraits<KIND>;
+  using G = Gemv1Traits<KIND>;
+  constexpr int CPC = G::CPC, XD = G::XD, XQ = G::XQ, GRP = G::GRP;
+  extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int KB = (int)(w.k * T::bits / 8);
+  const int nchunk = KB / 16;
+  const int gpr = (int)(w.k / GRP);
+  uint32_t* lut = smem;
+  uint32_t* xq = smem + (T::fmt == FMT_NF4 ? 256 * kLutCopies : 0);  // [MV][XQ][nchunk] quads
+  float* xsum = reinterpret_cast<float*>(xq + (size_t)MV * XQ * 4 * nchunk);  // [MV][nchunk]
+  const int cpl = (nchunk + 63) / 64;
+  const int nsteps = (cpl + CB - 1) / CB;
+  const int total = (active && g0 < g1) ? (g1 - g0) * nsteps : 0;
+  const int lane32 = lane & 31;
+  const int64_t nmeta = w.n * gpr;
+  const __amdgpu_buffer_rsrc_t r_w = make_rsrc(w.packed, w.n * KB);
+  __amdgpu_buffer_rsrc_t r_s, r_z;
+  if constexpr (T::fmt == FMT_MINMAX) {
+    r_s = make_rsrc(w.scales, nmeta * 4);
+    r_z = make_rsrc(w.zeros, nmeta);
+  } else if constexpr (T::dq) {
+    r_s = make_rsrc(w.absmax_scale, ((nmeta + 255) >> 8) * 4);
+    r_z = make_rsrc(w.absmax_q, nmeta);
+  } else {
+    r_s = make_rsrc(w.absmax, nmeta * 4);
+    r_z = r_s;
+  }
+  auto load = [&](int s, Step<KIND, R, CB>& st) {
+    const int g = g0 + s / nsteps, b = s % nsteps;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c = min((b * CB + cb) * 64 + lane, nchunk - 1);
+      const int gc = (c * CPC) / GRP;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = (int)min((int64_t)g * R + r, w.n - 1);
+        st.wq[cb][r] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_w, (uint32_t)c * 16u, row * KB, 2 /*nt*/));
+        if constexpr (T::fmt == FMT_MINMAX) {
+          st.sc[cb][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)gc * 4u, row * gpr * 4, 0));
+          st.zq[cb][r] = __builtin_amdgcn_raw_buffer_load_b8(r_z, (uint32_t)gc, row * gpr, 0);
+        } else if constexpr (T::dq) {
+          const int q2 = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(r_z, (uint32_t)gc, row * gpr, 0);
+          const float c2 = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)((row * gpr + gc) >> 8) * 4u, 0, 0));
+          st.sc[cb][r] = (float)q2 * c2;
+          st.zq[cb][r] = 0;
+        } else {
+          st.sc[cb][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)gc * 4u, row * gpr * 4, 0));
+          st.zq[cb][r] = 0;
+        }
+      }
+    }
+  };
+  Step<KIND, R, CB> st[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+    if (i < total) load(i, st[i]);
+
+  // prologue: NF4 table; arranged x of every row (zeros past m) in LDS
+  __shared__ float cbs[16];
+  if constexpr (T::fmt == FMT_NF4) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (tid == i) cbs[i] = tab.c[i];
+    lds_barrier();
+    for (int e = tid; e < 256 * kLutCopies; e += kThreads) {
+      const int b = e / kLutCopies;
+      lut[e] = (uint32_t)bf16_rne(cbs[b >> 4]) | ((uint32_t)bf16_rne(cbs[b & 15]) << 16);
+    }
+  }
+  for (int e = tid; e < MV * nchunk; e += kThreads) {
+    const int mv = e / nchunk, c = e % nchunk;
+    u32x4_t xv[XQ];
+    if (mv < m) {
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(X + (int64_t)mv * w.k + (int64_t)c * CPC);
+#pragma unroll
+      for (int q = 0; q < XQ; ++q) xv[q] = src[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < XQ; ++q) xv[q] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    uint32_t xo[XD];
+    const float sx = x_chunk<KIND>(xv, xo);
+    if constexpr (T::fmt == FMT_MINMAX) xsum[mv * nchunk + c] = sx;
+#pragma unroll
+    for (int q = 0; q < XQ; ++q)
+      reinterpret_cast<u32x4_t*>(xq)[((size_t)mv * XQ + q) * nchunk + c] =
+          u32x4_t{xo[4 * q], xo[4 * q + 1], xo[4 * q + 2], xo[4 * q + 3]};
+  }
+  lds_barrier();
+
+  float acc[R][MV];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int v = 0; v < MV; ++v) acc[r][v] = 0.f;
+
+  auto compute = [&](int s, const Step<KIND, R, CB>& st) {
+    const int g = g0 + s / nsteps, b = s % nsteps;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c = (b * CB + cb) * 64 + lane;
+      const bool cok = c < nchunk;
+      const int cc = cok ? c : 0;
+      uint32_t wv[R][XD];
+#pragma unroll
+      for (int r = 0; r < R; ++r) chunk_pairs<KIND>(st.wq[cb][r], lut, lane32, wv[r]);
+#pragma unroll
+      for (int v = 0; v < MV; ++v) {
+        uint32_t xa[XD];
+#pragma unroll
+        for (int q = 0; q < XQ; ++q) {
+          const u32x4_t t = reinterpret_cast<const u32x4_t*>(xq)[((size_t)v * XQ + q) * nchunk + cc];
+          xa[4 * q] = t[0]; xa[4 * q + 1] = t[1]; xa[4 * q + 2] = t[2]; xa[4 * q + 3] = t[3];
+        }
+        const float xs = (T::fmt == FMT_MINMAX) ? xsum[v * nchunk + cc] : 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float p = dot_pairs<XD>(wv[r], xa);
+          const float sr = (cok && (int64_t)g * R + r < w.n) ? st.sc[cb][r] : 0.f;
+          if constexpr (T::fmt == FMT_MINMAX) {
+            acc[r][v] = fmaf(sr, fmaf(-(float)(128 + st.zq[cb][r]), xs, p), acc[r][v]);
+          } else {
+            acc[r][v] = fmaf(sr, p, acc[r][v]);
+          }
+        }
+      }
+    }
+    if (b == nsteps - 1) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int64_t row = (int64_t)g * R + r;
+#pragma unroll
+        for (int v = 0; v < MV; ++v) {
+          if (v >= m) break;
+          if (lora.t != nullptr && lane < lora.r && row < w.n)
+            acc[r][v] = fmaf(bf16_lo(lora.t[(int64_t)v * lora.rp + lane]), bf16_lo(lora.b[row * lora.r + lane]),
+                             acc[r][v]);
+          const float y = wave_sum(acc[r][v]);
+          if (lane == 0 && row < w.n)
+            Y[(int64_t)v * ldy + (out_rows ? (int64_t)out_rows[row] : row)] = (uint16_t)bf16_rne(y);
+        }
+#pragma unroll
+        for (int v = 0; v < MV; ++v) acc[r][v] = 0.f;
+      }
+    }
+  };
+
+  for (int s = 0; s < total; s += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      if (s + i >= total) break;
+      compute(s + i, st[i]);
+      if (s + i + D < total) load(s + i + D, st[i]);
+    }
+  }
+}
+
+template <int KIND, int R, int CB, int D, int MV>
+__global__ __launch_bounds__(kThreads) void k_gemvm(WView w, const uint16_t* __restrict__ X, int m,
+                                                   uint16_t* __restrict__ Y, int64_t ldy,
+                                                   const int32_t* __restrict__ out_rows, LoraEpi lora,
+                                                   Nf4Table tab, int gpw) {
+  const int gw = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ngroups = (int)((w.n + R - 1) / R);
+  const int g0 = gw * gpw;
+  gemvm_body<KIND, R, CB, D, MV>(w, Y, ldy, out_rows, g0, min(g0 + gpw, ngroups), true, X, m, lora, tab);
+}
+
+template <int KIND, int R, int CB, int D, int MV>
+__global__ __launch_bounds__(kThreads) void k_gemvm_set(Gemv1Set set, const uint16_t* __restrict__ X, int m,
+                                                       Nf4Table tab, int gpw) {
+  const int gw = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int pi = 0, wbeg = 0, wlast = set.wave_end[0];
+#pragma unroll
+  for (int i = 1; i < kGemvMaxGroup; ++i)
+    if (i < set.count) {
+      if (gw >= set.wave_end[i - 1]) { pi = i; wbeg = set.wave_end[i - 1]; }
+      wlast = set.wave_end[i];
+    }
+  const int g0 = (gw - wbeg) * gpw;
+  const LoraEpi none{nullptr, nullptr, 0, 0};
+  gemvm_body<KIND, R, CB, D, MV>(set.w[pi], set.y[pi], set.ldy[pi], set.out_rows[pi], g0,
+                                 min(g0 + gpw, set.ngroups[pi]), gw < wlast, X, m, none, tab);
+}
+
 // Dynamic LDS per workgroup: the NF4 table, plus the arranged x and chunk sums
 // when x is staged.
 template <int KIND>
@@ -468,7 +718,85 @@ struct Gemv1Launcher {
   }
 };
 
+template <int KIND, int MV>
+size_t lds_bytes_m(int64_t k) {
+  using T = WKindTraits<KIND>;
+  using G = Gemv1Traits<KIND>;
+  const int64_t nchunk = k * T::bits / 8 / 16;
+  return (T::fmt == FMT_NF4 ? 256 * kLutCopies * 4 : 0) +
+         (size_t)MV * ((size_t)nchunk * G::XD * 4 + (T::fmt == FMT_MINMAX ? (size_t)nchunk * 4 : 0));
+}
+
+template <int KIND, int R, int CB, int D, int MV>
+hipError_t launch_setm(const WView* ws, uint16_t* const* ys, const int64_t* ldys, const int32_t* const* orows,
+                       int count, const uint16_t* X, int64_t m, const LoraEpi& lora, const Nf4Table& tab,
+                       hipStream_t s, int spw, int min_waves = 1024) {
+  using T = WKindTraits<KIND>;
+  const int64_t nchunk = ws[0].k * T::bits / 8 / 16;
+  const int64_t nsteps = ((nchunk + 63) / 64 + CB - 1) / CB;
+  int64_t groups = 0;
+  for (int i = 0; i < count; ++i) groups += (ws[i].n + R - 1) / R;
+  int64_t waves = (groups * nsteps + spw - 1) / spw;
+  waves = waves < min_waves ? min_waves : waves;
+  waves = waves > groups ? groups : waves;
+  const int64_t gpw = (groups + waves - 1) / waves;
+  const size_t lds = lds_bytes_m<KIND, MV>(ws[0].k);
+  if (count == 1) {
+    const int64_t nw = ((ws[0].n + R - 1) / R + gpw - 1) / gpw;
+    hipLaunchKernelGGL((k_gemvm<KIND, R, CB, D, MV>), dim3((unsigned)((nw + 3) / 4)), dim3(kThreads), lds, s, ws[0],
+                       X, (int)m, ys[0], ldys[0], orows[0], lora, tab, (int)gpw);
+    return hipGetLastError();
+  }
+  Gemv1Set set{};
+  set.count = count;
+  int64_t wend = 0;
+  for (int i = 0; i < count; ++i) {
+    const int64_t ng = (ws[i].n + R - 1) / R;
+    wend += (ng + gpw - 1) / gpw;
+    set.w[i] = ws[i];
+    set.y[i] = ys[i];
+    set.ldy[i] = ldys[i];
+    set.out_rows[i] = orows[i];
+    set.wave_end[i] = (int)wend;
+    set.ngroups[i] = (int)ng;
+  }
+  hipLaunchKernelGGL((k_gemvm_set<KIND, R, CB, D, MV>), dim3((unsigned)((wend + 3) / 4)), dim3(kThreads), lds, s, set,
+                     X, (int)m, tab, (int)gpw);
+  return hipGetLastError();
+}
+
+template <int KIND>
+struct GemvmLauncher {
+  static hipError_t run(const WView* ws, uint16_t* const* ys, const int64_t* ldys, const int32_t* const* orows,
+                        int count, const uint16_t* X, int64_t m, const LoraEpi& lora, const Nf4Table& tab,
+                        hipStream_t s) {
+    if (m <= 2) return launch_setm<KIND, 2, 1, 2, 2>(ws, ys, ldys, orows, count, X, m, lora, tab, s, 2);
+    return launch_setm<KIND, 2, 1, 2, 4>(ws, ys, ldys, orows, count, X, m, lora, tab, s, 2);
+  }
+};
+
 }  // namespace
+
+bool gemvm_fits(WKind kind, int64_t k, int64_t m) {
+  if (m < 2 || m > kGemvmMaxM) return false;
+  size_t b = 0;
+  switch (kind) {
+    case WK_I4G128: b = m <= 2 ? lds_bytes_m<WK_I4G128, 2>(k) : lds_bytes_m<WK_I4G128, 4>(k); break;
+    case WK_I4G64: b = m <= 2 ? lds_bytes_m<WK_I4G64, 2>(k) : lds_bytes_m<WK_I4G64, 4>(k); break;
+    case WK_I2G64: b = m <= 2 ? lds_bytes_m<WK_I2G64, 2>(k) : lds_bytes_m<WK_I2G64, 4>(k); break;
+    case WK_I2G128: b = m <= 2 ? lds_bytes_m<WK_I2G128, 2>(k) : lds_bytes_m<WK_I2G128, 4>(k); break;
+    case WK_NF4: b = m <= 2 ? lds_bytes_m<WK_NF4, 2>(k) : lds_bytes_m<WK_NF4, 4>(k); break;
+    case WK_NF4DQ: b = m <= 2 ? lds_bytes_m<WK_NF4DQ, 2>(k) : lds_bytes_m<WK_NF4DQ, 4>(k); break;
+  }
+  return b <= 65536;
+}
+
+hipError_t launch_gemvm(WKind kind, const WView* ws, uint16_t* const* ys, const int64_t* ldys,
+                        const int32_t* const* out_rows, int count, const uint16_t* X, int64_t m,
+                        const LoraEpi& lora, const Nf4Table& tab, hipStream_t s) {
+  if (count < 1 || count > kGemvMaxGroup || !gemvm_fits(kind, ws[0].k, m)) return hipErrorInvalidValue;
+  return dispatch_kind<GemvmLauncher>(kind, ws, ys, ldys, out_rows, count, X, m, lora, tab, s);
+}
 
 hipError_t launch_gemv1(WKind kind, const WView* ws, uint16_t* const* ys, const int32_t* const* out_rows,
                         int count, const uint16_t* X, const LoraEpi& lora, const Nf4Table& tab,

@@ -198,6 +198,7 @@ hipError_t dispatch_fwd(const lbq_desc* desc, const lbq::WView& w, const uint16_
                         const lbq::LoraEpi& lora, void* ws, hipStream_t s) {
   const lbq::WKind kind = kind_of(desc);
   if (m == 1) return lbq::launch_gemv1(kind, &w, &Y, &out_rows, 1, X, lora, nf4_table(), s);
+  if (lbq::gemvm_fits(kind, desc->k, m)) return lbq::launch_gemvm(kind, &w, &Y, &ldy, &out_rows, 1, X, m, lora, nf4_table(), s);
   if (m <= lbq::kSkinnyMaxM)
     return lbq::launch_skinny(kind, w, X, m, Y, ldy, out_rows, static_cast<float*>(ws), lora,
                               nf4_table(), s);
@@ -205,6 +206,7 @@ hipError_t dispatch_fwd(const lbq_desc* desc, const lbq::WView& w, const uint16_
 }
 
 size_t fwd_workspace(const lbq_desc* desc, int64_t m, bool lora) {
+  if (lbq::gemvm_fits(kind_of(desc), desc->k, m)) return 0;
   if (m >= 2 && m <= lbq::kSkinnyMaxM) return lbq::skinny_workspace_bytes(desc->n, desc->k, m, lora);
   return 0;
 }
@@ -322,7 +324,9 @@ lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lb
   const lbq::LoraEpi none{nullptr, nullptr, 0, 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  if (m == 1 || m > lbq::kSkinnyMaxM) {
+  bool streamed = m <= lbq::kGemvmMaxM;  // m == 1, or every weight's staged x rows fit
+  for (int32_t i = 0; i < count && streamed && m > 1; ++i) streamed = lbq::gemvm_fits(kind_of(&descs[i]), descs[i].k, m);
+  if (streamed || m > lbq::kSkinnyMaxM) {
     // One launch per distinct weight kind, in order of first appearance.
     bool done[LBQ_MAX_GROUP] = {};
     for (int32_t i = 0; i < count && e == hipSuccess; ++i) {
@@ -343,6 +347,7 @@ lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lb
         ++c;
       }
       if (m == 1) e = lbq::launch_gemv1(kind, ws, ys, rows, c, X, none, nf4_table(), s);
+      else if (streamed) e = lbq::launch_gemvm(kind, ws, ys, lds, rows, c, X, m, none, nf4_table(), s);
       else e = lbq::launch_gemm_fwd_set(kind, ws, ys, lds, rows, c, X, m, nf4_table(), s);
     }
   } else {

@@ -68,6 +68,14 @@ constexpr int kGemvMaxGroup = 8;
 hipError_t launch_gemv1(WKind kind, const WView* ws, uint16_t* const* ys, const int32_t* const* out_rows,
                         int count, const uint16_t* X, const LoraEpi& lora, const Nf4Table& tab,
                         hipStream_t s);
+// 2 <= m <= kGemvmMaxM: the GEMV streaming of up to kGemvMaxGroup weights of
+// one kind with every row of x staged in LDS (usable when gemvm_fits; the
+// LoRA term only with count 1).
+constexpr int64_t kGemvmMaxM = 4;
+bool gemvm_fits(WKind kind, int64_t k, int64_t m);
+hipError_t launch_gemvm(WKind kind, const WView* ws, uint16_t* const* ys, const int64_t* ldys,
+                        const int32_t* const* out_rows, int count, const uint16_t* X, int64_t m,
+                        const LoraEpi& lora, const Nf4Table& tab, hipStream_t s);
 // 2 <= m <= kSkinnyMaxM: MFMA with the weight streamed once; K split over
 // skinny_splits() workgroups whose fp32 partials (workspace) are summed by a
 // second kernel when more than one range is used or a LoRA term is added.

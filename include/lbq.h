@@ -160,9 +160,13 @@ size_t lbq_linear_workspace_bytes(const lbq_desc* desc, int64_t m);
  * (m + 256) * k * 2 and (n + 256) * k must be below 2^32 (LBQ_E_SHAPE
  * otherwise: the GEMM uses 32-bit byte offsets).  `workspace` must hold
  * lbq_linear_workspace_bytes(desc, m) bytes (may be NULL when that is 0).
- * m == 1 runs a GEMV that streams the packed weight once; 2 <= m <= 64 a
- * bf16-MFMA kernel that streams it once with K split over workgroups; larger
- * m a bf16-MFMA GEMM whose weight tiles are dequantized once into LDS. */
+ * m == 1 runs a GEMV that streams the packed weight once; 2 <= m <= 4 the
+ * same streaming with every row of X staged in LDS (when the rows fit in 64
+ * KiB: k up to 7680 for 4-bit MinMax, 7936 for 2-bit and 4096 for NF4 at
+ * m = 3..4; 15360, 15872 and 8192 at m = 2), each output row bit for bit what
+ * m == 1 gives for that row of X; otherwise, up to m = 64, a bf16-MFMA kernel that streams the weight
+ * once with K split over workgroups; larger m a bf16-MFMA GEMM whose weight
+ * tiles are dequantized once into LDS. */
 lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X,
                           int64_t m, uint16_t* Y, int64_t ldy, void* workspace,
                           size_t ws_bytes, void* stream);
@@ -180,10 +184,11 @@ size_t lbq_linear_fwd_grouped_workspace_bytes(int32_t count, const lbq_desc* des
  * descs, qs, Ys, ldys: host arrays of `count` entries (1 <= count <=
  * LBQ_MAX_GROUP); every weight has the same k.  Several weights may scatter
  * (out_rows) into disjoint columns of one Y.  Every weight is checked as in
- * lbq_linear_fwd before anything is enqueued.  At m == 1 and m > 64 the
- * weights of one kind run in a single launch (one launch per distinct kind:
- * a GEMV streaming all of them, or a GEMM whose column tiles cover all of
- * them); for 2 <= m <= 64 each weight is launched in turn, reusing the
+ * lbq_linear_fwd before anything is enqueued.  Where lbq_linear_fwd would
+ * stream the weight (m == 1; 2 <= m <= 4 with the rows of X in LDS) and for
+ * m > 64, the weights of one kind run in a single launch (one launch per
+ * distinct kind: a GEMV streaming all of them, or a GEMM whose column tiles
+ * cover all of them); otherwise each weight is launched in turn, reusing the
  * workspace (lbq_linear_fwd_grouped_workspace_bytes). */
 lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lbq_qtensor* qs,
                                   const uint16_t* X, int64_t m, uint16_t* const* Ys,

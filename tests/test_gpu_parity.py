@@ -114,6 +114,53 @@ def test_forward_gemv_many_rows(L, fmtspec, m):
     assert_close(bf16_bits_host(Y), O.linear_fwd(X, ref["w_exact"]))
 
 
+@pytest.mark.parametrize("fmtspec", FORMATS, ids=FMT_IDS)
+@pytest.mark.parametrize("m", [2, 3, 4])
+def test_forward_few_rows_match_single_rows(L, fmtspec, m):
+    """2 <= m <= 4 streams the weight once for all rows of X; each output row
+    equals, bit for bit, the m = 1 forward of that row (same per-row sums in
+    the same order), and the oracle within the matmul tolerance.  n = 300
+    leaves a ragged wave."""
+    fmt, bits, group, dq = fmtspec
+    n, k = 300, 2048
+    W = SI.gaussian_weights(9700 + m, n, k, outlier_seed=9701)
+    X = SI.bf16_normal(9702 + m, (m, k))
+    qw, ref = _quant_pair(L, W, fmt, bits, group, dq)
+    Xd = to_dev_bf16(X)
+    Y = L.lbq_linear_fwd(Xd, qw)
+    rows = [L.lbq_linear_fwd(Xd[i:i + 1].contiguous(), qw) for i in range(m)]
+    torch.cuda.synchronize()
+    for i in range(m):
+        assert torch.equal(Y[i:i + 1].view(torch.int16), rows[i].view(torch.int16)), f"row {i}"
+    assert_close(bf16_bits_host(Y), O.linear_fwd(X, ref["w_exact"]))
+
+
+# Largest k whose m rows of x (m = 3..4) fit the multi-row GEMV's 64 KiB of
+# LDS, per format: the next group up takes the small-batch MFMA kernel.
+FEW_ROWS_KMAX = {"i4g128": 7680, "i2g64": 7936, "nf4dq": 4096}
+
+
+@pytest.mark.parametrize("fid", list(FEW_ROWS_KMAX))
+@pytest.mark.parametrize("above", [False, True], ids=["at_limit", "above_limit"])
+def test_forward_few_rows_at_lds_limit(L, fid, above):
+    """m = 4 at the longest rows the multi-row GEMV stages, and one group
+    longer (the other kernel): both within the matmul tolerance of the oracle;
+    at the limit each row also equals the m = 1 forward bit for bit."""
+    fmt, bits, group, dq = FORMATS[FMT_IDS.index(fid)]
+    m, n = 4, 200
+    k = FEW_ROWS_KMAX[fid] + (group if above else 0)
+    W = SI.gaussian_weights(9800 + k, n, k, outlier_seed=9801)
+    X = SI.bf16_normal(9802 + k, (m, k))
+    qw, ref = _quant_pair(L, W, fmt, bits, group, dq)
+    Xd = to_dev_bf16(X)
+    Y = L.lbq_linear_fwd(Xd, qw)
+    rows = [L.lbq_linear_fwd(Xd[i:i + 1].contiguous(), qw) for i in range(m)] if not above else []
+    torch.cuda.synchronize()
+    for i, r in enumerate(rows):
+        assert torch.equal(Y[i:i + 1].view(torch.int16), r.view(torch.int16)), f"row {i}"
+    assert_close(bf16_bits_host(Y), O.linear_fwd(X, ref["w_exact"]), what=f"{fid} k={k}")
+
+
 @pytest.mark.parametrize("bits,group", [(4, 128), (2, 64), (4, 64), (2, 128)])
 @pytest.mark.parametrize("m", [1, 2, 4, 7, 16, 130])
 def test_forward_exact_on_grid_minmax(L, bits, group, m):
@@ -401,13 +448,14 @@ GROUP_SETS = {
 
 @pytest.mark.parametrize("name", list(GROUP_SETS))
 @pytest.mark.parametrize("k", [1280, 12288])
-@pytest.mark.parametrize("m", [1, 16, 130, 300])
+@pytest.mark.parametrize("m", [1, 3, 16, 130, 300])
 def test_grouped_fwd_matches_single(L, name, k, m):
     """Weights sharing X in one call: each output equals the single-weight
     forward bit for bit (same kernels, same per-row order) and the oracle
     within the matmul tolerance.  Ragged n; at m = 1 same-kind weights share
-    one launch and the mixed set needs three; at m > 64 the GEMM lays the
-    weights' column tiles side by side."""
+    one launch and the mixed set needs three, as at m = 3 with rows short
+    enough for the multi-row GEMV; at m > 64 the GEMM lays the weights'
+    column tiles side by side."""
     specs = GROUP_SETS[name]
     ns = [300, 64, 520, 130][:len(specs)]
     X = SI.bf16_normal(9400 + m, (m, k))

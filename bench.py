@@ -12,7 +12,8 @@ this order:
   gemv_m1_per_linear  the same with one launch per linear (7 per layer)
   gemv_m4      m = 4, launched like gemv_m1 (the rows of X staged together;
                down, k = 14336, takes the small-batch MFMA kernel)
-  gemv_m16     m = 16, one launch per linear
+  gemv_m16     m = 16, launched like gemv_m1 (the small-batch MFMA kernel; its
+               split-K partials are summed by a second launch per group)
   chmix_70b_m1     70B-shaped layer, per-channel 25% INT4 g128 / 75% INT2 g64
                    (each format's rows scatter into Y), m = 1: the linears that
                    share X in one call, one launch per format (8 per layer)
@@ -301,7 +302,7 @@ def build_workload(L, SI, torch, dev, R, want):
         ("gemv_m1", p_gemv_grouped(X1, Y1), lambda: {"bound": "hbm", "bytes": gemv_bytes_grouped(1), "launches": len(GROUPS) * R}),
         ("gemv_m1_per_linear", p_gemv(X1, Y1), lambda: {"bound": "hbm", "bytes": gemv_bytes(1), "launches": 7 * R}),
         ("gemv_m4", p_gemv_grouped(X4, Y4), lambda: {"bound": "hbm", "bytes": gemv_bytes_grouped(4), "launches": len(GROUPS) * R}),
-        ("gemv_m16", p_gemv(X16, Y16), lambda: {"bound": "hbm", "bytes": gemv_bytes(16), "launches": 7 * R}),
+        ("gemv_m16", p_gemv_grouped(X16, Y16), lambda: {"bound": "hbm", "bytes": gemv_bytes_grouped(16), "launches": len(GROUPS) * R}),
         ("chmix_70b_m1", p_chmix_m1, lambda: {"bound": "hbm", "bytes": sum(a.nbytes() + b.nbytes() + 2 * (a.n + b.n) for _, a, b, *_ in cm) + sum(2 * next(a.k for nm, a, *_ in cm if nm == g[0]) for g in GROUPS), "launches": 2 * len(GROUPS)}),
         ("quant_int4", p_quant_int4, lambda: {"bound": "hbm", "bytes": quant_bytes(q4), "launches": 7}),
         ("quant_nf4dq", p_quant_nf4dq, lambda: {"bound": "hbm", "bytes": quant_bytes(qn), "launches": 7}),

@@ -95,12 +95,14 @@ __device__ __forceinline__ int x_off(int lg, int t) {
   return 64 * (t >> 1) + 16 * lg + 8 * (t & 1);
 }
 
+// Row tile `tile` (ROWS rows of W) over K range `split` of ks_count; with
+// `part` set, the fp32 sums go to part[split][m][n], else bf16 to Y.
 template <int KIND, int MB>
-__global__ __launch_bounds__(kThreads) void k_skinny(WView w, const uint16_t* __restrict__ X, int m,
-                                                    uint16_t* __restrict__ Y, int64_t ldy,
-                                                    const int32_t* __restrict__ out_rows,
-                                                    float* __restrict__ part, int ks_count,
-                                                    LoraEpi lora, Nf4Table tab) {
+__device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __restrict__ X, int m,
+                                            uint16_t* __restrict__ Y, int64_t ldy,
+                                            const int32_t* __restrict__ out_rows,
+                                            float* __restrict__ part, int ks_count,
+                                            const LoraEpi& lora, const Nf4Table& tab, int tile, int split) {
   using T = WKindTraits<KIND>;
   using S = SkTraits<KIND>;
   constexpr int RB = S::RB, RBP = S::RBP, KSG = S::KSG, GRP = S::GRP;
@@ -118,13 +120,13 @@ __global__ __launch_bounds__(kThreads) void k_skinny(WView w, const uint16_t* __
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * ROWS;
+  const int64_t n0 = (int64_t)tile * ROWS;
   const int64_t K = w.k;
   const int64_t KB = K * T::bits / 8;
   const int64_t gpr = K / GRP;
   const int nchunk = (int)((K + KC - 1) / KC);
   const int per = (nchunk + ks_count - 1) / ks_count;
-  const int c_lo = blockIdx.y * per;
+  const int c_lo = split * per;
   const int c_hi = min(c_lo + per, nchunk);
 
   if constexpr (T::fmt == FMT_NF4) {
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void k_skinny(WView w, const uint16_t* __
       const int64_t n = n0 + trow + 4 * lg + i;
       if (n >= w.n) continue;
       if (part != nullptr) {
-        part[((int64_t)blockIdx.y * m + mrow) * w.n + n] = acc[q][i];
+        part[((int64_t)split * m + mrow) * w.n + n] = acc[q][i];
       } else {
         Y[(int64_t)mrow * ldy + (out_rows ? (int64_t)out_rows[n] : n)] = (uint16_t)bf16_rne(acc[q][i]);
       }
@@ -266,22 +268,131 @@ __global__ __launch_bounds__(kThreads) void k_skinny(WView w, const uint16_t* __
   }
 }
 
-// Y[m][col(n)] = bf16( sum over K ranges of part + LoRA term ).
+template <int KIND, int MB>
+__global__ __launch_bounds__(kThreads) void k_skinny(WView w, const uint16_t* __restrict__ X, int m,
+                                                    uint16_t* __restrict__ Y, int64_t ldy,
+                                                    const int32_t* __restrict__ out_rows,
+                                                    float* __restrict__ part, int ks_count,
+                                                    LoraEpi lora, Nf4Table tab) {
+  skinny_tile<KIND, MB>(w, X, m, Y, ldy, out_rows, part, ks_count, lora, tab, blockIdx.x, blockIdx.y);
+}
+
+// Several weights that share X in one launch.  Each keeps the K split it
+// has alone (ks[i], so its outputs equal the single-weight call's): weight i
+// owns workgroups [wg_end[i-1], wg_end[i]) = tiles x ks[i], and when
+// ks[i] > 1 its partials [ks][m][n] start at part + part_off[i].
+struct SkinnySet {
+  WView w[kGemvMaxGroup];
+  uint16_t* y[kGemvMaxGroup];
+  int64_t ldy[kGemvMaxGroup];
+  const int32_t* out_rows[kGemvMaxGroup];
+  int64_t part_off[kGemvMaxGroup];
+  int64_t col_end[kGemvMaxGroup];  // prefix sums of n (the reduce's column space)
+  int wg_end[kGemvMaxGroup];
+  int ks[kGemvMaxGroup];
+  int count;
+};
+
+template <int KIND, int MB>
+__global__ __launch_bounds__(kThreads) void k_skinny_set(SkinnySet set, const uint16_t* __restrict__ X, int m,
+                                                        float* __restrict__ part, Nf4Table tab) {
+  const int b = blockIdx.x;
+  int pi = 0, wbeg = 0;
+#pragma unroll
+  for (int i = 1; i < kGemvMaxGroup; ++i)
+    if (i < set.count && b >= set.wg_end[i - 1]) { pi = i; wbeg = set.wg_end[i - 1]; }
+  const int ks = set.ks[pi];
+  const int tiles = (int)((set.w[pi].n + ROWS - 1) / ROWS);
+  const int r = b - wbeg;
+  const LoraEpi none{nullptr, nullptr, 0, 0};
+  skinny_tile<KIND, MB>(set.w[pi], X, m, set.y[pi], set.ldy[pi], set.out_rows[pi],
+                        ks == 1 ? nullptr : part + set.part_off[pi], ks, none, tab, r % tiles, r / tiles);
+}
+
+// Y[m][col(n)] = bf16( sum over K ranges of part + LoRA term ).  Row mr =
+// blockIdx.y; the partials are summed in range order, their loads issued
+// eight at a time.
 __global__ __launch_bounds__(256) void k_skinny_reduce(const float* __restrict__ part, int ks_count,
                                                       int m, int64_t n, uint16_t* __restrict__ Y,
                                                       int64_t ldy, const int32_t* __restrict__ out_rows,
                                                       LoraEpi lora) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)m * n) return;
-  const int64_t mr = idx / n, c = idx % n;
+  const int64_t mr = blockIdx.y;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= n) return;
+  const float* p = part + mr * n + c;
+  const int64_t stride = (int64_t)m * n;
   float v = 0.f;
-  for (int s = 0; s < ks_count; ++s) v += part[((int64_t)s * m + mr) * n + c];
+  int s = 0;
+  for (; s + 8 <= ks_count; s += 8) {
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = p[(s + j) * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v += t[j];
+  }
+  for (; s < ks_count; ++s) v += p[s * stride];
   if (lora.t != nullptr) {
     for (int j = 0; j < lora.r; ++j)
       v = fmaf(bf16_lo(lora.t[mr * lora.rp + j]), bf16_lo(lora.b[c * lora.r + j]), v);
   }
   Y[mr * ldy + (out_rows ? (int64_t)out_rows[c] : c)] = (uint16_t)bf16_rne(v);
 }
+
+// The set form: columns of all weights side by side (weight i owns columns
+// [col_end[i-1], col_end[i])), same summation order as k_skinny_reduce.
+__global__ __launch_bounds__(256) void k_skinny_reduce_set(const float* __restrict__ part, int m, SkinnySet set) {
+  const int64_t mr = blockIdx.y;
+  const int64_t cg = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int64_t ncol = set.col_end[0];
+#pragma unroll
+  for (int i = 1; i < kGemvMaxGroup; ++i)
+    if (i < set.count) ncol = set.col_end[i];
+  if (cg >= ncol) return;
+  int pi = 0;
+  int64_t cbeg = 0;
+#pragma unroll
+  for (int i = 1; i < kGemvMaxGroup; ++i)
+    if (i < set.count && cg >= set.col_end[i - 1]) { pi = i; cbeg = set.col_end[i - 1]; }
+  const int ks_count = set.ks[pi];
+  if (ks_count == 1) return;  // written by the main kernel
+  const int64_t n = set.w[pi].n, c = cg - cbeg;
+  const float* p = part + set.part_off[pi] + mr * n + c;
+  const int64_t stride = (int64_t)m * n;
+  float v = 0.f;
+  int s = 0;
+  for (; s + 8 <= ks_count; s += 8) {
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = p[(s + j) * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v += t[j];
+  }
+  for (; s < ks_count; ++s) v += p[s * stride];
+  const int32_t* orow = set.out_rows[pi];
+  set.y[pi][mr * set.ldy[pi] + (orow ? (int64_t)orow[c] : c)] = (uint16_t)bf16_rne(v);
+}
+
+template <int KIND, int MB>
+hipError_t launch_set_mb(const SkinnySet& set, int64_t wgs, int64_t ncol, bool reduce, const uint16_t* X,
+                         int64_t m, float* part, const Nf4Table& tab, hipStream_t s) {
+  hipLaunchKernelGGL((k_skinny_set<KIND, MB>), dim3((unsigned)wgs), dim3(kThreads), 0, s, set, X, (int)m, part,
+                     tab);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !reduce) return e;
+  hipLaunchKernelGGL(k_skinny_reduce_set, dim3((unsigned)((ncol + 255) / 256), (unsigned)m), dim3(256), 0, s,
+                     part, (int)m, set);
+  return hipGetLastError();
+}
+
+template <int KIND>
+struct SkinnySetLauncher {
+  static hipError_t run(const SkinnySet& set, int64_t wgs, int64_t ncol, bool reduce, const uint16_t* X,
+                        int64_t m, float* part, const Nf4Table& tab, hipStream_t s) {
+    if (m <= 16) return launch_set_mb<KIND, 1>(set, wgs, ncol, reduce, X, m, part, tab, s);
+    if (m <= 32) return launch_set_mb<KIND, 2>(set, wgs, ncol, reduce, X, m, part, tab, s);
+    return launch_set_mb<KIND, 4>(set, wgs, ncol, reduce, X, m, part, tab, s);
+  }
+};
 
 template <int KIND, int MB>
 hipError_t launch_mb(const WView& w, const uint16_t* X, int64_t m, uint16_t* Y, int64_t ldy,
@@ -293,9 +404,8 @@ hipError_t launch_mb(const WView& w, const uint16_t* X, int64_t m, uint16_t* Y, 
                      direct ? nullptr : part, ks, lora, tab);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || direct) return e;
-  const int64_t total = m * w.n;
-  hipLaunchKernelGGL(k_skinny_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, ks,
-                     (int)m, w.n, Y, ldy, out_rows, lora);
+  hipLaunchKernelGGL(k_skinny_reduce, dim3((unsigned)((w.n + 255) / 256), (unsigned)m), dim3(256), 0, s, part,
+                     ks, (int)m, w.n, Y, ldy, out_rows, lora);
   return hipGetLastError();
 }
 
@@ -313,7 +423,10 @@ struct SkinnyLauncher {
 }  // namespace
 
 int skinny_splits(int64_t n, int64_t k, int64_t m) {
-  const int64_t tiles = (n + ROWS - 1) / ROWS;
+  return skinny_splits_tiles((n + ROWS - 1) / ROWS, k, m);
+}
+
+int skinny_splits_tiles(int64_t tiles, int64_t k, int64_t m) {
   const int64_t nchunk = (k + KC - 1) / KC;
   // Aim at ~512 workgroups, but keep the fp32 partial traffic (ks * m * n * 8
   // bytes) below the packed weight (n * k / 2 bytes for 4-bit).  Measured on
@@ -331,6 +444,40 @@ size_t skinny_workspace_bytes(int64_t n, int64_t k, int64_t m, bool lora) {
   const int ks = skinny_splits(n, k, m);
   if (ks == 1 && !lora) return 0;
   return (size_t)ks * (size_t)m * (size_t)n * sizeof(float);
+}
+
+size_t skinny_set_workspace_bytes(const int64_t* ns, int count, int64_t k, int64_t m) {
+  size_t b = 0;
+  for (int i = 0; i < count; ++i) b += skinny_workspace_bytes(ns[i], k, m, false);
+  return b;
+}
+
+hipError_t launch_skinny_set(WKind kind, const WView* ws, uint16_t* const* ys, const int64_t* ldys,
+                             const int32_t* const* out_rows, int count, const uint16_t* X, int64_t m, float* part,
+                             const Nf4Table& tab, hipStream_t s) {
+  if (count < 1 || count > kGemvMaxGroup || m < 1 || m > kSkinnyMaxM) return hipErrorInvalidValue;
+  SkinnySet set{};
+  set.count = count;
+  int64_t wgs = 0, ncol = 0, off = 0;
+  bool reduce = false;
+  for (int i = 0; i < count; ++i) {
+    set.w[i] = ws[i];
+    set.y[i] = ys[i];
+    set.ldy[i] = ldys[i];
+    set.out_rows[i] = out_rows[i];
+    const int ks = skinny_splits(ws[i].n, ws[i].k, m);
+    set.ks[i] = ks;
+    wgs += (ws[i].n + ROWS - 1) / ROWS * ks;
+    set.wg_end[i] = (int)wgs;
+    ncol += ws[i].n;
+    set.col_end[i] = ncol;
+    set.part_off[i] = off;  // weight i's partials: [ks][m][n_i], when ks > 1
+    if (ks > 1) {
+      off += (int64_t)ks * m * ws[i].n;
+      reduce = true;
+    }
+  }
+  return dispatch_kind<SkinnySetLauncher>(kind, set, wgs, ncol, reduce, X, m, part, tab, s);
 }
 
 hipError_t launch_skinny(WKind kind, const WView& w, const uint16_t* X, int64_t m, uint16_t* Y,

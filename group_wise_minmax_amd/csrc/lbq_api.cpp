@@ -294,11 +294,29 @@ lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint
                     "lbq_linear_fwd");
 }
 
+// Weights of one kind in a grouped call run as one launch (one launch pair
+// for the small-batch kernel when it splits K), one kind after another on the
+// stream; the workspace holds the partials of the largest kind group.
 size_t lbq_linear_fwd_grouped_workspace_bytes(int32_t count, const lbq_desc* descs, int64_t m) {
   if (count < 1 || count > LBQ_MAX_GROUP || descs == nullptr) return 0;
-  size_t need = 0;
   for (int32_t i = 0; i < count; ++i)
-    if (check_desc(&descs[i]) == LBQ_OK) need = std::max(need, fwd_workspace(&descs[i], m, false));
+    if (check_desc(&descs[i]) != LBQ_OK) return 0;
+  if (m < 2 || m > lbq::kSkinnyMaxM) return 0;
+  size_t need = 0;
+  bool done[LBQ_MAX_GROUP] = {};
+  for (int32_t i = 0; i < count; ++i) {
+    if (done[i]) continue;
+    const lbq::WKind kind = kind_of(&descs[i]);
+    if (lbq::gemvm_fits(kind, descs[i].k, m)) continue;
+    int64_t ns[LBQ_MAX_GROUP];
+    int c = 0;
+    for (int32_t j = i; j < count; ++j)
+      if (!done[j] && kind_of(&descs[j]) == kind) {
+        done[j] = true;
+        ns[c++] = descs[j].n;
+      }
+    need = std::max(need, lbq::skinny_set_workspace_bytes(ns, c, descs[i].k, m));
+  }
   return need;
 }
 
@@ -324,38 +342,31 @@ lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lb
   const lbq::LoraEpi none{nullptr, nullptr, 0, 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  bool streamed = m <= lbq::kGemvmMaxM;  // m == 1, or every weight's staged x rows fit
-  for (int32_t i = 0; i < count && streamed && m > 1; ++i) streamed = lbq::gemvm_fits(kind_of(&descs[i]), descs[i].k, m);
-  if (streamed || m > lbq::kSkinnyMaxM) {
-    // One launch per distinct weight kind, in order of first appearance.
-    bool done[LBQ_MAX_GROUP] = {};
-    for (int32_t i = 0; i < count && e == hipSuccess; ++i) {
-      if (done[i]) continue;
-      const lbq::WKind kind = kind_of(&descs[i]);
-      lbq::WView ws[LBQ_MAX_GROUP];
-      uint16_t* ys[LBQ_MAX_GROUP];
-      int64_t lds[LBQ_MAX_GROUP];
-      const int32_t* rows[LBQ_MAX_GROUP];
-      int c = 0;
-      for (int32_t j = i; j < count; ++j) {
-        if (done[j] || kind_of(&descs[j]) != kind) continue;
-        done[j] = true;
-        ws[c] = view_of(&descs[j], &qs[j]);
-        ys[c] = Ys[j];
-        lds[c] = ldys[j];
-        rows[c] = qs[j].out_rows;
-        ++c;
-      }
-      if (m == 1) e = lbq::launch_gemv1(kind, ws, ys, rows, c, X, none, nf4_table(), s);
-      else if (streamed) e = lbq::launch_gemvm(kind, ws, ys, lds, rows, c, X, m, none, nf4_table(), s);
-      else e = lbq::launch_gemm_fwd_set(kind, ws, ys, lds, rows, c, X, m, nf4_table(), s);
+  // One launch per distinct weight kind, in order of first appearance, with
+  // the kernel lbq_linear_fwd picks for that kind (all weights share k).
+  bool done[LBQ_MAX_GROUP] = {};
+  for (int32_t i = 0; i < count && e == hipSuccess; ++i) {
+    if (done[i]) continue;
+    const lbq::WKind kind = kind_of(&descs[i]);
+    lbq::WView ws[LBQ_MAX_GROUP];
+    uint16_t* ys[LBQ_MAX_GROUP];
+    int64_t lds[LBQ_MAX_GROUP];
+    const int32_t* rows[LBQ_MAX_GROUP];
+    int c = 0;
+    for (int32_t j = i; j < count; ++j) {
+      if (done[j] || kind_of(&descs[j]) != kind) continue;
+      done[j] = true;
+      ws[c] = view_of(&descs[j], &qs[j]);
+      ys[c] = Ys[j];
+      lds[c] = ldys[j];
+      rows[c] = qs[j].out_rows;
+      ++c;
     }
-  } else {
-    // The small-batch kernel launches each weight in turn (the workspace is
-    // reused: launches on one stream run in order).
-    for (int32_t i = 0; i < count && e == hipSuccess; ++i)
-      e = dispatch_fwd(&descs[i], view_of(&descs[i], &qs[i]), X, m, Ys[i], ldys[i], qs[i].out_rows, none,
-                       workspace, s);
+    if (m == 1) e = lbq::launch_gemv1(kind, ws, ys, rows, c, X, none, nf4_table(), s);
+    else if (lbq::gemvm_fits(kind, descs[i].k, m)) e = lbq::launch_gemvm(kind, ws, ys, lds, rows, c, X, m, none, nf4_table(), s);
+    else if (m <= lbq::kSkinnyMaxM)
+      e = lbq::launch_skinny_set(kind, ws, ys, lds, rows, c, X, m, static_cast<float*>(workspace), nf4_table(), s);
+    else e = lbq::launch_gemm_fwd_set(kind, ws, ys, lds, rows, c, X, m, nf4_table(), s);
   }
   return hip_status(e, "lbq_linear_fwd_grouped");
 }

@@ -80,6 +80,14 @@ hipError_t launch_gemvm(WKind kind, const WView* ws, uint16_t* const* ys, const 
 // skinny_splits() workgroups whose fp32 partials (workspace) are summed by a
 // second kernel when more than one range is used or a LoRA term is added.
 int skinny_splits(int64_t n, int64_t k, int64_t m);
+int skinny_splits_tiles(int64_t tiles, int64_t k, int64_t m);
+// Weights of one kind that share X (count <= kGemvMaxGroup, same k): one
+// launch over all their row tiles and, when K is split, one reduce launch.
+// Workspace: skinny_set_workspace_bytes() bytes of fp32 partials.
+size_t skinny_set_workspace_bytes(const int64_t* ns, int count, int64_t k, int64_t m);
+hipError_t launch_skinny_set(WKind kind, const WView* ws, uint16_t* const* ys, const int64_t* ldys,
+                             const int32_t* const* out_rows, int count, const uint16_t* X, int64_t m, float* part,
+                             const Nf4Table& tab, hipStream_t s);
 size_t skinny_workspace_bytes(int64_t n, int64_t k, int64_t m, bool lora);
 hipError_t launch_skinny(WKind kind, const WView& w, const uint16_t* X, int64_t m, uint16_t* Y,
                          int64_t ldy, const int32_t* out_rows, float* part, const LoraEpi& lora,

@@ -184,12 +184,15 @@ size_t lbq_linear_fwd_grouped_workspace_bytes(int32_t count, const lbq_desc* des
  * descs, qs, Ys, ldys: host arrays of `count` entries (1 <= count <=
  * LBQ_MAX_GROUP); every weight has the same k.  Several weights may scatter
  * (out_rows) into disjoint columns of one Y.  Every weight is checked as in
- * lbq_linear_fwd before anything is enqueued.  Where lbq_linear_fwd would
- * stream the weight (m == 1; 2 <= m <= 4 with the rows of X in LDS) and for
- * m > 64, the weights of one kind run in a single launch (one launch per
- * distinct kind: a GEMV streaming all of them, or a GEMM whose column tiles
- * cover all of them); otherwise each weight is launched in turn, reusing the
- * workspace (lbq_linear_fwd_grouped_workspace_bytes). */
+ * lbq_linear_fwd before anything is enqueued.  The weights of one kind run
+ * in a single launch of the kernel lbq_linear_fwd picks for that m (one
+ * launch per distinct kind, in order of first appearance: a GEMV streaming all
+ * of them, the small-batch kernel over all their row tiles, or a GEMM whose
+ * column tiles cover all of them); the small-batch kernel adds one launch
+ * that sums its K-split partials.  Each Ys[i] equals what lbq_linear_fwd
+ * writes for weight i alone, bit for bit.  `workspace` must hold
+ * lbq_linear_fwd_grouped_workspace_bytes(count, descs, m) bytes (16-byte
+ * aligned; 0 for m == 1, m > 64 and the multi-row GEMV). */
 lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lbq_qtensor* qs,
                                   const uint16_t* X, int64_t m, uint16_t* const* Ys,
                                   const int64_t* ldys, void* workspace, size_t ws_bytes,

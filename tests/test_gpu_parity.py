@@ -448,14 +448,15 @@ GROUP_SETS = {
 
 @pytest.mark.parametrize("name", list(GROUP_SETS))
 @pytest.mark.parametrize("k", [1280, 12288])
-@pytest.mark.parametrize("m", [1, 3, 16, 130, 300])
+@pytest.mark.parametrize("m", [1, 3, 16, 40, 130, 300])
 def test_grouped_fwd_matches_single(L, name, k, m):
     """Weights sharing X in one call: each output equals the single-weight
     forward bit for bit (same kernels, same per-row order) and the oracle
     within the matmul tolerance.  Ragged n; at m = 1 same-kind weights share
-    one launch and the mixed set needs three, as at m = 3 with rows short
-    enough for the multi-row GEMV; at m > 64 the GEMM lays the weights'
-    column tiles side by side."""
+    one launch and the mixed set needs three, at every m: the GEMVs, the
+    small-batch kernel (each weight keeping its own K split, so the sums run
+    in the same order) and the GEMM, which lays the weights' column tiles
+    side by side."""
     specs = GROUP_SETS[name]
     ns = [300, 64, 520, 130][:len(specs)]
     X = SI.bf16_normal(9400 + m, (m, k))

@@ -17,6 +17,8 @@
 
 #include "lbq_device.h"
 
+#include <cmath>
+
 namespace lbq {
 
 namespace {
@@ -105,7 +107,16 @@ __global__ __launch_bounds__(kThreads) void k_quant_minmax(const float* __restri
 // in LDS and the second-level int8 codes are produced in the same launch.
 // Eight lanes share a 64-block (8 weights each).
 // ---------------------------------------------------------------------------
-template <bool DQ>
+// Code of x = w / absmax (|x| <= 1): the number of midpoints strictly below
+// x.  BUCKET: [-1, 1] cut into 64 equal buckets, each holding at most one
+// midpoint, none within 1/1000 of a bucket width of an edge (the launcher
+// checks the table); bucket b stores the midpoints below its lower edge and
+// the one inside it, so a code is one LDS read and one compare.  The bucket
+// coordinate (x + 1) * 32 is within 4e-6 of a bucket width of exact, so the
+// bucket never changes the answer.  Otherwise a 4-probe binary search.
+constexpr int kNf4Buckets = 64;
+
+template <bool DQ, bool BUCKET>
 __global__ __launch_bounds__(kThreads) void k_quant_nf4(const float* __restrict__ W,
                                                        uint8_t* __restrict__ packed,
                                                        float* __restrict__ absmax,
@@ -113,17 +124,29 @@ __global__ __launch_bounds__(kThreads) void k_quant_nf4(const float* __restrict_
                                                        float* __restrict__ absmax_scale,
                                                        int64_t nblocks, Nf4Table tab) {
   __shared__ float mids[16];
+  __shared__ float2 bk[kNf4Buckets];  // (midpoint inside or +inf, midpoints below as int bits)
   __shared__ float am[256];
   __shared__ float red[kThreads / 64];
   const int t = threadIdx.x;
   if (t < 15) mids[t] = (tab.c[t] + tab.c[t + 1]) * 0.5f;
   __syncthreads();
+  if (BUCKET && t < kNf4Buckets) {
+    const float lo = -1.f + (float)t * (2.f / kNf4Buckets), hi = lo + 2.f / kNf4Buckets;
+    int below = 0;
+    float inside = __builtin_huge_valf();
+    for (int j = 0; j < 15; ++j) {
+      if (mids[j] < lo) ++below;
+      else if (mids[j] < hi) inside = mids[j];
+    }
+    bk[t] = make_float2(inside, __int_as_float(below));
+  }
+  if (BUCKET) __syncthreads();
 
   const int64_t b0 = (int64_t)blockIdx.x * 256;
   const int nb_here = (int)((nblocks - b0) < 256 ? (nblocks - b0) : 256);
 
-#pragma unroll 2
-  for (int it = 0; it < 8; ++it) {
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {  // all eight loads of a lane in flight together
     const int lb = it * 32 + (t >> 3);
     const bool valid = lb < nb_here;
     const int64_t c = (b0 + lb) * 8 + (t & 7);
@@ -146,11 +169,18 @@ __global__ __launch_bounds__(kThreads) void k_quant_nf4(const float* __restrict_
       int code = 7;
       if (a != 0.f) {
         const float x = w[i] / a;
-        // number of midpoints strictly below x (binary search, 4 probes)
-        code = (x > mids[7]) ? 8 : 0;
-        code += (x > mids[code + 3]) ? 4 : 0;
-        code += (x > mids[code + 1]) ? 2 : 0;
-        code += (x > mids[code]) ? 1 : 0;
+        if constexpr (BUCKET) {
+          // NaN lands in bucket 0 and compares false: code 0, as in the search
+          const float u = fminf(fmaxf((x + 1.f) * (kNf4Buckets / 2), 0.f), (float)(kNf4Buckets - 1));
+          const float2 e = bk[(int)u];
+          code = __float_as_int(e.y) + (x > e.x ? 1 : 0);
+        } else {
+          // number of midpoints strictly below x (binary search, 4 probes)
+          code = (x > mids[7]) ? 8 : 0;
+          code += (x > mids[code + 3]) ? 4 : 0;
+          code += (x > mids[code + 1]) ? 2 : 0;
+          code += (x > mids[code]) ? 1 : 0;
+        }
       }
       word |= (uint32_t)code << (8 * (i >> 1) + ((i & 1) ? 0 : 4));
     }
@@ -286,12 +316,30 @@ hipError_t launch_quant_nf4(bool dq, const float* W, uint8_t* packed, float* abs
                             const Nf4Table& tab, hipStream_t s) {
   const int64_t nblocks = n * k / 64;
   const dim3 grid((unsigned)((nblocks + 255) / 256)), block(kThreads);
+  // The bucket lookup needs at most one midpoint per bucket, each clear of
+  // the bucket edges (midpoints formed in fp32 as the kernel forms them).
+  bool bucket = true;
+  int per[kNf4Buckets] = {};
+  for (int j = 0; j < 15 && bucket; ++j) {
+    const float mid = (tab.c[j] + tab.c[j + 1]) * 0.5f;
+    const double u = ((double)mid + 1.0) * (kNf4Buckets / 2);
+    const double f = u - std::floor(u);
+    if (!(u > 0.0 && u < kNf4Buckets) || f < 1e-3 || f > 1.0 - 1e-3 || ++per[(int)u] > 1) bucket = false;
+  }
   if (dq) {
-    hipLaunchKernelGGL((k_quant_nf4<true>), grid, block, 0, s, W, packed, absmax, absmax_q,
-                       absmax_scale, nblocks, tab);
+    if (bucket)
+      hipLaunchKernelGGL((k_quant_nf4<true, true>), grid, block, 0, s, W, packed, absmax, absmax_q, absmax_scale,
+                         nblocks, tab);
+    else
+      hipLaunchKernelGGL((k_quant_nf4<true, false>), grid, block, 0, s, W, packed, absmax, absmax_q,
+                         absmax_scale, nblocks, tab);
   } else {
-    hipLaunchKernelGGL((k_quant_nf4<false>), grid, block, 0, s, W, packed, absmax, absmax_q,
-                       absmax_scale, nblocks, tab);
+    if (bucket)
+      hipLaunchKernelGGL((k_quant_nf4<false, true>), grid, block, 0, s, W, packed, absmax, absmax_q,
+                         absmax_scale, nblocks, tab);
+    else
+      hipLaunchKernelGGL((k_quant_nf4<false, false>), grid, block, 0, s, W, packed, absmax, absmax_q,
+                         absmax_scale, nblocks, tab);
   }
   return hipGetLastError();
 }

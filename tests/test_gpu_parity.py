@@ -73,6 +73,29 @@ def test_quantize_heavy_tailed_and_special_groups(L, fmtspec):
     assert np.array_equal(bf16_bits_host(wb), ref["w_bf16"])
 
 
+@pytest.mark.parametrize("dq", [False, True], ids=["nf4", "nf4dq"])
+def test_nf4_codes_at_midpoints_and_bucket_edges(L, dq):
+    """Blocks whose absmax is 1 or 1/2 (so x = w / absmax is exact) put x on
+    every NF4 midpoint (a tie takes the lower code), one ulp either side, and
+    on every multiple of 1/32 in [-1, 1] with its neighbours: the codes, the
+    absmax data and the dequantized weights equal the oracle's bit for bit."""
+    mids = O.nf4_midpoints(O.nf4_codebook())
+    steps = (-1.0 + np.arange(65, dtype=np.float64) / 32).astype(np.float32)
+    pts = np.concatenate([mids, steps]).astype(np.float32)
+    vals = np.concatenate([pts, np.nextafter(pts, np.float32(2)), np.nextafter(pts, np.float32(-2))])
+    vals = np.clip(vals, np.float32(-1), np.float32(1)).astype(np.float32)
+    nblk = -(-vals.size // 63)
+    nblk += (-nblk) % 4                                # 4 blocks per row of 256
+    body = np.resize(vals, nblk * 63).reshape(nblk, 63)
+    blocks = np.concatenate([np.ones((nblk, 1), np.float32), body], axis=1)
+    W = np.concatenate([blocks, blocks * np.float32(0.5)]).reshape(-1, 256).astype(np.float32)
+    qw, ref = _quant_pair(L, W, "nf4", 4, 64, dq)
+    wb = L.lbq_dequant(qw)
+    torch.cuda.synchronize()
+    check_quantized_equal(qw, ref, "nf4", dq)
+    assert np.array_equal(bf16_bits_host(wb), ref["w_bf16"])
+
+
 def test_quantize_config0_is_deterministic(L):
     """Single linear layer of 256x256, INT4 g128: two runs give identical bytes."""
     W = SI.gaussian_weights(SI.seed_of(0, 0, 0), 256, 256)

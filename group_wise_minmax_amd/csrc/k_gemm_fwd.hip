@@ -263,6 +263,32 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
   }
 
   // Epilogue: lane holds D[n = base + 4*lg + i][m = base + li], i = 0..3.
+  if (out_rows != nullptr) {
+    // Scattered columns: the lane's 4*TN target columns are loaded together,
+    // once (clamped indices; columns past n are never stored).
+    int32_t col[TN][4];
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t n = n0 + wn * WN + 16 * a + 4 * lg + i;
+        col[a][i] = out_rows[n < w.n ? n : w.n - 1];
+      }
+#pragma unroll
+    for (int a = 0; a < TN; ++a) {
+      const int64_t nb = n0 + wn * WN + 16 * a + 4 * lg;
+#pragma unroll
+      for (int b = 0; b < TM; ++b) {
+        const int64_t mr = m0 + wm * WM + 16 * b + li;
+        if (mr >= m) continue;
+        uint16_t* yrow = Y + mr * ldy;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (nb + i < w.n) yrow[col[a][i]] = (uint16_t)bf16_rne(acc[a][b][i]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int a = 0; a < TN; ++a) {
     const int64_t nb = n0 + wn * WN + 16 * a + 4 * lg;
@@ -278,10 +304,8 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
         *reinterpret_cast<uint2*>(yrow + nb) = v;
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t n = nb + i;
-          if (n < w.n) yrow[out_rows ? (int64_t)out_rows[n] : n] = (uint16_t)bf16_rne(acc[a][b][i]);
-        }
+        for (int i = 0; i < 4; ++i)
+          if (nb + i < w.n) yrow[nb + i] = (uint16_t)bf16_rne(acc[a][b][i]);
       }
     }
   }

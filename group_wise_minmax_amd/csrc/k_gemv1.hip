@@ -37,6 +37,8 @@
 //    with x; the block absmax scales the chunk sum.
 #include "lbq_device.h"
 
+#include <algorithm>
+
 namespace lbq {
 
 namespace {
@@ -386,6 +388,46 @@ __global__ __launch_bounds__(kThreads) void k_gemv1_set(Gemv1Set set, const uint
                                  gw < wlast, X, none, tab);
 }
 
+// Waves of set entries [lo, hi), whose wave ranges start at wave wbeg0.
+template <int KIND, int R, int CB, int D, bool XG>
+__device__ __forceinline__ void gemv1_set_part(const Gemv1Set& set, int lo, int hi, int wbeg0, int gw,
+                                               const uint16_t* __restrict__ X, const Nf4Table& tab, int gpw) {
+  int pi = lo, wbeg = wbeg0, wlast = set.wave_end[lo];
+#pragma unroll
+  for (int i = 1; i < kGemvMaxGroup; ++i)
+    if (i > lo && i < hi) {
+      if (gw >= set.wave_end[i - 1]) { pi = i; wbeg = set.wave_end[i - 1]; }
+      wlast = set.wave_end[i];
+    }
+  const int g0 = (gw - wbeg) * gpw;
+  const LoraEpi none{nullptr, nullptr, 0, 0};
+  gemv1_body<KIND, R, CB, D, XG>(set.w[pi], set.y[pi], set.out_rows[pi], g0, min(g0 + gpw, set.ngroups[pi]),
+                                 gw < wlast, X, none, tab);
+}
+
+template <int R_, int CB_, int D_, bool XG_>
+struct G1Cfg {
+  static constexpr int R = R_, CB = CB_, D = D_;
+  static constexpr bool XG = XG_;
+};
+
+// The INT4 g128 and INT2 g64 row sets of channel-mixed linears that share x,
+// in one launch: workgroups [0, wg_a) run set entries [0, first_b) (INT4),
+// the rest entries [first_b, count) (INT2), whose wave ranges start at wave
+// 4 * wg_a.  Each format keeps the launch shape and the per-wave work of its
+// own launch, so the outputs are the same bits.
+template <class CA, class CB2>
+__global__ __launch_bounds__(kThreads) void k_gemv1_mix(Gemv1Set set, const uint16_t* __restrict__ X,
+                                                       Nf4Table tab, int first_b, int wg_a, int gpw_a,
+                                                       int gpw_b) {
+  const int gw = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if ((int)blockIdx.x < wg_a)
+    gemv1_set_part<WK_I4G128, CA::R, CA::CB, CA::D, CA::XG>(set, 0, first_b, 0, gw, X, tab, gpw_a);
+  else
+    gemv1_set_part<WK_I2G64, CB2::R, CB2::CB, CB2::D, CB2::XG>(set, first_b, set.count, (kThreads / 64) * wg_a,
+                                                               gw, X, tab, gpw_b);
+}
+
 // ---------------------------------------------------------------------------
 // Several x rows (2 <= m <= MV <= 4): the same streaming of the weight, with
 // the arranged x of every row staged in LDS.  A chunk's codes become bf16
@@ -647,14 +689,12 @@ size_t lds_bytes(int64_t k, bool xg) {
   return b;
 }
 
-// spw: target steps per wave (each wave keeps up to D steps of loads in
-// flight); the grid never has fewer than min_waves waves when there is that
-// much work.  The row groups of all weights share one wave budget; each
-// weight gets whole waves.
-template <int KIND, int R, int CB, int D, bool XG>
-hipError_t launch_set(const WView* ws, uint16_t* const* ys, const int32_t* const* orows, int count,
-                      const uint16_t* X, const LoraEpi& lora, const Nf4Table& tab, hipStream_t s,
-                      int spw, int min_waves = 1024) {
+// Wave plan of `count` weights of one kind (entries [first, first + count) of
+// `set`, wave ranges from wave `base`): groups of R rows, gpw groups per wave.
+// Returns gpw; *wend = the end of the last wave range.
+template <int KIND, int R, int CB>
+int64_t plan_set(const WView* ws, uint16_t* const* ys, const int32_t* const* orows, int count, int spw,
+                 int min_waves, Gemv1Set& set, int first, int64_t base, int64_t* wend_out) {
   using T = WKindTraits<KIND>;
   const int64_t nchunk = ws[0].k * T::bits / 8 / 16;
   const int64_t nsteps = ((nchunk + 63) / 64 + CB - 1) / CB;
@@ -664,18 +704,32 @@ hipError_t launch_set(const WView* ws, uint16_t* const* ys, const int32_t* const
   waves = waves < min_waves ? min_waves : waves;
   waves = waves > groups ? groups : waves;
   const int64_t gpw = (groups + waves - 1) / waves;
-  Gemv1Set set{};
-  set.count = count;
-  int64_t wend = 0;
+  int64_t wend = base;
   for (int i = 0; i < count; ++i) {
     const int64_t ng = (ws[i].n + R - 1) / R;
     wend += (ng + gpw - 1) / gpw;
-    set.w[i] = ws[i];
-    set.y[i] = ys[i];
-    set.out_rows[i] = orows[i];
-    set.wave_end[i] = (int)wend;
-    set.ngroups[i] = (int)ng;
+    set.w[first + i] = ws[i];
+    set.y[first + i] = ys[i];
+    set.out_rows[first + i] = orows[i];
+    set.wave_end[first + i] = (int)wend;
+    set.ngroups[first + i] = (int)ng;
   }
+  *wend_out = wend;
+  return gpw;
+}
+
+// spw: target steps per wave (each wave keeps up to D steps of loads in
+// flight); the grid never has fewer than min_waves waves when there is that
+// much work.  The row groups of all weights share one wave budget; each
+// weight gets whole waves.
+template <int KIND, int R, int CB, int D, bool XG>
+hipError_t launch_set(const WView* ws, uint16_t* const* ys, const int32_t* const* orows, int count,
+                      const uint16_t* X, const LoraEpi& lora, const Nf4Table& tab, hipStream_t s,
+                      int spw, int min_waves = 1024) {
+  Gemv1Set set{};
+  set.count = count;
+  int64_t wend = 0;
+  const int64_t gpw = plan_set<KIND, R, CB>(ws, ys, orows, count, spw, min_waves, set, 0, 0, &wend);
   const dim3 grid((unsigned)((wend + 3) / 4));
   const size_t lds = lds_bytes<KIND>(ws[0].k, XG);
   if (count == 1)
@@ -717,6 +771,37 @@ struct Gemv1Launcher {
     }
   }
 };
+
+// The mixed launch: each format planned exactly as its own launch would be
+// (Gemv1Launcher's choice of shape), INT4 waves first, rounded up to whole
+// workgroups.
+template <class CA, class CB2>
+hipError_t launch_mix_cfg(const WView* ws, uint16_t* const* ys, const int32_t* const* orows, int count_a,
+                          int count_b, const uint16_t* X, const Nf4Table& tab, hipStream_t s, int spw_a,
+                          int spw_b) {
+  Gemv1Set set{};
+  set.count = count_a + count_b;
+  int64_t wend_a = 0, wend_b = 0;
+  const int64_t gpw_a = plan_set<WK_I4G128, CA::R, CA::CB>(ws, ys, orows, count_a, spw_a, 1024, set, 0, 0, &wend_a);
+  const int64_t wg_a = (wend_a + 3) / 4;
+  const int64_t gpw_b = plan_set<WK_I2G64, CB2::R, CB2::CB>(ws + count_a, ys + count_a, orows + count_a, count_b,
+                                                           spw_b, 1024, set, count_a, 4 * wg_a, &wend_b);
+  const int64_t k = ws[0].k;
+  const size_t lds = std::max(lds_bytes<WK_I4G128>(k, CA::XG), lds_bytes<WK_I2G64>(k, CB2::XG));
+  hipLaunchKernelGGL((k_gemv1_mix<CA, CB2>), dim3((unsigned)((wend_b + 3) / 4)), dim3(kThreads), lds, s, set, X,
+                     tab, count_a, (int)wg_a, (int)gpw_a, (int)gpw_b);
+  return hipGetLastError();
+}
+
+template <class CA>
+hipError_t launch_mix_b(const WView* ws, uint16_t* const* ys, const int32_t* const* orows, int count_a,
+                        int count_b, const uint16_t* X, const Nf4Table& tab, hipStream_t s) {
+  const int64_t k = ws[0].k;
+  if (lds_bytes<WK_I2G64>(k, false) > 65536)
+    return launch_mix_cfg<CA, G1Cfg<2, 1, 1, true>>(ws, ys, orows, count_a, count_b, X, tab, s, 1, 2);
+  if (k <= 8192) return launch_mix_cfg<CA, G1Cfg<2, 2, 2, false>>(ws, ys, orows, count_a, count_b, X, tab, s, 1, 1);
+  return launch_mix_cfg<CA, G1Cfg<2, 1, 4, false>>(ws, ys, orows, count_a, count_b, X, tab, s, 1, 2);
+}
 
 template <int KIND, int MV>
 size_t lds_bytes_m(int64_t k) {
@@ -796,6 +881,18 @@ hipError_t launch_gemvm(WKind kind, const WView* ws, uint16_t* const* ys, const 
                         const LoraEpi& lora, const Nf4Table& tab, hipStream_t s) {
   if (count < 1 || count > kGemvMaxGroup || !gemvm_fits(kind, ws[0].k, m)) return hipErrorInvalidValue;
   return dispatch_kind<GemvmLauncher>(kind, ws, ys, ldys, out_rows, count, X, m, lora, tab, s);
+}
+
+hipError_t launch_gemv1_mix(const WView* ws, uint16_t* const* ys, const int32_t* const* out_rows, int count_a,
+                            int count_b, const uint16_t* X, const Nf4Table& tab, hipStream_t s) {
+  if (count_a < 1 || count_b < 1 || count_a + count_b > kGemvMaxGroup) return hipErrorInvalidValue;
+  int64_t rows_a = 0;
+  for (int i = 0; i < count_a; ++i) rows_a += ws[i].n;
+  const int64_t k = ws[0].k;
+  if (rows_a < 2048) return launch_mix_b<G1Cfg<1, 2, 2, true>>(ws, ys, out_rows, count_a, count_b, X, tab, s);
+  if (rows_a <= 8192 && k <= 8192)
+    return launch_mix_b<G1Cfg<2, 2, 2, true>>(ws, ys, out_rows, count_a, count_b, X, tab, s);
+  return launch_mix_b<G1Cfg<2, 2, 1, true>>(ws, ys, out_rows, count_a, count_b, X, tab, s);
 }
 
 hipError_t launch_gemv1(WKind kind, const WView* ws, uint16_t* const* ys, const int32_t* const* out_rows,

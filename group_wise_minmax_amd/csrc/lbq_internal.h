@@ -65,6 +65,11 @@ hipError_t launch_dequant(WKind kind, const WView& w, uint16_t* out, const Nf4Ta
 // m == 1 decode GEMV over up to kGemvMaxGroup weights of one kind that share x
 // and k (ws[i], ys[i], out_rows[i] per weight; the LoRA term only with count 1).
 constexpr int kGemvMaxGroup = 8;
+// m = 1, the two row sets of channel-mixed linears that share x in one launch:
+// INT4 g128 weights ws[0, count_a), INT2 g64 weights ws[count_a, count_a +
+// count_b) (same k); outputs equal those of the two per-format launches.
+hipError_t launch_gemv1_mix(const WView* ws, uint16_t* const* ys, const int32_t* const* out_rows, int count_a,
+                            int count_b, const uint16_t* X, const Nf4Table& tab, hipStream_t s);
 hipError_t launch_gemv1(WKind kind, const WView* ws, uint16_t* const* ys, const int32_t* const* out_rows,
                         int count, const uint16_t* X, const LoraEpi& lora, const Nf4Table& tab,
                         hipStream_t s);

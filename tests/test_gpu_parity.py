@@ -466,6 +466,8 @@ def test_forward_gemv_long_rows(L, fmtspec):
 GROUP_SETS = {
     "three_i4g128": [FORMATS[0]] * 3,
     "mixed_kinds": [FORMATS[0], FORMATS[1], FORMATS[5], FORMATS[0]],
+    # the channel-mixed layer's two formats only (one launch at m = 1)
+    "channel_mix": [FORMATS[0], FORMATS[1], FORMATS[1], FORMATS[0]],
 }
 
 

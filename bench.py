@@ -16,7 +16,7 @@ this order:
                split-K partials are summed by a second launch per group)
   chmix_70b_m1     70B-shaped layer, per-channel 25% INT4 g128 / 75% INT2 g64
                    (each format's rows scatter into Y), m = 1: the linears that
-                   share X in one call, one launch per format (8 per layer)
+                   share X in one call, both formats in one launch (4 per layer)
   quant_int4   quantize + pack the 7 fp32 weights, MinMax INT4 g128
   quant_nf4dq  quantize + pack the 7 weights, NF4 block 64 + double quant
   dequant      dequantize the 7 NF4-DQ weights to bf16
@@ -29,7 +29,8 @@ this order:
   bwd_m4096    NF4-DQ input gradient dX = dY deq(W) at m = 4096
   lora_bwd_m4096  NF4-DQ LoRA backward (dX with the adapter term, dA, dB),
                rank 16 on q and v, at m = 4096
-  chmix_70b_m1024  the 70B-shaped channel-mix layer at m = 1024
+  chmix_70b_m1024  the 70B-shaped channel-mix layer at m = 1024, one call (one
+                   launch) per format and linear
   copy_1g      (only with --phases) a plain 1 GiB device-to-device copy, the
                reference kernel for scaling hardware byte counters
 
@@ -303,7 +304,7 @@ def build_workload(L, SI, torch, dev, R, want):
         ("gemv_m1_per_linear", p_gemv(X1, Y1), lambda: {"bound": "hbm", "bytes": gemv_bytes(1), "launches": 7 * R}),
         ("gemv_m4", p_gemv_grouped(X4, Y4), lambda: {"bound": "hbm", "bytes": gemv_bytes_grouped(4), "launches": len(GROUPS) * R}),
         ("gemv_m16", p_gemv_grouped(X16, Y16), lambda: {"bound": "hbm", "bytes": gemv_bytes_grouped(16), "launches": len(GROUPS) * R}),
-        ("chmix_70b_m1", p_chmix_m1, lambda: {"bound": "hbm", "bytes": sum(a.nbytes() + b.nbytes() + 2 * (a.n + b.n) for _, a, b, *_ in cm) + sum(2 * next(a.k for nm, a, *_ in cm if nm == g[0]) for g in GROUPS), "launches": 2 * len(GROUPS)}),
+        ("chmix_70b_m1", p_chmix_m1, lambda: {"bound": "hbm", "bytes": sum(a.nbytes() + b.nbytes() + 2 * (a.n + b.n) for _, a, b, *_ in cm) + sum(2 * next(a.k for nm, a, *_ in cm if nm == g[0]) for g in GROUPS), "launches": len(GROUPS)}),
         ("quant_int4", p_quant_int4, lambda: {"bound": "hbm", "bytes": quant_bytes(q4), "launches": 7}),
         ("quant_nf4dq", p_quant_nf4dq, lambda: {"bound": "hbm", "bytes": quant_bytes(qn), "launches": 7}),
         ("dequant", p_dequant, lambda: {"bound": "hbm", "bytes": sum(qn[nm].nbytes() + 2 * N_of[nm] * K_of[nm] for nm in names), "launches": 7}),

@@ -74,8 +74,7 @@ __device__ __forceinline__ void dequant32(const u32x4_t& raw, float s, float zs,
   }
 }
 
-// LDS of one workgroup, declared by the kernel (one copy however many weight
-// formats the kernel's tiles may take).
+// LDS of one workgroup, declared by the kernel and handed to the tile code.
 template <int BN, int BM>
 struct GemmLds {
   uint16_t Ws[2][BN * BK];
@@ -366,37 +365,10 @@ __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd_set(GemmSet set, con
                                                none, tab, tx - tbeg, ty, lds);
 }
 
-// The INT4 g128 and INT2 g64 row sets of channel-mixed linears that share X
-// in one launch: set entries [0, first_b) are INT4, the rest INT2; a
-// workgroup's tile belongs to one weight, so it runs that weight's format.
-template <int BN, int BM, int WGN, int WGM>
-__global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd_mix(GemmSet set, const uint16_t* __restrict__ X,
-                                                              int m, Nf4Table tab, int first_b) {
-  int nx = set.tile_end[0];
-#pragma unroll
-  for (int i = 1; i < kGemvMaxGroup; ++i)
-    if (i < set.count) nx = set.tile_end[i];
-  int tx, ty;
-  tile_of(blockIdx.x, nx, (m + BM - 1) / BM, tx, ty);
-  int pi = 0, tbeg = 0;
-#pragma unroll
-  for (int i = 1; i < kGemvMaxGroup; ++i)
-    if (i < set.count && tx >= set.tile_end[i - 1]) { pi = i; tbeg = set.tile_end[i - 1]; }
-  const LoraEpi none{nullptr, nullptr, 0, 0};
-  __shared__ __attribute__((aligned(16))) GemmLds<BN, BM> lds;
-  if (pi < first_b)
-    gemm_fwd_tile<WK_I4G128, BN, BM, WGN, WGM, false>(set.w[pi], X, m, set.y[pi], set.ldy[pi], set.out_rows[pi],
-                                                      none, tab, tx - tbeg, ty, lds);
-  else
-    gemm_fwd_tile<WK_I2G64, BN, BM, WGN, WGM, false>(set.w[pi], X, m, set.y[pi], set.ldy[pi], set.out_rows[pi],
-                                                     none, tab, tx - tbeg, ty, lds);
-}
-
-// first_b > 0: entries [0, first_b) INT4 g128, the rest INT2 g64, one mixed launch.
 template <int KIND, int BN, int BM, int WGN, int WGM>
 hipError_t launch_set_cfg(const WView* ws, uint16_t* const* ys, const int64_t* ldys,
                           const int32_t* const* orows, int count, const uint16_t* X, int64_t m,
-                          const Nf4Table& tab, hipStream_t s, int first_b = 0) {
+                          const Nf4Table& tab, hipStream_t s) {
   GemmSet set{};
   set.count = count;
   int64_t nx = 0;
@@ -409,10 +381,7 @@ hipError_t launch_set_cfg(const WView* ws, uint16_t* const* ys, const int64_t* l
     set.tile_end[i] = (int)nx;
   }
   const dim3 grid((unsigned)(nx * ((m + BM - 1) / BM))), block(WGN * WGM * 64);
-  if (first_b > 0)
-    hipLaunchKernelGGL((k_gemm_fwd_mix<BN, BM, WGN, WGM>), grid, block, 0, s, set, X, (int)m, tab, first_b);
-  else
-    hipLaunchKernelGGL((k_gemm_fwd_set<KIND, BN, BM, WGN, WGM>), grid, block, 0, s, set, X, (int)m, tab);
+  hipLaunchKernelGGL((k_gemm_fwd_set<KIND, BN, BM, WGN, WGM>), grid, block, 0, s, set, X, (int)m, tab);
   return hipGetLastError();
 }
 
@@ -486,18 +455,6 @@ hipError_t launch_gemm_fwd_set(WKind kind, const WView* ws, uint16_t* const* ys,
                                const Nf4Table& tab, hipStream_t s) {
   if (count < 1 || count > kGemvMaxGroup) return hipErrorInvalidValue;
   return dispatch_kind<GemmFwdSetLauncher>(kind, ws, ys, ldys, out_rows, count, X, m, tab, s);
-}
-
-hipError_t launch_gemm_fwd_mix(const WView* ws, uint16_t* const* ys, const int64_t* ldys,
-                               const int32_t* const* out_rows, int count_a, int count_b, const uint16_t* X,
-                               int64_t m, const Nf4Table& tab, hipStream_t s) {
-  const int count = count_a + count_b;
-  if (count_a < 1 || count_b < 1 || count > kGemvMaxGroup) return hipErrorInvalidValue;
-  switch (pick_tile(ws, count, m)) {
-    case 0: return launch_set_cfg<WK_I4G128, 256, 256, 4, 2>(ws, ys, ldys, out_rows, count, X, m, tab, s, count_a);
-    case 1: return launch_set_cfg<WK_I4G128, 256, 128, 4, 2>(ws, ys, ldys, out_rows, count, X, m, tab, s, count_a);
-    default: return launch_set_cfg<WK_I4G128, 128, 128, 2, 2>(ws, ys, ldys, out_rows, count, X, m, tab, s, count_a);
-  }
 }
 
 hipError_t launch_gemm_fwd(WKind kind, const WView& w, const uint16_t* X, int64_t m,

@@ -342,12 +342,11 @@ lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lb
   const lbq::LoraEpi none{nullptr, nullptr, 0, 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  if (m == 1 || m > lbq::kSkinnyMaxM) {
+  if (m == 1) {
     // The INT4 g128 and INT2 g64 row sets of channel-mixed linears (and
     // nothing else): one launch for both formats.
     lbq::WView ws[LBQ_MAX_GROUP];
     uint16_t* ys[LBQ_MAX_GROUP];
-    int64_t lds[LBQ_MAX_GROUP];
     const int32_t* rows[LBQ_MAX_GROUP];
     int ca = 0, cb = 0;
     for (int pass = 0; pass < 2; ++pass)
@@ -356,15 +355,11 @@ lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lb
           const int j = ca + cb;
           ws[j] = view_of(&descs[i], &qs[i]);
           ys[j] = Ys[i];
-          lds[j] = ldys[i];
           rows[j] = qs[i].out_rows;
           (pass == 0 ? ca : cb)++;
         }
-    if (ca > 0 && cb > 0 && ca + cb == count) {
-      e = m == 1 ? lbq::launch_gemv1_mix(ws, ys, rows, ca, cb, X, nf4_table(), s)
-                 : lbq::launch_gemm_fwd_mix(ws, ys, lds, rows, ca, cb, X, m, nf4_table(), s);
-      return hip_status(e, "lbq_linear_fwd_grouped");
-    }
+    if (ca > 0 && cb > 0 && ca + cb == count)
+      return hip_status(lbq::launch_gemv1_mix(ws, ys, rows, ca, cb, X, nf4_table(), s), "lbq_linear_fwd_grouped");
   }
   // One launch per distinct weight kind, in order of first appearance, with
   // the kernel lbq_linear_fwd picks for that kind (all weights share k).

@@ -70,10 +70,6 @@ constexpr int kGemvMaxGroup = 8;
 // count_b) (same k); outputs equal those of the two per-format launches.
 hipError_t launch_gemv1_mix(const WView* ws, uint16_t* const* ys, const int32_t* const* out_rows, int count_a,
                             int count_b, const uint16_t* X, const Nf4Table& tab, hipStream_t s);
-// m > 64, the same two row sets in one GEMM launch (see launch_gemv1_mix).
-hipError_t launch_gemm_fwd_mix(const WView* ws, uint16_t* const* ys, const int64_t* ldys,
-                               const int32_t* const* out_rows, int count_a, int count_b, const uint16_t* X,
-                               int64_t m, const Nf4Table& tab, hipStream_t s);
 hipError_t launch_gemv1(WKind kind, const WView* ws, uint16_t* const* ys, const int32_t* const* out_rows,
                         int count, const uint16_t* X, const LoraEpi& lora, const Nf4Table& tab,
                         hipStream_t s);

@@ -189,9 +189,9 @@ size_t lbq_linear_fwd_grouped_workspace_bytes(int32_t count, const lbq_desc* des
  * launch per distinct kind, in order of first appearance: a GEMV streaming all
  * of them, the small-batch kernel over all their row tiles, or a GEMM whose
  * column tiles cover all of them); the small-batch kernel adds one launch
- * that sums its K-split partials.  At m == 1 and m > 64 a set made of INT4
- * g128 and INT2 g64 weights only (the channel-mixed layer's two row sets)
- * runs as one launch for both formats.  Each Ys[i] equals what lbq_linear_fwd
+ * that sums its K-split partials.  At m == 1 a set made of INT4 g128 and
+ * INT2 g64 weights only (the channel-mixed layer's two row sets) runs as one
+ * launch for both formats.  Each Ys[i] equals what lbq_linear_fwd
  * writes for weight i alone, bit for bit.  `workspace` must hold
  * lbq_linear_fwd_grouped_workspace_bytes(count, descs, m) bytes (16-byte
  * aligned; 0 for m == 1, m > 64 and the multi-row GEMV). */

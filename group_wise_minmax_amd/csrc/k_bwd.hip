@@ -197,14 +197,43 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_
   if (BNR < N) load_stage(BNR);
   __syncthreads();
   int buf = 0;
-  for (int64_t nt = 0; nt < N; nt += BNR) {
-    if (nt + BNR < N) {
-      store_stage(buf ^ 1);
-      if (nt + 2 * BNR < N) load_stage(nt + 2 * BNR);
+  if constexpr (WGK * WGM == 8) {
+    // Two phases per stage, with a barrier between them: the first four waves
+    // stage the next tile while the last four run their MFMAs, then the other
+    // way round.  Waves w and w + 4 share a SIMD, so at any time one of them
+    // feeds the matrix core (at raised priority) while the other does the
+    // dequant and LDS writes.
+    const bool late = wave >= 4;
+    auto stage = [&](int64_t t) {
+      if (t + BNR < N) {
+        store_stage(buf ^ 1);
+        if (t + 2 * BNR < N) load_stage(t + 2 * BNR);
+      }
+    };
+    auto mfma_phase = [&]() {
+      __builtin_amdgcn_s_setprio(1);
+      compute(buf);
+      __builtin_amdgcn_s_setprio(0);
+    };
+    for (int64_t nt = 0; nt < N; nt += BNR) {
+      if (late) mfma_phase();
+      else stage(nt);
+      __syncthreads();
+      if (late) stage(nt);
+      else mfma_phase();
+      __syncthreads();
+      buf ^= 1;
     }
-    compute(buf);
-    __syncthreads();
-    buf ^= 1;
+  } else {
+    for (int64_t nt = 0; nt < N; nt += BNR) {
+      if (nt + BNR < N) {
+        store_stage(buf ^ 1);
+        if (nt + 2 * BNR < N) load_stage(nt + 2 * BNR);
+      }
+      compute(buf);
+      __syncthreads();
+      buf ^= 1;
+    }
   }
 
   // LoRA slab: acc[k][m] += sum over j of A[j][k] * G[m][j], r zero-padded to rp.

@@ -231,14 +231,43 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
   if (BK < K) load_stage(BK);
   __syncthreads();
   int buf = 0;
-  for (int64_t kt = 0; kt < K; kt += BK) {
-    if (kt + BK < K) {
-      store_stage(buf ^ 1);
-      if (kt + 2 * BK < K) load_stage(kt + 2 * BK);
+  if constexpr (WGN * WGM == 8) {
+    // Two phases per stage, with a barrier between them: the first four waves
+    // stage the next tile while the last four run their MFMAs, then the other
+    // way round.  Waves w and w + 4 share a SIMD, so at any time one of them
+    // feeds the matrix core (at raised priority) while the other does the
+    // dequant and LDS writes.
+    const bool late = wave >= 4;
+    auto stage = [&](int64_t t) {
+      if (t + BK < K) {
+        store_stage(buf ^ 1);
+        if (t + 2 * BK < K) load_stage(t + 2 * BK);
+      }
+    };
+    auto mfma_phase = [&]() {
+      __builtin_amdgcn_s_setprio(1);
+      compute(buf);
+      __builtin_amdgcn_s_setprio(0);
+    };
+    for (int64_t kt = 0; kt < K; kt += BK) {
+      if (late) mfma_phase();
+      else stage(kt);
+      __syncthreads();
+      if (late) stage(kt);
+      else mfma_phase();
+      __syncthreads();
+      buf ^= 1;
     }
-    compute(buf);
-    __syncthreads();
-    buf ^= 1;
+  } else {
+    for (int64_t kt = 0; kt < K; kt += BK) {
+      if (kt + BK < K) {
+        store_stage(buf ^ 1);
+        if (kt + 2 * BK < K) load_stage(kt + 2 * BK);
+      }
+      compute(buf);
+      __syncthreads();
+      buf ^= 1;
+    }
   }
 
   // LoRA slab: acc += B_lora[n][:] . T[m][:], r zero-padded to rp (multiple of 32).

@@ -231,12 +231,14 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
   if (BK < K) load_stage(BK);
   __syncthreads();
   int buf = 0;
-  if constexpr (WGN * WGM == 8) {
+  if constexpr (WGN * WGM == 8 && BM == 256) {
     // Two phases per stage, with a barrier between them: the first four waves
     // stage the next tile while the last four run their MFMAs, then the other
     // way round.  Waves w and w + 4 share a SIMD, so at any time one of them
     // feeds the matrix core (at raised priority) while the other does the
-    // dequant and LDS writes.
+    // dequant and LDS writes.  (With 128-row X tiles a wave's MFMA phase is
+    // no longer than its staging, and the extra barrier costs more than the
+    // overlap gains.)
     const bool late = wave >= 4;
     auto stage = [&](int64_t t) {
       if (t + BK < K) {

@@ -262,6 +262,33 @@ def test_bwd_dx_tolerance(L, fmtspec, nk, m):
     assert_close(bf16_bits_host(dX), O.linear_bwd_dx(dY, ref["w_exact"]), what=f"bwd {fmt} m={m}")
 
 
+# The 256x256 tiles (picked for m = 4096 and 4096 output columns) run their
+# K loop in two phases; few K-steps exercise its first and last stages.
+@pytest.mark.parametrize("fid,kk", [("nf4dq", 64), ("nf4dq", 192), ("i4g128", 128), ("i4g128", 384),
+                                    ("i2g64", 64)])
+def test_gemm_large_tiles_few_k_steps(L, fid, kk):
+    """Forward Y = X . W^T with k = kk and input gradient dX = dY . W with
+    n = kk (the reduction of each runs over one to six 64-wide steps), both
+    with 4096 x 4096 outputs; 64 sampled rows against the oracle."""
+    fmt, bits, group, dq = FORMATS[FMT_IDS.index(fid)]
+    m = 4096
+    rows = np.sort(np.random.default_rng(9950 + kk).choice(m, 64, replace=False))
+    # forward: W [4096][kk]
+    W = SI.gaussian_weights(9951 + kk, 4096, kk, outlier_seed=9952)
+    X = SI.bf16_normal(9953 + kk, (m, kk))
+    qw, ref = _quant_pair(L, W, fmt, bits, group, dq)
+    Y = L.lbq_linear_fwd(to_dev_bf16(X), qw)
+    torch.cuda.synchronize()
+    assert_close(bf16_bits_host(Y)[rows], O.linear_fwd(X[rows], ref["w_exact"]), what=f"fwd {fid} k={kk}")
+    # input gradient: W [kk][4096]
+    W2 = SI.gaussian_weights(9954 + kk, kk, 4096, outlier_seed=9955)
+    dY = SI.bf16_normal(9956 + kk, (m, kk))
+    qw2, ref2 = _quant_pair(L, W2, fmt, bits, group, dq)
+    dX = L.lbq_linear_bwd_dx(to_dev_bf16(dY), qw2)
+    torch.cuda.synchronize()
+    assert_close(bf16_bits_host(dX)[rows], O.linear_bwd_dx(dY[rows], ref2["w_exact"]), what=f"bwd {fid} n={kk}")
+
+
 @pytest.mark.parametrize("bits,group", [(4, 128), (2, 64)])
 @pytest.mark.parametrize("m", [3, 130])
 def test_bwd_dx_exact_on_grid(L, bits, group, m):

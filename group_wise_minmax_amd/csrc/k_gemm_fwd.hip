@@ -467,15 +467,59 @@ struct GemmFwdLauncher {
   }
 };
 
+// Time of one launch over weights ws[0..count), in 256x256-tile units at full
+// efficiency: the work divided by the best (chip fill x per-tile factor).
+double launch_cost(const WView* ws, int count, int64_t m) {
+  int64_t t0 = 0, t1 = 0, t2 = 0;
+  double work = 0.0;
+  for (int i = 0; i < count; ++i) {
+    t0 += ((ws[i].n + 255) / 256) * ((m + 255) / 256);
+    t1 += ((ws[i].n + 255) / 256) * ((m + 127) / 128);
+    t2 += ((ws[i].n + 127) / 128) * ((m + 127) / 128);
+    work += (double)ws[i].n * (double)m / 65536.0;
+  }
+  const double e = fmax(fill(t0) * 1.00, fmax(fill(t1) * 0.78, fill(t2) * 0.74));
+  return work / e;
+}
+
+// A set whose last round of tiles is partly empty under every tile shape can
+// run faster as two launches, a prefix of the weights and the rest, each with
+// its own tile shape: q (4096 rows) at m = 4096 fills one round of 256x256
+// tiles exactly, and k + v (2048 rows) one round of 256x128 tiles.  Returns
+// the prefix length, or 0 for one launch; a split must save over 5% (it pays
+// a second launch).
+int split_point(const WView* ws, int count, int64_t m) {
+  int best = 0;
+  double best_cost = 0.95 * launch_cost(ws, count, m);
+  for (int j = 1; j < count; ++j) {
+    const double c = launch_cost(ws, j, m) + launch_cost(ws + j, count - j, m);
+    if (c < best_cost) {
+      best = j;
+      best_cost = c;
+    }
+  }
+  return best;
+}
+
+template <int KIND>
+hipError_t launch_set_tiles(const WView* ws, uint16_t* const* ys, const int64_t* ldys, const int32_t* const* orows,
+                            int count, const uint16_t* X, int64_t m, const Nf4Table& tab, hipStream_t s) {
+  switch (pick_tile(ws, count, m)) {
+    case 0: return launch_set_cfg<KIND, 256, 256, 4, 2>(ws, ys, ldys, orows, count, X, m, tab, s);
+    case 1: return launch_set_cfg<KIND, 256, 128, 4, 2>(ws, ys, ldys, orows, count, X, m, tab, s);
+    default: return launch_set_cfg<KIND, 128, 128, 2, 2>(ws, ys, ldys, orows, count, X, m, tab, s);
+  }
+}
+
 template <int KIND>
 struct GemmFwdSetLauncher {
   static hipError_t run(const WView* ws, uint16_t* const* ys, const int64_t* ldys, const int32_t* const* orows,
                         int count, const uint16_t* X, int64_t m, const Nf4Table& tab, hipStream_t s) {
-    switch (pick_tile(ws, count, m)) {
-      case 0: return launch_set_cfg<KIND, 256, 256, 4, 2>(ws, ys, ldys, orows, count, X, m, tab, s);
-      case 1: return launch_set_cfg<KIND, 256, 128, 4, 2>(ws, ys, ldys, orows, count, X, m, tab, s);
-      default: return launch_set_cfg<KIND, 128, 128, 2, 2>(ws, ys, ldys, orows, count, X, m, tab, s);
-    }
+    const int j = split_point(ws, count, m);
+    if (j == 0) return launch_set_tiles<KIND>(ws, ys, ldys, orows, count, X, m, tab, s);
+    const hipError_t e = launch_set_tiles<KIND>(ws, ys, ldys, orows, j, X, m, tab, s);
+    if (e != hipSuccess) return e;
+    return launch_set_tiles<KIND>(ws + j, ys + j, ldys + j, orows + j, count - j, X, m, tab, s);
   }
 };
 

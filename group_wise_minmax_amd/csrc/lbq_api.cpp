@@ -295,8 +295,9 @@ lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint
 }
 
 // Weights of one kind in a grouped call run as one launch (one launch pair
-// for the small-batch kernel when it splits K), one kind after another on the
-// stream; the workspace holds the partials of the largest kind group.
+// for the small-batch kernel when it splits K, and up to two GEMM launches
+// when splitting the set fills the chip better), one kind after another on
+// the stream; the workspace holds the partials of the largest kind group.
 size_t lbq_linear_fwd_grouped_workspace_bytes(int32_t count, const lbq_desc* descs, int64_t m) {
   if (count < 1 || count > LBQ_MAX_GROUP || descs == nullptr) return 0;
   for (int32_t i = 0; i < count; ++i)

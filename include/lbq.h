@@ -189,7 +189,10 @@ size_t lbq_linear_fwd_grouped_workspace_bytes(int32_t count, const lbq_desc* des
  * launch per distinct kind, in order of first appearance: a GEMV streaming all
  * of them, the small-batch kernel over all their row tiles, or a GEMM whose
  * column tiles cover all of them); the small-batch kernel adds one launch
- * that sums its K-split partials.  At m == 1 a set made of INT4 g128 and
+ * that sums its K-split partials.  For m > 64 a kind's GEMM may instead run
+ * as two launches, a prefix of its weights and the rest, each with its own
+ * tile shape, when that fills the chip's rounds of tiles better (q with
+ * 256x256 tiles and k+v with 256x128 at m = 4096).  At m == 1 a set made of INT4 g128 and
  * INT2 g64 weights only (the channel-mixed layer's two row sets) runs as one
  * launch for both formats.  Each Ys[i] equals what lbq_linear_fwd
  * writes for weight i alone, bit for bit.  `workspace` must hold

@@ -526,6 +526,31 @@ def test_grouped_fwd_matches_single(L, name, k, m):
         assert_close(bf16_bits_host(Y), O.linear_fwd(X, ref["w_exact"]), what=f"{name} weight {i} m={m}")
 
 
+@pytest.mark.parametrize("fid", ["i4g128", "nf4dq", "i2g64"])
+def test_grouped_gemm_two_launch_split(L, fid):
+    """A q/k/v-like set at ragged m = 4000 whose GEMM runs as two launches:
+    the 4000-row weight alone fills one round of 256x256 tiles (256 tiles),
+    the two 1000-row weights one round of 256x128 tiles.  Each output equals
+    the single-weight forward bit for bit, and 48 sampled rows match the
+    oracle."""
+    fmt, bits, group, dq = FORMATS[FMT_IDS.index(fid)]
+    m, k = 4000, 256
+    rows = np.sort(np.random.default_rng(9460).choice(m, 48, replace=False))
+    X = SI.bf16_normal(9461, (m, k))
+    qws, refs = [], []
+    for i, n in enumerate((4000, 1000, 1000)):
+        qw, ref = _quant_pair(L, SI.gaussian_weights(9462 + i, n, k, outlier_seed=9465 + i), fmt, bits, group, dq)
+        qws.append(qw)
+        refs.append(ref)
+    Xd = to_dev_bf16(X)
+    Ys = L.lbq_linear_fwd_grouped(Xd, qws)
+    singles = [L.lbq_linear_fwd(Xd, q) for q in qws]
+    torch.cuda.synchronize()
+    for i, (Y, Y1, ref) in enumerate(zip(Ys, singles, refs)):
+        assert np.array_equal(bf16_bits_host(Y), bf16_bits_host(Y1)), f"{fid} weight {i}: grouped != single"
+        assert_close(bf16_bits_host(Y)[rows], O.linear_fwd(X[rows], ref["w_exact"]), what=f"{fid} weight {i}")
+
+
 def test_grouped_fwd_exact_on_grid(L):
     """Three grid weights in one m = 1 launch: exact integer arithmetic, so
     every output is bf16(X W_i^T) bit for bit."""

@@ -17,9 +17,12 @@ namespace {
 // 8 contiguous bytes of a dX row.
 //
 // The packed weight is contiguous along k, the reduction runs along n: per
-// stage a thread loads 8 codes (one k-chunk) of 4 consecutive rows n,
-// dequantizes them and writes, for each of its 8 k, the 4 values of the rows
-// as one 8-byte LDS store into the k-major tile.  The n-quad is the lane's low
+// stage a thread dequantizes 8 codes (one k-chunk) of 4 consecutive rows n
+// and writes, for each of its 8 k, the 4 values of the rows as one 8-byte LDS
+// store into the k-major tile.  It loads them row-wise, though: 32 codes of
+// one row (one 16- or 8-byte load, with that row's metadata), and four
+// permlane swaps transpose the 4 x 4 dwords across the lanes that share the
+// n-quad, so a stage costs 3 weight loads per thread instead of 12.  The n-quad is the lane's low
 // 4 bits, which (with the row swizzle) keeps these column writes
 // bank-conflict free.  dY chunks are staged like X in the forward GEMM.  Both
 // tiles are double-buffered with one barrier per stage, and every global load
@@ -27,6 +30,40 @@ namespace {
 // past n, m or k need no guards.
 // ---------------------------------------------------------------------------
 constexpr int BNR = 64;  // reduction (n) per stage = one 128-byte LDS row
+
+// Lane rows are the four groups of 16 lanes.  gfx950's permlane swaps:
+// swap32(a, b) exchanges lanes 32..63 of a with lanes 0..31 of b, swap16(a, b)
+// the odd lane rows of a with the even lane rows of b.
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+// 4 x 4 transpose over the lane rows: afterwards x_r in lane row j holds what
+// x_j held in lane row r (same lane within the row).
+__device__ __forceinline__ void transpose_rows4(uint32_t& x0, uint32_t& x1, uint32_t& x2, uint32_t& x3) {
+  swap32(x0, x2);
+  swap32(x1, x3);
+  swap16(x0, x1);
+  swap16(x2, x3);
+}
+// out[r] = v of lane row r (same lane within the row), in every lane row.
+__device__ __forceinline__ void gather_rows4(float v, float out[4]) {
+  uint32_t a = __float_as_uint(v), b = a;
+  swap32(a, b);  // a: v0 v1 v0 v1, b: v2 v3 v2 v3 (by lane row)
+  uint32_t a2 = a, b2 = b;
+  swap16(a, a2);  // a: v0 everywhere, a2: v1
+  swap16(b, b2);  // b: v2, b2: v3
+  out[0] = __uint_as_float(a);
+  out[1] = __uint_as_float(a2);
+  out[2] = __uint_as_float(b);
+  out[3] = __uint_as_float(b2);
+}
 
 template <int KIND, int BKO, int BM, int WGK, int WGM, bool LORA>
 __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_t* __restrict__ dY,
@@ -83,11 +120,14 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_
   }
 
   // Weight ownership: rows 4*q .. 4*q+3 of each stage, codes [8*c, +8) of the
-  // k tile, with q = lane & 15 and c = (NT/64 waves) x 4 chunks.
+  // k tile, with q = lane & 15 and c = (NT/64 waves) x 4 chunks.  The loads
+  // are row-wise: lane (q, lg) reads the 32 codes [32*wave, +32) of row
+  // 4*q + lg and that row's metadata, and a transpose over the lane rows
+  // (lanes q, q+16, q+32, q+48) hands each lane its chunk lg of the 4 rows.
   const int q = lane & 15, c = 4 * wave + lg;
-  const int64_t kc = k0 + 8 * c;
-  const uint32_t w_voff = (uint32_t)(4 * q * KB + kc * T::bits / 8);
-  const uint32_t g_voff = (uint32_t)(4 * q * gpr + kc / T::group);
+  const int64_t kp = k0 + 32 * wave;
+  const uint32_t w_voff = (uint32_t)((4 * q + lg) * KB + kp * T::bits / 8);
+  const uint32_t g_voff = (uint32_t)((4 * q + lg) * gpr + kp / T::group);
   // dY chunks of this thread: chunk ci = tid + NT*i -> row ci >> 3, chunk ci & 7.
   const uint32_t d_voff = (uint32_t)(((m0 + (tid >> 3)) * N + 8 * (tid & 7)) * 2);
   char* const wt_base = reinterpret_cast<char*>(&Wt[0][0]);
@@ -101,9 +141,9 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_
     for (int b = 0; b < TM; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   u32x4_t dr[DCH];
-  uint32_t wr[4];
-  float md_s[4];
-  int md_i[4];
+  u32x4_t wraw;  // 32 codes of row 4q + lg (2-bit: dwords 0 and 1)
+  float md_s;
+  int md_i;
   auto load_stage = [&](int64_t nt) {
 #pragma unroll
     for (int i = 0; i < DCH; ++i) {
@@ -111,25 +151,23 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_
       const int so = (int)((NT / 8) * i * N * 2 + nt * 2);
       dr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_d, d_voff, so, 0));
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int so = (int)((nt + r) * KB);
-      if constexpr (T::bits == 4) {
-        wr[r] = __builtin_amdgcn_raw_buffer_load_b32(r_w, w_voff, so, 0);
-      } else {
-        wr[r] = __builtin_amdgcn_raw_buffer_load_b16(r_w, w_voff, so, 0);
-      }
-      const int go = (int)((nt + r) * gpr);
-      if constexpr (T::fmt == FMT_MINMAX) {
-        md_s[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, g_voff * 4, go * 4, 0));
-        md_i[r] = __builtin_amdgcn_raw_buffer_load_b8(r_z, g_voff, go, 0);
-      } else if constexpr (T::dq) {
-        md_i[r] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(r_z, g_voff, go, 0);
-        md_s[r] = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(r_s, ((g_voff + (uint32_t)go) >> 8) * 4, 0, 0));
-      } else {
-        md_s[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, g_voff * 4, go * 4, 0));
-      }
+    const int so = (int)(nt * KB);
+    if constexpr (T::bits == 4) {
+      wraw = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_w, w_voff, so, 0));
+    } else {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(r_w, w_voff, so, 0);
+      wraw = u32x4_t{v[0], v[1], 0u, 0u};
+    }
+    const int go = (int)(nt * gpr);
+    if constexpr (T::fmt == FMT_MINMAX) {
+      md_s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, g_voff * 4, go * 4, 0));
+      md_i = __builtin_amdgcn_raw_buffer_load_b8(r_z, g_voff, go, 0);
+    } else if constexpr (T::dq) {
+      md_i = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(r_z, g_voff, go, 0);
+      md_s = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(r_s, ((g_voff + (uint32_t)go) >> 8) * 4, 0, 0));
+    } else {
+      md_s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, g_voff * 4, go * 4, 0));
     }
   };
   auto store_stage = [&](int buf) {
@@ -139,16 +177,32 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_
       const int ci = tid + NT * i;
       *reinterpret_cast<u32x4_t*>(ds + swz(ci >> 3, ci & 7)) = dr[i];
     }
+    // wr[r]: chunk lg (8 codes) of row 4q + r
+    uint32_t wr[4];
+    if constexpr (T::bits == 4) {
+      wr[0] = wraw[0], wr[1] = wraw[1], wr[2] = wraw[2], wr[3] = wraw[3];
+    } else {
+      wr[0] = wraw[0] & 0xFFFFu, wr[1] = wraw[0] >> 16, wr[2] = wraw[1] & 0xFFFFu, wr[3] = wraw[1] >> 16;
+    }
+    transpose_rows4(wr[0], wr[1], wr[2], wr[3]);
+    // scale (MinMax: and z*s; NF4: the block absmax) of row 4q + r
+    float sc[4], zc[4];
+    if constexpr (T::fmt == FMT_MINMAX) {
+      gather_rows4(md_s, sc);
+      gather_rows4((float)md_i * md_s, zc);
+    } else {
+      gather_rows4(T::dq ? (float)md_i * md_s : md_s, sc);
+    }
     // v[r][j]: row 4q + r, code j of the chunk
     float v[4][8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if constexpr (T::fmt == FMT_MINMAX) {
-        const float s = md_s[r], zs = (float)md_i[r] * md_s[r];
+        const float s = sc[r], zs = zc[r];
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[r][j] = fmaf((float)code_of<T::bits>(wr[r], j), s, -zs);
       } else {
-        const float a = T::dq ? (float)md_i[r] * md_s[r] : md_s[r];
+        const float a = sc[r];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const f32x2_t cc = pairlut[(wr[r] >> (8 * j)) & 0xFFu];

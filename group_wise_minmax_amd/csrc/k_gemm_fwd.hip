@@ -146,6 +146,19 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
   u32x4_t wr[NQ];
   float md_s = 0.f;  // scale (MinMax), absmax or second-level scale (NF4)
   int md_i = 0;      // zero point (MinMax) or int8 absmax code (NF4 + DQ)
+  // When every row's metadata starts 16-byte aligned (groups per row a
+  // multiple of 4, aligned arrays), the entries of 4 consecutive groups are
+  // loaded together once per 4 groups: one 16-byte load of scales or absmax
+  // and one 4-byte load of zero points or absmax codes, instead of two small
+  // loads per stage.  The stage picks its entry in store_stage.
+  const float* const mf_arr = T::fmt == FMT_MINMAX ? w.scales : (T::dq ? nullptr : w.absmax);
+  const uint8_t* const mb_arr =
+      T::fmt == FMT_MINMAX ? w.zeros : (T::dq ? reinterpret_cast<const uint8_t*>(w.absmax_q) : nullptr);
+  const bool md4 = (gpr & 3) == 0 && (reinterpret_cast<uintptr_t>(mf_arr) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(mb_arr) & 3) == 0;
+  float mb0 = 0.f, mb1 = 0.f, mb2 = 0.f, mb3 = 0.f;  // scales / absmax of the batch
+  uint32_t mb_b = 0;                                 // zero points / absmax codes of the batch
+  int md_j = 0;  // entry of the loaded stage in the batch (the same in every lane)
   auto load_stage = [&](int64_t kt) {
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
@@ -165,14 +178,24 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
       }
     }
     const int64_t gi = grow + kk / T::group;
-    if constexpr (T::fmt == FMT_MINMAX) {
-      md_s = w.scales[gi];
-      md_i = w.zeros[gi];
-    } else if constexpr (T::dq) {
-      md_i = w.absmax_q[gi];
-      md_s = w.absmax_scale[gi >> 8];
-    } else {
-      md_s = w.absmax[gi];
+    // Both forms fill the batch registers (the per-stage form as entry 0), so
+    // the same variables are written either way.
+    md_j = md4 ? (int)((kt / T::group) & 3) : 0;  // rows start at multiples of 4 entries
+    if (md_j == 0 && kt % T::group == 0) {       // first stage of a batch or group (uniform)
+      if (md4) {
+        if constexpr (T::fmt != FMT_NF4 || !T::dq) {
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(mf_arr + gi);
+          mb0 = v[0], mb1 = v[1], mb2 = v[2], mb3 = v[3];
+        }
+        if constexpr (T::fmt == FMT_MINMAX || T::dq) mb_b = *reinterpret_cast<const uint32_t*>(mb_arr + gi);
+      } else {
+        if constexpr (T::fmt != FMT_NF4 || !T::dq) {
+          const float v = mf_arr[gi];
+          mb0 = v, mb1 = v, mb2 = v, mb3 = v;
+        }
+        if constexpr (T::fmt == FMT_MINMAX || T::dq) mb_b = mb_arr[gi];
+      }
+      if constexpr (T::dq) md_s = w.absmax_scale[gi >> 8];  // one second-level block per batch
     }
   };
   auto store_stage = [&](int buf) {
@@ -180,6 +203,12 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
     for (int i = 0; i < XCH; ++i) {
       const int c = tid + NT * i;
       *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(&Xs[buf][0]) + swz(c >> 3, c & 7)) = xr[i];
+    }
+    {
+      const float f01 = (md_j & 1) ? mb1 : mb0, f23 = (md_j & 1) ? mb3 : mb2;
+      if constexpr (!T::dq) md_s = (md_j & 2) ? f23 : f01;
+      if constexpr (T::fmt == FMT_MINMAX) md_i = (int)((mb_b >> (8 * md_j)) & 0xFFu);
+      if constexpr (T::dq) md_i = (int)(int8_t)(uint8_t)((mb_b >> (8 * md_j)) & 0xFFu);
     }
     float ws_s, ws_zs = 0.f;
     if constexpr (T::fmt == FMT_MINMAX) {

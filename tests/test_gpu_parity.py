@@ -551,6 +551,38 @@ def test_grouped_gemm_two_launch_split(L, fid):
         assert_close(bf16_bits_host(Y)[rows], O.linear_fwd(X[rows], ref["w_exact"]), what=f"{fid} weight {i}")
 
 
+@pytest.mark.parametrize("fid", ["i4g64", "i4g128", "i2g64", "nf4", "nf4dq"])
+def test_metadata_at_minimum_alignment(L, fid):
+    """Metadata arrays that start one element past an aligned address (floats
+    4-byte aligned, zero points and absmax codes 1-byte aligned, the least
+    the API allows): the forward GEMM then loads one group's entries per stage
+    instead of four groups' together.  Forward at m = 1, 16 and 300 and the
+    input gradient equal those of the aligned weight bit for bit."""
+    import dataclasses
+    fmt, bits, group, dq = FORMATS[FMT_IDS.index(fid)]
+    n, k = 520, 2048
+    qw, _ = _quant_pair(L, SI.gaussian_weights(9480, n, k, outlier_seed=9481), fmt, bits, group, dq)
+
+    def shifted(t):
+        if t is None:
+            return None
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        buf[1:].copy_(t.reshape(-1))
+        return buf[1:].view(t.shape)
+
+    qs = dataclasses.replace(qw, scales=shifted(qw.scales), zeros=shifted(qw.zeros),
+                             absmax=shifted(qw.absmax), absmax_q=shifted(qw.absmax_q))
+    for m in (1, 16, 300):
+        X = to_dev_bf16(SI.bf16_normal(9482 + m, (m, k)))
+        Y0, Y1 = L.lbq_linear_fwd(X, qw), L.lbq_linear_fwd(X, qs)
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits_host(Y0), bf16_bits_host(Y1)), f"{fid} fwd m={m}"
+    dY = to_dev_bf16(SI.bf16_normal(9483, (300, n)))
+    dX0, dX1 = L.lbq_linear_bwd_dx(dY, qw), L.lbq_linear_bwd_dx(dY, qs)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits_host(dX0), bf16_bits_host(dX1)), f"{fid} bwd"
+
+
 def test_grouped_fwd_exact_on_grid(L):
     """Three grid weights in one m = 1 launch: exact integer arithmetic, so
     every output is bf16(X W_i^T) bit for bit."""

@@ -20,7 +20,8 @@ this order:
   quant_int4   quantize + pack the 7 fp32 weights, MinMax INT4 g128
   quant_nf4dq  quantize + pack the 7 weights, NF4 block 64 + double quant
   dequant      dequantize the 7 NF4-DQ weights to bf16
-  gemm_m2048   INT4 g128 forward at m = 2048
+  gemm_m2048   INT4 g128 forward at m = 2048, launched like fwd_m4096 (grouped
+               calls for q/k/v and gate/up)
   fwd_m4096    NF4-DQ forward at m = 4096 (2 x 2048 tokens)       <- headline;
                q/k/v and gate/up share X and run as one grouped call each
                (their column tiles side by side; q/k/v as two launches, q
@@ -30,8 +31,8 @@ this order:
   bwd_m4096    NF4-DQ input gradient dX = dY deq(W) at m = 4096
   lora_bwd_m4096  NF4-DQ LoRA backward (dX with the adapter term, dA, dB),
                rank 16 on q and v, at m = 4096
-  chmix_70b_m1024  the 70B-shaped channel-mix layer at m = 1024, one call (one
-                   launch) per format and linear
+  chmix_70b_m1024  the 70B-shaped channel-mix layer at m = 1024, grouped like
+                   chmix_70b_m1 (one GEMM launch per format and call: 8 per layer)
   copy_1g      (only with --phases) a plain 1 GiB device-to-device copy, the
                reference kernel for scaling hardware byte counters
 
@@ -251,6 +252,15 @@ def build_workload(L, SI, torch, dev, R, want):
                 L.lbq_linear_fwd(X[nm], qs[nm], out=Y[nm])
         return f
 
+    def p_gemm_grouped(qs, X, Y):
+        def f():
+            for g in GROUPS:
+                if len(g) == 1:
+                    L.lbq_linear_fwd(X[g[0]], qs[g[0]], out=Y[g[0]])
+                else:
+                    L.lbq_linear_fwd_grouped(X[g[0]], [qs[nm] for nm in g], outs=[Y[nm] for nm in g])
+        return f
+
     def gemm_group_units(qs, X, Y):
         def unit(g):
             if len(g) == 1:
@@ -284,9 +294,14 @@ def build_workload(L, SI, torch, dev, R, want):
             L.lbq_linear_fwd_grouped(x1, qs, outs=ys)
 
     def p_chmix_m1024():
-        for nm, a, b, x1, x1k, y1, y1k in cm:
-            L.lbq_linear_fwd(x1k, a, out=y1k)
-            L.lbq_linear_fwd(x1k, b, out=y1k)
+        # as at m = 1: per activation group, both row sets of every linear in
+        # one call (one GEMM launch per format)
+        by = {e[0]: e for e in cm}
+        for g in GROUPS:
+            x = by[g[0]][4]
+            qs = [q for nm in g for q in by[nm][1:3]]
+            ys = [by[nm][6] for nm in g for _ in range(2)]
+            L.lbq_linear_fwd_grouped(x, qs, outs=ys)
 
     def p_copy():
         cp_dst.copy_(cp_src)
@@ -309,7 +324,7 @@ def build_workload(L, SI, torch, dev, R, want):
         ("quant_int4", p_quant_int4, lambda: {"bound": "hbm", "bytes": quant_bytes(q4), "launches": 7}),
         ("quant_nf4dq", p_quant_nf4dq, lambda: {"bound": "hbm", "bytes": quant_bytes(qn), "launches": 7}),
         ("dequant", p_dequant, lambda: {"bound": "hbm", "bytes": sum(qn[nm].nbytes() + 2 * N_of[nm] * K_of[nm] for nm in names), "launches": 7}),
-        ("gemm_m2048", p_gemm(q4, X2k, Y2k), lambda: {"bound": "mfma", "flop": flop(2048), "launches": 7}),
+        ("gemm_m2048", p_gemm_grouped(q4, X2k, Y2k), lambda: {"bound": "mfma", "flop": flop(2048), "launches": len(GROUPS)}),
         ("fwd_m4096", None, lambda: {"bound": "mfma", "flop": flop(4096), "launches": len(GROUPS) + 1,
                                      "units": gemm_group_units(qn, X4k, Y4k),
                                      "unit_flop": {"+".join(g): sum(2 * 4096 * N_of[nm] * K_of[nm] for nm in g) for g in GROUPS},
@@ -323,7 +338,7 @@ def build_workload(L, SI, torch, dev, R, want):
         ("bwd_m4096", p_bwd, lambda: {"bound": "mfma", "flop": flop(4096), "launches": 7}),
         # dX = dY W + G A, G = dY B, T = X A^T, dA = G^T X, dB = (T^T dY)^T
         ("lora_bwd_m4096", p_lora_bwd, lambda: {"bound": "mfma", "flop": sum(2 * 4096 * N_of[nm] * K_of[nm] + 2 * 4096 * 16 * (2 * N_of[nm] + 3 * K_of[nm]) for nm in lora_bwd), "launches": 14}),
-        ("chmix_70b_m1024", p_chmix_m1024, lambda: {"bound": "mfma", "flop": sum(2 * 1024 * (a.n + b.n) * a.k for _, a, b, *_ in cm), "launches": 14}),
+        ("chmix_70b_m1024", p_chmix_m1024, lambda: {"bound": "mfma", "flop": sum(2 * 1024 * (a.n + b.n) * a.k for _, a, b, *_ in cm), "launches": 2 * len(GROUPS)}),
         ("copy_1g", p_copy, lambda: {"bound": "hbm", "bytes": 2 << 30, "launches": 1}),
     ]
     # Decode phases (HBM-bound reads) run first in each step, after the

@@ -28,7 +28,11 @@ this order:
                with 256x256 tiles and k+v with 256x128), o and down alone
   fwd_m4096_per_linear  the same with one launch per linear
   lora_m4096   NF4-DQ forward + rank-16 LoRA on q and v at m = 4096
-  bwd_m4096    NF4-DQ input gradient dX = dY deq(W) at m = 4096
+  bwd_m4096    NF4-DQ input gradient dX = dY deq(W) at m = 4096, one call per
+               linear
+  bwd_m4096_grouped  the layer's input gradients: q/k/v and gate/up each summed
+               into their shared input's gradient in one grouped call
+               (lbq_linear_bwd_dx_grouped), o and down alone
   lora_bwd_m4096  NF4-DQ LoRA backward (dX with the adapter term, dA, dB),
                rank 16 on q and v, at m = 4096
   chmix_70b_m1024  the 70B-shaped channel-mix layer at m = 1024, grouped like
@@ -87,7 +91,8 @@ def load_traffic(kernel: str, units_per_launch=None):
 
 
 ALL_PHASES = ("quant_int4", "quant_nf4dq", "dequant", "gemv_m1", "gemv_m1_per_linear", "gemv_m4", "gemv_m16", "gemm_m2048",
-              "fwd_m4096", "fwd_m4096_per_linear", "lora_m4096", "bwd_m4096", "lora_bwd_m4096", "chmix_70b_m1",
+              "fwd_m4096", "fwd_m4096_per_linear", "lora_m4096", "bwd_m4096", "bwd_m4096_grouped", "lora_bwd_m4096",
+              "chmix_70b_m1",
               "chmix_70b_m1024")
 EXTRA_PHASES = ("copy_1g",)  # opt-in: plain 1 GiB device copy (counter calibration)
 
@@ -172,8 +177,8 @@ def build_workload(L, SI, torch, dev, R, want):
     X2k, Y2k = xs(2, SI.SLOT_X, 200, 2048, K_of, need("gemm_m2048")), ys(2048, N_of, need("gemm_m2048"))
     X4k = xs(3, SI.SLOT_X, 0, 4096, K_of, need("fwd_m4096", "fwd_m4096_per_linear", "lora_m4096", "lora_bwd_m4096"))
     Y4k = ys(4096, N_of, need("fwd_m4096", "fwd_m4096_per_linear"))
-    dY = xs(3, SI.SLOT_DY, 0, 4096, N_of, need("bwd_m4096", "lora_bwd_m4096"))
-    dX = ys(4096, K_of, need("bwd_m4096", "lora_bwd_m4096"))
+    dY = xs(3, SI.SLOT_DY, 0, 4096, N_of, need("bwd_m4096", "bwd_m4096_grouped", "lora_bwd_m4096"))
+    dX = ys(4096, K_of, need("bwd_m4096", "bwd_m4096_grouped", "lora_bwd_m4096"))
     lora = {}
     if need("lora_m4096", "lora_bwd_m4096"):
         for nm in ("q", "v"):
@@ -279,6 +284,15 @@ def build_workload(L, SI, torch, dev, R, want):
         for nm in names:
             L.lbq_linear_bwd_dx(dY[nm], qn[nm], out=dX[nm])
 
+    def p_bwd_grouped():
+        # the layer's input gradients: the linears that read one X (q/k/v,
+        # gate/up) summed into that X's gradient in one grouped call
+        for g in GROUPS:
+            if len(g) == 1:
+                L.lbq_linear_bwd_dx(dY[g[0]], qn[g[0]], out=dX[g[0]])
+            else:
+                L.lbq_linear_bwd_dx_grouped([dY[nm] for nm in g], [qn[nm] for nm in g], out=dX[g[0]])
+
     def p_lora_bwd():
         for nm, (A, B, ws, dA, dB) in lora_bwd.items():
             L.lbq_lora_bwd(X4k[nm], dY[nm], qn[nm], A, B, 1.0, dX=dX[nm], dA=dA, dB=dB, workspace=ws)
@@ -336,6 +350,7 @@ def build_workload(L, SI, torch, dev, R, want):
                                                 "unit_flop": {nm: 2 * 4096 * n * k for nm, (n, k) in shapes.items()}}),
         ("lora_m4096", p_lora, lambda: {"bound": "mfma", "flop": sum(2 * 4096 * N_of[nm] * K_of[nm] + 2 * 4096 * 16 * (K_of[nm] + N_of[nm]) for nm in lora), "launches": 4}),
         ("bwd_m4096", p_bwd, lambda: {"bound": "mfma", "flop": flop(4096), "launches": 7}),
+        ("bwd_m4096_grouped", p_bwd_grouped, lambda: {"bound": "mfma", "flop": flop(4096), "launches": len(GROUPS)}),
         # dX = dY W + G A, G = dY B, T = X A^T, dA = G^T X, dB = (T^T dY)^T
         ("lora_bwd_m4096", p_lora_bwd, lambda: {"bound": "mfma", "flop": sum(2 * 4096 * N_of[nm] * K_of[nm] + 2 * 4096 * 16 * (2 * N_of[nm] + 3 * K_of[nm]) for nm in lora_bwd), "launches": 14}),
         ("chmix_70b_m1024", p_chmix_m1024, lambda: {"bound": "mfma", "flop": sum(2 * 1024 * (a.n + b.n) * a.k for _, a, b, *_ in cm), "launches": 2 * len(GROUPS)}),

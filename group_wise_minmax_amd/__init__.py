@@ -29,7 +29,7 @@ from ._lib import (LBQ_MAX_GROUP, LBQ_MINMAX, LBQ_NF4, Desc, LbqError, QTensor, 
 
 __all__ = [
     "QuantizedWeight", "make_desc", "lbq_layout", "lbq_quantize", "lbq_dequant",
-    "lbq_linear_fwd", "lbq_linear_bwd_dx", "lbq_lora_fwd", "lbq_nf4_codebook",
+    "lbq_linear_fwd", "lbq_linear_bwd_dx", "lbq_linear_bwd_dx_grouped", "lbq_lora_fwd", "lbq_nf4_codebook",
     "lbq_linear_workspace_bytes", "lbq_lora_workspace_bytes", "LbqError", "version",
 ]
 
@@ -296,6 +296,31 @@ def lbq_linear_bwd_dx(dY: torch.Tensor, qw: QuantizedWeight,
     q = qw.qtensor()
     check(lib.lbq_linear_bwd_dx(ctypes.byref(qw.desc), ctypes.byref(q), dY.data_ptr(), m,
                                 out.data_ptr(), _stream(dY.device)), "lbq_linear_bwd_dx")
+    return out
+
+
+def lbq_linear_bwd_dx_grouped(dYs, qws, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dX = sum_i dYs[i] . deq(W_i) in bf16 for weights of one format that
+    share X and k (see ``lbq_linear_bwd_dx_grouped`` in lbq.h)."""
+    qws, dYs = list(qws), list(dYs)
+    count = len(qws)
+    if not 1 <= count <= LBQ_MAX_GROUP or len(dYs) != count:
+        raise ValueError(f"between 1 and {LBQ_MAX_GROUP} weights, one dY each")
+    for i, (d, q) in enumerate(zip(dYs, qws)):
+        _need(d, f"dYs[{i}]", torch.bfloat16)
+        if d.dim() != 2 or d.shape[1] != q.n or d.shape[0] != dYs[0].shape[0]:
+            raise ValueError(f"dYs[{i}] must be [m, {q.n}]")
+        if q.k != qws[0].k:
+            raise ValueError("every weight must have the same k")
+    m, k = dYs[0].shape[0], qws[0].k
+    if out is None:
+        out = torch.empty((m, k), dtype=torch.bfloat16, device=dYs[0].device)
+    _need(out, "out", torch.bfloat16, (m, k))
+    descs = (Desc * count)(*[q.desc for q in qws])
+    qts = (QTensor * count)(*[q.qtensor() for q in qws])
+    dps = (ctypes.c_void_p * count)(*[d.data_ptr() for d in dYs])
+    check(lib.lbq_linear_bwd_dx_grouped(count, descs, qts, dps, m, out.data_ptr(), _stream(dYs[0].device)),
+          "lbq_linear_bwd_dx_grouped")
     return out
 
 

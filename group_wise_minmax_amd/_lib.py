@@ -24,7 +24,7 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 EXPORTED = (
     "lbq_layout", "lbq_quantize", "lbq_dequant", "lbq_linear_workspace_bytes",
     "lbq_linear_fwd", "lbq_linear_fwd_grouped_workspace_bytes", "lbq_linear_fwd_grouped",
-    "lbq_linear_bwd_dx", "lbq_lora_workspace_bytes", "lbq_lora_fwd",
+    "lbq_linear_bwd_dx", "lbq_linear_bwd_dx_grouped", "lbq_lora_workspace_bytes", "lbq_lora_fwd",
     "lbq_lora_bwd_workspace_bytes", "lbq_lora_bwd",
     "lbq_serialized_bytes", "lbq_serialize", "lbq_blob_desc", "lbq_deserialize",
     "lbq_nf4_codebook", "lbq_strerror", "lbq_last_error_detail", "lbq_version",
@@ -73,6 +73,7 @@ def _load() -> ctypes.CDLL:
         "lbq_linear_fwd_grouped_workspace_bytes": (SZ, [I32, DP, I64]),
         "lbq_linear_fwd_grouped": (I32, [I32, DP, QP, P, I64, ctypes.POINTER(P), ctypes.POINTER(I64), P, SZ, P]),
         "lbq_linear_bwd_dx": (I32, [DP, QP, P, I64, P, P]),
+        "lbq_linear_bwd_dx_grouped": (I32, [I32, DP, QP, ctypes.POINTER(P), I64, P, P]),
         "lbq_lora_workspace_bytes": (SZ, [DP, I64, I32]),
         "lbq_lora_fwd": (I32, [DP, QP, P, I64, P, P, I32, ctypes.c_float, P, I64, P, SZ, P]),
         "lbq_lora_bwd_workspace_bytes": (SZ, [DP, I64, I32]),

@@ -65,9 +65,21 @@ __device__ __forceinline__ void gather_rows4(float v, float out[4]) {
   out[3] = __uint_as_float(b2);
 }
 
-template <int KIND, int BKO, int BM, int WGK, int WGM, bool LORA>
-__global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_t* __restrict__ dY,
-                                                        int m, uint16_t* __restrict__ dX,
+// Weights of one kind and k whose input gradients add up (they share X):
+// dX = sum_i dY_i . deq(W_i).  The reduction runs over their rows one weight
+// after the other; weight i owns the 64-row stages [stage_end[i-1],
+// stage_end[i]).  A single weight is a set of one.
+struct BwdSet {
+  WView w[kGemvMaxGroup];
+  const uint16_t* dy[kGemvMaxGroup];
+  int stage_end[kGemvMaxGroup];
+  int count;
+};
+
+// SET: the set may hold several weights (the stage's weight is looked up at
+// every load); otherwise it holds one, bound once.
+template <int KIND, int BKO, int BM, int WGK, int WGM, bool LORA, bool SET>
+__global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(BwdSet set, int m, uint16_t* __restrict__ dX,
                                                         LoraDx lora, Nf4Table tab) {
   using T = WKindTraits<KIND>;
   constexpr int NT = WGK * WGM * 64;
@@ -87,12 +99,18 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_
   const int lane = tid & 63, wave = tid >> 6;
   const int wk = wave % WGK, wm = wave / WGK;
   const int li = lane & 15, lg = lane >> 4;
-  const int nx = (int)((w.k + BKO - 1) / BKO), ny = (m + BM - 1) / BM;
+  const int64_t K = set.w[0].k;
+  const int nx = (int)((K + BKO - 1) / BKO), ny = (m + BM - 1) / BM;
   int tx, ty;
   tile_of(blockIdx.x, nx, ny, tx, ty);
   const int64_t k0 = (int64_t)tx * BKO;
   const int64_t m0 = (int64_t)ty * BM;
-  const int64_t K = w.k, N = w.n;
+  // the reduction: 64-row stages over all weights of the set
+  int nstage = set.stage_end[0];
+#pragma unroll
+  for (int i = 1; i < kGemvMaxGroup; ++i)
+    if (i < set.count) nstage = set.stage_end[i];
+  const int64_t N = (int64_t)nstage * BNR;
   const int64_t KB = K * T::bits / 8;
   const int64_t gpr = K / T::group;
 
@@ -104,20 +122,53 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_
     for (int b = tid; b < 256; b += NT) pairlut[b] = (f32x2_t){cbs[b >> 4], cbs[b & 15]};
   }
 
-  const int64_t nblk = N * gpr;
-  const __amdgpu_buffer_rsrc_t r_w = make_rsrc(w.packed, N * KB);
-  const __amdgpu_buffer_rsrc_t r_d = make_rsrc(dY, (int64_t)m * N * 2);
-  __amdgpu_buffer_rsrc_t r_s, r_z;
-  if constexpr (T::fmt == FMT_MINMAX) {
-    r_s = make_rsrc(w.scales, nblk * 4);
-    r_z = make_rsrc(w.zeros, nblk);
-  } else if constexpr (T::dq) {
-    r_s = make_rsrc(w.absmax_scale, ((nblk + 255) >> 8) * 4);
-    r_z = make_rsrc(w.absmax_q, nblk);
-  } else {
-    r_s = make_rsrc(w.absmax, nblk * 4);
-    r_z = r_s;
-  }
+  // Buffer resources of the weight whose rows a stage reads, and that
+  // weight's row count (the dY row stride).  They are (re)bound only in code
+  // that every lane of the workgroup runs alike, before the stage's loads:
+  // the loads themselves run under a branch on the wave index, and a value
+  // changed inside that branch would be taken as varying per lane (every
+  // buffer load would then loop over distinct resources).
+  struct Bound {
+    __amdgpu_buffer_rsrc_t w, d, s, z;
+    int64_t n;
+    int beg;  // first stage of the weight
+  };
+  auto bind = [&](int i) {
+    const WView& w = set.w[i];
+    Bound b;
+    b.n = w.n;
+    b.beg = i == 0 ? 0 : set.stage_end[i - 1];
+    const int64_t nblk = b.n * gpr;
+    b.w = make_rsrc(w.packed, b.n * KB);
+    b.d = make_rsrc(set.dy[i], (int64_t)m * b.n * 2);
+    if constexpr (T::fmt == FMT_MINMAX) {
+      b.s = make_rsrc(w.scales, nblk * 4);
+      b.z = make_rsrc(w.zeros, nblk);
+    } else if constexpr (T::dq) {
+      b.s = make_rsrc(w.absmax_scale, ((nblk + 255) >> 8) * 4);
+      b.z = make_rsrc(w.absmax_q, nblk);
+    } else {
+      b.s = make_rsrc(w.absmax, nblk * 4);
+      b.z = b.s;
+    }
+    return b;
+  };
+  Bound cur = bind(0);
+  int cur_i = 0;
+  // bind the weight of the stage starting at row vt of the set
+  auto bind_for = [&](int64_t vt) {
+    if constexpr (SET) {
+      const int st = (int)(vt / BNR);
+      int wi = 0;
+#pragma unroll
+      for (int i = 1; i < kGemvMaxGroup; ++i)
+        if (i < set.count && st >= set.stage_end[i - 1]) wi = i;
+      if (wi != cur_i) {
+        cur_i = wi;
+        cur = bind(wi);
+      }
+    }
+  };
 
   // Weight ownership: rows 4*q .. 4*q+3 of each stage, codes [8*c, +8) of the
   // k tile, with q = lane & 15 and c = (NT/64 waves) x 4 chunks.  The loads
@@ -129,7 +180,7 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_
   const uint32_t w_voff = (uint32_t)((4 * q + lg) * KB + kp * T::bits / 8);
   const uint32_t g_voff = (uint32_t)((4 * q + lg) * gpr + kp / T::group);
   // dY chunks of this thread: chunk ci = tid + NT*i -> row ci >> 3, chunk ci & 7.
-  const uint32_t d_voff = (uint32_t)(((m0 + (tid >> 3)) * N + 8 * (tid & 7)) * 2);
+  const int64_t d_row = m0 + (tid >> 3), d_col = 8 * (tid & 7);
   char* const wt_base = reinterpret_cast<char*>(&Wt[0][0]);
   char* const ds_base = reinterpret_cast<char*>(&Ds[0][0]);
   constexpr uint32_t WT_BUF = BKO * BNR * 2, DS_BUF = BM * BNR * 2;
@@ -144,11 +195,18 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_
   u32x4_t wraw;  // 32 codes of row 4q + lg (2-bit: dwords 0 and 1)
   float md_s;
   int md_i;
-  auto load_stage = [&](int64_t nt) {
+  // loads of the stage starting at row vt of the set, from the bound weight
+  auto load_stage = [&](int64_t vt) {
+    const int st = (int)(vt / BNR);
+    const Bound& b = cur;
+    const __amdgpu_buffer_rsrc_t r_w = b.w, r_d = b.d, r_s = b.s, r_z = b.z;
+    const int64_t Nw = b.n;
+    const int64_t nt = (int64_t)(st - b.beg) * BNR;
+    const uint32_t d_voff = (uint32_t)((d_row * Nw + d_col) * 2);
 #pragma unroll
     for (int i = 0; i < DCH; ++i) {
       // chunk tid + NT*i: NT/8 rows further down per i
-      const int so = (int)((NT / 8) * i * N * 2 + nt * 2);
+      const int so = (int)((NT / 8) * i * Nw * 2 + nt * 2);
       dr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_d, d_voff, so, 0));
     }
     const int so = (int)(nt * KB);
@@ -243,12 +301,15 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_
     }
   };
 
-  // n % 8 == 0, so a 64-wide stage past N only meets zero weights (buffer
-  // reads past the end) times finite dY values.
+  // n % 8 == 0, so the rows of a weight's last 64-wide stage past its n only
+  // meet zero weights (buffer reads past the end) times finite dY values.
   if constexpr (T::fmt == FMT_NF4) __syncthreads();  // pair table visible
   load_stage(0);
   store_stage(0);
-  if (BNR < N) load_stage(BNR);
+  if (BNR < N) {
+    bind_for(BNR);
+    load_stage(BNR);
+  }
   __syncthreads();
   int buf = 0;
   if constexpr (WGK * WGM == 8) {
@@ -270,6 +331,7 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_
       __builtin_amdgcn_s_setprio(0);
     };
     for (int64_t nt = 0; nt < N; nt += BNR) {
+      if (nt + 2 * BNR < N) bind_for(nt + 2 * BNR);  // both wave groups load this stage
       if (late) mfma_phase();
       else stage(nt);
       __syncthreads();
@@ -282,7 +344,10 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_
     for (int64_t nt = 0; nt < N; nt += BNR) {
       if (nt + BNR < N) {
         store_stage(buf ^ 1);
-        if (nt + 2 * BNR < N) load_stage(nt + 2 * BNR);
+        if (nt + 2 * BNR < N) {
+          bind_for(nt + 2 * BNR);
+          load_stage(nt + 2 * BNR);
+        }
       }
       compute(buf);
       __syncthreads();
@@ -338,15 +403,19 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(WView w, const uint16_
 }
 
 template <int KIND, int BKO, int BM, int WGK, int WGM>
-hipError_t launch_bwd_cfg(const WView& w, const uint16_t* dY, int64_t m, uint16_t* dX,
-                          const LoraDx& lora, const Nf4Table& tab, hipStream_t s) {
-  const int64_t tiles = ((w.k + BKO - 1) / BKO) * ((m + BM - 1) / BM);
-  if (lora.g != nullptr) {
-    hipLaunchKernelGGL((k_bwd_dx<KIND, BKO, BM, WGK, WGM, true>), dim3((unsigned)tiles),
-                       dim3(WGK * WGM * 64), 0, s, w, dY, (int)m, dX, lora, tab);
+hipError_t launch_bwd_cfg(const BwdSet& set, int64_t m, uint16_t* dX, const LoraDx& lora, const Nf4Table& tab,
+                          hipStream_t s) {
+  const int64_t k = set.w[0].k;
+  const int64_t tiles = ((k + BKO - 1) / BKO) * ((m + BM - 1) / BM);
+  if (lora.g != nullptr) {  // LoRA: single weights only
+    hipLaunchKernelGGL((k_bwd_dx<KIND, BKO, BM, WGK, WGM, true, false>), dim3((unsigned)tiles),
+                       dim3(WGK * WGM * 64), 0, s, set, (int)m, dX, lora, tab);
+  } else if (set.count > 1) {
+    hipLaunchKernelGGL((k_bwd_dx<KIND, BKO, BM, WGK, WGM, false, true>), dim3((unsigned)tiles),
+                       dim3(WGK * WGM * 64), 0, s, set, (int)m, dX, lora, tab);
   } else {
-    hipLaunchKernelGGL((k_bwd_dx<KIND, BKO, BM, WGK, WGM, false>), dim3((unsigned)tiles),
-                       dim3(WGK * WGM * 64), 0, s, w, dY, (int)m, dX, lora, tab);
+    hipLaunchKernelGGL((k_bwd_dx<KIND, BKO, BM, WGK, WGM, false, false>), dim3((unsigned)tiles),
+                       dim3(WGK * WGM * 64), 0, s, set, (int)m, dX, lora, tab);
   }
   return hipGetLastError();
 }
@@ -358,21 +427,44 @@ double bwd_fill(int64_t tiles) {
 
 template <int KIND>
 struct BwdLauncher {
-  static hipError_t run(const WView& w, const uint16_t* dY, int64_t m, uint16_t* dX,
-                        const LoraDx& lora, const Nf4Table& tab, hipStream_t s) {
+  static hipError_t run(const BwdSet& set, int64_t m, uint16_t* dX, const LoraDx& lora, const Nf4Table& tab,
+                        hipStream_t s) {
     // 256 x 256 tiles (8 waves of 128 x 64) unless they leave most of the chip idle.
-    const int64_t t256 = ((w.k + 255) / 256) * ((m + 255) / 256);
-    const int64_t t128 = ((w.k + 127) / 128) * ((m + 127) / 128);
-    if (bwd_fill(t256) >= 0.5 * bwd_fill(t128)) return launch_bwd_cfg<KIND, 256, 256, 2, 4>(w, dY, m, dX, lora, tab, s);
-    return launch_bwd_cfg<KIND, 128, 128, 2, 2>(w, dY, m, dX, lora, tab, s);
+    const int64_t k = set.w[0].k;
+    const int64_t t256 = ((k + 255) / 256) * ((m + 255) / 256);
+    const int64_t t128 = ((k + 127) / 128) * ((m + 127) / 128);
+    if (bwd_fill(t256) >= 0.5 * bwd_fill(t128)) return launch_bwd_cfg<KIND, 256, 256, 2, 4>(set, m, dX, lora, tab, s);
+    return launch_bwd_cfg<KIND, 128, 128, 2, 2>(set, m, dX, lora, tab, s);
   }
 };
+
+BwdSet make_bwd_set(const WView* ws, const uint16_t* const* dys, int count) {
+  BwdSet set{};
+  set.count = count;
+  int end = 0;
+  for (int i = 0; i < count; ++i) {
+    set.w[i] = ws[i];
+    set.dy[i] = dys[i];
+    end += (int)((ws[i].n + BNR - 1) / BNR);
+    set.stage_end[i] = end;
+  }
+  return set;
+}
 
 }  // namespace
 
 hipError_t launch_bwd_dx(WKind kind, const WView& w, const uint16_t* dY, int64_t m,
                          uint16_t* dX, const LoraDx& lora, const Nf4Table& tab, hipStream_t s) {
-  return dispatch_kind<BwdLauncher>(kind, w, dY, m, dX, lora, tab, s);
+  return dispatch_kind<BwdLauncher>(kind, make_bwd_set(&w, &dY, 1), m, dX, lora, tab, s);
+}
+
+hipError_t launch_bwd_dx_set(WKind kind, const WView* ws, const uint16_t* const* dys, int count, int64_t m,
+                             uint16_t* dX, const Nf4Table& tab, hipStream_t s) {
+  if (count < 1 || count > kGemvMaxGroup) return hipErrorInvalidValue;
+  for (int i = 1; i < count; ++i)
+    if (ws[i].k != ws[0].k) return hipErrorInvalidValue;
+  const LoraDx none{nullptr, nullptr, 0, 0};
+  return dispatch_kind<BwdLauncher>(kind, make_bwd_set(ws, dys, count), m, dX, none, tab, s);
 }
 
 

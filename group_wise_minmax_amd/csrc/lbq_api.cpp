@@ -401,6 +401,28 @@ lbq_status lbq_linear_bwd_dx(const lbq_desc* desc, const lbq_qtensor* q, const u
                     "lbq_linear_bwd_dx");
 }
 
+lbq_status lbq_linear_bwd_dx_grouped(int32_t count, const lbq_desc* descs, const lbq_qtensor* qs,
+                                     const uint16_t* const* dYs, int64_t m, uint16_t* dX, void* stream) {
+  if (count < 1 || count > LBQ_MAX_GROUP)
+    return fail(LBQ_E_SHAPE, "count must be in [1, %d] (got %d)", LBQ_MAX_GROUP, count);
+  if (descs == nullptr || qs == nullptr || dYs == nullptr) return fail(LBQ_E_NULL, "descs, qs and dYs must be non-NULL");
+  for (int32_t i = 0; i < count; ++i) {
+    const lbq_status st = check_bwd_common(&descs[i], &qs[i], dYs[i], m, dX, "lbq_linear_bwd_dx_grouped");
+    if (st != LBQ_OK) return st;
+    if (descs[i].k != descs[0].k)
+      return fail(LBQ_E_SHAPE, "weight %d has k = %lld, weight 0 has %lld", i, (long long)descs[i].k,
+                  (long long)descs[0].k);
+    if (kind_of(&descs[i]) != kind_of(&descs[0]))
+      return fail(LBQ_E_UNSUPPORTED, "lbq_linear_bwd_dx_grouped takes weights of one format (weight %d differs)", i);
+  }
+  if (m == 0) return ok();
+  lbq::WView ws[LBQ_MAX_GROUP];
+  for (int32_t i = 0; i < count; ++i) ws[i] = view_of(&descs[i], &qs[i]);
+  return hip_status(lbq::launch_bwd_dx_set(kind_of(&descs[0]), ws, dYs, count, m, dX, nf4_table(),
+                                           static_cast<hipStream_t>(stream)),
+                    "lbq_linear_bwd_dx_grouped");
+}
+
 // LoRA backward workspace (16-byte aligned pieces): Bt = B^T [rp][n] bf16,
 // G = bf16(sigma dY B) [m][rp], T = bf16(sigma X A^T) [m][rp], then the fp32
 // partial sums of the dA / dB reductions (reused by both).

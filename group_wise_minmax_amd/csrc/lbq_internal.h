@@ -107,6 +107,10 @@ hipError_t launch_gemm_fwd_set(WKind kind, const WView* ws, uint16_t* const* ys,
                                const Nf4Table& tab, hipStream_t s);
 hipError_t launch_bwd_dx(WKind kind, const WView& w, const uint16_t* dY, int64_t m,
                          uint16_t* dX, const LoraDx& lora, const Nf4Table& tab, hipStream_t s);
+// Input gradient of several weights of one kind and k that share X, summed:
+// dX = sum_i dys[i] . deq(ws[i]), 1 <= count <= kGemvMaxGroup.
+hipError_t launch_bwd_dx_set(WKind kind, const WView* ws, const uint16_t* const* dys, int count, int64_t m,
+                             uint16_t* dX, const Nf4Table& tab, hipStream_t s);
 // Adapter products and gradients (k_lora.hip).
 // Bt = B^T zero-padded to rp rows.
 hipError_t launch_transpose_b(const uint16_t* B, int64_t n, int32_t r, int32_t rp, uint16_t* Bt,

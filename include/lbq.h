@@ -212,6 +212,20 @@ lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lb
 lbq_status lbq_linear_bwd_dx(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* dY,
                              int64_t m, uint16_t* dX, void* stream);
 
+/* Input gradient of several frozen linears that read the same X (q, k and v;
+ * gate and up), summed as the chain rule gives it for a shared input ([QL]
+ * QLoRA技术原理: the gradient passes through each frozen 4-bit weight):
+ *   dX = bf16( sum_i dYs[i] . deq(W_i) ), one fp32 accumulation over the
+ * rows of all the weights, weight 0's first.  descs, qs, dYs: host arrays of
+ * `count` entries (1 <= count <= LBQ_MAX_GROUP); the weights share one
+ * format (LBQ_E_UNSUPPORTED otherwise) and k; dYs[i]: bf16 [m][n_i] (device);
+ * dX: bf16 [m][k].  Each weight and dYs[i] are checked as in
+ * lbq_linear_bwd_dx before anything is enqueued.  One launch.  When every
+ * n_i but the last is a multiple of 64, dX equals lbq_linear_bwd_dx of the
+ * weights stacked along n (with the dY blocks side by side), bit for bit. */
+lbq_status lbq_linear_bwd_dx_grouped(int32_t count, const lbq_desc* descs, const lbq_qtensor* qs,
+                                     const uint16_t* const* dYs, int64_t m, uint16_t* dX, void* stream);
+
 /* Workspace bytes lbq_lora_bwd needs for m rows and rank r (0 for m <= 0). */
 size_t lbq_lora_bwd_workspace_bytes(const lbq_desc* desc, int64_t m, int32_t r);
 

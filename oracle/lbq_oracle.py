@@ -287,6 +287,13 @@ def linear_bwd_dx(dY_bits: np.ndarray, W_exact: np.ndarray) -> np.ndarray:
     return bf16_to_f64(dY_bits) @ W_exact
 
 
+def linear_bwd_dx_grouped(dY_bits_list, W_exact_list) -> np.ndarray:
+    """dX = sum_i dY_i . W_i in fp64 for linears that read the same X (the
+    chain rule sums the gradients that reach a shared input; [QL]: each passes
+    through its frozen quantized weight)."""
+    return sum(bf16_to_f64(d) @ W for d, W in zip(dY_bits_list, W_exact_list))
+
+
 def lora_fwd(X_bits, W_exact, A_bits, B_bits, sigma: float) -> np.ndarray:
     """Y = X . W^T + sigma * (X . A^T) . B^T in fp64; A is [r, K], B is [N, r]."""
     X = bf16_to_f64(X_bits)

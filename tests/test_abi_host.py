@@ -254,6 +254,28 @@ def test_grouped_fwd_error_paths(L):
     assert call(descs=dk, m=16, ws=FAKE + 8, wsb=need) == "LBQ_E_ALIGN"
 
 
+def test_grouped_bwd_error_paths(L):
+    lib = L.lib
+    d = [L.make_desc("minmax", 64, 256), L.make_desc("minmax", 128, 256), L.make_desc("minmax", 32, 256)]
+
+    def call(descs=d, dys=None, dX=FAKE, m=4, count=None):
+        c = len(descs) if count is None else count
+        D = (L.Desc * len(descs))(*descs)
+        Q = (L.QTensor * len(descs))(*[_q(L) for _ in descs])
+        P = (ctypes.c_void_p * len(descs))(*(dys or [FAKE] * len(descs)))
+        return _status(L, lib.lbq_linear_bwd_dx_grouped(c, D, Q, P, m, dX, None))
+
+    assert call(count=0) == "LBQ_E_SHAPE"
+    assert call(descs=d * 3) == "LBQ_E_SHAPE"  # 9 > LBQ_MAX_GROUP
+    assert _status(L, lib.lbq_linear_bwd_dx_grouped(1, None, None, None, 4, FAKE, None)) == "LBQ_E_NULL"
+    assert call(descs=[d[0], L.make_desc("minmax", 64, 512)]) == "LBQ_E_SHAPE"  # k differs
+    assert call(descs=[d[0], L.make_desc("minmax", 64, 256, 2, 64)]) == "LBQ_E_UNSUPPORTED"  # formats differ
+    assert call(descs=[d[0], L.make_desc("minmax", 60, 256)]) == "LBQ_E_SHAPE"  # n % 8 != 0
+    assert call(dys=[FAKE, FAKE + 8, FAKE]) == "LBQ_E_ALIGN"  # weight 1's dY
+    assert call(dX=FAKE + 8) == "LBQ_E_ALIGN"
+    assert call(m=0) == "LBQ_OK"  # empty batch: nothing enqueued
+
+
 def test_lora_bwd_error_paths(L):
     lib = L.lib
     B = ctypes.byref

@@ -289,6 +289,48 @@ def test_gemm_large_tiles_few_k_steps(L, fid, kk):
     assert_close(bf16_bits_host(dX)[rows], O.linear_bwd_dx(dY[rows], ref2["w_exact"]), what=f"bwd {fid} n={kk}")
 
 
+@pytest.mark.parametrize("fid", ["i4g128", "i2g64", "nf4dq"])
+@pytest.mark.parametrize("m", [3, 130, 300])
+def test_bwd_dx_grouped(L, fid, m):
+    """dX = sum_i dY_i . deq(W_i) for weights that share X, in one launch:
+    bit for bit the input gradient of the weights stacked along n (the 320-
+    and 64-row weights end on 64-row stage boundaries, the 200-row weight in
+    a partial stage; NF4+DQ's 256-block groups do not straddle weights), and
+    within the matmul tolerance of the oracle."""
+    fmt, bits, group, dq = FORMATS[FMT_IDS.index(fid)]
+    k, ns = 1280, (320, 64, 200)
+    Ws = [SI.gaussian_weights(9600 + i, n, k, outlier_seed=9610 + i) for i, n in enumerate(ns)]
+    pairs = [_quant_pair(L, W, fmt, bits, group, dq) for W in Ws]
+    dYs = [SI.bf16_normal(9620 + 10 * i + m, (m, n)) for i, n in enumerate(ns)]
+    dX = L.lbq_linear_bwd_dx_grouped([to_dev_bf16(d) for d in dYs], [p[0] for p in pairs])
+    q_all = L.lbq_quantize(to_dev_f32(np.concatenate(Ws)), fmt, bits, group, dq)
+    dX_all = L.lbq_linear_bwd_dx(to_dev_bf16(np.concatenate(dYs, axis=1)), q_all)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits_host(dX), bf16_bits_host(dX_all)), f"{fid} m={m}: grouped != stacked"
+    assert_close(bf16_bits_host(dX), O.linear_bwd_dx_grouped(dYs, [p[1]["w_exact"] for p in pairs]),
+                 what=f"grouped bwd {fid} m={m}")
+
+
+@pytest.mark.parametrize("fid", ["i4g64", "nf4"])
+def test_bwd_dx_grouped_ragged_and_single(L, fid):
+    """Weights whose row counts are not multiples of 64 (each ends in a
+    partial stage) against the oracle; a set of one equals lbq_linear_bwd_dx
+    bit for bit."""
+    fmt, bits, group, dq = FORMATS[FMT_IDS.index(fid)]
+    k, m, ns = 640, 130, (136, 8, 72)
+    pairs = [_quant_pair(L, SI.gaussian_weights(9640 + i, n, k, outlier_seed=9650 + i), fmt, bits, group, dq)
+             for i, n in enumerate(ns)]
+    dYs = [SI.bf16_normal(9660 + i, (m, n)) for i, n in enumerate(ns)]
+    dYd = [to_dev_bf16(d) for d in dYs]
+    dX = L.lbq_linear_bwd_dx_grouped(dYd, [p[0] for p in pairs])
+    one = L.lbq_linear_bwd_dx_grouped(dYd[:1], [pairs[0][0]])
+    single = L.lbq_linear_bwd_dx(dYd[0], pairs[0][0])
+    torch.cuda.synchronize()
+    assert_close(bf16_bits_host(dX), O.linear_bwd_dx_grouped(dYs, [p[1]["w_exact"] for p in pairs]),
+                 what=f"grouped bwd {fid} ragged")
+    assert np.array_equal(bf16_bits_host(one), bf16_bits_host(single))
+
+
 @pytest.mark.parametrize("bits,group", [(4, 128), (2, 64)])
 @pytest.mark.parametrize("m", [3, 130])
 def test_bwd_dx_exact_on_grid(L, bits, group, m):

@@ -455,3 +455,23 @@ def test_lora_bwd_brute_force_tiny():
         for j in range(r):
             v = sum(sigma * dYf[a, i] * Xf[a, c] * Af[j, c] for a in range(m) for c in range(k))
             assert abs(dB[i, j] - v) <= 1e-12 * max(1.0, abs(v))
+
+
+def test_grouped_input_gradient_is_the_adjoint_of_the_shared_forward():
+    """Linears that read one X: <dX, X> equals the sum over the linears of
+    <dY_i, X W_i^T> (exact on grid values, which pins the sum over the
+    weights and every transpose), and sampled entries equal the brute-force
+    sum over all the weights' rows."""
+    X = SI.bf16_small_ints(150, (3, 256))
+    Ws = [SI.grid_weights(151 + i, n, 256, 128, 4) for i, n in enumerate((16, 8, 24))]
+    qs = [O.quantize(W, "minmax", 4, 128) for W in Ws]
+    dYs = [SI.bf16_small_ints(160 + i, (3, W.shape[0])) for i, W in enumerate(Ws)]
+    dX = O.linear_bwd_dx_grouped(dYs, [q["w_exact"] for q in qs])
+    assert dX.shape == (3, 256)
+    lhs = (dX * O.bf16_to_f64(X)).sum()
+    rhs = sum((O.bf16_to_f64(d) * O.linear_fwd(X, q["w_exact"])).sum() for d, q in zip(dYs, qs))
+    assert lhs == rhs
+    for a in range(3):
+        for c in range(0, 256, 37):
+            v = sum(O.bf16_to_f64(d)[a, j] * q["w_exact"][j, c] for d, q in zip(dYs, qs) for j in range(d.shape[1]))
+            assert dX[a, c] == v

@@ -143,6 +143,30 @@ def test_8b_nf4dq_layer(li):
                  what=f"{nm} nf4dq bwd m={m}")
 
 
+@pytest.mark.parametrize("group", [("q", "k", "v"), ("gate", "up")], ids=["qkv", "gate_up"])
+def test_8b_grouped_bwd(group):
+    """The layer's summed input gradients as the grouped backward phase runs
+    them (NF4+DQ, m = 4096, one launch per group): 64 sampled rows of dX
+    against the oracle's sum over the group's weights."""
+    m = 4096
+    ms = sample(m, 64, 7600 + len(group))
+    ms_t = torch.from_numpy(ms).to(DEV)
+    qws, w_refs, dYs = [], [], []
+    for nm in group:
+        li = NAMES.index(nm)
+        n, k = SI.LLAMA3_8B[nm]
+        W = SI.dev_gaussian_weights(SI.seed_of(2, li, SI.SLOT_W), n, k, DEV)
+        qws.append(L.lbq_quantize(W, "nf4", double_quant=True))
+        w_refs.append(O.quantize(W.cpu().numpy(), "nf4", double_quant_on=True)["w_exact"])
+        del W
+        dYs.append(SI.dev_bf16_normal(SI.seed_of(3, li, SI.SLOT_DY), (m, n), DEV))
+    dX = L.lbq_linear_bwd_dx_grouped(dYs, qws)
+    ref = O.linear_bwd_dx_grouped([bf16_rows(d, ms) for d in dYs], w_refs)
+    assert_close(bf16_bits_host(dX[ms_t]), ref, what=f"{'+'.join(group)} grouped bwd m={m}")
+    del dX, dYs, qws
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------------------
 # LLaMA-3-8B layer, linears that share X in one launch (q/k/v, gate/up), as the
 # benchmark runs them: bit-identical to one launch per linear (whose outputs

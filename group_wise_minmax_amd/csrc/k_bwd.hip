@@ -19,15 +19,16 @@ namespace {
 // The packed weight is contiguous along k, the reduction runs along n: per
 // stage a thread dequantizes 8 codes (one k-chunk) of 4 consecutive rows n
 // and writes, for each of its 8 k, the 4 values of the rows as one 8-byte LDS
-// store into the k-major tile.  It loads them row-wise, though: 32 codes of
-// one row (one 16- or 8-byte load, with that row's metadata), and four
-// permlane swaps transpose the 4 x 4 dwords across the lanes that share the
-// n-quad, so a stage costs 3 weight loads per thread instead of 12.  The n-quad is the lane's low
-// 4 bits, which (with the row swizzle) keeps these column writes
-// bank-conflict free.  dY chunks are staged like X in the forward GEMM.  Both
-// tiles are double-buffered with one barrier per stage, and every global load
-// goes through a buffer resource (reads past the end return zeros), so rows
-// past n, m or k need no guards.
+// store into the k-major tile.  The n-quad is the lane's low 4 bits, which
+// (with the row swizzle) keeps these column writes bank-conflict free.  The
+// codes are loaded row-wise, though: 32 codes of one row (one 16- or 8-byte
+// load, with that row's metadata), and four permlane swaps transpose the
+// 4 x 4 dwords across the lanes that share the n-quad.  A stage so costs 3
+// weight loads per thread rather than a code word, a scale and a zero point
+// for each of 4 rows.  dY chunks are staged like X in the forward GEMM.  Both
+// tiles are double-buffered (one barrier per stage, two with the 8-wave
+// two-phase loop), and every global load goes through a buffer resource
+// (reads past the end return zeros), so rows past n, m or k need no guards.
 // ---------------------------------------------------------------------------
 constexpr int BNR = 64;  // reduction (n) per stage = one 128-byte LDS row
 
@@ -76,8 +77,9 @@ struct BwdSet {
   int count;
 };
 
-// SET: the set may hold several weights (the stage's weight is looked up at
-// every load); otherwise it holds one, bound once.
+// SET: the set may hold several weights (the weight of the stage about to be
+// loaded is looked up at the top of each K step and bound when it changes);
+// otherwise it holds one, bound once.
 template <int KIND, int BKO, int BM, int WGK, int WGM, bool LORA, bool SET>
 __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(BwdSet set, int m, uint16_t* __restrict__ dX,
                                                         LoraDx lora, Nf4Table tab) {

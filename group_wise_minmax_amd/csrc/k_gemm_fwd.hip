@@ -139,9 +139,11 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
 #pragma unroll
     for (int b = 0; b < TM; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Prefetch registers.  Loads are unconditional from clamped addresses (no
-  // branches, so they are all in flight at once); the metadata stays raw here
-  // and is combined in store_stage, one K-step later, so no wave waits on it.
+  // Prefetch registers.  Code and X loads are unconditional from clamped
+  // addresses (no branches, so they are all in flight at once).  Metadata is
+  // loaded at the first stage of each group, or of each batch of 4 groups (a
+  // branch that every lane takes alike); it stays raw here and is combined in
+  // store_stage, one K-step later, so no wave waits on it.
   u32x4_t xr[XCH];
   u32x4_t wr[NQ];
   float md_s = 0.f;  // scale (MinMax), absmax or second-level scale (NF4)
@@ -195,7 +197,7 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
         }
         if constexpr (T::fmt == FMT_MINMAX || T::dq) mb_b = mb_arr[gi];
       }
-      if constexpr (T::dq) md_s = w.absmax_scale[gi >> 8];  // one second-level block per batch
+      if constexpr (T::dq) md_s = w.absmax_scale[gi >> 8];  // a batch never straddles a 256-block one
     }
   };
   auto store_stage = [&](int buf) {

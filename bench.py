@@ -352,7 +352,7 @@ def build_workload(L, SI, torch, dev, R, want):
         ("bwd_m4096", p_bwd, lambda: {"bound": "mfma", "flop": flop(4096), "launches": 7}),
         ("bwd_m4096_grouped", p_bwd_grouped, lambda: {"bound": "mfma", "flop": flop(4096), "launches": len(GROUPS)}),
         # dX = dY W + G A, G = dY B, T = X A^T, dA = G^T X, dB = (T^T dY)^T
-        ("lora_bwd_m4096", p_lora_bwd, lambda: {"bound": "mfma", "flop": sum(2 * 4096 * N_of[nm] * K_of[nm] + 2 * 4096 * 16 * (2 * N_of[nm] + 3 * K_of[nm]) for nm in lora_bwd), "launches": 14}),
+        ("lora_bwd_m4096", p_lora_bwd, lambda: {"bound": "mfma", "flop": sum(2 * 4096 * N_of[nm] * K_of[nm] + 2 * 4096 * 16 * (2 * N_of[nm] + 3 * K_of[nm]) for nm in lora_bwd), "launches": 12}),
         ("chmix_70b_m1024", p_chmix_m1024, lambda: {"bound": "mfma", "flop": sum(2 * 1024 * (a.n + b.n) * a.k for _, a, b, *_ in cm), "launches": 2 * len(GROUPS)}),
         ("copy_1g", p_copy, lambda: {"bound": "hbm", "bytes": 2 << 30, "launches": 1}),
     ]

@@ -43,10 +43,25 @@ __global__ __launch_bounds__(256) void k_transpose_b(const uint16_t* __restrict_
 // ---------------------------------------------------------------------------
 constexpr int XA_ROWS = 64;
 
+// One adapter product of a launch; a launch runs one or two of them (blockIdx.z
+// picks the job, and blocks past a job's own split count return at once).
+struct XaJob {
+  const uint16_t* X;
+  int64_t K;
+  const uint16_t* A;
+  int steps_per_split, splits;
+  float* part;
+};
+
 template <int NT>
-__global__ __launch_bounds__(256) void k_lora_xa(const uint16_t* __restrict__ X, int m, int64_t K,
-                                                const uint16_t* __restrict__ A, int r,
-                                                int steps_per_split, float* __restrict__ part) {
+__global__ __launch_bounds__(256) void k_lora_xa(XaJob j0, XaJob j1, int m, int r) {
+  const XaJob J = blockIdx.z ? j1 : j0;
+  if ((int)blockIdx.y >= J.splits) return;
+  const uint16_t* __restrict__ X = J.X;
+  const int64_t K = J.K;
+  const uint16_t* __restrict__ A = J.A;
+  const int steps_per_split = J.steps_per_split;
+  float* __restrict__ part = J.part;
   __shared__ f32x4_t red[3][4 * NT][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -145,10 +160,20 @@ __device__ __forceinline__ float sum_splits(const float* __restrict__ part, int 
 // Fixed summation order.
 constexpr int FIN_ROWS = 16;
 
-__global__ __launch_bounds__(256) void k_lora_xa_finalize(const float* __restrict__ part, int splits,
-                                                         int rb, int m, int r, int rp, float sigma,
-                                                         uint16_t* __restrict__ Trm,
-                                                         uint16_t* __restrict__ Ttr, int64_t mp) {
+struct FinJob {
+  const float* part;
+  int splits;
+  uint16_t* Trm;
+  uint16_t* Ttr;
+};
+
+__global__ __launch_bounds__(256) void k_lora_xa_finalize(FinJob j0, FinJob j1, int rb, int m, int r, int rp,
+                                                         float sigma, int64_t mp) {
+  const FinJob J = blockIdx.z ? j1 : j0;
+  const float* __restrict__ part = J.part;
+  const int splits = J.splits;
+  uint16_t* __restrict__ Trm = J.Trm;
+  uint16_t* __restrict__ Ttr = J.Ttr;
   __shared__ uint16_t tile[FIN_ROWS][64 + 2];
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * FIN_ROWS;
@@ -188,10 +213,25 @@ __global__ __launch_bounds__(256) void k_lora_xa_finalize(const float* __restric
 // ---------------------------------------------------------------------------
 constexpr int OUT_COLS = 128;
 
+// One outer product of a launch; a launch runs one or two of them (blockIdx.z
+// picks the job; blocks past a job's columns or split count return at once).
+struct OuterJob {
+  const uint16_t* Pt;
+  const uint16_t* Q;
+  int64_t C;
+  int steps_per_split, splits;
+  float* part;
+};
+
 template <int NT>
-__global__ __launch_bounds__(256) void k_lora_outer(const uint16_t* __restrict__ Pt, int64_t mp,
-                                                   const uint16_t* __restrict__ Q, int m, int64_t C,
-                                                   int steps_per_split, float* __restrict__ part) {
+__global__ __launch_bounds__(256) void k_lora_outer(OuterJob j0, OuterJob j1, int64_t mp, int m) {
+  const OuterJob J = blockIdx.z ? j1 : j0;
+  if ((int)blockIdx.y >= J.splits || (int64_t)blockIdx.x * OUT_COLS >= J.C) return;
+  const uint16_t* __restrict__ Pt = J.Pt;
+  const uint16_t* __restrict__ Q = J.Q;
+  const int64_t C = J.C;
+  const int steps_per_split = J.steps_per_split;
+  float* __restrict__ part = J.part;
   __shared__ f32x4_t red[3][8][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -281,9 +321,22 @@ __global__ __launch_bounds__(256) void k_lora_outer(const uint16_t* __restrict__
 // summation order.
 constexpr int RED_COLS = 16;
 
-__global__ __launch_bounds__(256) void k_lora_outer_reduce(const float* __restrict__ part, int splits,
-                                                          int rb, int r, int64_t C, bool transpose,
-                                                          float* __restrict__ out) {
+struct RedJob {
+  const float* part;
+  int splits;
+  int64_t C;
+  bool transpose;
+  float* out;
+};
+
+__global__ __launch_bounds__(256) void k_lora_outer_reduce(RedJob j0, RedJob j1, int rb, int r) {
+  const RedJob J = blockIdx.z ? j1 : j0;
+  if ((int64_t)blockIdx.x * RED_COLS >= J.C) return;
+  const float* __restrict__ part = J.part;
+  const int splits = J.splits;
+  const int64_t C = J.C;
+  const bool transpose = J.transpose;
+  float* __restrict__ out = J.out;
   __shared__ float tile[RED_COLS][64 + 1];
   const int tid = threadIdx.x;
   const int64_t c0 = (int64_t)blockIdx.x * RED_COLS;
@@ -352,50 +405,92 @@ size_t lora_xa_part_bytes(int64_t m, int64_t K, int32_t r) {
   return (size_t)xa_splits(m, K) * (size_t)m * (size_t)(16 * tiles_of(r)) * sizeof(float);
 }
 
-hipError_t launch_lora_xa(const uint16_t* X, int64_t m, int64_t K, const uint16_t* A, int32_t r,
-                          int32_t rp, float sigma, float* part, uint16_t* Trm, uint16_t* Ttr,
-                          int64_t mp, hipStream_t s) {
-  const int sp = xa_splits(m, K);
-  const int64_t steps = K / 32;
-  const int sps = (int)((steps + sp - 1) / sp);
-  const dim3 grid((unsigned)((m + XA_ROWS - 1) / XA_ROWS), (unsigned)sp);
+// One or two adapter products (count = 1 or 2; jobs[i] = X, K, A with its
+// outputs), each with its own area of fp32 partials, in one product launch and
+// one finalize launch.
+hipError_t launch_lora_xa_jobs(int count, const uint16_t* const* Xs, const int64_t* Ks, const uint16_t* const* As,
+                               uint16_t* const* Trms, uint16_t* const* Ttrs, int64_t m, int32_t r, int32_t rp,
+                               float sigma, float* part, int64_t mp, hipStream_t s) {
+  XaJob xj[2];
+  FinJob fj[2];
+  int sp_max = 0;
+  float* p = part;
+  for (int i = 0; i < count; ++i) {
+    const int sp = xa_splits(m, Ks[i]);
+    const int64_t steps = Ks[i] / 32;
+    xj[i] = XaJob{Xs[i], Ks[i], As[i], (int)((steps + sp - 1) / sp), sp, p};
+    fj[i] = FinJob{p, sp, Trms[i], Ttrs[i]};
+    sp_max = sp > sp_max ? sp : sp_max;
+    p += lora_xa_part_bytes(m, Ks[i], r) / sizeof(float);
+  }
+  if (count == 1) xj[1] = xj[0], fj[1] = fj[0];
+  const dim3 grid((unsigned)((m + XA_ROWS - 1) / XA_ROWS), (unsigned)sp_max, (unsigned)count);
   const int nt = tiles_of(r);
   switch (nt) {
-    case 1: hipLaunchKernelGGL(k_lora_xa<1>, grid, dim3(256), 0, s, X, (int)m, K, A, (int)r, sps, part); break;
-    case 2: hipLaunchKernelGGL(k_lora_xa<2>, grid, dim3(256), 0, s, X, (int)m, K, A, (int)r, sps, part); break;
-    case 3: hipLaunchKernelGGL(k_lora_xa<3>, grid, dim3(256), 0, s, X, (int)m, K, A, (int)r, sps, part); break;
-    default: hipLaunchKernelGGL(k_lora_xa<4>, grid, dim3(256), 0, s, X, (int)m, K, A, (int)r, sps, part); break;
+    case 1: hipLaunchKernelGGL(k_lora_xa<1>, grid, dim3(256), 0, s, xj[0], xj[1], (int)m, (int)r); break;
+    case 2: hipLaunchKernelGGL(k_lora_xa<2>, grid, dim3(256), 0, s, xj[0], xj[1], (int)m, (int)r); break;
+    case 3: hipLaunchKernelGGL(k_lora_xa<3>, grid, dim3(256), 0, s, xj[0], xj[1], (int)m, (int)r); break;
+    default: hipLaunchKernelGGL(k_lora_xa<4>, grid, dim3(256), 0, s, xj[0], xj[1], (int)m, (int)r); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t rows = Ttr != nullptr ? mp : m;
-  hipLaunchKernelGGL(k_lora_xa_finalize, dim3((unsigned)((rows + FIN_ROWS - 1) / FIN_ROWS)), dim3(256), 0, s,
-                     part, sp, 16 * nt, (int)m, (int)r, (int)rp, sigma, Trm, Ttr, mp);
+  // every job with a transposed output covers mp rows, else m
+  int64_t rows = m;
+  for (int i = 0; i < count; ++i)
+    if (Ttrs[i] != nullptr) rows = mp;
+  hipLaunchKernelGGL(k_lora_xa_finalize, dim3((unsigned)((rows + FIN_ROWS - 1) / FIN_ROWS), 1, (unsigned)count),
+                     dim3(256), 0, s, fj[0], fj[1], 16 * nt, (int)m, (int)r, (int)rp, sigma, mp);
   return hipGetLastError();
+}
+
+hipError_t launch_lora_xa(const uint16_t* X, int64_t m, int64_t K, const uint16_t* A, int32_t r,
+                          int32_t rp, float sigma, float* part, uint16_t* Trm, uint16_t* Ttr,
+                          int64_t mp, hipStream_t s) {
+  return launch_lora_xa_jobs(1, &X, &K, &A, &Trm, &Ttr, m, r, rp, sigma, part, mp, s);
 }
 
 size_t lora_outer_part_bytes(int64_t m, int64_t C, int32_t r) {
   return (size_t)outer_splits(m, C) * (size_t)(16 * tiles_of(r)) * (size_t)C * sizeof(float);
 }
 
-hipError_t launch_lora_outer(const uint16_t* Pt, int64_t mp, int32_t r, const uint16_t* Q, int64_t m,
-                             int64_t C, bool transpose, float* part, float* out, hipStream_t s) {
-  const int sp = outer_splits(m, C);
-  const int64_t steps = (m + 31) / 32;
-  const int sps = (int)((steps + sp - 1) / sp);
-  const dim3 grid((unsigned)((C + OUT_COLS - 1) / OUT_COLS), (unsigned)sp);
+// One or two outer products (count = 1 or 2), each with its own area of fp32
+// partials, in one product launch and one reduce launch.
+hipError_t launch_lora_outer_jobs(int count, const uint16_t* const* Pts, const uint16_t* const* Qs,
+                                  const int64_t* Cs, const bool* transposes, float* const* outs, int64_t mp,
+                                  int32_t r, int64_t m, float* part, hipStream_t s) {
+  OuterJob oj[2];
+  RedJob rj[2];
+  int sp_max = 0;
+  int64_t c_max = 0;
+  float* p = part;
+  for (int i = 0; i < count; ++i) {
+    const int sp = outer_splits(m, Cs[i]);
+    const int64_t steps = (m + 31) / 32;
+    oj[i] = OuterJob{Pts[i], Qs[i], Cs[i], (int)((steps + sp - 1) / sp), sp, p};
+    rj[i] = RedJob{p, sp, Cs[i], transposes[i], outs[i]};
+    sp_max = sp > sp_max ? sp : sp_max;
+    c_max = Cs[i] > c_max ? Cs[i] : c_max;
+    p += lora_outer_part_bytes(m, Cs[i], r) / sizeof(float);
+  }
+  if (count == 1) oj[1] = oj[0], rj[1] = rj[0];
+  const dim3 grid((unsigned)((c_max + OUT_COLS - 1) / OUT_COLS), (unsigned)sp_max, (unsigned)count);
   const int nt = tiles_of(r);
   switch (nt) {
-    case 1: hipLaunchKernelGGL(k_lora_outer<1>, grid, dim3(256), 0, s, Pt, mp, Q, (int)m, C, sps, part); break;
-    case 2: hipLaunchKernelGGL(k_lora_outer<2>, grid, dim3(256), 0, s, Pt, mp, Q, (int)m, C, sps, part); break;
-    case 3: hipLaunchKernelGGL(k_lora_outer<3>, grid, dim3(256), 0, s, Pt, mp, Q, (int)m, C, sps, part); break;
-    default: hipLaunchKernelGGL(k_lora_outer<4>, grid, dim3(256), 0, s, Pt, mp, Q, (int)m, C, sps, part); break;
+    case 1: hipLaunchKernelGGL(k_lora_outer<1>, grid, dim3(256), 0, s, oj[0], oj[1], mp, (int)m); break;
+    case 2: hipLaunchKernelGGL(k_lora_outer<2>, grid, dim3(256), 0, s, oj[0], oj[1], mp, (int)m); break;
+    case 3: hipLaunchKernelGGL(k_lora_outer<3>, grid, dim3(256), 0, s, oj[0], oj[1], mp, (int)m); break;
+    default: hipLaunchKernelGGL(k_lora_outer<4>, grid, dim3(256), 0, s, oj[0], oj[1], mp, (int)m); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_lora_outer_reduce, dim3((unsigned)((C + RED_COLS - 1) / RED_COLS)), dim3(256), 0, s, part, sp,
-                     16 * nt, (int)r, C, transpose, out);
+  hipLaunchKernelGGL(k_lora_outer_reduce, dim3((unsigned)((c_max + RED_COLS - 1) / RED_COLS), 1, (unsigned)count),
+                     dim3(256), 0, s, rj[0], rj[1], 16 * nt, (int)r);
   return hipGetLastError();
+}
+
+hipError_t launch_lora_outer(const uint16_t* Pt, int64_t mp, int32_t r, const uint16_t* Q, int64_t m,
+                             int64_t C, bool transpose, float* part, float* out, hipStream_t s) {
+  return launch_lora_outer_jobs(1, &Pt, &Q, &C, &transpose, &out, mp, r, m, part, s);
 }
 
 }  // namespace lbq

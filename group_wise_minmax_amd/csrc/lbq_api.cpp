@@ -434,8 +434,9 @@ size_t lbq_lora_bwd_workspace_bytes(const lbq_desc* desc, int64_t m, int32_t r) 
   if (check_desc(desc) != LBQ_OK || m <= 0 || r < 1 || r > 64) return 0;
   const size_t rp = (size_t)round_rank(r);
   const size_t mp = (size_t)round_rows(m);
-  const size_t part = std::max(std::max(lbq::lora_xa_part_bytes(m, desc->n, r), lbq::lora_xa_part_bytes(m, desc->k, r)),
-                               std::max(lbq::lora_outer_part_bytes(m, desc->k, r), lbq::lora_outer_part_bytes(m, desc->n, r)));
+  // the two adapter products run together, then the two outer products
+  const size_t part = std::max(lbq::lora_xa_part_bytes(m, desc->n, r) + lbq::lora_xa_part_bytes(m, desc->k, r),
+                               lbq::lora_outer_part_bytes(m, desc->k, r) + lbq::lora_outer_part_bytes(m, desc->n, r));
   return align16(rp * (size_t)desc->n * 2) + align16((size_t)m * rp * 2) + 2 * align16(rp * mp * 2) + align16(part);
 }
 
@@ -478,14 +479,26 @@ lbq_status lbq_lora_bwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16
   // G = bf16(sigma dY B) row-major for the input gradient and transposed for
   // dA; T = bf16(sigma X A^T) transposed for dB.
   hipError_t e = lbq::launch_transpose_b(B, desc->n, r, rp, Bt, s);
-  if (e == hipSuccess) e = lbq::launch_lora_xa(dY, m, desc->n, Bt, r, rp, sigma, part, G, Gt, mp, s);
-  if (e == hipSuccess) e = lbq::launch_lora_xa(X, m, desc->k, A, r, rp, sigma, part, nullptr, Tt, mp, s);
+  if (e == hipSuccess) {
+    const uint16_t* xs[2] = {dY, X};
+    const int64_t ks[2] = {desc->n, desc->k};
+    const uint16_t* as[2] = {Bt, A};
+    uint16_t* trm[2] = {G, nullptr};
+    uint16_t* ttr[2] = {Gt, Tt};
+    e = lbq::launch_lora_xa_jobs(2, xs, ks, as, trm, ttr, m, r, rp, sigma, part, mp, s);
+  }
   if (e != hipSuccess) return hip_status(e, "lbq_lora_bwd (adapter products)");
   const lbq::LoraDx lora{G, A, r, rp};
   e = lbq::launch_bwd_dx(kind_of(desc), view_of(desc, q), dY, m, dX, lora, nf4_table(), s);
   if (e != hipSuccess) return hip_status(e, "lbq_lora_bwd (input gradient)");
-  e = lbq::launch_lora_outer(Gt, mp, r, X, m, desc->k, false, part, dA, s);
-  if (e == hipSuccess) e = lbq::launch_lora_outer(Tt, mp, r, dY, m, desc->n, true, part, dB, s);
+  {
+    const uint16_t* pts[2] = {Gt, Tt};
+    const uint16_t* qs2[2] = {X, dY};
+    const int64_t cs[2] = {desc->k, desc->n};
+    const bool tr[2] = {false, true};
+    float* outs[2] = {dA, dB};
+    e = lbq::launch_lora_outer_jobs(2, pts, qs2, cs, tr, outs, mp, r, m, part, s);
+  }
   return hip_status(e, "lbq_lora_bwd (adapter gradients)");
 }
 

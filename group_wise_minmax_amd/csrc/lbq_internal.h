@@ -125,9 +125,20 @@ hipError_t launch_lora_xa(const uint16_t* X, int64_t m, int64_t K, const uint16_
 // out = sum over rows t < m of Pt[j][t] * Q[t][c] (Pt [rp][mp], zero past m;
 // Q [m][C], C % 8 == 0), fp32 [r][C], or [C][r] with transpose.  `part`
 // holds lora_outer_part_bytes(m, C, r) bytes.
+// The same for count = 1 or 2 products in one launch pair, jobs[i] = (Xs[i],
+// Ks[i], As[i]) -> (Trms[i], Ttrs[i]); `part` holds the sum of their
+// lora_xa_part_bytes.
+hipError_t launch_lora_xa_jobs(int count, const uint16_t* const* Xs, const int64_t* Ks, const uint16_t* const* As,
+                               uint16_t* const* Trms, uint16_t* const* Ttrs, int64_t m, int32_t r, int32_t rp,
+                               float sigma, float* part, int64_t mp, hipStream_t s);
 size_t lora_outer_part_bytes(int64_t m, int64_t C, int32_t r);
 hipError_t launch_lora_outer(const uint16_t* Pt, int64_t mp, int32_t r, const uint16_t* Q, int64_t m,
                              int64_t C, bool transpose, float* part, float* out, hipStream_t s);
+// The same for count = 1 or 2 outer products in one launch pair; `part` holds
+// the sum of their lora_outer_part_bytes.
+hipError_t launch_lora_outer_jobs(int count, const uint16_t* const* Pts, const uint16_t* const* Qs,
+                                  const int64_t* Cs, const bool* transposes, float* const* outs, int64_t mp,
+                                  int32_t r, int64_t m, float* part, hipStream_t s);
 hipError_t launch_fill_zero_f32(float* p, int64_t count, hipStream_t s);
 
 // Largest m served by the small-batch MFMA kernel.

@@ -1,8 +1,9 @@
 // Low-rank adapter pieces around the frozen quantized weight ("QLoRA技术在量化
 // 微调中的应用", section QLoRA技术原理: the adapters are the only trained
 // parameters and the gradient reaches them through the frozen 4-bit weight;
-// "Making LLMs even more accessible with bitsandbytes, 4-bit quantization and
-// QLoRA", the LoRA forward it describes).  For
+// the bitsandbytes FSDP-QLoRA guide, section 训练 FSDP-QLoRA, step 4 (配置
+// LoRA): a LoraConfig with lora_alpha and rank r on every linear layer, so the
+// adapter term is scaled by lora_alpha / r).  For
 //     Y = X . deq(W)^T + sigma * (X . A^T) . B^T
 // and an output gradient dY:
 //     T  = bf16(sigma * X . A^T)   [m][r]   adapter product (forward and dB)

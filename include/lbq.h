@@ -151,7 +151,10 @@ lbq_status lbq_dequant(const lbq_desc* desc, const lbq_qtensor* q, uint16_t* W_b
 /* Workspace bytes lbq_linear_fwd needs for m rows (0 when none). */
 size_t lbq_linear_workspace_bytes(const lbq_desc* desc, int64_t m);
 
-/* Forward of the frozen low-bit linear layer, Y = X . deq(W)^T:
+/* Forward of the frozen low-bit linear layer, Y = X . deq(W)^T ([BNB]
+ * 通过BitsAndBytesConfig配置: the kernel unpacks the stored 4-bit weight and
+ * dequantizes it to the bf16 compute dtype for the matmul; [GB] 模型量化 for
+ * the INT4 g128 / INT2 g64 MinMax weights the same call multiplies):
  *   Y[i][col(j)] = bf16( sum_k X[i][k] * w_hat[j][k] ),  col(j) = out_rows ?
  *   out_rows[j] : j, with w_hat the dequantized weight and fp32 accumulation.
  * X: bf16 [m][k] (device); Y: bf16 [m][ldy] (device), ldy >= n (or >

@@ -238,6 +238,31 @@ def test_70b_channel_mix_layer(li):
         assert_close(Yh, O.linear_fwd(bf16_rows(X, ms), w_ref), what=f"70b {nm} chmix m={m}")
 
 
+@pytest.mark.parametrize("bits,group", [(4, 128), (2, 64)], ids=["int4", "int2"])
+@pytest.mark.parametrize("li", range(7), ids=NAMES70)
+def test_70b_layer_mix_layer(li, bits, group):
+    """Layer-mix: the whole 70B-shaped linear in one format (every linear all
+    INT4 g128, or all INT2 g64), m = 1 and 1024, sampled rows of codes and
+    metadata bit for bit and sampled outputs against the oracle."""
+    nm = NAMES70[li]
+    n, k = SI.LLAMA3_70B[nm]
+    W = SI.dev_gaussian_weights(SI.seed_of(4, li, SI.SLOT_W), n, k, DEV)
+    qw = L.lbq_quantize(W, "minmax", bits, group)
+    rows = sample(n, 96, 7800 + li + bits)
+    ref = O.quantize(rows_host(W, rows), "minmax", bits=bits, group=group)
+    del W
+    check_minmax_rows(qw, ref, rows, f"70b {nm} int{bits}")
+    cols = torch.from_numpy(rows).to(DEV)
+    for m, seed_off in ((1, 0), (1024, 100)):
+        X = SI.dev_bf16_normal(SI.seed_of(4, li, SI.SLOT_X) + seed_off, (m, k), DEV)
+        Y = L.lbq_linear_fwd(X, qw)
+        ms = np.arange(m) if m == 1 else sample(m, 64, 7900 + li)
+        Yh = bf16_bits_host(Y[torch.from_numpy(ms).to(DEV)][:, cols])
+        assert_close(Yh, O.linear_fwd(bf16_rows(X, ms), ref["w_exact"]), what=f"70b {nm} int{bits} m={m}")
+    del qw
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------------------
 # Qwen1.5-110B-shaped layer, INT2 g64, heavy-tailed weights: quantize the whole
 # layer, GEMV m=1, GEMM m=512

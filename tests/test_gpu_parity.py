@@ -681,3 +681,76 @@ def test_packed_bytes_survive_a_bf16_storage(L, fmtspec):
     moved = L.QuantizedWeight(qw.desc, as_bf16.view(torch.uint8), qw.scales, qw.zeros, qw.absmax, qw.absmax_q,
                               qw.absmax_scale)
     assert torch.equal(L.lbq_dequant(moved).view(torch.int16), L.lbq_dequant(qw).view(torch.int16))
+
+
+# ------------------------------------------------------------------ exact ties
+# The rounding rules on inputs built to sit exactly on them (tests/tie_inputs.py):
+# half-integer code, zero-point and double-quant quotients (round half to
+# even) and NF4 values on a midpoint (the lower code).  The HIP quantizer must
+# match the oracle and the exact-arithmetic expectation bit for bit.
+import tie_inputs as TI
+
+
+@pytest.mark.parametrize("bits,group", [(4, 128), (2, 64), (4, 64), (2, 128)],
+                         ids=["i4g128", "i2g64", "i4g64", "i2g128"])
+def test_quantize_minmax_ties_bitexact(L, bits, group):
+    W, want = TI.minmax_tie_groups(bits, group)
+    W = np.tile(W, (1, 2))  # two groups per row: the ties sit in both
+    qw, ref = _quant_pair(L, W, "minmax", bits, group, False)
+    wb = L.lbq_dequant(qw)
+    torch.cuda.synchronize()
+    check_quantized_equal(qw, ref, "minmax")
+    assert np.array_equal(ref["codes"], np.tile(want["codes"], (1, 2)))
+    assert np.array_equal(ref["zeros"], np.tile(want["zeros"], (1, 2)))
+    assert np.array_equal(bf16_bits_host(wb), ref["w_bf16"])
+
+
+def test_quantize_double_quant_ties_bitexact(L):
+    """Blocks whose absmax values make every a / c2 an exact half-integer (or
+    an integer): the int8 codes take the even neighbour."""
+    a, want = TI.dq_tie_absmax(nblocks=512)
+    W = np.zeros((512, 64), dtype=np.float32)
+    W[np.arange(512), np.arange(512) % 64] = a                  # the block's absmax
+    W[np.arange(512), (np.arange(512) + 7) % 64] = -a * np.float32(0.5)
+    W = W.reshape(128, 256)
+    qw, ref = _quant_pair(L, W, "nf4", 4, 64, True)
+    wb = L.lbq_dequant(qw)
+    torch.cuda.synchronize()
+    check_quantized_equal(qw, ref, "nf4", True)
+    assert np.array_equal(ref["absmax_q"], want["absmax_q"])
+    assert np.array_equal(bf16_bits_host(wb), ref["w_bf16"])
+
+
+@pytest.mark.parametrize("dq", [False, True], ids=["nf4", "nf4dq"])
+def test_nf4_power_of_two_blocks_dequant_exact(L, dq):
+    """Entries in {-a, 0, a}, a different per block and lossless under double
+    quantization: the dequantized weight is W itself, bit for bit."""
+    W = TI.nf4_power_of_two_blocks()
+    qw, ref = _quant_pair(L, W, "nf4", 4, 64, dq)
+    wb = L.lbq_dequant(qw)
+    torch.cuda.synchronize()
+    check_quantized_equal(qw, ref, "nf4", dq)
+    assert np.array_equal(bf16_bits_host(wb), SI.to_bf16_bits(W))
+
+
+@pytest.mark.parametrize("fmtspec", FORMATS, ids=FMT_IDS)
+def test_quantize_subnormal_scales_bitexact(L, fmtspec):
+    """Groups whose fp32 scale (or absmax, or second-level scale) is
+    subnormal: the kernels keep denormals, so codes, metadata and the
+    dequantized weight equal the oracle's bit for bit."""
+    fmt, bits, group, dq = fmtspec
+    rng = np.random.default_rng(4242)
+    # rows 0..31 are one double-quant run of 256 blocks (its c2 is subnormal)
+    W = (rng.uniform(-1.0, 1.0, size=(48, 512)) * np.float32(1e-38)).astype(np.float32)
+    W[16:32] *= np.float32(1e-3)            # deep subnormals
+    W[32:] = SI.gaussian_weights(4243, 16, 512)  # normal rows beside them
+    W[40, :64] = np.float32(1e-45)           # the smallest subnormal
+    qw, ref = _quant_pair(L, W, fmt, bits, group, dq)
+    wb = L.lbq_dequant(qw)
+    torch.cuda.synchronize()
+    if fmt == "minmax":
+        assert (ref["scales"] < np.float32(1.1754944e-38)).any()
+    elif dq:
+        assert ref["absmax_scale"][0] < np.float32(1.1754944e-38)
+    check_quantized_equal(qw, ref, fmt, dq)
+    assert np.array_equal(bf16_bits_host(wb), ref["w_bf16"])

@@ -475,3 +475,123 @@ def test_grouped_input_gradient_is_the_adjoint_of_the_shared_forward():
         for c in range(0, 256, 37):
             v = sum(O.bf16_to_f64(d)[a, j] * q["w_exact"][j, c] for d, q in zip(dYs, qs) for j in range(d.shape[1]))
             assert dX[a, c] == v
+
+
+# ---------------------------------------------------------------------------
+# Exact ties.  Random inputs almost never put a quotient exactly on a
+# half-integer or an NF4 value exactly on a midpoint, so the rounding rules
+# are pinned on inputs built to sit on them (tests/tie_inputs.py); the
+# expected integers come from exact rational arithmetic with the tie rule
+# written out.
+# ---------------------------------------------------------------------------
+import tie_inputs as TI
+
+
+def test_round_half_even_reference_rule():
+    from fractions import Fraction as Fr
+    got = [TI.round_half_even(Fr(t, 2)) for t in range(-7, 8)]
+    assert got == [-4, -3, -2, -2, -2, -1, 0, 0, 0, 1, 2, 2, 2, 3, 4]
+    assert TI.round_half_even(Fr(7, 3)) == 2 and TI.round_half_even(Fr(-7, 3)) == -2
+
+
+def test_minmax_ties_literal_cases():
+    """Literal expectations: with s = 2^-4, w = 2.5 s takes code 2 and 3.5 s
+    code 4 (z = 0); -1.5 s takes -2 + z; a zero point at -lo/s = 2.5 is 2."""
+    s = F32(1 / 16)
+    W = np.zeros((2, 128), dtype=F32)
+    W[0, :4] = [0.0, 15 * s, 2.5 * s, 3.5 * s]
+    W[0, 4:] = 15 * s
+    W[1, :4] = [-2.5 * s, 12.5 * s, -1.5 * s, 0.5 * s]
+    W[1, 4:] = 0.0
+    codes, sc, z = O.minmax_quantize(W, 4, 128)
+    assert sc[0, 0] == s and sc[1, 0] == s
+    assert z[0, 0] == 0 and list(codes[0, :4]) == [0, 15, 2, 4]
+    assert z[1, 0] == 2                         # rne(2.5) = 2, not 3
+    assert list(codes[1, :4]) == [0, 14, 0, 2]  # rne(-2.5)+2, rne(12.5)+2, rne(-1.5)+2, rne(0.5)+2
+
+
+@pytest.mark.parametrize("bits,group", CASES)
+def test_minmax_ties_round_half_to_even(bits, group):
+    """Every code tie and every zero-point tie resolves to the even integer."""
+    W, want = TI.minmax_tie_groups(bits, group)
+    codes, s, z = O.minmax_quantize(W, bits, group)
+    assert np.array_equal(s, want["scales"])
+    assert np.array_equal(z, want["zeros"])
+    assert np.array_equal(codes, want["codes"])
+
+
+def test_double_quant_ties_round_half_to_even():
+    a, want = TI.dq_tie_absmax()
+    q2, c2 = O.double_quant(a, 256)
+    assert np.array_equal(c2.view(np.uint32), want["absmax_scale"].view(np.uint32))
+    assert np.array_equal(q2, want["absmax_q"])
+    from fractions import Fraction as Fr
+    # literal: a = 2.5 c2 -> 2, a = 3.5 c2 -> 4, a = 0.5 c2 -> 0
+    lit = np.zeros(256, dtype=F32)
+    lit[0] = F32(127 / 1024)
+    lit[1:4] = [2.5 / 1024, 3.5 / 1024, 0.5 / 1024]
+    q, c = O.double_quant(lit, 256)
+    assert c[0] == F32(1 / 1024) and list(q[1:4]) == [2, 4, 0]
+    assert TI.round_half_even(Fr(5, 2)) == 2
+
+
+@pytest.mark.parametrize("scale_exp", [0, -3, 5])
+def test_nf4_midpoint_ties_take_the_lower_code(scale_exp):
+    """x exactly on midpoint m_i gives code i (a plain count of the midpoints
+    strictly below x); one fp32 step above gives i + 1."""
+    mids = O.nf4_midpoints(O.nf4_codebook())
+    W, xs = TI.nf4_midpoint_blocks(mids, scale_exp)
+    codes, a = O.nf4_quantize(W, 64)
+    assert np.all(a == F32(2.0 ** scale_exp))
+    for r in range(xs.shape[0]):
+        for c in range(64):
+            x = float(xs[r, c])
+            want = 0
+            for m in mids:
+                if x > float(m):
+                    want += 1
+            assert codes[r, c] == want, (r, c, x, want, codes[r, c])
+    for i, m in enumerate(mids):
+        one = np.zeros((1, 64), dtype=F32)
+        one[0, 0] = 1.0
+        one[0, 1] = m
+        one[0, 2] = np.nextafter(m, F32(2))
+        c1, _ = O.nf4_quantize(one, 64)
+        assert c1[0, 1] == i and c1[0, 2] == i + 1
+
+
+@pytest.mark.parametrize("dq", [False, True])
+def test_nf4_dequant_bf16_power_of_two_blocks(dq):
+    """Blocks in {-a, 0, a} with a different a per block: the codes are 0, 7,
+    15, double quantization is lossless on these a, and the dequantized bf16
+    weight equals W exactly (checked against torch's conversion of W); an
+    absmax read from the wrong block would change the value."""
+    W = TI.nf4_power_of_two_blocks()
+    ref = O.quantize(W, "nf4", double_quant_on=dq)
+    assert set(np.unique(ref["codes"])) <= {0, 7, 15}
+    expect = SI.to_bf16_bits(W)
+    assert np.array_equal(O.bf16_to_f64(expect), W.astype(np.float64))
+    assert np.array_equal(ref["w_bf16"], expect)
+    ahat = ref["absmax_hat"] if dq else ref["absmax"]
+    assert np.array_equal(O.nf4_dequant_bf16(ref["codes"], ahat, 64), expect)
+    assert np.array_equal(ref["w_exact"], W.astype(np.float64))
+    if dq:
+        assert np.array_equal(ref["absmax_hat"], np.abs(W).reshape(-1, 64).max(1))
+
+
+def test_minmax_dequant_bf16_per_group_scales():
+    """Groups with a different power-of-two scale each: the dequantized bf16
+    weight is W exactly; a scale or zero point read from another group would
+    change it."""
+    rng = np.random.default_rng(31)
+    n, k, g = 6, 512, 128
+    W = np.zeros((n, k), dtype=F32)
+    for r in range(n):
+        for j in range(k // g):
+            z = int(rng.integers(0, 16))
+            e = 3 + (r * (k // g) + j) % 9
+            lv = rng.integers(0, 16, size=g)
+            lv[0], lv[1] = 0, 15
+            W[r, j * g:(j + 1) * g] = ((lv - z) * 2.0 ** -e).astype(F32)
+    codes, s, z = O.minmax_quantize(W, 4, g)
+    assert np.array_equal(O.minmax_dequant_bf16(codes, s, z, g), SI.to_bf16_bits(W))

@@ -241,6 +241,25 @@ def lbq_linear_fwd(X: torch.Tensor, qw: QuantizedWeight, out: Optional[torch.Ten
     return out
 
 
+def lbq_linear_fwd_noalloc(X: torch.Tensor, qw: QuantizedWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``lbq_linear_fwd`` without a workspace (see ``lbq_linear_fwd_noalloc`` in
+    lbq.h): the library's own per-device scratch array holds the partial sums."""
+    _need(X, "X", torch.bfloat16)
+    m = X.shape[0]
+    if X.dim() != 2 or X.shape[1] != qw.k:
+        raise ValueError(f"X must be [m, {qw.k}]")
+    if out is None:
+        if qw.out_rows is not None:
+            raise ValueError("out must be given when out_rows is set")
+        out = torch.empty((m, qw.n), dtype=torch.bfloat16, device=X.device)
+    if out.dtype != torch.bfloat16 or out.dim() != 2 or out.shape[0] != m or out.stride(1) != 1:
+        raise ValueError("out must be bf16 [m, >=n] with unit column stride")
+    q = qw.qtensor()
+    check(lib.lbq_linear_fwd_noalloc(ctypes.byref(qw.desc), ctypes.byref(q), X.data_ptr(), m, out.data_ptr(),
+                                     out.stride(0), _stream(X.device)), "lbq_linear_fwd_noalloc")
+    return out
+
+
 def lbq_linear_fwd_grouped_workspace_bytes(qws, m: int) -> int:
     descs = (Desc * len(qws))(*[q.desc for q in qws])
     return lib.lbq_linear_fwd_grouped_workspace_bytes(len(qws), descs, m)

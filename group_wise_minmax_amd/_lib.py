@@ -23,7 +23,7 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 EXPORTED = (
     "lbq_layout", "lbq_quantize", "lbq_dequant", "lbq_linear_workspace_bytes",
-    "lbq_linear_fwd", "lbq_linear_fwd_grouped_workspace_bytes", "lbq_linear_fwd_grouped",
+    "lbq_linear_fwd", "lbq_linear_fwd_noalloc", "lbq_linear_fwd_grouped_workspace_bytes", "lbq_linear_fwd_grouped",
     "lbq_linear_bwd_dx", "lbq_linear_bwd_dx_grouped", "lbq_lora_workspace_bytes", "lbq_lora_fwd",
     "lbq_lora_bwd_workspace_bytes", "lbq_lora_bwd",
     "lbq_serialized_bytes", "lbq_serialize", "lbq_blob_desc", "lbq_deserialize",
@@ -70,6 +70,7 @@ def _load() -> ctypes.CDLL:
         "lbq_dequant": (I32, [DP, QP, P, P]),
         "lbq_linear_workspace_bytes": (SZ, [DP, I64]),
         "lbq_linear_fwd": (I32, [DP, QP, P, I64, P, I64, P, SZ, P]),
+        "lbq_linear_fwd_noalloc": (I32, [DP, QP, P, I64, P, I64, P]),
         "lbq_linear_fwd_grouped_workspace_bytes": (SZ, [I32, DP, I64]),
         "lbq_linear_fwd_grouped": (I32, [I32, DP, QP, P, I64, ctypes.POINTER(P), ctypes.POINTER(I64), P, SZ, P]),
         "lbq_linear_bwd_dx": (I32, [DP, QP, P, I64, P, P]),

@@ -233,6 +233,35 @@ lbq_status check_bwd_common(const lbq_desc* desc, const lbq_qtensor* q, const ui
 
 }  // namespace
 
+namespace lbq {
+
+// Shared with the allocation-free forward (k_noalloc.hip): records the
+// detail of a failure for lbq_last_error_detail().
+lbq_status set_error(lbq_status s, const char* what) { return fail(s, "%s", what); }
+
+lbq_status check_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X, int64_t m, uint16_t* Y,
+                     int64_t ldy) {
+  return check_fwd_common(desc, q, X, m, Y, ldy);
+}
+
+// The forward of lbq_linear_fwd once the arguments have passed check_fwd:
+// the workspace check and the dispatch.
+lbq_status linear_fwd_body(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X, int64_t m,
+                           uint16_t* Y, int64_t ldy, void* workspace, size_t ws_bytes, void* stream,
+                           const char* who) {
+  if (m == 0) return ok();
+  const size_t need = fwd_workspace(desc, m, false);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
+    return fail(LBQ_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  if (need > 0 && !aligned(workspace, 16)) return fail(LBQ_E_ALIGN, "workspace must be 16-byte aligned");
+  const lbq::LoraEpi none{nullptr, nullptr, 0, 0};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const lbq::WView w = view_of(desc, q);
+  return hip_status(dispatch_fwd(desc, w, X, m, Y, ldy, q->out_rows, none, workspace, s), who);
+}
+
+}  // namespace lbq
+
 extern "C" {
 
 lbq_status lbq_layout(const lbq_desc* desc, lbq_sizes* out) {
@@ -281,17 +310,9 @@ size_t lbq_linear_workspace_bytes(const lbq_desc* desc, int64_t m) {
 lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X,
                           int64_t m, uint16_t* Y, int64_t ldy, void* workspace, size_t ws_bytes,
                           void* stream) {
-  lbq_status st = check_fwd_common(desc, q, X, m, Y, ldy);
-  if (st != LBQ_OK || m == 0) return st == LBQ_OK ? ok() : st;
-  const size_t need = fwd_workspace(desc, m, false);
-  if (need > 0 && (workspace == nullptr || ws_bytes < need))
-    return fail(LBQ_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
-  if (need > 0 && !aligned(workspace, 16)) return fail(LBQ_E_ALIGN, "workspace must be 16-byte aligned");
-  const lbq::LoraEpi none{nullptr, nullptr, 0, 0};
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const lbq::WView w = view_of(desc, q);
-  return hip_status(dispatch_fwd(desc, w, X, m, Y, ldy, q->out_rows, none, workspace, s),
-                    "lbq_linear_fwd");
+  const lbq_status st = check_fwd_common(desc, q, X, m, Y, ldy);
+  if (st != LBQ_OK) return st;
+  return lbq::linear_fwd_body(desc, q, X, m, Y, ldy, workspace, ws_bytes, stream, "lbq_linear_fwd");
 }
 
 // Weights of one kind in a grouped call run as one launch (one launch pair

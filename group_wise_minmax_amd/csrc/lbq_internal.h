@@ -145,3 +145,22 @@ hipError_t launch_fill_zero_f32(float* p, int64_t count, hipStream_t s);
 constexpr int64_t kSkinnyMaxM = 64;
 
 }  // namespace lbq
+
+// C-ABI helpers shared between lbq_api.cpp and the allocation-free forward
+// (k_noalloc.hip); the types come from include/lbq.h.
+#include "lbq.h"
+
+namespace lbq {
+
+// Records `what` as the detail of the calling thread's last failure; returns s.
+lbq_status set_error(lbq_status s, const char* what);
+// Argument checks of lbq_linear_fwd (everything but the workspace).
+lbq_status check_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X, int64_t m, uint16_t* Y,
+                     int64_t ldy);
+// lbq_linear_fwd after check_fwd: workspace check and dispatch (`who` names
+// the entry point in error details).
+lbq_status linear_fwd_body(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X, int64_t m,
+                           uint16_t* Y, int64_t ldy, void* workspace, size_t ws_bytes, void* stream,
+                           const char* who);
+
+}  // namespace lbq

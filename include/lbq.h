@@ -174,6 +174,26 @@ lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint
                           int64_t m, uint16_t* Y, int64_t ldy, void* workspace,
                           size_t ws_bytes, void* stream);
 
+/* Scratch memory, per device, of lbq_linear_fwd_noalloc: 16 MiB. */
+#define LBQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* For callers that cannot allocate device memory (work captured into a HIP
+ * graph, tight serving loops, harnesses that forbid hipMalloc): the forward
+ * of lbq_linear_fwd, the same kernels and the same results bit for bit, with
+ * no workspace argument.  The only scratch memory the forward uses (the fp32
+ * K-split partial sums of the small-batch kernel, 2 <= m <= 64) lives in an
+ * array of LBQ_NOALLOC_SCRATCH_BYTES in the library's device image, one per
+ * device, held until the process ends; the call allocates and frees nothing.
+ * Arguments, layouts and errors as lbq_linear_fwd; LBQ_E_WORKSPACE when the
+ * call would need more scratch than the array holds (no shape with m <= 64
+ * does: at most 16.75 MB).  The array's device address is looked up on the
+ * first call on a device that needs it; that call uses the current device
+ * (which must be the stream's).  Every call on a device shares that device's
+ * array: calls that overlap on one device (two streams or two host threads)
+ * race and must be serialized by the caller. */
+lbq_status lbq_linear_fwd_noalloc(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X,
+                                  int64_t m, uint16_t* Y, int64_t ldy, void* stream);
+
 /* Largest count accepted by lbq_linear_fwd_grouped. */
 #define LBQ_MAX_GROUP 8
 

@@ -377,3 +377,142 @@ def rel_errors(Y: np.ndarray, Y_ref: np.ndarray):
     fro = math.sqrt(float((d * d).sum())) / nref if nref > 0 else math.sqrt(float((d * d).sum()))
     mx = float(np.abs(d).max()) / mref if mref > 0 else float(np.abs(d).max()) if d.size else 0.0
     return fro, mx
+
+
+# --------------------------------------------------------------------------
+# Format variants: compact MinMax metadata, and double quantization with an
+# offset.  Neither is spelled out on the pages; each function states the
+# reading it implements.
+# --------------------------------------------------------------------------
+
+
+def fp16_round_up(s) -> np.ndarray:
+    """The smallest fp16 value >= s for positive fp32 s (round toward +inf),
+    saturating at the largest finite fp16, 65504."""
+    s = np.asarray(s, dtype=F32)
+    with np.errstate(over="ignore"):                # values above 65504 saturate below
+        h = s.astype(np.float16)                   # round to nearest-even
+        below = h.astype(F32) < s
+        h = np.where(below, np.nextafter(h, np.float16(np.inf)), h).astype(np.float16)
+    return np.minimum(h, np.float16(65504.0))
+
+
+def minmax_quantize_compact(W: np.ndarray, bits: int, group: int):
+    """Group-wise MinMax RTN ([GB] §模型量化) with compact metadata: an fp16
+    scale and the integer zero point, both derived from the stored scale.
+
+    Returns (codes u8[N,K], scales f16[N,K/g], zeros u8[N,K/g]).
+      lo, hi, s32 as in :func:`minmax_quantize` (s32 := 1 if it comes out 0);
+      s  = fp16_round_up(s32)    (rounding up keeps Qmax * s >= hi - lo)
+      z  = clamp(rne(fl(-lo / s)), 0, Qmax)
+      q  = clamp(rne(fl(w / s)) + z, 0, Qmax)
+    """
+    W = np.ascontiguousarray(W, dtype=F32)
+    N, K = W.shape
+    assert K % group == 0
+    qmax = (1 << bits) - 1
+    Wg = W.reshape(N, K // group, group)
+    lo = np.minimum(F32(0.0), Wg.min(axis=2))
+    hi = np.maximum(F32(0.0), Wg.max(axis=2))
+    s32 = (hi - lo) / F32(qmax)
+    s32 = np.where(s32 == F32(0.0), F32(1.0), s32).astype(F32)
+    s16 = fp16_round_up(s32)
+    s = s16.astype(F32)
+    z = np.clip(np.rint(-lo / s), 0, qmax).astype(np.int32)
+    r = np.rint(Wg / s[:, :, None]).astype(np.int32)
+    q = np.clip(r + z[:, :, None], 0, qmax)
+    return q.reshape(N, K).astype(np.uint8), s16, z.astype(np.uint8)
+
+
+def fp32_tree_sum(a) -> np.float32:
+    """Sum of fp32 values over the binary tree of adjacent pairs in index
+    order: the array is padded with zeros to a power of two and each level
+    adds elements 2i and 2i+1 with one fp32 addition."""
+    v = np.asarray(a, dtype=F32).ravel()
+    size = 1
+    while size < v.shape[0]:
+        size *= 2
+    v = np.concatenate([v, np.zeros(size - v.shape[0], dtype=F32)])
+    while v.shape[0] > 1:
+        v = (v[0::2] + v[1::2]).astype(F32)
+    return F32(v[0]) if v.shape[0] else F32(0.0)
+
+
+def absmax_offset(absmax) -> np.float32:
+    """Per-tensor offset of double quantization with an offset: the mean of
+    the absmax values, fp32(fp64(tree sum) / nb).  ([QL] §结论 says double
+    quantization re-quantizes the scale factor and the offset; [BNB] §源码纵深
+    lists `offset` among the quantization-state fields.)"""
+    a = np.asarray(absmax, dtype=F32)
+    return F32(np.float64(fp32_tree_sum(a)) / np.float64(a.shape[0]))
+
+
+def double_quant_offset(absmax: np.ndarray, block: int = 256):
+    """Double quantization with an offset: the absmax values minus their
+    per-tensor mean are quantized to symmetric int8 codes in blocks of
+    ``block`` consecutive values with an fp32 scale per block:
+      off = absmax_offset(A);  d = fl(A - off)
+      c2  = fl(max |d| / 127);  q2 = clamp(rne(fl(d / c2)), -127, 127)  (0 if c2 == 0)
+    Returns (absmax_q i8[nb], absmax_scale f32[ceil(nb/block)], offset f32)."""
+    a = np.asarray(absmax, dtype=F32)
+    nb = a.shape[0]
+    off = absmax_offset(a)
+    d = (a - off).astype(F32)
+    nblk = -(-nb // block)
+    q2 = np.zeros(nb, dtype=np.int8)
+    c2 = np.zeros(nblk, dtype=F32)
+    for b in range(nblk):
+        seg = d[b * block:(b + 1) * block]
+        c = np.abs(seg).max() / F32(127.0)
+        c2[b] = c
+        if c != F32(0.0):
+            q2[b * block:(b + 1) * block] = np.clip(np.rint(seg / c), -127, 127).astype(np.int8)
+    return q2, c2, off
+
+
+def double_dequant_absmax_offset(absmax_q, absmax_scale, offset, block: int = 256) -> np.ndarray:
+    """fp32 A_hat = fl(fl(q2 * c2) + offset)."""
+    q2 = np.asarray(absmax_q, dtype=np.int8).astype(F32)
+    c2 = np.repeat(np.asarray(absmax_scale, dtype=F32), block)[: q2.shape[0]]
+    return ((q2 * c2).astype(F32) + F32(offset)).astype(F32)
+
+
+def quantize_variant(W: np.ndarray, variant: str) -> dict:
+    """Every stored array of a format variant, plus ``w_exact`` (fp64) and
+    ``w_bf16`` like :func:`quantize`.
+      'i4g128c', 'i2g64c': MinMax with compact metadata; ``scales`` f16,
+          ``zeros`` u8 unpacked and ``zeros_packed`` (zero points packed like
+          the codes, row by row);
+      'nf4dqo': NF4 with double quantization with an offset; ``absmax_q``
+          i8, ``absmax_scale`` f32 with the offset appended as one more entry.
+    """
+    out: dict = {}
+    if variant in ("i4g128c", "i2g64c"):
+        bits, group = (4, 128) if variant == "i4g128c" else (2, 64)
+        codes, s16, z = minmax_quantize_compact(W, bits, group)
+        s = s16.astype(F32)
+        out.update(codes=codes, scales=s16, zeros=z, zeros_packed=pack_codes(z, bits),
+                   packed=pack_codes(codes, bits))
+        out["w_exact"] = minmax_exact(codes, s, z, group)
+        out["w_bf16"] = minmax_dequant_bf16(codes, s, z, group)
+    elif variant == "nf4dqo":
+        codes, a = nf4_quantize(W, 64)
+        q2, c2, off = double_quant_offset(a, 256)
+        ahat = double_dequant_absmax_offset(q2, c2, off, 256)
+        out.update(codes=codes, packed=pack_codes(codes, 4), absmax=a, absmax_q=q2,
+                   absmax_scale=np.concatenate([c2, np.array([off], dtype=F32)]), absmax_hat=ahat)
+        out["w_exact"] = nf4_exact(codes, ahat, 64)
+        out["w_bf16"] = nf4_dequant_bf16(codes, ahat, 64)
+    else:
+        raise ValueError(variant)
+    return out
+
+
+def variant_bits_per_param(variant: str, n: int, k: int) -> float:
+    """Stored bits per weight of a format variant, from the byte counts."""
+    if variant in ("i4g128c", "i2g64c"):
+        bits, group = (4, 128) if variant == "i4g128c" else (2, 64)
+        g = k // group
+        return 8.0 * (n * k * bits // 8 + n * g * 2 + n * g * bits // 8) / (n * k)
+    nb = n * k // 64
+    return 8.0 * (n * k // 2 + nb + 4 * (-(-nb // 256) + 1)) / (n * k)

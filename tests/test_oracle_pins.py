@@ -595,3 +595,199 @@ def test_minmax_dequant_bf16_per_group_scales():
             W[r, j * g:(j + 1) * g] = ((lv - z) * 2.0 ** -e).astype(F32)
     codes, s, z = O.minmax_quantize(W, 4, g)
     assert np.array_equal(O.minmax_dequant_bf16(codes, s, z, g), SI.to_bf16_bits(W))
+
+
+# ---------------------------------------------------------------------------
+# Format variants: compact MinMax metadata (fp16 scale rounded up, packed
+# zero point) and double quantization with a per-tensor offset.
+# ---------------------------------------------------------------------------
+
+def _all_fp16_positive():
+    """Every positive finite fp16 value, ascending, as fp64 (enumerated from
+    the 16-bit patterns, independent of any rounding routine)."""
+    bits = np.arange(1, 0x7C00, dtype=np.uint16)
+    return bits.view(np.float16).astype(np.float64)
+
+
+def test_fp16_round_up_is_smallest_fp16_not_below():
+    table = _all_fp16_positive()
+    rng = np.random.default_rng(300)
+    s = np.concatenate([
+        np.exp(rng.uniform(np.log(1e-9), np.log(6e4), 20000)).astype(F32),
+        table[:2000].astype(F32), table[-2000:].astype(F32),                 # exact fp16 values stay
+        np.nextafter(table[100:3000].astype(F32), F32(np.inf)),              # just above: next one up
+        np.array([1e-30, 5.9604645e-08, 65504.0, 65505.0, 1e6], dtype=F32),
+    ]).astype(F32)
+    got = O.fp16_round_up(s).astype(np.float64)
+    idx = np.searchsorted(table, s.astype(np.float64), side="left")
+    want = np.where(idx < table.size, table[np.minimum(idx, table.size - 1)], 65504.0)
+    assert np.array_equal(got, want)
+    assert O.fp16_round_up(F32(1e-30)) == np.float16(2.0 ** -24)
+    assert O.fp16_round_up(F32(1e6)) == np.float16(65504.0)
+
+
+@pytest.mark.parametrize("bits,group", [(4, 128), (2, 64)])
+def test_minmax_compact_codes_nearest_level_and_range(bits, group):
+    """With the stored fp16 scale and zero point, every code is the nearest
+    level (exhaustive fp64 search, near-ties excused); the stored scale is
+    the fp32 scale rounded up, so Qmax * s covers the group's range."""
+    qmax = (1 << bits) - 1
+    W = np.concatenate([SI.gaussian_weights(310, 48, 4 * group, outlier_seed=311),
+                        SI.student_t_weights(312, 16, 4 * group)])
+    codes, s16, z = O.minmax_quantize_compact(W, bits, group)
+    _, s32, _ = O.minmax_quantize(W, bits, group)
+    s = s16.astype(np.float64)
+    assert np.all(s >= s32) and np.all(s <= s32.astype(np.float64) * (1 + 2.0 ** -10))
+    N, K = W.shape
+    w = W.astype(np.float64).reshape(N, K // group, group)
+    span = np.maximum(0, w.max(-1)) - np.minimum(0, w.min(-1))
+    assert np.all(qmax * s >= span * (1 - 2.0 ** -22))
+    levels = (np.arange(qmax + 1)[None, None, :] - z.astype(np.float64)[:, :, None]) * s[:, :, None]
+    dist = np.abs(w[..., None] - levels[:, :, None, :])
+    best = dist.argmin(-1)
+    srt = np.sort(dist, -1)
+    near = (srt[..., 1] - srt[..., 0]) <= 4 * _f32_ulp(w) + 1e-300
+    assert not ((best != codes.reshape(best.shape)) & ~near).any()
+    err = np.abs(w - (codes.reshape(w.shape).astype(np.float64) - z[:, :, None]) * s[:, :, None])
+    assert np.all(err <= s[:, :, None] * (0.5 + 2.0 ** -18))
+
+
+def test_minmax_compact_literal_and_power_of_two_cases():
+    """A scale that fp16 holds exactly (2^-4) gives the fp32-metadata result
+    bit for bit, ties included; s32 = 0.9/15 = 0.06 is stored as the fp16
+    value just above it."""
+    for bits, group in [(4, 128), (2, 64)]:
+        W, want = TI.minmax_tie_groups(bits, group)
+        codes, s16, z = O.minmax_quantize_compact(W, bits, group)
+        assert np.all(s16 == np.float16(1 / 16))
+        assert np.array_equal(codes, want["codes"]) and np.array_equal(z, want["zeros"])
+    W = np.zeros((1, 128), dtype=F32)
+    W[0, 0], W[0, 1] = F32(0.9), F32(-0.0)
+    codes, s16, z = O.minmax_quantize_compact(W, 4, 128)
+    table = _all_fp16_positive()
+    s32 = F32(0.9) / F32(15)
+    assert float(s16[0, 0]) == table[np.searchsorted(table, float(s32))] and float(s16[0, 0]) > float(s32)
+    assert z[0, 0] == 0 and codes[0, 0] == 15 and codes[0, 1] == 0
+
+
+@pytest.mark.parametrize("variant,bits", [("i4g128c", 4), ("i2g64c", 2)])
+def test_compact_variant_arrays_and_bits_per_param(variant, bits):
+    W = SI.gaussian_weights(320, 16, 1024)
+    r = O.quantize_variant(W, variant)
+    assert np.array_equal(O.unpack_codes(r["zeros_packed"], bits), r["zeros"])
+    assert r["scales"].dtype == np.float16 and r["zeros_packed"].shape[1] * 8 == r["zeros"].shape[1] * bits
+    expect = {"i4g128c": 4 + 16 / 128 + 4 / 128, "i2g64c": 2 + 16 / 64 + 2 / 64}[variant]
+    assert expect == (4.15625 if bits == 4 else 2.28125)
+    for n, k in list(SI.LLAMA3_8B.values()) + list(SI.QWEN15_110B.values()):
+        assert O.variant_bits_per_param(variant, n, k) == expect
+    got_bytes = r["packed"].nbytes + r["scales"].nbytes + r["zeros_packed"].nbytes
+    assert 8.0 * got_bytes / W.size == expect
+    assert np.array_equal(r["w_exact"], O.minmax_exact(r["codes"], r["scales"].astype(F32), r["zeros"],
+                                                        128 if bits == 4 else 64))
+
+
+def _tree_sum_recursive(a):
+    """Brute-force reference of the adjacent-pair tree: split the zero-padded
+    power-of-two range in halves, recursively, one fp32 addition per node."""
+    n = 1
+    while n < len(a):
+        n *= 2
+    v = [F32(x) for x in a] + [F32(0.0)] * (n - len(a))
+
+    def rec(lo, hi):
+        if hi - lo == 1:
+            return v[lo]
+        mid = (lo + hi) // 2
+        return F32(rec(lo, mid) + rec(mid, hi))
+    return rec(0, n) if n else F32(0.0)
+
+
+def test_fp32_tree_sum():
+    assert O.fp32_tree_sum(np.array([2.0 ** 24, 1, 1, 1], dtype=F32)) == F32(2.0 ** 24 + 2)  # a running sum gives 2^24
+    rng = np.random.default_rng(330)
+    for n in (1, 2, 3, 5, 8, 100, 255, 256, 257, 300):
+        a = np.abs(rng.standard_normal(n)).astype(F32) * F32(10.0) ** rng.integers(-6, 6, n).astype(F32)
+        assert O.fp32_tree_sum(a) == _tree_sum_recursive(a)
+        ints = rng.integers(0, 1000, n).astype(F32)
+        assert O.fp32_tree_sum(ints) == F32(int(ints.astype(np.int64).sum()))
+    assert O.absmax_offset(np.array([1, 2, 3, 4], dtype=F32)) == F32(2.5)
+    assert O.absmax_offset(np.full(1000, 0.375, dtype=F32)) == F32(0.375)
+
+
+def _offset_tie_absmax(runs=2):
+    """Absmax values in adjacent pairs 0.5 + t, 0.5 - t (each pair sums to 1
+    exactly, so the mean is 0.5), t = (j + 1/2) / 1024 or j / 1024 with
+    max t = 127/1024 in every run of 256: c2 = 2^-10 and d / c2 = +-(j + 1/2)."""
+    from fractions import Fraction as Fr
+    a, want = [], []
+    for r in range(runs):
+        for p in range(128):
+            t = Fr(127, 1024) if p == 0 else (Fr(2 * ((5 * p) % 127) + 1, 2048) if p % 2 else Fr((3 * p) % 128, 1024))
+            for sgn in (1, -1):
+                a.append(F32(float(Fr(1, 2) + sgn * t)))
+                assert Fr(float(a[-1])) == Fr(1, 2) + sgn * t
+                want.append(TI.round_half_even(sgn * t * 1024))
+    return np.array(a, dtype=F32), np.array(want, dtype=np.int8)
+
+
+def test_double_quant_offset_ties_and_literal():
+    a, want = _offset_tie_absmax()
+    q2, c2, off = O.double_quant_offset(a, 256)
+    assert off == F32(0.5) and np.all(c2 == F32(2.0 ** -10))
+    assert np.array_equal(q2, want)
+    assert (q2 < 0).any() and q2.min() == -127 and q2.max() == 127
+    lit = np.array([0.5 + 127 / 1024, 0.5 - 127 / 1024, 0.5 + 2.5 / 1024, 0.5 - 2.5 / 1024], dtype=F32)
+    q, c, o = O.double_quant_offset(np.tile(lit, 64), 256)
+    assert o == F32(0.5) and list(q[:4]) == [127, -127, 2, -2]
+
+
+def test_double_quant_offset_nearest_and_bound():
+    rng = np.random.default_rng(340)
+    a = (np.abs(rng.standard_normal(2000)) * 0.03 + 0.01).astype(F32)
+    q2, c2, off = O.double_quant_offset(a, 256)
+    q2p, c2p = O.double_quant(a, 256)
+    assert np.all(c2.astype(np.float64) <= c2p.astype(np.float64) * (1 + 2.0 ** -20))
+    d = (a - off).astype(np.float64)
+    assert abs(float(off) - float(np.mean(a.astype(np.float64)))) <= 1e-6 * float(np.mean(a))
+    for b in range(len(c2)):
+        seg = d[b * 256:(b + 1) * 256]
+        lv = np.arange(-127, 128) * np.float64(c2[b])
+        dist = np.abs(seg[:, None] - lv)
+        best = dist.argmin(1) - 127
+        srt = np.sort(dist, 1)
+        near = (srt[:, 1] - srt[:, 0]) <= 4 * _f32_ulp(a[b * 256:(b + 1) * 256]) + 1e-300
+        assert not ((best != q2[b * 256:(b + 1) * 256]) & ~near).any()
+        assert np.abs(q2[b * 256:(b + 1) * 256]).max() == 127
+    ah = O.double_dequant_absmax_offset(q2, c2, off, 256).astype(np.float64)
+    bound = 0.5 * np.repeat(c2, 256)[:2000] * (1 + 2.0 ** -20) + 2 * _f32_ulp(a)
+    assert np.all(np.abs(ah - a) <= bound)
+
+
+def test_nf4dqo_lossless_blocks_dequant_exact():
+    """Block entries in {-A, 0, A} with absmax values that the offset
+    variant reproduces exactly: the dequantized weight is W (fp32) exactly
+    and its bf16 rounding equals torch's; the 4-bit codes equal those of
+    plain NF4 (they come from the un-quantized absmax)."""
+    a, _ = _offset_tie_absmax()
+    # lossless: integer t, keep pairs; replace the half-integer ones by integers
+    a = np.where(np.abs((a.astype(np.float64) - 0.5) * 1024 % 1) > 0, F32(0.5), a).astype(F32)
+    rng = np.random.default_rng(350)
+    blocks = np.zeros((a.size, 64), dtype=F32)
+    for b in range(a.size):
+        pat = rng.integers(-1, 2, 64)
+        pat[rng.integers(0, 64)] = 1
+        blocks[b] = pat * a[b]
+    W = blocks.reshape(-1, 256)
+    r = O.quantize_variant(W, "nf4dqo")
+    assert np.array_equal(r["absmax_hat"], a)
+    assert np.array_equal(r["w_exact"], W.astype(np.float64))
+    assert np.array_equal(r["w_bf16"], SI.to_bf16_bits(W))
+    assert np.array_equal(r["codes"], O.quantize(W, "nf4", double_quant_on=False)["codes"])
+    assert r["absmax_scale"][-1] == F32(0.5) and r["absmax_scale"].shape == (a.size // 256 + 1,)
+
+
+def test_nf4dqo_bits_per_param():
+    """NF4 + double quantization costs 4.126953125 bit/param on these shapes
+    (0.5 - 0.373046875 bits over the codes); the offset adds one fp32 per tensor."""
+    for n, k in SI.LLAMA3_8B.values():
+        assert O.variant_bits_per_param("nf4dqo", n, k) == 4.126953125 + 32.0 / (n * k)

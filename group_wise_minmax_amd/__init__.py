@@ -24,7 +24,7 @@ from typing import Optional
 
 import torch
 
-from ._lib import (LBQ_MAX_GROUP, LBQ_MINMAX, LBQ_NF4, Desc, LbqError, QTensor, Sizes, check, lib,  # noqa: F401
+from ._lib import (LBQ_MAX_GROUP, LBQ_META_COMPACT, LBQ_META_F32, LBQ_MINMAX, LBQ_NF4, Desc, LbqError, QTensor, Sizes, check, lib,  # noqa: F401
                    STATUS_CODE, EXPORTED, LIB_PATH)
 
 __all__ = [
@@ -41,24 +41,27 @@ def version() -> str:
 
 
 def make_desc(fmt: str, n: int, k: int, bits: int = 4, group: Optional[int] = None,
-              double_quant: bool = True) -> Desc:
+              double_quant: bool = True, compact: bool = False, dq_offset: bool = False) -> Desc:
     """Descriptor for W[n][k]. MinMax: bits 4/2, group 128/64 (default 128 for
-    4-bit, 64 for 2-bit). NF4: absmax block 64, optional double quant (256)."""
+    4-bit, 64 for 2-bit), ``compact`` for fp16 scales and packed zero points.
+    NF4: absmax block 64, optional double quant (256), ``dq_offset`` for
+    double quantization with a per-tensor offset."""
     if fmt not in _FMT:
         raise ValueError(f"format must be one of {sorted(_FMT)}")
     d = Desc()
     d.format = _FMT[fmt]
+    d.meta = 0
     if fmt == "minmax":
         d.bits = bits
         d.group = group if group is not None else (128 if bits == 4 else 64)
         d.double_quant = 0
         d.dq_block = 0
+        d.meta = LBQ_META_COMPACT if compact else LBQ_META_F32
     else:
         d.bits = 4
         d.group = 64 if group is None else group
-        d.double_quant = 1 if double_quant else 0
+        d.double_quant = (2 if dq_offset else 1) if double_quant else 0
         d.dq_block = 256 if double_quant else 0
-    d.reserved = 0
     d.n = n
     d.k = k
     return d
@@ -167,7 +170,10 @@ class QuantizedWeight:
         n, k = desc.n, desc.k
         qw = QuantizedWeight(desc, torch.empty((n, sz["packed"] // n), dtype=torch.uint8, device=dev))
         if sz["scales"]:
-            qw.scales = torch.empty((n, sz["scales"] // 4 // n), dtype=torch.float32, device=dev)
+            if desc.meta == LBQ_META_COMPACT:
+                qw.scales = torch.empty((n, sz["scales"] // 2 // n), dtype=torch.float16, device=dev)
+            else:
+                qw.scales = torch.empty((n, sz["scales"] // 4 // n), dtype=torch.float32, device=dev)
             qw.zeros = torch.empty((n, sz["zeros"] // n), dtype=torch.uint8, device=dev)
         if sz["absmax"]:
             qw.absmax = torch.empty(sz["absmax"] // 4, dtype=torch.float32, device=dev)
@@ -178,12 +184,13 @@ class QuantizedWeight:
 
 
 def lbq_quantize(W: torch.Tensor, fmt: str = "minmax", bits: int = 4, group: Optional[int] = None,
-                 double_quant: bool = True, out: Optional[QuantizedWeight] = None) -> QuantizedWeight:
+                 double_quant: bool = True, out: Optional[QuantizedWeight] = None, compact: bool = False,
+                 dq_offset: bool = False) -> QuantizedWeight:
     """Quantize a device fp32 weight W[n][k] (see ``lbq_quantize`` in lbq.h)."""
     if W.dim() != 2:
         raise ValueError("W must be 2-D [n, k]")
     _need(W, "W", torch.float32)
-    desc = make_desc(fmt, W.shape[0], W.shape[1], bits, group, double_quant)
+    desc = make_desc(fmt, W.shape[0], W.shape[1], bits, group, double_quant, compact, dq_offset)
     qw = out if out is not None else QuantizedWeight.empty(desc, W.device)
     q = qw.qtensor()
     check(lib.lbq_quantize(ctypes.byref(desc), W.data_ptr(), ctypes.byref(q), _stream(W.device)),

@@ -13,6 +13,8 @@ LIB_PATH = os.path.join(HERE, "liblbq.so")
 
 LBQ_MINMAX = 0
 LBQ_NF4 = 1
+LBQ_META_F32 = 0
+LBQ_META_COMPACT = 1
 LBQ_MAX_GROUP = 8
 
 STATUS = {
@@ -34,7 +36,7 @@ EXPORTED = (
 class Desc(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("double_quant", ctypes.c_int32), ("dq_block", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("n", ctypes.c_int64), ("k", ctypes.c_int64)]
+                ("meta", ctypes.c_int32), ("n", ctypes.c_int64), ("k", ctypes.c_int64)]
 
 
 class QTensor(ctypes.Structure):

@@ -133,7 +133,8 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(BwdSet set, int m, uin
   struct Bound {
     __amdgpu_buffer_rsrc_t w, d, s, z;
     int64_t n;
-    int beg;  // first stage of the weight
+    int beg;    // first stage of the weight
+    float off;  // offset of double quantization with an offset
   };
   auto bind = [&](int i) {
     const WView& w = set.w[i];
@@ -143,12 +144,14 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(BwdSet set, int m, uin
     const int64_t nblk = b.n * gpr;
     b.w = make_rsrc(w.packed, b.n * KB);
     b.d = make_rsrc(set.dy[i], (int64_t)m * b.n * 2);
+    b.off = 0.f;
     if constexpr (T::fmt == FMT_MINMAX) {
-      b.s = make_rsrc(w.scales, nblk * 4);
-      b.z = make_rsrc(w.zeros, nblk);
+      b.s = make_rsrc(w.scales, scale_byte_index<KIND>(nblk));
+      b.z = make_rsrc(w.zeros, zero_byte_index<KIND>(nblk));
     } else if constexpr (T::dq) {
       b.s = make_rsrc(w.absmax_scale, ((nblk + 255) >> 8) * 4);
       b.z = make_rsrc(w.absmax_q, nblk);
+      if constexpr (T::dqo) b.off = nf4_dq_offset(w);
     } else {
       b.s = make_rsrc(w.absmax, nblk * 4);
       b.z = b.s;
@@ -197,6 +200,7 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(BwdSet set, int m, uin
   u32x4_t wraw;  // 32 codes of row 4q + lg (2-bit: dwords 0 and 1)
   float md_s;
   int md_i;
+  float md_off = 0.f;  // the loaded stage's weight's offset (the binding may move on before the store)
   // loads of the stage starting at row vt of the set, from the bound weight
   auto load_stage = [&](int64_t vt) {
     const int st = (int)(vt / BNR);
@@ -219,13 +223,20 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(BwdSet set, int m, uin
       wraw = u32x4_t{v[0], v[1], 0u, 0u};
     }
     const int go = (int)(nt * gpr);
-    if constexpr (T::fmt == FMT_MINMAX) {
+    if constexpr (T::fmt == FMT_MINMAX && T::compact) {
+      // fp16 scale; zero point packed bits wide (go is a multiple of 64 rows'
+      // entries, so entry go + g_voff has the parity of g_voff)
+      md_s = f16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r_s, g_voff * 2, go * 2, 0));
+      md_i = zero_from_byte<KIND>(
+          __builtin_amdgcn_raw_buffer_load_b8(r_z, g_voff * T::bits / 8, go * T::bits / 8, 0), g_voff);
+    } else if constexpr (T::fmt == FMT_MINMAX) {
       md_s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, g_voff * 4, go * 4, 0));
       md_i = __builtin_amdgcn_raw_buffer_load_b8(r_z, g_voff, go, 0);
     } else if constexpr (T::dq) {
       md_i = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(r_z, g_voff, go, 0);
       md_s = __builtin_bit_cast(
           float, __builtin_amdgcn_raw_buffer_load_b32(r_s, ((g_voff + (uint32_t)go) >> 8) * 4, 0, 0));
+      if constexpr (T::dqo) md_off = b.off;
     } else {
       md_s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, g_voff * 4, go * 4, 0));
     }
@@ -251,7 +262,7 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(BwdSet set, int m, uin
       gather_rows4(md_s, sc);
       gather_rows4((float)md_i * md_s, zc);
     } else {
-      gather_rows4(T::dq ? (float)md_i * md_s : md_s, sc);
+      gather_rows4(T::dqo ? (float)md_i * md_s + md_off : (T::dq ? (float)md_i * md_s : md_s), sc);
     }
     // v[r][j]: row 4q + r, code j of the chunk
     float v[4][8];

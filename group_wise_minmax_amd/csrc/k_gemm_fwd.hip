@@ -156,8 +156,11 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
   const float* const mf_arr = T::fmt == FMT_MINMAX ? w.scales : (T::dq ? nullptr : w.absmax);
   const uint8_t* const mb_arr =
       T::fmt == FMT_MINMAX ? w.zeros : (T::dq ? reinterpret_cast<const uint8_t*>(w.absmax_q) : nullptr);
-  const bool md4 = (gpr & 3) == 0 && (reinterpret_cast<uintptr_t>(mf_arr) & 15) == 0 &&
+  // (Compact metadata -- fp16 scales, packed zero points -- takes the
+  // per-stage form.)
+  const bool md4 = !T::compact && (gpr & 3) == 0 && (reinterpret_cast<uintptr_t>(mf_arr) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(mb_arr) & 3) == 0;
+  const float dqoff = T::dqo ? nf4_dq_offset(w) : 0.f;
   float mb0 = 0.f, mb1 = 0.f, mb2 = 0.f, mb3 = 0.f;  // scales / absmax of the batch
   uint32_t mb_b = 0;                                 // zero points / absmax codes of the batch
   int md_j = 0;  // entry of the loaded stage in the batch (the same in every lane)
@@ -191,11 +194,17 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
         }
         if constexpr (T::fmt == FMT_MINMAX || T::dq) mb_b = *reinterpret_cast<const uint32_t*>(mb_arr + gi);
       } else {
-        if constexpr (T::fmt != FMT_NF4 || !T::dq) {
-          const float v = mf_arr[gi];
+        if constexpr (T::fmt == FMT_MINMAX) {
+          const float v = minmax_scale<KIND>(w, gi);
           mb0 = v, mb1 = v, mb2 = v, mb3 = v;
+          mb_b = (uint32_t)minmax_zero<KIND>(w, gi);
+        } else {
+          if constexpr (!T::dq) {
+            const float v = mf_arr[gi];
+            mb0 = v, mb1 = v, mb2 = v, mb3 = v;
+          }
+          if constexpr (T::dq) mb_b = mb_arr[gi];
         }
-        if constexpr (T::fmt == FMT_MINMAX || T::dq) mb_b = mb_arr[gi];
       }
       if constexpr (T::dq) md_s = w.absmax_scale[gi >> 8];  // a batch never straddles a 256-block one
     }
@@ -218,6 +227,7 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
       ws_zs = (float)md_i * md_s;
     } else if constexpr (T::dq) {
       ws_s = (float)md_i * md_s;
+      if constexpr (T::dqo) ws_s += dqoff;
     } else {
       ws_s = md_s;
     }

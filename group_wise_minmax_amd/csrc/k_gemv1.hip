@@ -185,6 +185,52 @@ __device__ __forceinline__ float x_chunk(const u32x4_t* xv, uint32_t* xa) {
   return s0 + s1;
 }
 
+// Buffer resources over a weight's metadata arrays (scales / zero points, or
+// the NF4 absmax data).
+template <int KIND>
+__device__ __forceinline__ void meta_rsrc(const WView& w, int64_t nmeta, __amdgpu_buffer_rsrc_t& r_s,
+                                          __amdgpu_buffer_rsrc_t& r_z) {
+  using T = WKindTraits<KIND>;
+  if constexpr (T::fmt == FMT_MINMAX) {
+    r_s = make_rsrc(w.scales, scale_byte_index<KIND>(nmeta));
+    r_z = make_rsrc(w.zeros, zero_byte_index<KIND>(nmeta));
+  } else if constexpr (T::dq) {
+    r_s = make_rsrc(w.absmax_scale, ((nmeta + 255) >> 8) * 4);
+    r_z = make_rsrc(w.absmax_q, nmeta);
+  } else {
+    r_s = make_rsrc(w.absmax, nmeta * 4);
+    r_z = r_s;
+  }
+}
+
+// Metadata of entry gc of row `row` (gpr entries per row): the scale (MinMax
+// s, or the NF4 block absmax, decoded) and the MinMax zero point (0 for NF4).
+// The row offset is wave-uniform (a scalar offset), gc the lane's.
+template <int KIND>
+__device__ __forceinline__ void load_meta(__amdgpu_buffer_rsrc_t r_s, __amdgpu_buffer_rsrc_t r_z, int row, int gpr,
+                                          int gc, float dqoff, float& sc, int& zq) {
+  using T = WKindTraits<KIND>;
+  if constexpr (T::fmt == FMT_MINMAX && T::compact) {
+    // fp16 scales; zero points packed bits wide (rows hold whole bytes)
+    const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(r_s, (uint32_t)gc * 2u, row * gpr * 2, 0);
+    const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b8(r_z, (uint32_t)(gc * T::bits / 8), row * gpr * T::bits / 8, 0);
+    sc = f16_bits_to_f32(h);
+    zq = zero_from_byte<KIND>(zb, gc);
+  } else if constexpr (T::fmt == FMT_MINMAX) {
+    sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)gc * 4u, row * gpr * 4, 0));
+    zq = __builtin_amdgcn_raw_buffer_load_b8(r_z, (uint32_t)gc, row * gpr, 0);
+  } else if constexpr (T::dq) {
+    const int q2 = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(r_z, (uint32_t)gc, row * gpr, 0);
+    const float c2 = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)((row * gpr + gc) >> 8) * 4u, 0, 0));
+    sc = T::dqo ? (float)q2 * c2 + dqoff : (float)q2 * c2;
+    zq = 0;
+  } else {
+    sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)gc * 4u, row * gpr * 4, 0));
+    zq = 0;
+  }
+}
+
 // The work of one wave (and its share of the workgroup prologue): weight `w`,
 // output `Y` / `out_rows`, row groups [g0, g1) of R rows; `total` == 0 for a
 // wave without work (it still joins the prologue's barriers).
@@ -220,16 +266,8 @@ __device__ __forceinline__ void gemv1_body(const WView& w, uint16_t* __restrict_
   const __amdgpu_buffer_rsrc_t r_w = make_rsrc(w.packed, w.n * KB);
   const __amdgpu_buffer_rsrc_t r_x = make_rsrc(X, w.k * 2);
   __amdgpu_buffer_rsrc_t r_s, r_z;
-  if constexpr (T::fmt == FMT_MINMAX) {
-    r_s = make_rsrc(w.scales, nmeta * 4);
-    r_z = make_rsrc(w.zeros, nmeta);
-  } else if constexpr (T::dq) {
-    r_s = make_rsrc(w.absmax_scale, ((nmeta + 255) >> 8) * 4);
-    r_z = make_rsrc(w.absmax_q, nmeta);
-  } else {
-    r_s = make_rsrc(w.absmax, nmeta * 4);
-    r_z = r_s;
-  }
+  meta_rsrc<KIND>(w, nmeta, r_s, r_z);
+  const float dqoff = T::dqo ? nf4_dq_offset(w) : 0.f;
   auto load = [&](int s, Step<KIND, R, CB>& st) {
     const int g = g0 + s / nsteps, b = s % nsteps;
 #pragma unroll
@@ -241,19 +279,7 @@ __device__ __forceinline__ void gemv1_body(const WView& w, uint16_t* __restrict_
         const int row = (int)min((int64_t)g * R + r, w.n - 1);
         st.wq[cb][r] = __builtin_bit_cast(
             u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_w, (uint32_t)c * 16u, row * KB, 2 /*nt*/));
-        if constexpr (T::fmt == FMT_MINMAX) {
-          st.sc[cb][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)gc * 4u, row * gpr * 4, 0));
-          st.zq[cb][r] = __builtin_amdgcn_raw_buffer_load_b8(r_z, (uint32_t)gc, row * gpr, 0);
-        } else if constexpr (T::dq) {
-          const int q2 = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(r_z, (uint32_t)gc, row * gpr, 0);
-          const float c2 = __builtin_bit_cast(
-              float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)((row * gpr + gc) >> 8) * 4u, 0, 0));
-          st.sc[cb][r] = (float)q2 * c2;
-          st.zq[cb][r] = 0;
-        } else {
-          st.sc[cb][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)gc * 4u, row * gpr * 4, 0));
-          st.zq[cb][r] = 0;
-        }
+        load_meta<KIND>(r_s, r_z, row, gpr, gc, dqoff, st.sc[cb][r], st.zq[cb][r]);
       }
       if constexpr (XG) {
 #pragma unroll
@@ -507,16 +533,8 @@ __device__ __forceinline__ void gemvm_body(const WView& w, uint16_t* __restrict_
   const int64_t nmeta = w.n * gpr;
   const __amdgpu_buffer_rsrc_t r_w = make_rsrc(w.packed, w.n * KB);
   __amdgpu_buffer_rsrc_t r_s, r_z;
-  if constexpr (T::fmt == FMT_MINMAX) {
-    r_s = make_rsrc(w.scales, nmeta * 4);
-    r_z = make_rsrc(w.zeros, nmeta);
-  } else if constexpr (T::dq) {
-    r_s = make_rsrc(w.absmax_scale, ((nmeta + 255) >> 8) * 4);
-    r_z = make_rsrc(w.absmax_q, nmeta);
-  } else {
-    r_s = make_rsrc(w.absmax, nmeta * 4);
-    r_z = r_s;
-  }
+  meta_rsrc<KIND>(w, nmeta, r_s, r_z);
+  const float dqoff = T::dqo ? nf4_dq_offset(w) : 0.f;
   auto load = [&](int s, Step<KIND, R, CB>& st) {
     const int g = g0 + s / nsteps, b = s % nsteps;
 #pragma unroll
@@ -528,19 +546,7 @@ __device__ __forceinline__ void gemvm_body(const WView& w, uint16_t* __restrict_
         const int row = (int)min((int64_t)g * R + r, w.n - 1);
         st.wq[cb][r] = __builtin_bit_cast(
             u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_w, (uint32_t)c * 16u, row * KB, 2 /*nt*/));
-        if constexpr (T::fmt == FMT_MINMAX) {
-          st.sc[cb][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)gc * 4u, row * gpr * 4, 0));
-          st.zq[cb][r] = __builtin_amdgcn_raw_buffer_load_b8(r_z, (uint32_t)gc, row * gpr, 0);
-        } else if constexpr (T::dq) {
-          const int q2 = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(r_z, (uint32_t)gc, row * gpr, 0);
-          const float c2 = __builtin_bit_cast(
-              float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)((row * gpr + gc) >> 8) * 4u, 0, 0));
-          st.sc[cb][r] = (float)q2 * c2;
-          st.zq[cb][r] = 0;
-        } else {
-          st.sc[cb][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)gc * 4u, row * gpr * 4, 0));
-          st.zq[cb][r] = 0;
-        }
+        load_meta<KIND>(r_s, r_z, row, gpr, gc, dqoff, st.sc[cb][r], st.zq[cb][r]);
       }
     }
   };
@@ -872,6 +878,9 @@ bool gemvm_fits(WKind kind, int64_t k, int64_t m) {
     case WK_I2G128: b = m <= 2 ? lds_bytes_m<WK_I2G128, 2>(k) : lds_bytes_m<WK_I2G128, 4>(k); break;
     case WK_NF4: b = m <= 2 ? lds_bytes_m<WK_NF4, 2>(k) : lds_bytes_m<WK_NF4, 4>(k); break;
     case WK_NF4DQ: b = m <= 2 ? lds_bytes_m<WK_NF4DQ, 2>(k) : lds_bytes_m<WK_NF4DQ, 4>(k); break;
+    case WK_I4G128C: b = m <= 2 ? lds_bytes_m<WK_I4G128C, 2>(k) : lds_bytes_m<WK_I4G128C, 4>(k); break;
+    case WK_I2G64C: b = m <= 2 ? lds_bytes_m<WK_I2G64C, 2>(k) : lds_bytes_m<WK_I2G64C, 4>(k); break;
+    case WK_NF4DQO: b = m <= 2 ? lds_bytes_m<WK_NF4DQO, 2>(k) : lds_bytes_m<WK_NF4DQO, 4>(k); break;
   }
   return b <= 65536;
 }

@@ -128,6 +128,8 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
   const int per = (nchunk + ks_count - 1) / ks_count;
   const int c_lo = split * per;
   const int c_hi = min(c_lo + per, nchunk);
+  float dqoff = 0.f;  // offset of double quantization with an offset
+  if constexpr (T::dqo) dqoff = nf4_dq_offset(w);
 
   if constexpr (T::fmt == FMT_NF4) {
 #pragma unroll
@@ -171,9 +173,9 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
       const bool ok = j < NG && (int64_t)j * GRP < kend;
       const int64_t gi = n * gpr + (ok ? (kc / GRP + j) : 0);
       if constexpr (T::fmt == FMT_MINMAX) {
-        mr = make_float2(w.scales[gi], (float)(128 + (int)w.zeros[gi]));
+        mr = make_float2(minmax_scale<KIND>(w, gi), (float)(128 + minmax_zero<KIND>(w, gi)));
       } else {
-        mr = make_float2(nf4_block_scale<T::dq>(w, gi), 0.f);
+        mr = make_float2(nf4_block_scale<KIND>(w, gi, dqoff), 0.f);
       }
     }
   };

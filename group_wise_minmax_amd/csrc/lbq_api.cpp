@@ -85,16 +85,21 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 lbq_status check_desc(const lbq_desc* d) {
   if (d == nullptr) return fail(LBQ_E_NULL, "desc is NULL");
-  if (d->reserved != 0) return fail(LBQ_E_FORMAT, "desc.reserved must be 0");
   if (d->format == LBQ_MINMAX) {
     if (d->bits != 4 && d->bits != 2) return fail(LBQ_E_FORMAT, "MINMAX bits must be 4 or 2 (got %d)", d->bits);
     if (d->group != 128 && d->group != 64) return fail(LBQ_E_FORMAT, "MINMAX group must be 64 or 128 (got %d)", d->group);
     if (d->double_quant != 0 || d->dq_block != 0) return fail(LBQ_E_FORMAT, "MINMAX takes no double quantization");
+    if (d->meta != LBQ_META_F32 && d->meta != LBQ_META_COMPACT)
+      return fail(LBQ_E_FORMAT, "MINMAX meta must be 0 (fp32 scale, byte zero point) or 1 (compact), got %d", d->meta);
+    if (d->meta == LBQ_META_COMPACT && !((d->bits == 4 && d->group == 128) || (d->bits == 2 && d->group == 64)))
+      return fail(LBQ_E_FORMAT, "compact metadata is defined for INT4 g128 and INT2 g64 only");
   } else if (d->format == LBQ_NF4) {
+    if (d->meta != 0) return fail(LBQ_E_FORMAT, "NF4 takes meta = 0");
     if (d->bits != 4) return fail(LBQ_E_FORMAT, "NF4 bits must be 4 (got %d)", d->bits);
     if (d->group != 64) return fail(LBQ_E_FORMAT, "NF4 absmax block must be 64 (got %d)", d->group);
-    if (d->double_quant != 0 && d->double_quant != 1) return fail(LBQ_E_FORMAT, "double_quant must be 0 or 1");
-    if (d->dq_block != (d->double_quant ? 256 : 0)) return fail(LBQ_E_FORMAT, "dq_block must be 256 with double_quant=1 and 0 otherwise");
+    if (d->double_quant < 0 || d->double_quant > 2)
+      return fail(LBQ_E_FORMAT, "double_quant must be 0, 1 or 2 (with an offset), got %d", d->double_quant);
+    if (d->dq_block != (d->double_quant ? 256 : 0)) return fail(LBQ_E_FORMAT, "dq_block must be 256 with double quantization and 0 otherwise");
   } else {
     return fail(LBQ_E_FORMAT, "unknown format %d (MINMAX=0, NF4=1)", d->format);
   }
@@ -102,11 +107,15 @@ lbq_status check_desc(const lbq_desc* d) {
   if (d->k < 64 || d->k > (int64_t(1) << 24)) return fail(LBQ_E_SHAPE, "k must be in [64, 2^24] (got %lld)", (long long)d->k);
   if (d->k % 64 != 0 || d->k % d->group != 0) return fail(LBQ_E_SHAPE, "k (%lld) must be a multiple of 64 and of the group", (long long)d->k);
   if (d->n * d->k > (int64_t(1) << 40)) return fail(LBQ_E_SHAPE, "n*k too large");
+  if (d->format == LBQ_MINMAX && d->meta == LBQ_META_COMPACT && (d->k / d->group) * d->bits % 8 != 0)
+    return fail(LBQ_E_SHAPE, "compact metadata needs (k / group) * bits %% 8 == 0 (k %lld)", (long long)d->k);
   return LBQ_OK;
 }
 
 lbq::WKind kind_of(const lbq_desc* d) {
-  if (d->format == LBQ_NF4) return d->double_quant ? lbq::WK_NF4DQ : lbq::WK_NF4;
+  if (d->format == LBQ_NF4)
+    return d->double_quant == 2 ? lbq::WK_NF4DQO : (d->double_quant ? lbq::WK_NF4DQ : lbq::WK_NF4);
+  if (d->meta == LBQ_META_COMPACT) return d->bits == 4 ? lbq::WK_I4G128C : lbq::WK_I2G64C;
   if (d->bits == 4) return d->group == 128 ? lbq::WK_I4G128 : lbq::WK_I4G64;
   return d->group == 64 ? lbq::WK_I2G64 : lbq::WK_I2G128;
 }
@@ -122,13 +131,20 @@ void sizes_of(const lbq_desc* d, lbq_sizes* s) {
   std::memset(s, 0, sizeof *s);
   s->packed = (size_t)(d->n * d->k * d->bits / 8);
   if (d->format == LBQ_MINMAX) {
-    s->scales = (size_t)(d->n * (d->k / d->group)) * sizeof(float);
-    s->zeros = (size_t)(d->n * (d->k / d->group));
+    const int64_t ng = d->n * (d->k / d->group);
+    if (d->meta == LBQ_META_COMPACT) {
+      s->scales = (size_t)ng * 2;                 // fp16
+      s->zeros = (size_t)(ng * d->bits / 8);      // packed like the codes
+    } else {
+      s->scales = (size_t)ng * sizeof(float);
+      s->zeros = (size_t)ng;
+    }
   } else {
     const int64_t nb = d->n * d->k / 64;
     if (d->double_quant) {
       s->absmax_q = (size_t)nb;
-      s->absmax_scale = (size_t)((nb + 255) / 256) * sizeof(float);
+      // with an offset, one more fp32 after the per-run scales
+      s->absmax_scale = (size_t)((nb + 255) / 256 + (d->double_quant == 2 ? 1 : 0)) * sizeof(float);
     } else {
       s->absmax = (size_t)nb * sizeof(float);
     }
@@ -142,7 +158,8 @@ lbq_status check_qtensor(const lbq_desc* d, const lbq_qtensor* q) {
   if (!aligned(q->packed, 16)) return fail(LBQ_E_ALIGN, "qtensor.packed must be 16-byte aligned");
   if (d->format == LBQ_MINMAX) {
     if (q->scales == nullptr || q->zeros == nullptr) return fail(LBQ_E_NULL, "MINMAX needs scales and zeros");
-    if (!aligned(q->scales, 4)) return fail(LBQ_E_ALIGN, "scales must be 4-byte aligned");
+    if (!aligned(q->scales, d->meta == LBQ_META_COMPACT ? 2 : 4))
+      return fail(LBQ_E_ALIGN, "scales must be 4-byte (fp32) or 2-byte (fp16) aligned");
   } else if (d->double_quant) {
     if (q->absmax_q == nullptr || q->absmax_scale == nullptr) return fail(LBQ_E_NULL, "NF4 with double quant needs absmax_q and absmax_scale");
     if (!aligned(q->absmax_scale, 4)) return fail(LBQ_E_ALIGN, "absmax_scale must be 4-byte aligned");
@@ -156,7 +173,7 @@ lbq_status check_qtensor(const lbq_desc* d, const lbq_qtensor* q) {
 lbq::WView view_of(const lbq_desc* d, const lbq_qtensor* q) {
   lbq::WView w;
   w.packed = static_cast<const uint8_t*>(q->packed);
-  w.scales = q->scales;
+  w.scales = static_cast<const float*>(q->scales);
   w.zeros = q->zeros;
   w.absmax = q->absmax;
   w.absmax_q = q->absmax_q;
@@ -281,10 +298,11 @@ lbq_status lbq_quantize(const lbq_desc* desc, const float* W, const lbq_qtensor*
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (desc->format == LBQ_MINMAX) {
-    e = lbq::launch_quant_minmax(desc->bits, desc->group, W, static_cast<uint8_t*>(q->packed),
-                                 q->scales, q->zeros, desc->n, desc->k, s);
+    e = lbq::launch_quant_minmax(desc->bits, desc->group, desc->meta == LBQ_META_COMPACT, W,
+                                 static_cast<uint8_t*>(q->packed), static_cast<float*>(q->scales), q->zeros,
+                                 desc->n, desc->k, s);
   } else {
-    e = lbq::launch_quant_nf4(desc->double_quant != 0, W, static_cast<uint8_t*>(q->packed),
+    e = lbq::launch_quant_nf4(desc->double_quant, W, static_cast<uint8_t*>(q->packed),
                               q->absmax, q->absmax_q, q->absmax_scale, desc->n, desc->k,
                               nf4_table(), s);
   }

@@ -125,18 +125,89 @@ __device__ __forceinline__ void tile_of(int bid, int nx, int ny, int& tx, int& t
   tx = r / gm;
 }
 
+// compact: fp16 scales and zero points packed `bits` wide, like the codes.
+// dqo: double quantization with a per-tensor offset (absmax_scale holds the
+// per-256 scales and then the offset).
 template <int K> struct WKindTraits;
-template <> struct WKindTraits<WK_I4G128> { static constexpr int fmt = FMT_MINMAX, bits = 4, group = 128; static constexpr bool dq = false; };
-template <> struct WKindTraits<WK_I4G64>  { static constexpr int fmt = FMT_MINMAX, bits = 4, group = 64;  static constexpr bool dq = false; };
-template <> struct WKindTraits<WK_I2G64>  { static constexpr int fmt = FMT_MINMAX, bits = 2, group = 64;  static constexpr bool dq = false; };
-template <> struct WKindTraits<WK_I2G128> { static constexpr int fmt = FMT_MINMAX, bits = 2, group = 128; static constexpr bool dq = false; };
-template <> struct WKindTraits<WK_NF4>    { static constexpr int fmt = FMT_NF4,    bits = 4, group = 64;  static constexpr bool dq = false; };
-template <> struct WKindTraits<WK_NF4DQ>  { static constexpr int fmt = FMT_NF4,    bits = 4, group = 64;  static constexpr bool dq = true; };
+template <> struct WKindTraits<WK_I4G128>  { static constexpr int fmt = FMT_MINMAX, bits = 4, group = 128; static constexpr bool dq = false, compact = false, dqo = false; };
+template <> struct WKindTraits<WK_I4G64>   { static constexpr int fmt = FMT_MINMAX, bits = 4, group = 64;  static constexpr bool dq = false, compact = false, dqo = false; };
+template <> struct WKindTraits<WK_I2G64>   { static constexpr int fmt = FMT_MINMAX, bits = 2, group = 64;  static constexpr bool dq = false, compact = false, dqo = false; };
+template <> struct WKindTraits<WK_I2G128>  { static constexpr int fmt = FMT_MINMAX, bits = 2, group = 128; static constexpr bool dq = false, compact = false, dqo = false; };
+template <> struct WKindTraits<WK_NF4>     { static constexpr int fmt = FMT_NF4,    bits = 4, group = 64;  static constexpr bool dq = false, compact = false, dqo = false; };
+template <> struct WKindTraits<WK_NF4DQ>   { static constexpr int fmt = FMT_NF4,    bits = 4, group = 64;  static constexpr bool dq = true,  compact = false, dqo = false; };
+template <> struct WKindTraits<WK_I4G128C> { static constexpr int fmt = FMT_MINMAX, bits = 4, group = 128; static constexpr bool dq = false, compact = true,  dqo = false; };
+template <> struct WKindTraits<WK_I2G64C>  { static constexpr int fmt = FMT_MINMAX, bits = 2, group = 64;  static constexpr bool dq = false, compact = true,  dqo = false; };
+template <> struct WKindTraits<WK_NF4DQO>  { static constexpr int fmt = FMT_NF4,    bits = 4, group = 64;  static constexpr bool dq = true,  compact = false, dqo = true; };
 
-// Block absmax of NF4 block `blk` (fp32, or fl(q2 * c2) under double quant).
-template <bool DQ>
-__device__ __forceinline__ float nf4_block_scale(const WView& w, int64_t blk) {
-  if constexpr (DQ) {
+// fp16 bit pattern -> its exact fp32 value (normal and subnormal; no NaN/Inf
+// in the contract).
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  const uint32_t e = (h >> 10) & 0x1Fu, mant = h & 0x3FFu;
+  const float v = e == 0 ? (float)mant * 5.9604644775390625e-8f  // mant * 2^-24, exact
+                         : __uint_as_float(((e + 112u) << 23) | (mant << 13));
+  return (h & 0x8000u) ? -v : v;
+}
+
+// Zero point of metadata entry gi from the zeros array: one byte per entry,
+// or (compact) `bits`-wide fields packed like the codes, the first entry in
+// the high bits; rows hold whole bytes, so entry gi sits in byte gi*bits/8.
+template <int KIND>
+__device__ __forceinline__ int zero_from_byte(uint32_t byte, int64_t gi) {
+  using T = WKindTraits<KIND>;
+  if constexpr (!T::compact) {
+    return (int)(byte & 0xFFu);
+  } else if constexpr (T::bits == 4) {
+    return (int)((byte >> ((gi & 1) ? 0 : 4)) & 0xFu);
+  } else {
+    return (int)((byte >> (6 - 2 * (int)(gi & 3))) & 0x3u);
+  }
+}
+// Byte offset in the zeros array of metadata entry gi.
+template <int KIND>
+__device__ __forceinline__ int64_t zero_byte_index(int64_t gi) {
+  using T = WKindTraits<KIND>;
+  if constexpr (T::compact) return gi * T::bits / 8;
+  return gi;
+}
+// Byte offset in the scales array of metadata entry gi (fp32 or fp16).
+template <int KIND>
+__device__ __forceinline__ int64_t scale_byte_index(int64_t gi) {
+  return gi * (WKindTraits<KIND>::compact ? 2 : 4);
+}
+// Scale value from the raw bits loaded at scale_byte_index (fp32, or fp16 in
+// the low 16 bits).
+template <int KIND>
+__device__ __forceinline__ float scale_from_bits(uint32_t raw) {
+  if constexpr (WKindTraits<KIND>::compact) return f16_bits_to_f32(raw & 0xFFFFu);
+  return __uint_as_float(raw);
+}
+// MinMax scale and zero point of metadata entry gi (generic loads).
+template <int KIND>
+__device__ __forceinline__ float minmax_scale(const WView& w, int64_t gi) {
+  if constexpr (WKindTraits<KIND>::compact)
+    return f16_bits_to_f32(reinterpret_cast<const uint16_t*>(w.scales)[gi]);
+  return w.scales[gi];
+}
+template <int KIND>
+__device__ __forceinline__ int minmax_zero(const WView& w, int64_t gi) {
+  return zero_from_byte<KIND>(w.zeros[zero_byte_index<KIND>(gi)], gi);
+}
+
+// Per-tensor offset of double quantization with an offset: the entry after
+// the ceil(nb / 256) per-block scales.
+__device__ __forceinline__ float nf4_dq_offset(const WView& w) {
+  return w.absmax_scale[(w.n * w.k / 64 + 255) >> 8];
+}
+
+// Block absmax of NF4 block `blk`: fp32, fl(q2 * c2) under double quant, or
+// fl(fl(q2 * c2) + off) with an offset (`off` from nf4_dq_offset).
+template <int KIND>
+__device__ __forceinline__ float nf4_block_scale(const WView& w, int64_t blk, float off) {
+  using T = WKindTraits<KIND>;
+  if constexpr (T::dqo) {
+    const float p = (float)w.absmax_q[blk] * w.absmax_scale[blk >> 8];
+    return p + off;
+  } else if constexpr (T::dq) {
     return (float)w.absmax_q[blk] * w.absmax_scale[blk >> 8];
   } else {
     return w.absmax[blk];
@@ -153,6 +224,9 @@ hipError_t dispatch_kind(WKind kind, Args&&... args) {
     case WK_I2G128: return F<WK_I2G128>::run(args...);
     case WK_NF4: return F<WK_NF4>::run(args...);
     case WK_NF4DQ: return F<WK_NF4DQ>::run(args...);
+    case WK_I4G128C: return F<WK_I4G128C>::run(args...);
+    case WK_I2G64C: return F<WK_I2G64C>::run(args...);
+    case WK_NF4DQO: return F<WK_NF4DQO>::run(args...);
   }
   return hipErrorInvalidValue;
 }

@@ -10,6 +10,7 @@ namespace lbq {
 enum Fmt : int { FMT_MINMAX = 0, FMT_NF4 = 1 };
 
 // One quantized weight as the kernels see it (device pointers + shape).
+// `scales` holds fp32 values, or fp16 bit patterns under compact metadata.
 struct WView {
   const uint8_t* packed;
   const float* scales;
@@ -51,13 +52,18 @@ enum WKind : int {
   WK_I2G128 = 3,  // MinMax 2-bit, group 128
   WK_NF4 = 4,     // NF4, block 64, fp32 absmax
   WK_NF4DQ = 5,   // NF4, block 64, int8 absmax + fp32 scale per 256 blocks
+  WK_I4G128C = 6, // MinMax 4-bit, group 128, compact metadata (fp16 scale, packed zero)
+  WK_I2G64C = 7,  // MinMax 2-bit, group 64, compact metadata
+  WK_NF4DQO = 8,  // NF4, block 64, double quant with a per-tensor offset
 };
 
 // ---- launchers (each returns hipGetLastError() after the launch) ----------
-hipError_t launch_quant_minmax(int bits, int group, const float* W, uint8_t* packed,
+// compact: fp16 scales and packed zero points (INT4 g128 and INT2 g64 only).
+hipError_t launch_quant_minmax(int bits, int group, bool compact, const float* W, uint8_t* packed,
                                float* scales, uint8_t* zeros, int64_t n, int64_t k,
                                hipStream_t s);
-hipError_t launch_quant_nf4(bool dq, const float* W, uint8_t* packed, float* absmax,
+// dq: 0 none, 1 double quantization, 2 double quantization with an offset.
+hipError_t launch_quant_nf4(int dq, const float* W, uint8_t* packed, float* absmax,
                             int8_t* absmax_q, float* absmax_scale, int64_t n, int64_t k,
                             const Nf4Table& tab, hipStream_t s);
 hipError_t launch_dequant(WKind kind, const WView& w, uint16_t* out, const Nf4Table& tab,

@@ -38,8 +38,8 @@
  *               weight); X is m x k; Y is m x ldy; dY is m x n; dX is m x k.
  *               bf16 tensors are passed as uint16_t bit patterns.
  *   Alignment:  `packed`, W, X, dY, dX, LoRA A and the LoRA workspace must
- *               be 16-byte aligned; Y, LoRA B 2-byte aligned; scales, absmax
- *               and absmax_scale 4-byte aligned.
+ *               be 16-byte aligned; Y, LoRA B 2-byte aligned; scales (fp16
+ *               scales 2-byte), absmax and absmax_scale 4-byte aligned.
  */
 #ifndef LBQ_H
 #define LBQ_H
@@ -67,12 +67,22 @@ typedef enum {
   LBQ_NF4 = 1     /* 4-bit NormalFloat, blockwise absmax, optional DQ [QL]   */
 } lbq_format;
 
+/* MinMax metadata layouts (lbq_desc.meta). */
+typedef enum {
+  LBQ_META_F32 = 0,     /* fp32 scale and one byte per zero point            */
+  LBQ_META_COMPACT = 1  /* fp16 scale and the zero point packed bits wide    */
+} lbq_meta;
+
 /* Describes one quantized weight W[n][k].
  *   MINMAX: bits in {4, 2}, group in {64, 128}, k % group == 0;
- *           double_quant = 0, dq_block = 0.
+ *           double_quant = 0, dq_block = 0; meta = LBQ_META_F32, or
+ *           LBQ_META_COMPACT for INT4 g128 and INT2 g64 with
+ *           (k / group) * bits % 8 == 0 (see lbq_quantize).
  *   NF4:    bits = 4, group = 64 (absmax block; blocks run row-major and never
- *           straddle rows because k % 64 == 0); double_quant in {0, 1};
- *           dq_block = 256 when double_quant = 1, else 0.
+ *           straddle rows because k % 64 == 0); meta = 0; double_quant 0
+ *           (fp32 absmax), 1 (absmax double-quantized) or 2 (double-quantized
+ *           with a per-tensor offset); dq_block = 256 with double
+ *           quantization, else 0.
  * n >= 1, k >= 64. */
 typedef struct {
   int32_t format;
@@ -80,7 +90,7 @@ typedef struct {
   int32_t group;
   int32_t double_quant;
   int32_t dq_block;
-  int32_t reserved; /* must be 0 */
+  int32_t meta;
   int64_t n;
   int64_t k;
 } lbq_desc;
@@ -91,11 +101,16 @@ typedef struct {
  *                              [BNB]; 2-bit: code 4i in bits 7..6, then 5..4,
  *                              3..2, 1..0.  Only the bytes matter: the caller
  *                              may hold them in any dtype of the same size.
- *   scales        MINMAX       f32[n][k/group]
- *   zeros         MINMAX       u8 [n][k/group]  (integer zero point 0..2^bits-1)
+ *   scales        MINMAX       f32[n][k/group]; compact: fp16 bit patterns
+ *                              u16[n][k/group] (2-byte aligned)
+ *   zeros         MINMAX       u8 [n][k/group]  (integer zero point 0..2^bits-1);
+ *                              compact: u8[n][(k/group)*bits/8], the zero
+ *                              points of a row packed like the codes (first
+ *                              group in the high bits)
  *   absmax        NF4, DQ=0    f32[n*k/64]
- *   absmax_q      NF4, DQ=1    i8 [n*k/64]      (0..127)
- *   absmax_scale  NF4, DQ=1    f32[ceil(n*k/64/256)]
+ *   absmax_q      NF4, DQ=1    i8 [n*k/64]      (0..127); DQ=2: -127..127
+ *   absmax_scale  NF4, DQ=1    f32[ceil(n*k/64/256)]; DQ=2: one more entry
+ *                              at the end, the per-tensor offset
  *   out_rows      optional (forward only): int32[n]; row i of W writes output
  *                 column out_rows[i] of Y (channel-mix scatter [GB]).  NULL
  *                 means row i writes column i.  Entries must be distinct and
@@ -103,7 +118,7 @@ typedef struct {
  * Unused fields are ignored. */
 typedef struct {
   void* packed;
-  float* scales;
+  void* scales;
   uint8_t* zeros;
   float* absmax;
   int8_t* absmax_q;
@@ -135,6 +150,17 @@ lbq_status lbq_layout(const lbq_desc* desc, lbq_sizes* out);
  *     double_quant = 1 the block absmax values are re-quantized in runs of
  *     256: c2 = fl(max/127), q2 = clamp(rne(fl(a/c2)), 0, 127) (0 if c2 == 0);
  *     the 4-bit codes always use the un-quantized a.
+ *   MINMAX, compact metadata (an fp16 scale per group, the form GPTQ-style
+ *     checkpoints store [GB] 模型量化): s32 as above; the stored scale s is
+ *     the smallest fp16 value >= s32 (65504 at most), and z and q are formed
+ *     with that s, so Qmax * s still spans the group's range.
+ *   NF4, double_quant = 2 ([QL] 结论: double quantization re-quantizes the
+ *     scale factor and the offset; [BNB] 源码纵深: `offset` is a field of the
+ *     quantization state): off = fp32(fp64(S) / nb), S the sum of the nb
+ *     absmax values over the binary tree of adjacent pairs in index order
+ *     (zero-padded to a power of two, fp32 additions); per run of 256:
+ *     d = fl(a - off), c2 = fl(max|d|/127), q2 = clamp(rne(fl(d/c2)), -127,
+ *     127) (0 if c2 == 0); decoded as fl(fl(q2 * c2) + off).  Three launches.
  * Every fp32 step is one IEEE operation rounded to nearest-even (true
  * division, no contraction); results are bit-exact across runs.
  * Pure: it never inspects the old contents of the outputs. */
@@ -143,8 +169,9 @@ lbq_status lbq_quantize(const lbq_desc* desc, const float* W, const lbq_qtensor*
 
 /* Dequantize to bf16 W_bf16[n][k] (device) [BNB] 通过BitsAndBytesConfig配置:
  *   MINMAX: bf16(fl((q - z) * s));  NF4: bf16(fl(c[code] * A)) with A the block
- *   absmax, or fl(q2 * c2) under double quantization.  bf16 rounding is
- *   round-to-nearest-even; the result is bit-exact. */
+ *   absmax, fl(q2 * c2) under double quantization, or fl(fl(q2 * c2) + off)
+ *   with an offset.  bf16 rounding is round-to-nearest-even; the result is
+ *   bit-exact. */
 lbq_status lbq_dequant(const lbq_desc* desc, const lbq_qtensor* q, uint16_t* W_bf16,
                        void* stream);
 
@@ -291,7 +318,7 @@ lbq_status lbq_lora_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16
  * dtype holds them).  A blob is little-endian host memory:
  *   bytes  0..3   the characters "LBQ1"
  *          4..7   uint32 version, 1
- *          8..47  the lbq_desc (reserved = 0)
+ *          8..47  the lbq_desc
  *         48..95  six uint64 byte counts, as lbq_layout reports them, of
  *                 packed, scales, zeros, absmax, absmax_q, absmax_scale
  *         96..    those six buffers in that order, each starting at a

@@ -74,6 +74,31 @@ def test_layout_double_quant_saving(L):
             assert 8.0 * saved / (n * k) == 0.373046875
 
 
+def test_layout_format_variants(L):
+    """Compact MinMax metadata (fp16 scales, zero points packed like the
+    codes) and double quantization with an offset (one more fp32 after the
+    per-run scales): byte counts and bits per parameter by the closed forms."""
+    import synth_inputs as SI
+    for shapes in (SI.LLAMA3_8B, SI.LLAMA3_70B, SI.QWEN15_110B):
+        for n, k in shapes.values():
+            for bits, group, bpp in ((4, 128, 4.15625), (2, 64, 2.28125)):
+                s = L.lbq_layout(L.make_desc("minmax", n, k, bits, group, compact=True))
+                assert s["scales"] == 2 * n * (k // group) and s["zeros"] == n * (k // group) * bits // 8
+                assert 8.0 * (s["packed"] + s["scales"] + s["zeros"]) / (n * k) == bpp
+            nb = n * k // 64
+            s = L.lbq_layout(L.make_desc("nf4", n, k, double_quant=True, dq_offset=True))
+            assert s["absmax_q"] == nb and s["absmax_scale"] == 4 * (-(-nb // 256) + 1) and s["absmax"] == 0
+    d = L.make_desc("nf4", 64, 256, double_quant=True, dq_offset=True)
+    assert d.double_quant == 2 and d.dq_block == 256
+    for bad in (dict(double_quant=3), dict(meta=1)):
+        e = L.make_desc("nf4", 64, 256)
+        for k_, v in bad.items():
+            setattr(e, k_, v)
+        with pytest.raises(L.LbqError) as err:
+            L.lbq_layout(e)
+        assert err.value.name == "LBQ_E_FORMAT"
+
+
 def _desc(L, **kw):
     d = L.make_desc("minmax", 64, 256, 4, 128)
     for k, v in kw.items():
@@ -84,7 +109,8 @@ def _desc(L, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(format=7), "LBQ_E_FORMAT"), (dict(bits=3), "LBQ_E_FORMAT"), (dict(bits=8), "LBQ_E_FORMAT"),
     (dict(group=32), "LBQ_E_FORMAT"), (dict(group=100), "LBQ_E_FORMAT"),
-    (dict(double_quant=1), "LBQ_E_FORMAT"), (dict(reserved=1), "LBQ_E_FORMAT"),
+    (dict(double_quant=1), "LBQ_E_FORMAT"), (dict(meta=2), "LBQ_E_FORMAT"), (dict(meta=-1), "LBQ_E_FORMAT"),
+    (dict(meta=1, group=64), "LBQ_E_FORMAT"), (dict(meta=1, k=128), "LBQ_E_SHAPE"),
     (dict(n=0), "LBQ_E_SHAPE"), (dict(k=0), "LBQ_E_SHAPE"), (dict(k=96), "LBQ_E_SHAPE"),
     (dict(k=192), "LBQ_E_SHAPE"), (dict(n=-5), "LBQ_E_SHAPE"),
 ])

@@ -714,24 +714,8 @@ def test_fp32_tree_sum():
     assert O.absmax_offset(np.full(1000, 0.375, dtype=F32)) == F32(0.375)
 
 
-def _offset_tie_absmax(runs=2):
-    """Absmax values in adjacent pairs 0.5 + t, 0.5 - t (each pair sums to 1
-    exactly, so the mean is 0.5), t = (j + 1/2) / 1024 or j / 1024 with
-    max t = 127/1024 in every run of 256: c2 = 2^-10 and d / c2 = +-(j + 1/2)."""
-    from fractions import Fraction as Fr
-    a, want = [], []
-    for r in range(runs):
-        for p in range(128):
-            t = Fr(127, 1024) if p == 0 else (Fr(2 * ((5 * p) % 127) + 1, 2048) if p % 2 else Fr((3 * p) % 128, 1024))
-            for sgn in (1, -1):
-                a.append(F32(float(Fr(1, 2) + sgn * t)))
-                assert Fr(float(a[-1])) == Fr(1, 2) + sgn * t
-                want.append(TI.round_half_even(sgn * t * 1024))
-    return np.array(a, dtype=F32), np.array(want, dtype=np.int8)
-
-
 def test_double_quant_offset_ties_and_literal():
-    a, want = _offset_tie_absmax()
+    a, want = TI.offset_tie_absmax()
     q2, c2, off = O.double_quant_offset(a, 256)
     assert off == F32(0.5) and np.all(c2 == F32(2.0 ** -10))
     assert np.array_equal(q2, want)
@@ -768,7 +752,7 @@ def test_nf4dqo_lossless_blocks_dequant_exact():
     variant reproduces exactly: the dequantized weight is W (fp32) exactly
     and its bf16 rounding equals torch's; the 4-bit codes equal those of
     plain NF4 (they come from the un-quantized absmax)."""
-    a, _ = _offset_tie_absmax()
+    a, _ = TI.offset_tie_absmax()
     # lossless: integer t, keep pairs; replace the half-integer ones by integers
     a = np.where(np.abs((a.astype(np.float64) - 0.5) * 1024 % 1) > 0, F32(0.5), a).astype(F32)
     rng = np.random.default_rng(350)

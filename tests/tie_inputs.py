@@ -140,3 +140,18 @@ def nf4_power_of_two_blocks(rows: int = 128, k: int = 256, seed: int = 17):
         pat[rng.integers(0, 64)] = 1 if rng.random() < 0.5 else -1
         W[b] = (pat * a).astype(F32)
     return W.reshape(rows, k)
+
+
+def offset_tie_absmax(runs=2):
+    """Absmax values in adjacent pairs 0.5 + t, 0.5 - t (each pair sums to 1
+    exactly, so the mean is 0.5), t = (j + 1/2) / 1024 or j / 1024 with
+    max t = 127/1024 in every run of 256: c2 = 2^-10 and d / c2 = +-(j + 1/2)."""
+    a, want = [], []
+    for r in range(runs):
+        for p in range(128):
+            t = Fraction(127, 1024) if p == 0 else (Fraction(2 * ((5 * p) % 127) + 1, 2048) if p % 2 else Fraction((3 * p) % 128, 1024))
+            for sgn in (1, -1):
+                a.append(F32(float(Fraction(1, 2) + sgn * t)))
+                assert Fraction(float(a[-1])) == Fraction(1, 2) + sgn * t
+                want.append(round_half_even(sgn * t * 1024))
+    return np.array(a, dtype=F32), np.array(want, dtype=np.int8)

@@ -3,7 +3,8 @@
     python -m group_wise_minmax_amd.build        # or __graft_entry__.build()
 
 Every call recompiles every source.  The shared library lands next to this
-file, where the Python binding loads it.
+file, where the Python binding loads it.  The benchmark's streaming-read
+ceiling (bench_stream.hip, not part of liblbq) is built beside bench.py.
 """
 from __future__ import annotations
 
@@ -49,10 +50,27 @@ def _compile(src: str) -> str:
     return obj
 
 
+# The benchmark's streaming-read ceiling (not part of liblbq), beside bench.py.
+BENCH_STREAM_SRC = os.path.join(ROOT, "bench_stream.hip")
+BENCH_STREAM_LIB = os.path.join(ROOT, "libbench_stream.so")
+
+
+def _build_bench_stream() -> str:
+    tmp = BENCH_STREAM_LIB + ".tmp"
+    cmd = [hipcc(), *COMMON, "-shared", BENCH_STREAM_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, BENCH_STREAM_LIB)
+    return BENCH_STREAM_LIB
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES) + 1)) as ex:
+        bench_lib = ex.submit(_build_bench_stream)
         objs = list(ex.map(_compile, SOURCES))
+        bench_lib.result()
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -224,11 +224,10 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(BwdSet set, int m, uin
     }
     const int go = (int)(nt * gpr);
     if constexpr (T::fmt == FMT_MINMAX && T::compact) {
-      // fp16 scale; zero point packed bits wide (go is a multiple of 64 rows'
-      // entries, so entry go + g_voff has the parity of g_voff)
-      md_s = f16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r_s, g_voff * 2, go * 2, 0));
-      md_i = zero_from_byte<KIND>(
-          __builtin_amdgcn_raw_buffer_load_b8(r_z, g_voff * T::bits / 8, go * T::bits / 8, 0), g_voff);
+      // fp16 scale bits and the packed zero byte, as loaded (decoded in
+      // store_stage: a use here would make the wave wait for the load)
+      md_s = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b16(r_s, g_voff * 2, go * 2, 0));
+      md_i = __builtin_amdgcn_raw_buffer_load_b8(r_z, g_voff * T::bits / 8, go * T::bits / 8, 0);
     } else if constexpr (T::fmt == FMT_MINMAX) {
       md_s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, g_voff * 4, go * 4, 0));
       md_i = __builtin_amdgcn_raw_buffer_load_b8(r_z, g_voff, go, 0);
@@ -259,8 +258,16 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(BwdSet set, int m, uin
     // scale (MinMax: and z*s; NF4: the block absmax) of row 4q + r
     float sc[4], zc[4];
     if constexpr (T::fmt == FMT_MINMAX) {
-      gather_rows4(md_s, sc);
-      gather_rows4((float)md_i * md_s, zc);
+      float s_ = md_s;
+      int z_ = md_i;
+      if constexpr (T::compact) {
+        // go is a multiple of 64 rows' entries, so entry go + g_voff has the
+        // parity of g_voff within its zero byte
+        s_ = f16_bits_to_f32(__float_as_uint(md_s));
+        z_ = zero_from_byte<KIND>((uint32_t)md_i, g_voff);
+      }
+      gather_rows4(s_, sc);
+      gather_rows4((float)z_ * s_, zc);
     } else {
       gather_rows4(T::dqo ? (float)md_i * md_s + md_off : (T::dq ? (float)md_i * md_s : md_s), sc);
     }

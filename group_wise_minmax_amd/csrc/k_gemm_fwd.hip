@@ -164,6 +164,7 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
   float mb0 = 0.f, mb1 = 0.f, mb2 = 0.f, mb3 = 0.f;  // scales / absmax of the batch
   uint32_t mb_b = 0;                                 // zero points / absmax codes of the batch
   int md_j = 0;  // entry of the loaded stage in the batch (the same in every lane)
+  int64_t md_gi = 0;  // metadata entry of the loaded stage (compact zero points)
   auto load_stage = [&](int64_t kt) {
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
@@ -195,9 +196,13 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
         if constexpr (T::fmt == FMT_MINMAX || T::dq) mb_b = *reinterpret_cast<const uint32_t*>(mb_arr + gi);
       } else {
         if constexpr (T::fmt == FMT_MINMAX) {
-          const float v = minmax_scale<KIND>(w, gi);
+          // raw words (compact: fp16 bits and the packed zero byte), decoded
+          // in store_stage so that no wave waits for them here
+          const MetaRaw r = load_meta_raw<KIND>(w, gi);
+          const float v = __uint_as_float(r.s);
           mb0 = v, mb1 = v, mb2 = v, mb3 = v;
-          mb_b = (uint32_t)minmax_zero<KIND>(w, gi);
+          mb_b = r.z;
+          md_gi = gi;
         } else {
           if constexpr (!T::dq) {
             const float v = mf_arr[gi];
@@ -218,7 +223,12 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
     {
       const float f01 = (md_j & 1) ? mb1 : mb0, f23 = (md_j & 1) ? mb3 : mb2;
       if constexpr (!T::dq) md_s = (md_j & 2) ? f23 : f01;
-      if constexpr (T::fmt == FMT_MINMAX) md_i = (int)((mb_b >> (8 * md_j)) & 0xFFu);
+      if constexpr (T::compact) {
+        md_s = f16_bits_to_f32(__float_as_uint(md_s));
+        md_i = zero_from_byte<KIND>(mb_b, md_gi);
+      } else if constexpr (T::fmt == FMT_MINMAX) {
+        md_i = (int)((mb_b >> (8 * md_j)) & 0xFFu);
+      }
       if constexpr (T::dq) md_i = (int)(int8_t)(uint8_t)((mb_b >> (8 * md_j)) & 0xFFu);
     }
     float ws_s, ws_zs = 0.f;

@@ -145,8 +145,8 @@ __device__ __forceinline__ float chunk_dot(const u32x4_t& wq, const uint32_t* xa
 template <int KIND, int R, int CB>
 struct Step {
   u32x4_t wq[CB][R];
-  float sc[CB][R];
-  int zq[CB][R];
+  uint32_t sc[CB][R];  // raw metadata as loaded (load_meta)
+  uint32_t zq[CB][R];
   u32x4_t xv[CB][Gemv1Traits<KIND>::XQ];  // x of the chunk (global-x mode only)
 };
 
@@ -203,32 +203,51 @@ __device__ __forceinline__ void meta_rsrc(const WView& w, int64_t nmeta, __amdgp
   }
 }
 
-// Metadata of entry gc of row `row` (gpr entries per row): the scale (MinMax
-// s, or the NF4 block absmax, decoded) and the MinMax zero point (0 for NF4).
-// The row offset is wave-uniform (a scalar offset), gc the lane's.
+// Metadata of entry gc of row `row` (gpr entries per row), as loaded: the
+// raw scale word (MinMax fp32 or fp16 bits, NF4 absmax or second-level
+// scale) and the raw zero-point / absmax-code byte.  Nothing is computed on
+// the loaded values here: a use right after the load would make the wave wait
+// for it at once and empty the prefetch ring; meta_scale / meta_zero decode
+// them where the step is consumed.  The row offset is wave-uniform (a scalar
+// offset), gc the lane's.
 template <int KIND>
 __device__ __forceinline__ void load_meta(__amdgpu_buffer_rsrc_t r_s, __amdgpu_buffer_rsrc_t r_z, int row, int gpr,
-                                          int gc, float dqoff, float& sc, int& zq) {
+                                          int gc, uint32_t& sraw, uint32_t& zraw) {
   using T = WKindTraits<KIND>;
   if constexpr (T::fmt == FMT_MINMAX && T::compact) {
     // fp16 scales; zero points packed bits wide (rows hold whole bytes)
-    const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(r_s, (uint32_t)gc * 2u, row * gpr * 2, 0);
-    const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b8(r_z, (uint32_t)(gc * T::bits / 8), row * gpr * T::bits / 8, 0);
-    sc = f16_bits_to_f32(h);
-    zq = zero_from_byte<KIND>(zb, gc);
+    sraw = __builtin_amdgcn_raw_buffer_load_b16(r_s, (uint32_t)gc * 2u, row * gpr * 2, 0);
+    zraw = __builtin_amdgcn_raw_buffer_load_b8(r_z, (uint32_t)(gc * T::bits / 8), row * gpr * T::bits / 8, 0);
   } else if constexpr (T::fmt == FMT_MINMAX) {
-    sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)gc * 4u, row * gpr * 4, 0));
-    zq = __builtin_amdgcn_raw_buffer_load_b8(r_z, (uint32_t)gc, row * gpr, 0);
+    sraw = __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)gc * 4u, row * gpr * 4, 0);
+    zraw = __builtin_amdgcn_raw_buffer_load_b8(r_z, (uint32_t)gc, row * gpr, 0);
   } else if constexpr (T::dq) {
-    const int q2 = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(r_z, (uint32_t)gc, row * gpr, 0);
-    const float c2 = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)((row * gpr + gc) >> 8) * 4u, 0, 0));
-    sc = T::dqo ? (float)q2 * c2 + dqoff : (float)q2 * c2;
-    zq = 0;
+    zraw = __builtin_amdgcn_raw_buffer_load_b8(r_z, (uint32_t)gc, row * gpr, 0);
+    sraw = __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)((row * gpr + gc) >> 8) * 4u, 0, 0);
   } else {
-    sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)gc * 4u, row * gpr * 4, 0));
-    zq = 0;
+    sraw = __builtin_amdgcn_raw_buffer_load_b32(r_s, (uint32_t)gc * 4u, row * gpr * 4, 0);
+    zraw = 0;
   }
+}
+// The scale of a loaded entry: MinMax s, or the NF4 block absmax (decoded
+// from the int8 code and second-level scale under double quantization).
+template <int KIND>
+__device__ __forceinline__ float meta_scale(uint32_t sraw, uint32_t zraw, float dqoff) {
+  using T = WKindTraits<KIND>;
+  if constexpr (T::fmt == FMT_MINMAX) {
+    return scale_from_bits<KIND>(sraw);
+  } else if constexpr (T::dq) {
+    const float p = (float)(int)(int8_t)(uint8_t)zraw * __uint_as_float(sraw);
+    return T::dqo ? p + dqoff : p;
+  } else {
+    return __uint_as_float(sraw);
+  }
+}
+// The MinMax zero point of entry gc of a row (rows hold whole bytes of zero
+// points, so the row's offset does not change the field's position).
+template <int KIND>
+__device__ __forceinline__ int meta_zero(uint32_t zraw, int gc) {
+  return zero_from_byte<KIND>(zraw, gc);
 }
 
 // The work of one wave (and its share of the workgroup prologue): weight `w`,
@@ -279,7 +298,7 @@ __device__ __forceinline__ void gemv1_body(const WView& w, uint16_t* __restrict_
         const int row = (int)min((int64_t)g * R + r, w.n - 1);
         st.wq[cb][r] = __builtin_bit_cast(
             u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_w, (uint32_t)c * 16u, row * KB, 2 /*nt*/));
-        load_meta<KIND>(r_s, r_z, row, gpr, gc, dqoff, st.sc[cb][r], st.zq[cb][r]);
+        load_meta<KIND>(r_s, r_z, row, gpr, gc, st.sc[cb][r], st.zq[cb][r]);
       }
       if constexpr (XG) {
 #pragma unroll
@@ -353,9 +372,10 @@ __device__ __forceinline__ void gemv1_body(const WView& w, uint16_t* __restrict_
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const float p = chunk_dot<KIND>(st.wq[cb][r], xa, lut, lane32);
-        const float sr = (cok && (int64_t)g * R + r < w.n) ? st.sc[cb][r] : 0.f;
+        const float sr = (cok && (int64_t)g * R + r < w.n) ? meta_scale<KIND>(st.sc[cb][r], st.zq[cb][r], dqoff) : 0.f;
         if constexpr (T::fmt == FMT_MINMAX) {
-          acc[r] = fmaf(sr, fmaf(-(float)(128 + st.zq[cb][r]), xs, p), acc[r]);
+          const int z = meta_zero<KIND>(st.zq[cb][r], (c * CPC) / GRP);
+          acc[r] = fmaf(sr, fmaf(-(float)(128 + z), xs, p), acc[r]);
         } else {
           acc[r] = fmaf(sr, p, acc[r]);
         }
@@ -546,7 +566,7 @@ __device__ __forceinline__ void gemvm_body(const WView& w, uint16_t* __restrict_
         const int row = (int)min((int64_t)g * R + r, w.n - 1);
         st.wq[cb][r] = __builtin_bit_cast(
             u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_w, (uint32_t)c * 16u, row * KB, 2 /*nt*/));
-        load_meta<KIND>(r_s, r_z, row, gpr, gc, dqoff, st.sc[cb][r], st.zq[cb][r]);
+        load_meta<KIND>(r_s, r_z, row, gpr, gc, st.sc[cb][r], st.zq[cb][r]);
       }
     }
   };
@@ -616,9 +636,10 @@ __device__ __forceinline__ void gemvm_body(const WView& w, uint16_t* __restrict_
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const float p = dot_pairs<XD>(wv[r], xa);
-          const float sr = (cok && (int64_t)g * R + r < w.n) ? st.sc[cb][r] : 0.f;
+          const float sr = (cok && (int64_t)g * R + r < w.n) ? meta_scale<KIND>(st.sc[cb][r], st.zq[cb][r], dqoff) : 0.f;
           if constexpr (T::fmt == FMT_MINMAX) {
-            acc[r][v] = fmaf(sr, fmaf(-(float)(128 + st.zq[cb][r]), xs, p), acc[r][v]);
+            const int z = meta_zero<KIND>(st.zq[cb][r], (c * CPC) / GRP);
+            acc[r][v] = fmaf(sr, fmaf(-(float)(128 + z), xs, p), acc[r][v]);
           } else {
             acc[r][v] = fmaf(sr, p, acc[r][v]);
           }

@@ -95,14 +95,33 @@ __device__ __forceinline__ int x_off(int lg, int t) {
   return 64 * (t >> 1) + 16 * lg + 8 * (t & 1);
 }
 
+// LDS of one workgroup, declared by the kernel and sized for the weight kinds
+// its tiles may take: packed rows of pitch RBP_, NG_ metadata entries per
+// row and chunk, the NF4 table (LUT entries) when a kind needs it.
+template <int RBP_, int NG_, int MB, int LUT>
+struct SkLds {
+  uint8_t Ws[2][ROWS * RBP_];
+  uint16_t Xs[2][MB * 16 * (KC + 8)];
+  float2 meta[2][ROWS][NG_];  // (scale, 128 + zero) or (absmax, 0)
+  uint32_t lut[LUT];
+  float cbs[16];
+};
+template <int KIND, int MB>
+using SkLdsOf = SkLds<SkTraits<KIND>::RBP, KC / SkTraits<KIND>::GRP, MB,
+                      WKindTraits<KIND>::fmt == FMT_NF4 ? 256 * kLutCopies : 1>;
+// A workgroup of the INT4 g128 / INT2 g64 mix holds either kind's tile.
+template <int MB>
+using SkLdsMix = SkLds<SkTraits<WK_I4G128>::RBP, KC / SkTraits<WK_I2G64>::GRP, MB, 1>;
+
 // Row tile `tile` (ROWS rows of W) over K range `split` of ks_count; with
 // `part` set, the fp32 sums go to part[split][m][n], else bf16 to Y.
-template <int KIND, int MB>
+template <int KIND, int MB, typename LDS>
 __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __restrict__ X, int m,
                                             uint16_t* __restrict__ Y, int64_t ldy,
                                             const int32_t* __restrict__ out_rows,
                                             float* __restrict__ part, int ks_count,
-                                            const LoraEpi& lora, const Nf4Table& tab, int tile, int split) {
+                                            const LoraEpi& lora, const Nf4Table& tab, int tile, int split,
+                                            LDS& lds) {
   using T = WKindTraits<KIND>;
   using S = SkTraits<KIND>;
   constexpr int RB = S::RB, RBP = S::RBP, KSG = S::KSG, GRP = S::GRP;
@@ -111,11 +130,14 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
   constexpr int WCOL = RB / 16;         // 16-byte W columns per row
   constexpr int WLD = ROWS * WCOL / kThreads;   // W loads per thread per chunk
   constexpr int XLD = MB * 16 * (KC / 8) / kThreads;  // X loads per thread per chunk
-  __shared__ __attribute__((aligned(16))) uint8_t Ws[2][ROWS * RBP];
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][MB * 16 * LDX];
-  __shared__ float2 meta[2][ROWS][NG];  // (scale, 128 + zero) or (absmax, 0)
-  __shared__ uint32_t lut[T::fmt == FMT_NF4 ? 256 * kLutCopies : 1];
-  __shared__ float cbs[16];
+  static_assert(sizeof(lds.Ws[0]) >= ROWS * RBP && sizeof(lds.Xs[0]) == MB * 16 * LDX * 2, "tile LDS");
+  static_assert(sizeof(lds.meta[0][0]) >= NG * sizeof(float2), "tile LDS");
+  static_assert(T::fmt != FMT_NF4 || sizeof(lds.lut) >= 256 * kLutCopies * 4, "tile LDS");
+  auto& Ws = lds.Ws;
+  auto& Xs = lds.Xs;
+  auto& meta = lds.meta;
+  uint32_t* const lut = lds.lut;
+  float* const cbs = lds.cbs;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -144,7 +166,8 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
 
   // ---- staging of one chunk: packed W rows, arranged X rows, group metadata --
   u32x4_t wr[WLD], xr[XLD];
-  float2 mr;
+  MetaRaw mraw;      // this thread's metadata entry of the loaded chunk, as loaded
+  int64_t mgi = 0;   // its entry index
   auto load = [&](int c) {
     const int64_t kc = (int64_t)c * KC;
     const int64_t kend = (K - kc) < KC ? (K - kc) : KC;  // codes in this chunk (multiple of 64)
@@ -154,9 +177,12 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
       const int row = e / WCOL, col = e % WCOL;
       const int64_t n = min(n0 + row, w.n - 1);
       const bool ok = col * 16 * 8 / T::bits < kend;
+      // Past the chunk's end (a last, partial chunk) the load reads the
+      // chunk's first bytes instead; compute() stops at the first group at or
+      // past kend, so those LDS bytes are never used.  (Zeroing them here
+      // would make the wave wait for the load at once.)
       const int64_t off = n * KB + kc * T::bits / 8 + (ok ? col * 16 : 0);
       wr[i] = *reinterpret_cast<const u32x4_t*>(w.packed + off);
-      if (!ok) wr[i] = u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < XLD; ++i) {
@@ -164,19 +190,14 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
       const int row = e / (KC / 8), col = e % (KC / 8);
       const int64_t mrow = min((int64_t)row, (int64_t)m - 1);
       const bool ok = col * 8 < kend;
-      xr[i] = *reinterpret_cast<const u32x4_t*>(X + mrow * K + kc + (ok ? col * 8 : 0));
-      if (!ok) xr[i] = u32x4_t{0u, 0u, 0u, 0u};
+      xr[i] = *reinterpret_cast<const u32x4_t*>(X + mrow * K + kc + (ok ? col * 8 : 0));  // as above
     }
     {
       const int row = tid / 4, j = tid % 4;
       const int64_t n = min(n0 + row, w.n - 1);
       const bool ok = j < NG && (int64_t)j * GRP < kend;
-      const int64_t gi = n * gpr + (ok ? (kc / GRP + j) : 0);
-      if constexpr (T::fmt == FMT_MINMAX) {
-        mr = make_float2(minmax_scale<KIND>(w, gi), (float)(128 + minmax_zero<KIND>(w, gi)));
-      } else {
-        mr = make_float2(nf4_block_scale<KIND>(w, gi, dqoff), 0.f);
-      }
+      mgi = n * gpr + (ok ? (kc / GRP + j) : 0);
+      mraw = load_meta_raw<KIND>(w, mgi);  // decoded in store(), one chunk later
     }
   };
   auto store = [&](int b) {
@@ -190,7 +211,11 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
       const int e = tid + kThreads * i;
       *reinterpret_cast<u32x4_t*>(&Xs[b][(e / (KC / 8)) * LDX + (e % (KC / 8)) * 8]) = arrange8<KIND>(xr[i]);
     }
-    if (tid / 4 < ROWS && tid % 4 < NG) meta[b][tid / 4][tid % 4] = mr;
+    if (tid / 4 < ROWS && tid % 4 < NG) {
+      const float sc = meta_raw_scale<KIND>(mraw, dqoff);
+      meta[b][tid / 4][tid % 4] =
+          make_float2(sc, T::fmt == FMT_MINMAX ? (float)(128 + meta_raw_zero<KIND>(mraw, mgi)) : 0.f);
+    }
   };
 
   f32x4_t acc[MB];
@@ -276,7 +301,8 @@ __global__ __launch_bounds__(kThreads) void k_skinny(WView w, const uint16_t* __
                                                     const int32_t* __restrict__ out_rows,
                                                     float* __restrict__ part, int ks_count,
                                                     LoraEpi lora, Nf4Table tab) {
-  skinny_tile<KIND, MB>(w, X, m, Y, ldy, out_rows, part, ks_count, lora, tab, blockIdx.x, blockIdx.y);
+  __shared__ __attribute__((aligned(16))) SkLdsOf<KIND, MB> lds;
+  skinny_tile<KIND, MB>(w, X, m, Y, ldy, out_rows, part, ks_count, lora, tab, blockIdx.x, blockIdx.y, lds);
 }
 
 // Several weights that share X in one launch.  Each keeps the K split it
@@ -307,8 +333,36 @@ __global__ __launch_bounds__(kThreads) void k_skinny_set(SkinnySet set, const ui
   const int tiles = (int)((set.w[pi].n + ROWS - 1) / ROWS);
   const int r = b - wbeg;
   const LoraEpi none{nullptr, nullptr, 0, 0};
+  __shared__ __attribute__((aligned(16))) SkLdsOf<KIND, MB> lds;
   skinny_tile<KIND, MB>(set.w[pi], X, m, set.y[pi], set.ldy[pi], set.out_rows[pi],
-                        ks == 1 ? nullptr : part + set.part_off[pi], ks, none, tab, r % tiles, r / tiles);
+                        ks == 1 ? nullptr : part + set.part_off[pi], ks, none, tab, r % tiles, r / tiles, lds);
+}
+
+// The INT4 g128 and INT2 g64 row sets of channel-mixed linears that share X
+// in one launch: set entries [0, first_b) are INT4 g128, the rest INT2 g64.
+// A workgroup's tile belongs to one weight and runs that weight's format;
+// each weight keeps the K split it has alone, so the outputs equal those of
+// the per-format launches bit for bit.
+template <int MB>
+__global__ __launch_bounds__(kThreads) void k_skinny_mix(SkinnySet set, const uint16_t* __restrict__ X, int m,
+                                                        float* __restrict__ part, Nf4Table tab, int first_b) {
+  const int b = blockIdx.x;
+  int pi = 0, wbeg = 0;
+#pragma unroll
+  for (int i = 1; i < kGemvMaxGroup; ++i)
+    if (i < set.count && b >= set.wg_end[i - 1]) { pi = i; wbeg = set.wg_end[i - 1]; }
+  const int ks = set.ks[pi];
+  const int tiles = (int)((set.w[pi].n + ROWS - 1) / ROWS);
+  const int r = b - wbeg;
+  const LoraEpi none{nullptr, nullptr, 0, 0};
+  float* const p = ks == 1 ? nullptr : part + set.part_off[pi];
+  __shared__ __attribute__((aligned(16))) SkLdsMix<MB> lds;
+  if (pi < first_b)
+    skinny_tile<WK_I4G128, MB>(set.w[pi], X, m, set.y[pi], set.ldy[pi], set.out_rows[pi], p, ks, none, tab,
+                               r % tiles, r / tiles, lds);
+  else
+    skinny_tile<WK_I2G64, MB>(set.w[pi], X, m, set.y[pi], set.ldy[pi], set.out_rows[pi], p, ks, none, tab,
+                              r % tiles, r / tiles, lds);
 }
 
 // Y[m][col(n)] = bf16( sum over K ranges of part + LoRA term ).  Row mr =
@@ -422,6 +476,46 @@ struct SkinnyLauncher {
   }
 };
 
+// The set's per-weight tiles, K splits and partial-sum areas.
+void plan_skinny_set(const WView* ws, uint16_t* const* ys, const int64_t* ldys, const int32_t* const* out_rows,
+                     int count, int64_t m, SkinnySet& set, int64_t& wgs, int64_t& ncol, bool& reduce) {
+  set = SkinnySet{};
+  set.count = count;
+  wgs = 0;
+  ncol = 0;
+  int64_t off = 0;
+  reduce = false;
+  for (int i = 0; i < count; ++i) {
+    set.w[i] = ws[i];
+    set.y[i] = ys[i];
+    set.ldy[i] = ldys[i];
+    set.out_rows[i] = out_rows[i];
+    const int ks = skinny_splits(ws[i].n, ws[i].k, m);
+    set.ks[i] = ks;
+    wgs += (ws[i].n + ROWS - 1) / ROWS * ks;
+    set.wg_end[i] = (int)wgs;
+    ncol += ws[i].n;
+    set.col_end[i] = ncol;
+    set.part_off[i] = off;  // weight i's partials: [ks][m][n_i], when ks > 1
+    if (ks > 1) {
+      off += (int64_t)ks * m * ws[i].n;
+      reduce = true;
+    }
+  }
+}
+
+template <int MB>
+hipError_t launch_mix_mb(const SkinnySet& set, int64_t wgs, int64_t ncol, bool reduce, const uint16_t* X, int64_t m,
+                         float* part, const Nf4Table& tab, int first_b, hipStream_t s) {
+  hipLaunchKernelGGL((k_skinny_mix<MB>), dim3((unsigned)wgs), dim3(kThreads), 0, s, set, X, (int)m, part, tab,
+                     first_b);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !reduce) return e;
+  hipLaunchKernelGGL(k_skinny_reduce_set, dim3((unsigned)((ncol + 255) / 256), (unsigned)m), dim3(256), 0, s,
+                     part, (int)m, set);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int skinny_splits(int64_t n, int64_t k, int64_t m) {
@@ -458,28 +552,25 @@ hipError_t launch_skinny_set(WKind kind, const WView* ws, uint16_t* const* ys, c
                              const int32_t* const* out_rows, int count, const uint16_t* X, int64_t m, float* part,
                              const Nf4Table& tab, hipStream_t s) {
   if (count < 1 || count > kGemvMaxGroup || m < 1 || m > kSkinnyMaxM) return hipErrorInvalidValue;
-  SkinnySet set{};
-  set.count = count;
-  int64_t wgs = 0, ncol = 0, off = 0;
-  bool reduce = false;
-  for (int i = 0; i < count; ++i) {
-    set.w[i] = ws[i];
-    set.y[i] = ys[i];
-    set.ldy[i] = ldys[i];
-    set.out_rows[i] = out_rows[i];
-    const int ks = skinny_splits(ws[i].n, ws[i].k, m);
-    set.ks[i] = ks;
-    wgs += (ws[i].n + ROWS - 1) / ROWS * ks;
-    set.wg_end[i] = (int)wgs;
-    ncol += ws[i].n;
-    set.col_end[i] = ncol;
-    set.part_off[i] = off;  // weight i's partials: [ks][m][n_i], when ks > 1
-    if (ks > 1) {
-      off += (int64_t)ks * m * ws[i].n;
-      reduce = true;
-    }
-  }
+  SkinnySet set;
+  int64_t wgs, ncol;
+  bool reduce;
+  plan_skinny_set(ws, ys, ldys, out_rows, count, m, set, wgs, ncol, reduce);
   return dispatch_kind<SkinnySetLauncher>(kind, set, wgs, ncol, reduce, X, m, part, tab, s);
+}
+
+hipError_t launch_skinny_mix(const WView* ws, uint16_t* const* ys, const int64_t* ldys, const int32_t* const* out_rows,
+                             int count_a, int count_b, const uint16_t* X, int64_t m, float* part, const Nf4Table& tab,
+                             hipStream_t s) {
+  const int count = count_a + count_b;
+  if (count_a < 1 || count_b < 1 || count > kGemvMaxGroup || m < 1 || m > kSkinnyMaxM) return hipErrorInvalidValue;
+  SkinnySet set;
+  int64_t wgs, ncol;
+  bool reduce;
+  plan_skinny_set(ws, ys, ldys, out_rows, count, m, set, wgs, ncol, reduce);
+  if (m <= 16) return launch_mix_mb<1>(set, wgs, ncol, reduce, X, m, part, tab, count_a, s);
+  if (m <= 32) return launch_mix_mb<2>(set, wgs, ncol, reduce, X, m, part, tab, count_a, s);
+  return launch_mix_mb<4>(set, wgs, ncol, reduce, X, m, part, tab, count_a, s);
 }
 
 hipError_t launch_skinny(WKind kind, const WView& w, const uint16_t* X, int64_t m, uint16_t* Y,

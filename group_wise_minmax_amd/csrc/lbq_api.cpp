@@ -333,15 +333,38 @@ lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint
   return lbq::linear_fwd_body(desc, q, X, m, Y, ldy, workspace, ws_bytes, stream, "lbq_linear_fwd");
 }
 
+// A grouped call at 2 <= m <= 64 whose weights are all INT4 g128 or INT2 g64,
+// with both formats present and neither served by the multi-row GEMV (the
+// two row sets of channel-mixed linears that share X): one small-batch launch
+// for both formats.
+bool skinny_mix_set(int32_t count, const lbq_desc* descs, int64_t m) {
+  if (m < 2 || m > lbq::kSkinnyMaxM) return false;
+  int ca = 0, cb = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const lbq::WKind kd = kind_of(&descs[i]);
+    if (kd == lbq::WK_I4G128) ++ca;
+    else if (kd == lbq::WK_I2G64) ++cb;
+    else return false;
+  }
+  return ca > 0 && cb > 0 && !lbq::gemvm_fits(lbq::WK_I4G128, descs[0].k, m) &&
+         !lbq::gemvm_fits(lbq::WK_I2G64, descs[0].k, m);
+}
+
 // Weights of one kind in a grouped call run as one launch (one launch pair
 // for the small-batch kernel when it splits K, and up to two GEMM launches
 // when splitting the set fills the chip better), one kind after another on
-// the stream; the workspace holds the partials of the largest kind group.
+// the stream; the workspace holds the partials of the largest kind group (of
+// all the weights when the two channel-mix formats share one launch).
 size_t lbq_linear_fwd_grouped_workspace_bytes(int32_t count, const lbq_desc* descs, int64_t m) {
   if (count < 1 || count > LBQ_MAX_GROUP || descs == nullptr) return 0;
   for (int32_t i = 0; i < count; ++i)
-    if (check_desc(&descs[i]) != LBQ_OK) return 0;
+    if (check_desc(&descs[i]) != LBQ_OK || descs[i].k != descs[0].k) return 0;
   if (m < 2 || m > lbq::kSkinnyMaxM) return 0;
+  if (skinny_mix_set(count, descs, m)) {
+    int64_t ns[LBQ_MAX_GROUP];
+    for (int32_t i = 0; i < count; ++i) ns[i] = descs[i].n;
+    return lbq::skinny_set_workspace_bytes(ns, count, descs[0].k, m);
+  }
   size_t need = 0;
   bool done[LBQ_MAX_GROUP] = {};
   for (int32_t i = 0; i < count; ++i) {
@@ -382,11 +405,13 @@ lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lb
   const lbq::LoraEpi none{nullptr, nullptr, 0, 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  if (m == 1) {
+  if (m == 1 || skinny_mix_set(count, descs, m)) {
     // The INT4 g128 and INT2 g64 row sets of channel-mixed linears (and
-    // nothing else): one launch for both formats.
+    // nothing else): one launch for both formats (m = 1: the GEMV; 2 <= m <=
+    // 64: the small-batch kernel and its reduce).
     lbq::WView ws[LBQ_MAX_GROUP];
     uint16_t* ys[LBQ_MAX_GROUP];
+    int64_t lds[LBQ_MAX_GROUP];
     const int32_t* rows[LBQ_MAX_GROUP];
     int ca = 0, cb = 0;
     for (int pass = 0; pass < 2; ++pass)
@@ -395,11 +420,17 @@ lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lb
           const int j = ca + cb;
           ws[j] = view_of(&descs[i], &qs[i]);
           ys[j] = Ys[i];
+          lds[j] = ldys[i];
           rows[j] = qs[i].out_rows;
           (pass == 0 ? ca : cb)++;
         }
-    if (ca > 0 && cb > 0 && ca + cb == count)
-      return hip_status(lbq::launch_gemv1_mix(ws, ys, rows, ca, cb, X, nf4_table(), s), "lbq_linear_fwd_grouped");
+    if (ca > 0 && cb > 0 && ca + cb == count) {
+      if (m == 1)
+        return hip_status(lbq::launch_gemv1_mix(ws, ys, rows, ca, cb, X, nf4_table(), s), "lbq_linear_fwd_grouped");
+      return hip_status(lbq::launch_skinny_mix(ws, ys, lds, rows, ca, cb, X, m, static_cast<float*>(workspace),
+                                               nf4_table(), s),
+                        "lbq_linear_fwd_grouped");
+    }
   }
   // One launch per distinct weight kind, in order of first appearance, with
   // the kernel lbq_linear_fwd picks for that kind (all weights share k).

@@ -193,10 +193,55 @@ __device__ __forceinline__ int minmax_zero(const WView& w, int64_t gi) {
   return zero_from_byte<KIND>(w.zeros[zero_byte_index<KIND>(gi)], gi);
 }
 
+// The metadata words of entry gi as loaded: the scale word (MinMax fp32 or
+// fp16 bits, NF4 absmax or second-level scale) and the zero-point byte (the
+// int8 absmax code under double quantization).  No arithmetic touches the
+// loaded values, so a prefetch is not waited for where it is issued; decode
+// them where they are used (meta_raw_scale, meta_raw_zero).
+struct MetaRaw {
+  uint32_t s, z;
+};
+template <int KIND>
+__device__ __forceinline__ MetaRaw load_meta_raw(const WView& w, int64_t gi) {
+  using T = WKindTraits<KIND>;
+  MetaRaw r{0u, 0u};
+  if constexpr (T::fmt == FMT_MINMAX && T::compact) {
+    r.s = reinterpret_cast<const uint16_t*>(w.scales)[gi];
+    r.z = w.zeros[gi * T::bits / 8];
+  } else if constexpr (T::fmt == FMT_MINMAX) {
+    r.s = __float_as_uint(w.scales[gi]);
+    r.z = w.zeros[gi];
+  } else if constexpr (T::dq) {
+    r.s = __float_as_uint(w.absmax_scale[gi >> 8]);
+    r.z = (uint8_t)w.absmax_q[gi];
+  } else {
+    r.s = __float_as_uint(w.absmax[gi]);
+  }
+  return r;
+}
 // Per-tensor offset of double quantization with an offset: the entry after
 // the ceil(nb / 256) per-block scales.
 __device__ __forceinline__ float nf4_dq_offset(const WView& w) {
   return w.absmax_scale[(w.n * w.k / 64 + 255) >> 8];
+}
+
+// Decoded scale (MinMax s or the NF4 block absmax) and MinMax zero point of
+// a MetaRaw loaded for entry gi.
+template <int KIND>
+__device__ __forceinline__ float meta_raw_scale(const MetaRaw& r, float off) {
+  using T = WKindTraits<KIND>;
+  if constexpr (T::fmt == FMT_MINMAX) {
+    return T::compact ? f16_bits_to_f32(r.s) : __uint_as_float(r.s);
+  } else if constexpr (T::dq) {
+    const float p = (float)(int)(int8_t)(uint8_t)r.z * __uint_as_float(r.s);
+    return T::dqo ? p + off : p;
+  } else {
+    return __uint_as_float(r.s);
+  }
+}
+template <int KIND>
+__device__ __forceinline__ int meta_raw_zero(const MetaRaw& r, int64_t gi) {
+  return zero_from_byte<KIND>(r.z, gi);
 }
 
 // Block absmax of NF4 block `blk`: fp32, fl(q2 * c2) under double quant, or

@@ -99,6 +99,13 @@ size_t skinny_set_workspace_bytes(const int64_t* ns, int count, int64_t k, int64
 hipError_t launch_skinny_set(WKind kind, const WView* ws, uint16_t* const* ys, const int64_t* ldys,
                              const int32_t* const* out_rows, int count, const uint16_t* X, int64_t m, float* part,
                              const Nf4Table& tab, hipStream_t s);
+// The INT4 g128 weights ws[0, count_a) and INT2 g64 weights ws[count_a,
+// count_a + count_b) (same k) in one small-batch launch (plus one reduce),
+// each weight with the K split it has alone: outputs equal the per-format
+// launches'.  Workspace: skinny_set_workspace_bytes() over all the weights.
+hipError_t launch_skinny_mix(const WView* ws, uint16_t* const* ys, const int64_t* ldys, const int32_t* const* out_rows,
+                             int count_a, int count_b, const uint16_t* X, int64_t m, float* part, const Nf4Table& tab,
+                             hipStream_t s);
 size_t skinny_workspace_bytes(int64_t n, int64_t k, int64_t m, bool lora);
 hipError_t launch_skinny(WKind kind, const WView& w, const uint16_t* X, int64_t m, uint16_t* Y,
                          int64_t ldy, const int32_t* out_rows, float* part, const LoraEpi& lora,

@@ -118,6 +118,7 @@ TRAFFIC_KERNELS = {
     "gemvm_m4": ("k_gemvm<0,", "k_gemvm_set<0,"),
     "skinny_m16": ("k_skinny<0,", "k_skinny_set<0,"),
     "skinny_reduce_m16": ("k_skinny_reduce",),
+    "skinny_mix_m40": ("k_skinny_mix<",),
     "quant_int4": ("k_quant_minmax<4, 128, false>",),
     "quant_nf4dq": ("k_quant_nf4<1,",),
     "dequant_nf4dq": ("k_dequant<5>",),
@@ -159,6 +160,79 @@ def write_traffic(fetch_csv: str, write_csv: str) -> dict:
     return out
 
 
+SIMDS = 256 * 4                 # MI355X: 256 CUs x 4 SIMDs
+SCLK_HZ = 2.4e9                 # MI355X peak engine clock
+
+
+def _short_kernel(name: str) -> str:
+    return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").replace("lbq::", "")
+
+
+def counter_summary(csvs, out_md: str, commands=(), match: str = "lbq::") -> None:
+    """Per kernel (name + grid), the mean of every counter over its dispatches
+    in one or more rocprofv3 --pmc CSVs (each pass its own run of the same
+    bench.py command), and the figures derived from them:
+      TF/s        SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flop / duration
+      MFMA busy   SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x duration x 2.4 GHz)
+      VALU/MFMA   (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA
+      LDS conf    SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
+      wait, issue, valu, lds, vmem
+                  SQ_WAIT_ANY, SQ_WAIT_INST_ANY, SQ_ACTIVE_INST_VALU,
+                  SQ_ACTIVE_INST_LDS, SQ_ACTIVE_INST_VMEM / SQ_WAVE_CYCLES
+    Durations are the counter run's own (dispatches serialised)."""
+    import csv
+    import numpy as np
+    acc = {}
+    for path in csvs:
+        disp = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if match not in r["Kernel_Name"]:
+                    continue
+                key = (_short_kernel(r["Kernel_Name"]), int(r["Grid_Size"]) // int(r["Workgroup_Size"]))
+                d = disp.setdefault((key, r["Dispatch_Id"]), {"dur": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
+                d[r["Counter_Name"]] = float(r["Counter_Value"])
+        for (key, _), d in disp.items():
+            for c, v in d.items():
+                acc.setdefault(key, {}).setdefault(c, []).append(v)
+    lines = ["# Hardware counters per kernel and grid (rocprofv3 --pmc)", ""]
+    if commands:
+        lines += ["Commands (on the MI355X box, from the repository root `$R`; one counter pass per run):", ""]
+        lines += ["    " + c for c in commands] + [""]
+    lines += ["Derived figures: TF/s = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / duration; MFMA busy = "
+              "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x duration x 2.4 GHz); VALU/MFMA = (SQ_INSTS_VALU - "
+              "SQ_INSTS_MFMA) / SQ_INSTS_MFMA; LDS conf = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; wait / issue / "
+              "valu / lds / vmem = SQ_WAIT_ANY / SQ_WAIT_INST_ANY / SQ_ACTIVE_INST_VALU / SQ_ACTIVE_INST_LDS / "
+              "SQ_ACTIVE_INST_VMEM over SQ_WAVE_CYCLES.  Durations (us) are the counter runs' own.", "",
+              "| kernel | workgroups | n | us | TF/s | MFMA busy | VALU/MFMA | LDS conf | wait | issue | valu | lds | vmem |",
+              "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+
+    def m(d, c):
+        return float(np.mean(d[c])) if c in d else None
+
+    def fmt(x, p=3):
+        return "" if x is None else f"{x:.{p}f}"
+
+    raw = {}
+    for key, d in sorted(acc.items(), key=lambda kv: -sum(kv[1]["dur"])):
+        dur = m(d, "dur")
+        mops, busy = m(d, "SQ_INSTS_VALU_MFMA_MOPS_BF16"), m(d, "SQ_VALU_MFMA_BUSY_CYCLES")
+        valu, mf = m(d, "SQ_INSTS_VALU"), m(d, "SQ_INSTS_MFMA")
+        conf, act = m(d, "SQ_LDS_BANK_CONFLICT"), m(d, "SQ_LDS_IDX_ACTIVE")
+        wc = m(d, "SQ_WAVE_CYCLES")
+        share = {c: (m(d, c) / wc if wc and m(d, c) is not None else None)
+                 for c in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM")}
+        tf = mops * 512 / dur / 1e12 if mops else None
+        mb = busy / (SIMDS * dur * SCLK_HZ) if busy is not None else None
+        vpm = (valu - mf) / mf if valu is not None and mf else None
+        lc = conf / act if conf is not None and act else None
+        lines.append(f"| `{key[0]}` | {key[1]} | {len(d['dur'])} | {dur * 1e6:.1f} | {fmt(tf, 0)} | {fmt(mb)} | {fmt(vpm, 2)} | "
+                     f"{fmt(lc)} | " + " | ".join(fmt(share[c]) for c in share) + " |")
+        raw[f"{key[0]} [{key[1]}]"] = {c: round(float(np.mean(v)), 1) for c, v in d.items() if c != "dur"}
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n\nMean counter values per dispatch:\n\n```json\n" + json.dumps(raw, indent=1) + "\n```\n")
+
+
 def trace_summary(trace_csv: str, phases_json: str, out_md: str, command: str = "") -> None:
     """Per phase and per launch shape (kernel name + grid), the count and the
     median / p10 / p90 / mean duration of the dispatches of a rocprofv3
@@ -182,7 +256,7 @@ def trace_summary(trace_csv: str, phases_json: str, out_md: str, command: str = 
     seg, segs = None, []
     for s, e, name, grid in rows:
         if "FillFunctor<double>" in name:  # the phase marker (nothing else here fills doubles)
-            if seg is not None:
+            if seg:  # two markers in a row (an older run's zero-filled marker) bound no phase
                 segs.append(seg)
             seg = []
             continue
@@ -453,7 +527,7 @@ def build_workload(L, SI, torch, dev, R, want):
         for i, nm in enumerate(n70):
             n, k = s70[nm]
             w = SI.dev_gaussian_weights(SI.seed_of(4, i, SI.SLOT_W), n, k, dev)
-            if need("chmix_70b_m1", "chmix_70b_m1024"):
+            if need("chmix_70b_m1", "chmix_70b_m3", "chmix_70b_m16", "chmix_70b_m40", "chmix_70b_m1024"):
                 rows4 = SI.dev_channel_mask(SI.seed_of(4, i, SI.SLOT_CHMASK), n, dev)
                 mask = torch.zeros(n, dtype=torch.bool, device=dev)
                 mask[rows4.long()] = True
@@ -786,12 +860,19 @@ def main():
     ap.add_argument("--trace-summary", nargs=3, metavar=("TRACE_CSV", "PHASES_JSON", "OUT_MD"),
                     help="summarize a rocprofv3 kernel trace per phase and launch shape and exit")
     ap.add_argument("--trace-command", default="", help="command line recorded in the trace summary")
+    ap.add_argument("--counter-summary", nargs="+", metavar="CSV_OR_OUT",
+                    help="summarize rocprofv3 --pmc CSVs (one per counter pass) into the markdown file given "
+                         "last and exit; --trace-command may repeat the commands, separated by ' ;; '")
     args = ap.parse_args()
     if args.traffic_from:
         print(json.dumps(write_traffic(*args.traffic_from)), flush=True)
         return
     if args.trace_summary:
         trace_summary(*args.trace_summary, command=args.trace_command)
+        return
+    if args.counter_summary:
+        cmds = [c.strip() for c in args.trace_command.split(";;") if c.strip()]
+        counter_summary(args.counter_summary[:-1], args.counter_summary[-1], cmds)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -840,7 +921,7 @@ def main():
                 run()
     torch.cuda.synchronize()
 
-    marker = torch.zeros(1, device=dev, dtype=torch.float64) if args.mark_phases else None
+    marker = torch.empty(1, device=dev, dtype=torch.float64) if args.mark_phases else None
     if args.mark_phases:
         with open(args.mark_phases, "w") as fh:
             json.dump({"phases": [name for name, _, _ in runners]}, fh)

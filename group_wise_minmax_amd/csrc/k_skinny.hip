@@ -45,7 +45,6 @@ struct SkTraits {
   static constexpr int RB = KC * T::bits / 8;   // packed bytes per row per chunk (128 / 64)
   static constexpr int RBP = RB + 16;           // padded LDS row: conflict-free A reads
   static constexpr int GRP = T::fmt == FMT_MINMAX ? T::group : 64;
-  static constexpr int KSG = GRP / 32;          // k-steps per group / block
 };
 
 // A fragment (8 codes -> 4 dwords of bf16 pairs) for k-step t of row `row`
@@ -96,8 +95,9 @@ __device__ __forceinline__ int x_off(int lg, int t) {
 }
 
 // LDS of one workgroup, declared by the kernel and sized for the weight kinds
-// its tiles may take: packed rows of pitch RBP_, NG_ metadata entries per
-// row and chunk, the NF4 table (LUT entries) when a kind needs it.
+// its tiles may take: packed rows of pitch RBP_, NG_ metadata slots per row
+// and chunk (one per 64 codes; groups of 128 use the first half), the NF4
+// table (LUT entries) when a kind needs it.
 template <int RBP_, int NG_, int MB, int LUT>
 struct SkLds {
   uint8_t Ws[2][ROWS * RBP_];
@@ -107,11 +107,11 @@ struct SkLds {
   float cbs[16];
 };
 template <int KIND, int MB>
-using SkLdsOf = SkLds<SkTraits<KIND>::RBP, KC / SkTraits<KIND>::GRP, MB,
+using SkLdsOf = SkLds<SkTraits<KIND>::RBP, KC / 64, MB,
                       WKindTraits<KIND>::fmt == FMT_NF4 ? 256 * kLutCopies : 1>;
 // A workgroup of the INT4 g128 / INT2 g64 mix holds either kind's tile.
 template <int MB>
-using SkLdsMix = SkLds<SkTraits<WK_I4G128>::RBP, KC / SkTraits<WK_I2G64>::GRP, MB, 1>;
+using SkLdsMix = SkLds<SkTraits<WK_I4G128>::RBP, KC / 64, MB, 1>;
 
 // Row tile `tile` (ROWS rows of W) over K range `split` of ks_count; with
 // `part` set, the fp32 sums go to part[split][m][n], else bf16 to Y.
@@ -124,14 +124,14 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
                                             LDS& lds) {
   using T = WKindTraits<KIND>;
   using S = SkTraits<KIND>;
-  constexpr int RB = S::RB, RBP = S::RBP, KSG = S::KSG, GRP = S::GRP;
+  constexpr int RB = S::RB, RBP = S::RBP, GRP = S::GRP;
   constexpr int NG = KC / GRP;          // groups (blocks) per chunk
   constexpr int LDX = KC + 8;           // padded x row (bf16)
   constexpr int WCOL = RB / 16;         // 16-byte W columns per row
   constexpr int WLD = ROWS * WCOL / kThreads;   // W loads per thread per chunk
   constexpr int XLD = MB * 16 * (KC / 8) / kThreads;  // X loads per thread per chunk
   static_assert(sizeof(lds.Ws[0]) >= ROWS * RBP && sizeof(lds.Xs[0]) == MB * 16 * LDX * 2, "tile LDS");
-  static_assert(sizeof(lds.meta[0][0]) >= NG * sizeof(float2), "tile LDS");
+  static_assert(sizeof(lds.meta[0][0]) == 4 * sizeof(float2) && NG <= 4 && kThreads == 4 * ROWS, "tile LDS");
   static_assert(T::fmt != FMT_NF4 || sizeof(lds.lut) >= 256 * kLutCopies * 4, "tile LDS");
   auto& Ws = lds.Ws;
   auto& Xs = lds.Xs;
@@ -178,9 +178,9 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
       const int64_t n = min(n0 + row, w.n - 1);
       const bool ok = col * 16 * 8 / T::bits < kend;
       // Past the chunk's end (a last, partial chunk) the load reads the
-      // chunk's first bytes instead; compute() stops at the first group at or
-      // past kend, so those LDS bytes are never used.  (Zeroing them here
-      // would make the wave wait for the load at once.)
+      // chunk's first bytes instead; the waves whose codes start at or past
+      // kend skip the chunk, so those LDS bytes are never used.  (Zeroing
+      // them here would make the wave wait for the load at once.)
       const int64_t off = n * KB + kc * T::bits / 8 + (ok ? col * 16 : 0);
       wr[i] = *reinterpret_cast<const u32x4_t*>(w.packed + off);
     }
@@ -211,49 +211,66 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
       const int e = tid + kThreads * i;
       *reinterpret_cast<u32x4_t*>(&Xs[b][(e / (KC / 8)) * LDX + (e % (KC / 8)) * 8]) = arrange8<KIND>(xr[i]);
     }
-    if (tid / 4 < ROWS && tid % 4 < NG) {
+    if (tid % 4 < NG) {
       const float sc = meta_raw_scale<KIND>(mraw, dqoff);
       meta[b][tid / 4][tid % 4] =
           make_float2(sc, T::fmt == FMT_MINMAX ? (float)(128 + meta_raw_zero<KIND>(mraw, mgi)) : 0.f);
     }
   };
 
-  f32x4_t acc[MB];
+  // Wave w takes k-steps 2w and 2w+1 of every chunk (codes [64w, 64w + 64))
+  // for all ROWS rows: each x fragment it reads feeds the 4 row tiles, and
+  // the sum of x (MinMax) is formed once for them.  The waves' sums are
+  // added in wave order at the end.
+  f32x4_t acc[4][MB];
 #pragma unroll
-  for (int b = 0; b < MB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int q = 0; q < MB; ++q) acc[j][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const u32x4_t ones = u32x4_t{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
   const int lane32 = lane & 31;
-  const int trow = 16 * wave;  // this wave's 16-row tile
+  const int t0 = 2 * wave;                // this wave's first k-step in a chunk
+  const int gw = (KC / 4) * wave / GRP;   // the group (block) its codes belong to
 
   auto compute = [&](int b, int c) {
     const int64_t kc = (int64_t)c * KC;
-    const int64_t kend = (K - kc) < KC ? (K - kc) : KC;
+    const int64_t kend = (K - kc) < KC ? (K - kc) : KC;  // a multiple of 64
+    if ((int64_t)(KC / 4) * wave >= kend) return;
     const uint8_t* wl = Ws[b];
-    for (int gi = 0; gi < NG; ++gi) {
-      if ((int64_t)gi * GRP >= kend) break;
-      f32x4_t ag[MB], xs[MB];
+    f32x4_t ag[4][MB], xs[MB];
 #pragma unroll
-      for (int q = 0; q < MB; ++q) ag[q] = xs[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < MB; ++q) {
+      xs[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int tt = 0; tt < KSG; ++tt) {
-        const int t = gi * KSG + tt;
-        const u32x4_t af = a_frag<KIND>(wl, trow + li, lg, t, lut, lane32);
+      for (int j = 0; j < 4; ++j) ag[j][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-        for (int q = 0; q < MB; ++q) {
-          const u32x4_t xf = *reinterpret_cast<const u32x4_t*>(&Xs[b][(16 * q + li) * LDX + x_off<KIND>(lg, t)]);
-          if constexpr (T::fmt == FMT_MINMAX) xs[q] = mfma16x16x32(ones, xf, xs[q]);
-          ag[q] = mfma16x16x32(af, xf, ag[q]);
-        }
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = t0 + tt;
+      u32x4_t xf[MB];
+#pragma unroll
+      for (int q = 0; q < MB; ++q) {
+        xf[q] = *reinterpret_cast<const u32x4_t*>(&Xs[b][(16 * q + li) * LDX + x_off<KIND>(lg, t)]);
+        if constexpr (T::fmt == FMT_MINMAX) xs[q] = mfma16x16x32(ones, xf[q], xs[q]);
       }
 #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4_t af = a_frag<KIND>(wl, 16 * j + li, lg, t, lut, lane32);
+#pragma unroll
+        for (int q = 0; q < MB; ++q) ag[j][q] = mfma16x16x32(af, xf[q], ag[j][q]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float2 md = meta[b][trow + 4 * lg + i][gi];
+        const float2 md = meta[b][16 * j + 4 * lg + i][gw];
 #pragma unroll
         for (int q = 0; q < MB; ++q) {
           if constexpr (T::fmt == FMT_MINMAX) {
-            acc[q][i] = fmaf(md.x, fmaf(-md.y, xs[q][i], ag[q][i]), acc[q][i]);
+            acc[j][q][i] = fmaf(md.x, fmaf(-md.y, xs[q][i], ag[j][q][i]), acc[j][q][i]);
           } else {
-            acc[q][i] = fmaf(md.x, ag[q][i], acc[q][i]);
+            acc[j][q][i] = fmaf(md.x, ag[j][q][i], acc[j][q][i]);
           }
         }
       }
@@ -277,7 +294,31 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
     }
   }
 
-  // lane holds D[n = n0 + trow + 4lg + i][m = 16q + li]
+  // Sum of the four waves' accumulators through LDS (the x buffers are free
+  // after the last barrier): red[w][j][q][i][lane]; wave w then adds row
+  // tile j = w's values in wave order.
+  static_assert(sizeof(lds.Xs) >= 4 * 4 * MB * 4 * 64 * sizeof(float), "reduction LDS");
+  float* const red = reinterpret_cast<float*>(&Xs[0][0]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int q = 0; q < MB; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[(((wave * 4 + j) * MB + q) * 4 + i) * 64 + lane] = acc[j][q][i];
+  __syncthreads();
+  f32x4_t sum[MB];
+#pragma unroll
+  for (int q = 0; q < MB; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = red[(((0 * 4 + wave) * MB + q) * 4 + i) * 64 + lane];
+#pragma unroll
+      for (int w2 = 1; w2 < 4; ++w2) v += red[(((w2 * 4 + wave) * MB + q) * 4 + i) * 64 + lane];
+      sum[q][i] = v;
+    }
+
+  // lane holds D[n = n0 + 16 wave + 4lg + i][m = 16q + li]
+  const int trow = 16 * wave;
 #pragma unroll
   for (int q = 0; q < MB; ++q) {
     const int mrow = 16 * q + li;
@@ -287,9 +328,9 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
       const int64_t n = n0 + trow + 4 * lg + i;
       if (n >= w.n) continue;
       if (part != nullptr) {
-        part[((int64_t)split * m + mrow) * w.n + n] = acc[q][i];
+        part[((int64_t)split * m + mrow) * w.n + n] = sum[q][i];
       } else {
-        Y[(int64_t)mrow * ldy + (out_rows ? (int64_t)out_rows[n] : n)] = (uint16_t)bf16_rne(acc[q][i]);
+        Y[(int64_t)mrow * ldy + (out_rows ? (int64_t)out_rows[n] : n)] = (uint16_t)bf16_rne(sum[q][i]);
       }
     }
   }
@@ -446,6 +487,7 @@ struct SkinnySetLauncher {
                         int64_t m, float* part, const Nf4Table& tab, hipStream_t s) {
     if (m <= 16) return launch_set_mb<KIND, 1>(set, wgs, ncol, reduce, X, m, part, tab, s);
     if (m <= 32) return launch_set_mb<KIND, 2>(set, wgs, ncol, reduce, X, m, part, tab, s);
+    if (m <= 48) return launch_set_mb<KIND, 3>(set, wgs, ncol, reduce, X, m, part, tab, s);
     return launch_set_mb<KIND, 4>(set, wgs, ncol, reduce, X, m, part, tab, s);
   }
 };
@@ -472,6 +514,7 @@ struct SkinnyLauncher {
                         const Nf4Table& tab, hipStream_t s) {
     if (m <= 16) return launch_mb<KIND, 1>(w, X, m, Y, ldy, out_rows, part, ks, lora, tab, s);
     if (m <= 32) return launch_mb<KIND, 2>(w, X, m, Y, ldy, out_rows, part, ks, lora, tab, s);
+    if (m <= 48) return launch_mb<KIND, 3>(w, X, m, Y, ldy, out_rows, part, ks, lora, tab, s);
     return launch_mb<KIND, 4>(w, X, m, Y, ldy, out_rows, part, ks, lora, tab, s);
   }
 };
@@ -570,6 +613,7 @@ hipError_t launch_skinny_mix(const WView* ws, uint16_t* const* ys, const int64_t
   plan_skinny_set(ws, ys, ldys, out_rows, count, m, set, wgs, ncol, reduce);
   if (m <= 16) return launch_mix_mb<1>(set, wgs, ncol, reduce, X, m, part, tab, count_a, s);
   if (m <= 32) return launch_mix_mb<2>(set, wgs, ncol, reduce, X, m, part, tab, count_a, s);
+  if (m <= 48) return launch_mix_mb<3>(set, wgs, ncol, reduce, X, m, part, tab, count_a, s);
   return launch_mix_mb<4>(set, wgs, ncol, reduce, X, m, part, tab, count_a, s);
 }
 

@@ -140,12 +140,11 @@ template <> struct WKindTraits<WK_I2G64C>  { static constexpr int fmt = FMT_MINM
 template <> struct WKindTraits<WK_NF4DQO>  { static constexpr int fmt = FMT_NF4,    bits = 4, group = 64;  static constexpr bool dq = true,  compact = false, dqo = true; };
 
 // fp16 bit pattern -> its exact fp32 value (normal and subnormal; no NaN/Inf
-// in the contract).
+// in the contract).  One v_cvt_f32_f16: every fp16 value, subnormals
+// included, is a normal fp32 number, and fp16 denormals are kept by the
+// default floating-point mode, so the conversion is exact.
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
-  const uint32_t e = (h >> 10) & 0x1Fu, mant = h & 0x3FFu;
-  const float v = e == 0 ? (float)mant * 5.9604644775390625e-8f  // mant * 2^-24, exact
-                         : __uint_as_float(((e + 112u) << 23) | (mant << 13));
-  return (h & 0x8000u) ? -v : v;
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
 // Zero point of metadata entry gi from the zeros array: one byte per entry,

@@ -233,6 +233,27 @@ def counter_summary(csvs, out_md: str, commands=(), match: str = "lbq::") -> Non
         fh.write("\n".join(lines) + "\n\nMean counter values per dispatch:\n\n```json\n" + json.dumps(raw, indent=1) + "\n```\n")
 
 
+def stats_summary(stats_csv: str, out_md: str, command: str = "") -> None:
+    """The library's rows of a rocprofv3 --stats kernel summary (all phases of
+    one run pooled per kernel; the per-phase split is trace_summary's)."""
+    import csv
+    lines = [f"# rocprofv3 --stats kernel summary (liblbq kernels): {os.path.basename(stats_csv)}", ""]
+    if command:
+        lines += ["Command (on the MI355X box, from the repository root `$R`):", "", "    " + command, ""]
+    lines += ["Each kernel pooled over every phase of the run; durations in microseconds.  Template arguments: "
+              "first = weight kind (0 INT4 g128, 1 INT4 g64, 2 INT2 g64, 3 INT2 g128, 4 NF4, 5 NF4+DQ, "
+              "6 compact INT4 g128, 7 compact INT2 g64, 8 NF4+DQ with offset).", "",
+              "| kernel | calls | total us | avg us | min us | max us |", "|---|---:|---:|---:|---:|---:|"]
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            if "lbq::" not in r["Name"]:
+                continue
+            lines.append(f"| `{_short_kernel(r['Name'])}` | {r['Calls']} | {int(r['TotalDurationNs']) / 1e3:.1f} | "
+                         f"{float(r['AverageNs']) / 1e3:.2f} | {int(r['MinNs']) / 1e3:.2f} | {int(r['MaxNs']) / 1e3:.2f} |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def trace_summary(trace_csv: str, phases_json: str, out_md: str, command: str = "") -> None:
     """Per phase and per launch shape (kernel name + grid), the count and the
     median / p10 / p90 / mean duration of the dispatches of a rocprofv3
@@ -860,6 +881,8 @@ def main():
     ap.add_argument("--trace-summary", nargs=3, metavar=("TRACE_CSV", "PHASES_JSON", "OUT_MD"),
                     help="summarize a rocprofv3 kernel trace per phase and launch shape and exit")
     ap.add_argument("--trace-command", default="", help="command line recorded in the trace summary")
+    ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
+                    help="summarize a rocprofv3 --stats kernel CSV (library kernels) and exit")
     ap.add_argument("--counter-summary", nargs="+", metavar="CSV_OR_OUT",
                     help="summarize rocprofv3 --pmc CSVs (one per counter pass) into the markdown file given "
                          "last and exit; --trace-command may repeat the commands, separated by ' ;; '")
@@ -869,6 +892,9 @@ def main():
         return
     if args.trace_summary:
         trace_summary(*args.trace_summary, command=args.trace_command)
+        return
+    if args.stats_summary:
+        stats_summary(*args.stats_summary, command=args.trace_command)
         return
     if args.counter_summary:
         cmds = [c.strip() for c in args.trace_command.split(";;") if c.strip()]

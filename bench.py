@@ -126,7 +126,7 @@ TRAFFIC_KERNELS = {
 }
 
 
-def write_traffic(fetch_csv: str, write_csv: str) -> dict:
+def write_traffic(fetch_csv: str, write_csv: str, commands=()) -> dict:
     """profiles/traffic.json from two rocprofv3 --pmc runs (FETCH_SIZE, then
     WRITE_SIZE, KiB per dispatch) of the same bench.py command (with copy_1g).
     Each counter is scaled by what it reads for the plain 1 GiB device copy
@@ -146,6 +146,7 @@ def write_traffic(fetch_csv: str, write_csv: str) -> dict:
     copy_w = max(v for k, vs in wr.items() if "copy" in k.lower() for v in vs)
     cf, cw = float(1 << 30) / copy_f, float(1 << 30) / copy_w
     out = {"kernel_source_hash": kernel_source_hash(),
+           "commands": list(commands),
            "copy_1GiB": {"FETCH_SIZE_bytes": copy_f, "WRITE_SIZE_bytes": copy_w, "fetch_factor": cf, "write_factor": cw},
            "kernels": {}}
     for key, pats in TRAFFIC_KERNELS.items():
@@ -888,7 +889,8 @@ def main():
                          "last and exit; --trace-command may repeat the commands, separated by ' ;; '")
     args = ap.parse_args()
     if args.traffic_from:
-        print(json.dumps(write_traffic(*args.traffic_from)), flush=True)
+        cmds = [c.strip() for c in args.trace_command.split(";;") if c.strip()]
+        print(json.dumps(write_traffic(*args.traffic_from, commands=cmds)), flush=True)
         return
     if args.trace_summary:
         trace_summary(*args.trace_summary, command=args.trace_command)

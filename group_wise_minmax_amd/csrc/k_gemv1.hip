@@ -185,24 +185,6 @@ __device__ __forceinline__ float x_chunk(const u32x4_t* xv, uint32_t* xa) {
   return s0 + s1;
 }
 
-// Buffer resources over a weight's metadata arrays (scales / zero points, or
-// the NF4 absmax data).
-template <int KIND>
-__device__ __forceinline__ void meta_rsrc(const WView& w, int64_t nmeta, __amdgpu_buffer_rsrc_t& r_s,
-                                          __amdgpu_buffer_rsrc_t& r_z) {
-  using T = WKindTraits<KIND>;
-  if constexpr (T::fmt == FMT_MINMAX) {
-    r_s = make_rsrc(w.scales, scale_byte_index<KIND>(nmeta));
-    r_z = make_rsrc(w.zeros, zero_byte_index<KIND>(nmeta));
-  } else if constexpr (T::dq) {
-    r_s = make_rsrc(w.absmax_scale, ((nmeta + 255) >> 8) * 4);
-    r_z = make_rsrc(w.absmax_q, nmeta);
-  } else {
-    r_s = make_rsrc(w.absmax, nmeta * 4);
-    r_z = r_s;
-  }
-}
-
 // Metadata of entry gc of row `row` (gpr entries per row), as loaded: the
 // raw scale word (MinMax fp32 or fp16 bits, NF4 absmax or second-level
 // scale) and the raw zero-point / absmax-code byte.  Nothing is computed on

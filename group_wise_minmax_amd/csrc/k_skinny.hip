@@ -165,6 +165,12 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
   }
 
   // ---- staging of one chunk: packed W rows, arranged X rows, group metadata --
+  // Buffer loads with 32-bit lane offsets: the boundary keeps the packed
+  // weight and X below 2^32 bytes.
+  const __amdgpu_buffer_rsrc_t r_w = make_rsrc(w.packed, w.n * KB);
+  const __amdgpu_buffer_rsrc_t r_x = make_rsrc(X, (int64_t)m * K * 2);
+  __amdgpu_buffer_rsrc_t r_s, r_z;
+  meta_rsrc<KIND>(w, w.n * gpr, r_s, r_z);
   u32x4_t wr[WLD], xr[XLD];
   MetaRaw mraw;      // this thread's metadata entry of the loaded chunk, as loaded
   int64_t mgi = 0;   // its entry index
@@ -181,8 +187,8 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
       // chunk's first bytes instead; the waves whose codes start at or past
       // kend skip the chunk, so those LDS bytes are never used.  (Zeroing
       // them here would make the wave wait for the load at once.)
-      const int64_t off = n * KB + kc * T::bits / 8 + (ok ? col * 16 : 0);
-      wr[i] = *reinterpret_cast<const u32x4_t*>(w.packed + off);
+      const uint32_t off = (uint32_t)n * (uint32_t)KB + (uint32_t)(kc * T::bits / 8) + (ok ? col * 16u : 0u);
+      wr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_w, off, 0, 0));
     }
 #pragma unroll
     for (int i = 0; i < XLD; ++i) {
@@ -190,14 +196,15 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
       const int row = e / (KC / 8), col = e % (KC / 8);
       const int64_t mrow = min((int64_t)row, (int64_t)m - 1);
       const bool ok = col * 8 < kend;
-      xr[i] = *reinterpret_cast<const u32x4_t*>(X + mrow * K + kc + (ok ? col * 8 : 0));  // as above
+      const uint32_t xo = 2u * ((uint32_t)mrow * (uint32_t)K + (uint32_t)kc + (ok ? col * 8u : 0u));  // as above
+      xr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_x, xo, 0, 0));
     }
     {
       const int row = tid / 4, j = tid % 4;
       const int64_t n = min(n0 + row, w.n - 1);
       const bool ok = j < NG && (int64_t)j * GRP < kend;
       mgi = n * gpr + (ok ? (kc / GRP + j) : 0);
-      mraw = load_meta_raw<KIND>(w, mgi);  // decoded in store(), one chunk later
+      mraw = load_meta_buf<KIND>(r_s, r_z, (uint32_t)mgi);  // decoded in store(), one chunk later
     }
   };
   auto store = [&](int b) {

@@ -218,6 +218,46 @@ __device__ __forceinline__ MetaRaw load_meta_raw(const WView& w, int64_t gi) {
   }
   return r;
 }
+// Buffer resources over a weight's metadata arrays (scales / zero points, or
+// the NF4 absmax data).
+template <int KIND>
+__device__ __forceinline__ void meta_rsrc(const WView& w, int64_t nmeta, __amdgpu_buffer_rsrc_t& r_s,
+                                          __amdgpu_buffer_rsrc_t& r_z) {
+  using T = WKindTraits<KIND>;
+  if constexpr (T::fmt == FMT_MINMAX) {
+    r_s = make_rsrc(w.scales, scale_byte_index<KIND>(nmeta));
+    r_z = make_rsrc(w.zeros, zero_byte_index<KIND>(nmeta));
+  } else if constexpr (T::dq) {
+    r_s = make_rsrc(w.absmax_scale, ((nmeta + 255) >> 8) * 4);
+    r_z = make_rsrc(w.absmax_q, nmeta);
+  } else {
+    r_s = make_rsrc(w.absmax, nmeta * 4);
+    r_z = r_s;
+  }
+}
+
+// The metadata words of entry gi through the buffer resources of
+// meta_rsrc, as loaded (a 32-bit lane offset; nothing computed on the loaded
+// values, see MetaRaw).
+template <int KIND>
+__device__ __forceinline__ MetaRaw load_meta_buf(__amdgpu_buffer_rsrc_t r_s, __amdgpu_buffer_rsrc_t r_z,
+                                                 uint32_t gi) {
+  using T = WKindTraits<KIND>;
+  MetaRaw r{0u, 0u};
+  if constexpr (T::fmt == FMT_MINMAX && T::compact) {
+    r.s = __builtin_amdgcn_raw_buffer_load_b16(r_s, gi * 2u, 0, 0);
+    r.z = __builtin_amdgcn_raw_buffer_load_b8(r_z, gi * (uint32_t)T::bits / 8u, 0, 0);
+  } else if constexpr (T::fmt == FMT_MINMAX) {
+    r.s = __builtin_amdgcn_raw_buffer_load_b32(r_s, gi * 4u, 0, 0);
+    r.z = __builtin_amdgcn_raw_buffer_load_b8(r_z, gi, 0, 0);
+  } else if constexpr (T::dq) {
+    r.z = __builtin_amdgcn_raw_buffer_load_b8(r_z, gi, 0, 0);
+    r.s = __builtin_amdgcn_raw_buffer_load_b32(r_s, (gi >> 8) * 4u, 0, 0);
+  } else {
+    r.s = __builtin_amdgcn_raw_buffer_load_b32(r_s, gi * 4u, 0, 0);
+  }
+  return r;
+}
 // Per-tensor offset of double quantization with an offset: the entry after
 // the ceil(nb / 256) per-block scales.
 __device__ __forceinline__ float nf4_dq_offset(const WView& w) {

@@ -406,14 +406,16 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(BwdSet set, int m, uin
     }
   }
 
+  // Row tile b outer, column tile a inner: the TK stores that fill a row's
+  // WK contiguous outputs (whole 128-byte lines) follow one another.
 #pragma unroll
-  for (int a = 0; a < TK; ++a) {
-    const int64_t kb = k0 + wk * WK + 16 * a + 4 * lg;
-    if (kb >= K) continue;
+  for (int b = 0; b < TM; ++b) {
+    const int64_t mr = m0 + wm * WM + 16 * b + li;
+    if (mr >= m) continue;
 #pragma unroll
-    for (int b = 0; b < TM; ++b) {
-      const int64_t mr = m0 + wm * WM + 16 * b + li;
-      if (mr >= m) continue;
+    for (int a = 0; a < TK; ++a) {
+      const int64_t kb = k0 + wk * WK + 16 * a + 4 * lg;
+      if (kb >= K) continue;
       uint2 v;
       v.x = cvt_pk_bf16(acc[a][b][0], acc[a][b][1]);
       v.y = cvt_pk_bf16(acc[a][b][2], acc[a][b][3]);

@@ -381,14 +381,17 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
     }
     return;
   }
+  // Row tile b outer, column tile a inner: the TN stores that fill a row's
+  // WN contiguous outputs (whole 128-byte lines for WN = 64) follow one
+  // another, so each line is complete in L2 before it is written back.
 #pragma unroll
-  for (int a = 0; a < TN; ++a) {
-    const int64_t nb = n0 + wn * WN + 16 * a + 4 * lg;
+  for (int b = 0; b < TM; ++b) {
+    const int64_t mr = m0 + wm * WM + 16 * b + li;
+    if (mr >= m) continue;
+    uint16_t* yrow = Y + mr * ldy;
 #pragma unroll
-    for (int b = 0; b < TM; ++b) {
-      const int64_t mr = m0 + wm * WM + 16 * b + li;
-      if (mr >= m) continue;
-      uint16_t* yrow = Y + mr * ldy;
+    for (int a = 0; a < TN; ++a) {
+      const int64_t nb = n0 + wn * WN + 16 * a + 4 * lg;
       if (vec_store && nb + 3 < w.n) {
         uint2 v;
         v.x = cvt_pk_bf16(acc[a][b][0], acc[a][b][1]);

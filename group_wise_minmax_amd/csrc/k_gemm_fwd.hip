@@ -20,7 +20,7 @@
 // accumulators are four consecutive n of one m, so the epilogue writes 8
 // contiguous bytes of a Y row.  Workgroups are renumbered so that each of the
 // 8 XCDs (each with its own L2) receives a contiguous run of tiles, walked in
-// groups of 2 X-row tiles so that concurrently running tiles share operands.
+// groups of 4 X-row tiles so that concurrently running tiles share operands.
 #include "lbq_device.h"
 
 namespace lbq {

@@ -116,7 +116,7 @@ __device__ __forceinline__ void tile_of(int bid, int nx, int ny, int& tx, int& t
   const int start = xcd * per + (xcd < rem ? xcd : rem);
   int t = start + slot;
   if (slot >= per + (xcd < rem ? 1 : 0)) t = bid;  // cannot happen for grid == total
-  constexpr int GM = 2;  // X-row tiles per group
+  constexpr int GM = 4;  // X-row tiles per group (measured: 2 -> 4 +1.5% on the 8B layer at m = 4096)
   const int group = t / (GM * nx);
   const int first = group * GM;
   const int gm = (ny - first) < GM ? (ny - first) : GM;

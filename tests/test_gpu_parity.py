@@ -568,6 +568,39 @@ def test_grouped_fwd_matches_single(L, name, k, m):
         assert_close(bf16_bits_host(Y), O.linear_fwd(X, ref["w_exact"]), what=f"{name} weight {i} m={m}")
 
 
+@pytest.mark.parametrize("m", [130, 300])
+def test_grouped_mixed_kinds_gemm_graph_replay(L, m):
+    """A grouped call whose weights have several kinds (the two row sets of
+    channel-mixed linears) launches one GEMM per kind on the caller's stream.
+    Captured into a HIP graph after an eager call, every replay -- with eager
+    work and cleared outputs in between -- reproduces the eager outputs bit
+    for bit."""
+    specs = GROUP_SETS["channel_mix"]
+    ns = [300, 64, 520, 130]
+    k = 1280
+    X = SI.bf16_normal(9500 + m, (m, k))
+    qws = [_quant_pair(L, SI.gaussian_weights(9510 + i, n, k, outlier_seed=9520 + i), *spec)[0]
+           for i, (spec, n) in enumerate(zip(specs, ns))]
+    Xd = to_dev_bf16(X)
+    outs = [torch.empty((m, n), dtype=torch.bfloat16, device=DEV) for n in ns]
+    L.lbq_linear_fwd_grouped(Xd, qws, outs=outs)
+    torch.cuda.synchronize()
+    ref = [bf16_bits_host(y) for y in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.lbq_linear_fwd_grouped(Xd, qws, outs=outs)
+    for rep in range(4):
+        for y in outs:
+            y.zero_()
+        junk = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert float(junk) == float(junk)
+        for i, y in enumerate(outs):
+            assert np.array_equal(bf16_bits_host(y), ref[i]), f"replay {rep} weight {i}"
+
+
 @pytest.mark.parametrize("fid", ["i4g128", "nf4dq", "i2g64"])
 def test_grouped_gemm_two_launch_split(L, fid):
     """A q/k/v-like set at ragged m = 4000 whose GEMM runs as two launches:

@@ -572,12 +572,32 @@ int skinny_splits(int64_t n, int64_t k, int64_t m) {
   return skinny_splits_tiles((n + ROWS - 1) / ROWS, k, m);
 }
 
+// Workgroups of the small-batch kernel resident at once on the chip for m
+// (LDS-limited; the INT4 g128 tile, which the other 4- and 2-bit kinds match
+// or undercut).
+template <int MB>
+constexpr int64_t skinny_slots() {
+  return 256 * ((160 * 1024) / (int64_t)sizeof(SkLdsOf<WK_I4G128, MB>) > 0
+                    ? (160 * 1024) / (int64_t)sizeof(SkLdsOf<WK_I4G128, MB>) : 1);
+}
+
 int skinny_splits_tiles(int64_t tiles, int64_t k, int64_t m) {
   const int64_t nchunk = (k + KC - 1) / KC;
-  // Aim at ~512 workgroups, but keep the fp32 partial traffic (ks * m * n * 8
-  // bytes) below the packed weight (n * k / 2 bytes for 4-bit).  Measured on
-  // the 8B layer: more splits lose to the shorter K ranges, a tighter cap
-  // (a quarter of the weight) costs 3% at m = 16 and 15% at m = 32.
+  // A weight whose row tiles alone fill a fifth of the resident workgroups,
+  // with at most 16 chunks per 16-column tile of m, runs unsplit: no partial
+  // sums and no reduce launch.  (Such weights come in sets -- gate and up --
+  // that fill the chip together.  Measured: 8B gate+up at m = 16 31.1 ->
+  // 25.7 us and at m = 48 56.1 -> 41.5 us; the 70B channel-mix layer at
+  // m = 40 +8%.  Longer K ranges -- the 70B INT2 gate/up rows at m = 3 and
+  // 16 -- and m > 48, where the 256 resident workgroups are too few, lost
+  // 4-7% and up to 2.6x unsplit.)  Other weights aim at ~512 workgroups,
+  // with the fp32 partial traffic (ks * m * n * 8 bytes) kept below the
+  // packed weight (n * k / 2 bytes for 4-bit).  Measured on the 8B layer:
+  // more splits lose to the shorter K ranges, a tighter cap (a quarter of the
+  // weight) costs 3% at m = 16 and 15% at m = 32.
+  const int mb = m <= 16 ? 1 : m <= 32 ? 2 : m <= 48 ? 3 : 4;
+  const int64_t slots = mb == 1 ? skinny_slots<1>() : mb == 2 ? skinny_slots<2>() : skinny_slots<3>();
+  if (mb <= 3 && tiles * 5 >= slots && nchunk <= 16 * mb) return 1;
   int64_t ks = (512 + tiles - 1) / tiles;
   const int64_t cap = (k / 16) / (m < 1 ? 1 : m);
   if (ks > cap) ks = cap;

@@ -29,7 +29,11 @@ COMMON = [
     "-I", CSRC, "-I", INCLUDE,
 ]
 # Quantize/dequantize must be bit-exact: one IEEE op per step, no contraction.
-PER_FILE = {"k_quant.hip": ["-ffp-contract=off"]}
+# The small-batch kernel accumulates its MFMAs in ordinary registers: its
+# epilogue reads every accumulator once per group, which the accumulation
+# registers would cost an extra move each.
+PER_FILE = {"k_quant.hip": ["-ffp-contract=off"],
+            "k_skinny.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 SOURCES = ["lbq_api.cpp", "k_quant.hip", "k_gemv1.hip", "k_skinny.hip", "k_gemm_fwd.hip", "k_bwd.hip", "k_lora.hip",
            "k_noalloc.hip"]
 

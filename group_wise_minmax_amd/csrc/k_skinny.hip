@@ -174,36 +174,40 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
   u32x4_t wr[WLD], xr[XLD];
   MetaRaw mraw;      // this thread's metadata entry of the loaded chunk, as loaded
   int64_t mgi = 0;   // its entry index
+  // Loop-invariant parts of this thread's load offsets (32-bit: the
+  // boundary keeps the packed weight and X below 2^32 bytes): the clamped
+  // packed row, x row and metadata row of each load.
+  uint32_t wrow[WLD], xrow[XLD];
+#pragma unroll
+  for (int i = 0; i < WLD; ++i)
+    wrow[i] = (uint32_t)min(n0 + (tid + kThreads * i) / WCOL, w.n - 1) * (uint32_t)KB;
+#pragma unroll
+  for (int i = 0; i < XLD; ++i)
+    xrow[i] = 2u * (uint32_t)min((tid + kThreads * i) / (KC / 8), m - 1) * (uint32_t)K;
+  const uint32_t mrow = (uint32_t)min(n0 + tid / 4, w.n - 1) * (uint32_t)gpr;
   auto load = [&](int c) {
-    const int64_t kc = (int64_t)c * KC;
-    const int64_t kend = (K - kc) < KC ? (K - kc) : KC;  // codes in this chunk (multiple of 64)
+    const uint32_t kc = (uint32_t)c * (uint32_t)KC;
+    const int kend = (int)min(K - (int64_t)kc, (int64_t)KC);  // codes in this chunk (multiple of 64)
 #pragma unroll
     for (int i = 0; i < WLD; ++i) {
-      const int e = tid + kThreads * i;
-      const int row = e / WCOL, col = e % WCOL;
-      const int64_t n = min(n0 + row, w.n - 1);
-      const bool ok = col * 16 * 8 / T::bits < kend;
+      const int col = (tid + kThreads * i) % WCOL;
       // Past the chunk's end (a last, partial chunk) the load reads the
       // chunk's first bytes instead; the waves whose codes start at or past
       // kend skip the chunk, so those LDS bytes are never used.  (Zeroing
       // them here would make the wave wait for the load at once.)
-      const uint32_t off = (uint32_t)n * (uint32_t)KB + (uint32_t)(kc * T::bits / 8) + (ok ? col * 16u : 0u);
+      const uint32_t off = wrow[i] + kc * T::bits / 8 + (col * 16 * 8 / T::bits < kend ? col * 16u : 0u);
       wr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_w, off, 0, 0));
     }
 #pragma unroll
     for (int i = 0; i < XLD; ++i) {
-      const int e = tid + kThreads * i;
-      const int row = e / (KC / 8), col = e % (KC / 8);
-      const int64_t mrow = min((int64_t)row, (int64_t)m - 1);
-      const bool ok = col * 8 < kend;
-      const uint32_t xo = 2u * ((uint32_t)mrow * (uint32_t)K + (uint32_t)kc + (ok ? col * 8u : 0u));  // as above
+      const int col = (tid + kThreads * i) % (KC / 8);
+      const uint32_t xo = xrow[i] + 2u * (kc + (col * 8 < kend ? col * 8u : 0u));  // as above
       xr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_x, xo, 0, 0));
     }
     {
-      const int row = tid / 4, j = tid % 4;
-      const int64_t n = min(n0 + row, w.n - 1);
-      const bool ok = j < NG && (int64_t)j * GRP < kend;
-      mgi = n * gpr + (ok ? (kc / GRP + j) : 0);
+      const int j = tid % 4;
+      const bool ok = j < NG && j * GRP < kend;
+      mgi = (int64_t)(mrow + (ok ? kc / GRP + j : 0u));
       mraw = load_meta_buf<KIND>(r_s, r_z, (uint32_t)mgi);  // decoded in store(), one chunk later
     }
   };

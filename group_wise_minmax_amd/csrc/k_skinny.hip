@@ -585,6 +585,18 @@ constexpr int64_t skinny_slots() {
                     ? (160 * 1024) / (int64_t)sizeof(SkLdsOf<WK_I4G128, MB>) : 1);
 }
 
+namespace {
+bool fills_unsplit(int64_t tiles, int64_t nchunk, int64_t m) {
+  const int mb = m <= 16 ? 1 : m <= 32 ? 2 : m <= 48 ? 3 : 4;
+  const int64_t slots = mb == 1 ? skinny_slots<1>() : mb == 2 ? skinny_slots<2>() : skinny_slots<3>();
+  return mb <= 3 && tiles * 5 >= slots && nchunk <= 16 * mb;
+}
+}  // namespace
+
+bool skinny_fills_unsplit(int64_t n, int64_t k, int64_t m) {
+  return fills_unsplit((n + ROWS - 1) / ROWS, (k + KC - 1) / KC, m);
+}
+
 int skinny_splits_tiles(int64_t tiles, int64_t k, int64_t m) {
   const int64_t nchunk = (k + KC - 1) / KC;
   // A weight whose row tiles alone fill a fifth of the resident workgroups,
@@ -599,9 +611,7 @@ int skinny_splits_tiles(int64_t tiles, int64_t k, int64_t m) {
   // packed weight (n * k / 2 bytes for 4-bit).  Measured on the 8B layer:
   // more splits lose to the shorter K ranges, a tighter cap (a quarter of the
   // weight) costs 3% at m = 16 and 15% at m = 32.
-  const int mb = m <= 16 ? 1 : m <= 32 ? 2 : m <= 48 ? 3 : 4;
-  const int64_t slots = mb == 1 ? skinny_slots<1>() : mb == 2 ? skinny_slots<2>() : skinny_slots<3>();
-  if (mb <= 3 && tiles * 5 >= slots && nchunk <= 16 * mb) return 1;
+  if (fills_unsplit(tiles, nchunk, m)) return 1;
   int64_t ks = (512 + tiles - 1) / tiles;
   const int64_t cap = (k / 16) / (m < 1 ? 1 : m);
   if (ks > cap) ks = cap;

@@ -210,12 +210,25 @@ int64_t round_rows(int64_t m) { return (m + 31) / 32 * 32; }
 // Forward kernel choice: single-token decode streams the weight (GEMV);
 // 2 <= m <= 64 uses the small-batch MFMA kernel (fp32 partials in `ws` when K
 // is split); larger m the MFMA GEMM with the dequantized weight tile in LDS.
+// The multi-row GEMV serves 2 <= m <= 4 while the m rows of x fit its LDS
+// (gemvm_fits) -- except, at m >= 3, a weight large enough that the
+// small-batch MFMA kernel runs it unsplit (its row tiles alone fill a fifth of
+// that kernel's resident workgroups, with a short K range: n > 13056 and
+// k <= 4096 for m = 3..4): there the MFMA
+// kernel is faster (8B gate+up at m = 3 and 4: 29.7 -> 23.7 and 30.6 ->
+// 23.6 us; q+k+v and o stay faster on the GEMV).  Decided per weight, so a
+// grouped call serves each weight as the single-weight call does.
+bool use_gemvm(const lbq_desc* d, int64_t m) {
+  if (!lbq::gemvm_fits(kind_of(d), d->k, m)) return false;
+  return m < 3 || !lbq::skinny_fills_unsplit(d->n, d->k, m);
+}
+
 hipError_t dispatch_fwd(const lbq_desc* desc, const lbq::WView& w, const uint16_t* X, int64_t m,
                         uint16_t* Y, int64_t ldy, const int32_t* out_rows,
                         const lbq::LoraEpi& lora, void* ws, hipStream_t s) {
   const lbq::WKind kind = kind_of(desc);
   if (m == 1) return lbq::launch_gemv1(kind, &w, &Y, &out_rows, 1, X, lora, nf4_table(), s);
-  if (lbq::gemvm_fits(kind, desc->k, m)) return lbq::launch_gemvm(kind, &w, &Y, &ldy, &out_rows, 1, X, m, lora, nf4_table(), s);
+  if (use_gemvm(desc, m)) return lbq::launch_gemvm(kind, &w, &Y, &ldy, &out_rows, 1, X, m, lora, nf4_table(), s);
   if (m <= lbq::kSkinnyMaxM)
     return lbq::launch_skinny(kind, w, X, m, Y, ldy, out_rows, static_cast<float*>(ws), lora,
                               nf4_table(), s);
@@ -223,7 +236,7 @@ hipError_t dispatch_fwd(const lbq_desc* desc, const lbq::WView& w, const uint16_
 }
 
 size_t fwd_workspace(const lbq_desc* desc, int64_t m, bool lora) {
-  if (lbq::gemvm_fits(kind_of(desc), desc->k, m)) return 0;
+  if (use_gemvm(desc, m)) return 0;
   if (m >= 2 && m <= lbq::kSkinnyMaxM) return lbq::skinny_workspace_bytes(desc->n, desc->k, m, lora);
   return 0;
 }
@@ -346,8 +359,10 @@ bool skinny_mix_set(int32_t count, const lbq_desc* descs, int64_t m) {
     else if (kd == lbq::WK_I2G64) ++cb;
     else return false;
   }
-  return ca > 0 && cb > 0 && !lbq::gemvm_fits(lbq::WK_I4G128, descs[0].k, m) &&
-         !lbq::gemvm_fits(lbq::WK_I2G64, descs[0].k, m);
+  if (ca == 0 || cb == 0) return false;
+  for (int32_t i = 0; i < count; ++i)
+    if (use_gemvm(&descs[i], m)) return false;
+  return true;
 }
 
 // Weights of one kind in a grouped call run as one launch (one launch pair
@@ -370,11 +385,11 @@ size_t lbq_linear_fwd_grouped_workspace_bytes(int32_t count, const lbq_desc* des
   for (int32_t i = 0; i < count; ++i) {
     if (done[i]) continue;
     const lbq::WKind kind = kind_of(&descs[i]);
-    if (lbq::gemvm_fits(kind, descs[i].k, m)) continue;
+    if (use_gemvm(&descs[i], m)) continue;
     int64_t ns[LBQ_MAX_GROUP];
     int c = 0;
     for (int32_t j = i; j < count; ++j)
-      if (!done[j] && kind_of(&descs[j]) == kind) {
+      if (!done[j] && kind_of(&descs[j]) == kind && !use_gemvm(&descs[j], m)) {
         done[j] = true;
         ns[c++] = descs[j].n;
       }
@@ -432,19 +447,21 @@ lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lb
                         "lbq_linear_fwd_grouped");
     }
   }
-  // One launch per distinct weight kind, in order of first appearance, with
-  // the kernel lbq_linear_fwd picks for that kind (all weights share k).
+  // One launch per distinct (weight kind, kernel) pair, in order of first
+  // appearance, with the kernel lbq_linear_fwd picks for each weight (all
+  // weights share k).
   bool done[LBQ_MAX_GROUP] = {};
   for (int32_t i = 0; i < count && e == hipSuccess; ++i) {
     if (done[i]) continue;
     const lbq::WKind kind = kind_of(&descs[i]);
+    const bool gemvm = use_gemvm(&descs[i], m);
     lbq::WView ws[LBQ_MAX_GROUP];
     uint16_t* ys[LBQ_MAX_GROUP];
     int64_t lds[LBQ_MAX_GROUP];
     const int32_t* rows[LBQ_MAX_GROUP];
     int c = 0;
     for (int32_t j = i; j < count; ++j) {
-      if (done[j] || kind_of(&descs[j]) != kind) continue;
+      if (done[j] || kind_of(&descs[j]) != kind || use_gemvm(&descs[j], m) != gemvm) continue;
       done[j] = true;
       ws[c] = view_of(&descs[j], &qs[j]);
       ys[c] = Ys[j];
@@ -453,7 +470,7 @@ lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lb
       ++c;
     }
     if (m == 1) e = lbq::launch_gemv1(kind, ws, ys, rows, c, X, none, nf4_table(), s);
-    else if (lbq::gemvm_fits(kind, descs[i].k, m)) e = lbq::launch_gemvm(kind, ws, ys, lds, rows, c, X, m, none, nf4_table(), s);
+    else if (gemvm) e = lbq::launch_gemvm(kind, ws, ys, lds, rows, c, X, m, none, nf4_table(), s);
     else if (m <= lbq::kSkinnyMaxM)
       e = lbq::launch_skinny_set(kind, ws, ys, lds, rows, c, X, m, static_cast<float*>(workspace), nf4_table(), s);
     else e = lbq::launch_gemm_fwd_set(kind, ws, ys, lds, rows, c, X, m, nf4_table(), s);

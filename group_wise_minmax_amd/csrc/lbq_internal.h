@@ -92,6 +92,9 @@ hipError_t launch_gemvm(WKind kind, const WView* ws, uint16_t* const* ys, const 
 // second kernel when more than one range is used or a LoRA term is added.
 int skinny_splits(int64_t n, int64_t k, int64_t m);
 int skinny_splits_tiles(int64_t tiles, int64_t k, int64_t m);
+// True when the small-batch kernel runs an n x k weight at m unsplit because
+// its row tiles alone fill the chip (then skinny_splits() == 1).
+bool skinny_fills_unsplit(int64_t n, int64_t k, int64_t m);
 // Weights of one kind that share X (count <= kGemvMaxGroup, same k): one
 // launch over all their row tiles and, when K is split, one reduce launch.
 // Workspace: skinny_set_workspace_bytes() bytes of fp32 partials.

@@ -194,7 +194,9 @@ size_t lbq_linear_workspace_bytes(const lbq_desc* desc, int64_t m);
  * same streaming with every row of X staged in LDS (when the rows fit in 64
  * KiB: k up to 7680 for 4-bit MinMax, 7936 for 2-bit and 4096 for NF4 at
  * m = 3..4; 15360, 15872 and 8192 at m = 2), each output row bit for bit what
- * m == 1 gives for that row of X; otherwise, up to m = 64, a bf16-MFMA kernel that streams the weight
+ * m == 1 gives for that row of X -- except at m = 3..4 for a weight of
+ * n > 13056 rows and k <= 4096, which takes the next kernel (faster there);
+ * otherwise, up to m = 64, a bf16-MFMA kernel that streams the weight
  * once with K split over workgroups; larger m a bf16-MFMA GEMM whose weight
  * tiles are dequantized once into LDS. */
 lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16_t* X,

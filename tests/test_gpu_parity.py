@@ -184,6 +184,29 @@ def test_forward_few_rows_at_lds_limit(L, fid, above):
     assert_close(bf16_bits_host(Y), O.linear_fwd(X, ref["w_exact"]), what=f"{fid} k={k}")
 
 
+@pytest.mark.parametrize("fid", ["i4g128", "nf4dq"])
+@pytest.mark.parametrize("m", [3, 4])
+@pytest.mark.parametrize("n", [13056, 13120], ids=["gemv_rows", "mfma_rows"])
+def test_forward_few_rows_tall_weight(L, fid, m, n):
+    """At m = 3..4 a weight of more than 13056 rows (205 row tiles of 64, K
+    within 16 chunks of 256) takes the small-batch MFMA kernel unsplit, one of
+    13056 rows the multi-row GEMV: both within the matmul tolerance of the
+    oracle, and on the GEMV side each row equals the m = 1 forward bit for
+    bit."""
+    fmt, bits, group, dq = FORMATS[FMT_IDS.index(fid)]
+    k = 512
+    W = SI.gaussian_weights(9900 + n + m, n, k, outlier_seed=9901)
+    X = SI.bf16_normal(9902 + m, (m, k))
+    qw, ref = _quant_pair(L, W, fmt, bits, group, dq)
+    Xd = to_dev_bf16(X)
+    Y = L.lbq_linear_fwd(Xd, qw)
+    rows = [L.lbq_linear_fwd(Xd[i:i + 1].contiguous(), qw) for i in range(m)] if n == 13056 else []
+    torch.cuda.synchronize()
+    for i, r in enumerate(rows):
+        assert torch.equal(Y[i:i + 1].view(torch.int16), r.view(torch.int16)), f"row {i}"
+    assert_close(bf16_bits_host(Y), O.linear_fwd(X, ref["w_exact"]), what=f"{fid} n={n} m={m}")
+
+
 @pytest.mark.parametrize("bits,group", [(4, 128), (2, 64), (4, 64), (2, 128)])
 @pytest.mark.parametrize("m", [1, 2, 4, 7, 16, 130])
 def test_forward_exact_on_grid_minmax(L, bits, group, m):

@@ -311,21 +311,45 @@ def _fill(t):
     return t / (((t + 255) // 256) * 256)
 
 
-def gemm_set_launches(ns, m) -> int:
+def gemm_splits(n, k, m) -> int:
+    """K ranges of an n x k weight's GEMM at m (the library's rule,
+    k_gemm_fwd.hip): split when its 256x256 tiles fill under half the chip."""
+    t = ((n + 255) // 256) * ((m + 255) // 256)
+    if t >= 128:
+        return 1
+    ks = min(256 // t, 8, k // 3200)
+    if ks < 2:
+        return 1
+    per = ((k + ks - 1) // ks + 1023) // 1024 * 1024
+    return (k + per - 1) // per
+
+
+def gemm_set_launches(ns, k, m) -> int:
     """Launches of one weight kind's GEMM (m > 64) over weights of ns rows:
     the library's rule (k_gemm_fwd.hip) splits a set in two when two tile
-    shapes fill the chip's rounds better by over 5%."""
+    shapes fill the chip's rounds better by over 5%, and a launch in which a
+    weight splits K adds the reduce of its partials."""
     def cost(ns_):
-        a = sum((n + 255) // 256 for n in ns_)
-        t0, t1, t2 = a * ((m + 255) // 256), a * ((m + 127) // 128), sum((n + 127) // 128 for n in ns_) * ((m + 127) // 128)
+        ks = [gemm_splits(n, k, m) for n in ns_]
+        t0 = sum((n + 255) // 256 * ((m + 255) // 256) * s for n, s in zip(ns_, ks))
+        t1 = sum((n + 255) // 256 * ((m + 127) // 128) * s for n, s in zip(ns_, ks))
+        t2 = sum((n + 127) // 128 * ((m + 127) // 128) * s for n, s in zip(ns_, ks))
         return sum(n * m / 65536 for n in ns_) / max(_fill(t0), _fill(t1) * 0.78, _fill(t2) * 0.74)
-    best = 0.95 * cost(ns)
-    return 2 if any(cost(ns[:j]) + cost(ns[j:]) < best for j in range(1, len(ns))) else 1
+
+    def launches(ns_):
+        return 1 + (1 if any(gemm_splits(n, k, m) > 1 for n in ns_) else 0)
+    best, best_cost = 0, 0.95 * cost(ns)
+    for j in range(1, len(ns)):
+        c = cost(ns[:j]) + cost(ns[j:])
+        if c < best_cost:
+            best, best_cost = j, c
+    return launches(ns) if best == 0 else launches(ns[:best]) + launches(ns[best:])
 
 
 def grouped_launches(L, qws, m) -> int:
     """Launches of one lbq_linear_fwd_grouped call (one per weight kind; the
-    small-batch kernel adds its K-split reduce when it needs a workspace)."""
+    small-batch kernel adds its K-split reduce when it needs a workspace, and
+    so does a GEMM launch in which a weight splits K)."""
     kinds = []
     for q in qws:
         key = (q.desc.format, q.desc.bits, q.desc.group, q.desc.double_quant, q.desc.meta)
@@ -343,16 +367,15 @@ def grouped_launches(L, qws, m) -> int:
         if m <= 64:
             n += 1 + (1 if L.lbq_linear_fwd_grouped_workspace_bytes(sub, m) > 0 else 0)
         else:
-            n += gemm_set_launches([q.n for q in sub], m)
+            n += gemm_set_launches([q.n for q in sub], sub[0].k, m)
     return n
 
 
 def single_launches(L, q, m) -> int:
     if m == 1:
         return 1
-    if m <= 64:
-        return 1 + (1 if L.lbq_linear_workspace_bytes(q, m) > 0 else 0)
-    return 1
+    # the small-batch kernel's reduce, or the reduce of a GEMM that splits K
+    return 1 + (1 if L.lbq_linear_workspace_bytes(q, m) > 0 else 0)
 
 
 # ---------------------------------------------------------------------------

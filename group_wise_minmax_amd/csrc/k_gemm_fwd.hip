@@ -83,13 +83,17 @@ struct GemmLds {
   float cbs[16];
 };
 
-// One BN x BM output tile (tx, ty) of Y = X . deq(W)^T (+ the LoRA slab).
+// One BN x BM output tile (tx, ty) of Y = X . deq(W)^T (+ the LoRA slab),
+// summed over K range [k_lo, k_hi) (multiples of 1024 codes, or k_hi = K).
+// With `part` set the fp32 sums go to part[m][n] (a K-split partial; the
+// LoRA slab belongs to the range that starts at 0), else bf16 to Y.
 template <int KIND, int BN, int BM, int WGN, int WGM, bool LORA>
 __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __restrict__ X, int m,
                                               uint16_t* __restrict__ Y, int64_t ldy,
                                               const int32_t* __restrict__ out_rows,
                                               const LoraEpi& lora, const Nf4Table& tab, int tx, int ty,
-                                              GemmLds<BN, BM>& lds) {
+                                              GemmLds<BN, BM>& lds, int64_t k_lo, int64_t k_hi,
+                                              float* __restrict__ part) {
   using T = WKindTraits<KIND>;
   constexpr int NT = WGN * WGM * 64;
   constexpr int CPT = BN * BK / NT;  // codes of one W row a thread dequantizes per stage
@@ -277,9 +281,9 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
   };
 
   if constexpr (T::fmt == FMT_NF4) __syncthreads();  // pair table visible
-  load_stage(0);
+  load_stage(k_lo);
   store_stage(0);
-  if (BK < K) load_stage(BK);
+  if (k_lo + BK < k_hi) load_stage(k_lo + BK);
   __syncthreads();
   int buf = 0;
   if constexpr (WGN * WGM == 8 && BM == 256) {
@@ -292,9 +296,9 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
     // overlap gains.)
     const bool late = wave >= 4;
     auto stage = [&](int64_t t) {
-      if (t + BK < K) {
+      if (t + BK < k_hi) {
         store_stage(buf ^ 1);
-        if (t + 2 * BK < K) load_stage(t + 2 * BK);
+        if (t + 2 * BK < k_hi) load_stage(t + 2 * BK);
       }
     };
     auto mfma_phase = [&]() {
@@ -302,7 +306,7 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
       compute(buf);
       __builtin_amdgcn_s_setprio(0);
     };
-    for (int64_t kt = 0; kt < K; kt += BK) {
+    for (int64_t kt = k_lo; kt < k_hi; kt += BK) {
       if (late) mfma_phase();
       else stage(kt);
       __syncthreads();
@@ -312,10 +316,10 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
       buf ^= 1;
     }
   } else {
-    for (int64_t kt = 0; kt < K; kt += BK) {
-      if (kt + BK < K) {
+    for (int64_t kt = k_lo; kt < k_hi; kt += BK) {
+      if (kt + BK < k_hi) {
         store_stage(buf ^ 1);
-        if (kt + 2 * BK < K) load_stage(kt + 2 * BK);
+        if (kt + 2 * BK < k_hi) load_stage(kt + 2 * BK);
       }
       compute(buf);
       __syncthreads();
@@ -325,7 +329,7 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
 
   // LoRA slab: acc += B_lora[n][:] . T[m][:], r zero-padded to rp (multiple of 32).
   if constexpr (LORA) {
-    for (int ks = 0; ks < lora.rp; ks += 32) {
+    for (int ks = 0; ks < (k_lo == 0 ? lora.rp : 0); ks += 32) {
       u32x4_t af[TN], bf[TM];
 #pragma unroll
       for (int a = 0; a < TN; ++a) {
@@ -355,6 +359,28 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
   }
 
   // Epilogue: lane holds D[n = base + 4*lg + i][m = base + li], i = 0..3.
+  if (part != nullptr) {
+    // fp32 partial sums, [m][n] (the reduce applies out_rows)
+    const bool vec = (w.n & 3) == 0;
+#pragma unroll
+    for (int b = 0; b < TM; ++b) {
+      const int64_t mr = m0 + wm * WM + 16 * b + li;
+      if (mr >= m) continue;
+      float* prow = part + mr * w.n;
+#pragma unroll
+      for (int a = 0; a < TN; ++a) {
+        const int64_t nb = n0 + wn * WN + 16 * a + 4 * lg;
+        if (vec && nb + 3 < w.n) {
+          *reinterpret_cast<f32x4_t*>(prow + nb) = acc[a][b];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (nb + i < w.n) prow[nb + i] = acc[a][b][i];
+        }
+      }
+    }
+    return;
+  }
   if (out_rows != nullptr) {
     // Scattered columns: the lane's 4*TN target columns are loaded together,
     // once (clamped indices; columns past n are never stored).
@@ -406,104 +432,268 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
   }
 }
 
-template <int KIND, int BN, int BM, int WGN, int WGM, bool LORA>
+// K split of an n x k weight at m (its outputs are the same whichever launch
+// runs it): a weight whose 256x256 tiles fill under half the chip runs its K
+// in ks ranges of whole 1024-code blocks -- ks up to 256 / tiles, at most 8,
+// and at most k / 3200 so that the fp32 partials (ks * m * n * 8 bytes of
+// traffic) stay small beside the tile work (2 * m * n * k flops).
+int gemm_splits(int64_t n, int64_t k, int64_t m) {
+  const int64_t t = ((n + 255) / 256) * ((m + 255) / 256);
+  if (t >= 128) return 1;
+  int64_t ks = 256 / t;
+  if (ks > 8) ks = 8;
+  if (ks > k / 3200) ks = k / 3200;
+  if (ks < 2) return 1;
+  const int64_t per = ((k + ks - 1) / ks + 1023) / 1024 * 1024;
+  return (int)((k + per - 1) / per);  // every range non-empty
+}
+
+// K range [lo, hi) of range `split` of ks.
+__device__ __forceinline__ void split_range(int64_t k, int ks, int split, int64_t& lo, int64_t& hi) {
+  const int64_t per = ((k + ks - 1) / ks + 1023) / 1024 * 1024;
+  lo = (int64_t)split * per;
+  hi = lo + per < k ? lo + per : k;
+}
+
+template <int KIND, int BN, int BM, int WGN, int WGM, bool LORA, bool SPLIT>
 __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint16_t* __restrict__ X,
                                                           int m, uint16_t* __restrict__ Y,
                                                           int64_t ldy,
                                                           const int32_t* __restrict__ out_rows,
-                                                          LoraEpi lora, Nf4Table tab) {
+                                                          LoraEpi lora, Nf4Table tab, float* __restrict__ part,
+                                                          int ks) {
   const int nx = (int)((w.n + BN - 1) / BN), ny = (m + BM - 1) / BM;
   int tx, ty;
-  tile_of(blockIdx.x, nx, ny, tx, ty);
   __shared__ __attribute__((aligned(16))) GemmLds<BN, BM> lds;
-  gemm_fwd_tile<KIND, BN, BM, WGN, WGM, LORA>(w, X, m, Y, ldy, out_rows, lora, tab, tx, ty, lds);
+  if constexpr (!SPLIT) {
+    tile_of(blockIdx.x, nx, ny, tx, ty);
+    gemm_fwd_tile<KIND, BN, BM, WGN, WGM, LORA>(w, X, m, Y, ldy, out_rows, lora, tab, tx, ty, lds, 0, w.k,
+                                                nullptr);
+  } else {
+    // workgroups [split * tiles, (split + 1) * tiles) run K range `split`
+    const int tiles = nx * ny;
+    const int split = (int)blockIdx.x / tiles;
+    tile_of((int)blockIdx.x - split * tiles, nx, ny, tx, ty);
+    int64_t lo, hi;
+    split_range(w.k, ks, split, lo, hi);
+    gemm_fwd_tile<KIND, BN, BM, WGN, WGM, LORA>(w, X, m, Y, ldy, out_rows, lora, tab, tx, ty, lds, lo, hi,
+                                                part + (int64_t)split * m * w.n);
+  }
 }
 
 // Several weights that share X: their column tiles are laid side by side
 // (weight i owns tile columns [tile_end[i-1], tile_end[i])), so one launch
-// covers them all and its last round of tiles is shared.
+// covers them all and its last round of tiles is shared.  With K splits
+// (SPLIT), weight i owns workgroups [wg_end[i-1], wg_end[i]) = its tiles x
+// ks[i] instead, and when ks[i] > 1 its partials [ks][m][n] start at part +
+// part_off[i].
 struct GemmSet {
   WView w[kGemvMaxGroup];
   uint16_t* y[kGemvMaxGroup];
   int64_t ldy[kGemvMaxGroup];
   const int32_t* out_rows[kGemvMaxGroup];
   int tile_end[kGemvMaxGroup];
+  int wg_end[kGemvMaxGroup];
+  int ks[kGemvMaxGroup];
+  int64_t part_off[kGemvMaxGroup];
+  int64_t col_end[kGemvMaxGroup];  // prefix sums of n (the reduce's column space)
+  float* part;
   int count;
 };
 
-template <int KIND, int BN, int BM, int WGN, int WGM>
+template <int KIND, int BN, int BM, int WGN, int WGM, bool SPLIT>
 __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd_set(GemmSet set, const uint16_t* __restrict__ X,
                                                               int m, Nf4Table tab) {
-  int nx = set.tile_end[0];
-#pragma unroll
-  for (int i = 1; i < kGemvMaxGroup; ++i)
-    if (i < set.count) nx = set.tile_end[i];
-  int tx, ty;
-  tile_of(blockIdx.x, nx, (m + BM - 1) / BM, tx, ty);
-  int pi = 0, tbeg = 0;
-#pragma unroll
-  for (int i = 1; i < kGemvMaxGroup; ++i)
-    if (i < set.count && tx >= set.tile_end[i - 1]) { pi = i; tbeg = set.tile_end[i - 1]; }
   const LoraEpi none{nullptr, nullptr, 0, 0};
   __shared__ __attribute__((aligned(16))) GemmLds<BN, BM> lds;
-  gemm_fwd_tile<KIND, BN, BM, WGN, WGM, false>(set.w[pi], X, m, set.y[pi], set.ldy[pi], set.out_rows[pi],
-                                               none, tab, tx - tbeg, ty, lds);
+  const int ny = (m + BM - 1) / BM;
+  int tx, ty;
+  if constexpr (!SPLIT) {
+    int nx = set.tile_end[0];
+#pragma unroll
+    for (int i = 1; i < kGemvMaxGroup; ++i)
+      if (i < set.count) nx = set.tile_end[i];
+    tile_of(blockIdx.x, nx, ny, tx, ty);
+    int pi = 0, tbeg = 0;
+#pragma unroll
+    for (int i = 1; i < kGemvMaxGroup; ++i)
+      if (i < set.count && tx >= set.tile_end[i - 1]) { pi = i; tbeg = set.tile_end[i - 1]; }
+    gemm_fwd_tile<KIND, BN, BM, WGN, WGM, false>(set.w[pi], X, m, set.y[pi], set.ldy[pi], set.out_rows[pi],
+                                                 none, tab, tx - tbeg, ty, lds, 0, set.w[pi].k, nullptr);
+  } else {
+    const int b = blockIdx.x;
+    int pi = 0, wbeg = 0;
+#pragma unroll
+    for (int i = 1; i < kGemvMaxGroup; ++i)
+      if (i < set.count && b >= set.wg_end[i - 1]) { pi = i; wbeg = set.wg_end[i - 1]; }
+    const int nx = (int)((set.w[pi].n + BN - 1) / BN);
+    const int tiles = nx * ny, ks = set.ks[pi];
+    const int split = (b - wbeg) / tiles;
+    tile_of(b - wbeg - split * tiles, nx, ny, tx, ty);
+    int64_t lo, hi;
+    split_range(set.w[pi].k, ks, split, lo, hi);
+    float* const p = ks == 1 ? nullptr : set.part + set.part_off[pi] + (int64_t)split * m * set.w[pi].n;
+    gemm_fwd_tile<KIND, BN, BM, WGN, WGM, false>(set.w[pi], X, m, set.y[pi], set.ldy[pi], set.out_rows[pi],
+                                                 none, tab, tx, ty, lds, lo, hi, p);
+  }
+}
+
+// Y[m][col(c)] = bf16(sum over the K ranges of the partials), for the weights
+// of a set with ks > 1 (columns of all weights side by side: weight i owns
+// [col_end[i-1], col_end[i])); row mr = blockIdx.y; the ranges are added in
+// order, their loads issued eight at a time.
+__global__ __launch_bounds__(256) void k_gemm_reduce(GemmSet set, int m) {
+  const int64_t mr = blockIdx.y;
+  const int64_t cg = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int64_t ncol = set.col_end[0];
+#pragma unroll
+  for (int i = 1; i < kGemvMaxGroup; ++i)
+    if (i < set.count) ncol = set.col_end[i];
+  if (cg >= ncol) return;
+  int pi = 0;
+  int64_t cbeg = 0;
+#pragma unroll
+  for (int i = 1; i < kGemvMaxGroup; ++i)
+    if (i < set.count && cg >= set.col_end[i - 1]) { pi = i; cbeg = set.col_end[i - 1]; }
+  const int ks = set.ks[pi];
+  if (ks == 1) return;  // written by the GEMM itself
+  const int64_t n = set.w[pi].n, c = cg - cbeg;
+  const float* p = set.part + set.part_off[pi] + mr * n + c;
+  const int64_t stride = (int64_t)m * n;
+  float v = 0.f;
+  int sidx = 0;
+  for (; sidx + 8 <= ks; sidx += 8) {
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = p[(sidx + j) * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v += t[j];
+  }
+  for (; sidx < ks; ++sidx) v += p[sidx * stride];
+  const int32_t* orow = set.out_rows[pi];
+  set.y[pi][mr * set.ldy[pi] + (orow ? (int64_t)orow[c] : c)] = (uint16_t)bf16_rne(v);
+}
+
+// The set's K splits and partial areas (ks[i] = 1 for every weight when
+// `part` is null); returns whether any weight splits.
+bool plan_splits(GemmSet& set, const WView* ws, int count, int64_t m, float* part) {
+  int64_t off = 0, ncol = 0;
+  bool any = false;
+  for (int i = 0; i < count; ++i) {
+    const int ks = part == nullptr ? 1 : gemm_splits(ws[i].n, ws[i].k, m);
+    set.ks[i] = ks;
+    set.part_off[i] = off;
+    if (ks > 1) {
+      off += ((int64_t)ks * m * ws[i].n + 3) / 4 * 4;  // 16-byte aligned areas
+      any = true;
+    }
+    ncol += ws[i].n;
+    set.col_end[i] = ncol;
+  }
+  set.part = part;
+  return any;
+}
+
+template <int BN, int BM>
+int64_t tiles_of(int64_t n, int64_t m) {
+  return ((n + BN - 1) / BN) * ((m + BM - 1) / BM);
 }
 
 template <int KIND, int BN, int BM, int WGN, int WGM>
 hipError_t launch_set_cfg(const WView* ws, uint16_t* const* ys, const int64_t* ldys,
                           const int32_t* const* orows, int count, const uint16_t* X, int64_t m,
-                          const Nf4Table& tab, hipStream_t s) {
+                          float* part, const Nf4Table& tab, hipStream_t s) {
   GemmSet set{};
   set.count = count;
-  int64_t nx = 0;
+  int64_t nx = 0, wgs = 0;
+  const bool split = plan_splits(set, ws, count, m, part);
   for (int i = 0; i < count; ++i) {
     nx += (ws[i].n + BN - 1) / BN;
+    wgs += tiles_of<BN, BM>(ws[i].n, m) * set.ks[i];
     set.w[i] = ws[i];
     set.y[i] = ys[i];
     set.ldy[i] = ldys[i];
     set.out_rows[i] = orows[i];
     set.tile_end[i] = (int)nx;
+    set.wg_end[i] = (int)wgs;
   }
-  const dim3 grid((unsigned)(nx * ((m + BM - 1) / BM))), block(WGN * WGM * 64);
-  hipLaunchKernelGGL((k_gemm_fwd_set<KIND, BN, BM, WGN, WGM>), grid, block, 0, s, set, X, (int)m, tab);
+  const dim3 block(WGN * WGM * 64);
+  if (!split) {
+    hipLaunchKernelGGL((k_gemm_fwd_set<KIND, BN, BM, WGN, WGM, false>), dim3((unsigned)(nx * ((m + BM - 1) / BM))),
+                       block, 0, s, set, X, (int)m, tab);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((k_gemm_fwd_set<KIND, BN, BM, WGN, WGM, true>), dim3((unsigned)wgs), block, 0, s, set, X,
+                     (int)m, tab);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((set.col_end[count - 1] + 255) / 256), (unsigned)m), dim3(256),
+                     0, s, set, (int)m);
   return hipGetLastError();
 }
 
 template <int KIND, int BN, int BM, int WGN, int WGM>
 hipError_t launch_cfg(const WView& w, const uint16_t* X, int64_t m, uint16_t* Y, int64_t ldy,
-                      const int32_t* out_rows, const LoraEpi& lora, const Nf4Table& tab,
+                      const int32_t* out_rows, const LoraEpi& lora, float* part, const Nf4Table& tab,
                       hipStream_t s) {
-  const int64_t tiles = ((w.n + BN - 1) / BN) * ((m + BM - 1) / BM);
-  const dim3 grid((unsigned)tiles), block(WGN * WGM * 64);
-  if (lora.t != nullptr) {
-    hipLaunchKernelGGL((k_gemm_fwd<KIND, BN, BM, WGN, WGM, true>), grid, block, 0, s, w, X, (int)m,
-                       Y, ldy, out_rows, lora, tab);
-  } else {
-    hipLaunchKernelGGL((k_gemm_fwd<KIND, BN, BM, WGN, WGM, false>), grid, block, 0, s, w, X, (int)m,
-                       Y, ldy, out_rows, lora, tab);
+  const int64_t tiles = tiles_of<BN, BM>(w.n, m);
+  const int ks = part == nullptr ? 1 : gemm_splits(w.n, w.k, m);
+  const dim3 block(WGN * WGM * 64);
+  if (ks == 1) {
+    if (lora.t != nullptr)
+      hipLaunchKernelGGL((k_gemm_fwd<KIND, BN, BM, WGN, WGM, true, false>), dim3((unsigned)tiles), block, 0, s, w,
+                         X, (int)m, Y, ldy, out_rows, lora, tab, nullptr, 1);
+    else
+      hipLaunchKernelGGL((k_gemm_fwd<KIND, BN, BM, WGN, WGM, false, false>), dim3((unsigned)tiles), block, 0, s, w,
+                         X, (int)m, Y, ldy, out_rows, lora, tab, nullptr, 1);
+    return hipGetLastError();
   }
+  const dim3 grid((unsigned)(tiles * ks));
+  if (lora.t != nullptr)
+    hipLaunchKernelGGL((k_gemm_fwd<KIND, BN, BM, WGN, WGM, true, true>), grid, block, 0, s, w, X, (int)m, Y, ldy,
+                       out_rows, lora, tab, part, ks);
+  else
+    hipLaunchKernelGGL((k_gemm_fwd<KIND, BN, BM, WGN, WGM, false, true>), grid, block, 0, s, w, X, (int)m, Y, ldy,
+                       out_rows, lora, tab, part, ks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  GemmSet set{};
+  set.count = 1;
+  set.w[0] = w;
+  set.y[0] = Y;
+  set.ldy[0] = ldy;
+  set.out_rows[0] = out_rows;
+  plan_splits(set, &w, 1, m, part);
+  hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((w.n + 255) / 256), (unsigned)m), dim3(256), 0, s, set, (int)m);
   return hipGetLastError();
 }
 
-// Fraction of the chip's 256 CUs kept busy by `tiles` one-per-CU workgroups.
-double fill(int64_t tiles) {
-  const int64_t waves = (tiles + 255) / 256;
-  return (double)tiles / (double)(waves * 256);
+// Fraction of the chip's 256 CUs kept busy by `wgs` one-per-CU workgroups.
+double fill(int64_t wgs) {
+  const int64_t waves = (wgs + 255) / 256;
+  return (double)wgs / (double)(waves * 256);
+}
+
+// Workgroups of each tile shape (0 = 256x256, 1 = 256x128, 2 = 128x128) for
+// weights ws[0..count), with their K splits when `split`.
+void shape_wgs(const WView* ws, int count, int64_t m, bool split, int64_t t[3]) {
+  t[0] = t[1] = t[2] = 0;
+  for (int i = 0; i < count; ++i) {
+    const int64_t ks = split ? gemm_splits(ws[i].n, ws[i].k, m) : 1;
+    t[0] += tiles_of<256, 256>(ws[i].n, m) * ks;
+    t[1] += tiles_of<256, 128>(ws[i].n, m) * ks;
+    t[2] += tiles_of<128, 128>(ws[i].n, m) * ks;
+  }
 }
 
 // Tile shape with the best (chip fill x per-tile efficiency) for weights of
 // n[0..count) rows: 0 = 256x256, 1 = 256x128, 2 = 128x128.  The per-tile
 // factors are the measured throughput of each shape relative to 256x256 (8
 // waves of 64x128) at full occupancy.
-int pick_tile(const WView* ws, int count, int64_t m) {
-  int64_t t0 = 0, t1 = 0, t2 = 0;
-  for (int i = 0; i < count; ++i) {
-    t0 += ((ws[i].n + 255) / 256) * ((m + 255) / 256);
-    t1 += ((ws[i].n + 255) / 256) * ((m + 127) / 128);
-    t2 += ((ws[i].n + 127) / 128) * ((m + 127) / 128);
-  }
-  const double e0 = fill(t0) * 1.00, e1 = fill(t1) * 0.78, e2 = fill(t2) * 0.74;
+int pick_tile(const WView* ws, int count, int64_t m, bool split) {
+  int64_t t[3];
+  shape_wgs(ws, count, m, split, t);
+  const double e0 = fill(t[0]) * 1.00, e1 = fill(t[1]) * 0.78, e2 = fill(t[2]) * 0.74;
   if (e0 >= e1 && e0 >= e2) return 0;
   return e1 >= e2 ? 1 : 2;
 }
@@ -511,28 +701,24 @@ int pick_tile(const WView* ws, int count, int64_t m) {
 template <int KIND>
 struct GemmFwdLauncher {
   static hipError_t run(const WView& w, const uint16_t* X, int64_t m, uint16_t* Y, int64_t ldy,
-                        const int32_t* out_rows, const LoraEpi& lora, const Nf4Table& tab,
+                        const int32_t* out_rows, const LoraEpi& lora, float* part, const Nf4Table& tab,
                         hipStream_t s) {
-    switch (pick_tile(&w, 1, m)) {
-      case 0: return launch_cfg<KIND, 256, 256, 4, 2>(w, X, m, Y, ldy, out_rows, lora, tab, s);
-      case 1: return launch_cfg<KIND, 256, 128, 4, 2>(w, X, m, Y, ldy, out_rows, lora, tab, s);
-      default: return launch_cfg<KIND, 128, 128, 2, 2>(w, X, m, Y, ldy, out_rows, lora, tab, s);
+    switch (pick_tile(&w, 1, m, part != nullptr)) {
+      case 0: return launch_cfg<KIND, 256, 256, 4, 2>(w, X, m, Y, ldy, out_rows, lora, part, tab, s);
+      case 1: return launch_cfg<KIND, 256, 128, 4, 2>(w, X, m, Y, ldy, out_rows, lora, part, tab, s);
+      default: return launch_cfg<KIND, 128, 128, 2, 2>(w, X, m, Y, ldy, out_rows, lora, part, tab, s);
     }
   }
 };
 
 // Time of one launch over weights ws[0..count), in 256x256-tile units at full
 // efficiency: the work divided by the best (chip fill x per-tile factor).
-double launch_cost(const WView* ws, int count, int64_t m) {
-  int64_t t0 = 0, t1 = 0, t2 = 0;
+double launch_cost(const WView* ws, int count, int64_t m, bool split) {
+  int64_t t[3];
+  shape_wgs(ws, count, m, split, t);
   double work = 0.0;
-  for (int i = 0; i < count; ++i) {
-    t0 += ((ws[i].n + 255) / 256) * ((m + 255) / 256);
-    t1 += ((ws[i].n + 255) / 256) * ((m + 127) / 128);
-    t2 += ((ws[i].n + 127) / 128) * ((m + 127) / 128);
-    work += (double)ws[i].n * (double)m / 65536.0;
-  }
-  const double e = fmax(fill(t0) * 1.00, fmax(fill(t1) * 0.78, fill(t2) * 0.74));
+  for (int i = 0; i < count; ++i) work += (double)ws[i].n * (double)m / 65536.0;
+  const double e = fmax(fill(t[0]) * 1.00, fmax(fill(t[1]) * 0.78, fill(t[2]) * 0.74));
   return work / e;
 }
 
@@ -542,11 +728,11 @@ double launch_cost(const WView* ws, int count, int64_t m) {
 // tiles exactly, and k + v (2048 rows) one round of 256x128 tiles.  Returns
 // the prefix length, or 0 for one launch; a split must save over 5% (it pays
 // a second launch).
-int split_point(const WView* ws, int count, int64_t m) {
+int split_point(const WView* ws, int count, int64_t m, bool split) {
   int best = 0;
-  double best_cost = 0.95 * launch_cost(ws, count, m);
+  double best_cost = 0.95 * launch_cost(ws, count, m, split);
   for (int j = 1; j < count; ++j) {
-    const double c = launch_cost(ws, j, m) + launch_cost(ws + j, count - j, m);
+    const double c = launch_cost(ws, j, m, split) + launch_cost(ws + j, count - j, m, split);
     if (c < best_cost) {
       best = j;
       best_cost = c;
@@ -557,39 +743,51 @@ int split_point(const WView* ws, int count, int64_t m) {
 
 template <int KIND>
 hipError_t launch_set_tiles(const WView* ws, uint16_t* const* ys, const int64_t* ldys, const int32_t* const* orows,
-                            int count, const uint16_t* X, int64_t m, const Nf4Table& tab, hipStream_t s) {
-  switch (pick_tile(ws, count, m)) {
-    case 0: return launch_set_cfg<KIND, 256, 256, 4, 2>(ws, ys, ldys, orows, count, X, m, tab, s);
-    case 1: return launch_set_cfg<KIND, 256, 128, 4, 2>(ws, ys, ldys, orows, count, X, m, tab, s);
-    default: return launch_set_cfg<KIND, 128, 128, 2, 2>(ws, ys, ldys, orows, count, X, m, tab, s);
+                            int count, const uint16_t* X, int64_t m, float* part, const Nf4Table& tab,
+                            hipStream_t s) {
+  switch (pick_tile(ws, count, m, part != nullptr)) {
+    case 0: return launch_set_cfg<KIND, 256, 256, 4, 2>(ws, ys, ldys, orows, count, X, m, part, tab, s);
+    case 1: return launch_set_cfg<KIND, 256, 128, 4, 2>(ws, ys, ldys, orows, count, X, m, part, tab, s);
+    default: return launch_set_cfg<KIND, 128, 128, 2, 2>(ws, ys, ldys, orows, count, X, m, part, tab, s);
   }
 }
 
+// The two launches of a divided set run one after the other on the stream
+// and reuse the same partial area.
 template <int KIND>
 struct GemmFwdSetLauncher {
   static hipError_t run(const WView* ws, uint16_t* const* ys, const int64_t* ldys, const int32_t* const* orows,
-                        int count, const uint16_t* X, int64_t m, const Nf4Table& tab, hipStream_t s) {
-    const int j = split_point(ws, count, m);
-    if (j == 0) return launch_set_tiles<KIND>(ws, ys, ldys, orows, count, X, m, tab, s);
-    const hipError_t e = launch_set_tiles<KIND>(ws, ys, ldys, orows, j, X, m, tab, s);
+                        int count, const uint16_t* X, int64_t m, float* part, const Nf4Table& tab, hipStream_t s) {
+    const int j = split_point(ws, count, m, part != nullptr);
+    if (j == 0) return launch_set_tiles<KIND>(ws, ys, ldys, orows, count, X, m, part, tab, s);
+    const hipError_t e = launch_set_tiles<KIND>(ws, ys, ldys, orows, j, X, m, part, tab, s);
     if (e != hipSuccess) return e;
-    return launch_set_tiles<KIND>(ws + j, ys + j, ldys + j, orows + j, count - j, X, m, tab, s);
+    return launch_set_tiles<KIND>(ws + j, ys + j, ldys + j, orows + j, count - j, X, m, part, tab, s);
   }
 };
 
 }  // namespace
 
+size_t gemm_fwd_workspace_bytes(const int64_t* ns, int count, int64_t k, int64_t m) {
+  size_t b = 0;
+  for (int i = 0; i < count; ++i) {
+    const int ks = gemm_splits(ns[i], k, m);
+    if (ks > 1) b += (size_t)(((int64_t)ks * m * ns[i] + 3) / 4 * 4) * sizeof(float);
+  }
+  return b;
+}
+
 hipError_t launch_gemm_fwd_set(WKind kind, const WView* ws, uint16_t* const* ys, const int64_t* ldys,
                                const int32_t* const* out_rows, int count, const uint16_t* X, int64_t m,
-                               const Nf4Table& tab, hipStream_t s) {
+                               float* part, const Nf4Table& tab, hipStream_t s) {
   if (count < 1 || count > kGemvMaxGroup) return hipErrorInvalidValue;
-  return dispatch_kind<GemmFwdSetLauncher>(kind, ws, ys, ldys, out_rows, count, X, m, tab, s);
+  return dispatch_kind<GemmFwdSetLauncher>(kind, ws, ys, ldys, out_rows, count, X, m, part, tab, s);
 }
 
 hipError_t launch_gemm_fwd(WKind kind, const WView& w, const uint16_t* X, int64_t m,
                            uint16_t* Y, int64_t ldy, const int32_t* out_rows,
-                           const LoraEpi& lora, const Nf4Table& tab, hipStream_t s) {
-  return dispatch_kind<GemmFwdLauncher>(kind, w, X, m, Y, ldy, out_rows, lora, tab, s);
+                           const LoraEpi& lora, float* part, const Nf4Table& tab, hipStream_t s) {
+  return dispatch_kind<GemmFwdLauncher>(kind, w, X, m, Y, ldy, out_rows, lora, part, tab, s);
 }
 
 }  // namespace lbq

@@ -2,8 +2,9 @@
 // cannot allocate device memory (code under stream capture, tight serving
 // loops, harnesses that forbid hipMalloc).  The only scratch memory the
 // forward uses -- the fp32 split-K partial sums of the small-batch kernel
-// (2 <= m <= 64) -- lives in a fixed array in the library's device image
-// instead of a caller workspace; inputs and outputs are still the caller's.
+// (2 <= m <= 64) and of GEMM launches that split K (m > 64) -- lives in a
+// fixed array in the library's device image instead of a caller workspace;
+// inputs and outputs are still the caller's.
 //
 // The array below is a device symbol.  Host code never passes its name to a
 // kernel (on the host the name is only a stand-in, not a device address):
@@ -57,8 +58,11 @@ extern "C" lbq_status lbq_linear_fwd_noalloc(const lbq_desc* desc, const lbq_qte
   lbq_status st = lbq::check_fwd(desc, q, X, m, Y, ldy);
   if (st != LBQ_OK) return st;
   if (m == 0) return lbq::linear_fwd_body(desc, q, X, m, Y, ldy, nullptr, 0, stream, "lbq_linear_fwd_noalloc");
+  // The small-batch kernel's partials are required; the GEMM's K-split
+  // partials (m > kSkinnyMaxM) are used when they fit the array, and the
+  // GEMM runs unsplit when they do not.
   const size_t need = lbq_linear_workspace_bytes(desc, m);
-  if (need > kScratchBytes) {
+  if (m <= lbq::kSkinnyMaxM && need > kScratchBytes) {
     char buf[160];
     snprintf(buf, sizeof buf, "needs %zu bytes of scratch; the allocation-free forward holds %zu", need,
              kScratchBytes);

@@ -223,21 +223,38 @@ bool use_gemvm(const lbq_desc* d, int64_t m) {
   return m < 3 || !lbq::skinny_fills_unsplit(d->n, d->k, m);
 }
 
+// The GEMM's K-split partials (m > kSkinnyMaxM) for weights ns[0..count):
+// the workspace when it holds them (16-byte aligned), else nullptr -- then
+// nothing splits.  Only the small-batch kernel's partials are required.
+float* gemm_part(const int64_t* ns, int count, int64_t k, int64_t m, void* ws, size_t ws_bytes) {
+  const size_t need = lbq::gemm_fwd_workspace_bytes(ns, count, k, m);
+  if (need == 0 || ws == nullptr || ws_bytes < need || !aligned(ws, 16)) return nullptr;
+  return static_cast<float*>(ws);
+}
+
 hipError_t dispatch_fwd(const lbq_desc* desc, const lbq::WView& w, const uint16_t* X, int64_t m,
                         uint16_t* Y, int64_t ldy, const int32_t* out_rows,
-                        const lbq::LoraEpi& lora, void* ws, hipStream_t s) {
+                        const lbq::LoraEpi& lora, void* ws, size_t ws_bytes, hipStream_t s) {
   const lbq::WKind kind = kind_of(desc);
   if (m == 1) return lbq::launch_gemv1(kind, &w, &Y, &out_rows, 1, X, lora, nf4_table(), s);
   if (use_gemvm(desc, m)) return lbq::launch_gemvm(kind, &w, &Y, &ldy, &out_rows, 1, X, m, lora, nf4_table(), s);
   if (m <= lbq::kSkinnyMaxM)
     return lbq::launch_skinny(kind, w, X, m, Y, ldy, out_rows, static_cast<float*>(ws), lora,
                               nf4_table(), s);
-  return lbq::launch_gemm_fwd(kind, w, X, m, Y, ldy, out_rows, lora, nf4_table(), s);
+  const int64_t n = desc->n;
+  return lbq::launch_gemm_fwd(kind, w, X, m, Y, ldy, out_rows, lora, gemm_part(&n, 1, desc->k, m, ws, ws_bytes),
+                              nf4_table(), s);
 }
 
+// Workspace of the forward: the small-batch kernel's partials (required) or,
+// for m > kSkinnyMaxM, the GEMM's K-split partials (optional).
 size_t fwd_workspace(const lbq_desc* desc, int64_t m, bool lora) {
   if (use_gemvm(desc, m)) return 0;
   if (m >= 2 && m <= lbq::kSkinnyMaxM) return lbq::skinny_workspace_bytes(desc->n, desc->k, m, lora);
+  if (m > lbq::kSkinnyMaxM) {
+    const int64_t n = desc->n;
+    return lbq::gemm_fwd_workspace_bytes(&n, 1, desc->k, m);
+  }
   return 0;
 }
 
@@ -281,13 +298,15 @@ lbq_status linear_fwd_body(const lbq_desc* desc, const lbq_qtensor* q, const uin
                            const char* who) {
   if (m == 0) return ok();
   const size_t need = fwd_workspace(desc, m, false);
-  if (need > 0 && (workspace == nullptr || ws_bytes < need))
-    return fail(LBQ_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
-  if (need > 0 && !aligned(workspace, 16)) return fail(LBQ_E_ALIGN, "workspace must be 16-byte aligned");
+  if (m <= lbq::kSkinnyMaxM && need > 0) {  // the GEMM's partials are optional
+    if (workspace == nullptr || ws_bytes < need)
+      return fail(LBQ_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+    if (!aligned(workspace, 16)) return fail(LBQ_E_ALIGN, "workspace must be 16-byte aligned");
+  }
   const lbq::LoraEpi none{nullptr, nullptr, 0, 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
   const lbq::WView w = view_of(desc, q);
-  return hip_status(dispatch_fwd(desc, w, X, m, Y, ldy, q->out_rows, none, workspace, s), who);
+  return hip_status(dispatch_fwd(desc, w, X, m, Y, ldy, q->out_rows, none, workspace, ws_bytes, s), who);
 }
 
 }  // namespace lbq
@@ -374,7 +393,23 @@ size_t lbq_linear_fwd_grouped_workspace_bytes(int32_t count, const lbq_desc* des
   if (count < 1 || count > LBQ_MAX_GROUP || descs == nullptr) return 0;
   for (int32_t i = 0; i < count; ++i)
     if (check_desc(&descs[i]) != LBQ_OK || descs[i].k != descs[0].k) return 0;
-  if (m < 2 || m > lbq::kSkinnyMaxM) return 0;
+  if (m > lbq::kSkinnyMaxM) {  // the GEMM's K-split partials, per kind group
+    size_t need = 0;
+    bool done[LBQ_MAX_GROUP] = {};
+    for (int32_t i = 0; i < count; ++i) {
+      if (done[i]) continue;
+      int64_t ns[LBQ_MAX_GROUP];
+      int c = 0;
+      for (int32_t j = i; j < count; ++j)
+        if (!done[j] && kind_of(&descs[j]) == kind_of(&descs[i])) {
+          done[j] = true;
+          ns[c++] = descs[j].n;
+        }
+      need = std::max(need, lbq::gemm_fwd_workspace_bytes(ns, c, descs[i].k, m));
+    }
+    return need;
+  }
+  if (m < 2) return 0;
   if (skinny_mix_set(count, descs, m)) {
     int64_t ns[LBQ_MAX_GROUP];
     for (int32_t i = 0; i < count; ++i) ns[i] = descs[i].n;
@@ -414,9 +449,11 @@ lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lb
   }
   if (m == 0) return ok();
   const size_t need = lbq_linear_fwd_grouped_workspace_bytes(count, descs, m);
-  if (need > 0 && (workspace == nullptr || ws_bytes < need))
-    return fail(LBQ_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
-  if (need > 0 && !aligned(workspace, 16)) return fail(LBQ_E_ALIGN, "workspace must be 16-byte aligned");
+  if (m <= lbq::kSkinnyMaxM && need > 0) {  // the GEMM's partials are optional
+    if (workspace == nullptr || ws_bytes < need)
+      return fail(LBQ_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+    if (!aligned(workspace, 16)) return fail(LBQ_E_ALIGN, "workspace must be 16-byte aligned");
+  }
   const lbq::LoraEpi none{nullptr, nullptr, 0, 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
@@ -473,7 +510,12 @@ lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lb
     else if (gemvm) e = lbq::launch_gemvm(kind, ws, ys, lds, rows, c, X, m, none, nf4_table(), s);
     else if (m <= lbq::kSkinnyMaxM)
       e = lbq::launch_skinny_set(kind, ws, ys, lds, rows, c, X, m, static_cast<float*>(workspace), nf4_table(), s);
-    else e = lbq::launch_gemm_fwd_set(kind, ws, ys, lds, rows, c, X, m, nf4_table(), s);
+    else {
+      int64_t ns[LBQ_MAX_GROUP];
+      for (int j = 0; j < c; ++j) ns[j] = ws[j].n;
+      e = lbq::launch_gemm_fwd_set(kind, ws, ys, lds, rows, c, X, m,
+                                   gemm_part(ns, c, descs[i].k, m, workspace, ws_bytes), nf4_table(), s);
+    }
   }
   return hip_status(e, "lbq_linear_fwd_grouped");
 }
@@ -624,7 +666,8 @@ lbq_status lbq_lora_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint16
   if (e != hipSuccess) return hip_status(e, "lbq_lora_fwd (adapter product)");
   const lbq::LoraEpi lora{T, B, r, rp};
   const lbq::WView w = view_of(desc, q);
-  return hip_status(dispatch_fwd(desc, w, X, m, Y, ldy, q->out_rows, lora, part, s), "lbq_lora_fwd");
+  return hip_status(dispatch_fwd(desc, w, X, m, Y, ldy, q->out_rows, lora, part, ws_bytes - lora_t_bytes(m, r), s),
+                    "lbq_lora_fwd");
 }
 
 // ---- serialization --------------------------------------------------------

@@ -113,14 +113,20 @@ size_t skinny_workspace_bytes(int64_t n, int64_t k, int64_t m, bool lora);
 hipError_t launch_skinny(WKind kind, const WView& w, const uint16_t* X, int64_t m, uint16_t* Y,
                          int64_t ldy, const int32_t* out_rows, float* part, const LoraEpi& lora,
                          const Nf4Table& tab, hipStream_t s);
+// m > kSkinnyMaxM: the MFMA GEMM.  With `part` (at least
+// gemm_fwd_workspace_bytes() bytes, 16-byte aligned) a weight whose tiles
+// fill under half the chip splits K over several workgroups, whose fp32
+// partials a second kernel sums; with part == nullptr nothing splits.
+size_t gemm_fwd_workspace_bytes(const int64_t* ns, int count, int64_t k, int64_t m);
 hipError_t launch_gemm_fwd(WKind kind, const WView& w, const uint16_t* X, int64_t m,
                            uint16_t* Y, int64_t ldy, const int32_t* out_rows,
-                           const LoraEpi& lora, const Nf4Table& tab, hipStream_t s);
+                           const LoraEpi& lora, float* part, const Nf4Table& tab, hipStream_t s);
 // m > kSkinnyMaxM over up to kGemvMaxGroup weights of one kind that share X
-// (their column tiles side by side in one launch).
+// (their column tiles side by side in one launch; each weight keeps the K
+// split it has alone, so its outputs equal the single-weight call's).
 hipError_t launch_gemm_fwd_set(WKind kind, const WView* ws, uint16_t* const* ys, const int64_t* ldys,
                                const int32_t* const* out_rows, int count, const uint16_t* X, int64_t m,
-                               const Nf4Table& tab, hipStream_t s);
+                               float* part, const Nf4Table& tab, hipStream_t s);
 hipError_t launch_bwd_dx(WKind kind, const WView& w, const uint16_t* dY, int64_t m,
                          uint16_t* dX, const LoraDx& lora, const Nf4Table& tab, hipStream_t s);
 // Input gradient of several weights of one kind and k that share X, summed:

@@ -175,7 +175,9 @@ lbq_status lbq_quantize(const lbq_desc* desc, const float* W, const lbq_qtensor*
 lbq_status lbq_dequant(const lbq_desc* desc, const lbq_qtensor* q, uint16_t* W_bf16,
                        void* stream);
 
-/* Workspace bytes lbq_linear_fwd needs for m rows (0 when none). */
+/* Workspace bytes lbq_linear_fwd takes for m rows (0 when none): for
+ * 2 <= m <= 64 the small-batch kernel's partial sums (required); for m > 64
+ * the partial sums of a GEMM that splits K (optional, see lbq_linear_fwd). */
 size_t lbq_linear_workspace_bytes(const lbq_desc* desc, int64_t m);
 
 /* Forward of the frozen low-bit linear layer, Y = X . deq(W)^T ([BNB]
@@ -188,8 +190,14 @@ size_t lbq_linear_workspace_bytes(const lbq_desc* desc, int64_t m);
  * max(out_rows)); only the n addressed columns of each row are written.
  * m >= 0 (m == 0 is an empty batch: nothing is read or written);
  * (m + 256) * k * 2 and (n + 256) * k must be below 2^32 (LBQ_E_SHAPE
- * otherwise: the GEMM uses 32-bit byte offsets).  `workspace` must hold
- * lbq_linear_workspace_bytes(desc, m) bytes (may be NULL when that is 0).
+ * otherwise: the GEMM uses 32-bit byte offsets).  For m <= 64 `workspace`
+ * must hold lbq_linear_workspace_bytes(desc, m) bytes, 16-byte aligned (may
+ * be NULL when that is 0; LBQ_E_WORKSPACE / LBQ_E_ALIGN otherwise).  For
+ * m > 64 it is optional: with that many bytes (16-byte aligned), a weight
+ * whose 256x256 output tiles fill under half the chip splits K over up to 8
+ * workgroups and a second kernel sums their fp32 partials in a fixed order;
+ * with less (or NULL) the GEMM runs unsplit.  The two results agree within
+ * fp32 rounding, not bit for bit.
  * m == 1 runs a GEMV that streams the packed weight once; 2 <= m <= 4 the
  * same streaming with every row of X staged in LDS (when the rows fit in 64
  * KiB: k up to 7680 for 4-bit MinMax, 7936 for 2-bit and 4096 for NF4 at
@@ -210,12 +218,16 @@ lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint
  * graph, tight serving loops, harnesses that forbid hipMalloc): the forward
  * of lbq_linear_fwd, the same kernels and the same results bit for bit, with
  * no workspace argument.  The only scratch memory the forward uses (the fp32
- * K-split partial sums of the small-batch kernel, 2 <= m <= 64) lives in an
- * array of LBQ_NOALLOC_SCRATCH_BYTES in the library's device image, one per
- * device, held until the process ends; the call allocates and frees nothing.
- * Arguments, layouts and errors as lbq_linear_fwd; LBQ_E_WORKSPACE when the
- * call would need more scratch than the array holds (no shape with m <= 64
- * does: at most 16.75 MB).  The array's device address is looked up on the
+ * K-split partial sums of the small-batch kernel, 2 <= m <= 64, and of a
+ * GEMM that splits K, m > 64) lives in an array of LBQ_NOALLOC_SCRATCH_BYTES
+ * in the library's device image, one per device, held until the process
+ * ends; the call allocates and frees nothing.  Arguments, layouts and errors
+ * as lbq_linear_fwd; LBQ_E_WORKSPACE when a call with m <= 64 would need
+ * more scratch than the array holds (no shape does: at most 16.75 MB).  For
+ * m > 64 a GEMM whose partials do not fit the array runs unsplit, as
+ * lbq_linear_fwd does without a workspace (then the results agree with
+ * lbq_linear_fwd given its workspace within fp32 rounding, not bit for
+ * bit).  The array's device address is looked up on the
  * first call on a device that needs it; that call uses the current device
  * (which must be the stream's).  Every call on a device shares that device's
  * array: calls that overlap on one device (two streams or two host threads)
@@ -226,7 +238,7 @@ lbq_status lbq_linear_fwd_noalloc(const lbq_desc* desc, const lbq_qtensor* q, co
 /* Largest count accepted by lbq_linear_fwd_grouped. */
 #define LBQ_MAX_GROUP 8
 
-/* Workspace bytes lbq_linear_fwd_grouped needs for m rows (0 when none). */
+/* Workspace bytes lbq_linear_fwd_grouped takes for m rows (0 when none). */
 size_t lbq_linear_fwd_grouped_workspace_bytes(int32_t count, const lbq_desc* descs, int64_t m);
 
 /* Forward of several frozen linears that read the same input X (the q, k and
@@ -247,9 +259,11 @@ size_t lbq_linear_fwd_grouped_workspace_bytes(int32_t count, const lbq_desc* des
  * 256x256 tiles and k+v with 256x128 at m = 4096).  At m == 1 a set made of INT4 g128 and
  * INT2 g64 weights only (the channel-mixed layer's two row sets) runs as one
  * launch for both formats.  Each Ys[i] equals what lbq_linear_fwd
- * writes for weight i alone, bit for bit.  `workspace` must hold
+ * writes for weight i alone, bit for bit (given workspaces of the queried
+ * sizes: each weight splits K as it does alone).  `workspace` takes
  * lbq_linear_fwd_grouped_workspace_bytes(count, descs, m) bytes (16-byte
- * aligned; 0 for m == 1, m > 64 and the multi-row GEMV). */
+ * aligned; 0 for m == 1 and the multi-row GEMV): required for m <= 64,
+ * optional for m > 64 as in lbq_linear_fwd. */
 lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lbq_qtensor* qs,
                                   const uint16_t* X, int64_t m, uint16_t* const* Ys,
                                   const int64_t* ldys, void* workspace, size_t ws_bytes,

@@ -280,6 +280,29 @@ def test_grouped_fwd_error_paths(L):
     assert call(descs=dk, m=16, ws=FAKE + 8, wsb=need) == "LBQ_E_ALIGN"
 
 
+def test_gemm_split_workspace_sizes(L):
+    """For m > 64 the workspace queries report the GEMM's K-split partials,
+    ks * m * n fp32 per weight, when a weight's 256x256 output tiles fill under
+    half the chip: ks up to 256 / tiles, at most 8 and at most k / 3200, in
+    whole 1024-code ranges (then the count of non-empty ranges); 0 when the
+    tiles fill the chip or K is short.  The grouped query takes the largest
+    kind group's sum.  A call with less (here: none) runs the GEMM unsplit,
+    so no error."""
+    lib, B = L.lib, ctypes.byref
+    ws = lambda d, m: lib.lbq_linear_workspace_bytes(B(d), m)
+    d8k = L.make_desc("minmax", 1024, 8192)
+    assert ws(d8k, 257) == 2 * 257 * 1024 * 4              # 8 tiles; k / 3200 = 2
+    assert ws(L.make_desc("minmax", 2048, 28672), 1024) == 7 * 1024 * 2048 * 4  # 32 tiles: 8 ranges of 3584 -> 7 of 4096
+    assert ws(L.make_desc("minmax", 4096, 4096), 4096) == 0   # 256 tiles fill the chip
+    assert ws(L.make_desc("minmax", 4096, 14336), 2048) == 0  # 128 tiles: half the chip
+    assert ws(L.make_desc("minmax", 1024, 4096), 257) == 0    # k / 3200 = 1
+    assert ws(L.make_desc("nf4", 8192, 49152, double_quant=True), 512) == 4 * 512 * 8192 * 4  # 64 tiles: 256 / 64
+    dk = [d8k, L.make_desc("minmax", 512, 8192), L.make_desc("minmax", 256, 8192, bits=2)]
+    D = (L.Desc * 3)(*dk)
+    i4 = ws(dk[0], 130) + ws(dk[1], 130)
+    assert lib.lbq_linear_fwd_grouped_workspace_bytes(3, D, 130) == max(i4, ws(dk[2], 130)) > 0
+
+
 def test_grouped_bwd_error_paths(L):
     lib = L.lib
     d = [L.make_desc("minmax", 64, 256), L.make_desc("minmax", 128, 256), L.make_desc("minmax", 32, 256)]

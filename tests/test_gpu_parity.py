@@ -539,6 +539,78 @@ def test_channel_mix_scatter(L, m):
     assert np.array_equal(bf16_bits_host(Yg), bf16_bits_host(Y))
 
 
+# ------------------------------------------------------------------ GEMM K split
+
+# k / 3200 >= 2: a GEMM whose 256x256 tiles fill under half the chip splits K.
+SPLIT_K = 8192
+
+
+@pytest.mark.parametrize("fmtspec", FORMATS, ids=FMT_IDS)
+@pytest.mark.parametrize("n,m", [(518, 100), (1024, 257)])
+def test_gemm_split_k(L, fmtspec, n, m):
+    """m > 64 with few output tiles and long K: the GEMM splits K over
+    workgroups (whole 1024-code blocks, so every metadata batch starts in its
+    range) and a second kernel sums their fp32 partials.  That forward and the
+    unsplit GEMM (an empty workspace) both meet the matmul tolerance; n = 518
+    takes the partials' scalar stores."""
+    fmt, bits, group, dq = fmtspec
+    k = SPLIT_K
+    W = SI.gaussian_weights(9600 + n, n, k, outlier_seed=9601)
+    X = SI.bf16_normal(9602 + m, (m, k))
+    qw, ref = _quant_pair(L, W, fmt, bits, group, dq)
+    assert L.lbq_linear_workspace_bytes(qw, m) > 0  # the split is on
+    Xd = to_dev_bf16(X)
+    Ys = L.lbq_linear_fwd(Xd, qw)
+    Yu = L.lbq_linear_fwd(Xd, qw, workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    Yref = O.linear_fwd(X, ref["w_exact"])
+    assert_close(bf16_bits_host(Ys), Yref, what=f"{fmt}{bits}g{group} split n={n} m={m}")
+    assert_close(bf16_bits_host(Yu), Yref, what=f"{fmt}{bits}g{group} unsplit n={n} m={m}")
+
+
+def test_gemm_split_k_channel_mix_scatter(L):
+    """The channel-mixed layer's two row sets at m = 130 and k = 8192: both
+    GEMMs split K and the reduce scatters through out_rows; one grouped call
+    equals the two single calls bit for bit."""
+    m, n, k = 130, 512, SPLIT_K
+    W = SI.gaussian_weights(9650, n, k, outlier_seed=9651)
+    rows4 = SI.channel_mask(9652, n)
+    rows2 = np.setdiff1d(np.arange(n), rows4).astype(np.int32)
+    X = SI.bf16_normal(9653, (m, k))
+    q4, r4 = _quant_pair(L, W[rows4], "minmax", 4, 128, False)
+    q2, r2 = _quant_pair(L, W[rows2], "minmax", 2, 64, False)
+    q4.out_rows = torch.from_numpy(rows4).to(DEV)
+    q2.out_rows = torch.from_numpy(rows2).to(DEV)
+    assert L.lbq_linear_workspace_bytes(q4, m) > 0 and L.lbq_linear_workspace_bytes(q2, m) > 0
+    Xd = to_dev_bf16(X)
+    Y = torch.zeros((m, n), dtype=torch.bfloat16, device=DEV)
+    L.lbq_linear_fwd(Xd, q4, out=Y)
+    L.lbq_linear_fwd(Xd, q2, out=Y)
+    Yg = torch.zeros((m, n), dtype=torch.bfloat16, device=DEV)
+    L.lbq_linear_fwd_grouped(Xd, [q4, q2], outs=[Yg, Yg])
+    torch.cuda.synchronize()
+    ref = O.channel_mix_fwd(X, [(rows4, r4["w_exact"]), (rows2, r2["w_exact"])])
+    assert_close(bf16_bits_host(Y), ref)
+    assert np.array_equal(bf16_bits_host(Yg), bf16_bits_host(Y))
+
+
+@pytest.mark.parametrize("fmtspec", [FORMATS[0], FORMATS[5]], ids=["i4g128", "nf4dq"])
+def test_gemm_split_k_lora(L, fmtspec):
+    """LoRA forward through a GEMM that splits K: the adapter slab is added
+    once, by the range that starts at k = 0."""
+    fmt, bits, group, dq = fmtspec
+    m, n, k, r = 130, 512, SPLIT_K, 16
+    W = SI.gaussian_weights(9660, n, k)
+    X = SI.bf16_normal(9661, (m, k))
+    A = SI.bf16_normal(9662, (r, k), std=0.01)
+    B = SI.bf16_normal(9663, (n, r), std=0.01)
+    qw, ref = _quant_pair(L, W, fmt, bits, group, dq)
+    assert L.lbq_linear_workspace_bytes(qw, m) > 0
+    Y = L.lbq_lora_fwd(to_dev_bf16(X), qw, to_dev_bf16(A), to_dev_bf16(B), 1.0)
+    torch.cuda.synchronize()
+    assert_close(bf16_bits_host(Y), O.lora_fwd(X, ref["w_exact"], A, B, 1.0))
+
+
 @pytest.mark.parametrize("fmtspec", FORMATS, ids=FMT_IDS)
 def test_forward_gemv_long_rows(L, fmtspec):
     """k = 36864: the arranged x no longer fits the GEMV's LDS budget, so x is
@@ -591,16 +663,16 @@ def test_grouped_fwd_matches_single(L, name, k, m):
         assert_close(bf16_bits_host(Y), O.linear_fwd(X, ref["w_exact"]), what=f"{name} weight {i} m={m}")
 
 
+@pytest.mark.parametrize("k", [1280, 8192], ids=["k1280", "k8192_split"])
 @pytest.mark.parametrize("m", [130, 300])
-def test_grouped_mixed_kinds_gemm_graph_replay(L, m):
+def test_grouped_mixed_kinds_gemm_graph_replay(L, m, k):
     """A grouped call whose weights have several kinds (the two row sets of
-    channel-mixed linears) launches one GEMM per kind on the caller's stream.
-    Captured into a HIP graph after an eager call, every replay -- with eager
-    work and cleared outputs in between -- reproduces the eager outputs bit
-    for bit."""
+    channel-mixed linears) launches one GEMM per kind on the caller's stream
+    (at k = 8192 each splits K and adds a reduce launch).  Captured into a HIP
+    graph after an eager call, every replay -- with eager work and cleared
+    outputs in between -- reproduces the eager outputs bit for bit."""
     specs = GROUP_SETS["channel_mix"]
     ns = [300, 64, 520, 130]
-    k = 1280
     X = SI.bf16_normal(9500 + m, (m, k))
     qws = [_quant_pair(L, SI.gaussian_weights(9510 + i, n, k, outlier_seed=9520 + i), *spec)[0]
            for i, (spec, n) in enumerate(zip(specs, ns))]

@@ -32,18 +32,21 @@ def _case(L, fmt, bits, group, dq, n, k, m, seed):
 
 
 # (format, bits, group, dq), then (n, k, m) of the first and the second call:
-# the second is smaller in every dimension, and m spans the small-batch range
-# that uses the scratch (split K) as well as m = 1 and a GEMM size that do not.
+# the second is smaller in every dimension (or equal in k), and m spans the
+# small-batch range that uses the scratch (split K), m = 1 and a GEMM size that
+# do not, and GEMMs whose K split uses it.
 CASES = [
     (("minmax", 4, 128, False), (4096, 4096, 40), (1040, 1280, 20)),
     (("minmax", 2, 64, False), (2048, 8192, 64), (300, 1024, 16)),
     (("nf4", 4, 64, True), (4096, 4096, 16), (512, 512, 5)),
     (("minmax", 4, 128, False), (32704, 2048, 64), (4096, 2048, 33)),   # the largest scratch any shape needs
     (("minmax", 4, 128, False), (1024, 1024, 1), (256, 256, 130)),
+    (("nf4", 4, 64, True), (1024, 8192, 257), (512, 8192, 100)),       # GEMMs that split K
 ]
 
 
-@pytest.mark.parametrize("spec,first,second", CASES, ids=["i4g128", "i2g64", "nf4dq", "max_scratch", "gemv_gemm"])
+@pytest.mark.parametrize("spec,first,second", CASES,
+                         ids=["i4g128", "i2g64", "nf4dq", "max_scratch", "gemv_gemm", "gemm_split"])
 def test_noalloc_matches_workspace_forward_twice(L, spec, first, second):
     fmt, bits, group, dq = spec
     for call, (n, k, m) in enumerate((first, second)):

@@ -313,9 +313,9 @@ def _fill(t):
 
 def gemm_splits(n, k, m) -> int:
     """K ranges of an n x k weight's GEMM at m (the library's rule,
-    k_gemm_fwd.hip): split when its 256x256 tiles fill under half the chip."""
+    k_gemm_fwd.hip): split when its 256x256 tiles fill at most half the chip."""
     t = ((n + 255) // 256) * ((m + 255) // 256)
-    if t >= 128:
+    if t > 128:
         return 1
     ks = min(256 // t, 8, k // 3200)
     if ks < 2:

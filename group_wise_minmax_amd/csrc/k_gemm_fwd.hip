@@ -433,13 +433,13 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
 }
 
 // K split of an n x k weight at m (its outputs are the same whichever launch
-// runs it): a weight whose 256x256 tiles fill under half the chip runs its K
-// in ks ranges of whole 1024-code blocks -- ks up to 256 / tiles, at most 8,
-// and at most k / 3200 so that the fp32 partials (ks * m * n * 8 bytes of
+// runs it): a weight whose 256x256 tiles fill at most half the chip runs its
+// K in ks ranges of whole 1024-code blocks -- ks up to 256 / tiles, at most
+// 8, and at most k / 3200 so that the fp32 partials (ks * m * n * 8 bytes of
 // traffic) stay small beside the tile work (2 * m * n * k flops).
 int gemm_splits(int64_t n, int64_t k, int64_t m) {
   const int64_t t = ((n + 255) / 256) * ((m + 255) / 256);
-  if (t >= 128) return 1;
+  if (t > 128) return 1;
   int64_t ks = 256 / t;
   if (ks > 8) ks = 8;
   if (ks > k / 3200) ks = k / 3200;

@@ -115,7 +115,7 @@ hipError_t launch_skinny(WKind kind, const WView& w, const uint16_t* X, int64_t 
                          const Nf4Table& tab, hipStream_t s);
 // m > kSkinnyMaxM: the MFMA GEMM.  With `part` (at least
 // gemm_fwd_workspace_bytes() bytes, 16-byte aligned) a weight whose tiles
-// fill under half the chip splits K over several workgroups, whose fp32
+// fill at most half the chip splits K over several workgroups, whose fp32
 // partials a second kernel sums; with part == nullptr nothing splits.
 size_t gemm_fwd_workspace_bytes(const int64_t* ns, int count, int64_t k, int64_t m);
 hipError_t launch_gemm_fwd(WKind kind, const WView& w, const uint16_t* X, int64_t m,

@@ -194,7 +194,7 @@ size_t lbq_linear_workspace_bytes(const lbq_desc* desc, int64_t m);
  * must hold lbq_linear_workspace_bytes(desc, m) bytes, 16-byte aligned (may
  * be NULL when that is 0; LBQ_E_WORKSPACE / LBQ_E_ALIGN otherwise).  For
  * m > 64 it is optional: with that many bytes (16-byte aligned), a weight
- * whose 256x256 output tiles fill under half the chip splits K over up to 8
+ * whose 256x256 output tiles fill at most half the chip splits K over up to 8
  * workgroups and a second kernel sums their fp32 partials in a fixed order;
  * with less (or NULL) the GEMM runs unsplit.  The two results agree within
  * fp32 rounding, not bit for bit.

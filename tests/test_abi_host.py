@@ -282,8 +282,8 @@ def test_grouped_fwd_error_paths(L):
 
 def test_gemm_split_workspace_sizes(L):
     """For m > 64 the workspace queries report the GEMM's K-split partials,
-    ks * m * n fp32 per weight, when a weight's 256x256 output tiles fill under
-    half the chip: ks up to 256 / tiles, at most 8 and at most k / 3200, in
+    ks * m * n fp32 per weight, when a weight's 256x256 output tiles fill at
+    most half the chip: ks up to 256 / tiles, at most 8 and at most k / 3200, in
     whole 1024-code ranges (then the count of non-empty ranges); 0 when the
     tiles fill the chip or K is short.  The grouped query takes the largest
     kind group's sum.  A call with less (here: none) runs the GEMM unsplit,
@@ -294,7 +294,8 @@ def test_gemm_split_workspace_sizes(L):
     assert ws(d8k, 257) == 2 * 257 * 1024 * 4              # 8 tiles; k / 3200 = 2
     assert ws(L.make_desc("minmax", 2048, 28672), 1024) == 7 * 1024 * 2048 * 4  # 32 tiles: 8 ranges of 3584 -> 7 of 4096
     assert ws(L.make_desc("minmax", 4096, 4096), 4096) == 0   # 256 tiles fill the chip
-    assert ws(L.make_desc("minmax", 4096, 14336), 2048) == 0  # 128 tiles: half the chip
+    assert ws(L.make_desc("minmax", 4096, 14336), 2048) == 2 * 2048 * 4096 * 4  # 128 tiles: half the chip
+    assert ws(L.make_desc("minmax", 4096, 14336), 2304) == 0  # 144 tiles
     assert ws(L.make_desc("minmax", 1024, 4096), 257) == 0    # k / 3200 = 1
     assert ws(L.make_desc("nf4", 8192, 49152, double_quant=True), 512) == 4 * 512 * 8192 * 4  # 64 tiles: 256 / 64
     dk = [d8k, L.make_desc("minmax", 512, 8192), L.make_desc("minmax", 256, 8192, bits=2)]

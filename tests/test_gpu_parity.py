@@ -541,7 +541,7 @@ def test_channel_mix_scatter(L, m):
 
 # ------------------------------------------------------------------ GEMM K split
 
-# k / 3200 >= 2: a GEMM whose 256x256 tiles fill under half the chip splits K.
+# k / 3200 >= 2: a GEMM whose 256x256 tiles fill at most half the chip splits K.
 SPLIT_K = 8192
 
 

@@ -496,7 +496,7 @@ struct GemmSet {
   int wg_end[kGemvMaxGroup];
   int ks[kGemvMaxGroup];
   int64_t part_off[kGemvMaxGroup];
-  int64_t col_end[kGemvMaxGroup];  // prefix sums of n (the reduce's column space)
+  int64_t quad_end[kGemvMaxGroup];  // prefix sums of ceil(n / 4) (the reduce's column quads)
   float* part;
   int count;
 };
@@ -539,45 +539,65 @@ __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd_set(GemmSet set, con
 }
 
 // Y[m][col(c)] = bf16(sum over the K ranges of the partials), for the weights
-// of a set with ks > 1 (columns of all weights side by side: weight i owns
-// [col_end[i-1], col_end[i])); row mr = blockIdx.y; the ranges are added in
-// order, their loads issued eight at a time.
+// of a set with ks > 1.  A thread takes 4 adjacent columns of one weight
+// (weight i owns the quads [quad_end[i-1], quad_end[i]) of the column space,
+// its n rounded up to a multiple of 4) in row mr = blockIdx.y; the ranges are
+// added in order, 16-byte partial loads when n % 4 == 0, and an 8-byte store
+// of the 4 bf16 results when Y is contiguous and aligned.
 __global__ __launch_bounds__(256) void k_gemm_reduce(GemmSet set, int m) {
   const int64_t mr = blockIdx.y;
-  const int64_t cg = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  int64_t ncol = set.col_end[0];
+  const int64_t qg = (int64_t)blockIdx.x * 256 + threadIdx.x;  // column quad
+  int64_t nq = set.quad_end[0];
 #pragma unroll
   for (int i = 1; i < kGemvMaxGroup; ++i)
-    if (i < set.count) ncol = set.col_end[i];
-  if (cg >= ncol) return;
+    if (i < set.count) nq = set.quad_end[i];
+  if (qg >= nq) return;
   int pi = 0;
-  int64_t cbeg = 0;
+  int64_t qbeg = 0;
 #pragma unroll
   for (int i = 1; i < kGemvMaxGroup; ++i)
-    if (i < set.count && cg >= set.col_end[i - 1]) { pi = i; cbeg = set.col_end[i - 1]; }
+    if (i < set.count && qg >= set.quad_end[i - 1]) { pi = i; qbeg = set.quad_end[i - 1]; }
   const int ks = set.ks[pi];
   if (ks == 1) return;  // written by the GEMM itself
-  const int64_t n = set.w[pi].n, c = cg - cbeg;
+  const int64_t n = set.w[pi].n, c = 4 * (qg - qbeg);
   const float* p = set.part + set.part_off[pi] + mr * n + c;
   const int64_t stride = (int64_t)m * n;
-  float v = 0.f;
-  int sidx = 0;
-  for (; sidx + 8 <= ks; sidx += 8) {
-    float t[8];
+  const int nc = n - c < 4 ? (int)(n - c) : 4;
+  f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if ((n & 3) == 0) {
+    int sidx = 0;
+    for (; sidx + 4 <= ks; sidx += 4) {
+      f32x4_t t[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) t[j] = p[(sidx + j) * stride];
+      for (int j = 0; j < 4; ++j) t[j] = *reinterpret_cast<const f32x4_t*>(p + (sidx + j) * stride);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v += t[j];
+      for (int j = 0; j < 4; ++j) v += t[j];
+    }
+    for (; sidx < ks; ++sidx) v += *reinterpret_cast<const f32x4_t*>(p + sidx * stride);
+  } else {
+    for (int sidx = 0; sidx < ks; ++sidx)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e < nc) v[e] += p[sidx * stride + e];
   }
-  for (; sidx < ks; ++sidx) v += p[sidx * stride];
+  uint16_t* yrow = set.y[pi] + mr * set.ldy[pi];
   const int32_t* orow = set.out_rows[pi];
-  set.y[pi][mr * set.ldy[pi] + (orow ? (int64_t)orow[c] : c)] = (uint16_t)bf16_rne(v);
+  if (orow == nullptr && nc == 4 && (set.ldy[pi] & 3) == 0 && (reinterpret_cast<uintptr_t>(set.y[pi]) & 7) == 0) {
+    uint2 o;
+    o.x = cvt_pk_bf16(v[0], v[1]);
+    o.y = cvt_pk_bf16(v[2], v[3]);
+    *reinterpret_cast<uint2*>(yrow + c) = o;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e < nc) yrow[orow ? (int64_t)orow[c + e] : c + e] = (uint16_t)bf16_rne(v[e]);
+  }
 }
 
 // The set's K splits and partial areas (ks[i] = 1 for every weight when
 // `part` is null); returns whether any weight splits.
 bool plan_splits(GemmSet& set, const WView* ws, int count, int64_t m, float* part) {
-  int64_t off = 0, ncol = 0;
+  int64_t off = 0, nq = 0;
   bool any = false;
   for (int i = 0; i < count; ++i) {
     const int ks = part == nullptr ? 1 : gemm_splits(ws[i].n, ws[i].k, m);
@@ -587,8 +607,8 @@ bool plan_splits(GemmSet& set, const WView* ws, int count, int64_t m, float* par
       off += ((int64_t)ks * m * ws[i].n + 3) / 4 * 4;  // 16-byte aligned areas
       any = true;
     }
-    ncol += ws[i].n;
-    set.col_end[i] = ncol;
+    nq += (ws[i].n + 3) / 4;
+    set.quad_end[i] = nq;
   }
   set.part = part;
   return any;
@@ -627,7 +647,7 @@ hipError_t launch_set_cfg(const WView* ws, uint16_t* const* ys, const int64_t* l
                      (int)m, tab);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((set.col_end[count - 1] + 255) / 256), (unsigned)m), dim3(256),
+  hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((set.quad_end[count - 1] + 255) / 256), (unsigned)m), dim3(256),
                      0, s, set, (int)m);
   return hipGetLastError();
 }
@@ -664,7 +684,8 @@ hipError_t launch_cfg(const WView& w, const uint16_t* X, int64_t m, uint16_t* Y,
   set.ldy[0] = ldy;
   set.out_rows[0] = out_rows;
   plan_splits(set, &w, 1, m, part);
-  hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((w.n + 255) / 256), (unsigned)m), dim3(256), 0, s, set, (int)m);
+  hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((set.quad_end[0] + 255) / 256), (unsigned)m), dim3(256), 0, s,
+                     set, (int)m);
   return hipGetLastError();
 }
 

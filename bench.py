@@ -113,7 +113,7 @@ EXTRA_PHASES = ("copy_1g",)  # opt-in: plain 1 GiB device copy (counter calibrat
 # Kernel-name patterns (rocprofv3 demangled names) whose HBM traffic the
 # counter summary reports, with the phase they are measured in.
 TRAFFIC_KERNELS = {
-    "fwd_m4096_big": ("k_gemm_fwd<5, 256, 256, 4, 2, false>", "k_gemm_fwd_set<5, 256, 256, 4, 2>"),
+    "fwd_m4096_big": ("k_gemm_fwd<5, 256, 256, 4, 2, false, false>", "k_gemm_fwd_set<5, 256, 256, 4, 2, false>"),
     "gemv_m1": ("k_gemv1<0,", "k_gemv1_set<0,"),
     "gemvm_m4": ("k_gemvm<0,", "k_gemvm_set<0,"),
     "skinny_m16": ("k_skinny<0,", "k_skinny_set<0,"),
@@ -123,6 +123,7 @@ TRAFFIC_KERNELS = {
     "quant_nf4dq": ("k_quant_nf4<1,",),
     "dequant_nf4dq": ("k_dequant<5>",),
     "bwd_m4096": ("k_bwd_dx<5, 256, 256",),
+    "gemm_reduce_m1024": ("k_gemm_reduce",),
 }
 
 

@@ -39,10 +39,17 @@ constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
 __device__ __forceinline__ uint32_t pr01(uint32_t v) { return perm_b32(k43, v, 0x04010400u); }
 __device__ __forceinline__ uint32_t pr23(uint32_t v) { return perm_b32(k43, v, 0x04030402u); }
 
-template <int KIND>
+// Codes per chunk of the MB x 16-row tiles: 256, or 128 for MB = 4, whose x
+// tile would otherwise leave room for one workgroup per CU (90 KB of LDS;
+// with 128-code chunks, 49 KB: three).  K splits are still counted in
+// 256-code chunks.
+template <int MB>
+constexpr int kct_of() { return MB == 4 ? 128 : KC; }
+
+template <int KIND, int KCT = KC>
 struct SkTraits {
   using T = WKindTraits<KIND>;
-  static constexpr int RB = KC * T::bits / 8;   // packed bytes per row per chunk (128 / 64)
+  static constexpr int RB = KCT * T::bits / 8;  // packed bytes per row per chunk (128 / 64 at KCT = 256)
   static constexpr int RBP = RB + 16;           // padded LDS row: conflict-free A reads
   static constexpr int GRP = T::fmt == FMT_MINMAX ? T::group : 64;
 };
@@ -50,11 +57,11 @@ struct SkTraits {
 // A fragment (8 codes -> 4 dwords of bf16 pairs) for k-step t of row `row`
 // and lane group lg from a staged chunk.  Its k-slot order matches the order
 // in which x is stored (arrange8()).
-template <int KIND>
+template <int KIND, int KCT>
 __device__ __forceinline__ u32x4_t a_frag(const uint8_t* wl, int row, int lg, int t,
                                           const uint32_t* lut, int lane32) {
   using T = WKindTraits<KIND>;
-  using S = SkTraits<KIND>;
+  using S = SkTraits<KIND, KCT>;
   if constexpr (T::bits == 4) {
     const uint32_t w = *reinterpret_cast<const uint32_t*>(wl + row * S::RBP + 16 * t + 4 * lg);
     if constexpr (T::fmt == FMT_MINMAX) {
@@ -101,17 +108,17 @@ __device__ __forceinline__ int x_off(int lg, int t) {
 template <int RBP_, int NG_, int MB, int LUT>
 struct SkLds {
   uint8_t Ws[2][ROWS * RBP_];
-  uint16_t Xs[2][MB * 16 * (KC + 8)];
+  uint16_t Xs[2][MB * 16 * (kct_of<MB>() + 8)];
   float2 meta[2][ROWS][NG_];  // (scale, 128 + zero) or (absmax, 0)
   uint32_t lut[LUT];
   float cbs[16];
 };
 template <int KIND, int MB>
-using SkLdsOf = SkLds<SkTraits<KIND>::RBP, KC / 64, MB,
+using SkLdsOf = SkLds<SkTraits<KIND, kct_of<MB>()>::RBP, KC / 64, MB,
                       WKindTraits<KIND>::fmt == FMT_NF4 ? 256 * kLutCopies : 1>;
 // A workgroup of the INT4 g128 / INT2 g64 mix holds either kind's tile.
 template <int MB>
-using SkLdsMix = SkLds<SkTraits<WK_I4G128>::RBP, KC / 64, MB, 1>;
+using SkLdsMix = SkLds<SkTraits<WK_I4G128, kct_of<MB>()>::RBP, KC / 64, MB, 1>;
 
 // Row tile `tile` (ROWS rows of W) over K range `split` of ks_count; with
 // `part` set, the fp32 sums go to part[split][m][n], else bf16 to Y.
@@ -123,13 +130,16 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
                                             const LoraEpi& lora, const Nf4Table& tab, int tile, int split,
                                             LDS& lds) {
   using T = WKindTraits<KIND>;
-  using S = SkTraits<KIND>;
+  constexpr int KCT = kct_of<MB>();     // codes per chunk
+  using S = SkTraits<KIND, KCT>;
   constexpr int RB = S::RB, RBP = S::RBP, GRP = S::GRP;
-  constexpr int NG = KC / GRP;          // groups (blocks) per chunk
-  constexpr int LDX = KC + 8;           // padded x row (bf16)
+  constexpr int NG = KCT / GRP;         // groups (blocks) per chunk
+  constexpr int LDX = KCT + 8;          // padded x row (bf16)
   constexpr int WCOL = RB / 16;         // 16-byte W columns per row
-  constexpr int WLD = ROWS * WCOL / kThreads;   // W loads per thread per chunk
-  constexpr int XLD = MB * 16 * (KC / 8) / kThreads;  // X loads per thread per chunk
+  constexpr int WLDN = ROWS * WCOL;     // 16-byte W loads per chunk
+  constexpr int WLD = (WLDN + kThreads - 1) / kThreads;  // per thread (the last partly idle)
+  constexpr int XLD = MB * 16 * (KCT / 8) / kThreads;    // X loads per thread per chunk
+  constexpr int KSW = KCT / 128;        // k-steps of 32 codes per wave and chunk
   static_assert(sizeof(lds.Ws[0]) >= ROWS * RBP && sizeof(lds.Xs[0]) == MB * 16 * LDX * 2, "tile LDS");
   static_assert(sizeof(lds.meta[0][0]) == 4 * sizeof(float2) && NG <= 4 && kThreads == 4 * ROWS, "tile LDS");
   static_assert(T::fmt != FMT_NF4 || sizeof(lds.lut) >= 256 * kLutCopies * 4, "tile LDS");
@@ -146,10 +156,11 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
   const int64_t K = w.k;
   const int64_t KB = K * T::bits / 8;
   const int64_t gpr = K / GRP;
+  // The split's range of 256-code chunks, then in chunks of KCT codes.
   const int nchunk = (int)((K + KC - 1) / KC);
   const int per = (nchunk + ks_count - 1) / ks_count;
-  const int c_lo = split * per;
-  const int c_hi = min(c_lo + per, nchunk);
+  const int c_lo = split * per * (KC / KCT);
+  const int c_hi = (int)min((int64_t)min(split * per + per, nchunk) * (KC / KCT), (K + KCT - 1) / KCT);
   float dqoff = 0.f;  // offset of double quantization with an offset
   if constexpr (T::dqo) dqoff = nf4_dq_offset(w);
 
@@ -180,14 +191,14 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
   uint32_t wrow[WLD], xrow[XLD];
 #pragma unroll
   for (int i = 0; i < WLD; ++i)
-    wrow[i] = (uint32_t)min(n0 + (tid + kThreads * i) / WCOL, w.n - 1) * (uint32_t)KB;
+    wrow[i] = (uint32_t)min(n0 + min(tid + kThreads * i, WLDN - 1) / WCOL, w.n - 1) * (uint32_t)KB;
 #pragma unroll
   for (int i = 0; i < XLD; ++i)
-    xrow[i] = 2u * (uint32_t)min((tid + kThreads * i) / (KC / 8), m - 1) * (uint32_t)K;
+    xrow[i] = 2u * (uint32_t)min((tid + kThreads * i) / (KCT / 8), m - 1) * (uint32_t)K;
   const uint32_t mrow = (uint32_t)min(n0 + tid / 4, w.n - 1) * (uint32_t)gpr;
   auto load = [&](int c) {
-    const uint32_t kc = (uint32_t)c * (uint32_t)KC;
-    const int kend = (int)min(K - (int64_t)kc, (int64_t)KC);  // codes in this chunk (multiple of 64)
+    const uint32_t kc = (uint32_t)c * (uint32_t)KCT;
+    const int kend = (int)min(K - (int64_t)kc, (int64_t)KCT);  // codes in this chunk (multiple of 64)
 #pragma unroll
     for (int i = 0; i < WLD; ++i) {
       const int col = (tid + kThreads * i) % WCOL;
@@ -200,7 +211,7 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
     }
 #pragma unroll
     for (int i = 0; i < XLD; ++i) {
-      const int col = (tid + kThreads * i) % (KC / 8);
+      const int col = (tid + kThreads * i) % (KCT / 8);
       const uint32_t xo = xrow[i] + 2u * (kc + (col * 8 < kend ? col * 8u : 0u));  // as above
       xr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r_x, xo, 0, 0));
     }
@@ -215,12 +226,13 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
 #pragma unroll
     for (int i = 0; i < WLD; ++i) {
       const int e = tid + kThreads * i;
-      *reinterpret_cast<u32x4_t*>(&Ws[b][(e / WCOL) * RBP + (e % WCOL) * 16]) = wr[i];
+      if (WLDN % kThreads == 0 || e < WLDN)  // (2-bit 128-code chunks: half the threads)
+        *reinterpret_cast<u32x4_t*>(&Ws[b][(e / WCOL) * RBP + (e % WCOL) * 16]) = wr[i];
     }
 #pragma unroll
     for (int i = 0; i < XLD; ++i) {
       const int e = tid + kThreads * i;
-      *reinterpret_cast<u32x4_t*>(&Xs[b][(e / (KC / 8)) * LDX + (e % (KC / 8)) * 8]) = arrange8<KIND>(xr[i]);
+      *reinterpret_cast<u32x4_t*>(&Xs[b][(e / (KCT / 8)) * LDX + (e % (KCT / 8)) * 8]) = arrange8<KIND>(xr[i]);
     }
     if (tid % 4 < NG) {
       const float sc = meta_raw_scale<KIND>(mraw, dqoff);
@@ -229,10 +241,10 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
     }
   };
 
-  // Wave w takes k-steps 2w and 2w+1 of every chunk (codes [64w, 64w + 64))
-  // for all ROWS rows: each x fragment it reads feeds the 4 row tiles, and
-  // the sum of x (MinMax) is formed once for them.  The waves' sums are
-  // added in wave order at the end.
+  // Wave w takes k-steps KSW w .. KSW w + KSW - 1 of every chunk (codes
+  // [KCT w / 4, KCT (w + 1) / 4)) for all ROWS rows: each x fragment it reads
+  // feeds the 4 row tiles, and the sum of x (MinMax) is formed once for them.
+  // The waves' sums are added in wave order at the end.
   f32x4_t acc[4][MB];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -240,13 +252,13 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
     for (int q = 0; q < MB; ++q) acc[j][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const u32x4_t ones = u32x4_t{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
   const int lane32 = lane & 31;
-  const int t0 = 2 * wave;                // this wave's first k-step in a chunk
-  const int gw = (KC / 4) * wave / GRP;   // the group (block) its codes belong to
+  const int t0 = KSW * wave;               // this wave's first k-step in a chunk
+  const int gw = (KCT / 4) * wave / GRP;   // the group (block) its codes belong to
 
   auto compute = [&](int b, int c) {
-    const int64_t kc = (int64_t)c * KC;
-    const int64_t kend = (K - kc) < KC ? (K - kc) : KC;  // a multiple of 64
-    if ((int64_t)(KC / 4) * wave >= kend) return;
+    const int64_t kc = (int64_t)c * KCT;
+    const int64_t kend = (K - kc) < KCT ? (K - kc) : KCT;  // a multiple of 64
+    if ((int64_t)(KCT / 4) * wave >= kend) return;
     const uint8_t* wl = Ws[b];
     f32x4_t ag[4][MB], xs[MB];
 #pragma unroll
@@ -256,7 +268,7 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
       for (int j = 0; j < 4; ++j) ag[j][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < KSW; ++tt) {
       const int t = t0 + tt;
       u32x4_t xf[MB];
 #pragma unroll
@@ -266,7 +278,7 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const u32x4_t af = a_frag<KIND>(wl, 16 * j + li, lg, t, lut, lane32);
+        const u32x4_t af = a_frag<KIND, KCT>(wl, 16 * j + li, lg, t, lut, lane32);
 #pragma unroll
         for (int q = 0; q < MB; ++q) ag[j][q] = mfma16x16x32(af, xf[q], ag[j][q]);
       }
@@ -306,27 +318,34 @@ __device__ __forceinline__ void skinny_tile(const WView& w, const uint16_t* __re
   }
 
   // Sum of the four waves' accumulators through LDS (the x buffers are free
-  // after the last barrier): red[w][j][q][i][lane]; wave w then adds row
-  // tile j = w's values in wave order.
-  static_assert(sizeof(lds.Xs) >= 4 * 4 * MB * 4 * 64 * sizeof(float), "reduction LDS");
+  // after the last barrier): red[w][j][q][i][lane] for RQ of the MB column
+  // tiles at a time (all of them unless the x buffers are too small); wave w
+  // then adds row tile j = w's values in wave order.
+  constexpr int RQ1 = (int)(sizeof(lds.Xs) / (4 * 4 * 4 * 64 * sizeof(float)));
+  constexpr int RQ = RQ1 < MB ? RQ1 : MB;
+  static_assert(RQ >= 1 && MB % RQ == 0, "reduction LDS");
   float* const red = reinterpret_cast<float*>(&Xs[0][0]);
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int q = 0; q < MB; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[(((wave * 4 + j) * MB + q) * 4 + i) * 64 + lane] = acc[j][q][i];
-  __syncthreads();
   f32x4_t sum[MB];
 #pragma unroll
-  for (int q = 0; q < MB; ++q)
+  for (int q0 = 0; q0 < MB; q0 += RQ) {
+    if (q0 > 0) __syncthreads();  // the previous part has been read
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = red[(((0 * 4 + wave) * MB + q) * 4 + i) * 64 + lane];
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int w2 = 1; w2 < 4; ++w2) v += red[(((w2 * 4 + wave) * MB + q) * 4 + i) * 64 + lane];
-      sum[q][i] = v;
-    }
+      for (int q = 0; q < RQ; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[(((wave * 4 + j) * RQ + q) * 4 + i) * 64 + lane] = acc[j][q0 + q][i];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < RQ; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = red[(((0 * 4 + wave) * RQ + q) * 4 + i) * 64 + lane];
+#pragma unroll
+        for (int w2 = 1; w2 < 4; ++w2) v += red[(((w2 * 4 + wave) * RQ + q) * 4 + i) * 64 + lane];
+        sum[q0 + q][i] = v;
+      }
+  }
 
   // lane holds D[n = n0 + 16 wave + 4lg + i][m = 16q + li]
   const int trow = 16 * wave;

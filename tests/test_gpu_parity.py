@@ -637,7 +637,7 @@ GROUP_SETS = {
 
 @pytest.mark.parametrize("name", list(GROUP_SETS))
 @pytest.mark.parametrize("k", [1280, 12288])
-@pytest.mark.parametrize("m", [1, 3, 16, 40, 130, 300])
+@pytest.mark.parametrize("m", [1, 3, 16, 40, 57, 130, 300])
 def test_grouped_fwd_matches_single(L, name, k, m):
     """Weights sharing X in one call: each output equals the single-weight
     forward bit for bit (same kernels, same per-row order) and the oracle

@@ -607,8 +607,9 @@ constexpr int64_t skinny_slots() {
 namespace {
 bool fills_unsplit(int64_t tiles, int64_t nchunk, int64_t m) {
   const int mb = m <= 16 ? 1 : m <= 32 ? 2 : m <= 48 ? 3 : 4;
-  const int64_t slots = mb == 1 ? skinny_slots<1>() : mb == 2 ? skinny_slots<2>() : skinny_slots<3>();
-  return mb <= 3 && tiles * 5 >= slots && nchunk <= 16 * mb;
+  const int64_t slots = mb == 1 ? skinny_slots<1>() : mb == 2 ? skinny_slots<2>() : mb == 3 ? skinny_slots<3>()
+                                                                                           : skinny_slots<4>();
+  return tiles * 5 >= slots && nchunk <= 16 * mb;
 }
 }  // namespace
 
@@ -623,9 +624,9 @@ int skinny_splits_tiles(int64_t tiles, int64_t k, int64_t m) {
   // sums and no reduce launch.  (Such weights come in sets -- gate and up --
   // that fill the chip together.  Measured: 8B gate+up at m = 16 31.1 ->
   // 25.7 us and at m = 48 56.1 -> 41.5 us; the 70B channel-mix layer at
-  // m = 40 +8%.  Longer K ranges -- the 70B INT2 gate/up rows at m = 3 and
-  // 16 -- and m > 48, where the 256 resident workgroups are too few, lost
-  // 4-7% and up to 2.6x unsplit.)  Other weights aim at ~512 workgroups,
+  // m = 40 +8%, gate+up at m = 64 75.0 -> 55.5 us.  Longer K ranges -- the
+  // 70B INT2 gate/up rows at m = 3 and 16 -- lost 4-7% unsplit.)  Other
+  // weights aim at ~512 workgroups,
   // with the fp32 partial traffic (ks * m * n * 8 bytes) kept below the
   // packed weight (n * k / 2 bytes for 4-bit).  Measured on the 8B layer:
   // more splits lose to the shorter K ranges, a tighter cap (a quarter of the

@@ -216,8 +216,8 @@ lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint
 
 /* For callers that cannot allocate device memory (work captured into a HIP
  * graph, tight serving loops, harnesses that forbid hipMalloc): the forward
- * of lbq_linear_fwd, the same kernels and the same results bit for bit, with
- * no workspace argument.  The only scratch memory the forward uses (the fp32
+ * of lbq_linear_fwd, the same kernels and the same results bit for bit
+ * (except as noted below for m > 64), with no workspace argument.  The only scratch memory the forward uses (the fp32
  * K-split partial sums of the small-batch kernel, 2 <= m <= 64, and of a
  * GEMM that splits K, m > 64) lives in an array of LBQ_NOALLOC_SCRATCH_BYTES
  * in the library's device image, one per device, held until the process

@@ -318,10 +318,11 @@ def gemm_splits(n, k, m) -> int:
     t = ((n + 255) // 256) * ((m + 255) // 256)
     if t > 128:
         return 1
-    ks = min(256 // t, 8, k // 3200)
+    unit = 512 if m <= 256 and t <= 32 else 1024
+    ks = min(256 // t, 8, k // 512 if unit == 512 else k // 3200)
     if ks < 2:
         return 1
-    per = ((k + ks - 1) // ks + 1023) // 1024 * 1024
+    per = ((k + ks - 1) // ks + unit - 1) // unit * unit
     return (k + per - 1) // per
 
 

@@ -434,23 +434,38 @@ __device__ __forceinline__ void gemm_fwd_tile(const WView& w, const uint16_t* __
 
 // K split of an n x k weight at m (its outputs are the same whichever launch
 // runs it): a weight whose 256x256 tiles fill at most half the chip runs its
-// K in ks ranges of whole 1024-code blocks -- ks up to 256 / tiles, at most
-// 8, and at most k / 3200 so that the fp32 partials (ks * m * n * 8 bytes of
-// traffic) stay small beside the tile work (2 * m * n * k flops).
+// K in ks ranges -- ks up to 256 / tiles and at most 8.  Its tile time is
+// that of the whole K whatever the tile count, so a split saves about
+// (1 - 1/ks) of it against fp32 partials of ks * m * n * 8 bytes of traffic.
+//  * In general ks is kept to k / 3200 (the partials at most about a quarter
+//    of the tile time at 1 PFLOP/s and 5 TB/s), in ranges of whole 1024-code
+//    blocks.
+//  * For m <= 256 a weight that alone fills at most an eighth of the chip (32
+//    tiles: q, k, v, o or down of an 8B layer, whose tile time does not
+//    shrink with m there) may use ranges of 512 codes, k / 512 of them: its
+//    partials are small.  A larger weight (gate or up) is left alone: its
+//    set already fills the chip.
+// Either way every range starts on a metadata batch of four groups (or four
+// NF4 blocks).
+__host__ __device__ inline int split_unit(int64_t n, int64_t m) {
+  return m <= 256 && ((n + 255) / 256) * ((m + 255) / 256) <= 32 ? 512 : 1024;
+}
 int gemm_splits(int64_t n, int64_t k, int64_t m) {
   const int64_t t = ((n + 255) / 256) * ((m + 255) / 256);
   if (t > 128) return 1;
   int64_t ks = 256 / t;
   if (ks > 8) ks = 8;
-  if (ks > k / 3200) ks = k / 3200;
+  const int unit = split_unit(n, m);
+  const int64_t kmax = unit == 512 ? k / 512 : k / 3200;
+  if (ks > kmax) ks = kmax;
   if (ks < 2) return 1;
-  const int64_t per = ((k + ks - 1) / ks + 1023) / 1024 * 1024;
+  const int64_t per = ((k + ks - 1) / ks + unit - 1) / unit * unit;
   return (int)((k + per - 1) / per);  // every range non-empty
 }
 
-// K range [lo, hi) of range `split` of ks.
-__device__ __forceinline__ void split_range(int64_t k, int ks, int split, int64_t& lo, int64_t& hi) {
-  const int64_t per = ((k + ks - 1) / ks + 1023) / 1024 * 1024;
+// K range [lo, hi) of range `split` of ks (unit: split_unit of the weight).
+__device__ __forceinline__ void split_range(int64_t k, int ks, int unit, int split, int64_t& lo, int64_t& hi) {
+  const int64_t per = ((k + ks - 1) / ks + unit - 1) / unit * unit;
   lo = (int64_t)split * per;
   hi = lo + per < k ? lo + per : k;
 }
@@ -475,7 +490,7 @@ __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd(WView w, const uint1
     const int split = (int)blockIdx.x / tiles;
     tile_of((int)blockIdx.x - split * tiles, nx, ny, tx, ty);
     int64_t lo, hi;
-    split_range(w.k, ks, split, lo, hi);
+    split_range(w.k, ks, split_unit(w.n, m), split, lo, hi);
     gemm_fwd_tile<KIND, BN, BM, WGN, WGM, LORA>(w, X, m, Y, ldy, out_rows, lora, tab, tx, ty, lds, lo, hi,
                                                 part + (int64_t)split * m * w.n);
   }
@@ -531,7 +546,7 @@ __global__ __launch_bounds__(WGN* WGM * 64) void k_gemm_fwd_set(GemmSet set, con
     const int split = (b - wbeg) / tiles;
     tile_of(b - wbeg - split * tiles, nx, ny, tx, ty);
     int64_t lo, hi;
-    split_range(set.w[pi].k, ks, split, lo, hi);
+    split_range(set.w[pi].k, ks, split_unit(set.w[pi].n, m), split, lo, hi);
     float* const p = ks == 1 ? nullptr : set.part + set.part_off[pi] + (int64_t)split * m * set.w[pi].n;
     gemm_fwd_tile<KIND, BN, BM, WGN, WGM, false>(set.w[pi], X, m, set.y[pi], set.ldy[pi], set.out_rows[pi],
                                                  none, tab, tx, ty, lds, lo, hi, p);

@@ -194,8 +194,9 @@ size_t lbq_linear_workspace_bytes(const lbq_desc* desc, int64_t m);
  * must hold lbq_linear_workspace_bytes(desc, m) bytes, 16-byte aligned (may
  * be NULL when that is 0; LBQ_E_WORKSPACE / LBQ_E_ALIGN otherwise).  For
  * m > 64 it is optional: with that many bytes (16-byte aligned), a weight
- * whose 256x256 output tiles fill at most half the chip splits K over up to 8
- * workgroups and a second kernel sums their fp32 partials in a fixed order;
+ * whose 256x256 output tiles fill at most half the chip (for m <= 256 and
+ * short K, at most an eighth) splits K over up to 8 workgroups and a second
+ * kernel sums their fp32 partials in a fixed order;
  * with less (or NULL) the GEMM runs unsplit.  The two results agree within
  * fp32 rounding, not bit for bit.
  * m == 1 runs a GEMV that streams the packed weight once; 2 <= m <= 4 the

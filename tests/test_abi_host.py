@@ -283,8 +283,9 @@ def test_grouped_fwd_error_paths(L):
 def test_gemm_split_workspace_sizes(L):
     """For m > 64 the workspace queries report the GEMM's K-split partials,
     ks * m * n fp32 per weight, when a weight's 256x256 output tiles fill at
-    most half the chip: ks up to 256 / tiles, at most 8 and at most k / 3200, in
-    whole 1024-code ranges (then the count of non-empty ranges); 0 when the
+    most half the chip: ks up to 256 / tiles, at most 8 and at most k / 3200
+    in 1024-code ranges (k / 512 in 512-code ranges for m <= 256 and at most
+    32 tiles), then the count of non-empty ranges; 0 when the
     tiles fill the chip or K is short.  The grouped query takes the largest
     kind group's sum.  A call with less (here: none) runs the GEMM unsplit,
     so no error."""
@@ -293,6 +294,9 @@ def test_gemm_split_workspace_sizes(L):
     d8k = L.make_desc("minmax", 1024, 8192)
     assert ws(d8k, 257) == 2 * 257 * 1024 * 4              # 8 tiles; k / 3200 = 2
     assert ws(L.make_desc("minmax", 2048, 28672), 1024) == 7 * 1024 * 2048 * 4  # 32 tiles: 8 ranges of 3584 -> 7 of 4096
+    assert ws(L.make_desc("minmax", 4096, 4096), 128) == 8 * 128 * 4096 * 4    # m <= 256, 16 tiles: 512-code ranges
+    assert ws(L.make_desc("minmax", 4096, 1536), 100) == 3 * 100 * 4096 * 4    # k / 512 = 3
+    assert ws(L.make_desc("minmax", 14336, 4096), 128) == 0                    # 56 tiles: k / 3200 = 1
     assert ws(L.make_desc("minmax", 4096, 4096), 4096) == 0   # 256 tiles fill the chip
     assert ws(L.make_desc("minmax", 4096, 14336), 2048) == 2 * 2048 * 4096 * 4  # 128 tiles: half the chip
     assert ws(L.make_desc("minmax", 4096, 14336), 2304) == 0  # 144 tiles

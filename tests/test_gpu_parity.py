@@ -541,7 +541,9 @@ def test_channel_mix_scatter(L, m):
 
 # ------------------------------------------------------------------ GEMM K split
 
-# k / 3200 >= 2: a GEMM whose 256x256 tiles fill at most half the chip splits K.
+# A GEMM whose 256x256 tiles fill at most half the chip splits K into ranges
+# of at least 3200 codes (512 for m <= 256 when it fills at most an eighth of
+# the chip): k = 8192 splits at any m.
 SPLIT_K = 8192
 
 
@@ -566,6 +568,24 @@ def test_gemm_split_k(L, fmtspec, n, m):
     Yref = O.linear_fwd(X, ref["w_exact"])
     assert_close(bf16_bits_host(Ys), Yref, what=f"{fmt}{bits}g{group} split n={n} m={m}")
     assert_close(bf16_bits_host(Yu), Yref, what=f"{fmt}{bits}g{group} unsplit n={n} m={m}")
+
+
+@pytest.mark.parametrize("fmtspec", FORMATS, ids=FMT_IDS)
+@pytest.mark.parametrize("n,k,m", [(520, 2048, 130), (300, 1536, 65), (4096, 4096, 256)])
+def test_gemm_split_k_short_k(L, fmtspec, n, k, m):
+    """65 <= m <= 256: ranges down to 512 codes (3 and 4 of them here, 8 at
+    the 8B o shape), against the oracle, and equal run to run."""
+    fmt, bits, group, dq = fmtspec
+    W = SI.gaussian_weights(9670 + n, n, k, outlier_seed=9671)
+    X = SI.bf16_normal(9672 + m, (m, k))
+    qw, ref = _quant_pair(L, W, fmt, bits, group, dq)
+    assert L.lbq_linear_workspace_bytes(qw, m) > 0  # the split is on
+    Xd = to_dev_bf16(X)
+    Y = L.lbq_linear_fwd(Xd, qw)
+    Y2 = L.lbq_linear_fwd(Xd, qw)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16))
+    assert_close(bf16_bits_host(Y), O.linear_fwd(X, ref["w_exact"]), what=f"{fmt}{bits}g{group} n={n} k={k} m={m}")
 
 
 def test_gemm_split_k_channel_mix_scatter(L):

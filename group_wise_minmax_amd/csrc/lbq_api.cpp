@@ -772,7 +772,7 @@ const char* lbq_strerror(lbq_status s) {
     case LBQ_E_FORMAT: return "unknown or unsupported quantization format";
     case LBQ_E_ALIGN: return "pointer or leading dimension misaligned";
     case LBQ_E_WORKSPACE: return "workspace missing or too small";
-    case LBQ_E_UNSUPPORTED: return "request not supported by this build";
+    case LBQ_E_UNSUPPORTED: return "request not supported by this library";
     case LBQ_E_HIP: return "HIP runtime error";
   }
   return "unknown status";

@@ -58,7 +58,7 @@ typedef enum {
   LBQ_E_FORMAT = 3,      /* unknown format / bits / group / dq settings      */
   LBQ_E_ALIGN = 4,       /* a pointer or leading dimension is misaligned     */
   LBQ_E_WORKSPACE = 5,   /* workspace missing or smaller than required       */
-  LBQ_E_UNSUPPORTED = 6, /* valid request this build does not implement      */
+  LBQ_E_UNSUPPORTED = 6, /* valid request this library does not implement    */
   LBQ_E_HIP = 7          /* the HIP runtime reported an error                */
 } lbq_status;
 

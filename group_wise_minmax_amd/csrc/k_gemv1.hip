@@ -686,6 +686,40 @@ __global__ __launch_bounds__(kThreads) void k_gemvm_set(Gemv1Set set, const uint
                                  min(g0 + gpw, set.ngroups[pi]), gw < wlast, X, m, none, tab);
 }
 
+// Waves of set entries [lo, hi), whose wave ranges start at wave wbeg0.
+template <int KIND, int R, int CB, int D, int MV>
+__device__ __forceinline__ void gemvm_set_part(const Gemv1Set& set, int lo, int hi, int wbeg0, int gw,
+                                               const uint16_t* __restrict__ X, int m, const Nf4Table& tab,
+                                               int gpw) {
+  int pi = lo, wbeg = wbeg0, wlast = set.wave_end[lo];
+#pragma unroll
+  for (int i = 1; i < kGemvMaxGroup; ++i)
+    if (i > lo && i < hi) {
+      if (gw >= set.wave_end[i - 1]) { pi = i; wbeg = set.wave_end[i - 1]; }
+      wlast = set.wave_end[i];
+    }
+  const int g0 = (gw - wbeg) * gpw;
+  const LoraEpi none{nullptr, nullptr, 0, 0};
+  gemvm_body<KIND, R, CB, D, MV>(set.w[pi], set.y[pi], set.ldy[pi], set.out_rows[pi], g0,
+                                 min(g0 + gpw, set.ngroups[pi]), gw < wlast, X, m, none, tab);
+}
+
+// The INT4 g128 and INT2 g64 row sets of channel-mixed linears that share X
+// (2 <= m <= MV), in one launch: workgroups [0, wg_a) run set entries
+// [0, first_b) (INT4), the rest entries [first_b, count) (INT2), whose wave
+// ranges start at wave 4 * wg_a.  A workgroup stages x in its own format's
+// order, and each format keeps the plan of its own launch, so the outputs
+// are the bits of the two per-format launches.
+template <int R, int CB, int D, int MV>
+__global__ __launch_bounds__(kThreads) void k_gemvm_mix(Gemv1Set set, const uint16_t* __restrict__ X, int m,
+                                                       Nf4Table tab, int first_b, int wg_a, int gpw_a, int gpw_b) {
+  const int gw = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if ((int)blockIdx.x < wg_a)
+    gemvm_set_part<WK_I4G128, R, CB, D, MV>(set, 0, first_b, 0, gw, X, m, tab, gpw_a);
+  else
+    gemvm_set_part<WK_I2G64, R, CB, D, MV>(set, first_b, set.count, (kThreads / 64) * wg_a, gw, X, m, tab, gpw_b);
+}
+
 // Dynamic LDS per workgroup: the NF4 table, plus the arranged x and chunk sums
 // when x is staged.
 template <int KIND>
@@ -869,6 +903,28 @@ struct GemvmLauncher {
   }
 };
 
+// The mixed multi-row launch: each format planned as GemvmLauncher plans its
+// own launch (2 rows per group, 1 chunk per step, 2 steps in flight, 2 steps
+// per wave), INT4 waves first, rounded up to whole workgroups.
+template <int MV>
+hipError_t launch_gemvm_mix_mv(const WView* ws, uint16_t* const* ys, const int64_t* ldys,
+                               const int32_t* const* orows, int count_a, int count_b, const uint16_t* X, int64_t m,
+                               const Nf4Table& tab, hipStream_t s) {
+  Gemv1Set set{};
+  set.count = count_a + count_b;
+  int64_t wend_a = 0, wend_b = 0;
+  const int64_t gpw_a = plan_set<WK_I4G128, 2, 1>(ws, ys, orows, count_a, 2, 1024, set, 0, 0, &wend_a);
+  const int64_t wg_a = (wend_a + 3) / 4;
+  const int64_t gpw_b = plan_set<WK_I2G64, 2, 1>(ws + count_a, ys + count_a, orows + count_a, count_b, 2, 1024, set,
+                                                 count_a, 4 * wg_a, &wend_b);
+  for (int i = 0; i < set.count; ++i) set.ldy[i] = ldys[i];
+  const int64_t k = ws[0].k;
+  const size_t lds = std::max(lds_bytes_m<WK_I4G128, MV>(k), lds_bytes_m<WK_I2G64, MV>(k));
+  hipLaunchKernelGGL((k_gemvm_mix<2, 1, 2, MV>), dim3((unsigned)((wend_b + 3) / 4)), dim3(kThreads), lds, s, set, X,
+                     (int)m, tab, count_a, (int)wg_a, (int)gpw_a, (int)gpw_b);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool gemvm_fits(WKind kind, int64_t k, int64_t m) {
@@ -893,6 +949,16 @@ hipError_t launch_gemvm(WKind kind, const WView* ws, uint16_t* const* ys, const 
                         const LoraEpi& lora, const Nf4Table& tab, hipStream_t s) {
   if (count < 1 || count > kGemvMaxGroup || !gemvm_fits(kind, ws[0].k, m)) return hipErrorInvalidValue;
   return dispatch_kind<GemvmLauncher>(kind, ws, ys, ldys, out_rows, count, X, m, lora, tab, s);
+}
+
+hipError_t launch_gemvm_mix(const WView* ws, uint16_t* const* ys, const int64_t* ldys, const int32_t* const* out_rows,
+                            int count_a, int count_b, const uint16_t* X, int64_t m, const Nf4Table& tab,
+                            hipStream_t s) {
+  if (count_a < 1 || count_b < 1 || count_a + count_b > kGemvMaxGroup || !gemvm_fits(WK_I4G128, ws[0].k, m) ||
+      !gemvm_fits(WK_I2G64, ws[0].k, m))
+    return hipErrorInvalidValue;
+  if (m <= 2) return launch_gemvm_mix_mv<2>(ws, ys, ldys, out_rows, count_a, count_b, X, m, tab, s);
+  return launch_gemvm_mix_mv<4>(ws, ys, ldys, out_rows, count_a, count_b, X, m, tab, s);
 }
 
 hipError_t launch_gemv1_mix(const WView* ws, uint16_t* const* ys, const int32_t* const* out_rows, int count_a,

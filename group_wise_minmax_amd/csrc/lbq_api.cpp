@@ -369,7 +369,7 @@ lbq_status lbq_linear_fwd(const lbq_desc* desc, const lbq_qtensor* q, const uint
 // with both formats present and neither served by the multi-row GEMV (the
 // two row sets of channel-mixed linears that share X): one small-batch launch
 // for both formats.
-bool skinny_mix_set(int32_t count, const lbq_desc* descs, int64_t m) {
+static bool skinny_mix_set(int32_t count, const lbq_desc* descs, int64_t m) {
   if (m < 2 || m > lbq::kSkinnyMaxM) return false;
   int ca = 0, cb = 0;
   for (int32_t i = 0; i < count; ++i) {
@@ -382,6 +382,22 @@ bool skinny_mix_set(int32_t count, const lbq_desc* descs, int64_t m) {
   for (int32_t i = 0; i < count; ++i)
     if (use_gemvm(&descs[i], m)) return false;
   return true;
+}
+
+// A grouped call of INT4 g128 and INT2 g64 weights (both present) that all
+// take the multi-row GEMV (2 <= m <= 4, rows short enough): one multi-row
+// launch for both formats.
+static bool gemvm_mix_set(int32_t count, const lbq_desc* descs, int64_t m) {
+  if (m < 2 || m > lbq::kGemvmMaxM) return false;
+  int ca = 0, cb = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const lbq::WKind kd = kind_of(&descs[i]);
+    if (kd == lbq::WK_I4G128) ++ca;
+    else if (kd == lbq::WK_I2G64) ++cb;
+    else return false;
+    if (!use_gemvm(&descs[i], m)) return false;
+  }
+  return ca > 0 && cb > 0;
 }
 
 // Weights of one kind in a grouped call run as one launch (one launch pair
@@ -457,10 +473,11 @@ lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lb
   const lbq::LoraEpi none{nullptr, nullptr, 0, 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  if (m == 1 || skinny_mix_set(count, descs, m)) {
+  if (m == 1 || skinny_mix_set(count, descs, m) || gemvm_mix_set(count, descs, m)) {
     // The INT4 g128 and INT2 g64 row sets of channel-mixed linears (and
     // nothing else): one launch for both formats (m = 1: the GEMV; 2 <= m <=
-    // 64: the small-batch kernel and its reduce).
+    // 4 with rows the multi-row GEMV takes: that kernel; else up to m = 64
+    // the small-batch kernel and its reduce).
     lbq::WView ws[LBQ_MAX_GROUP];
     uint16_t* ys[LBQ_MAX_GROUP];
     int64_t lds[LBQ_MAX_GROUP];
@@ -479,6 +496,9 @@ lbq_status lbq_linear_fwd_grouped(int32_t count, const lbq_desc* descs, const lb
     if (ca > 0 && cb > 0 && ca + cb == count) {
       if (m == 1)
         return hip_status(lbq::launch_gemv1_mix(ws, ys, rows, ca, cb, X, nf4_table(), s), "lbq_linear_fwd_grouped");
+      if (gemvm_mix_set(count, descs, m))
+        return hip_status(lbq::launch_gemvm_mix(ws, ys, lds, rows, ca, cb, X, m, nf4_table(), s),
+                          "lbq_linear_fwd_grouped");
       return hip_status(lbq::launch_skinny_mix(ws, ys, lds, rows, ca, cb, X, m, static_cast<float*>(workspace),
                                                nf4_table(), s),
                         "lbq_linear_fwd_grouped");

@@ -87,6 +87,12 @@ bool gemvm_fits(WKind kind, int64_t k, int64_t m);
 hipError_t launch_gemvm(WKind kind, const WView* ws, uint16_t* const* ys, const int64_t* ldys,
                         const int32_t* const* out_rows, int count, const uint16_t* X, int64_t m,
                         const LoraEpi& lora, const Nf4Table& tab, hipStream_t s);
+// The INT4 g128 weights ws[0, count_a) and INT2 g64 weights ws[count_a,
+// count_a + count_b) (same k, both fitting the multi-row GEMV at m) in one
+// multi-row launch; outputs equal those of the two per-format launches.
+hipError_t launch_gemvm_mix(const WView* ws, uint16_t* const* ys, const int64_t* ldys, const int32_t* const* out_rows,
+                            int count_a, int count_b, const uint16_t* X, int64_t m, const Nf4Table& tab,
+                            hipStream_t s);
 // 2 <= m <= kSkinnyMaxM: MFMA with the weight streamed once; K split over
 // skinny_splits() workgroups whose fp32 partials (workspace) are summed by a
 // second kernel when more than one range is used or a LoRA term is added.

@@ -257,9 +257,11 @@ size_t lbq_linear_fwd_grouped_workspace_bytes(int32_t count, const lbq_desc* des
  * that sums its K-split partials.  For m > 64 a kind's GEMM may instead run
  * as two launches, a prefix of its weights and the rest, each with its own
  * tile shape, when that fills the chip's rounds of tiles better (q with
- * 256x256 tiles and k+v with 256x128 at m = 4096).  At m == 1 a set made of INT4 g128 and
- * INT2 g64 weights only (the channel-mixed layer's two row sets) runs as one
- * launch for both formats.  Each Ys[i] equals what lbq_linear_fwd
+ * 256x256 tiles and k+v with 256x128 at m = 4096).  For m <= 64 a set made
+ * of INT4 g128 and INT2 g64 weights only (the channel-mixed layer's two row
+ * sets) runs as one launch for both formats: the GEMV at m == 1, the
+ * multi-row GEMV at 2 <= m <= 4 when every weight takes it, else the
+ * small-batch kernel (and its reduce).  Each Ys[i] equals what lbq_linear_fwd
  * writes for weight i alone, bit for bit (given workspaces of the queried
  * sizes: each weight splits K as it does alone).  `workspace` takes
  * lbq_linear_fwd_grouped_workspace_bytes(count, descs, m) bytes (16-byte

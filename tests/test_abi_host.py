@@ -35,6 +35,20 @@ def test_library_exports_every_declared_symbol(L):
     assert "gfx950" in L.version()
 
 
+def test_library_exports_only_declared_symbols(L):
+    """Every C-linkage symbol the library defines is one include/lbq.h declares
+    (runtime-internal names start with an underscore)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm is not installed")
+    out = subprocess.run([nm, "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    names = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    extra = sorted(n for n in names if not n.startswith("_") and n not in set(declared_symbols()))
+    assert not extra, extra
+
+
 def test_nf4_codebook_matches_oracle(L):
     """The library builds its table itself (bisection on erfc); the oracle
     uses a different quantile routine.  After fp32 rounding they must agree."""

@@ -268,6 +268,31 @@ def test_forward_repeatable_bits(L):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+# Calls on different streams, each with its own workspace, share no state:
+# the forwards of two weights launched in turn on two streams (so that they
+# overlap) give the bits of the same calls run one after the other, for the
+# GEMV (m = 1), the multi-row GEMV (2), the small-batch kernel with split K
+# (16) and the GEMM with split K (300).
+@pytest.mark.parametrize("m", [1, 2, 16, 300])
+def test_forward_concurrent_streams(L, m):
+    n, k, reps = 1024, 8192, 12
+    qws = [L.lbq_quantize(to_dev_f32(SI.gaussian_weights(7600 + i, n, k)), "minmax", 4, 128) for i in range(2)]
+    X = to_dev_bf16(SI.bf16_normal(7610 + m, (m, k)))
+    ref = [L.lbq_linear_fwd(X, q).clone() for q in qws]
+    wss = [torch.empty(max(16, L.lbq_linear_workspace_bytes(q, m)), dtype=torch.uint8, device=DEV) for q in qws]
+    outs = [[torch.empty((m, n), dtype=torch.bfloat16, device=DEV) for _ in range(reps)] for _ in qws]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for r in range(reps):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                L.lbq_linear_fwd(X, qws[i], out=outs[i][r], workspace=wss[i])
+    torch.cuda.synchronize()
+    for i in range(2):
+        for r in range(reps):
+            assert torch.equal(outs[i][r].view(torch.int16), ref[i].view(torch.int16)), (i, r)
+
+
 # ------------------------------------------------------------------ backward
 
 
@@ -514,7 +539,7 @@ def test_lora_autograd_layer(L):
 # ------------------------------------------------------------------ mixed precision
 
 
-@pytest.mark.parametrize("m", [1, 3, 16, 130])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 16, 130])
 def test_channel_mix_scatter(L, m):
     """25% of the output channels in INT4 g128, 75% in INT2 g64, each a
     separate quantized tensor whose out_rows scatter into one Y."""
@@ -657,13 +682,13 @@ GROUP_SETS = {
 
 @pytest.mark.parametrize("name", list(GROUP_SETS))
 @pytest.mark.parametrize("k", [1280, 12288])
-@pytest.mark.parametrize("m", [1, 3, 16, 40, 57, 130, 300])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 16, 40, 57, 130, 300])
 def test_grouped_fwd_matches_single(L, name, k, m):
     """Weights sharing X in one call: each output equals the single-weight
     forward bit for bit (same kernels, same per-row order) and the oracle
     within the matmul tolerance.  Ragged n; at m = 1 same-kind weights share
-    one launch and the mixed set needs three, at every m: the GEMVs, the
-    small-batch kernel (each weight keeping its own K split, so the sums run
+    one launch and the mixed set needs three, at every m (the channel-mix set
+    one, up to m = 64): the GEMVs, the multi-row GEMV, the small-batch kernel (each weight keeping its own K split, so the sums run
     in the same order) and the GEMM, which lays the weights' column tiles
     side by side."""
     specs = GROUP_SETS[name]

@@ -283,6 +283,52 @@ def test_70b_channel_mix_small_batch_one_launch(grp):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("grp", [("q", "k", "v"), ("o",), ("down",)], ids=["qkv", "o", "down"])
+def test_8b_channel_mix_multirow_one_launch(grp):
+    """Channel-mixed 8B-shaped linears (25% INT4 g128 / 75% INT2 g64 rows) that
+    share X, at m = 2 and 4 where every row set takes the multi-row GEMV (down,
+    k = 14336, only at m = 2): both formats of every linear in one grouped call
+    -- one mixed multi-row launch -- equal the per-format calls bit for bit,
+    and sampled columns meet the oracle's tolerance."""
+    parts, refs = [], []
+    for nm in grp:
+        li = NAMES.index(nm)
+        n, k = SI.LLAMA3_8B[nm]
+        W = SI.dev_gaussian_weights(SI.seed_of(5, li, SI.SLOT_W), n, k, DEV)
+        rows4 = SI.dev_channel_mask(SI.seed_of(5, li, SI.SLOT_CHMASK), n, DEV)
+        mask = torch.zeros(n, dtype=torch.bool, device=DEV)
+        mask[rows4.long()] = True
+        rows2 = torch.nonzero(~mask).flatten().to(torch.int32)
+        a = L.lbq_quantize(W[rows4.long()].contiguous(), "minmax", 4, 128)
+        b = L.lbq_quantize(W[rows2.long()].contiguous(), "minmax", 2, 64)
+        a.out_rows, b.out_rows = rows4, rows2
+        cols = sample(n, 48, 8300 + li)
+        is4 = host(mask)[cols]
+        Wc = rows_host(W, cols)
+        w_ref = np.empty((len(cols), k), dtype=np.float64)
+        if is4.any():
+            w_ref[is4] = O.quantize(Wc[is4], "minmax", bits=4, group=128)["w_exact"]
+        w_ref[~is4] = O.quantize(Wc[~is4], "minmax", bits=2, group=64)["w_exact"]
+        del W
+        parts.append((nm, n, a, b))
+        refs.append((cols, w_ref))
+    k = parts[0][2].k
+    for m in ((2,) if k > 8192 else (2, 4)):
+        X = SI.dev_bf16_normal(SI.seed_of(5, NAMES.index(grp[0]), SI.SLOT_X) + 400 + m, (m, k), DEV)
+        Yg = [torch.zeros((m, n), dtype=torch.bfloat16, device=DEV) for _, n, _, _ in parts]
+        L.lbq_linear_fwd_grouped(X, [q for _, _, a, b in parts for q in (a, b)], outs=[y for y in Yg for _ in range(2)])
+        Xh = bf16_bits_host(X)
+        for (nm, n, a, b), y, (cols, w_ref) in zip(parts, Yg, refs):
+            Ys = torch.zeros((m, n), dtype=torch.bfloat16, device=DEV)
+            L.lbq_linear_fwd(X, a, out=Ys)
+            L.lbq_linear_fwd(X, b, out=Ys)
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), Ys.view(torch.int16)), f"8b {nm} m={m}: one launch != per format"
+            Yh = bf16_bits_host(y[:, torch.from_numpy(cols).to(DEV)])
+            assert_close(Yh, O.linear_fwd(Xh, w_ref), what=f"8b {nm} chmix m={m}")
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("bits,group", [(4, 128), (2, 64)], ids=["int4", "int2"])
 @pytest.mark.parametrize("li", range(7), ids=NAMES70)
 def test_70b_layer_mix_layer(li, bits, group):

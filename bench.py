@@ -326,11 +326,13 @@ def gemm_splits(n, k, m) -> int:
     return (k + per - 1) // per
 
 
-def gemm_set_launches(ns, k, m) -> int:
+def gemm_set_launches(ns, k, m, cuttable=True) -> int:
     """Launches of one weight kind's GEMM (m > 64) over weights of ns rows:
     the library's rule (k_gemm_fwd.hip) splits a set in two when two tile
-    shapes fill the chip's rounds better by over 5%, and a launch in which a
-    weight splits K adds the reduce of its partials."""
+    shapes fill the chip's rounds better by over 5% (between weights, or,
+    when no weight splits K, inside the weight where whole rounds of 256x256
+    tiles end; not for the offset kind), and a launch in which a weight
+    splits K adds the reduce of its partials."""
     def cost(ns_):
         ks = [gemm_splits(n, k, m) for n in ns_]
         t0 = sum((n + 255) // 256 * ((m + 255) // 256) * s for n, s in zip(ns_, ks))
@@ -345,6 +347,21 @@ def gemm_set_launches(ns, k, m) -> int:
         c = cost(ns[:j]) + cost(ns[j:])
         if c < best_cost:
             best, best_cost = j, c
+    if cuttable and not any(gemm_splits(n, k, m) > 1 for n in ns):
+        ny = (m + 255) // 256
+        t0 = sum((n + 255) // 256 * ny for n in ns)
+        if t0 > 256 and t0 % 256:
+            left = (t0 // 256) * 256 // ny
+            for jw, n in enumerate(ns):
+                if left < (n + 255) // 256:
+                    break
+                left -= (n + 255) // 256
+            else:
+                jw = len(ns)
+            if jw < len(ns) and left > 0:
+                r = 256 * left
+                if cost(ns[:jw] + [r]) + cost([ns[jw] - r] + ns[jw + 1:]) < best_cost:
+                    return 2
     return launches(ns) if best == 0 else launches(ns[:best]) + launches(ns[best:])
 
 
@@ -369,7 +386,7 @@ def grouped_launches(L, qws, m) -> int:
         if m <= 64:
             n += 1 + (1 if L.lbq_linear_fwd_grouped_workspace_bytes(sub, m) > 0 else 0)
         else:
-            n += gemm_set_launches([q.n for q in sub], sub[0].k, m)
+            n += gemm_set_launches([q.n for q in sub], sub[0].k, m, cuttable=key[3] != 2)
     return n
 
 

@@ -788,6 +788,73 @@ hipError_t launch_set_tiles(const WView* ws, uint16_t* const* ys, const int64_t*
   }
 }
 
+// Rows [r0, r1) of a weight as a weight of its own (r0 a multiple of 256):
+// every buffer starts r0 rows further on.  Not for the offset kind, whose
+// offset entry is found from the weight's own row count.
+template <int KIND>
+WView row_view(const WView& w, int64_t r0, int64_t r1) {
+  using T = WKindTraits<KIND>;
+  static_assert(!T::dqo, "row views of the offset kind");
+  WView v = w;
+  v.n = r1 - r0;
+  v.packed = w.packed + r0 * (w.k * T::bits / 8);
+  if constexpr (T::fmt == FMT_MINMAX) {
+    const int64_t g = r0 * (w.k / T::group);  // metadata entries before row r0 (a multiple of 4)
+    v.scales = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(w.scales) + (T::compact ? 2 : 4) * g);
+    v.zeros = w.zeros + (T::compact ? g * T::bits / 8 : g);
+  } else {
+    const int64_t b = r0 * (w.k / 64);  // absmax blocks before row r0 (a multiple of 256)
+    if constexpr (T::dq) {
+      v.absmax_q = w.absmax_q + b;
+      v.absmax_scale = w.absmax_scale + b / 256;
+    } else {
+      v.absmax = w.absmax + b;
+    }
+  }
+  return v;
+}
+
+// A set whose 256x256 tiles leave the last round partly empty can also be cut
+// inside a weight, at the n-tile where whole rounds end: the prefix runs full
+// rounds of 256x256 tiles, the rest its own launch with the shape that fills
+// the chip best (8B gate + up at m = 2048: 896 tiles = 3 rounds + 128 tiles).
+// Only sets that split K nowhere: every output is then the same sum as in the
+// single-weight call, whatever the tile shape.  Returns false when the cut
+// does not save over the best of one launch or a cut between weights.
+template <int KIND>
+bool row_cut(const WView* ws, int count, int64_t m, float* part, int j_weights, WView* wa, int& na, WView* wb,
+             int& nb, int& jw, int64_t& r) {
+  if constexpr (WKindTraits<KIND>::dqo) {
+    return false;
+  } else {
+    int64_t t0 = 0;
+    for (int i = 0; i < count; ++i) {
+      if (part != nullptr && gemm_splits(ws[i].n, ws[i].k, m) > 1) return false;
+      t0 += tiles_of<256, 256>(ws[i].n, m);
+    }
+    const int64_t ny = (m + 255) / 256;
+    if (t0 <= 256 || t0 % 256 == 0) return false;
+    int64_t left = (t0 / 256) * 256 / ny;  // n-tiles of the prefix
+    for (jw = 0; jw < count; ++jw) {
+      const int64_t nt = (ws[jw].n + 255) / 256;
+      if (left < nt) break;
+      left -= nt;
+    }
+    if (jw == count || left == 0) return false;  // the cut falls between weights
+    r = left * 256;
+    na = nb = 0;
+    for (int i = 0; i < jw; ++i) wa[na++] = ws[i];
+    wa[na++] = row_view<KIND>(ws[jw], 0, r);
+    wb[nb++] = row_view<KIND>(ws[jw], r, ws[jw].n);
+    for (int i = jw + 1; i < count; ++i) wb[nb++] = ws[i];
+    const double cut = launch_cost(wa, na, m, false) + launch_cost(wb, nb, m, false);
+    const double best = j_weights == 0 ? 0.95 * launch_cost(ws, count, m, false)
+                                       : launch_cost(ws, j_weights, m, false) +
+                                             launch_cost(ws + j_weights, count - j_weights, m, false);
+    return cut < best;
+  }
+}
+
 // The two launches of a divided set run one after the other on the stream
 // and reuse the same partial area.
 template <int KIND>
@@ -795,6 +862,26 @@ struct GemmFwdSetLauncher {
   static hipError_t run(const WView* ws, uint16_t* const* ys, const int64_t* ldys, const int32_t* const* orows,
                         int count, const uint16_t* X, int64_t m, float* part, const Nf4Table& tab, hipStream_t s) {
     const int j = split_point(ws, count, m, part != nullptr);
+    {
+      WView wa[kGemvMaxGroup], wb[kGemvMaxGroup];
+      int na = 0, nb = 0, jw = 0;
+      int64_t r = 0;
+      if (row_cut<KIND>(ws, count, m, part, j, wa, na, wb, nb, jw, r)) {
+        // outputs of the cut weight: its columns from r on (or its out_rows from r on)
+        uint16_t* yb[kGemvMaxGroup];
+        int64_t lb[kGemvMaxGroup];
+        const int32_t* ob[kGemvMaxGroup];
+        for (int i = jw; i < count; ++i) {
+          const bool cut = i == jw;
+          yb[i - jw] = cut && orows[i] == nullptr ? ys[i] + r : ys[i];
+          ob[i - jw] = cut && orows[i] != nullptr ? orows[i] + r : orows[i];
+          lb[i - jw] = ldys[i];
+        }
+        const hipError_t e = launch_set_tiles<KIND>(wa, ys, ldys, orows, na, X, m, nullptr, tab, s);
+        if (e != hipSuccess) return e;
+        return launch_set_tiles<KIND>(wb, yb, lb, ob, nb, X, m, nullptr, tab, s);
+      }
+    }
     if (j == 0) return launch_set_tiles<KIND>(ws, ys, ldys, orows, count, X, m, part, tab, s);
     const hipError_t e = launch_set_tiles<KIND>(ws, ys, ldys, orows, j, X, m, part, tab, s);
     if (e != hipSuccess) return e;

@@ -766,6 +766,44 @@ def test_grouped_gemm_two_launch_split(L, fid):
         assert_close(bf16_bits_host(Y)[rows], O.linear_fwd(X[rows], ref["w_exact"]), what=f"{fid} weight {i}")
 
 
+@pytest.mark.parametrize("fid", FMT_IDS)
+def test_grouped_gemm_row_cut(L, fid):
+    """Two 2560-row weights at ragged m = 4000 have 320 tiles of 256x256 (one
+    round and a quarter), so the set runs as two launches cut inside the
+    second weight at row 1536: the first launch fills one round of 256x256
+    tiles, the second (its last 1024 rows) takes its own tile shape.  Each
+    output equals the single-weight forward bit for bit, and 48 sampled rows
+    match the oracle.  With out_rows on the cut weight, its rows scatter into
+    a wider Y exactly as the single-weight call scatters them."""
+    fmt, bits, group, dq = FORMATS[FMT_IDS.index(fid)]
+    m, k, n = 4000, 256, 2560
+    rows = np.sort(np.random.default_rng(9470).choice(m, 48, replace=False))
+    X = SI.bf16_normal(9471, (m, k))
+    qws, refs = [], []
+    for i in range(2):
+        qw, ref = _quant_pair(L, SI.gaussian_weights(9472 + i, n, k, outlier_seed=9474 + i), fmt, bits, group, dq)
+        qws.append(qw)
+        refs.append(ref)
+    Xd = to_dev_bf16(X)
+    Ys = L.lbq_linear_fwd_grouped(Xd, qws)
+    singles = [L.lbq_linear_fwd(Xd, q) for q in qws]
+    torch.cuda.synchronize()
+    for i, (Y, Y1, ref) in enumerate(zip(Ys, singles, refs)):
+        assert np.array_equal(bf16_bits_host(Y), bf16_bits_host(Y1)), f"{fid} weight {i}: grouped != single"
+        assert_close(bf16_bits_host(Y)[rows], O.linear_fwd(X[rows], ref["w_exact"]), what=f"{fid} weight {i}")
+    cols = np.random.default_rng(9476).permutation(n + 64)[:n].astype(np.int32)
+    qws[1].out_rows = torch.from_numpy(cols).to(DEV)
+    Yg = torch.zeros((m, n + 64), dtype=torch.bfloat16, device=DEV)
+    Y1 = torch.zeros((m, n + 64), dtype=torch.bfloat16, device=DEV)
+    L.lbq_linear_fwd_grouped(Xd, qws, outs=[None, Yg])
+    L.lbq_linear_fwd(Xd, qws[1], out=Y1)
+    torch.cuda.synchronize()
+    yg = bf16_bits_host(Yg)
+    assert np.array_equal(yg, bf16_bits_host(Y1)), f"{fid}: scattered grouped != single"
+    assert np.array_equal(yg[:, cols], bf16_bits_host(Ys[1])), f"{fid}: scattered columns"
+    assert not np.any(np.delete(yg, cols, axis=1)), f"{fid}: columns outside out_rows written"
+
+
 @pytest.mark.parametrize("fid", ["i4g64", "i4g128", "i2g64", "nf4", "nf4dq"])
 def test_metadata_at_minimum_alignment(L, fid):
     """Metadata arrays that start one element past an aligned address (floats

@@ -201,6 +201,31 @@ def test_variant_grouped_equals_single(L, variant, m):
                  what=f"{variant} grouped bwd m={m}")
 
 
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_variant_grouped_row_cut(L, variant):
+    """Two 2560-row weights at m = 4000: 320 tiles of 256x256, so a set of a
+    compact kind runs as two launches cut inside the second weight at row
+    1536 (the fp16 scales and packed zero points read from that row on).  The
+    offset kind is never cut (its offset entry is found from the weight's row
+    count).  Either way each grouped output equals the single-weight call bit
+    for bit, and 32 sampled rows match the oracle."""
+    m, k, n = 4000, 256, 2560
+    rows = np.sort(np.random.default_rng(8680).choice(m, 32, replace=False))
+    Xh = SI.bf16_normal(8681, (m, k))
+    qws, refs = [], []
+    for i in range(2):
+        W = SI.gaussian_weights(8682 + i, n, k, outlier_seed=8684 + i)
+        qws.append(quant(L, W, variant))
+        refs.append(O.quantize_variant(W, variant))
+    X = to_dev_bf16(Xh)
+    Ys = L.lbq_linear_fwd_grouped(X, qws)
+    singles = [L.lbq_linear_fwd(X, q) for q in qws]
+    torch.cuda.synchronize()
+    for i, (Yg, Y1, ref) in enumerate(zip(Ys, singles, refs)):
+        assert torch.equal(Yg.view(torch.int16), Y1.view(torch.int16)), f"{variant} weight {i}"
+        assert_close(bf16_bits_host(Yg)[rows], O.linear_fwd(Xh[rows], ref["w_exact"]), what=f"{variant} weight {i}")
+
+
 @pytest.mark.parametrize("m", [1, 16, 130])
 def test_nf4dqo_lora_fwd_bwd(L, m):
     n, k, r = 512, 1024, 16

@@ -164,6 +164,7 @@ def write_traffic(fetch_csv: str, write_csv: str, commands=()) -> dict:
 
 SIMDS = 256 * 4                 # MI355X: 256 CUs x 4 SIMDs
 SCLK_HZ = 2.4e9                 # MI355X peak engine clock
+XCDS = 8                        # MI355X: GRBM_COUNT sums one clock counter per XCD
 
 
 def _short_kernel(name: str) -> str:
@@ -181,6 +182,12 @@ def counter_summary(csvs, out_md: str, commands=(), match: str = "lbq::") -> Non
       wait, issue, valu, lds, vmem
                   SQ_WAIT_ANY, SQ_WAIT_INST_ANY, SQ_ACTIVE_INST_VALU,
                   SQ_ACTIVE_INST_LDS, SQ_ACTIVE_INST_VMEM / SQ_WAVE_CYCLES
+      clock       GRBM_COUNT / 8 XCDs / duration: the engine clock while the
+                  kernel ran, for dispatches of at least 500 us (an upper
+                  bound: the counter window also covers some dispatch set-up,
+                  which shorter kernels cannot absorb)
+      busy@clk    SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_COUNT / 8):
+                  MFMA busy against the cycles the clock actually ran
     Durations are the counter run's own (dispatches serialised)."""
     import csv
     import numpy as np
@@ -205,9 +212,13 @@ def counter_summary(csvs, out_md: str, commands=(), match: str = "lbq::") -> Non
               "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x duration x 2.4 GHz); VALU/MFMA = (SQ_INSTS_VALU - "
               "SQ_INSTS_MFMA) / SQ_INSTS_MFMA; LDS conf = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; wait / issue / "
               "valu / lds / vmem = SQ_WAIT_ANY / SQ_WAIT_INST_ANY / SQ_ACTIVE_INST_VALU / SQ_ACTIVE_INST_LDS / "
-              "SQ_ACTIVE_INST_VMEM over SQ_WAVE_CYCLES.  Durations (us) are the counter runs' own.", "",
-              "| kernel | workgroups | n | us | TF/s | MFMA busy | VALU/MFMA | LDS conf | wait | issue | valu | lds | vmem |",
-              "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+              "SQ_ACTIVE_INST_VMEM over SQ_WAVE_CYCLES; clock = GRBM_COUNT / 8 XCDs / duration (GHz; dispatches of "
+              "at least 500 us only, and an upper bound: the counter window also covers dispatch set-up); "
+              "busy@clk = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_COUNT / 8).  Durations (us) are the "
+              "counter runs' own.", "",
+              "| kernel | workgroups | n | us | TF/s | MFMA busy | VALU/MFMA | LDS conf | wait | issue | valu | lds | vmem "
+              "| clock | busy@clk |",
+              "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
 
     def m(d, c):
         return float(np.mean(d[c])) if c in d else None
@@ -228,8 +239,12 @@ def counter_summary(csvs, out_md: str, commands=(), match: str = "lbq::") -> Non
         mb = busy / (SIMDS * dur * SCLK_HZ) if busy is not None else None
         vpm = (valu - mf) / mf if valu is not None and mf else None
         lc = conf / act if conf is not None and act else None
+        grbm = m(d, "GRBM_COUNT")
+        long_run = dur >= 500e-6  # the set-up in the window is then at most a few per cent
+        clk = grbm / XCDS / dur / 1e9 if grbm and long_run else None
+        mbc = busy / (SIMDS * grbm / XCDS) if grbm and long_run and busy is not None else None
         lines.append(f"| `{key[0]}` | {key[1]} | {len(d['dur'])} | {dur * 1e6:.1f} | {fmt(tf, 0)} | {fmt(mb)} | {fmt(vpm, 2)} | "
-                     f"{fmt(lc)} | " + " | ".join(fmt(share[c]) for c in share) + " |")
+                     f"{fmt(lc)} | " + " | ".join(fmt(share[c]) for c in share) + f" | {fmt(clk, 2)} | {fmt(mbc)} |")
         raw[f"{key[0]} [{key[1]}]"] = {c: round(float(np.mean(v)), 1) for c, v in d.items() if c != "dur"}
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n\nMean counter values per dispatch:\n\n```json\n" + json.dumps(raw, indent=1) + "\n```\n")

@@ -793,15 +793,17 @@ struct Gemv1Launcher {
     // launch together).  4-bit MinMax reads x from global memory and takes 2
     // chunks (32 B) of each row per step: 1 row per wave with 2 steps in
     // flight under 2048 rows in all (more waves), 2 rows with 2 steps up to
-    // 8192 rows of length <= 8192, else 2 rows with 1 step.  2-bit MinMax
-    // (128 B of x per chunk) and NF4 stage x in LDS: 2 chunks per step with 2
-    // steps in flight, or, for 2-bit rows longer than 8192, 1 chunk with 4.
-    // Rows whose staged x would not fit 64 KiB read x from global memory;
-    // 2-bit ones then take 4 rows per wave, so each 128 B of x a lane loads
-    // serves 64 B of weights (Qwen-shaped down, k = 49152: 2 rows per wave
-    // made the Qwen decode layer 9-11% slower).  The rows per wave, chunks
-    // per step and steps in flight never change a row's sum: every lane adds
-    // its chunks c, c + 64, ... in the same order.
+    // 8192 rows of length <= 8192, else 2 rows with 1 step.  NF4 stages x in
+    // LDS, 2 chunks per step with 2 steps in flight.  2-bit MinMax (128 B of x
+    // per 16-byte chunk) takes 4 rows per wave with 1 chunk per step and 1
+    // step in flight, so each x read serves four rows of weights: x staged in
+    // LDS (70B-shaped all-INT2 layer 7% faster than 2 rows with 2 chunks and
+    // 2 steps, or, over 8192, 1 chunk and 4 steps; the compact layer 8%, the
+    // Qwen-shaped layer 10%), or read from global memory when the staged copy
+    // would not fit 64 KiB (Qwen-shaped down, k = 49152: the Qwen decode layer
+    // 9-11% faster than with 2 rows).  The rows per wave, chunks per step and
+    // steps in flight never change a row's sum: every lane adds its chunks
+    // c, c + 64, ... in the same order.
     const bool fits = lds_bytes<KIND>(k, false) <= 65536;
     int64_t rows = 0;
     for (int i = 0; i < count; ++i) rows += ws[i].n;
@@ -811,8 +813,7 @@ struct Gemv1Launcher {
       return launch_set<KIND, 2, 2, 1, true>(ws, ys, orows, count, X, lora, tab, s, 1);
     } else if constexpr (T::fmt == FMT_MINMAX) {
       if (!fits) return launch_set<KIND, 4, 1, 1, true>(ws, ys, orows, count, X, lora, tab, s, 2);
-      if (k <= 8192) return launch_set<KIND, 2, 2, 2, false>(ws, ys, orows, count, X, lora, tab, s, 1);
-      return launch_set<KIND, 2, 1, 4, false>(ws, ys, orows, count, X, lora, tab, s, 2);
+      return launch_set<KIND, 4, 1, 1, false>(ws, ys, orows, count, X, lora, tab, s, k <= 8192 ? 1 : 2);
     } else {
       if (fits) return launch_set<KIND, 2, 2, 2, false>(ws, ys, orows, count, X, lora, tab, s, 4);
       return launch_set<KIND, 2, 2, 1, true>(ws, ys, orows, count, X, lora, tab, s, 4);
@@ -847,8 +848,7 @@ hipError_t launch_mix_b(const WView* ws, uint16_t* const* ys, const int32_t* con
   const int64_t k = ws[0].k;
   if (lds_bytes<WK_I2G64>(k, false) > 65536)
     return launch_mix_cfg<CA, G1Cfg<4, 1, 1, true>>(ws, ys, orows, count_a, count_b, X, tab, s, 1, 2);
-  if (k <= 8192) return launch_mix_cfg<CA, G1Cfg<2, 2, 2, false>>(ws, ys, orows, count_a, count_b, X, tab, s, 1, 1);
-  return launch_mix_cfg<CA, G1Cfg<2, 1, 4, false>>(ws, ys, orows, count_a, count_b, X, tab, s, 1, 2);
+  return launch_mix_cfg<CA, G1Cfg<4, 1, 1, false>>(ws, ys, orows, count_a, count_b, X, tab, s, 1, k <= 8192 ? 1 : 2);
 }
 
 template <int KIND, int MV>

@@ -257,7 +257,10 @@ size_t lbq_linear_fwd_grouped_workspace_bytes(int32_t count, const lbq_desc* des
  * that sums its K-split partials.  For m > 64 a kind's GEMM may instead run
  * as two launches, a prefix of its weights and the rest, each with its own
  * tile shape, when that fills the chip's rounds of tiles better (q with
- * 256x256 tiles and k+v with 256x128 at m = 4096).  For m <= 64 a set made
+ * 256x256 tiles and k+v with 256x128 at m = 4096); when no weight of the
+ * kind splits K, the two launches may also divide one weight at a multiple
+ * of 256 rows (gate + up at m = 2048: the rows that fill three whole rounds
+ * of 256x256 tiles, then the rest).  For m <= 64 a set made
  * of INT4 g128 and INT2 g64 weights only (the channel-mixed layer's two row
  * sets) runs as one launch for both formats: the GEMV at m == 1, the
  * multi-row GEMV at 2 <= m <= 4 when every weight takes it, else the

@@ -336,20 +336,22 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(BwdSet set, int m, uin
     // Two phases per stage, with a barrier between them: the first four waves
     // stage the next tile while the last four run their MFMAs, then the other
     // way round.  Waves w and w + 4 share a SIMD, so at any time one of them
-    // feeds the matrix core (at raised priority) while the other does the
-    // dequant and LDS writes.
+    // feeds the matrix core while the other does the dequant and LDS writes.
+    // The staging wave runs at raised priority: its loads, table reads and
+    // conversions are a chain of short instructions that would otherwise wait
+    // behind the MFMA wave's issue slots, while the MFMAs queue up anyway
+    // (8B NF4+DQ layer at m = 4096, against raising the MFMA wave: forward
+    // +0.8-1.5%, input gradient +1%).
     const bool late = wave >= 4;
     auto stage = [&](int64_t t) {
+      __builtin_amdgcn_s_setprio(1);
       if (t + BNR < N) {
         store_stage(buf ^ 1);
         if (t + 2 * BNR < N) load_stage(t + 2 * BNR);
       }
-    };
-    auto mfma_phase = [&]() {
-      __builtin_amdgcn_s_setprio(1);
-      compute(buf);
       __builtin_amdgcn_s_setprio(0);
     };
+    auto mfma_phase = [&]() { compute(buf); };
     for (int64_t nt = 0; nt < N; nt += BNR) {
       if (nt + 2 * BNR < N) bind_for(nt + 2 * BNR);  // both wave groups load this stage
       if (late) mfma_phase();

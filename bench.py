@@ -578,8 +578,9 @@ def build_workload(L, SI, torch, dev, R, want):
                                             "units": units(qn, X4k, Y4k, per_linear=True)}),
             ("lora_m4096", p_lora, {"bound": "mfma", "flop": sum(2 * 4096 * N_of[nm] * K_of[nm] + 2 * 4096 * 16 * (K_of[nm] + N_of[nm])
                                                                  for nm in lora), "launches": lora_launches}),
-            ("bwd_m4096", p_bwd, {"bound": "mfma", "flop": flop(4096), "launches": 7}),
-            ("bwd_m4096_grouped", p_bwd_grouped, {"bound": "mfma", "flop": flop(4096), "launches": len(GROUPS)}),
+            # down's input gradient (k = 14336: 3.5 rounds of 256x256 tiles) runs as two launches
+            ("bwd_m4096", p_bwd, {"bound": "mfma", "flop": flop(4096), "launches": 8}),
+            ("bwd_m4096_grouped", p_bwd_grouped, {"bound": "mfma", "flop": flop(4096), "launches": len(GROUPS) + 1}),
             # dX = dY W + G A, G = dY B, T = X A^T, dA = G^T X, dB = (T^T dY)^T: 6 launches per adapted linear
             ("lora_bwd_m4096", p_lora_bwd, {"bound": "mfma", "flop": sum(2 * 4096 * N_of[nm] * K_of[nm] +
                                                                          2 * 4096 * 16 * (2 * N_of[nm] + 3 * K_of[nm])

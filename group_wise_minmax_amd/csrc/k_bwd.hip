@@ -75,6 +75,7 @@ struct BwdSet {
   const uint16_t* dy[kGemvMaxGroup];
   int stage_end[kGemvMaxGroup];
   int count;
+  int k_begin, k_cols;  // the launch's columns of dX: [k_begin, k_begin + k_cols)
 };
 
 // SET: the set may hold several weights (the weight of the stage about to be
@@ -102,10 +103,10 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(BwdSet set, int m, uin
   const int wk = wave % WGK, wm = wave / WGK;
   const int li = lane & 15, lg = lane >> 4;
   const int64_t K = set.w[0].k;
-  const int nx = (int)((K + BKO - 1) / BKO), ny = (m + BM - 1) / BM;
+  const int nx = (set.k_cols + BKO - 1) / BKO, ny = (m + BM - 1) / BM;
   int tx, ty;
   tile_of(blockIdx.x, nx, ny, tx, ty);
-  const int64_t k0 = (int64_t)tx * BKO;
+  const int64_t k0 = set.k_begin + (int64_t)tx * BKO;
   const int64_t m0 = (int64_t)ty * BM;
   // the reduction: 64-row stages over all weights of the set
   int nstage = set.stage_end[0];
@@ -429,8 +430,7 @@ __global__ __launch_bounds__(WGK* WGM * 64) void k_bwd_dx(BwdSet set, int m, uin
 template <int KIND, int BKO, int BM, int WGK, int WGM>
 hipError_t launch_bwd_cfg(const BwdSet& set, int64_t m, uint16_t* dX, const LoraDx& lora, const Nf4Table& tab,
                           hipStream_t s) {
-  const int64_t k = set.w[0].k;
-  const int64_t tiles = ((k + BKO - 1) / BKO) * ((m + BM - 1) / BM);
+  const int64_t tiles = ((set.k_cols + BKO - 1) / BKO) * ((m + BM - 1) / BM);
   if (lora.g != nullptr) {  // LoRA: single weights only
     hipLaunchKernelGGL((k_bwd_dx<KIND, BKO, BM, WGK, WGM, true, false>), dim3((unsigned)tiles),
                        dim3(WGK * WGM * 64), 0, s, set, (int)m, dX, lora, tab);
@@ -454,9 +454,26 @@ struct BwdLauncher {
   static hipError_t run(const BwdSet& set, int64_t m, uint16_t* dX, const LoraDx& lora, const Nf4Table& tab,
                         hipStream_t s) {
     // 256 x 256 tiles (8 waves of 128 x 64) unless they leave most of the chip idle.
-    const int64_t k = set.w[0].k;
+    const int64_t k = set.k_cols;
     const int64_t t256 = ((k + 255) / 256) * ((m + 255) / 256);
     const int64_t t128 = ((k + 127) / 128) * ((m + 127) / 128);
+    // Several rounds of 256 x 256 tiles with a partly empty last one: the
+    // columns that fill whole rounds in one launch, the rest in a second one
+    // on 128 x 128 tiles (8B down at m = 4096: 896 tiles = 3.5 rounds become
+    // 768 tiles and 512 small ones; the layer's input gradient +1-1.5%).
+    // Each output's sum runs over n in the same order whatever the tile, so
+    // the cut changes no bit.
+    const int64_t ny = (m + 255) / 256;
+    const int64_t kc = (t256 / 256) * 256 / ny * 256;  // columns of the whole rounds
+    if (t256 > 256 && t256 % 256 != 0 && kc > 0 && kc < k) {
+      BwdSet a = set, b = set;
+      a.k_cols = (int)kc;
+      b.k_begin = set.k_begin + (int)kc;
+      b.k_cols = (int)(k - kc);
+      const hipError_t e = launch_bwd_cfg<KIND, 256, 256, 2, 4>(a, m, dX, lora, tab, s);
+      if (e != hipSuccess) return e;
+      return launch_bwd_cfg<KIND, 128, 128, 2, 2>(b, m, dX, lora, tab, s);
+    }
     if (bwd_fill(t256) >= 0.5 * bwd_fill(t128)) return launch_bwd_cfg<KIND, 256, 256, 2, 4>(set, m, dX, lora, tab, s);
     return launch_bwd_cfg<KIND, 128, 128, 2, 2>(set, m, dX, lora, tab, s);
   }
@@ -472,6 +489,8 @@ BwdSet make_bwd_set(const WView* ws, const uint16_t* const* dys, int count) {
     end += (int)((ws[i].n + BNR - 1) / BNR);
     set.stage_end[i] = end;
   }
+  set.k_begin = 0;
+  set.k_cols = (int)ws[0].k;
   return set;
 }
 

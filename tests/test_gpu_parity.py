@@ -379,6 +379,30 @@ def test_bwd_dx_grouped_ragged_and_single(L, fid):
     assert np.array_equal(bf16_bits_host(one), bf16_bits_host(single))
 
 
+@pytest.mark.parametrize("fid", ["i4g128", "i2g64", "i4g64"])
+def test_bwd_dx_column_cut(L, fid):
+    """An input gradient whose 256x256 tiles leave the last round partly
+    empty (k = 4608 at m = 4000: 18 x 16 = 288 tiles) runs as two launches,
+    columns [0, 4096) on 256x256 tiles and the rest on 128x128 tiles.  The
+    same weight without its first 512 columns (k = 4096: one round of
+    256x256 tiles) must give the same bits for the shared columns, and 48
+    sampled rows match the oracle."""
+    fmt, bits, group, dq = FORMATS[FMT_IDS.index(fid)]
+    m, n, k = 4000, 256, 4608
+    rows = np.sort(np.random.default_rng(9490).choice(m, 48, replace=False))
+    W = SI.gaussian_weights(9491, n, k, outlier_seed=9492)
+    dY = SI.bf16_normal(9493, (m, n))
+    qw, ref = _quant_pair(L, W, fmt, bits, group, dq)
+    qw2, _ = _quant_pair(L, np.ascontiguousarray(W[:, 512:]), fmt, bits, group, dq)
+    dYd = to_dev_bf16(dY)
+    dX = L.lbq_linear_bwd_dx(dYd, qw)
+    dX2 = L.lbq_linear_bwd_dx(dYd, qw2)
+    torch.cuda.synchronize()
+    got = bf16_bits_host(dX)
+    assert np.array_equal(got[:, 512:], bf16_bits_host(dX2)), f"{fid}: the cut changed bits"
+    assert_close(got[rows], O.linear_bwd_dx(dY[rows], ref["w_exact"]), what=f"{fid} cut bwd")
+
+
 @pytest.mark.parametrize("bits,group", [(4, 128), (2, 64)])
 @pytest.mark.parametrize("m", [3, 130])
 def test_bwd_dx_exact_on_grid(L, bits, group, m):
